@@ -1,0 +1,149 @@
+/*
+ * attn_bwd.h -- attention backward (dQ, dK, dV) on AMD Instinct MI355X (gfx950).
+ *
+ * Two forms of the same backward pass over variable-length TND batches with
+ * grouped-query attention:
+ *
+ *   dense    -- page "aclnnFlashAttentionUnpaddingScoreGradV3", Formula section:
+ *               Y = Softmax(Mask(Q K^T * scale)) V with Q = [query, queryRope] and
+ *               K = [key, keyRope] concatenated on the head dimension;
+ *               dV = P^T dY, dQ = dS K * scale, dqRope = dS kRope * scale,
+ *               dK = dS^T Q * scale, dkRope = dS^T qRope * scale.
+ *   selected -- page "NsaSelectedAttentionGrad" (README), formula section: every
+ *               query token and KV head gathers selectedBlockCount blocks of
+ *               selectedBlockSize key/value rows through topkIndices
+ *               (selectedKey = Gather(key, topkIndices[i])), then the same backward.
+ *
+ * dS is the softmax Jacobian applied to dP = dY V^T:  dS = P * (dP - rowsum(dY * O)),
+ * where rowsum(dY * O) equals rowsum(P * dP) because O = P V (no dropout; keep_prob
+ * is 1, the only value the dense page's constraints allow).
+ *
+ * Calling convention (both pages describe a two-phase call: a workspace-size query
+ * that validates the parameters, then an execute call on a stream with a caller-
+ * allocated workspace):
+ *   1. attn_bwd_workspace_size(&problem, &bytes)   -- host only, validates.
+ *   2. allocate `bytes` of device memory (any alignment >= 256 B).
+ *   3. attn_bwd_dense_varlen(...) or attn_bwd_selected(...) on a HIP stream.
+ * The problem struct is passed again at execute time; the library keeps no state
+ * between calls other than a small pinned host staging ring for schedule tables.
+ *
+ * Layouts (all device tensors contiguous, row-major, TND = [tokens, heads, dim],
+ * the rows of every sequence packed back to back with no padding):
+ *   query [T1, N1, d_qk]     query_rope [T1, N1, d_rope]     dq / dq_rope likewise
+ *   key   [T2, N2, d_qk]     key_rope   [T2, N2, d_rope]     dk / dk_rope likewise
+ *   value [T2, N2, d_v]      out, dy    [T1, N1, d_v]        dv [T2, N2, d_v]
+ *   softmax_max, softmax_sum [T1, N1, 8] float32 -- the row maximum m of the
+ *       scaled, masked scores and l = sum_j exp(s_j - m); lane 0 is read.
+ *   topk_indices [T1, N2, block_count] int32 -- block ids inside the token's own
+ *       sequence: id selects KV rows cu_seqlens_kv[b] + id*block_size + [0, block_size).
+ * Query head h uses KV head h / (N1 / N2).
+ *
+ * Ownership: the caller owns every device buffer, including the workspace.  The
+ * library allocates no device memory.  Outputs are fully overwritten (KV rows that
+ * no query attends receive 0).  Work is enqueued on `hip_stream` (NULL = default
+ * stream) and returns before it completes; inputs, outputs and workspace must stay
+ * valid until the stream reaches that point.
+ *
+ * Errors: every check runs before anything is enqueued; on failure nothing is
+ * enqueued and no output is touched.  Out-of-range topk ids are caller errors: the
+ * kernels skip such entries and raise a device-side flag that the next call on the
+ * same workspace does not read (see attn_bwd_check_index_flag).
+ *
+ * Determinism: with deterministic = 1 the outputs are bitwise identical for
+ * identical inputs, problem and device.  Both pages say the default is
+ * non-deterministic and determinism can be enabled; every kernel behind this
+ * interface happens to be deterministic in both modes unless
+ * `dkdv_atomic` is set (see below).
+ */
+#ifndef ATTN_BWD_H_
+#define ATTN_BWD_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULLPTR = 1,      /* a required pointer is NULL                        */
+  ATTN_ERR_INVALID = 2,      /* a shape / value constraint of the pages is broken */
+  ATTN_ERR_UNSUPPORTED = 3,  /* valid per the pages but not built here            */
+  ATTN_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the query returned */
+  ATTN_ERR_HIP = 5           /* a HIP runtime call failed                         */
+} attn_status_t;
+
+typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1, ATTN_FP32 = 2 } attn_dtype_t;
+typedef enum { ATTN_OP_DENSE = 0, ATTN_OP_SELECTED = 1 } attn_op_t;
+
+typedef struct {
+  int32_t op;                     /* attn_op_t                                              */
+  int32_t dtype;                  /* dense: ATTN_BF16 or ATTN_FP32; selected: ATTN_BF16    */
+  int32_t batch;                  /* B >= 1                                                 */
+  const int64_t* cu_seqlens_q;    /* HOST [B+1]: 0, then running sums of query lengths;
+                                     a length may be 0 (dense constraints allow S = 0)     */
+  const int64_t* cu_seqlens_kv;   /* HOST [B+1]: same for key/value lengths                */
+  int32_t n1, n2;                 /* query / KV heads, n1 % n2 == 0                         */
+  int32_t d_qk;                   /* head dim of query / key (the non-rope part)            */
+  int32_t d_rope;                 /* dense: head dim of queryRope / keyRope (0 = none);
+                                     selected: must be 0                                    */
+  int32_t d_v;                    /* head dim of value / out / dy                           */
+  double scale;                   /* scaleValue: the factor written 1/sqrt(d) on the pages  */
+  int32_t causal;                 /* dense: 1 = key j visible to query i iff j <= i within
+                                     the sequence (needs equal q / kv lengths); selected: 0 */
+  int32_t block_size;             /* selected: selectedBlockSize (<= 128, multiple of 16)  */
+  int32_t block_count;            /* selected: selectedBlockCount (1..128, count*size < 8192)*/
+  int32_t deterministic;          /* 1 = bitwise reproducible                               */
+  int32_t dkdv_atomic;            /* selected only: 1 = scatter dK/dV with fp32 atomics from
+                                     the query-major pass (non-deterministic; needs a larger
+                                     workspace); 0 = inverted-index KV-major pass.
+                                     Ignored (treated as 0) when deterministic = 1.          */
+} attn_bwd_problem_t;
+
+/* Validate `p` and return the workspace size in bytes for its execute call.
+ * Host only; touches no device.  Returns ATTN_OK, ATTN_ERR_NULLPTR (p, bytes or a
+ * cu_seqlens array is NULL), ATTN_ERR_INVALID or ATTN_ERR_UNSUPPORTED. */
+attn_status_t attn_bwd_workspace_size(const attn_bwd_problem_t* p, uint64_t* bytes);
+
+/* Dense varlen backward (page "aclnnFlashAttentionUnpaddingScoreGradV3").
+ * p->op must be ATTN_OP_DENSE.  Tensors are in p->dtype (bf16 or fp32) except the
+ * float32 statistics.  q_rope / k_rope / dq_rope / dk_rope must be NULL iff
+ * p->d_rope == 0.  `out` is the forward output O (used for rowsum(dY * O)). */
+attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p,
+                                    const void* q, const void* q_rope,
+                                    const void* k, const void* k_rope,
+                                    const void* v, const void* out, const void* dy,
+                                    const float* softmax_max, const float* softmax_sum,
+                                    void* dq, void* dq_rope, void* dk, void* dk_rope, void* dv,
+                                    void* workspace, uint64_t workspace_bytes,
+                                    void* hip_stream);
+
+/* Selected (NSA) backward (page "NsaSelectedAttentionGrad").  p->op must be
+ * ATTN_OP_SELECTED, p->dtype ATTN_BF16.  The page lists attentionOut as optional;
+ * this build requires it (NULL -> ATTN_ERR_UNSUPPORTED). */
+attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p,
+                                const void* q, const void* k, const void* v,
+                                const void* out, const void* dy,
+                                const float* softmax_max, const float* softmax_sum,
+                                const int32_t* topk_indices,
+                                void* dq, void* dk, void* dv,
+                                void* workspace, uint64_t workspace_bytes,
+                                void* hip_stream);
+
+/* Read (synchronously, on `hip_stream`) the device flag that a selected call raises
+ * when it meets a topk id outside [0, S2_b / block_size).  Writes 1 to *raised when
+ * the flag is set, 0 otherwise.  `workspace` is the one passed to that call. */
+attn_status_t attn_bwd_check_index_flag(const attn_bwd_problem_t* p, const void* workspace,
+                                        int32_t* raised, void* hip_stream);
+
+/* Short English text for a status code (static storage). */
+const char* attn_bwd_status_string(attn_status_t s);
+
+/* Library version, "major.minor.patch" (static storage). */
+const char* attn_bwd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_BWD_H_ */

@@ -1,0 +1,209 @@
+"""Attention backward (dense varlen FlashAttention-style and NSA selected) on MI355X.
+
+Thin ctypes binding over libattnbwd.so, whose C ABI is declared in
+include/attn_bwd.h.  The functions below keep the C names and only marshal
+arguments: every step of the backward runs in the library's HIP kernels.  torch
+is used for device memory and streams.
+
+    import sparse_attention_backward_amd as sab
+    prob = sab.Problem.dense(cu_q, cu_kv, n1, n2, d_qk, d_v, scale, causal=True, d_rope=64)
+    dq, dq_rope, dk, dk_rope, dv = sab.dense_backward(prob, q, q_rope, k, k_rope, v, out, dy, smax, ssum)
+
+The library must have been built (``python -m sparse_attention_backward_amd.build``);
+importing this package without it raises ImportError -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_double, c_int32, c_int64, c_uint64, c_void_p
+
+import torch
+
+__all__ = [
+    "AttnError", "Problem", "LIB_PATH", "lib",
+    "attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_selected",
+    "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version",
+    "dense_backward", "selected_backward", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnbwd.so")
+
+ATTN_OK, ATTN_ERR_NULLPTR, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
+ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
+ATTN_OP_DENSE, ATTN_OP_SELECTED = 0, 1
+
+EXPORTED_SYMBOLS = ("attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_selected",
+                    "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version")
+
+
+class attn_bwd_problem_t(ctypes.Structure):
+    _fields_ = [
+        ("op", c_int32), ("dtype", c_int32), ("batch", c_int32),
+        ("cu_seqlens_q", POINTER(c_int64)), ("cu_seqlens_kv", POINTER(c_int64)),
+        ("n1", c_int32), ("n2", c_int32),
+        ("d_qk", c_int32), ("d_rope", c_int32), ("d_v", c_int32),
+        ("scale", c_double), ("causal", c_int32),
+        ("block_size", c_int32), ("block_count", c_int32),
+        ("deterministic", c_int32), ("dkdv_atomic", c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_backward_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = POINTER(attn_bwd_problem_t)
+    L.attn_bwd_workspace_size.argtypes = [P, POINTER(c_uint64)]
+    L.attn_bwd_workspace_size.restype = c_int32
+    L.attn_bwd_dense_varlen.argtypes = [P] + [c_void_p] * 7 + [c_void_p, c_void_p] + [c_void_p] * 5 + \
+        [c_void_p, c_uint64, c_void_p]
+    L.attn_bwd_dense_varlen.restype = c_int32
+    L.attn_bwd_selected.argtypes = [P] + [c_void_p] * 5 + [c_void_p, c_void_p, c_void_p] + [c_void_p] * 3 + \
+        [c_void_p, c_uint64, c_void_p]
+    L.attn_bwd_selected.restype = c_int32
+    L.attn_bwd_check_index_flag.argtypes = [P, c_void_p, POINTER(c_int32), c_void_p]
+    L.attn_bwd_check_index_flag.restype = c_int32
+    L.attn_bwd_status_string.argtypes = [c_int32]
+    L.attn_bwd_status_string.restype = c_char_p
+    L.attn_bwd_version.argtypes = []
+    L.attn_bwd_version.restype = c_char_p
+    return L
+
+
+lib = _load()
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where}: {lib.attn_bwd_status_string(self.status).decode()} (status {self.status})")
+
+
+def _check(st, where):
+    if st != ATTN_OK:
+        raise AttnError(st, where)
+
+
+class Problem:
+    """attn_bwd_problem_t plus the host cu_seqlens arrays it points to (kept alive here)."""
+
+    def __init__(self, op, dtype, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, d_rope=0, causal=False,
+                 block_size=0, block_count=0, deterministic=False, dkdv_atomic=False):
+        cu_q = [int(x) for x in cu_q]
+        cu_kv = [int(x) for x in cu_kv]
+        self.cu_q_arr = (c_int64 * len(cu_q))(*cu_q)
+        self.cu_kv_arr = (c_int64 * len(cu_kv))(*cu_kv)
+        self.s = attn_bwd_problem_t(
+            op=op, dtype=dtype, batch=len(cu_q) - 1,
+            cu_seqlens_q=ctypes.cast(self.cu_q_arr, POINTER(c_int64)),
+            cu_seqlens_kv=ctypes.cast(self.cu_kv_arr, POINTER(c_int64)),
+            n1=n1, n2=n2, d_qk=d_qk, d_rope=d_rope, d_v=d_v, scale=float(scale), causal=int(bool(causal)),
+            block_size=block_size, block_count=block_count,
+            deterministic=int(bool(deterministic)), dkdv_atomic=int(bool(dkdv_atomic)))
+        self.T1, self.T2 = cu_q[-1], cu_kv[-1]
+
+    @classmethod
+    def dense(cls, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, causal=False, d_rope=0, dtype="bf16",
+              deterministic=False):
+        return cls(ATTN_OP_DENSE, {"bf16": ATTN_BF16, "fp32": ATTN_FP32, "fp16": ATTN_FP16}[dtype], cu_q, cu_kv,
+                   n1, n2, d_qk, d_v, scale, d_rope=d_rope, causal=causal, deterministic=deterministic)
+
+    @classmethod
+    def selected(cls, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, block_size, block_count, deterministic=False,
+                 dkdv_atomic=False, dtype="bf16"):
+        return cls(ATTN_OP_SELECTED, {"bf16": ATTN_BF16, "fp32": ATTN_FP32, "fp16": ATTN_FP16}[dtype], cu_q,
+                   cu_kv, n1, n2, d_qk, d_v, scale, block_size=block_size, block_count=block_count,
+                   deterministic=deterministic, dkdv_atomic=dkdv_atomic)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.s)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---- the C functions, same names ----------------------------------------------
+
+def attn_bwd_status_string(status: int) -> str:
+    return lib.attn_bwd_status_string(int(status)).decode()
+
+
+def attn_bwd_version() -> str:
+    return lib.attn_bwd_version().decode()
+
+
+def attn_bwd_workspace_size(problem: Problem) -> int:
+    n = c_uint64(0)
+    _check(lib.attn_bwd_workspace_size(problem.ref, ctypes.byref(n)), "attn_bwd_workspace_size")
+    return int(n.value)
+
+
+def attn_bwd_dense_varlen(problem, q, q_rope, k, k_rope, v, out, dy, softmax_max, softmax_sum,
+                          dq, dq_rope, dk, dk_rope, dv, workspace, workspace_bytes=None, stream=None):
+    wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = lib.attn_bwd_dense_varlen(problem.ref, _ptr(q), _ptr(q_rope), _ptr(k), _ptr(k_rope), _ptr(v), _ptr(out),
+                                   _ptr(dy), _ptr(softmax_max), _ptr(softmax_sum), _ptr(dq), _ptr(dq_rope), _ptr(dk),
+                                   _ptr(dk_rope), _ptr(dv), _ptr(workspace), wb, _stream(stream))
+    _check(st, "attn_bwd_dense_varlen")
+
+
+def attn_bwd_selected(problem, q, k, v, out, dy, softmax_max, softmax_sum, topk_indices, dq, dk, dv,
+                      workspace, workspace_bytes=None, stream=None):
+    wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = lib.attn_bwd_selected(problem.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dy), _ptr(softmax_max),
+                               _ptr(softmax_sum), _ptr(topk_indices), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                               wb, _stream(stream))
+    _check(st, "attn_bwd_selected")
+
+
+def attn_bwd_check_index_flag(problem, workspace, stream=None) -> bool:
+    r = c_int32(0)
+    _check(lib.attn_bwd_check_index_flag(problem.ref, _ptr(workspace), ctypes.byref(r), _stream(stream)),
+           "attn_bwd_check_index_flag")
+    return bool(r.value)
+
+
+# ---- allocation helpers (torch owns the memory) ----------------------------------
+
+def _workspace(problem, device):
+    n = attn_bwd_workspace_size(problem)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def dense_backward(problem, q, q_rope, k, k_rope, v, out, dy, softmax_max, softmax_sum, workspace=None,
+                   stream=None):
+    """Allocate outputs (and the workspace unless given) and run attn_bwd_dense_varlen.
+    Returns dq, dq_rope, dk, dk_rope, dv (rope outputs are None without rope)."""
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq_rope = torch.empty_like(q_rope) if q_rope is not None else None
+    dk_rope = torch.empty_like(k_rope) if k_rope is not None else None
+    ws = workspace if workspace is not None else _workspace(problem, q.device)
+    attn_bwd_dense_varlen(problem, q, q_rope, k, k_rope, v, out, dy, softmax_max, softmax_sum,
+                          dq, dq_rope, dk, dk_rope, dv, ws, stream=stream)
+    return dq, dq_rope, dk, dk_rope, dv
+
+
+def selected_backward(problem, q, k, v, out, dy, softmax_max, softmax_sum, topk_indices, workspace=None,
+                      stream=None):
+    """Allocate outputs (and the workspace unless given) and run attn_bwd_selected.
+    Returns dq, dk, dv."""
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = workspace if workspace is not None else _workspace(problem, q.device)
+    attn_bwd_selected(problem, q, k, v, out, dy, softmax_max, softmax_sum, topk_indices, dq, dk, dv, ws,
+                      stream=stream)
+    return dq, dk, dv

@@ -1,0 +1,381 @@
+// C-ABI layer: parameter validation, workspace layout, schedule tables, launches.
+//
+// The two-phase shape (workspace-size query that validates, then execute with a
+// caller-owned workspace on a stream) follows the calling convention that pages
+// "aclnnFlashAttentionUnpaddingScoreGradV3", "aclnnMoeTokenPermuteGrad" and the others
+// describe for their operators; the constraint checks restate the constraint lists of
+// the dense page and of page "NsaSelectedAttentionGrad".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "../../include/attn_bwd.h"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace ab;
+
+constexpr int64_t kDenseMaxT = 1 << 20;      // dense constraints: T in 1..1M
+constexpr int64_t kSelMaxT = 2 << 20;        // selected constraints: T1, T2 in 1..2M
+constexpr int64_t kSelMaxS = 128 << 10;      // selected constraints: S in 1..128K
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int B = 0, G = 0;
+  int64_t T1 = 0, T2 = 0;
+  // dense schedule
+  std::vector<int32_t> kv_tiles, q_tiles;
+  // selected
+  std::vector<int32_t> blkoff;
+  int nblk_total = 0;
+  int64_t entries = 0;
+  // workspace layout (byte offsets)
+  size_t off_cu_q = 0, off_cu_kv = 0, off_tab1 = 0, off_tab2 = 0, table_bytes = 0;
+  size_t off_lse2 = 0, off_drow = 0;
+  size_t off_counts = 0, off_offsets = 0, off_cursor = 0, off_list = 0, off_scratch = 0, off_flag = 0;
+  size_t total = 0;
+};
+
+attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
+  if (!p) return ATTN_ERR_NULLPTR;
+  if (p->op != ATTN_OP_DENSE && p->op != ATTN_OP_SELECTED) return ATTN_ERR_INVALID;
+  if (p->batch < 1) return ATTN_ERR_INVALID;
+  if (!p->cu_seqlens_q || !p->cu_seqlens_kv) return ATTN_ERR_NULLPTR;
+  const int B = p->batch;
+  const int64_t* cq = p->cu_seqlens_q;
+  const int64_t* ck = p->cu_seqlens_kv;
+  if (cq[0] != 0 || ck[0] != 0) return ATTN_ERR_INVALID;
+  for (int b = 0; b < B; ++b)
+    if (cq[b + 1] < cq[b] || ck[b + 1] < ck[b]) return ATTN_ERR_INVALID;
+  if (p->n1 < 1 || p->n2 < 1 || p->n1 % p->n2 != 0) return ATTN_ERR_INVALID;
+  if (p->d_qk < 1 || p->d_v < 1 || p->d_rope < 0) return ATTN_ERR_INVALID;
+  if (!std::isfinite(p->scale)) return ATTN_ERR_INVALID;
+  if ((p->causal != 0 && p->causal != 1) || (p->deterministic != 0 && p->deterministic != 1) ||
+      (p->dkdv_atomic != 0 && p->dkdv_atomic != 1))
+    return ATTN_ERR_INVALID;
+  pl.B = B;
+  pl.G = p->n1 / p->n2;
+  pl.T1 = cq[B];
+  pl.T2 = ck[B];
+
+  if (p->op == ATTN_OP_DENSE) {
+    if (p->dtype == ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
+    if (p->dtype != ATTN_BF16 && p->dtype != ATTN_FP32) return ATTN_ERR_INVALID;
+    // D of query / key and of value / dy: multiples of 8, value D <= query D; D <= 768; N <= 256
+    if (p->d_qk % 8 || p->d_v % 8 || p->d_rope % 8) return ATTN_ERR_INVALID;
+    if (p->d_v > p->d_qk) return ATTN_ERR_INVALID;
+    if (p->d_qk + p->d_rope > 768 || p->n1 > 256) return ATTN_ERR_INVALID;
+    if (pl.T1 > kDenseMaxT || pl.T2 > kDenseMaxT) return ATTN_ERR_INVALID;
+    if (p->causal)
+      for (int b = 0; b < B; ++b)
+        if (cq[b + 1] - cq[b] != ck[b + 1] - ck[b]) return ATTN_ERR_INVALID;
+    const int dqk = p->d_qk + p->d_rope;
+    if (p->dtype == ATTN_BF16 && !dense_bf16_supported(dqk, p->d_v)) return ATTN_ERR_UNSUPPORTED;
+    if (p->dtype == ATTN_FP32 && (dqk > 256 || p->d_v > 256)) return ATTN_ERR_UNSUPPORTED;
+    // schedule: heaviest tiles first
+    struct W { int64_t work; int32_t b, tile; };
+    std::vector<W> kv, qv;
+    for (int b = 0; b < B; ++b) {
+      const int64_t S1 = cq[b + 1] - cq[b], S2 = ck[b + 1] - ck[b];
+      const int64_t nqt = (S1 + kDenseTile - 1) / kDenseTile, nkt = (S2 + kDenseTile - 1) / kDenseTile;
+      for (int64_t t = 0; t < nkt; ++t) kv.push_back({p->causal ? nqt - t : nqt, b, (int32_t)t});
+      for (int64_t t = 0; t < nqt; ++t) qv.push_back({p->causal ? t + 1 : nkt, b, (int32_t)t});
+    }
+    auto heavy_first = [](const W& x, const W& y) { return x.work > y.work; };
+    std::stable_sort(kv.begin(), kv.end(), heavy_first);
+    std::stable_sort(qv.begin(), qv.end(), heavy_first);
+    for (auto& x : kv) { pl.kv_tiles.push_back(x.b); pl.kv_tiles.push_back(x.tile); }
+    for (auto& x : qv) { pl.q_tiles.push_back(x.b); pl.q_tiles.push_back(x.tile); }
+  } else {
+    if (p->dtype == ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
+    if (p->dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+    if (p->d_rope != 0 || p->causal != 0) return ATTN_ERR_INVALID;
+    // D is 192 or 128 (K and V may differ); N1, N2 in 1..128; G in 1..32
+    if ((p->d_qk != 128 && p->d_qk != 192) || (p->d_v != 128 && p->d_v != 192)) return ATTN_ERR_INVALID;
+    if (p->n1 > 128 || p->n2 > 128 || pl.G > 32) return ATTN_ERR_INVALID;
+    // selectedBlockSize <= 128, multiple of 16; selectedBlockCount 1..128; count*size < 8K
+    const int bs = p->block_size, cnt = p->block_count;
+    if (bs <= 0 || bs > 128 || bs % 16) return ATTN_ERR_INVALID;
+    if (cnt < 1 || cnt > 128 || (int64_t)cnt * bs >= 8192) return ATTN_ERR_INVALID;
+    if (pl.T1 > kSelMaxT || pl.T2 > kSelMaxT) return ATTN_ERR_INVALID;
+    pl.blkoff.assign(B + 1, 0);
+    for (int b = 0; b < B; ++b) {
+      const int64_t S1 = cq[b + 1] - cq[b], S2 = ck[b + 1] - ck[b];
+      if (S1 > kSelMaxS || S2 > kSelMaxS) return ATTN_ERR_INVALID;
+      // KV S of each sequence: a multiple of blockSize and >= count*size (read as >=)
+      if (S2 % bs) return ATTN_ERR_INVALID;
+      if (S1 > 0 && S2 < (int64_t)cnt * bs) return ATTN_ERR_INVALID;
+      pl.blkoff[b + 1] = pl.blkoff[b] + (int32_t)(S2 / bs);
+    }
+    pl.nblk_total = pl.blkoff[B];
+    if (!selected_supported(p->d_qk, p->d_v, pl.G, bs)) return ATTN_ERR_UNSUPPORTED;
+    if (p->dkdv_atomic && !p->deterministic) return ATTN_ERR_UNSUPPORTED;
+    pl.entries = pl.T1 * p->n2 * cnt;
+    if (pl.entries >= (int64_t(1) << 31) || (int64_t)p->n2 * pl.nblk_total >= (int64_t(1) << 31))
+      return ATTN_ERR_UNSUPPORTED;
+  }
+
+  // ---- workspace layout ----
+  size_t o = 0;
+  pl.off_cu_q = o;  o += 8 * (size_t)(B + 1);
+  pl.off_cu_kv = o; o += 8 * (size_t)(B + 1);
+  pl.off_tab1 = o;
+  if (p->op == ATTN_OP_DENSE) {
+    o += 4 * pl.kv_tiles.size();
+    pl.off_tab2 = o;
+    o += 4 * pl.q_tiles.size();
+  } else {
+    o += 4 * pl.blkoff.size();
+    pl.off_tab2 = o;
+  }
+  pl.table_bytes = o;
+  o = align_up(o);
+  const size_t rows = (size_t)pl.T1 * p->n1;
+  pl.off_lse2 = o; o = align_up(o + 4 * rows);
+  pl.off_drow = o; o = align_up(o + 4 * rows);
+  if (p->op == ATTN_OP_SELECTED) {
+    const size_t nkeys = (size_t)p->n2 * pl.nblk_total;
+    pl.off_counts = o;  o = align_up(o + 4 * nkeys);
+    pl.off_offsets = o; o = align_up(o + 4 * (nkeys + 1));
+    pl.off_cursor = o;  o = align_up(o + 4 * nkeys);
+    pl.off_list = o;    o = align_up(o + 4 * (size_t)pl.entries);
+    pl.off_scratch = o; o = align_up(o + 8 * (size_t)pl.entries);
+    pl.off_flag = o;    o = align_up(o + 4);
+  }
+  pl.total = o;
+  return ATTN_OK;
+}
+
+// ---- pinned staging ring for the per-call tables --------------------------------
+// A slot is reused only after the copy that last read it has executed (its event).
+struct StagingSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+struct DeviceStaging {
+  std::mutex mu;
+  StagingSlot slots[4];
+  int next = 0;
+};
+std::mutex g_staging_mu;
+std::map<int, DeviceStaging*> g_staging;
+
+hipError_t upload_tables(const std::vector<uint8_t>& bytes, void* dst, hipStream_t s) {
+  if (bytes.empty()) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  DeviceStaging* ds;
+  {
+    std::lock_guard<std::mutex> lk(g_staging_mu);
+    auto it = g_staging.find(dev);
+    if (it == g_staging.end()) it = g_staging.emplace(dev, new DeviceStaging).first;
+    ds = it->second;
+  }
+  std::lock_guard<std::mutex> lk(ds->mu);
+  StagingSlot& sl = ds->slots[ds->next];
+  ds->next = (ds->next + 1) % 4;
+  if (sl.pending) {
+    e = hipEventSynchronize(sl.ev);
+    if (e != hipSuccess) return e;
+    sl.pending = false;
+  }
+  if (!sl.ev) {
+    e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  if (sl.cap < bytes.size()) {
+    if (sl.host) (void)hipHostFree(sl.host);
+    sl.host = nullptr;
+    sl.cap = 0;
+    const size_t cap = std::max<size_t>(bytes.size(), 4096);
+    e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return e;
+    sl.cap = cap;
+  }
+  std::memcpy(sl.host, bytes.data(), bytes.size());
+  e = hipMemcpyAsync(dst, sl.host, bytes.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(sl.ev, s);
+  if (e != hipSuccess) return e;
+  sl.pending = true;
+  return hipSuccess;
+}
+
+std::vector<uint8_t> pack_tables(const attn_bwd_problem_t* p, const Plan& pl) {
+  std::vector<uint8_t> t(pl.table_bytes, 0);
+  std::memcpy(t.data() + pl.off_cu_q, p->cu_seqlens_q, 8 * (size_t)(pl.B + 1));
+  std::memcpy(t.data() + pl.off_cu_kv, p->cu_seqlens_kv, 8 * (size_t)(pl.B + 1));
+  if (p->op == ATTN_OP_DENSE) {
+    if (!pl.kv_tiles.empty()) std::memcpy(t.data() + pl.off_tab1, pl.kv_tiles.data(), 4 * pl.kv_tiles.size());
+    if (!pl.q_tiles.empty()) std::memcpy(t.data() + pl.off_tab2, pl.q_tiles.data(), 4 * pl.q_tiles.size());
+  } else {
+    std::memcpy(t.data() + pl.off_tab1, pl.blkoff.data(), 4 * pl.blkoff.size());
+  }
+  return t;
+}
+
+bool misaligned(const void* ptr) { return ptr && (reinterpret_cast<uintptr_t>(ptr) & 15u); }
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off); }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_bwd_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULLPTR: return "null pointer";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported combination";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* attn_bwd_version(void) { return "0.1.0"; }
+
+attn_status_t attn_bwd_workspace_size(const attn_bwd_problem_t* p, uint64_t* bytes) {
+  if (!bytes) return ATTN_ERR_NULLPTR;
+  Plan pl;
+  const attn_status_t st = validate_and_plan(p, pl);
+  if (st != ATTN_OK) return st;
+  *bytes = pl.total;
+  return ATTN_OK;
+}
+
+attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, const void* q_rope,
+                                    const void* k, const void* k_rope, const void* v, const void* out,
+                                    const void* dy, const float* softmax_max, const float* softmax_sum,
+                                    void* dq, void* dq_rope, void* dk, void* dk_rope, void* dv,
+                                    void* workspace, uint64_t workspace_bytes, void* hip_stream) {
+  Plan pl;
+  attn_status_t st = validate_and_plan(p, pl);
+  if (st != ATTN_OK) return st;
+  if (p->op != ATTN_OP_DENSE) return ATTN_ERR_INVALID;
+  const bool has_q = pl.T1 > 0, has_k = pl.T2 > 0;
+  if (has_q && (!q || !out || !dy || !softmax_max || !softmax_sum || !dq)) return ATTN_ERR_NULLPTR;
+  if (has_k && (!k || !v || !dk || !dv)) return ATTN_ERR_NULLPTR;
+  if (p->d_rope > 0) {
+    if ((has_q && (!q_rope || !dq_rope)) || (has_k && (!k_rope || !dk_rope))) return ATTN_ERR_NULLPTR;
+  } else if (q_rope || k_rope || dq_rope || dk_rope) {
+    return ATTN_ERR_INVALID;
+  }
+  for (const void* ptr : {q, q_rope, k, k_rope, v, out, dy, (const void*)softmax_max, (const void*)softmax_sum,
+                          (const void*)dq, (const void*)dq_rope, (const void*)dk, (const void*)dk_rope, (const void*)dv})
+    if (misaligned(ptr)) return ATTN_ERR_INVALID;
+  if (!workspace || workspace_bytes < pl.total || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return ATTN_ERR_WORKSPACE;
+  if (!has_q && !has_k) return ATTN_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (upload_tables(pack_tables(p, pl), workspace, s) != hipSuccess) return ATTN_ERR_HIP;
+
+  PreArgs pa{};
+  pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
+  pa.lse2 = at<float>(workspace, pl.off_lse2); pa.drow = at<float>(workspace, pl.off_drow);
+  pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = p->dtype == ATTN_BF16;
+  if (launch_preprocess(pa, s) != hipSuccess) return ATTN_ERR_HIP;
+
+  DenseArgs a{};
+  a.q = q; a.q_rope = q_rope; a.k = k; a.k_rope = k_rope; a.v = v; a.dy = dy;
+  a.lse2 = pa.lse2; a.drow = pa.drow;
+  a.dq = dq; a.dq_rope = dq_rope; a.dk = dk; a.dk_rope = dk_rope; a.dv = dv;
+  a.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
+  a.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
+  a.kv_tiles = at<const int32_t>(workspace, pl.off_tab1);
+  a.q_tiles = at<const int32_t>(workspace, pl.off_tab2);
+  a.n_kv_tiles = (int)(pl.kv_tiles.size() / 2);
+  a.n_q_tiles = (int)(pl.q_tiles.size() / 2);
+  a.batch = pl.B; a.n1 = p->n1; a.n2 = p->n2; a.G = pl.G;
+  a.T1 = pl.T1; a.T2 = pl.T2;
+  a.d_main = p->d_qk; a.d_rope = p->d_rope; a.d_v = p->d_v;
+  a.scale = (float)p->scale;
+  a.scale_log2e = (float)(p->scale * 1.4426950408889634);
+  a.causal = p->causal;
+  const hipError_t e = p->dtype == ATTN_BF16 ? launch_dense_bf16(a, s) : launch_dense_fp32(a, s);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, const void* k, const void* v,
+                                const void* out, const void* dy, const float* softmax_max,
+                                const float* softmax_sum, const int32_t* topk_indices, void* dq, void* dk,
+                                void* dv, void* workspace, uint64_t workspace_bytes, void* hip_stream) {
+  Plan pl;
+  attn_status_t st = validate_and_plan(p, pl);
+  if (st != ATTN_OK) return st;
+  if (p->op != ATTN_OP_SELECTED) return ATTN_ERR_INVALID;
+  const bool has_q = pl.T1 > 0, has_k = pl.T2 > 0;
+  if (has_q && !out) return ATTN_ERR_UNSUPPORTED;  // attentionOut is optional on the page; required here
+  if (has_q && (!q || !dy || !softmax_max || !softmax_sum || !topk_indices || !dq)) return ATTN_ERR_NULLPTR;
+  if (has_k && (!k || !v || !dk || !dv)) return ATTN_ERR_NULLPTR;
+  for (const void* ptr : {q, k, v, out, dy, (const void*)softmax_max, (const void*)softmax_sum,
+                          (const void*)topk_indices, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (misaligned(ptr)) return ATTN_ERR_INVALID;
+  if (!workspace || workspace_bytes < pl.total || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return ATTN_ERR_WORKSPACE;
+  if (!has_q && !has_k) return ATTN_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (upload_tables(pack_tables(p, pl), workspace, s) != hipSuccess) return ATTN_ERR_HIP;
+
+  PreArgs pa{};
+  pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
+  pa.lse2 = at<float>(workspace, pl.off_lse2); pa.drow = at<float>(workspace, pl.off_drow);
+  pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = 1;
+  if (launch_preprocess(pa, s) != hipSuccess) return ATTN_ERR_HIP;
+
+  SelArgs a{};
+  a.q = q; a.k = k; a.v = v; a.dy = dy; a.lse2 = pa.lse2; a.drow = pa.drow; a.topk = topk_indices;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
+  a.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
+  a.blkoff = at<const int32_t>(workspace, pl.off_tab1);
+  a.batch = pl.B; a.n1 = p->n1; a.n2 = p->n2; a.G = pl.G;
+  a.d_qk = p->d_qk; a.d_v = p->d_v; a.bs = p->block_size; a.cnt = p->block_count;
+  a.nblk_total = pl.nblk_total; a.T1 = pl.T1; a.T2 = pl.T2;
+  a.scale = (float)p->scale;
+  a.scale_log2e = (float)(p->scale * 1.4426950408889634);
+  a.counts = at<int32_t>(workspace, pl.off_counts);
+  a.offsets = at<int32_t>(workspace, pl.off_offsets);
+  a.cursor = at<int32_t>(workspace, pl.off_cursor);
+  a.list = at<int32_t>(workspace, pl.off_list);
+  a.sort_scratch = at<int32_t>(workspace, pl.off_scratch);
+  a.flag = at<int32_t>(workspace, pl.off_flag);
+  if (launch_selected_index(a, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (launch_selected_dq(a, 0, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (launch_selected_dkdv(a, s) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status_t attn_bwd_check_index_flag(const attn_bwd_problem_t* p, const void* workspace, int32_t* raised,
+                                        void* hip_stream) {
+  if (!raised || !workspace) return ATTN_ERR_NULLPTR;
+  Plan pl;
+  attn_status_t st = validate_and_plan(p, pl);
+  if (st != ATTN_OK) return st;
+  if (p->op != ATTN_OP_SELECTED) return ATTN_ERR_INVALID;
+  int32_t h = 0;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (hipMemcpyAsync(&h, static_cast<const uint8_t*>(workspace) + pl.off_flag, 4, hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return ATTN_ERR_HIP;
+  *raised = h ? 1 : 0;
+  return ATTN_OK;
+}
+
+}  // extern "C"

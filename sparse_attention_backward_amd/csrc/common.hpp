@@ -1,0 +1,101 @@
+// Shared device helpers for the gfx950 attention-backward kernels.
+//
+// MFMA lane layouts used throughout (64-lane wavefront, l = lane id, g = l / 16):
+//   v_mfma_f32_16x16x32_bf16   A (16 x 32): lane holds row l%16, k = 8g .. 8g+7
+//                              B (32 x 16): lane holds col l%16, k = 8g .. 8g+7
+//                              C (16 x 16): lane holds col l%16, rows 4g .. 4g+3
+//   v_mfma_f32_16x16x16_bf16   A / B as above with k = 4g .. 4g+3, same C.
+// A contraction may permute its k index freely as long as A and B agree, so the
+// C tile of one product (lane: fixed column, four consecutive rows) feeds the A
+// operand of the next product when two row tiles are packed into the 8 k-slots:
+// slot j < 4 <- rows 4g+j of tile t0, slot j >= 4 <- rows 4g+j-4 of tile t1.
+//
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, output lane i,
+// element j comes from element i%4 of the 8-byte word addressed by lane 4j + i/4
+// of the same group.  If lane (jj = (l%16)/4, q = l%4) addresses
+// &M[row(jj)][c0 + 4q] of a row-major bf16 tile M, lane i of the group receives
+// M[row(j)][c0 + i] for j = 0..3: a column slice, i.e. the B operand of an MFMA
+// whose k index runs over rows of M.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ab {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Transposed 4 x bf16 read from LDS (see header comment).  `p` points into LDS.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join8(i16x4 lo, i16x4 hi) {
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);  // round to nearest even
+}
+
+// Pack eight floats (two C tiles' four values each) into an A operand.
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+  r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+  r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+  return r;
+}
+
+__device__ __forceinline__ i16x4 pack4(f32x4 v) {
+  bf16x4 r;
+  r[0] = (__bf16)v[0]; r[1] = (__bf16)v[1]; r[2] = (__bf16)v[2]; r[3] = (__bf16)v[3];
+  return __builtin_bit_cast(i16x4, r);
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ void sts16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Sequence of a packed row: largest b with cu[b] <= row (cu has B + 1 entries).
+__device__ __forceinline__ int seq_of(const int64_t* cu, int batch, int64_t row) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int seq_of32(const int32_t* cu, int batch, int32_t v) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= v) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace ab

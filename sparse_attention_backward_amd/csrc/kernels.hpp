@@ -1,0 +1,80 @@
+// Kernel argument blocks and launchers (host-callable), shared by the C-ABI layer
+// and the kernel translation units.  All pointers are device pointers unless noted.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ab {
+
+// ---- row statistics: lse2 = (m + ln l) * log2(e), drow = rowsum(dY * O) -------
+struct PreArgs {
+  const void* out;        // [rows, dv] bf16 or fp32
+  const void* dy;         // [rows, dv]
+  const float* smax;      // [rows, 8]
+  const float* ssum;      // [rows, 8]
+  float* lse2;            // [rows]
+  float* drow;            // [rows]
+  int64_t rows;           // T1 * N1
+  int dv;
+  int is_bf16;
+};
+hipError_t launch_preprocess(const PreArgs& a, hipStream_t s);
+
+// ---- dense varlen ------------------------------------------------------------
+struct DenseArgs {
+  const void* q;  const void* q_rope;
+  const void* k;  const void* k_rope;
+  const void* v;  const void* dy;
+  const float* lse2; const float* drow;
+  void* dq; void* dq_rope; void* dk; void* dk_rope; void* dv;
+  const int64_t* cu_q;      // [B+1]
+  const int64_t* cu_kv;     // [B+1]
+  const int32_t* kv_tiles;  // [n_kv_tiles, 2] = (sequence, key tile), heaviest first
+  const int32_t* q_tiles;   // [n_q_tiles, 2]  = (sequence, query tile), heaviest first
+  int n_kv_tiles, n_q_tiles;
+  int batch, n1, n2, G;
+  int64_t T1, T2;
+  int d_main, d_rope, d_v;  // head dims: query/key main part, rope part, value
+  float scale, scale_log2e;
+  int causal;
+};
+constexpr int kDenseTile = 64;  // query and key tile length of the bf16 dense kernels
+bool dense_bf16_supported(int d_qk_total, int d_v);
+hipError_t launch_dense_bf16(const DenseArgs& a, hipStream_t s);     // KV-major dK/dV, then query-major dQ
+hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s);  // KV-major dK/dV only
+constexpr int kDenseTileF32 = 64;
+hipError_t launch_dense_fp32(const DenseArgs& a, hipStream_t s);
+
+// ---- selected (NSA) ----------------------------------------------------------
+struct SelArgs {
+  const void* q; const void* k; const void* v; const void* dy;
+  const float* lse2; const float* drow;
+  const int32_t* topk;      // [T1, N2, cnt]
+  void* dq; void* dk; void* dv;
+  const int64_t* cu_q;      // [B+1]
+  const int64_t* cu_kv;     // [B+1]
+  const int32_t* blkoff;    // [B+1] running sum of blocks per sequence (S2_b / bs)
+  int batch, n1, n2, G, d_qk, d_v, bs, cnt;
+  int nblk_total;           // blkoff[B]
+  int64_t T1;
+  float scale, scale_log2e;
+  // inverted index (workspace)
+  int32_t* counts;          // [nkeys]      nkeys = n2 * nblk_total
+  int32_t* offsets;         // [nkeys + 1]
+  int32_t* cursor;          // [nkeys]
+  int32_t* list;            // [T1 * n2 * cnt]  entries t * cnt + slot, sorted per key
+  int32_t* sort_scratch;    // [2 * T1 * n2 * cnt]
+  int32_t* flag;            // [1] raised on an out-of-range topk id
+  float* dkdv_acc;          // [T2, n2, d_qk + d_v] fp32, atomic mode only
+  int64_t T2;
+};
+bool selected_supported(int d_qk, int d_v, int G, int bs);
+hipError_t launch_selected_index(const SelArgs& a, hipStream_t s);
+hipError_t launch_selected_dq(const SelArgs& a, int atomic_dkdv, hipStream_t s);
+hipError_t launch_selected_dkdv(const SelArgs& a, hipStream_t s);
+
+// ---- misc --------------------------------------------------------------------
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);  // kernel, not a memset node
+
+}  // namespace ab

@@ -1,0 +1,103 @@
+"""Shared helpers for the parity tests: oracle-side inputs, GPU calls, tolerances.
+
+Inputs come from the seeded generators in ``workloads``; O and the softmax
+statistics come from the float64 oracle forward (never from the GPU path).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import workloads as W
+
+# Tolerances per output tensor.
+BF16_REL_L2 = 1e-2
+BF16_MAX_ABS = 2e-2   # times max |ref|
+FP32_REL_L2 = 1e-4
+
+
+def f64(t):
+    return None if t is None else t.detach().to("cpu", torch.float64).numpy()
+
+
+def assert_close(name, got, ref, dtype):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    if ref.size == 0:
+        return
+    nref = np.linalg.norm(ref)
+    err = np.linalg.norm(got - ref)
+    rel = err / nref if nref > 0 else err
+    mx = np.abs(got - ref).max()
+    mref = np.abs(ref).max()
+    if dtype == "fp32":
+        assert rel <= FP32_REL_L2 or (nref == 0 and err <= 1e-6), f"{name}: rel L2 {rel:.3e} > {FP32_REL_L2}"
+    else:
+        if nref == 0:
+            assert mx <= 1e-6, f"{name}: expected zeros, max |x| = {mx:.3e}"
+            return
+        assert rel <= BF16_REL_L2, f"{name}: rel L2 {rel:.3e} > {BF16_REL_L2}"
+        assert mx <= BF16_MAX_ABS * mref, f"{name}: max abs {mx:.3e} > {BF16_MAX_ABS} * {mref:.3e}"
+
+
+def oracle_forward(w: W.Workload, x):
+    """O (cast to the workload dtype) and the [T, N, 8] statistics, from the oracle."""
+    if w.form == "dense":
+        o, m, l = O.forward_dense(f64(x["query"]), f64(x["key"]), f64(x["value"]), w.cu_q, w.cu_kv, w.n1, w.n2,
+                                  w.scale, w.causal, f64(x["query_rope"]), f64(x["key_rope"]))
+    else:
+        o, m, l = O.forward_selected(f64(x["query"]), f64(x["key"]), f64(x["value"]), x["topk"].numpy(),
+                                     w.cu_q, w.cu_kv, w.n1, w.n2, w.scale, w.block_size)
+    smax, ssum = O.stats_tensor(m, l)
+    return W.cast(o, w.dtype), torch.from_numpy(smax), torch.from_numpy(ssum)
+
+
+def oracle_backward(w: W.Workload, x):
+    if w.form == "dense":
+        dq, dqr, dk, dkr, dv = O.backward_dense(f64(x["query"]), f64(x["key"]), f64(x["value"]), f64(x["dy"]),
+                                                w.cu_q, w.cu_kv, w.n1, w.n2, w.scale, w.causal,
+                                                f64(x["query_rope"]), f64(x["key_rope"]))
+        return {"dq": dq, "dq_rope": dqr if w.d_rope else None, "dk": dk, "dk_rope": dkr if w.d_rope else None,
+                "dv": dv}
+    dq, dk, dv = O.backward_selected(f64(x["query"]), f64(x["key"]), f64(x["value"]), f64(x["dy"]),
+                                     x["topk"].numpy(), w.cu_q, w.cu_kv, w.n1, w.n2, w.scale, w.block_size)
+    return {"dq": dq, "dk": dk, "dv": dv}
+
+
+def problem_for(w: W.Workload, deterministic=None):
+    import sparse_attention_backward_amd as sab
+    det = w.deterministic if deterministic is None else deterministic
+    if w.form == "dense":
+        return sab.Problem.dense(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, causal=w.causal,
+                                 d_rope=w.d_rope, dtype=w.dtype, deterministic=det)
+    return sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size, w.block_count,
+                                deterministic=det)
+
+
+def gpu_backward(w: W.Workload, x, o, smax, ssum, device="cuda", deterministic=None):
+    """Run the library on the GPU; returns the outputs as float64 numpy arrays."""
+    import sparse_attention_backward_amd as sab
+    dev = lambda t: None if t is None else t.to(device).contiguous()  # noqa: E731
+    prob = problem_for(w, deterministic)
+    if w.form == "dense":
+        outs = sab.dense_backward(prob, dev(x["query"]), dev(x["query_rope"]), dev(x["key"]), dev(x["key_rope"]),
+                                  dev(x["value"]), dev(o), dev(x["dy"]), dev(smax), dev(ssum))
+        torch.cuda.synchronize()
+        names = ("dq", "dq_rope", "dk", "dk_rope", "dv")
+    else:
+        outs = sab.selected_backward(prob, dev(x["query"]), dev(x["key"]), dev(x["value"]), dev(o), dev(x["dy"]),
+                                     dev(smax), dev(ssum), dev(x["topk"]))
+        torch.cuda.synchronize()
+        names = ("dq", "dk", "dv")
+    return {n: (None if t is None else t) for n, t in zip(names, outs)}
+
+
+def check_against_oracle(w: W.Workload, got, ref):
+    for name, r in ref.items():
+        if r is None:
+            assert got.get(name) is None
+            continue
+        assert_close(f"{w.name}:{name}", f64(got[name]), r, w.dtype)

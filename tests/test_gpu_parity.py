@@ -1,0 +1,101 @@
+"""GPU parity: the HIP library against the float64 oracle, element by element,
+on seeded inputs that span several tiles and a ragged tail."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from helpers import (assert_close, check_against_oracle, f64, gpu_backward, oracle_backward, oracle_forward)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, deterministic=None):
+    x = W.make_inputs(w)
+    o, smax, ssum = oracle_forward(w, x)
+    print(f"[parity] {w.name} seqlens={w.seqlens_q}/{w.seqlens_kv} n1={w.n1} n2={w.n2}", flush=True)
+    got = gpu_backward(w, x, o, smax, ssum, deterministic=deterministic)
+    ref = oracle_backward(w, x)
+    check_against_oracle(w, got, ref)
+    return x, got, ref
+
+
+def test_dense_fp32_config1():
+    _run(W.config(1))
+
+
+@pytest.mark.parametrize("seqlens,n1,n2,d_qk,d_rope,d_v", [
+    ((200, 130), 8, 2, 128, 64, 128),     # rope split, GQA G=4, ragged tails
+    ((64, 1, 129), 4, 4, 128, 0, 128),    # no rope, G=1, a one-token sequence
+    ((97,), 4, 1, 64, 0, 64),             # small head dim, G=4
+])
+def test_dense_bf16_causal(seqlens, n1, n2, d_qk, d_rope, d_v):
+    _run(W.small_dense(seqlens=seqlens, n1=n1, n2=n2, d_qk=d_qk, d_rope=d_rope, d_v=d_v))
+
+
+def test_dense_bf16_noncausal_unequal_lengths():
+    w = W.small_dense(seqlens=(150,), n1=4, n2=2, d_qk=128, d_rope=64, d_v=128, causal=False)
+    w = w.with_(seqlens_q=(150, 0, 70), seqlens_kv=(77, 64, 200), name="dense-noncausal-unequal")
+    _run(w)
+
+
+def test_dense_fp32_small_rope():
+    w = W.small_dense(seqlens=(70, 33), n1=4, n2=2, d_qk=64, d_rope=32, d_v=64, dtype="fp32")
+    _run(w)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(seqlens=(256, 384), block_size=64, block_count=3),
+    dict(seqlens=(256, 512), block_size=128, block_count=2),
+    dict(seqlens=(192, 96), block_size=32, block_count=3, n1=16, n2=2),
+    dict(seqlens=(128, 128), block_size=16, block_count=5, n1=8, n2=1, d_qk=128, d_v=128),
+    dict(seqlens=(200, 0, 64), seqlens_kv=(256, 128, 192), block_size=64, block_count=2, index_dist="zipf"),
+])
+def test_selected(kw):
+    _run(W.small_selected(**kw))
+
+
+def test_selected_duplicate_ids():
+    w = W.small_selected(seqlens=(128, 192), block_size=64, block_count=2)
+    x = W.make_inputs(w)
+    x["topk"][::3, :, 1] = x["topk"][::3, :, 0]   # literal Gather: a repeated block counts twice
+    o, smax, ssum = oracle_forward(w, x)
+    got = gpu_backward(w, x, o, smax, ssum)
+    check_against_oracle(w, got, oracle_backward(w, x))
+
+
+def test_selected_deterministic_bitwise():
+    w = W.small_selected(seqlens=(256, 384), block_size=64, block_count=4, index_dist="zipf")
+    x = W.make_inputs(w)
+    o, smax, ssum = oracle_forward(w, x)
+    a = gpu_backward(w, x, o, smax, ssum, deterministic=True)
+    b = gpu_backward(w, x, o, smax, ssum, deterministic=True)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_dense_deterministic_bitwise():
+    w = W.small_dense(seqlens=(300, 77))
+    x = W.make_inputs(w)
+    o, smax, ssum = oracle_forward(w, x)
+    a = gpu_backward(w, x, o, smax, ssum, deterministic=True)
+    b = gpu_backward(w, x, o, smax, ssum, deterministic=True)
+    for n in a:
+        if a[n] is not None:
+            assert torch.equal(a[n], b[n]), n
+
+
+def test_selected_gradient_sums_on_gpu_outputs():
+    """rowsum(dS) = 0 => sum_j dK_j = 0 per (sequence, KV head); sum_j dV_j = sum of dY over the group."""
+    w = W.small_selected(seqlens=(256, 384), block_size=64, block_count=3)
+    x, got, ref = _run(w)
+    dk, dv, dy = f64(got["dk"]), f64(got["dv"]), f64(x["dy"])
+    G = w.G
+    for b in range(w.batch):
+        ks, ke = w.cu_kv[b], w.cu_kv[b + 1]
+        qs, qe = w.cu_q[b], w.cu_q[b + 1]
+        for h in range(w.n2):
+            sk = dk[ks:ke, h].sum(axis=0)
+            assert np.abs(sk).max() <= 2e-2 * np.abs(dk[ks:ke, h]).sum(axis=0).max() + 1e-6
+            want = dy[qs:qe, h * G:(h + 1) * G].sum(axis=(0, 1))
+            np.testing.assert_allclose(dv[ks:ke, h].sum(axis=0), want, rtol=2e-2, atol=2e-2 * np.abs(want).max())
