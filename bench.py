@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Attention-backward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-extra] [--no-cpu-baseline]
+
+A step is one complete C-ABI call (row statistics, schedule upload, every kernel)
+over one batch of synthetic input already resident in HBM.  The default workload
+is the dense varlen bf16 case (causal, rope split, GQA 32/8, D 128+64 / 128, four
+sequences with seeded lengths); --workload 3/4/5 selects a selected-attention case.
+`value` is algorithmic TFLOP/s: attended (query row, key row) pairs x 2(3 D_qk + 2 D_v),
+causal pairs only (the five GEMMs S, dP, dV, dQ, dK; recomputation is not counted).
+
+O and the softmax statistics fed to the timed call are produced once, before timing,
+by a plain fp32 torch forward on the GPU (input preparation only).  The float64
+oracle runs only in the CPU-baseline leg, on a bounded sample of the same workload.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import sparse_attention_backward_amd as sab  # noqa: E402
+import workloads as W  # noqa: E402
+
+METRIC = "selected/dense attention-backward TFLOP/s and % of bf16 MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work
+# ----------------------------------------------------------------------------
+
+def attended_pairs(w: W.Workload) -> int:
+    """(query row, key row) pairs the backward must touch, summed over query heads."""
+    if w.form == "selected":
+        return w.T1 * w.n1 * w.block_count * w.block_size
+    tot = 0
+    for s1, s2 in zip(w.seqlens_q, w.seqlens_kv):
+        tot += s1 * (s1 + 1) // 2 if w.causal else s1 * s2
+    return tot * w.n1
+
+
+def flops_per_pair(w: W.Workload, gemms=("S", "dP", "dV", "dQ", "dK")) -> int:
+    dqk, dv = w.d_qk + w.d_rope, w.d_v
+    width = {"S": dqk, "dP": dv, "dV": dv, "dQ": dqk, "dK": dqk}
+    return 2 * sum(width[g] for g in gemms)
+
+
+# kernel -> the GEMMs it performs (for its roofline point)
+KERNEL_GEMMS = {
+    "dense_kv_major": ("S", "dP", "dV", "dK"),
+    "dense_dq": ("S", "dP", "dQ"),
+    "selected_kv_major": ("S", "dP", "dV", "dK"),
+    "selected_dq": ("S", "dP", "dQ"),
+    "dense_fp32": ("S", "dP", "dV", "dQ", "dK", "S", "dP"),
+}
+
+
+# ----------------------------------------------------------------------------
+# input preparation (GPU, fp32 torch; not timed)
+# ----------------------------------------------------------------------------
+
+def _cat(a, b):
+    return a if b is None else torch.cat([a, b], dim=-1)
+
+
+@torch.no_grad()
+def gpu_forward(w: W.Workload, x):
+    """O (workload dtype) and [T1, N1, 8] fp32 softmax max / sum of the forward."""
+    dev = x["query"].device
+    T1 = w.T1
+    O = torch.zeros((T1, w.n1, w.d_v), device=dev, dtype=torch.float32)
+    m = torch.full((T1, w.n1), -math.inf, device=dev)
+    l = torch.zeros((T1, w.n1), device=dev)
+    G = w.G
+    if w.form == "dense":
+        Q = _cat(x["query"], x["query_rope"]).float()
+        K = _cat(x["key"], x["key_rope"]).float()
+        V = x["value"].float()
+        cq, ck = w.cu_q, w.cu_kv
+        for b in range(w.batch):
+            qs, qe, ks, ke = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+            if qe == qs or ke == ks:
+                continue
+            Qb = Q[qs:qe].transpose(0, 1).contiguous()                                # [N1, S1, D]
+            Kb = K[ks:ke].repeat_interleave(G, dim=1).transpose(0, 1).contiguous()   # [N1, S2, D]
+            Vb = V[ks:ke].repeat_interleave(G, dim=1).transpose(0, 1).contiguous()
+            S = torch.bmm(Qb, Kb.transpose(1, 2).contiguous()) * w.scale
+            if w.causal:
+                mask = torch.ones(qe - qs, ke - ks, dtype=torch.bool, device=dev).triu(1)
+                S.masked_fill_(mask, -math.inf)
+            mb = S.amax(dim=-1)
+            P = torch.exp(S - mb[..., None])
+            lb = P.sum(-1)
+            O[qs:qe] = torch.bmm(P / lb[..., None], Vb).transpose(0, 1)
+            m[qs:qe] = mb.transpose(0, 1)
+            l[qs:qe] = lb.transpose(0, 1)
+            del S, P
+    else:
+        Q, K, V = x["query"], x["key"], x["value"]
+        n = w.block_count * w.block_size
+        ar = torch.arange(w.block_size, device=dev)
+        chunk = max(1, int(1.5e8 // (w.n2 * n * (w.d_qk + w.d_v))))
+        cq, ck = w.cu_q, w.cu_kv
+        for b in range(w.batch):
+            qs, qe, ks = int(cq[b]), int(cq[b + 1]), int(ck[b])
+            for t0 in range(qs, qe, chunk):
+                t1 = min(qe, t0 + chunk)
+                ids = x["topk"][t0:t1].long()                                           # [C, N2, cnt]
+                rows = (ks + ids[..., None] * w.block_size + ar).reshape(t1 - t0, w.n2, n)
+                hh = torch.arange(w.n2, device=dev)[None, :, None].expand_as(rows)
+                Ks = K[rows, hh].float()                                                 # [C, N2, n, D]
+                Vs = V[rows, hh].float()
+                Qg = Q[t0:t1].float().reshape(t1 - t0, w.n2, G, w.d_qk)
+                S = torch.matmul(Qg, Ks.transpose(-1, -2).contiguous()) * w.scale       # [C, N2, G, n]
+                mb = S.amax(-1)
+                P = torch.exp(S - mb[..., None])
+                lb = P.sum(-1)
+                O[t0:t1] = torch.matmul(P / lb[..., None], Vs).reshape(t1 - t0, w.n1, w.d_v)
+                m[t0:t1] = mb.reshape(t1 - t0, w.n1)
+                l[t0:t1] = lb.reshape(t1 - t0, w.n1)
+                del Ks, Vs, S, P
+    smax = m[..., None].expand(T1, w.n1, 8).contiguous()
+    ssum = l[..., None].expand(T1, w.n1, 8).contiguous()
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return O.to(dt), smax, ssum
+
+
+# ----------------------------------------------------------------------------
+# timed run
+# ----------------------------------------------------------------------------
+
+def run_workload(w: W.Workload, steps: int, warmup: int, deterministic=False):
+    dev = torch.device("cuda", 0)
+    x = W.make_inputs(w, device=dev, backend="torch")
+    o, smax, ssum = gpu_forward(w, x)
+    if w.form == "dense":
+        prob = sab.Problem.dense(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, causal=w.causal,
+                                 d_rope=w.d_rope, dtype=w.dtype, deterministic=deterministic)
+        outs = [torch.empty_like(x["query"]), torch.empty_like(x["query_rope"]) if w.d_rope else None,
+                torch.empty_like(x["key"]), torch.empty_like(x["key_rope"]) if w.d_rope else None,
+                torch.empty_like(x["value"])]
+    else:
+        prob = sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size,
+                                    w.block_count, deterministic=deterministic)
+        outs = [torch.empty_like(x["query"]), torch.empty_like(x["key"]), torch.empty_like(x["value"])]
+    ws = torch.empty(max(1, sab.attn_bwd_workspace_size(prob)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if w.form == "dense":
+            sab.attn_bwd_dense_varlen(prob, x["query"], x["query_rope"], x["key"], x["key_rope"], x["value"], o,
+                                      x["dy"], smax, ssum, *outs, ws, stream=stream)
+        else:
+            sab.attn_bwd_selected(prob, x["query"], x["key"], x["value"], o, x["dy"], smax, ssum, x["topk"],
+                                  *outs, ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    sab.attn_bwd_profile_reset()
+    sab.attn_bwd_profiling(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    sab.attn_bwd_profiling(False)
+    ms = start.elapsed_time(end) / steps
+    kernels = sab.attn_bwd_profile_read()
+    return x, ms, kernels
+
+
+def roofline_for(w: W.Workload, kernels: dict):
+    name = max(kernels, key=lambda k: kernels[k][0])
+    tot_ms, n = kernels[name]
+    avg_ms = tot_ms / max(n, 1)
+    pairs = attended_pairs(w)
+    gemms = KERNEL_GEMMS.get(name)
+    if gemms is None:  # non-GEMM kernel: report bytes against HBM
+        return {"kernel": name, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": None, "traffic": None, "avg_ms": avg_ms}
+    fl = pairs * flops_per_pair(w, gemms)
+    achieved = fl / (avg_ms * 1e-3) / 1e12
+    if w.dtype == "fp32":
+        return {"kernel": name, "bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": None, "avg_ms": avg_ms,
+                "flop_per_launch": fl}
+    return {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "avg_ms": avg_ms, "flop_per_launch": fl}
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample of the same workload
+# ----------------------------------------------------------------------------
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max(n) if n else os.cpu_count()
+    except Exception:
+        return os.cpu_count()
+
+
+def cpu_baseline(w: W.Workload, x, budget_s=12.0):
+    import oracle as O
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    G = w.G
+    done_flops, done_units, elapsed = 0, [], 0.0
+    if w.form == "dense":
+        # units: (sequence, KV head) groups, shortest sequence first
+        order = sorted(range(w.batch), key=lambda b: w.seqlens_q[b])
+        for b in order:
+            qs, qe, ks, ke = (int(w.cu_q[b]), int(w.cu_q[b + 1]), int(w.cu_kv[b]), int(w.cu_kv[b + 1]))
+            for kvh in range(w.n2):
+                hs = slice(kvh * G, (kvh + 1) * G)
+                sub = lambda t, h: None if t is None else f64(t[qs:qe, h])  # noqa: E731
+                args = (sub(x["query"], hs), f64(x["key"][ks:ke, kvh:kvh + 1]), f64(x["value"][ks:ke, kvh:kvh + 1]),
+                        sub(x["dy"], hs), np.array([0, qe - qs]), np.array([0, ke - ks]), G, 1, w.scale, w.causal,
+                        sub(x["query_rope"], hs), None if x["key_rope"] is None else f64(x["key_rope"][ks:ke, kvh:kvh + 1]))
+                t0 = time.perf_counter()
+                O.backward_dense(*args)
+                elapsed += time.perf_counter() - t0
+                s1, s2 = qe - qs, ke - ks
+                pairs = (s1 * (s1 + 1) // 2 if w.causal else s1 * s2) * G
+                done_flops += pairs * flops_per_pair(w)
+                done_units.append(f"seq{b}/kvhead{kvh}")
+                if elapsed >= budget_s:
+                    break
+            if elapsed >= budget_s:
+                break
+        sample = f"{len(done_units)} of {w.batch * w.n2} (sequence, KV-head group) units ({done_units[0]}..{done_units[-1]})"
+    else:
+        b = 0
+        qs, qe, ks, ke = (int(w.cu_q[b]), int(w.cu_q[b + 1]), int(w.cu_kv[b]), int(w.cu_kv[b + 1]))
+        Kc, Vc = f64(x["key"][ks:ke]), f64(x["value"][ks:ke])
+        ntok, step_t = 0, 16
+        while elapsed < budget_s and qs + ntok < qe:
+            t0, t1 = qs + ntok, min(qe, qs + ntok + step_t)
+            a = time.perf_counter()
+            O.backward_selected(f64(x["query"][t0:t1]), Kc, Vc, f64(x["dy"][t0:t1]), x["topk"][t0:t1].cpu().numpy(),
+                                np.array([0, t1 - t0]), np.array([0, ke - ks]), w.n1, w.n2, w.scale, w.block_size)
+            elapsed += time.perf_counter() - a
+            ntok += t1 - t0
+        done_flops = ntok * w.n1 * w.block_count * w.block_size * flops_per_pair(w)
+        sample = f"first {ntok} query tokens of sequence 0 (all heads)"
+    return {"value": done_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": sample, "seconds": round(elapsed, 2), "host_cpus": os.cpu_count()}
+
+
+# ----------------------------------------------------------------------------
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="workload number 1..5 (default 2: dense bf16)")
+    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary selected-attention measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+
+    w = W.config(args.workload)
+    x, ms, kernels = run_workload(w, args.steps, args.warmup, args.deterministic)
+    total_flops = attended_pairs(w) * flops_per_pair(w)
+    value = total_flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "form": w.form, "seqlens": list(w.seqlens_q), "n1": w.n1, "n2": w.n2,
+                   "d_qk": w.d_qk, "d_rope": w.d_rope, "d_v": w.d_v, "causal": w.causal,
+                   "block_size": w.block_size, "block_count": w.block_count, "index_dist": w.index_dist,
+                   "deterministic": bool(args.deterministic), "algorithmic_tflop_per_step": total_flops / 1e12},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline_for(w, kernels),
+        "kernels_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in kernels.items()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, x)
+    del x
+    torch.cuda.empty_cache()
+    if not args.no_extra and args.workload == 2:
+        w3 = W.config(3)
+        x3, ms3, k3 = run_workload(w3, max(3, args.steps // 2), 2)
+        v3 = attended_pairs(w3) * flops_per_pair(w3) / (ms3 * 1e-3) / 1e12
+        line["extra"] = {"workload": w3.name, "tflops": round(v3, 3), "ms_per_step": round(ms3, 3),
+                         "pct_bf16_peak": round(100 * v3 / PEAK_BF16_TFLOPS, 2),
+                         "kernels_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in k3.items()}}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -136,6 +136,18 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p,
 attn_status_t attn_bwd_check_index_flag(const attn_bwd_problem_t* p, const void* workspace,
                                         int32_t* raised, void* hip_stream);
 
+/* Per-kernel timing, a measurement aid (off by default).  While enabled, every kernel
+ * the library launches is bracketed by two HIP events on the caller's stream; no
+ * synchronisation is added to the launches.  attn_bwd_profile_read synchronises on the
+ * recorded events, folds them into per-kernel totals, and returns entry `index`
+ * (0-based, in first-seen order): the kernel's name (static storage), total elapsed
+ * milliseconds and number of launches; ATTN_ERR_INVALID when `index` is past the last
+ * entry.  attn_bwd_profile_reset clears the totals.  Not thread-safe with respect to
+ * concurrent calls that launch work. */
+attn_status_t attn_bwd_profiling(int32_t enable);
+attn_status_t attn_bwd_profile_reset(void);
+attn_status_t attn_bwd_profile_read(int32_t index, const char** name, double* total_ms, int64_t* launches);
+
 /* Short English text for a status code (static storage). */
 const char* attn_bwd_status_string(attn_status_t s);
 

@@ -24,6 +24,7 @@ __all__ = [
     "AttnError", "Problem", "LIB_PATH", "lib",
     "attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_selected",
     "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version",
+    "attn_bwd_profiling", "attn_bwd_profile_reset", "attn_bwd_profile_read",
     "dense_backward", "selected_backward", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,7 +35,8 @@ ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
 ATTN_OP_DENSE, ATTN_OP_SELECTED = 0, 1
 
 EXPORTED_SYMBOLS = ("attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_selected",
-                    "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version")
+                    "attn_bwd_check_index_flag", "attn_bwd_profiling", "attn_bwd_profile_reset",
+                    "attn_bwd_profile_read", "attn_bwd_status_string", "attn_bwd_version")
 
 
 class attn_bwd_problem_t(ctypes.Structure):
@@ -64,6 +66,12 @@ def _load():
     L.attn_bwd_selected.restype = c_int32
     L.attn_bwd_check_index_flag.argtypes = [P, c_void_p, POINTER(c_int32), c_void_p]
     L.attn_bwd_check_index_flag.restype = c_int32
+    L.attn_bwd_profiling.argtypes = [c_int32]
+    L.attn_bwd_profiling.restype = c_int32
+    L.attn_bwd_profile_reset.argtypes = []
+    L.attn_bwd_profile_reset.restype = c_int32
+    L.attn_bwd_profile_read.argtypes = [c_int32, POINTER(c_char_p), POINTER(c_double), POINTER(c_int64)]
+    L.attn_bwd_profile_read.restype = c_int32
     L.attn_bwd_status_string.argtypes = [c_int32]
     L.attn_bwd_status_string.restype = c_char_p
     L.attn_bwd_version.argtypes = []
@@ -71,13 +79,27 @@ def _load():
     return L
 
 
-lib = _load()
+_LIB = None
+
+
+def _L():
+    """The loaded library (loaded on first use; ImportError when it is missing)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):  # module attribute `lib`, loaded on first access
+    if name == "lib":
+        return _L()
+    raise AttributeError(name)
 
 
 class AttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = int(status)
-        super().__init__(f"{where}: {lib.attn_bwd_status_string(self.status).decode()} (status {self.status})")
+        super().__init__(f"{where}: {_L().attn_bwd_status_string(self.status).decode()} (status {self.status})")
 
 
 def _check(st, where):
@@ -140,23 +162,23 @@ def _stream(stream):
 # ---- the C functions, same names ----------------------------------------------
 
 def attn_bwd_status_string(status: int) -> str:
-    return lib.attn_bwd_status_string(int(status)).decode()
+    return _L().attn_bwd_status_string(int(status)).decode()
 
 
 def attn_bwd_version() -> str:
-    return lib.attn_bwd_version().decode()
+    return _L().attn_bwd_version().decode()
 
 
 def attn_bwd_workspace_size(problem: Problem) -> int:
     n = c_uint64(0)
-    _check(lib.attn_bwd_workspace_size(problem.ref, ctypes.byref(n)), "attn_bwd_workspace_size")
+    _check(_L().attn_bwd_workspace_size(problem.ref, ctypes.byref(n)), "attn_bwd_workspace_size")
     return int(n.value)
 
 
 def attn_bwd_dense_varlen(problem, q, q_rope, k, k_rope, v, out, dy, softmax_max, softmax_sum,
                           dq, dq_rope, dk, dk_rope, dv, workspace, workspace_bytes=None, stream=None):
     wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
-    st = lib.attn_bwd_dense_varlen(problem.ref, _ptr(q), _ptr(q_rope), _ptr(k), _ptr(k_rope), _ptr(v), _ptr(out),
+    st = _L().attn_bwd_dense_varlen(problem.ref, _ptr(q), _ptr(q_rope), _ptr(k), _ptr(k_rope), _ptr(v), _ptr(out),
                                    _ptr(dy), _ptr(softmax_max), _ptr(softmax_sum), _ptr(dq), _ptr(dq_rope), _ptr(dk),
                                    _ptr(dk_rope), _ptr(dv), _ptr(workspace), wb, _stream(stream))
     _check(st, "attn_bwd_dense_varlen")
@@ -165,7 +187,7 @@ def attn_bwd_dense_varlen(problem, q, q_rope, k, k_rope, v, out, dy, softmax_max
 def attn_bwd_selected(problem, q, k, v, out, dy, softmax_max, softmax_sum, topk_indices, dq, dk, dv,
                       workspace, workspace_bytes=None, stream=None):
     wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
-    st = lib.attn_bwd_selected(problem.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dy), _ptr(softmax_max),
+    st = _L().attn_bwd_selected(problem.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dy), _ptr(softmax_max),
                                _ptr(softmax_sum), _ptr(topk_indices), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                wb, _stream(stream))
     _check(st, "attn_bwd_selected")
@@ -173,9 +195,30 @@ def attn_bwd_selected(problem, q, k, v, out, dy, softmax_max, softmax_sum, topk_
 
 def attn_bwd_check_index_flag(problem, workspace, stream=None) -> bool:
     r = c_int32(0)
-    _check(lib.attn_bwd_check_index_flag(problem.ref, _ptr(workspace), ctypes.byref(r), _stream(stream)),
+    _check(_L().attn_bwd_check_index_flag(problem.ref, _ptr(workspace), ctypes.byref(r), _stream(stream)),
            "attn_bwd_check_index_flag")
     return bool(r.value)
+
+
+def attn_bwd_profiling(enable: bool) -> None:
+    _check(_L().attn_bwd_profiling(int(bool(enable))), "attn_bwd_profiling")
+
+
+def attn_bwd_profile_reset() -> None:
+    _check(_L().attn_bwd_profile_reset(), "attn_bwd_profile_reset")
+
+
+def attn_bwd_profile_read() -> dict:
+    """All per-kernel totals: {name: (total_ms, launches)} (synchronises on the events)."""
+    out, i = {}, 0
+    while True:
+        name, ms, n = c_char_p(), c_double(), c_int64()
+        st = _L().attn_bwd_profile_read(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n))
+        if st == ATTN_ERR_INVALID:
+            return out
+        _check(st, "attn_bwd_profile_read")
+        out[name.value.decode()] = (ms.value, n.value)
+        i += 1
 
 
 # ---- allocation helpers (torch owns the memory) ----------------------------------

@@ -225,6 +225,46 @@ std::vector<uint8_t> pack_tables(const attn_bwd_problem_t* p, const Plan& pl) {
   return t;
 }
 
+// ---- optional per-kernel timing (attn_bwd_profiling) ------------------------------
+struct ProfRec { const char* name; hipEvent_t a, b; };
+struct ProfTotal { const char* name; double ms; int64_t n; };
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_pending;
+std::vector<ProfTotal> g_prof_totals;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Run one launcher; while profiling is on, bracket it with events on the stream.
+template <typename F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  if (!g_prof_on) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    a = prof_event();
+    b = prof_event();
+  }
+  if (!a || !b) return launch();
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  const hipError_t e2 = hipEventRecord(b, s);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_pending.push_back({name, a, b});
+  return e != hipSuccess ? e : e2;
+}
+
 bool misaligned(const void* ptr) { return ptr && (reinterpret_cast<uintptr_t>(ptr) & 15u); }
 
 template <typename T>
@@ -288,7 +328,7 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, 
   pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
   pa.lse2 = at<float>(workspace, pl.off_lse2); pa.drow = at<float>(workspace, pl.off_drow);
   pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = p->dtype == ATTN_BF16;
-  if (launch_preprocess(pa, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (timed("row_stats", s, [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
 
   DenseArgs a{};
   a.q = q; a.q_rope = q_rope; a.k = k; a.k_rope = k_rope; a.v = v; a.dy = dy;
@@ -306,8 +346,11 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, 
   a.scale = (float)p->scale;
   a.scale_log2e = (float)(p->scale * 1.4426950408889634);
   a.causal = p->causal;
-  const hipError_t e = p->dtype == ATTN_BF16 ? launch_dense_bf16(a, s) : launch_dense_fp32(a, s);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  if (p->dtype == ATTN_FP32)
+    return timed("dense_fp32", s, [&] { return launch_dense_fp32(a, s); }) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  if (timed("dense_kv_major", s, [&] { return launch_dense_kv_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (timed("dense_dq", s, [&] { return launch_dense_dq_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
 }
 
 attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, const void* k, const void* v,
@@ -336,7 +379,7 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
   pa.lse2 = at<float>(workspace, pl.off_lse2); pa.drow = at<float>(workspace, pl.off_drow);
   pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = 1;
-  if (launch_preprocess(pa, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (timed("row_stats", s, [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
 
   SelArgs a{};
   a.q = q; a.k = k; a.v = v; a.dy = dy; a.lse2 = pa.lse2; a.drow = pa.drow; a.topk = topk_indices;
@@ -355,9 +398,9 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   a.list = at<int32_t>(workspace, pl.off_list);
   a.sort_scratch = at<int32_t>(workspace, pl.off_scratch);
   a.flag = at<int32_t>(workspace, pl.off_flag);
-  if (launch_selected_index(a, s) != hipSuccess) return ATTN_ERR_HIP;
-  if (launch_selected_dq(a, 0, s) != hipSuccess) return ATTN_ERR_HIP;
-  if (launch_selected_dkdv(a, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (timed("selected_index", s, [&] { return launch_selected_index(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (timed("selected_dq", s, [&] { return launch_selected_dq(a, 0, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (timed("selected_kv_major", s, [&] { return launch_selected_dkdv(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
@@ -375,6 +418,45 @@ attn_status_t attn_bwd_check_index_flag(const attn_bwd_problem_t* p, const void*
       hipStreamSynchronize(s) != hipSuccess)
     return ATTN_ERR_HIP;
   *raised = h ? 1 : 0;
+  return ATTN_OK;
+}
+
+attn_status_t attn_bwd_profiling(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = enable != 0;
+  return ATTN_OK;
+}
+
+attn_status_t attn_bwd_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_pending) {
+    (void)hipEventSynchronize(r.b);
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_pending.clear();
+  g_prof_totals.clear();
+  return ATTN_OK;
+}
+
+attn_status_t attn_bwd_profile_read(int32_t index, const char** name, double* total_ms, int64_t* launches) {
+  if (!name || !total_ms || !launches) return ATTN_ERR_NULLPTR;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return ATTN_ERR_HIP;
+    auto it = std::find_if(g_prof_totals.begin(), g_prof_totals.end(),
+                           [&](const ProfTotal& t) { return std::strcmp(t.name, r.name) == 0; });
+    if (it == g_prof_totals.end()) g_prof_totals.push_back({r.name, (double)ms, 1});
+    else { it->ms += ms; it->n += 1; }
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_pending.clear();
+  if (index < 0 || index >= (int32_t)g_prof_totals.size()) return ATTN_ERR_INVALID;
+  *name = g_prof_totals[index].name;
+  *total_ms = g_prof_totals[index].ms;
+  *launches = g_prof_totals[index].n;
   return ATTN_OK;
 }
 

@@ -286,11 +286,13 @@ QArgs from_dense(const DenseArgs& a) {
 
 }  // namespace
 
-hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s);
-
 hipError_t launch_dense_bf16(const DenseArgs& a, hipStream_t s) {
   hipError_t e = launch_dense_kv_bf16(a, s);
   if (e != hipSuccess) return e;
+  return launch_dense_dq_bf16(a, s);
+}
+
+hipError_t launch_dense_dq_bf16(const DenseArgs& a, hipStream_t s) {
   if (a.n_q_tiles == 0) return hipSuccess;
   const QArgs k = from_dense(a);
   const dim3 grid(a.n_q_tiles, a.n1);

@@ -43,6 +43,7 @@ constexpr int kDenseTile = 64;  // query and key tile length of the bf16 dense k
 bool dense_bf16_supported(int d_qk_total, int d_v);
 hipError_t launch_dense_bf16(const DenseArgs& a, hipStream_t s);     // KV-major dK/dV, then query-major dQ
 hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s);  // KV-major dK/dV only
+hipError_t launch_dense_dq_bf16(const DenseArgs& a, hipStream_t s);  // query-major dQ only
 constexpr int kDenseTileF32 = 64;
 hipError_t launch_dense_fp32(const DenseArgs& a, hipStream_t s);
 
