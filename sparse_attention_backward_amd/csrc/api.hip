@@ -41,6 +41,7 @@ struct Plan {
   size_t off_cu_q = 0, off_cu_kv = 0, off_tab1 = 0, off_tab2 = 0, table_bytes = 0;
   size_t off_lse2 = 0, off_drow = 0;
   size_t off_counts = 0, off_offsets = 0, off_cursor = 0, off_list = 0, off_scratch = 0, off_flag = 0;
+  size_t off_dq_part = 0;
   size_t total = 0;
 };
 
@@ -149,6 +150,7 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     pl.off_list = o;    o = align_up(o + 4 * (size_t)pl.entries);
     pl.off_scratch = o; o = align_up(o + 8 * (size_t)pl.entries);
     pl.off_flag = o;    o = align_up(o + 4);
+    pl.off_dq_part = o; o = align_up(o + 2 * (size_t)pl.entries * pl.G * p->d_qk);
   }
   pl.total = o;
   return ATTN_OK;
@@ -398,9 +400,11 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   a.list = at<int32_t>(workspace, pl.off_list);
   a.sort_scratch = at<int32_t>(workspace, pl.off_scratch);
   a.flag = at<int32_t>(workspace, pl.off_flag);
+  a.dq_part = at<void>(workspace, pl.off_dq_part);
   if (timed("selected_index", s, [&] { return launch_selected_index(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
-  if (timed("selected_dq", s, [&] { return launch_selected_dq(a, 0, s); }) != hipSuccess) return ATTN_ERR_HIP;
   if (timed("selected_kv_major", s, [&] { return launch_selected_dkdv(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (timed("selected_dq_reduce", s, [&] { return launch_selected_dq_reduce(a, s); }) != hipSuccess)
+    return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 

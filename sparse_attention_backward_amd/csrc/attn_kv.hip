@@ -1,24 +1,28 @@
-// KV-major backward: dK and dV, accumulated in registers (bf16 MFMA, fp32 accumulation).
+// KV-major backward on bf16 MFMA with fp32 accumulation.
 //
 // Page "aclnnFlashAttentionUnpaddingScoreGradV3", Formula section (dV = P^T dY,
 // dK = dS^T Q / sqrt(d), dkRope = dS^T qRope / sqrt(d)) and page
 // "NsaSelectedAttentionGrad", formula section (the same products over the gathered
-// selectedKey / selectedValue rows).
+// selectedKey / selectedValue rows, plus dQ = dS K / sqrt(d)).
 //
 // One workgroup (4 waves) owns a set of key rows and streams query rows past them in
-// tiles of 64 rows:
+// steps of 64 rows:
 //   dense:    the key rows are one 64-row tile of a sequence for one KV head; the query
 //             rows are the tiles of each of the G query heads of that KV head, from the
-//             diagonal tile on when causal.
+//             diagonal tile on when causal.  dK and dV only (dQ has its own kernel).
 //   selected: the key rows are one selected block (block_size rows) of one sequence and
 //             KV head; the query rows are the G heads of the tokens whose topk rows name
-//             the block, read from the inverted index (ascending token order, so the
-//             summation order, and hence the result, is fixed).
-// Wave w holds key tiles {w, w+4, ...} (16 keys each) of K and V in registers as MFMA B
-// operands.  Per 64-row step: S = Q K^T and dP = dY V^T (A operands from LDS),
-// P = exp2(S*scale*log2e - lse2), dS = P (dP - drow), then dV += P^T dY and dK += dS^T Q
-// with the P / dS C tiles reused directly as A operands and dY / Q read column-wise
-// from LDS with ds_read_b64_tr_b16.  No atomics: every key row is owned by one workgroup.
+//             the block, read from the inverted index in ascending token order.  Besides
+//             dK and dV the workgroup writes, for every (token, slot) it serves, the
+//             block's share of dQ -- dS_block K_block, rounded to bf16 -- into a partial
+//             buffer that dq_reduce_kernel sums over the slots in a fixed order.
+// Wave w holds key tiles {w, w+4} (16 keys each) of K and V as MFMA B operands (dense:
+// in registers; selected: in LDS, where the K block also feeds the dQ product).  Per step: S = Q K^T and dP = dY V^T (A operands from LDS),
+// P = exp2(S*scale*log2e - lse2), dS = P (dP - drow); dV += P^T dY and dK += dS^T Q with
+// the P / dS C tiles reused directly as A operands and dY / Q read column-wise from LDS
+// with ds_read_b64_tr_b16; selected: dS^T goes to LDS and dQ^T = K^T dS^T is formed with
+// both operands read column-wise.  The next step's rows are fetched into registers
+// while the current step computes.  No atomics: every output row has one owner.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,6 +39,7 @@ struct KvArgs {
   const uint16_t* v; const uint16_t* dy;
   const float* lse2; const float* drow;
   uint16_t* dk; uint16_t* dk_rope; uint16_t* dv;
+  uint16_t* dq_part;                           // selected: [T1, N2, cnt, G, d_qk] bf16
   const int64_t* cu_q; const int64_t* cu_kv;
   const int32_t* tiles;                        // dense: (sequence, key tile)
   const int32_t* blkoff;                       // selected: blocks before each sequence
@@ -45,13 +50,22 @@ struct KvArgs {
 };
 
 template <int DQK, int DV, int NKT, bool SEL>
-__global__ __launch_bounds__(256) void kv_major_kernel(KvArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL ? 1 : 2, SEL ? 1 : 2)))
+void kv_major_kernel(KvArgs a) {
   constexpr int QST = DQK + kPad, YST = DV + kPad;
   constexpr int KS = DQK / 32, VS = DV / 32, NQ = DQK / 16, NV = DV / 16;
   constexpr int QCH = DQK / 8, YCH = DV / 8;  // 16-byte chunks per row
+  constexpr int KEYS = 64 * NKT;
+  constexpr int KST = DQK + kPad;             // selected: K block rows in LDS
+  constexpr int DST = kRows + kPad;           // selected: dS^T [key][row]
+  constexpr int NQW = NQ / 4;                 // selected: dQ dim tiles per wave
   __shared__ __attribute__((aligned(16))) uint16_t Qs[kRows * QST];
   __shared__ __attribute__((aligned(16))) uint16_t Ys[kRows * YST];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[SEL ? KEYS * KST : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Vsl[KEYS * (DV + kPad)];
+  __shared__ __attribute__((aligned(16))) uint16_t dSt[SEL ? KEYS * DST : 8];
   __shared__ float lse_s[kRows], drow_s[kRows];
+  __shared__ int ent_s[kRows];                // selected: list value of each row's token, or -1
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4, jj = l16 >> 2, qq = l16 & 3;
@@ -87,7 +101,11 @@ __global__ __launch_bounds__(256) void kv_major_kernel(KvArgs a) {
   }
 
   // ---- resident keys: B operands of S = Q K^T and dP = dY V^T ---------------------
-  bf16x8 Kf[NKT][KS], Vf[NKT][VS];
+  // K: dense in registers, selected in LDS (the K block is also the A operand of dQ^T);
+  // V: in LDS (keeps the dense kernel within 256 registers: two waves per SIMD).
+  constexpr int NKR = SEL ? 1 : NKT;
+  constexpr int KSR = SEL ? 1 : KS;
+  bf16x8 Kf[NKR][KSR];
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt) {
     const int key = 16 * (kt * 4 + w) + l16;
@@ -98,16 +116,24 @@ __global__ __launch_bounds__(256) void kv_major_kernel(KvArgs a) {
       const int d = 32 * s + 8 * g;
       uint4 x = make_uint4(0, 0, 0, 0);
       if (valid) x = ldg16(d < a.d_main ? a.k + kr * a.d_main + d : a.k_rope + kr * a.d_rope + (d - a.d_main));
-      Kf[kt][s] = __builtin_bit_cast(bf16x8, x);
+      if constexpr (SEL) sts16(&Ks[key * KST + d], x);
+      else Kf[kt][s] = __builtin_bit_cast(bf16x8, x);
     }
 #pragma unroll
     for (int s = 0; s < VS; ++s) {
       const int d = 32 * s + 8 * g;
       uint4 x = make_uint4(0, 0, 0, 0);
       if (valid) x = ldg16(a.v + kr * a.d_v + d);
-      Vf[kt][s] = __builtin_bit_cast(bf16x8, x);
+      sts16(&Vsl[key * (DV + kPad) + d], x);
     }
   }
+  auto kfrag = [&](int kt, int s) -> bf16x8 {
+    if constexpr (SEL) return lds_read_b128(&Ks[(16 * (kt * 4 + w) + l16) * KST + 32 * s + 8 * g]);
+    else return Kf[kt][s];
+  };
+  auto vfrag = [&](int kt, int s) -> bf16x8 {
+    return lds_read_b128(&Vsl[(16 * (kt * 4 + w) + l16) * (DV + kPad) + 32 * s + 8 * g]);
+  };
 
   f32x4 dK[NKT][NQ], dV[NKT][NV];
 #pragma unroll
@@ -119,76 +145,133 @@ __global__ __launch_bounds__(256) void kv_major_kernel(KvArgs a) {
   }
 
   const int nsteps = SEL ? (e_end - e_begin + TPS - 1) / TPS : a.G * (nqt - qt0);
-  for (int st = 0; st < nsteps; ++st) {
-    int hg = 0, qt = 0, ebase = 0;
-    if constexpr (SEL) {
-      ebase = e_begin + st * TPS;
-    } else {
-      hg = st / (nqt - qt0);
-      qt = qt0 + (st - hg * (nqt - qt0));
-    }
-    // query row r of this step -> (token, head) or invalid
-    auto row_of = [&](int r, int64_t& t, int& h) -> bool {
-      if constexpr (SEL) {
-        const int slot = r / a.G;
-        const int e = ebase + slot;
-        h = kvh * a.G + (r - slot * a.G);
-        if (slot >= TPS || e >= e_end) { t = 0; return false; }
-        t = a.list[e] / a.cnt;
-        return true;
-      } else {
-        h = kvh * a.G + hg;
-        t = qs + qt * kRows + r;
-        return qt * kRows + r < S1;
-      }
-    };
 
-    __syncthreads();  // previous step finished reading Qs / Ys
-    for (int idx = tid; idx < kRows * QCH; idx += 256) {
-      const int r = idx / QCH, d = 8 * (idx - r * QCH);
-      int64_t t; int h;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (row_of(r, t, h)) {
-        const int64_t qr = t * a.n1 + h;
-        x = ldg16(d < a.d_main ? a.q + qr * a.d_main + d : a.q_rope + qr * a.d_rope + (d - a.d_main));
-      }
-      sts16(&Qs[r * QST + d], x);
+  // Row loads: thread tid serves row r = tid / 4 of a step and its 16-byte chunks
+  // c = tid % 4 + 4k, so each row needs one (token, head) lookup per thread.  In the
+  // selected form the token comes from the inverted index; that list entry is loaded one
+  // step ahead so the Q / dY loads of a step never wait on it.
+  constexpr int QPT = QCH / 4, YPT = YCH / 4;
+  const int my_r = tid >> 2, my_c = tid & 3;
+  auto list_entry = [&](int st) -> int {  // selected: list value of row my_r at step st, or -1
+    const int slot = my_r / a.G;
+    const int e = e_begin + st * TPS + slot;
+    return (slot < TPS && e < e_end) ? a.list[e] : -1;
+  };
+  uint4 pq[QPT], py[YPT];
+  float plse = INFINITY, pdrow = 0.f;
+  int pent = -1, ent_ahead = -1;
+  auto prefetch = [&](int st, int ent) {
+    int64_t t = 0;
+    int h = 0;
+    bool ok;
+    if constexpr (SEL) {
+      h = kvh * a.G + (my_r - (my_r / a.G) * a.G);
+      ok = ent >= 0;
+      if (ok) t = ent / a.cnt;
+      pent = ent;
+    } else {
+      const int hg = st / (nqt - qt0);
+      const int qt = qt0 + (st - hg * (nqt - qt0));
+      h = kvh * a.G + hg;
+      t = qs + qt * kRows + my_r;
+      ok = qt * kRows + my_r < S1;
     }
-    for (int idx = tid; idx < kRows * YCH; idx += 256) {
-      const int r = idx / YCH, d = 8 * (idx - r * YCH);
-      int64_t t; int h;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (row_of(r, t, h)) x = ldg16(a.dy + (t * a.n1 + h) * a.d_v + d);
-      sts16(&Ys[r * YST + d], x);
+    const int64_t qr = t * a.n1 + h;
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int d = 8 * (my_c + 4 * k);
+      pq[k] = make_uint4(0, 0, 0, 0);
+      if (ok) pq[k] = ldg16(d < a.d_main ? a.q + qr * a.d_main + d : a.q_rope + qr * a.d_rope + (d - a.d_main));
     }
-    if (tid < kRows) {
-      int64_t t; int h;
-      const bool ok = row_of(tid, t, h);
-      lse_s[tid] = ok ? a.lse2[t * a.n1 + h] : INFINITY;
-      drow_s[tid] = ok ? a.drow[t * a.n1 + h] : 0.f;
+#pragma unroll
+    for (int k = 0; k < YPT; ++k) {
+      py[k] = make_uint4(0, 0, 0, 0);
+      if (ok) py[k] = ldg16(a.dy + qr * a.d_v + 8 * (my_c + 4 * k));
+    }
+    if (my_c == 0) {
+      plse = ok ? a.lse2[qr] : INFINITY;
+      pdrow = ok ? a.drow[qr] : 0.f;
+    }
+  };
+
+  if (nsteps > 0) {
+    if constexpr (SEL) {
+      prefetch(0, list_entry(0));
+      ent_ahead = nsteps > 1 ? list_entry(1) : -1;
+    } else {
+      prefetch(0, -1);
+    }
+  }
+  for (int st = 0; st < nsteps; ++st) {
+    __syncthreads();  // every wave is done with the previous step's LDS tiles
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) sts16(&Qs[my_r * QST + 8 * (my_c + 4 * k)], pq[k]);
+#pragma unroll
+    for (int k = 0; k < YPT; ++k) sts16(&Ys[my_r * YST + 8 * (my_c + 4 * k)], py[k]);
+    if (my_c == 0) {
+      lse_s[my_r] = plse;
+      drow_s[my_r] = pdrow;
+      if constexpr (SEL) ent_s[my_r] = pent;
     }
     __syncthreads();
+    if constexpr (SEL) {
+      if (st + 1 < nsteps) {
+        const int ent = ent_ahead;
+        ent_ahead = st + 2 < nsteps ? list_entry(st + 2) : -1;
+        prefetch(st + 1, ent);
+      }
+    } else {
+      if (st + 1 < nsteps) prefetch(st + 1, -1);
+    }
 
-    // S = Q K^T, dP = dY V^T for the wave's key tiles (C: lane = key, 4 rows)
+    // S = Q K^T, dP = dY V^T for the wave's key tiles (C: lane = key, 4 rows).
+    // Items i = (k-step gi, row tile rt) with gi < KS for S and KS <= gi for dP; the A
+    // fragment of item i + PD1 is read from LDS while item i's MFMAs issue.
+    constexpr int NI1 = 4 * (KS + VS), PD1 = SEL ? 6 : 4;
     f32x4 S[4][NKT], D[4][NKT];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) { S[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f}; D[rt][kt] = S[rt][kt]; }
+    auto a1 = [&](int i) -> bf16x8 {
+      const int gi = i >> 2, rt = i & 3;
+      return gi < KS ? lds_read_b128(&Qs[(16 * rt + l16) * QST + 32 * gi + 8 * g])
+                     : lds_read_b128(&Ys[(16 * rt + l16) * YST + 32 * (gi - KS) + 8 * g]);
+    };
+    auto b1 = [&](int gi, int kt) -> bf16x8 { return gi < KS ? kfrag(kt, gi) : vfrag(kt, gi - KS); };
+    bf16x8 ring1[PD1], bcur[NKT], bnext[NKT];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 x = lds_read_b128(&Qs[(16 * rt + l16) * QST + 32 * s + 8 * g]);
+    for (int i = 0; i < PD1; ++i) ring1[i] = a1(i);
+    // B fragments from LDS (selected K, and V) are read one k-step ahead; the dense K
+    // fragments are used straight from registers.
+    constexpr int G0 = SEL ? 0 : KS;  // first k-step whose B fragment comes from LDS
+    if (G0 < KS + VS) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) S[rt][kt] = mfma_16x16x32(x, Kf[kt][s], S[rt][kt]);
+      for (int kt = 0; kt < NKT; ++kt) bcur[kt] = b1(G0, kt);
+    }
+#pragma unroll
+    for (int i = 0; i < NI1; ++i) {
+      const int gi = i >> 2, rt = i & 3;
+      if (rt == 0 && gi >= G0 && gi + 1 < KS + VS) {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) bnext[kt] = b1(gi + 1, kt);
       }
+      const bf16x8 x = ring1[i % PD1];
+      if (i + PD1 < NI1) ring1[i % PD1] = a1(i + PD1);
 #pragma unroll
-      for (int s = 0; s < VS; ++s) {
-        const bf16x8 x = lds_read_b128(&Ys[(16 * rt + l16) * YST + 32 * s + 8 * g]);
+      for (int kt = 0; kt < NKT; ++kt) {
+        const bf16x8 bk = gi < G0 ? kfrag(kt, gi < KS ? gi : 0) : bcur[kt];
+        if (gi < KS) S[rt][kt] = mfma_16x16x32(x, bk, S[rt][kt]);
+        else D[rt][kt] = mfma_16x16x32(x, bk, D[rt][kt]);
+      }
+      if (rt == 3 && gi >= G0) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) D[rt][kt] = mfma_16x16x32(x, Vf[kt][s], D[rt][kt]);
+        for (int kt = 0; kt < NKT; ++kt) bcur[kt] = bnext[kt];
       }
     }
     // P and dS in place
+    int qt = 0;
+    if constexpr (!SEL) { const int hg = st / (nqt - qt0); qt = qt0 + (st - hg * (nqt - qt0)); }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
@@ -197,37 +280,101 @@ __global__ __launch_bounds__(256) void kv_major_kernel(KvArgs a) {
         const float lse = lse_s[r], dr = drow_s[r];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
+          const int key = 16 * (kt * 4 + w) + l16;
           float p = __builtin_amdgcn_exp2f(S[rt][kt][i] * a.scale_log2e - lse);
-          if constexpr (!SEL) {
-            if (a.causal && kt0 * kRows + 16 * (kt * 4 + w) + l16 > qt * kRows + r) p = 0.f;
+          if constexpr (SEL) {
+            if (key >= nk) p = 0.f;
+          } else {
+            if (a.causal && kt0 * kRows + key > qt * kRows + r) p = 0.f;
           }
           D[rt][kt][i] = p * (D[rt][kt][i] - dr);
           S[rt][kt][i] = p;
         }
       }
     }
-    // dV += P^T dY, dK += dS^T Q over the two 32-row halves of the step
+    if constexpr (SEL) {
+      // dS^T [key][row] for the dQ product (4 consecutive rows per lane: one 8-byte store)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pa[NKT], da[NKT];
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          *reinterpret_cast<i16x4*>(&dSt[(16 * (kt * 4 + w) + l16) * DST + 16 * rt + 4 * g]) = pack4(D[rt][kt]);
+    }
+    // dV += P^T dY, dK += dS^T Q over the two 32-row halves of the step.  Items
+    // i = (half ks, output tile j): j < NV feeds dV from dY, else dK from Q; the column
+    // fragments (two transposed reads each) run PD2 items ahead of the MFMAs.
+    bf16x8 pa[2][NKT], da[2][NKT];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
-        pa[kt] = pack8(S[2 * ks][kt], S[2 * ks + 1][kt]);
-        da[kt] = pack8(D[2 * ks][kt], D[2 * ks + 1][kt]);
+        pa[ks][kt] = pack8(S[2 * ks][kt], S[2 * ks + 1][kt]);
+        da[ks][kt] = pack8(D[2 * ks][kt], D[2 * ks + 1][kt]);
       }
+    constexpr int NJ = NV + NQ, NI2 = 2 * NJ, PD2 = SEL ? 6 : 4;
+    auto b2 = [&](int i) -> bf16x8 {
+      const int ks = i / NJ, j = i - (i / NJ) * NJ;
+      const uint16_t* p = j < NV ? &Ys[(32 * ks + 4 * g + jj) * YST + 16 * j + 4 * qq]
+                                 : &Qs[(32 * ks + 4 * g + jj) * QST + 16 * (j - NV) + 4 * qq];
+      const int st16 = j < NV ? 16 * YST : 16 * QST;
+      return join8(lds_read_tr16(p), lds_read_tr16(p + st16));
+    };
+    bf16x8 ring2[PD2];
 #pragma unroll
-      for (int nt = 0; nt < NV; ++nt) {
-        const uint16_t* p = &Ys[(32 * ks + 4 * g + jj) * YST + 16 * nt + 4 * qq];
-        const bf16x8 bv = join8(lds_read_tr16(p), lds_read_tr16(p + 16 * YST));
+    for (int i = 0; i < PD2; ++i) ring2[i] = b2(i);
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) dV[kt][nt] = mfma_16x16x32(pa[kt], bv, dV[kt][nt]);
+    for (int i = 0; i < NI2; ++i) {
+      const int ks = i / NJ, j = i - (i / NJ) * NJ;
+      const bf16x8 bv = ring2[i % PD2];
+      if (i + PD2 < NI2) ring2[i % PD2] = b2(i + PD2);
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        if (j < NV) dV[kt][j] = mfma_16x16x32(pa[ks][kt], bv, dV[kt][j]);
+        else dK[kt][j - NV] = mfma_16x16x32(da[ks][kt], bv, dK[kt][j - NV]);
       }
+    }
+    if constexpr (SEL) {
+      __syncthreads();  // dS^T complete
+      // dQ^T (dims x rows) = K^T dS^T over the block's keys; wave w takes NQW dim tiles
+      f32x4 acc[NQW][4];
 #pragma unroll
-      for (int nt = 0; nt < NQ; ++nt) {
-        const uint16_t* p = &Qs[(32 * ks + 4 * g + jj) * QST + 16 * nt + 4 * qq];
-        const bf16x8 bq = join8(lds_read_tr16(p), lds_read_tr16(p + 16 * QST));
+      for (int dt = 0; dt < NQW; ++dt)
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) dK[kt][nt] = mfma_16x16x32(da[kt], bq, dK[kt][nt]);
+        for (int rt = 0; rt < 4; ++rt) acc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      auto ld3 = [&](int ks, bf16x8* bs_, bf16x8* ak) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const uint16_t* p = &dSt[(32 * ks + 8 * g + jj) * DST + 16 * rt + 4 * qq];
+          bs_[rt] = join8(lds_read_tr16(p), lds_read_tr16(p + 4 * DST));
+        }
+#pragma unroll
+        for (int dt = 0; dt < NQW; ++dt) {
+          const uint16_t* p = &Ks[(32 * ks + 8 * g + jj) * KST + 16 * (w * NQW + dt) + 4 * qq];
+          ak[dt] = join8(lds_read_tr16(p), lds_read_tr16(p + 4 * KST));
+        }
+      };
+      bf16x8 bs3[2][4], ak3[2][NQW];
+      ld3(0, bs3[0], ak3[0]);
+#pragma unroll
+      for (int ks = 0; ks < KEYS / 32; ++ks) {
+        if (ks + 1 < KEYS / 32) ld3(ks + 1, bs3[(ks + 1) & 1], ak3[(ks + 1) & 1]);
+#pragma unroll
+        for (int dt = 0; dt < NQW; ++dt)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) acc[dt][rt] = mfma_16x16x32(ak3[ks & 1][dt], bs3[ks & 1][rt], acc[dt][rt]);
+      }
+      // C tile: lane holds row 16rt + l16, dims 16(w*NQW+dt) + 4g .. +3 -> one 8-byte store
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int r = 16 * rt + l16;
+        const int ent = ent_s[r];
+        if (ent >= 0) {
+          const int64_t t = ent / a.cnt, sl = ent - t * a.cnt;
+          uint16_t* dst = a.dq_part + (((t * a.n2 + kvh) * a.cnt + sl) * a.G + (r - (r / a.G) * a.G)) * DQK;
+#pragma unroll
+          for (int dt = 0; dt < NQW; ++dt)
+            *reinterpret_cast<i16x4*>(dst + 16 * (w * NQW + dt) + 4 * g) = pack4(acc[dt][rt]);
+        }
       }
     }
   }
@@ -258,6 +405,60 @@ __global__ __launch_bounds__(256) void kv_major_kernel(KvArgs a) {
       const int r = idx / YCH, d = 8 * (idx - r * YCH);
       const int key = kt * kRows + r;
       if (key < nk) sts16(a.dv + ((k0 + key) * a.n2 + kvh) * a.d_v + d, *reinterpret_cast<const uint4*>(&Ys[r * YST + d]));
+    }
+  }
+}
+
+// dQ[t, kvh*G + g, :] = scale * sum over slots of the bf16 partials, slots in order.
+// One wave per (token, KV head); each lane owns 8-element chunks of the G x DQK block.
+// A slot whose topk id is out of range was never written and is skipped.
+template <int DQK>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, uint16_t* dq, int64_t pairs, int n2,
+                                                        int n1, int G, int cnt, float scale, const int32_t* topk,
+                                                        const int64_t* cu_q, const int32_t* blkoff, int batch) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= pairs) return;
+  const int64_t t = pair / n2;
+  const int kvh = (int)(pair - t * n2);
+  const int b = seq_of(cu_q, batch, t);
+  const int nblk = blkoff[b + 1] - blkoff[b];
+  const int chunks = G * DQK / 8;
+  const uint16_t* src = part + pair * (int64_t)cnt * G * DQK;
+  uint16_t* out = dq + (t * n1 + (int64_t)kvh * G) * DQK;
+  for (int c0 = lane; c0 < chunks; c0 += 64 * 4) {
+    float acc[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[u][j] = 0.f;
+    for (int sl = 0; sl < cnt; ++sl) {
+      const int id = topk[pair * cnt + sl];
+      if (id < 0 || id >= nblk) continue;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < chunks) {
+          const uint4 x = ldg16(src + (int64_t)sl * G * DQK + 8 * c);
+          const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[u][2 * j] += __uint_as_float(xv[j] << 16);
+            acc[u][2 * j + 1] += __uint_as_float(xv[j] & 0xffff0000u);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 64 * u;
+      if (c < chunks) {
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = (uint32_t)f2bf(acc[u][2 * j] * scale) | ((uint32_t)f2bf(acc[u][2 * j + 1] * scale) << 16);
+        sts16(out + 8 * c, make_uint4(o[0], o[1], o[2], o[3]));
+      }
     }
   }
 }
@@ -303,7 +504,7 @@ hipError_t launch_selected_dkdv(const SelArgs& a, hipStream_t s) {
   KvArgs k{};
   k.q = (const uint16_t*)a.q; k.k = (const uint16_t*)a.k; k.v = (const uint16_t*)a.v;
   k.dy = (const uint16_t*)a.dy; k.lse2 = a.lse2; k.drow = a.drow;
-  k.dk = (uint16_t*)a.dk; k.dv = (uint16_t*)a.dv;
+  k.dk = (uint16_t*)a.dk; k.dv = (uint16_t*)a.dv; k.dq_part = (uint16_t*)a.dq_part;
   k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.blkoff = a.blkoff; k.offsets = a.offsets; k.list = a.list;
   k.batch = a.batch; k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;
   k.d_main = a.d_qk; k.d_rope = 0; k.d_v = a.d_v;
@@ -316,6 +517,21 @@ hipError_t launch_selected_dkdv(const SelArgs& a, hipStream_t s) {
   if (a.d_qk == 128 && a.d_v == 128)
     return two ? launch_kv<128, 128, 2, true>(k, grid, s) : launch_kv<128, 128, 1, true>(k, grid, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_selected_dq_reduce(const SelArgs& a, hipStream_t s) {
+  const int64_t pairs = a.T1 * a.n2;
+  if (pairs == 0) return hipSuccess;
+  const dim3 grid((unsigned)((pairs + 3) / 4)), block(256);
+  if (a.d_qk == 192)
+    hipLaunchKernelGGL(dq_reduce_kernel<192>, grid, block, 0, s, (const uint16_t*)a.dq_part, (uint16_t*)a.dq, pairs,
+                       a.n2, a.n1, a.G, a.cnt, a.scale, a.topk, a.cu_q, a.blkoff, a.batch);
+  else if (a.d_qk == 128)
+    hipLaunchKernelGGL(dq_reduce_kernel<128>, grid, block, 0, s, (const uint16_t*)a.dq_part, (uint16_t*)a.dq, pairs,
+                       a.n2, a.n1, a.G, a.cnt, a.scale, a.topk, a.cu_q, a.blkoff, a.batch);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace ab

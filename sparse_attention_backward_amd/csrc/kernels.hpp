@@ -68,12 +68,14 @@ struct SelArgs {
   int32_t* sort_scratch;    // [2 * T1 * n2 * cnt]
   int32_t* flag;            // [1] raised on an out-of-range topk id
   float* dkdv_acc;          // [T2, n2, d_qk + d_v] fp32, atomic mode only
+  void* dq_part;            // [T1, n2, cnt, G, d_qk] bf16: each block's share of dQ
   int64_t T2;
 };
 bool selected_supported(int d_qk, int d_v, int G, int bs);
 hipError_t launch_selected_index(const SelArgs& a, hipStream_t s);
 hipError_t launch_selected_dq(const SelArgs& a, int atomic_dkdv, hipStream_t s);
-hipError_t launch_selected_dkdv(const SelArgs& a, hipStream_t s);
+hipError_t launch_selected_dkdv(const SelArgs& a, hipStream_t s);       // dK, dV and dQ partials
+hipError_t launch_selected_dq_reduce(const SelArgs& a, hipStream_t s);  // dQ = scale * sum of partials
 
 // ---- misc --------------------------------------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);  // kernel, not a memset node
