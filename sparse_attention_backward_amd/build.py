@@ -19,8 +19,13 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattnbwd.so")
-SOURCES = ["api.hip", "preprocess.hip", "dense_fp32.hip", "attn_kv.hip", "attn_q.hip", "index.hip"]
+SOURCES = ["api.hip", "preprocess.hip", "dense_fp32.hip", "attn_kv.hip", "attn_kv_dense.hip", "attn_q.hip",
+           "index.hip"]
 ARCH = os.environ.get("ATTN_BWD_ARCH", "gfx950")
+# Per-source code generation options.  The dense KV-major kernel keeps every MFMA
+# accumulator in architectural VGPRs: the default heuristic puts the score tiles in AGPRs
+# and then shuttles the dK / dV accumulators between the two files every step.
+EXTRA = {"attn_kv_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc():
@@ -39,7 +44,7 @@ def flags():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -21,7 +21,8 @@
 // P = exp2(S*scale*log2e - lse2), dS = P (dP - drow); dV += P^T dY and dK += dS^T Q with
 // the P / dS C tiles reused directly as A operands and dY / Q read column-wise from LDS
 // with ds_read_b64_tr_b16; selected: dS^T goes to LDS and dQ^T = K^T dS^T is formed with
-// both operands read column-wise.  The next step's rows are fetched into registers
+// both operands read column-wise (same key permutation on both sides).  LDS tiles are
+// unpadded and XOR-swizzled (Swz) so that row and column reads are bank-conflict free.  The next step's rows are fetched into registers
 // while the current step computes.  No atomics: every output row has one owner.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -31,7 +32,6 @@ namespace ab {
 namespace {
 
 constexpr int kRows = 64;  // query rows per step
-constexpr int kPad = 8;    // LDS row padding (bf16 elements)
 
 struct KvArgs {
   const uint16_t* q; const uint16_t* q_rope;
@@ -50,20 +50,20 @@ struct KvArgs {
 };
 
 template <int DQK, int DV, int NKT, bool SEL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL ? 1 : 2, SEL ? 1 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL || DQK > 128 ? 1 : 2, SEL || DQK > 128 ? 1 : 2)))
 void kv_major_kernel(KvArgs a) {
-  constexpr int QST = DQK + kPad, YST = DV + kPad;
+  using SQ = Swz<DQK>;   // Qs, and the selected K block
+  using SY = Swz<DV>;    // Ys, V block
+  using SD = Swz<kRows>; // selected: dS^T [key][row]
   constexpr int KS = DQK / 32, VS = DV / 32, NQ = DQK / 16, NV = DV / 16;
   constexpr int QCH = DQK / 8, YCH = DV / 8;  // 16-byte chunks per row
   constexpr int KEYS = 64 * NKT;
-  constexpr int KST = DQK + kPad;             // selected: K block rows in LDS
-  constexpr int DST = kRows + kPad;           // selected: dS^T [key][row]
   constexpr int NQW = NQ / 4;                 // selected: dQ dim tiles per wave
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kRows * QST];
-  __shared__ __attribute__((aligned(16))) uint16_t Ys[kRows * YST];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[SEL ? KEYS * KST : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Vsl[KEYS * (DV + kPad)];
-  __shared__ __attribute__((aligned(16))) uint16_t dSt[SEL ? KEYS * DST : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kRows * DQK];
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[kRows * DV];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[SEL ? KEYS * DQK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Vsl[KEYS * DV];
+  __shared__ __attribute__((aligned(16))) uint16_t dSt[SEL ? KEYS * kRows : 8];
   __shared__ float lse_s[kRows], drow_s[kRows];
   __shared__ int ent_s[kRows];                // selected: list value of each row's token, or -1
 
@@ -116,7 +116,7 @@ void kv_major_kernel(KvArgs a) {
       const int d = 32 * s + 8 * g;
       uint4 x = make_uint4(0, 0, 0, 0);
       if (valid) x = ldg16(d < a.d_main ? a.k + kr * a.d_main + d : a.k_rope + kr * a.d_rope + (d - a.d_main));
-      if constexpr (SEL) sts16(&Ks[key * KST + d], x);
+      if constexpr (SEL) sts16(&Ks[SQ::off(key, d)], x);
       else Kf[kt][s] = __builtin_bit_cast(bf16x8, x);
     }
 #pragma unroll
@@ -124,15 +124,15 @@ void kv_major_kernel(KvArgs a) {
       const int d = 32 * s + 8 * g;
       uint4 x = make_uint4(0, 0, 0, 0);
       if (valid) x = ldg16(a.v + kr * a.d_v + d);
-      sts16(&Vsl[key * (DV + kPad) + d], x);
+      sts16(&Vsl[SY::off(key, d)], x);
     }
   }
   auto kfrag = [&](int kt, int s) -> bf16x8 {
-    if constexpr (SEL) return lds_read_b128(&Ks[(16 * (kt * 4 + w) + l16) * KST + 32 * s + 8 * g]);
+    if constexpr (SEL) return lds_read_b128(&Ks[SQ::off(16 * (kt * 4 + w) + l16, 32 * s + 8 * g)]);
     else return Kf[kt][s];
   };
   auto vfrag = [&](int kt, int s) -> bf16x8 {
-    return lds_read_b128(&Vsl[(16 * (kt * 4 + w) + l16) * (DV + kPad) + 32 * s + 8 * g]);
+    return lds_read_b128(&Vsl[SY::off(16 * (kt * 4 + w) + l16, 32 * s + 8 * g)]);
   };
 
   f32x4 dK[NKT][NQ], dV[NKT][NV];
@@ -205,9 +205,9 @@ void kv_major_kernel(KvArgs a) {
   for (int st = 0; st < nsteps; ++st) {
     __syncthreads();  // every wave is done with the previous step's LDS tiles
 #pragma unroll
-    for (int k = 0; k < QPT; ++k) sts16(&Qs[my_r * QST + 8 * (my_c + 4 * k)], pq[k]);
+    for (int k = 0; k < QPT; ++k) sts16(&Qs[SQ::off(my_r, 8 * (my_c + 4 * k))], pq[k]);
 #pragma unroll
-    for (int k = 0; k < YPT; ++k) sts16(&Ys[my_r * YST + 8 * (my_c + 4 * k)], py[k]);
+    for (int k = 0; k < YPT; ++k) sts16(&Ys[SY::off(my_r, 8 * (my_c + 4 * k))], py[k]);
     if (my_c == 0) {
       lse_s[my_r] = plse;
       drow_s[my_r] = pdrow;
@@ -235,8 +235,8 @@ void kv_major_kernel(KvArgs a) {
       for (int kt = 0; kt < NKT; ++kt) { S[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f}; D[rt][kt] = S[rt][kt]; }
     auto a1 = [&](int i) -> bf16x8 {
       const int gi = i >> 2, rt = i & 3;
-      return gi < KS ? lds_read_b128(&Qs[(16 * rt + l16) * QST + 32 * gi + 8 * g])
-                     : lds_read_b128(&Ys[(16 * rt + l16) * YST + 32 * (gi - KS) + 8 * g]);
+      return gi < KS ? lds_read_b128(&Qs[SQ::off(16 * rt + l16, 32 * gi + 8 * g)])
+                     : lds_read_b128(&Ys[SY::off(16 * rt + l16, 32 * (gi - KS) + 8 * g)]);
     };
     auto b1 = [&](int gi, int kt) -> bf16x8 { return gi < KS ? kfrag(kt, gi) : vfrag(kt, gi - KS); };
     bf16x8 ring1[PD1], bcur[NKT], bnext[NKT];
@@ -298,7 +298,7 @@ void kv_major_kernel(KvArgs a) {
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
-          *reinterpret_cast<i16x4*>(&dSt[(16 * (kt * 4 + w) + l16) * DST + 16 * rt + 4 * g]) = pack4(D[rt][kt]);
+          *reinterpret_cast<i16x4*>(&dSt[SD::off(16 * (kt * 4 + w) + l16, 16 * rt + 4 * g)]) = pack4(D[rt][kt]);
     }
     // dV += P^T dY, dK += dS^T Q over the two 32-row halves of the step.  Items
     // i = (half ks, output tile j): j < NV feeds dV from dY, else dK from Q; the column
@@ -314,10 +314,13 @@ void kv_major_kernel(KvArgs a) {
     constexpr int NJ = NV + NQ, NI2 = 2 * NJ, PD2 = SEL ? 6 : 4;
     auto b2 = [&](int i) -> bf16x8 {
       const int ks = i / NJ, j = i - (i / NJ) * NJ;
-      const uint16_t* p = j < NV ? &Ys[(32 * ks + 4 * g + jj) * YST + 16 * j + 4 * qq]
-                                 : &Qs[(32 * ks + 4 * g + jj) * QST + 16 * (j - NV) + 4 * qq];
-      const int st16 = j < NV ? 16 * YST : 16 * QST;
-      return join8(lds_read_tr16(p), lds_read_tr16(p + st16));
+      const int r = 32 * ks + 4 * g + jj;
+      if (j < NV) {
+        const int col = 16 * j + 4 * qq;
+        return join8(lds_read_tr16(&Ys[SY::off(r, col)]), lds_read_tr16(&Ys[SY::off(r + 16, col)]));
+      }
+      const int col = 16 * (j - NV) + 4 * qq;
+      return join8(lds_read_tr16(&Qs[SQ::off(r, col)]), lds_read_tr16(&Qs[SQ::off(r + 16, col)]));
     };
     bf16x8 ring2[PD2];
 #pragma unroll
@@ -344,13 +347,13 @@ void kv_major_kernel(KvArgs a) {
       auto ld3 = [&](int ks, bf16x8* bs_, bf16x8* ak) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          const uint16_t* p = &dSt[(32 * ks + 8 * g + jj) * DST + 16 * rt + 4 * qq];
-          bs_[rt] = join8(lds_read_tr16(p), lds_read_tr16(p + 4 * DST));
+          const int r = 32 * ks + 4 * g + jj, col = 16 * rt + 4 * qq;
+          bs_[rt] = join8(lds_read_tr16(&dSt[SD::off(r, col)]), lds_read_tr16(&dSt[SD::off(r + 16, col)]));
         }
 #pragma unroll
         for (int dt = 0; dt < NQW; ++dt) {
-          const uint16_t* p = &Ks[(32 * ks + 8 * g + jj) * KST + 16 * (w * NQW + dt) + 4 * qq];
-          ak[dt] = join8(lds_read_tr16(p), lds_read_tr16(p + 4 * KST));
+          const int r = 32 * ks + 4 * g + jj, col = 16 * (w * NQW + dt) + 4 * qq;
+          ak[dt] = join8(lds_read_tr16(&Ks[SQ::off(r, col)]), lds_read_tr16(&Ks[SQ::off(r + 16, col)]));
         }
       };
       bf16x8 bs3[2][4], ak3[2][NQW];
@@ -386,11 +389,11 @@ void kv_major_kernel(KvArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NQ; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Qs[(16 * w + 4 * g + i) * QST + 16 * nt + l16] = f2bf(dK[kt][nt][i] * a.scale);
+      for (int i = 0; i < 4; ++i) Qs[SQ::off(16 * w + 4 * g + i, 16 * nt + l16)] = f2bf(dK[kt][nt][i] * a.scale);
 #pragma unroll
     for (int nt = 0; nt < NV; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Ys[(16 * w + 4 * g + i) * YST + 16 * nt + l16] = f2bf(dV[kt][nt][i]);
+      for (int i = 0; i < 4; ++i) Ys[SY::off(16 * w + 4 * g + i, 16 * nt + l16)] = f2bf(dV[kt][nt][i]);
     __syncthreads();
     for (int idx = tid; idx < kRows * QCH; idx += 256) {
       const int r = idx / QCH, d = 8 * (idx - r * QCH);
@@ -398,13 +401,13 @@ void kv_major_kernel(KvArgs a) {
       if (key < nk) {
         const int64_t kr = (k0 + key) * a.n2 + kvh;
         uint16_t* dst = d < a.d_main ? a.dk + kr * a.d_main + d : a.dk_rope + kr * a.d_rope + (d - a.d_main);
-        sts16(dst, *reinterpret_cast<const uint4*>(&Qs[r * QST + d]));
+        sts16(dst, *reinterpret_cast<const uint4*>(&Qs[SQ::off(r, d)]));
       }
     }
     for (int idx = tid; idx < kRows * YCH; idx += 256) {
       const int r = idx / YCH, d = 8 * (idx - r * YCH);
       const int key = kt * kRows + r;
-      if (key < nk) sts16(a.dv + ((k0 + key) * a.n2 + kvh) * a.d_v + d, *reinterpret_cast<const uint4*>(&Ys[r * YST + d]));
+      if (key < nk) sts16(a.dv + ((k0 + key) * a.n2 + kvh) * a.d_v + d, *reinterpret_cast<const uint4*>(&Ys[SY::off(r, d)]));
     }
   }
 }
@@ -471,29 +474,6 @@ hipError_t launch_kv(const KvArgs& k, dim3 grid, hipStream_t s) {
 }
 
 }  // namespace
-
-bool dense_bf16_supported(int d_qk_total, int d_v) {
-  return (d_qk_total == 192 && d_v == 128) || (d_qk_total == 128 && d_v == 128) || (d_qk_total == 64 && d_v == 64);
-}
-
-hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) {
-  KvArgs k{};
-  k.q = (const uint16_t*)a.q; k.q_rope = (const uint16_t*)a.q_rope;
-  k.k = (const uint16_t*)a.k; k.k_rope = (const uint16_t*)a.k_rope;
-  k.v = (const uint16_t*)a.v; k.dy = (const uint16_t*)a.dy;
-  k.lse2 = a.lse2; k.drow = a.drow;
-  k.dk = (uint16_t*)a.dk; k.dk_rope = (uint16_t*)a.dk_rope; k.dv = (uint16_t*)a.dv;
-  k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.tiles = a.kv_tiles;
-  k.batch = a.batch; k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;
-  k.d_main = a.d_main; k.d_rope = a.d_rope; k.d_v = a.d_v;
-  k.causal = a.causal; k.scale = a.scale; k.scale_log2e = a.scale_log2e;
-  const dim3 grid(a.n_kv_tiles, a.n2);
-  const int dqk = a.d_main + a.d_rope;
-  if (dqk == 192 && a.d_v == 128) return launch_kv<192, 128, 1, false>(k, grid, s);
-  if (dqk == 128 && a.d_v == 128) return launch_kv<128, 128, 1, false>(k, grid, s);
-  if (dqk == 64 && a.d_v == 64) return launch_kv<64, 64, 1, false>(k, grid, s);
-  return hipErrorInvalidValue;
-}
 
 bool selected_supported(int d_qk, int d_v, int G, int bs) {
   return ((d_qk == 192 && d_v == 128) || (d_qk == 128 && d_v == 128)) && G >= 1 && G <= 16 && bs % 16 == 0 &&

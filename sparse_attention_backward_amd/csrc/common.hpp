@@ -79,6 +79,46 @@ __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast
 
 __device__ __forceinline__ void sts16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// Bank-conflict-free LDS tile of bf16 rows, C columns, no padding (64 banks x 4 B).
+// The 16-byte chunk c of row r is stored at chunk c ^ h(r).  h is chosen so that
+//   * a ds_read_b128 over 16 consecutive rows at one column chunk, and
+//   * a ds_read_b64_tr_b16 over 8 consecutive rows x 32 contiguous bytes
+// both touch 64 distinct banks.  A row of C/2 words starts at bank 32*(r&1) when
+// C/2 = 32 (mod 64) and at bank 0 when C/2 = 0 (mod 64); h makes up the rest.
+template <int C>
+struct Swz {
+  static_assert(C % 64 == 0, "swizzled rows hold a multiple of 64 bf16");
+  static constexpr int W = C / 2;
+  static_assert(W % 64 == 32 || (W % 64 == 0 && C % 128 == 0), "unsupported row length");
+  __device__ __forceinline__ static int h(int r) {
+    if constexpr (W % 64 == 32) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+    else return 2 * (r & 7) + ((r >> 3) & 1);
+  }
+  // element offset of (row r, column col); columns col..col+k stay contiguous while
+  // they lie in one 8-element chunk
+  __device__ __forceinline__ static int off(int r, int col) { return r * C + (((col >> 3) ^ h(r)) << 3) + (col & 7); }
+  // h touches the low HB bits of a chunk index only
+  static constexpr int HB = (W % 64 == 32) ? 3 : 4, M = 1 << HB;
+};
+
+// Addresses of the chunks STEP*k + part (k unrolled at compile time, part per lane) of
+// rows that share h: the XOR only changes the low HB bits, so the offset is a per-lane
+// table of M/STEP entries plus a compile-time multiple of M chunks.  Keeps swizzled
+// addressing to a few registers instead of one per access.
+template <int C, int STEP>
+struct SwzCursor {
+  static constexpr int M = Swz<C>::M, T = M / STEP;
+  static_assert(M % STEP == 0, "step must divide the swizzle period");
+  int lo[T];
+  __device__ __forceinline__ void init(int r, int part) {
+    const int hh = Swz<C>::h(r);
+#pragma unroll
+    for (int t = 0; t < T; ++t) lo[t] = ((STEP * t + part) ^ hh) << 3;
+  }
+  // element offset of chunk STEP*k + part within its row
+  __device__ __forceinline__ int off(int k) const { return (k / T) * (M * 8) + lo[k % T]; }
+};
+
 // Sequence of a packed row: largest b with cu[b] <= row (cu has B + 1 entries).
 __device__ __forceinline__ int seq_of(const int64_t* cu, int batch, int64_t row) {
   int lo = 0, hi = batch - 1;

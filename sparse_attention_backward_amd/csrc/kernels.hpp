@@ -73,7 +73,6 @@ struct SelArgs {
 };
 bool selected_supported(int d_qk, int d_v, int G, int bs);
 hipError_t launch_selected_index(const SelArgs& a, hipStream_t s);
-hipError_t launch_selected_dq(const SelArgs& a, int atomic_dkdv, hipStream_t s);
 hipError_t launch_selected_dkdv(const SelArgs& a, hipStream_t s);       // dK, dV and dQ partials
 hipError_t launch_selected_dq_reduce(const SelArgs& a, hipStream_t s);  // dQ = scale * sum of partials
 
