@@ -98,6 +98,14 @@ typedef struct {
                                      the query-major pass (non-deterministic; needs a larger
                                      workspace); 0 = inverted-index KV-major pass.
                                      Ignored (treated as 0) when deterministic = 1.          */
+  int32_t dense_dq_mode;          /* dense bf16 only (0 for every other problem): how dQ is
+                                     formed.  1 = the KV-major pass stores dS (bf16, 8 KiB per
+                                     64 x 64 (query tile, key tile) block and query head, in the
+                                     workspace) and dQ = scale * dS K is a plain product;
+                                     2 = dQ is recomputed query-major (S and dP formed again, no
+                                     dS storage); 0 = automatic: 1 while the dS storage is at
+                                     most 8 GiB, else 2.  Both give results within the same
+                                     tolerance and are deterministic.                          */
 } attn_bwd_problem_t;
 
 /* Validate `p` and return the workspace size in bytes for its execute call.

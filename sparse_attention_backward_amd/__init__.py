@@ -47,7 +47,7 @@ class attn_bwd_problem_t(ctypes.Structure):
         ("d_qk", c_int32), ("d_rope", c_int32), ("d_v", c_int32),
         ("scale", c_double), ("causal", c_int32),
         ("block_size", c_int32), ("block_count", c_int32),
-        ("deterministic", c_int32), ("dkdv_atomic", c_int32),
+        ("deterministic", c_int32), ("dkdv_atomic", c_int32), ("dense_dq_mode", c_int32),
     ]
 
 
@@ -111,7 +111,7 @@ class Problem:
     """attn_bwd_problem_t plus the host cu_seqlens arrays it points to (kept alive here)."""
 
     def __init__(self, op, dtype, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, d_rope=0, causal=False,
-                 block_size=0, block_count=0, deterministic=False, dkdv_atomic=False):
+                 block_size=0, block_count=0, deterministic=False, dkdv_atomic=False, dense_dq_mode=0):
         cu_q = [int(x) for x in cu_q]
         cu_kv = [int(x) for x in cu_kv]
         self.cu_q_arr = (c_int64 * len(cu_q))(*cu_q)
@@ -122,14 +122,17 @@ class Problem:
             cu_seqlens_kv=ctypes.cast(self.cu_kv_arr, POINTER(c_int64)),
             n1=n1, n2=n2, d_qk=d_qk, d_rope=d_rope, d_v=d_v, scale=float(scale), causal=int(bool(causal)),
             block_size=block_size, block_count=block_count,
-            deterministic=int(bool(deterministic)), dkdv_atomic=int(bool(dkdv_atomic)))
+            deterministic=int(bool(deterministic)), dkdv_atomic=int(bool(dkdv_atomic)),
+            dense_dq_mode=int(dense_dq_mode))
         self.T1, self.T2 = cu_q[-1], cu_kv[-1]
 
     @classmethod
     def dense(cls, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, causal=False, d_rope=0, dtype="bf16",
-              deterministic=False):
+              deterministic=False, dq_mode=0):
+        """dq_mode: 0 automatic, 1 stored dS, 2 recompute (field dense_dq_mode of the C struct)."""
         return cls(ATTN_OP_DENSE, {"bf16": ATTN_BF16, "fp32": ATTN_FP32, "fp16": ATTN_FP16}[dtype], cu_q, cu_kv,
-                   n1, n2, d_qk, d_v, scale, d_rope=d_rope, causal=causal, deterministic=deterministic)
+                   n1, n2, d_qk, d_v, scale, d_rope=d_rope, causal=causal, deterministic=deterministic,
+                   dense_dq_mode=dq_mode)
 
     @classmethod
     def selected(cls, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, block_size, block_count, deterministic=False,

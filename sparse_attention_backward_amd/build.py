@@ -19,13 +19,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattnbwd.so")
-SOURCES = ["api.hip", "preprocess.hip", "dense_fp32.hip", "attn_kv.hip", "attn_kv_dense.hip", "attn_q.hip",
-           "index.hip"]
+SOURCES = ["api.hip", "preprocess.hip", "dense_fp32.hip", "attn_kv.hip", "dense_kv.hip", "dense_dq.hip",
+           "attn_q.hip", "index.hip"]
 ARCH = os.environ.get("ATTN_BWD_ARCH", "gfx950")
-# Per-source code generation options.  The dense KV-major kernel keeps every MFMA
-# accumulator in architectural VGPRs: the default heuristic puts the score tiles in AGPRs
-# and then shuttles the dK / dV accumulators between the two files every step.
-EXTRA = {"attn_kv_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source code generation options.
+EXTRA = {}
 
 
 def hipcc():

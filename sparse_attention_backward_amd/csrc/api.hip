@@ -33,6 +33,8 @@ struct Plan {
   int64_t T1 = 0, T2 = 0;
   // dense schedule
   std::vector<int32_t> kv_tiles, q_tiles;
+  std::vector<int64_t> ds_base;
+  bool dense_ds = false;  // dQ from stored dS tiles (else recomputed)
   // selected
   std::vector<int32_t> blkoff;
   int nblk_total = 0;
@@ -42,8 +44,76 @@ struct Plan {
   size_t off_lse2 = 0, off_drow = 0;
   size_t off_counts = 0, off_offsets = 0, off_cursor = 0, off_list = 0, off_scratch = 0, off_flag = 0;
   size_t off_dq_part = 0;
+  size_t off_ds_base = 0, off_ds = 0;
   size_t total = 0;
 };
+
+constexpr int kXcds = 8;                          // workgroups are dealt to the XCDs round-robin
+constexpr uint64_t kDenseDsAutoMax = 8ull << 30;  // stored dS above this size: recompute instead
+
+// Dense schedule tables.
+//  * Key tiles (sequence, key tile, KV head): the tiles of one (sequence, KV head) read the
+//    same query rows, so each such group goes to one XCD (groups dealt to the least loaded
+//    XCD, largest first) and its tiles share that XCD's L2.  Within an XCD tiles run
+//    heaviest first.  Slot p of the launch belongs to XCD p % 8; slots an XCD does not
+//    need are idle (-1).  The dealing affects speed only, never results.
+//  * Query tiles (sequence, query tile), heaviest first.
+//  * ds_base: (query tile, key tile) blocks before each sequence (stored-dS layout).
+void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
+  const int B = pl.B;
+  const int64_t* cq = p->cu_seqlens_q;
+  const int64_t* ck = p->cu_seqlens_kv;
+  struct W { int64_t work; int32_t b, tile, kvh; };
+  std::vector<std::vector<W>> groups;  // per (sequence, KV head)
+  std::vector<int64_t> gwork;
+  std::vector<W> qv;
+  pl.ds_base.assign(B + 1, 0);
+  for (int b = 0; b < B; ++b) {
+    const int64_t S1 = cq[b + 1] - cq[b], S2 = ck[b + 1] - ck[b];
+    const int64_t nqt = (S1 + kDenseTile - 1) / kDenseTile, nkt = (S2 + kDenseTile - 1) / kDenseTile;
+    pl.ds_base[b + 1] = pl.ds_base[b] + (p->causal ? nqt * (nqt + 1) / 2 : nqt * nkt);
+    for (int h = 0; h < p->n2; ++h) {
+      std::vector<W> gl;
+      int64_t tot = 0;
+      for (int64_t t = 0; t < nkt; ++t) {
+        const int64_t work = (p->causal ? std::max<int64_t>(nqt - t, 0) : nqt) * pl.G;
+        gl.push_back({work, b, (int32_t)t, h});
+        tot += work;
+      }
+      if (!gl.empty()) { groups.push_back(std::move(gl)); gwork.push_back(tot); }
+    }
+    for (int64_t t = 0; t < nqt; ++t) qv.push_back({p->causal ? std::min(t + 1, nkt) : nkt, b, (int32_t)t, 0});
+  }
+  std::vector<size_t> order(groups.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return gwork[x] > gwork[y]; });
+  std::vector<std::vector<W>> bins(kXcds);
+  std::vector<int64_t> load(kXcds, 0);
+  for (size_t gi : order) {
+    const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[x] += gwork[gi];
+    bins[x].insert(bins[x].end(), groups[gi].begin(), groups[gi].end());
+  }
+  size_t rounds = 0;
+  for (auto& bin : bins) {
+    std::stable_sort(bin.begin(), bin.end(), [](const W& x, const W& y) { return x.work > y.work; });
+    rounds = std::max(rounds, bin.size());
+  }
+  for (size_t r = 0; r < rounds; ++r)
+    for (int x = 0; x < kXcds; ++x) {
+      if (r < bins[x].size()) {
+        const W& t = bins[x][r];
+        pl.kv_tiles.insert(pl.kv_tiles.end(), {t.b, t.tile, t.kvh});
+      } else {
+        pl.kv_tiles.insert(pl.kv_tiles.end(), {-1, 0, 0});
+      }
+    }
+  std::stable_sort(qv.begin(), qv.end(), [](const W& x, const W& y) { return x.work > y.work; });
+  for (auto& x : qv) { pl.q_tiles.push_back(x.b); pl.q_tiles.push_back(x.tile); }
+  const uint64_t ds_bytes = (uint64_t)pl.ds_base[B] * p->n1 * kDenseTile * kDenseTile * 2;
+  pl.dense_ds = p->dtype == ATTN_BF16 &&
+                (p->dense_dq_mode == 1 || (p->dense_dq_mode == 0 && ds_bytes <= kDenseDsAutoMax));
+}
 
 attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   if (!p) return ATTN_ERR_NULLPTR;
@@ -81,24 +151,12 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     const int dqk = p->d_qk + p->d_rope;
     if (p->dtype == ATTN_BF16 && !dense_bf16_supported(dqk, p->d_v)) return ATTN_ERR_UNSUPPORTED;
     if (p->dtype == ATTN_FP32 && (dqk > 256 || p->d_v > 256)) return ATTN_ERR_UNSUPPORTED;
-    // schedule: heaviest tiles first
-    struct W { int64_t work; int32_t b, tile; };
-    std::vector<W> kv, qv;
-    for (int b = 0; b < B; ++b) {
-      const int64_t S1 = cq[b + 1] - cq[b], S2 = ck[b + 1] - ck[b];
-      const int64_t nqt = (S1 + kDenseTile - 1) / kDenseTile, nkt = (S2 + kDenseTile - 1) / kDenseTile;
-      for (int64_t t = 0; t < nkt; ++t) kv.push_back({p->causal ? nqt - t : nqt, b, (int32_t)t});
-      for (int64_t t = 0; t < nqt; ++t) qv.push_back({p->causal ? t + 1 : nkt, b, (int32_t)t});
-    }
-    auto heavy_first = [](const W& x, const W& y) { return x.work > y.work; };
-    std::stable_sort(kv.begin(), kv.end(), heavy_first);
-    std::stable_sort(qv.begin(), qv.end(), heavy_first);
-    for (auto& x : kv) { pl.kv_tiles.push_back(x.b); pl.kv_tiles.push_back(x.tile); }
-    for (auto& x : qv) { pl.q_tiles.push_back(x.b); pl.q_tiles.push_back(x.tile); }
+    if (p->dense_dq_mode < 0 || p->dense_dq_mode > 2) return ATTN_ERR_INVALID;
+    plan_dense_schedule(p, pl);
   } else {
     if (p->dtype == ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
     if (p->dtype != ATTN_BF16) return ATTN_ERR_INVALID;
-    if (p->d_rope != 0 || p->causal != 0) return ATTN_ERR_INVALID;
+    if (p->d_rope != 0 || p->causal != 0 || p->dense_dq_mode != 0) return ATTN_ERR_INVALID;
     // D is 192 or 128 (K and V may differ); N1, N2 in 1..128; G in 1..32
     if ((p->d_qk != 128 && p->d_qk != 192) || (p->d_v != 128 && p->d_v != 192)) return ATTN_ERR_INVALID;
     if (p->n1 > 128 || p->n2 > 128 || pl.G > 32) return ATTN_ERR_INVALID;
@@ -133,6 +191,9 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     o += 4 * pl.kv_tiles.size();
     pl.off_tab2 = o;
     o += 4 * pl.q_tiles.size();
+    o = (o + 7) / 8 * 8;
+    pl.off_ds_base = o;
+    o += 8 * pl.ds_base.size();
   } else {
     o += 4 * pl.blkoff.size();
     pl.off_tab2 = o;
@@ -151,6 +212,10 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     pl.off_scratch = o; o = align_up(o + 8 * (size_t)pl.entries);
     pl.off_flag = o;    o = align_up(o + 4);
     pl.off_dq_part = o; o = align_up(o + 2 * (size_t)pl.entries * pl.G * p->d_qk);
+  }
+  if (p->op == ATTN_OP_DENSE && pl.dense_ds) {
+    pl.off_ds = o;
+    o = align_up(o + (size_t)pl.ds_base[pl.B] * p->n1 * kDenseTile * kDenseTile * 2);
   }
   pl.total = o;
   return ATTN_OK;
@@ -221,6 +286,7 @@ std::vector<uint8_t> pack_tables(const attn_bwd_problem_t* p, const Plan& pl) {
   if (p->op == ATTN_OP_DENSE) {
     if (!pl.kv_tiles.empty()) std::memcpy(t.data() + pl.off_tab1, pl.kv_tiles.data(), 4 * pl.kv_tiles.size());
     if (!pl.q_tiles.empty()) std::memcpy(t.data() + pl.off_tab2, pl.q_tiles.data(), 4 * pl.q_tiles.size());
+    std::memcpy(t.data() + pl.off_ds_base, pl.ds_base.data(), 8 * pl.ds_base.size());
   } else {
     std::memcpy(t.data() + pl.off_tab1, pl.blkoff.data(), 4 * pl.blkoff.size());
   }
@@ -340,7 +406,9 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, 
   a.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
   a.kv_tiles = at<const int32_t>(workspace, pl.off_tab1);
   a.q_tiles = at<const int32_t>(workspace, pl.off_tab2);
-  a.n_kv_tiles = (int)(pl.kv_tiles.size() / 2);
+  a.ds_base = at<const int64_t>(workspace, pl.off_ds_base);
+  a.ds = pl.dense_ds ? at<void>(workspace, pl.off_ds) : nullptr;
+  a.n_kv_tiles = (int)(pl.kv_tiles.size() / 3);
   a.n_q_tiles = (int)(pl.q_tiles.size() / 2);
   a.batch = pl.B; a.n1 = p->n1; a.n2 = p->n2; a.G = pl.G;
   a.T1 = pl.T1; a.T2 = pl.T2;
@@ -351,7 +419,11 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, 
   if (p->dtype == ATTN_FP32)
     return timed("dense_fp32", s, [&] { return launch_dense_fp32(a, s); }) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   if (timed("dense_kv_major", s, [&] { return launch_dense_kv_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
-  if (timed("dense_dq", s, [&] { return launch_dense_dq_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (pl.dense_ds) {
+    if (timed("dense_dq", s, [&] { return launch_dense_dq_from_ds(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  } else {
+    if (timed("dense_dq_recompute", s, [&] { return launch_dense_dq_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  }
   return ATTN_OK;
 }
 

@@ -179,12 +179,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-hipError_t launch_dense_bf16(const DenseArgs& a, hipStream_t s) {
-  hipError_t e = launch_dense_kv_bf16(a, s);
-  if (e != hipSuccess) return e;
-  return launch_dense_dq_bf16(a, s);
-}
-
 hipError_t launch_dense_dq_bf16(const DenseArgs& a, hipStream_t s) {
   if (a.n_q_tiles == 0) return hipSuccess;
   QArgs k{};

@@ -28,9 +28,11 @@ struct DenseArgs {
   const void* v;  const void* dy;
   const float* lse2; const float* drow;
   void* dq; void* dq_rope; void* dk; void* dk_rope; void* dv;
+  void* ds;                 // bf16 dS^T blocks [block][N1][64][64] (stored-dS mode), else null
   const int64_t* cu_q;      // [B+1]
   const int64_t* cu_kv;     // [B+1]
-  const int32_t* kv_tiles;  // [n_kv_tiles, 2] = (sequence, key tile), heaviest first
+  const int64_t* ds_base;   // [B+1] (query tile, key tile) blocks before each sequence
+  const int32_t* kv_tiles;  // [n_kv_tiles, 3] = (sequence, key tile, KV head), -1 = idle slot
   const int32_t* q_tiles;   // [n_q_tiles, 2]  = (sequence, query tile), heaviest first
   int n_kv_tiles, n_q_tiles;
   int batch, n1, n2, G;
@@ -41,9 +43,9 @@ struct DenseArgs {
 };
 constexpr int kDenseTile = 64;  // query and key tile length of the bf16 dense kernels
 bool dense_bf16_supported(int d_qk_total, int d_v);
-hipError_t launch_dense_bf16(const DenseArgs& a, hipStream_t s);     // KV-major dK/dV, then query-major dQ
-hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s);  // KV-major dK/dV only
-hipError_t launch_dense_dq_bf16(const DenseArgs& a, hipStream_t s);  // query-major dQ only
+hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s);     // KV-major dK, dV (+ dS when a.ds)
+hipError_t launch_dense_dq_from_ds(const DenseArgs& a, hipStream_t s);  // dQ = scale dS K from stored dS
+hipError_t launch_dense_dq_bf16(const DenseArgs& a, hipStream_t s);     // query-major dQ, recomputing S, dP
 constexpr int kDenseTileF32 = 64;
 hipError_t launch_dense_fp32(const DenseArgs& a, hipStream_t s);
 

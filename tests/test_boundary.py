@@ -180,3 +180,19 @@ def test_workspace_grows_with_the_problem():
     a = status_ws(selected())[1]
     b = status_ws(selected(cu_q=[0, 512, 1280], cu_kv=[0, 512, 1280]))[1]
     assert b > a
+
+
+def test_dense_dq_mode_field():
+    assert status_ws(dense(dq_mode=3))[0] == INVALID
+    assert status_ws(dense(dq_mode=-1))[0] == INVALID
+    st1, n1 = status_ws(dense(dq_mode=1))
+    st2, n2 = status_ws(dense(dq_mode=2))
+    st0, n0 = status_ws(dense())
+    assert st0 == st1 == st2 == OK
+    # stored dS: causal (query tile, key tile) blocks of the two sequences (lengths 100 and 64:
+    # 2 and 1 tiles of 64 -> 3 + 1 blocks), 8 heads, 8 KiB each
+    assert n1 - n2 == (3 + 1) * 8 * 64 * 64 * 2
+    assert n0 == n1  # small problems store dS
+    p = selected()
+    p.s.dense_dq_mode = 1
+    assert status_ws(p)[0] == INVALID

@@ -10,11 +10,11 @@ from helpers import (assert_close, check_against_oracle, f64, gpu_backward, orac
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, deterministic=None):
+def _run(w, deterministic=None, dq_mode=0):
     x = W.make_inputs(w)
     o, smax, ssum = oracle_forward(w, x)
-    print(f"[parity] {w.name} seqlens={w.seqlens_q}/{w.seqlens_kv} n1={w.n1} n2={w.n2}", flush=True)
-    got = gpu_backward(w, x, o, smax, ssum, deterministic=deterministic)
+    print(f"[parity] {w.name} seqlens={w.seqlens_q}/{w.seqlens_kv} n1={w.n1} n2={w.n2} dq_mode={dq_mode}", flush=True)
+    got = gpu_backward(w, x, o, smax, ssum, deterministic=deterministic, dq_mode=dq_mode)
     ref = oracle_backward(w, x)
     check_against_oracle(w, got, ref)
     return x, got, ref
@@ -24,19 +24,24 @@ def test_dense_fp32_config1():
     _run(W.config(1))
 
 
+# dq_mode 1: dQ from the dS tiles stored by the KV-major pass; 2: dQ recomputed query-major
+@pytest.mark.parametrize("dq_mode", [1, 2])
 @pytest.mark.parametrize("seqlens,n1,n2,d_qk,d_rope,d_v", [
     ((200, 130), 8, 2, 128, 64, 128),     # rope split, GQA G=4, ragged tails
     ((64, 1, 129), 4, 4, 128, 0, 128),    # no rope, G=1, a one-token sequence
     ((97,), 4, 1, 64, 0, 64),             # small head dim, G=4
+    ((300, 64), 16, 2, 128, 64, 128),     # G=8: two passes of four heads in the dQ product
+    ((190,), 6, 3, 128, 64, 128),         # G=2
 ])
-def test_dense_bf16_causal(seqlens, n1, n2, d_qk, d_rope, d_v):
-    _run(W.small_dense(seqlens=seqlens, n1=n1, n2=n2, d_qk=d_qk, d_rope=d_rope, d_v=d_v))
+def test_dense_bf16_causal(seqlens, n1, n2, d_qk, d_rope, d_v, dq_mode):
+    _run(W.small_dense(seqlens=seqlens, n1=n1, n2=n2, d_qk=d_qk, d_rope=d_rope, d_v=d_v), dq_mode=dq_mode)
 
 
-def test_dense_bf16_noncausal_unequal_lengths():
+@pytest.mark.parametrize("dq_mode", [1, 2])
+def test_dense_bf16_noncausal_unequal_lengths(dq_mode):
     w = W.small_dense(seqlens=(150,), n1=4, n2=2, d_qk=128, d_rope=64, d_v=128, causal=False)
-    w = w.with_(seqlens_q=(150, 0, 70), seqlens_kv=(77, 64, 200), name="dense-noncausal-unequal")
-    _run(w)
+    w = w.with_(seqlens_q=(150, 0, 70, 33), seqlens_kv=(77, 64, 200, 0), name="dense-noncausal-unequal")
+    _run(w, dq_mode=dq_mode)
 
 
 def test_dense_fp32_small_rope():
