@@ -149,7 +149,7 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
       for (int b = 0; b < B; ++b)
         if (cq[b + 1] - cq[b] != ck[b + 1] - ck[b]) return ATTN_ERR_INVALID;
     const int dqk = p->d_qk + p->d_rope;
-    if (p->dtype == ATTN_BF16 && !dense_bf16_supported(dqk, p->d_v)) return ATTN_ERR_UNSUPPORTED;
+    if (p->dtype == ATTN_BF16 && !dense_bf16_supported(p->d_qk, p->d_rope, p->d_v)) return ATTN_ERR_UNSUPPORTED;
     if (p->dtype == ATTN_FP32 && (dqk > 256 || p->d_v > 256)) return ATTN_ERR_UNSUPPORTED;
     if (p->dense_dq_mode < 0 || p->dense_dq_mode > 2) return ATTN_ERR_INVALID;
     plan_dense_schedule(p, pl);

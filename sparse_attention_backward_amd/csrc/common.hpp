@@ -30,6 +30,8 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -44,6 +46,25 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
 // Transposed 4 x bf16 read from LDS (see header comment).  `p` points into LDS.
 __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// Reads at an LDS byte address (an integer); a constant added to the address becomes the
+// instruction's immediate offset.
+__device__ __forceinline__ bf16x8 lds_b128_at(uint32_t addr) {
+  return *reinterpret_cast<const lds_bf16x8*>((uintptr_t)addr);
+}
+__device__ __forceinline__ f32x4 lds_f32x4_at(uint32_t addr) {
+  return *reinterpret_cast<const lds_f32x4*>((uintptr_t)addr);
+}
+__device__ __forceinline__ i16x4 lds_tr16_at(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>((uintptr_t)addr));
+}
+// Hides how a value was computed, so that the compiler keeps it as one base register and
+// folds the constants added to it into immediate offsets instead of re-associating the
+// sum into one register per constant.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
 }
 
 __device__ __forceinline__ bf16x8 join8(i16x4 lo, i16x4 hi) {
@@ -117,6 +138,29 @@ struct SwzCursor {
   }
   // element offset of chunk STEP*k + part within its row
   __device__ __forceinline__ int off(int k) const { return (k / T) * (M * 8) + lo[k % T]; }
+};
+
+// LDS tile of 64 rows of W 16-byte chunks (W = 8 or 16), row-major, filled by
+// global->LDS transfers that each move 1024 contiguous LDS bytes = RPI = 64 / W whole rows
+// (lane l: row l / W, slot l % W).  Chunk c of row r sits in slot c ^ swz(r); the lane that
+// fills a slot reads the matching chunk, so every transfer reads whole rows (full cache
+// lines).  swz makes both kinds of read conflict free:
+//   * 16 consecutive rows (16-aligned) at one chunk (ds_read_b128 of a 16-row A operand):
+//     the slots are distinct (W = 16), resp. distinct within each row parity (W = 8, where
+//     even and odd rows start 32 banks apart);
+//   * 8 consecutive rows (8-aligned) x chunks {2j, 2j + 1} (ds_read_b64_tr_b16): the 16
+//     (row, chunk) pairs land in distinct slots, resp. distinct within each row parity.
+template <int W>
+struct RowTile {
+  static_assert(W == 8 || W == 16, "rows of 128 or 256 bytes");
+  static constexpr int RB = 16 * W;        // bytes per row
+  static constexpr int RPI = 1024 / RB;    // rows per transfer instruction
+  static constexpr int BYTES = 64 * RB;
+  __device__ __forceinline__ static int swz(int r) {
+    if constexpr (W == 16) return 2 * (r & 7) + ((r >> 3) & 1);
+    else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  }
+  __device__ __forceinline__ static int off(int r, int c) { return r * RB + 16 * (c ^ swz(r)); }
 };
 
 // Sequence of a packed row: largest b with cu[b] <= row (cu has B + 1 entries).

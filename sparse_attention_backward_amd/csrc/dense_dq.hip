@@ -6,13 +6,14 @@
 // in the workspace; this kernel is then a plain product, with no recomputation of S or dP.
 //
 // One workgroup (4 waves) owns a 64-row query tile of HP query heads that share a KV head
-// (all G heads, in passes of HP).  Per key tile it stages the K tile and the HP dS^T blocks
-// in LDS (double buffered, global->LDS transfers one tile ahead) and accumulates
-// dQ += dS K.  The waves form a 2 x 2 grid: rows 32(w>>1) .. +31 and feature columns
-// (DQK/2)(w&1) .. of every head.  Both operands are read with ds_read_b64_tr_b16: the
-// contraction runs over keys, which are the rows of both staged tiles.  Keys are taken
-// in the order {4g + j, 16 + 4g + j} on both sides, which keeps the reads conflict free.
-// Fixed loop order, no atomics: deterministic.
+// (all G heads, in passes of HP).  Per key tile it stages the K tile (key and keyRope
+// parts) and the HP dS^T blocks in LDS (double buffered, global->LDS transfers one tile
+// ahead) and accumulates dQ += dS K.  The waves form a 2 x 2 grid: rows 32(w>>1) .. +31
+// and feature columns (DQK/2)(w&1) .. of every head.  Both operands are read with
+// ds_read_b64_tr_b16: the contraction runs over keys, which are the rows of both staged
+// tiles (RowTile layout: whole-row transfers, conflict-free column reads).  Keys are
+// taken in the order {4g + j, 16 + 4g + j} on both sides.  Fixed loop order, no atomics:
+// deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,8 +21,7 @@ namespace ab {
 
 namespace {
 
-constexpr int kT = 64;           // rows per query tile, keys per key tile
-constexpr int kCB = 1024 + 128;  // bytes per chunk column of a staged 64-row tile
+constexpr int kT = 64;  // rows per query tile, keys per key tile
 typedef __attribute__((address_space(3))) void lds_void;
 
 struct DqArgs {
@@ -31,7 +31,7 @@ struct DqArgs {
   const int64_t* cu_q; const int64_t* cu_kv;
   const int64_t* ds_base;       // [B + 1]
   const int32_t* tiles;         // [n][2] (sequence, query tile)
-  int n1, n2, G, d_main, d_rope;
+  int n1, n2, G;
   int causal;
   float scale;
 };
@@ -52,10 +52,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* lds) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
 }
 
-template <int MOFF, int OFF>
+template <int MOFF>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%3"
-               ::"v"(src), "s"(lds), "i"(MOFF), "i"(OFF) : "memory", "m0", "scc");
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(src), "s"(lds), "i"(MOFF) : "memory", "m0", "scc");
 }
 
 template <int N, typename F, int I = 0>
@@ -66,17 +66,37 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int DQK, int HP>
+// Per-lane addressing of one staged part (RowTile of W chunks, 64 key rows) for wave w:
+// transfer row / chunk (as in the KV-major kernel) and the transposed column reads
+// (keys 4g + jj (+16), chunk 2j + qq/2, half qq&1).
+template <int W>
+struct KeyPartLanes {
+  using T = RowTile<W>;
+  int row0;
+  uint32_t gchunk;
+  int colB[W / 2];
+  __device__ __forceinline__ void init(int w, int lane) {
+    const int l16 = lane & 15, g = lane >> 4, jj = l16 >> 2, qq = l16 & 3;
+    row0 = w * T::RPI + lane / W;
+    gchunk = 16u * (uint32_t)((lane % W) ^ T::swz(row0));
+#pragma unroll
+    for (int j = 0; j < W / 2; ++j) colB[j] = T::off(4 * g + jj, 2 * j + (qq >> 1)) + 8 * (qq & 1);
+  }
+};
+
+template <int DM, int DR, int HP>
 __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
-  constexpr int NQ = DQK / 16, NF = NQ / 2;   // feature tiles in total / per wave
-  constexpr int QCH = DQK / 8;                // 16-byte chunks per K row
-  constexpr int KLD = QCH / 4;                // K transfer instructions per wave
-  constexpr int DLD = 2 * HP;                 // dS transfer instructions per wave (8 chunks per block)
-  constexpr int KB = QCH * kCB, DB = 8 * kCB;
-  constexpr int SB = KB + HP * DB;            // one stage
+  constexpr int DQK = DM + DR;
+  constexpr int NQ = DQK / 16, NF = NQ / 2, NQM = DM / 16;  // feature tiles: all / per wave / key part
+  constexpr int WM = DM / 8, WR = DR > 0 ? DR / 8 : 8;
+  using TM = RowTile<WM>;
+  using TR = RowTile<WR>;
+  using TD = RowTile<8>;                                     // dS^T block: 64 keys x 64 rows
+  constexpr int OKM = 0, OKR = TM::BYTES, OD = OKR + (DR > 0 ? TR::BYTES : 0);
+  constexpr int SB = OD + HP * TD::BYTES;                    // one stage
   static_assert(2 * SB <= 160 * 1024, "two stages must fit in LDS");
-  static_assert(HP * (KB + 0) <= 2 * SB, "output tiles must fit");
-  __shared__ __attribute__((aligned(16))) char smem[2 * SB];
+  static_assert(HP * kT * DQK * 2 <= 2 * SB, "output tiles must fit");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * SB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -90,36 +110,70 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
   const int nkt = (S2 + kT - 1) / kT;
   const int nkt_run = a.causal ? min(qt + 1, nkt) : nkt;
   const int nvalid = min(kT, S1 - qt * kT);
-  const int qmain = a.d_main / 8;
   const int64_t blk0 = a.ds_base[b];
-
-  // per-lane LDS offset of a column read: keys 4g + jj (+16, +32 ks), chunk qq/2, half qq&1
-  const int colb = (qq >> 1) * kCB + 16 * (4 * g + jj) + 8 * (qq & 1);
-  const int kq = (qmain - w + 3) >> 2;  // K chunks k < kq come from `key`, the rest from keyRope
   const uint32_t smem_lds = lds_addr(smem);
+
+  KeyPartLanes<WM> pm;
+  KeyPartLanes<WR> pr;
+  KeyPartLanes<8> pd;
+  pm.init(w, lane);
+  if constexpr (DR > 0) pr.init(w, lane);
+  pd.init(w, lane);
+  // K column reads of this wave's feature tiles ft = fh NF + f, resolved now so that the
+  // step loop indexes only by compile-time f: [f][ks2][first / second read]
+  uint32_t kcol[NF][2][2];
+  auto tile_base = [&](auto ftc) -> int {  // compile-time feature tile
+    constexpr int ft = decltype(ftc)::value;
+    if constexpr (ft < NQM) return OKM + pm.colB[ft];
+    else return OKR + pr.colB[ft - NQM];
+  };
+  static_for<NF>([&](auto fc) {
+    constexpr int f = decltype(fc)::value;
+    constexpr int rb0 = f < NQM ? TM::RB : TR::RB, rb1 = NF + f < NQM ? TM::RB : TR::RB;
+    const int b0 = tile_base(std::integral_constant<int, f>{});
+    const int b1 = tile_base(std::integral_constant<int, NF + f>{});
+    const int base = fh ? b1 : b0, rb = fh ? rb1 : rb0;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      kcol[f][ks2][0] = base + ks2 * 32 * rb;
+      kcol[f][ks2][1] = base + ks2 * 32 * rb + 16 * rb;
+    }
+  });
+  // dS^T column reads of this wave's row tiles rt: rows (columns of the block) 16(2rh + rt)..
+  int dsA[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) dsA[rt] = TD::off(4 * g + jj, 2 * (2 * rh + rt) + (qq >> 1)) + 8 * (qq & 1);
+
+  const uint32_t rs_m = (uint32_t)a.n2 * DM * 2, rs_r = (uint32_t)a.n2 * DR * 2;
 
   for (int hp0 = 0; hp0 < a.G; hp0 += HP) {
     const int h0 = kvh * a.G + hp0;  // first query head of this pass
 
-    // issue(): K tile (chunks w + 4k, lane = key) and the HP dS^T blocks (chunks w, w + 4)
+    auto issue_part = [&](auto wtag, const auto& pl, const char* gtile, uint32_t rs, uint32_t lds_part, int nrows) {
+      constexpr int W = decltype(wtag)::value;
+      constexpr int RPI = RowTile<W>::RPI;
+      static_for<W / 4>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        const int r = min(pl.row0 + 4 * RPI * k, nrows - 1);
+        dma16<4096 * k>(gtile + __umul24((uint32_t)r, rs) + pl.gchunk, lds_part + w * 1024);
+      });
+    };
+    // issue(): the K tile (both parts) and the HP dS^T blocks of key tile kt
     auto issue = [&](int kt, int soff) {
       const int nk = min(kT, S2 - kt * kT);
-      const int64_t kr = (ks + (int64_t)kt * kT + min(lane, nk - 1)) * a.n2 + kvh;
-      const char* krow = reinterpret_cast<const char*>(a.k + kr * a.d_main) + 16 * w;
-      const char* rrow = reinterpret_cast<const char*>(a.k_rope + kr * a.d_rope) + 16 * (w - qmain);
-      const uint32_t kb = smem_lds + soff + w * kCB;
-      static_for<KLD>([&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        dma16<k * (4 * kCB - 64), 64 * k>(k < kq ? krow : rrow, kb);
-      });
+      const int64_t kr0 = (ks + (int64_t)kt * kT) * a.n2 + kvh;
+      const uint32_t stage = smem_lds + soff;
+      issue_part(std::integral_constant<int, WM>{}, pm, reinterpret_cast<const char*>(a.k + kr0 * DM), rs_m,
+                 stage + OKM, nk);
+      if constexpr (DR > 0)
+        issue_part(std::integral_constant<int, WR>{}, pr, reinterpret_cast<const char*>(a.k_rope + kr0 * DR), rs_r,
+                   stage + OKR, nk);
       const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt : (int64_t)qt * nkt + kt);
-      const char* drow = reinterpret_cast<const char*>(a.ds + ((blk * a.n1 + h0) * (kT * kT) + lane * kT)) + 16 * w;
+      const char* dblk = reinterpret_cast<const char*>(a.ds + (blk * a.n1 + h0) * (kT * kT));
       static_for<HP>([&](auto hc) {
         constexpr int hh = decltype(hc)::value;
-        const uint32_t db = smem_lds + soff + KB + hh * DB + w * kCB;
-        // chunks w and w + 4 of key row `lane` of head h0 + hh (block rows are 128 bytes)
-        dma16<0, 0>(drow + hh * (kT * kT * 2), db);
-        dma16<4 * kCB - 64, 64>(drow + hh * (kT * kT * 2), db);
+        issue_part(std::integral_constant<int, 8>{}, pd, dblk + hh * (kT * kT * 2), kT * 2,
+                   stage + OD + hh * TD::BYTES, kT);
       });
     };
 
@@ -131,29 +185,26 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) acc[hh][rt][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto colfrag = [&](const char* base, int chunk, int ks2) -> bf16x8 {
-      const int o = colb + chunk * kCB + 512 * ks2;
-      return join8(lds_read_tr16(reinterpret_cast<const uint16_t*>(base + o)),
-                   lds_read_tr16(reinterpret_cast<const uint16_t*>(base + o + 256)));
-    };
-
     __syncthreads();  // the previous pass's output tiles have been read
     if (nkt_run > 0) issue(0, 0);
     for (int kt = 0; kt < nkt_run; ++kt) {
       wait_vmcnt<0>();
       barrier_no_vm_wait();  // tile kt is in LDS; the other stage is free
-      const char* cur = smem + (kt & 1) * SB;
+      const uint32_t stage = smem_lds + (kt & 1) * SB;
       if (kt + 1 < nkt_run) issue(kt + 1, (~kt & 1) * SB);
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
+        // K column fragments of this wave's feature tiles (keys 32 ks2 ..)
         bf16x8 kb[NF];
 #pragma unroll
-        for (int f = 0; f < NF; ++f) kb[f] = colfrag(cur, 2 * (fh * NF + f), ks2);
+        for (int f = 0; f < NF; ++f)
+          kb[f] = join8(lds_tr16_at(stage + kcol[f][ks2][0]), lds_tr16_at(stage + kcol[f][ks2][1]));
 #pragma unroll
         for (int hh = 0; hh < HP; ++hh) {
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) {
-            const bf16x8 da = colfrag(cur + KB + hh * DB, 2 * (2 * rh + rt), ks2);
+            const uint32_t o = stage + OD + hh * TD::BYTES + dsA[rt] + ks2 * 32 * TD::RB;
+            const bf16x8 da = join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB));
 #pragma unroll
             for (int f = 0; f < NF; ++f) acc[hh][rt][f] = mfma_16x16x32(da, kb[f], acc[hh][rt][f]);
           }
@@ -161,39 +212,38 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
       }
     }
 
-    // ---- epilogue: bf16 through LDS (chunk-major [chunk][64 rows] per head), 16-byte stores
+    // ---- epilogue: bf16 through LDS (row-major [64 rows][DQK] per head), 16-byte stores
     __syncthreads();
 #pragma unroll
     for (int hh = 0; hh < HP; ++hh) {
-      uint16_t* O = reinterpret_cast<uint16_t*>(smem + hh * KB);
+      uint16_t* O = reinterpret_cast<uint16_t*>(smem) + hh * kT * DQK;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int f = 0; f < NF; ++f)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 32 * rh + 16 * rt + 4 * g + i, col = 16 * (fh * NF + f) + l16;
-            O[((col >> 3) * kCB + 16 * r) / 2 + (col & 7)] = f2bf(acc[hh][rt][f][i] * a.scale);
-          }
+          for (int i = 0; i < 4; ++i)
+            O[(32 * rh + 16 * rt + 4 * g + i) * DQK + 16 * (fh * NF + f) + l16] = f2bf(acc[hh][rt][f][i] * a.scale);
     }
     __syncthreads();
+    constexpr int QCH = DQK / 8;
     for (int idx = tid; idx < HP * kT * QCH; idx += 256) {
       const int hh = idx / (kT * QCH), rem = idx - hh * (kT * QCH);
       const int r = rem / QCH, c = rem - r * QCH, d = 8 * c;
       if (r < nvalid) {
         const int64_t qr = (qs + (int64_t)qt * kT + r) * a.n1 + h0 + hh;
-        uint16_t* dst = d < a.d_main ? a.dq + qr * a.d_main + d : a.dq_rope + qr * a.d_rope + (d - a.d_main);
-        sts16(dst, *reinterpret_cast<const uint4*>(smem + hh * KB + c * kCB + 16 * r));
+        uint16_t* dst = d < DM ? a.dq + qr * DM + d : a.dq_rope + qr * DR + (d - DM);
+        sts16(dst, *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(smem) + (hh * kT + r) * DQK + d));
       }
     }
   }
 }
 
-template <int DQK>
+template <int DM, int DR>
 hipError_t launch_hp(const DqArgs& k, int G, dim3 grid, hipStream_t s) {
-  if (G % 4 == 0) hipLaunchKernelGGL((dense_dq_ds_kernel<DQK, 4>), grid, dim3(256), 0, s, k);
-  else if (G % 2 == 0) hipLaunchKernelGGL((dense_dq_ds_kernel<DQK, 2>), grid, dim3(256), 0, s, k);
-  else hipLaunchKernelGGL((dense_dq_ds_kernel<DQK, 1>), grid, dim3(256), 0, s, k);
+  if (G % 4 == 0) hipLaunchKernelGGL((dense_dq_ds_kernel<DM, DR, 4>), grid, dim3(256), 0, s, k);
+  else if (G % 2 == 0) hipLaunchKernelGGL((dense_dq_ds_kernel<DM, DR, 2>), grid, dim3(256), 0, s, k);
+  else hipLaunchKernelGGL((dense_dq_ds_kernel<DM, DR, 1>), grid, dim3(256), 0, s, k);
   return hipGetLastError();
 }
 
@@ -207,13 +257,11 @@ hipError_t launch_dense_dq_from_ds(const DenseArgs& a, hipStream_t s) {
   k.dq = (uint16_t*)a.dq; k.dq_rope = (uint16_t*)a.dq_rope;
   k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.ds_base = a.ds_base; k.tiles = a.q_tiles;
   k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;
-  k.d_main = a.d_main; k.d_rope = a.d_rope;
   k.causal = a.causal; k.scale = a.scale;
   const dim3 grid(a.n_q_tiles, a.n2);
-  const int dqk = a.d_main + a.d_rope;
-  if (dqk == 192) return launch_hp<192>(k, a.G, grid, s);
-  if (dqk == 128) return launch_hp<128>(k, a.G, grid, s);
-  if (dqk == 64) return launch_hp<64>(k, a.G, grid, s);
+  if (a.d_main == 128 && a.d_rope == 64) return launch_hp<128, 64>(k, a.G, grid, s);
+  if (a.d_main == 128 && a.d_rope == 0) return launch_hp<128, 0>(k, a.G, grid, s);
+  if (a.d_main == 64 && a.d_rope == 0) return launch_hp<64, 0>(k, a.G, grid, s);
   return hipErrorInvalidValue;
 }
 

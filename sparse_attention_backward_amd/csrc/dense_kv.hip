@@ -5,8 +5,8 @@
 // dK = dS^T Q / sqrt(d), dkRope = dS^T qRope / sqrt(d), with Q = [query, queryRope].
 //
 // One workgroup (4 waves) owns a 64-key tile of one sequence and KV head.  Query rows
-// stream past in steps of 64 rows: for each of the G query heads of the KV head, the
-// query tiles from the last one down to the diagonal (causal) or down to the first.
+// stream past in steps of 64 rows: the query tiles from the last one down to the diagonal
+// (causal) or down to the first, each for the G query heads of the KV head in turn.
 // Walking every key tile's list from the same end keeps the workgroups of one
 // (sequence, KV head) on the same query tile at the same time, so their row loads
 // share the L2.
@@ -23,10 +23,10 @@
 // Each key row's dK / dV is the sum of the two row-half waves' registers, added once
 // through LDS at the end.  Every output row has one writer: no atomics, deterministic.
 //
-// Staging: a step's Q / dY / lse2 / drow land in one of three LDS stages, moved by
-// global->LDS transfers issued two steps ahead.  Stage tiles are chunk-major: the
-// 16-byte chunk c of row r sits at byte c * kCB + 16 r, so one transfer moves one chunk
-// of all 64 rows (lane = row) and every LDS read is a per-lane base plus an immediate.
+// Staging: a step's Q (query and queryRope parts), dY, lse2 and drow land in one of three
+// LDS stages, moved by global->LDS transfers issued two steps ahead.  Each part is a
+// RowTile: every transfer instruction reads whole rows (full cache lines) and the chunk
+// swizzle keeps the row and column reads conflict free.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -34,8 +34,7 @@ namespace ab {
 
 namespace {
 
-constexpr int kRows = 64;        // query rows per step, keys per workgroup
-constexpr int kCB = 1024 + 128;  // bytes per chunk column of a staged 64-row tile
+constexpr int kRows = 64;  // query rows per step, keys per workgroup
 typedef __attribute__((address_space(3))) void lds_void;
 
 struct DkvArgs {
@@ -48,7 +47,7 @@ struct DkvArgs {
   const int64_t* cu_q; const int64_t* cu_kv;
   const int64_t* ds_base;     // [B + 1] (query tile, key tile) blocks before each sequence
   const int32_t* tiles;       // [n][3] (sequence, key tile, KV head); sequence < 0: idle slot
-  int n1, n2, G, d_main, d_rope, d_v;
+  int n1, n2, G;
   int causal;
   float scale, scale_log2e;
 };
@@ -72,13 +71,13 @@ __device__ __forceinline__ void barrier_no_vm_wait() {
 __device__ __forceinline__ uint32_t lds_addr(const void* lds) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
 }
-// global -> LDS transfer of 16 bytes per lane: lane l reads `src` + OFF and writes LDS
-// byte M0 + OFF + 16 l with M0 = `lds` + MOFF.  Inline assembly keeps the compiler from
-// adding waits of its own: every wait on these transfers is an explicit wait_vmcnt.
-template <int MOFF, int OFF>
+// global -> LDS transfer of 16 bytes per lane: lane l reads `src` and writes LDS byte
+// M0 + 16 l with M0 = `lds` + MOFF.  Inline assembly keeps the compiler from adding waits
+// of its own: every wait on these transfers is an explicit wait_vmcnt.
+template <int MOFF>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%3"
-               ::"v"(src), "s"(lds), "i"(MOFF), "i"(OFF) : "memory", "m0", "scc");
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(src), "s"(lds), "i"(MOFF) : "memory", "m0", "scc");
 }
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
@@ -98,27 +97,52 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <typename T>
-__device__ __forceinline__ const T* at_bytes(const void* base, int bytes) {
-  return reinterpret_cast<const T*>(static_cast<const char*>(base) + bytes);
-}
+// Per-lane addressing of one staged part (a RowTile of W chunks per row) for one wave.
+//   transfers: the wave issues instructions i = w + 4k (k < W/4); lane l fills row
+//              (w + 4k) RPI + l / W, slot l % W, i.e. reads chunk (l % W) ^ swz(row) --
+//              the same chunk for every k, because 4 RPI rows is a multiple of 16.
+//   row reads (A operands): rows 32rh + 16rt + l16, chunk 4s + g.
+//   column reads (transposed, B operands): rows 32rh + 4g + jj (+16), chunk 2j + qq/2,
+//              half qq&1.
+template <int W>
+struct PartLanes {
+  using T = RowTile<W>;
+  int row0;          // transfer row for k = 0
+  uint32_t gchunk;   // byte offset of the chunk this lane reads within its row
+  int rowA[W / 4];   // tile-relative byte offsets of the row reads (k-step s)
+  int colB[W / 2];   // tile-relative byte offsets of the column reads (column tile j)
+  __device__ __forceinline__ void init(int w, int lane, int rh) {
+    const int l16 = lane & 15, g = lane >> 4, jj = l16 >> 2, qq = l16 & 3;
+    row0 = w * T::RPI + lane / W;
+    gchunk = 16u * (uint32_t)((lane % W) ^ T::swz(row0));
+#pragma unroll
+    for (int s = 0; s < W / 4; ++s) rowA[s] = T::off(32 * rh + l16, 4 * s + g);
+#pragma unroll
+    for (int j = 0; j < W / 2; ++j) colB[j] = T::off(32 * rh + 4 * g + jj, 2 * j + (qq >> 1)) + 8 * (qq & 1);
+  }
+};
 
-template <int DQK, int DV, bool DS>
+template <int DM, int DR, int DV, bool DS>
 __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
+  constexpr int DQK = DM + DR;
   constexpr int KS = DQK / 32, VS = DV / 32, NQ = DQK / 16, NV = DV / 16;
-  constexpr int QCH = DQK / 8, YCH = DV / 8;   // 16-byte chunks per row
-  constexpr int QLD = QCH / 4, YLD = YCH / 4;  // transfer instructions per wave per tile
-  constexpr int NLD = QLD + YLD + 2;           // + lse2, drow
-  constexpr int QB = QCH * kCB, YB = YCH * kCB;
-  constexpr int SB = QB + YB + 2 * 256;        // one stage: Q, dY, lse2, drow
+  constexpr int KSM = DM / 32, NQM = DM / 16;  // k-steps / column tiles of the query part
+  constexpr int WM = DM / 8, WR = DR > 0 ? DR / 8 : 8, WY = DV / 8;
+  using TM = RowTile<WM>;
+  using TR = RowTile<WR>;
+  using TY = RowTile<WY>;
+  constexpr int OQM = 0, OQR = TM::BYTES, OY = OQR + (DR > 0 ? TR::BYTES : 0);
+  constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = ORW + 256;  // stage: QM, QR, Y, lse2, drow
+  constexpr int NLD = DM / 32 + DR / 32 + DV / 32 + 2;                // transfers per wave per stage
+  constexpr int NACC = 2 * (NQ + NV);
   static_assert(3 * SB <= 160 * 1024, "three stages must fit in LDS");
-  static_assert(2 * 2 * (NQ + NV) * 1024 + (QCH + YCH) * kCB <= 3 * SB, "epilogue buffers must fit");
-  __shared__ __attribute__((aligned(16))) char smem[3 * SB];
+  static_assert(2 * NACC * 1024 + 64 * (DQK + DV) * 2 <= 3 * SB, "epilogue buffers must fit");
+  __shared__ __attribute__((aligned(1024))) char smem[3 * SB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = w & 1, rh = w >> 1;
-  const int l16 = lane & 15, g = lane >> 4, jj = l16 >> 2, qq = l16 & 3;
+  const int l16 = lane & 15, g = lane >> 4;
 
   const int b = a.tiles[3 * blockIdx.x];
   if (b < 0) return;  // idle slot of the schedule
@@ -135,7 +159,6 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
   const int qt0 = a.causal ? min(kt0, nqt) : 0;
   const int nq = nqt - qt0;
   const int nsteps = a.G * nq;
-  const int qmain = a.d_main / 8;  // chunks of a Q row that come from `query` (the rest: queryRope)
   const int64_t blk0 = a.ds_base[b];
 
   // ---- resident keys: K and V as MFMA B operands ------------------------------------
@@ -149,16 +172,20 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     for (int s = 0; s < KS; ++s) {
       const int d = 32 * s + 8 * g;
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (valid) x = ldg16(d < a.d_main ? a.k + kr * a.d_main + d : a.k_rope + kr * a.d_rope + (d - a.d_main));
+      if (valid) x = ldg16(d < DM ? a.k + kr * DM + d : a.k_rope + kr * DR + (d - DM));
       Kf[t][s] = __builtin_bit_cast(bf16x8, x);
     }
 #pragma unroll
     for (int s = 0; s < VS; ++s) {
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (valid) x = ldg16(a.v + kr * a.d_v + 32 * s + 8 * g);
+      if (valid) x = ldg16(a.v + kr * DV + 32 * s + 8 * g);
       Vf[t][s] = __builtin_bit_cast(bf16x8, x);
     }
   }
+  // The K / V loads are the only vector-memory operations the compiler tracks; waiting for
+  // them here keeps it from placing a full wait (which would also drain the transfers
+  // issued ahead) inside the step loop, where the registers are first used.
+  wait_vmcnt<0>();
 
   f32x4 dK[2][NQ], dV[2][NV];
 #pragma unroll
@@ -169,52 +196,187 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     for (int n = 0; n < NV; ++n) dV[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Per-lane LDS byte offsets within a stage.  Row reads: rows 32rh + 16rt + l16, chunk
-  // 4s + g.  Column reads: rows 32rh + 4g + jj (+16), chunk 2j + qq/2, half qq&1.
-  const int rd_row = g * kCB + 16 * (32 * rh + l16);
-  const int rd_col = (qq >> 1) * kCB + 16 * (32 * rh + 4 * g + jj) + 8 * (qq & 1);
+  PartLanes<WM> pm;
+  PartLanes<WR> pr;
+  PartLanes<WY> py;
+  pm.init(w, lane, rh);
+  if constexpr (DR > 0) pr.init(w, lane, rh);
+  py.init(w, lane, rh);
 
-  // step st -> (head hg, query tile qt), query tiles walked from the last one down
+  // step st -> (query tile qt, head hg): query tiles walked from the last one down, the G
+  // heads of a query tile back to back
   auto step_tile = [&](int st, int& hg, int& qt) {
-    hg = st / nq;
-    qt = nqt - 1 - (st - hg * nq);
+    const int i = st / a.G;
+    hg = st - i * a.G;
+    qt = nqt - 1 - i;
   };
 
-  // issue(): wave w moves chunks c = w + 4k of the 64 rows (lane = row) into one stage.
-  // Chunk c lands at c * kCB in the stage: with the per-lane row address + 16 w and the
-  // stage + w * kCB as bases, chunk k is the immediate 64 k (global) / 4 k kCB (LDS).
-  const int kq = (qmain - w + 3) >> 2;  // chunks k < kq come from `query`, the rest from queryRope
   const uint32_t smem_lds = lds_addr(smem);
+  const uint32_t rs_m = (uint32_t)a.n1 * DM * 2, rs_r = (uint32_t)a.n1 * DR * 2, rs_y = (uint32_t)a.n1 * DV * 2;
+
+  // Transfers of one part: wave w's instructions k move rows (w + 4k) RPI + l / W.  Row
+  // addresses: the tile's first row (uniform) plus (row, clamped to the last valid row)
+  // times the token stride.
+  auto issue_part = [&](auto wtag, const auto& pl, const char* gtile, uint32_t rs, uint32_t lds_part, int nvalid) {
+    constexpr int W = decltype(wtag)::value;
+    constexpr int RPI = RowTile<W>::RPI;
+    static_for<W / 4>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const int r = min(pl.row0 + 4 * RPI * k, nvalid - 1);
+      dma16<4096 * k>(gtile + __umul24((uint32_t)r, rs) + pl.gchunk, lds_part + w * 1024);
+    });
+  };
   auto issue = [&](int st, int soff) {
     int hg, qt;
     step_tile(st, hg, qt);
     const int h = kvh * a.G + hg;
     const int nvalid = min(kRows, S1 - qt * kRows);
-    const int64_t r0 = qs + (int64_t)qt * kRows;
-    const int64_t qr = (r0 + min(lane, nvalid - 1)) * a.n1 + h;
-    const char* qrow = reinterpret_cast<const char*>(a.q + qr * a.d_main) + 16 * w;
-    const char* rrow = reinterpret_cast<const char*>(a.q_rope + qr * a.d_rope) + 16 * (w - qmain);
-    const char* yrow = reinterpret_cast<const char*>(a.dy + qr * a.d_v) + 16 * w;
-    const uint32_t qb = smem_lds + soff + w * kCB, yb = smem_lds + soff + QB + w * kCB;
-    static_for<QLD>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      dma16<k * (4 * kCB - 64), 64 * k>(k < kq ? qrow : rrow, qb);
-    });
-    static_for<YLD>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      dma16<k * (4 * kCB - 64), 64 * k>(yrow, yb);
-    });
+    const int64_t rh0 = (qs + (int64_t)qt * kRows) * a.n1 + h;  // (first row) * n1 + h
+    const uint32_t stage = smem_lds + soff;
+    issue_part(std::integral_constant<int, WM>{}, pm, reinterpret_cast<const char*>(a.q + rh0 * DM), rs_m,
+               stage + OQM, nvalid);
+    if constexpr (DR > 0)
+      issue_part(std::integral_constant<int, WR>{}, pr, reinterpret_cast<const char*>(a.q_rope + rh0 * DR), rs_r,
+                 stage + OQR, nvalid);
+    issue_part(std::integral_constant<int, WY>{}, py, reinterpret_cast<const char*>(a.dy + rh0 * DV), rs_y,
+               stage + OY, nvalid);
     // lse2 / drow of rows 16w .. 16w+15 (lanes 0..15)
-    const int64_t lr = (r0 + min(16 * w + l16, nvalid - 1)) * a.n1 + h;
-    if (lane < 16) dma4(a.lse2 + lr, smem_lds + soff + QB + YB + 64 * w);
-    if (lane < 16) dma4(a.drow + lr, smem_lds + soff + QB + YB + 256 + 64 * w);
+    const int64_t lrow = rh0 + (int64_t)min(16 * w + l16, nvalid - 1) * a.n1;
+    if (lane < 16) dma4(a.lse2 + lrow, stage + OL + 64 * w);
+    if (lane < 16) dma4(a.drow + lrow, stage + ORW + 64 * w);
   };
 
   // dS of the previous step, stored at the start of the next one (see the loop)
   i16x4 dsv[2][2];
   uint16_t* dsp = nullptr;
 
-  auto step = [&](int st, const char* stage) {
+  // One step.  Masks, all applied outside the MFMA stream: rows past the end of the
+  // sequence get lse2 = +inf (P = 0); on the causal diagonal a short wave-uniform fix-up
+  // zeroes P where key > row; keys past the end only matter for the stored dS, which is
+  // zeroed for them (their dK / dV rows are never written).
+  auto step_body = [&](int nvalid, bool diag, int soff) {
+    const uint32_t stage = smem_lds + soff;
+    const uint32_t statb = opaque(stage + OL + 4 * (32 * rh + 4 * g));  // lse2; drow at + 256
+
+    f32x4 lse[2], dr[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      lse[rt] = lds_f32x4_at(statb + 64 * rt);
+      dr[rt] = lds_f32x4_at(statb + 256 + 64 * rt);
+    }
+    if (nvalid < kRows) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lse[rt][i] = 32 * rh + 16 * rt + 4 * g + i < nvalid ? lse[rt][i] : INFINITY;
+    }
+    // S = Q K^T, dP = dY V^T.  k-steps s < KSM read the query part, KSM <= s < KS the rope
+    // part, the rest dY; the A fragments of a k-step (both row tiles) serve both key tiles
+    // and are read PA k-steps ahead.
+    constexpr int NS = KS + VS, PA = 3;
+    auto afrag = [&](int s, int rt) -> bf16x8 {
+      if (s < KSM) return lds_b128_at(stage + OQM + pm.rowA[s] + rt * 16 * TM::RB);
+      if (s < KS) return lds_b128_at(stage + OQR + pr.rowA[s - KSM] + rt * 16 * TR::RB);
+      return lds_b128_at(stage + OY + py.rowA[s - KS] + rt * 16 * TY::RB);
+    };
+    bf16x8 aring[PA][2];
+#pragma unroll
+    for (int i = 0; i < PA; ++i) { aring[i][0] = afrag(i, 0); aring[i][1] = afrag(i, 1); }
+    f32x4 S[2][2], D[2][2];  // [key tile][row tile]
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 a0 = aring[s % PA][0], a1 = aring[s % PA][1];
+      if (s + PA < NS) { aring[s % PA][0] = afrag(s + PA, 0); aring[s % PA][1] = afrag(s + PA, 1); }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (s < KS) {
+          S[t][0] = mfma_16x16x32(a0, Kf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][0]);
+          S[t][1] = mfma_16x16x32(a1, Kf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][1]);
+        } else {
+          D[t][0] = mfma_16x16x32(a0, Vf[t][s - KS], s == KS ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t][0]);
+          D[t][1] = mfma_16x16x32(a1, Vf[t][s - KS], s == KS ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t][1]);
+        }
+      }
+    }
+    // schedule: the PA k-steps' reads first, then per k-step its 4 MFMAs and the reads of
+    // the k-step PA ahead, so that each read has PA k-steps of MFMA work to land
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PA, 0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (s + PA < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    // P, then dS in place
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t][rt][i] = __builtin_amdgcn_exp2f(S[t][rt][i] * a.scale_log2e - lse[rt][i]);
+    if (diag && kh == rh) {
+      // keys 32kh + 16t + l16 against rows 32rh + 16rt + 4g + i: with kh == rh, tile pair
+      // (t, rt) = (1, 0) lies wholly after the diagonal, (0, 1) wholly before it, and on
+      // (0, 0) / (1, 1) the key lies after the row iff l16 - 4g > i
+      const int dl = l16 - 4 * g;
+      S[1][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool after = dl > i;
+        S[0][0][i] = after ? 0.f : S[0][0][i];
+        S[1][1][i] = after ? 0.f : S[1][1][i];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) D[t][rt][i] = S[t][rt][i] * (D[t][rt][i] - dr[rt][i]);
+    // dV += P^T dY, dK += dS^T Q.  Items j < NV: dY columns 16j.. (dV); then the query and
+    // rope columns (dK).  Each column fragment (two transposed reads) serves both key tiles
+    // and is read PD items ahead of its MFMAs.
+    bf16x8 pa[2], da[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      pa[t] = pack8(S[t][0], S[t][1]);
+      da[t] = pack8(D[t][0], D[t][1]);
+      const i16x8 dv8 = __builtin_bit_cast(i16x8, da[t]);
+      dsv[t][0] = i16x4{dv8[0], dv8[1], dv8[2], dv8[3]};
+      dsv[t][1] = i16x4{dv8[4], dv8[5], dv8[6], dv8[7]};
+      if (nk < kRows && 32 * kh + 16 * t + l16 >= nk) dsv[t][0] = dsv[t][1] = i16x4{0, 0, 0, 0};
+    }
+    auto colfrag = [&](int j) -> bf16x8 {
+      uint32_t o, second;
+      if (j < NV) { o = stage + OY + py.colB[j]; second = 16 * TY::RB; }
+      else if (j < NV + NQM) { o = stage + OQM + pm.colB[j - NV]; second = 16 * TM::RB; }
+      else { o = stage + OQR + pr.colB[j - NV - NQM]; second = 16 * TR::RB; }
+      return join8(lds_tr16_at(o), lds_tr16_at(o + second));
+    };
+    constexpr int NJ = NV + NQ, PD = 4;
+    bf16x8 ring[PD];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) ring[i] = colfrag(i);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const bf16x8 bj = ring[j % PD];
+      if (j + PD < NJ) ring[j % PD] = colfrag(j + PD);
+      if (j < NV) {
+        dV[0][j] = mfma_16x16x32(pa[0], bj, dV[0][j]);
+        dV[1][j] = mfma_16x16x32(pa[1], bj, dV[1][j]);
+      } else {
+        dK[0][j - NV] = mfma_16x16x32(da[0], bj, dK[0][j - NV]);
+        dK[1][j - NV] = mfma_16x16x32(da[1], bj, dK[1][j - NV]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      if (j + PD < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+  };
+
+  auto step = [&](int st, int soff) {
     int hg, qt;
     step_tile(st, hg, qt);
     const int h = kvh * a.G + hg;
@@ -230,83 +392,7 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
       for (int t = 0; t < 2; ++t) dsv[t][0] = dsv[t][1] = i16x4{0, 0, 0, 0};
       return;
     }
-    const char* Qs = stage;
-    const char* Ys = stage + QB;
-    const float* Ls = at_bytes<float>(stage, QB + YB);
-    const float* Rs = at_bytes<float>(stage, QB + YB + 256);
-
-    // S = Q K^T, dP = dY V^T for both key tiles; the A fragments are shared by them
-    bf16x8 qa[2][KS], ya[2][VS];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qa[rt][s] = *at_bytes<bf16x8>(Qs, rd_row + 4 * s * kCB + 256 * rt);
-#pragma unroll
-      for (int s = 0; s < VS; ++s) ya[rt][s] = *at_bytes<bf16x8>(Ys, rd_row + 4 * s * kCB + 256 * rt);
-    }
-    f32x4 S[2][2], D[2][2];  // [key tile][row tile]
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        S[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        D[t][rt] = S[t][rt];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) S[t][rt] = mfma_16x16x32(qa[rt][s], Kf[t][s], S[t][rt]);
-#pragma unroll
-        for (int s = 0; s < VS; ++s) D[t][rt] = mfma_16x16x32(ya[rt][s], Vf[t][s], D[t][rt]);
-      }
-    // P and dS in place
-    f32x4 lse[2], dr[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      lse[rt] = *reinterpret_cast<const f32x4*>(&Ls[32 * rh + 16 * rt + 4 * g]);
-      dr[rt] = *reinterpret_cast<const f32x4*>(&Rs[32 * rh + 16 * rt + 4 * g]);
-    }
-    const bool masked = diag || nvalid < kRows || nk < kRows;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int key = 32 * kh + 16 * t + l16;  // local to the key tile
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float p = __builtin_amdgcn_exp2f(S[t][rt][i] * a.scale_log2e - lse[rt][i]);
-          if (masked) {
-            const int r = 32 * rh + 16 * rt + 4 * g + i;  // local to the query tile
-            const bool off = r >= nvalid || key >= nk || (diag && key > r);
-            p = off ? 0.f : p;
-          }
-          D[t][rt][i] = p * (D[t][rt][i] - dr[rt][i]);
-          S[t][rt][i] = p;
-        }
-    }
-    // dV += P^T dY, dK += dS^T Q; the column fragments are shared by both key tiles
-    bf16x8 pa[2], da[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      pa[t] = pack8(S[t][0], S[t][1]);
-      da[t] = pack8(D[t][0], D[t][1]);
-      dsv[t][0] = pack4(D[t][0]);
-      dsv[t][1] = pack4(D[t][1]);
-    }
-    auto colfrag = [&](const char* base, int j) -> bf16x8 {
-      const int o = rd_col + 2 * j * kCB;
-      return join8(lds_read_tr16(reinterpret_cast<const uint16_t*>(base + o)),
-                   lds_read_tr16(reinterpret_cast<const uint16_t*>(base + o + 256)));
-    };
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const bf16x8 bv = colfrag(Ys, j);
-      dV[0][j] = mfma_16x16x32(pa[0], bv, dV[0][j]);
-      dV[1][j] = mfma_16x16x32(pa[1], bv, dV[1][j]);
-    }
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const bf16x8 bq = colfrag(Qs, j);
-      dK[0][j] = mfma_16x16x32(da[0], bq, dK[0][j]);
-      dK[1][j] = mfma_16x16x32(da[1], bq, dK[1][j]);
-    }
+    step_body(nvalid, diag, soff);
   };
 
   auto store_ds = [&]() {
@@ -333,7 +419,7 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     if (DS && st > 0) store_ds();
     const int ph = st % 3;
     if (st + 2 < nsteps) issue(st + 2, (ph == 0 ? 2 : ph - 1) * SB);
-    step(st, smem + ph * SB);
+    step(st, ph * SB);
   }
   if (DS && nsteps > 0) store_ds();
 
@@ -341,7 +427,6 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
   __syncthreads();
   // partials of the rh = 1 waves: [kh][index][lane] as f32x4 (conflict-free)
   f32x4* part = reinterpret_cast<f32x4*>(smem);
-  constexpr int NACC = 2 * (NQ + NV);
   if (rh == 1) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -352,9 +437,9 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     }
   }
   __syncthreads();
-  char* outt = smem + 2 * NACC * 1024;  // [chunk][64 keys] output tile, chunk-major
-  uint16_t* Ko = reinterpret_cast<uint16_t*>(outt);
-  uint16_t* Vo = reinterpret_cast<uint16_t*>(outt + QCH * kCB);
+  // output tiles, row-major: dK [64 keys][DQK], dV [64 keys][DV]
+  uint16_t* Ko = reinterpret_cast<uint16_t*>(smem + 2 * NACC * 1024);
+  uint16_t* Vo = Ko + 64 * DQK;
   if (rh == 0) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -362,42 +447,45 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
       for (int n = 0; n < NQ; ++n) {
         const f32x4 o = part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 32 * kh + 16 * t + 4 * g + i, col = 16 * n + l16;
-          Ko[((col >> 3) * kCB + 16 * r) / 2 + (col & 7)] = f2bf((dK[t][n][i] + o[i]) * a.scale);
-        }
+        for (int i = 0; i < 4; ++i)
+          Ko[(32 * kh + 16 * t + 4 * g + i) * DQK + 16 * n + l16] = f2bf((dK[t][n][i] + o[i]) * a.scale);
       }
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
         const f32x4 o = part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 32 * kh + 16 * t + 4 * g + i, col = 16 * n + l16;
-          Vo[((col >> 3) * kCB + 16 * r) / 2 + (col & 7)] = f2bf(dV[t][n][i] + o[i]);
-        }
+        for (int i = 0; i < 4; ++i) Vo[(32 * kh + 16 * t + 4 * g + i) * DV + 16 * n + l16] = f2bf(dV[t][n][i] + o[i]);
       }
     }
   }
   __syncthreads();
+  constexpr int QCH = DQK / 8, YCH = DV / 8;
   for (int idx = tid; idx < kRows * QCH; idx += 256) {
     const int r = idx / QCH, c = idx - r * QCH, d = 8 * c;
     if (r < nk) {
       const int64_t kr = (k0 + r) * a.n2 + kvh;
-      uint16_t* dst = d < a.d_main ? a.dk + kr * a.d_main + d : a.dk_rope + kr * a.d_rope + (d - a.d_main);
-      sts16(dst, *at_bytes<uint4>(outt, c * kCB + 16 * r));
+      uint16_t* dst = d < DM ? a.dk + kr * DM + d : a.dk_rope + kr * DR + (d - DM);
+      sts16(dst, *reinterpret_cast<const uint4*>(Ko + r * DQK + d));
     }
   }
   for (int idx = tid; idx < kRows * YCH; idx += 256) {
     const int r = idx / YCH, c = idx - r * YCH;
-    if (r < nk)
-      sts16(a.dv + ((k0 + r) * a.n2 + kvh) * a.d_v + 8 * c, *at_bytes<uint4>(outt, QCH * kCB + c * kCB + 16 * r));
+    if (r < nk) sts16(a.dv + ((k0 + r) * a.n2 + kvh) * DV + 8 * c, *reinterpret_cast<const uint4*>(Vo + r * DV + 8 * c));
   }
+}
+
+template <int DM, int DR, int DV>
+hipError_t launch_kv(const DkvArgs& k, dim3 grid, bool ds, hipStream_t s) {
+  if (ds) hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, true>), grid, dim3(256), 0, s, k);
+  else hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, false>), grid, dim3(256), 0, s, k);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-bool dense_bf16_supported(int d_qk_total, int d_v) {
-  return (d_qk_total == 192 && d_v == 128) || (d_qk_total == 128 && d_v == 128) || (d_qk_total == 64 && d_v == 64);
+bool dense_bf16_supported(int d_main, int d_rope, int d_v) {
+  return (d_main == 128 && d_rope == 64 && d_v == 128) || (d_main == 128 && d_rope == 0 && d_v == 128) ||
+         (d_main == 64 && d_rope == 0 && d_v == 64);
 }
 
 hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) {
@@ -411,20 +499,13 @@ hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) {
   k.ds = (uint16_t*)a.ds;
   k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.ds_base = a.ds_base; k.tiles = a.kv_tiles;
   k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;
-  k.d_main = a.d_main; k.d_rope = a.d_rope; k.d_v = a.d_v;
   k.causal = a.causal; k.scale = a.scale; k.scale_log2e = a.scale_log2e;
   const dim3 grid(a.n_kv_tiles);
-  const int dqk = a.d_main + a.d_rope;
   const bool ds = a.ds != nullptr;
-#define ATTN_KV_LAUNCH(DQ, DV_)                                                                      \
-  if (ds) hipLaunchKernelGGL((dense_kv_kernel<DQ, DV_, true>), grid, dim3(256), 0, s, k);            \
-  else hipLaunchKernelGGL((dense_kv_kernel<DQ, DV_, false>), grid, dim3(256), 0, s, k);
-  if (dqk == 192 && a.d_v == 128) { ATTN_KV_LAUNCH(192, 128) }
-  else if (dqk == 128 && a.d_v == 128) { ATTN_KV_LAUNCH(128, 128) }
-  else if (dqk == 64 && a.d_v == 64) { ATTN_KV_LAUNCH(64, 64) }
-  else return hipErrorInvalidValue;
-#undef ATTN_KV_LAUNCH
-  return hipGetLastError();
+  if (a.d_main == 128 && a.d_rope == 64 && a.d_v == 128) return launch_kv<128, 64, 128>(k, grid, ds, s);
+  if (a.d_main == 128 && a.d_rope == 0 && a.d_v == 128) return launch_kv<128, 0, 128>(k, grid, ds, s);
+  if (a.d_main == 64 && a.d_rope == 0 && a.d_v == 64) return launch_kv<64, 0, 64>(k, grid, ds, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ab

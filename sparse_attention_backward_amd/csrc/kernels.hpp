@@ -42,7 +42,7 @@ struct DenseArgs {
   int causal;
 };
 constexpr int kDenseTile = 64;  // query and key tile length of the bf16 dense kernels
-bool dense_bf16_supported(int d_qk_total, int d_v);
+bool dense_bf16_supported(int d_main, int d_rope, int d_v);
 hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s);     // KV-major dK, dV (+ dS when a.ds)
 hipError_t launch_dense_dq_from_ds(const DenseArgs& a, hipStream_t s);  // dQ = scale dS K from stored dS
 hipError_t launch_dense_dq_bf16(const DenseArgs& a, hipStream_t s);     // query-major dQ, recomputing S, dP
