@@ -59,6 +59,14 @@ __device__ __forceinline__ f32x4 lds_f32x4_at(uint32_t addr) {
 __device__ __forceinline__ i16x4 lds_tr16_at(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>((uintptr_t)addr));
 }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+__device__ __forceinline__ void lds_st16_at(uint32_t addr, uint4 v) {
+  *reinterpret_cast<lds_u32x4*>((uintptr_t)addr) = u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ void lds_st4_at(uint32_t addr, float v) {
+  *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)addr) = v;
+}
 // Hides how a value was computed, so that the compiler keeps it as one base register and
 // folds the constants added to it into immediate offsets instead of re-associating the
 // sum into one register per constant.

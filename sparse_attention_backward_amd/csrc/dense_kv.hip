@@ -23,10 +23,12 @@
 // Each key row's dK / dV is the sum of the two row-half waves' registers, added once
 // through LDS at the end.  Every output row has one writer: no atomics, deterministic.
 //
-// Staging: a step's Q (query and queryRope parts), dY, lse2 and drow land in one of three
-// LDS stages, moved by global->LDS transfers issued two steps ahead.  Each part is a
-// RowTile: every transfer instruction reads whole rows (full cache lines) and the chunk
-// swizzle keeps the row and column reads conflict free.
+// Staging: a step's Q (query and queryRope parts), dY, lse2 and drow are loaded into
+// registers one step ahead (while the current step computes) and written to one of two
+// LDS stages at the end of the step.  (Global->LDS transfers were measured to slow the
+// LDS reads of the compute phases in proportion to the bytes they move.)  Each part is a
+// RowTile: every load instruction reads whole rows (full cache lines) and the chunk
+// swizzle keeps the LDS writes and the row / column reads conflict free.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -71,20 +73,8 @@ __device__ __forceinline__ void barrier_no_vm_wait() {
 __device__ __forceinline__ uint32_t lds_addr(const void* lds) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
 }
-// global -> LDS transfer of 16 bytes per lane: lane l reads `src` and writes LDS byte
-// M0 + 16 l with M0 = `lds` + MOFF.  Inline assembly keeps the compiler from adding waits
-// of its own: every wait on these transfers is an explicit wait_vmcnt.
-template <int MOFF>
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(src), "s"(lds), "i"(MOFF) : "memory", "m0", "scc");
-}
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-}
-// 8-byte store issued as inline assembly as well, so that the compiler does not insert a
-// full vmcnt wait before the next step's transfers (it cannot see that the waits on
-// those transfers are exact; see the ordering note in the step loop).
+// 8-byte store issued as inline assembly, so that the compiler does not hold back the
+// next step's loads behind it.
 __device__ __forceinline__ void st8(void* dst, i16x4 v) {
   asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(dst), "v"(v) : "memory");
 }
@@ -98,7 +88,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Per-lane addressing of one staged part (a RowTile of W chunks per row) for one wave.
-//   transfers: the wave issues instructions i = w + 4k (k < W/4); lane l fills row
+//   loads: the wave fills 1 KB blocks i = w + 4k (k < W/4) of the part; lane l fills row
 //              (w + 4k) RPI + l / W, slot l % W, i.e. reads chunk (l % W) ^ swz(row) --
 //              the same chunk for every k, because 4 RPI rows is a multiple of 16.
 //   row reads (A operands): rows 32rh + 16rt + l16, chunk 4s + g.
@@ -133,11 +123,11 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
   using TY = RowTile<WY>;
   constexpr int OQM = 0, OQR = TM::BYTES, OY = OQR + (DR > 0 ? TR::BYTES : 0);
   constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = ORW + 256;  // stage: QM, QR, Y, lse2, drow
-  constexpr int NLD = DM / 32 + DR / 32 + DV / 32 + 2;                // transfers per wave per stage
   constexpr int NACC = 2 * (NQ + NV);
-  static_assert(3 * SB <= 160 * 1024, "three stages must fit in LDS");
-  static_assert(2 * NACC * 1024 + 64 * (DQK + DV) * 2 <= 3 * SB, "epilogue buffers must fit");
-  __shared__ __attribute__((aligned(1024))) char smem[3 * SB];
+  constexpr int EPI = 2 * NACC * 1024 + 64 * (DQK + DV) * 2;           // epilogue buffers
+  constexpr int SMEM = 2 * SB > EPI ? 2 * SB : EPI;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -214,36 +204,48 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
   const uint32_t smem_lds = lds_addr(smem);
   const uint32_t rs_m = (uint32_t)a.n1 * DM * 2, rs_r = (uint32_t)a.n1 * DR * 2, rs_y = (uint32_t)a.n1 * DV * 2;
 
-  // Transfers of one part: wave w's instructions k move rows (w + 4k) RPI + l / W.  Row
-  // addresses: the tile's first row (uniform) plus (row, clamped to the last valid row)
-  // times the token stride.
-  auto issue_part = [&](auto wtag, const auto& pl, const char* gtile, uint32_t rs, uint32_t lds_part, int nvalid) {
+  // Registers holding the next stage: W / 4 16-byte chunks per lane per part, plus one
+  // lse2 (wave 0) or drow (wave 1) value per lane (row = lane).
+  uint4 nm[WM / 4], nr[WR / 4], ny[WY / 4];
+  float nst = 0.f;
+  auto load_part = [&](auto wtag, const auto& pl, uint4* dst, const char* gtile, uint32_t rs, int nvalid) {
     constexpr int W = decltype(wtag)::value;
     constexpr int RPI = RowTile<W>::RPI;
-    static_for<W / 4>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
+#pragma unroll
+    for (int k = 0; k < W / 4; ++k) {
       const int r = min(pl.row0 + 4 * RPI * k, nvalid - 1);
-      dma16<4096 * k>(gtile + __umul24((uint32_t)r, rs) + pl.gchunk, lds_part + w * 1024);
-    });
+      dst[k] = ldg16(gtile + __umul24((uint32_t)r, rs) + pl.gchunk);
+    }
   };
-  auto issue = [&](int st, int soff) {
+  auto load_stage = [&](int st) {
     int hg, qt;
     step_tile(st, hg, qt);
-    const int h = kvh * a.G + hg;
     const int nvalid = min(kRows, S1 - qt * kRows);
-    const int64_t rh0 = (qs + (int64_t)qt * kRows) * a.n1 + h;  // (first row) * n1 + h
-    const uint32_t stage = smem_lds + soff;
-    issue_part(std::integral_constant<int, WM>{}, pm, reinterpret_cast<const char*>(a.q + rh0 * DM), rs_m,
-               stage + OQM, nvalid);
+    const int64_t rh0 = (qs + (int64_t)qt * kRows) * a.n1 + kvh * a.G + hg;  // (first row) * n1 + h
+    load_part(std::integral_constant<int, WM>{}, pm, nm, reinterpret_cast<const char*>(a.q + rh0 * DM), rs_m, nvalid);
     if constexpr (DR > 0)
-      issue_part(std::integral_constant<int, WR>{}, pr, reinterpret_cast<const char*>(a.q_rope + rh0 * DR), rs_r,
-                 stage + OQR, nvalid);
-    issue_part(std::integral_constant<int, WY>{}, py, reinterpret_cast<const char*>(a.dy + rh0 * DV), rs_y,
-               stage + OY, nvalid);
-    // lse2 / drow of rows 16w .. 16w+15 (lanes 0..15)
-    const int64_t lrow = rh0 + (int64_t)min(16 * w + l16, nvalid - 1) * a.n1;
-    if (lane < 16) dma4(a.lse2 + lrow, stage + OL + 64 * w);
-    if (lane < 16) dma4(a.drow + lrow, stage + ORW + 64 * w);
+      load_part(std::integral_constant<int, WR>{}, pr, nr, reinterpret_cast<const char*>(a.q_rope + rh0 * DR), rs_r,
+                nvalid);
+    load_part(std::integral_constant<int, WY>{}, py, ny, reinterpret_cast<const char*>(a.dy + rh0 * DV), rs_y, nvalid);
+    if (w < 2) {
+      const int64_t lrow = rh0 + (int64_t)min(lane, nvalid - 1) * a.n1;
+      nst = w == 0 ? a.lse2[lrow] : a.drow[lrow];
+    }
+  };
+  auto write_stage = [&](int soff) {
+    const uint32_t stage = smem_lds + soff;
+#pragma unroll
+    for (int k = 0; k < WM / 4; ++k)
+      lds_st16_at(stage + OQM + (w + 4 * k) * 1024 + 16 * lane, nm[k]);
+    if constexpr (DR > 0) {
+#pragma unroll
+      for (int k = 0; k < WR / 4; ++k)
+        lds_st16_at(stage + OQR + (w + 4 * k) * 1024 + 16 * lane, nr[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < WY / 4; ++k)
+      lds_st16_at(stage + OY + (w + 4 * k) * 1024 + 16 * lane, ny[k]);
+    if (w < 2) lds_st4_at(stage + OL + 256 * w + 4 * lane, nst);
   };
 
   // dS of the previous step, stored at the start of the next one (see the loop)
@@ -404,22 +406,22 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     }
   };
 
-  // Ordering of the vector-memory operations.  Iteration st: wait for stage st, barrier,
-  // store the dS of step st-1, issue the transfers of stage st+2, compute step st.  At
-  // the top of iteration st the operations issued after stage st's transfers are the
-  // stores of step st-2 and the transfers of stage st+1, in that order.  Loads complete
-  // in order, so "at most NLD outstanding" can only hold once stage st has landed,
-  // however the stores complete.
-  if (nsteps > 0) issue(0, 0);
-  if (nsteps > 1) issue(1, SB);
+  // Iteration st: barrier (stage st is written; stage st+1 is no longer read), store the
+  // dS of step st-1, load stage st+1 into registers, compute step st, then write the
+  // registers into stage st+1.  The loads have a whole step to arrive.
+  if (nsteps > 0) {
+    load_stage(0);
+    write_stage(0);
+  }
   for (int st = 0; st < nsteps; ++st) {
-    if (st + 1 < nsteps) wait_vmcnt<NLD>();
-    else wait_vmcnt<0>();
-    barrier_no_vm_wait();  // every wave's share of stage st is in LDS; stage st-1 is free
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    barrier_no_vm_wait();
     if (DS && st > 0) store_ds();
-    const int ph = st % 3;
-    if (st + 2 < nsteps) issue(st + 2, (ph == 0 ? 2 : ph - 1) * SB);
-    step(st, ph * SB);
+    const bool more = st + 1 < nsteps;
+    if (more) load_stage(st + 1);
+    asm volatile("" ::: "memory");  // keep the loads ahead of the step
+    step(st, (st & 1) * SB);
+    if (more) write_stage((~st & 1) * SB);
   }
   if (DS && nsteps > 0) store_ds();
 
