@@ -60,6 +60,73 @@ def flops_per_pair(w: W.Workload, gemms=("S", "dP", "dV", "dQ", "dK")) -> int:
     return 2 * sum(width[g] for g in gemms)
 
 
+# library timing name -> (kernel symbol prefix in profiler output, kernel source file)
+KERNEL_SOURCES = {
+    "dense_kv_major": ("dense_kv_kernel<", "dense_kv.hip"),
+    "dense_dq": ("dense_dq_ds_kernel<", "dense_dq.hip"),
+    "dense_dq_recompute": ("dense_dq_kernel<", "attn_q.hip"),
+    "selected_kv_major": ("kv_major_kernel<", "attn_kv.hip"),
+    "selected_dq_reduce": ("dq_reduce_kernel<", "attn_kv.hip"),
+    "row_stats": ("preprocess_kernel<", "preprocess.hip"),
+}
+CSRC = os.path.join(ROOT, "sparse_attention_backward_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash(name: str) -> str:
+    """sha256 over the kernel's source file and the shared headers it includes."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[name][1], "common.hpp", "kernels.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(name: str, workload: str):
+    """HBM bytes per launch recorded in profiles/traffic_<kernel>_<workload>.md (FETCH_SIZE + WRITE_SIZE,
+    each scaled by the copy-kernel calibration), or None when absent or taken from other kernel source."""
+    path = os.path.join(PROFILES, f"traffic_{name}_{workload}.md")
+    if not os.path.exists(path) or name not in KERNEL_SOURCES:
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != kernel_source_hash(name):
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_counters(dirs, calib_dir=None):
+    """Mean counter value per dispatch, per library kernel, from rocprofv3 --pmc CSV output directories;
+    with a copy-calibration directory also the FETCH_SIZE / WRITE_SIZE scale factors."""
+    import csv
+    import glob
+    out = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                kn = r["Kernel_Name"]
+                for lib_name, (prefix, _) in KERNEL_SOURCES.items():
+                    if prefix in kn:
+                        acc = out.setdefault(lib_name, {}).setdefault(r["Counter_Name"], [])
+                        acc.append(float(r["Counter_Value"]))
+    res = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in out.items()}
+    if calib_dir:
+        cal = {}
+        for f in glob.glob(os.path.join(calib_dir, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if "copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower():
+                    cal.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        res["_copy_calibration"] = {c: max(v) for c, v in cal.items()}
+    return res
+
+
 # kernel -> the GEMMs it performs (for its roofline point)
 KERNEL_GEMMS = {
     "dense_kv_major": ("S", "dP", "dV", "dK"),
@@ -198,12 +265,13 @@ def roofline_for(w: W.Workload, kernels: dict):
                 "frac": None, "traffic": None, "avg_ms": avg_ms}
     fl = pairs * flops_per_pair(w, gemms)
     achieved = fl / (avg_ms * 1e-3) / 1e12
+    traffic = recorded_traffic(name, w.name)
     if w.dtype == "fp32":
         return {"kernel": name, "bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": None, "avg_ms": avg_ms,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": traffic, "avg_ms": avg_ms,
                 "flop_per_launch": fl}
     return {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "avg_ms": avg_ms, "flop_per_launch": fl}
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "avg_ms": avg_ms, "flop_per_launch": fl}
 
 
 # ----------------------------------------------------------------------------
@@ -278,7 +346,18 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 5 times (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="print per-kernel mean counters of rocprofv3 --pmc output directories and exit "
+                         "(with --calibration DIR: also the copy kernel's FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--calibration", metavar="DIR")
+    ap.add_argument("--source-hash", metavar="KERNEL", help="print the kernel source hash used by traffic records")
     args = ap.parse_args(argv)
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters, args.calibration), indent=1))
+        return 0
+    if args.source_hash:
+        print(kernel_source_hash(args.source_hash))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
