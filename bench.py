@@ -65,7 +65,7 @@ KERNEL_SOURCES = {
     "dense_kv_major": ("dense_kv_kernel<", "dense_kv.hip"),
     "dense_dq": ("dense_dq_ds_kernel<", "dense_dq.hip"),
     "dense_dq_recompute": ("dense_dq_kernel<", "attn_q.hip"),
-    "selected_kv_major": ("kv_major_kernel<", "attn_kv.hip"),
+    "selected_kv_major": ("sel_kv_kernel<", "sel_kv.hip"),
     "selected_dq_reduce": ("dq_reduce_kernel<", "attn_kv.hip"),
     "row_stats": ("preprocess_kernel<", "preprocess.hip"),
 }

@@ -1,0 +1,503 @@
+// Selected (NSA) backward, KV-major: dK and dV of one selected block in registers, and the
+// block's share of dQ for every (token, slot) that selected it (bf16 MFMA, fp32
+// accumulation).
+//
+// Page "NsaSelectedAttentionGrad", formula section: each query token gathers
+// selectedBlockCount blocks of selectedBlockSize key / value rows through topkIndices
+// (selectedKey = Gather(key, topkIndices[i]), likewise for value), then the backward of
+// attention over the gathered rows: dV = P^T dY, dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
+// The gradient of a gather is a scatter-add onto the gathered rows; here it is formed
+// per block instead: the inverted index lists, for each (KV head, block), the (token,
+// slot) entries that selected it in ascending order, and one workgroup owns the block.
+//
+// One workgroup (4 waves) owns a block of up to 64 key rows of one KV head.  Query rows
+// stream past in steps of 64 rows = 64 / G listed entries x the G query heads of the KV
+// head.  The waves form a 2 x 2 grid as in the dense KV-major kernel: wave w owns keys
+// 32(w&1) .. +31 (K and V resident in registers) and rows 32(w>>1) .. +31 of every step.
+// Per step:
+//   S = Q K^T, dP = dY V^T, P = exp2(S*scale*log2e - lse2), dS = P (dP - drow)
+//   dV += P^T dY, dK += dS^T Q                       (registers, summed over all entries)
+//   dS^T -> LDS, then dQ_part^T = K^T dS^T over the block's keys (K staged in LDS once):
+//   every wave owns a quarter of the feature columns for all 64 rows, and each lane
+//   stores 4 consecutive features of one row (bf16) to dq_part[t, kvh, slot, head, :].
+// dq_reduce_kernel then sums the slots of each (token, KV head) in slot order.  Every
+// output row has one writer; no floating-point atomics: deterministic.
+//
+// Row staging as in the dense KV-major kernel: coalesced whole-row loads into registers
+// one step ahead, written to one of two swizzled LDS stages.  The list entries of a step
+// are read two steps ahead; lanes exchange row tokens with __shfl.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ab {
+
+namespace {
+
+constexpr int kRows = 64;  // query rows per step, key rows per workgroup (block_size <= 64)
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct SkvArgs {
+  const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* dy;
+  const float* lse2; const float* drow;
+  uint16_t* dk; uint16_t* dv;
+  uint16_t* dq_part;          // [T1, n2, cnt, G, DQK] bf16
+  const int64_t* cu_kv;
+  const int32_t* blkoff;      // [B+1] blocks before each sequence
+  const int32_t* offsets;     // inverted index: [n2 * nblk_total + 1]
+  const int32_t* list;        // entries t * cnt + slot, ascending per (KV head, block)
+  int batch, n1, n2, G, bs, cnt, nblk_total;
+  float scale, scale_log2e;
+};
+
+__device__ __forceinline__ void barrier_no_vm_wait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for_i(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_i<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
+}
+
+// Per-lane addressing of one staged part (RowTile of W chunks) for one wave; see the dense
+// KV-major kernel.  Rows of the part: step rows (row reads / column reads for dV, dK) or
+// key rows (column reads of the K tile for the dQ product).
+template <int W>
+struct PartLanes {
+  using T = RowTile<W>;
+  int row0;
+  uint32_t gchunk;
+  int rowA[W / 4];
+  int colB[W / 2];
+  __device__ __forceinline__ void init(int w, int lane, int rh) {
+    const int l16 = lane & 15, g = lane >> 4, jj = l16 >> 2, qq = l16 & 3;
+    row0 = w * T::RPI + lane / W;
+    gchunk = 16u * (uint32_t)((lane % W) ^ T::swz(row0));
+#pragma unroll
+    for (int s = 0; s < W / 4; ++s) rowA[s] = T::off(32 * rh + l16, 4 * s + g);
+#pragma unroll
+    for (int j = 0; j < W / 2; ++j) colB[j] = T::off(32 * rh + 4 * g + jj, 2 * j + (qq >> 1)) + 8 * (qq & 1);
+  }
+};
+
+template <int DM, int DR, int DV>
+__global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
+  constexpr int DQK = DM + DR;
+  constexpr int KS = DQK / 32, VS = DV / 32, NQ = DQK / 16, NV = DV / 16;
+  constexpr int KSM = DM / 32, NQM = DM / 16;
+  constexpr int WM = DM / 8, WR = DR > 0 ? DR / 8 : 8, WY = DV / 8;
+  constexpr int NFW = NQ / 4;  // dQ-part feature tiles per wave
+  using TM = RowTile<WM>;
+  using TR = RowTile<WR>;
+  using TY = RowTile<WY>;
+  using TD = RowTile<8>;       // dS^T tile: 64 keys x 64 rows
+  constexpr int OQM = 0, OQR = TM::BYTES, OY = OQR + (DR > 0 ? TR::BYTES : 0);
+  constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = ORW + 256;  // stage: QM, QR, Y, lse2, drow
+  constexpr int OKM = 2 * SB, OKR = OKM + TM::BYTES;                  // K tile (dQ product)
+  constexpr int ODS = OKR + (DR > 0 ? TR::BYTES : 0);                 // dS^T tile
+  constexpr int NACC = 2 * (NQ + NV);
+  constexpr int EPI = 2 * NACC * 1024 + 64 * (DQK + DV) * 2;
+  constexpr int MAIN = ODS + TD::BYTES;
+  constexpr int SMEM = MAIN > EPI ? MAIN : EPI;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = w & 1, rh = w >> 1;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  // ---- work unit: (KV head, block) and its list of entries -------------------------
+  const int u = blockIdx.x;
+  const int kvh = u / a.nblk_total;
+  const int rem = u - kvh * a.nblk_total;
+  const int b = seq_of32(a.blkoff, a.batch, rem);
+  const int64_t k0 = a.cu_kv[b] + (int64_t)(rem - a.blkoff[b]) * a.bs;
+  const int nk = a.bs;
+  const int e_begin = a.offsets[u], e_end = a.offsets[u + 1];
+  const int G = a.G, TPS = kRows / G;
+  const int nsteps = (e_end - e_begin + TPS - 1) / TPS;
+  const int hh_row = lane % G;  // head (within the group) of step row `lane`
+
+  // ---- resident keys: K and V as MFMA B operands; K also staged in LDS for dQ --------
+  bf16x8 Kf[2][KS], Vf[2][VS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int key = 32 * kh + 16 * t + l16;
+    const bool valid = key < nk;
+    const int64_t kr = (k0 + key) * a.n2 + kvh;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (valid) x = ldg16(a.k + kr * DQK + 32 * s + 8 * g);
+      Kf[t][s] = __builtin_bit_cast(bf16x8, x);
+    }
+#pragma unroll
+    for (int s = 0; s < VS; ++s) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (valid) x = ldg16(a.v + kr * DV + 32 * s + 8 * g);
+      Vf[t][s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  PartLanes<WM> pm;
+  PartLanes<WR> pr;
+  PartLanes<WY> py;
+  pm.init(w, lane, rh);
+  if constexpr (DR > 0) pr.init(w, lane, rh);
+  py.init(w, lane, rh);
+  const uint32_t smem_lds = lds_addr(smem);
+
+  // K tile in LDS (RowTile layout, key rows; keys past the block repeat its last key)
+  {
+    PartLanes<WM> km;
+    km.init(w, lane, 0);
+#pragma unroll
+    for (int kk = 0; kk < WM / 4; ++kk) {
+      const int r = min(km.row0 + 4 * TM::RPI * kk, nk - 1);
+      const uint4 x = ldg16(reinterpret_cast<const char*>(a.k + ((k0 + r) * a.n2 + kvh) * DQK) + km.gchunk);
+      lds_st16_at(smem_lds + OKM + (w + 4 * kk) * 1024 + 16 * lane, x);
+    }
+    if constexpr (DR > 0) {
+      PartLanes<WR> kr_;
+      kr_.init(w, lane, 0);
+#pragma unroll
+      for (int kk = 0; kk < WR / 4; ++kk) {
+        const int r = min(kr_.row0 + 4 * TR::RPI * kk, nk - 1);
+        const uint4 x =
+            ldg16(reinterpret_cast<const char*>(a.k + ((k0 + r) * a.n2 + kvh) * DQK + DM) + kr_.gchunk);
+        lds_st16_at(smem_lds + OKR + (w + 4 * kk) * 1024 + 16 * lane, x);
+      }
+    }
+  }
+  // K^T column reads for the dQ product: wave w's feature tiles ft = NFW w + f, keys
+  // {4g + jj, 16 + 4g + jj} + 32 ks; dS^T column reads: rows 16 rt + .., same keys
+  uint32_t kcol[NFW][2][2];
+  {
+    PartLanes<WM> km;
+    km.init(0, lane, 0);
+    PartLanes<WR> kr_;
+    if constexpr (DR > 0) kr_.init(0, lane, 0);
+    auto tile_base = [&](auto ftc) -> int {
+      constexpr int ft = decltype(ftc)::value;
+      if constexpr (ft < NQM) return OKM + km.colB[ft];
+      else return OKR + kr_.colB[ft - NQM];
+    };
+    static_for_i<NFW>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      int base = 0, rb = 0;
+      static_for_i<4>([&](auto wc) {  // pick wave w's tile with compile-time indices only
+        constexpr int ww = decltype(wc)::value;
+        constexpr int ft = NFW * ww + f;
+        if (w == ww) { base = tile_base(std::integral_constant<int, ft>{}); rb = ft < NQM ? TM::RB : TR::RB; }
+      });
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        kcol[f][ks2][0] = base + ks2 * 32 * rb;
+        kcol[f][ks2][1] = base + ks2 * 32 * rb + 16 * rb;
+      }
+    });
+  }
+  int dscol[4];
+  {
+    const int jj = l16 >> 2, qq = l16 & 3;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) dscol[rt] = ODS + TD::off(4 * g + jj, 2 * rt + (qq >> 1)) + 8 * (qq & 1);
+  }
+
+  f32x4 dK[2][NQ], dV[2][NV];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) dK[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < NV; ++n) dV[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- list entries: row `lane` of step st is entry e_begin + st * TPS + lane / G ------
+  auto entry_of = [&](int st) -> int {
+    const int ei = e_begin + st * TPS + lane / G;
+    return ei < e_end ? a.list[ei] : -1;
+  };
+  const int first_entry = e_begin < e_end ? a.list[e_begin] : 0;  // stands in for missing rows
+
+  // ---- staging: registers for the next stage ------------------------------------------
+  uint4 nm[WM / 4], nr[WR / 4], ny[WY / 4];
+  float nst = 0.f;
+  const int64_t hrow = (int64_t)kvh * G;  // first query head of the group
+  auto load_stage = [&](int ent) {  // ent: this lane's entry for its row (row = lane) of the step
+    const int tok_lane = (ent >= 0 ? ent : first_entry) / a.cnt;
+    // element offset of (row r of the step) in a [T1, n1, D] tensor, without the D factor
+    auto row_index = [&](int r) -> int64_t { return (int64_t)__shfl(tok_lane, r) * a.n1 + hrow + r % G; };
+#pragma unroll
+    for (int kk = 0; kk < WM / 4; ++kk)
+      nm[kk] = ldg16(reinterpret_cast<const char*>(a.q + row_index(pm.row0 + 4 * TM::RPI * kk) * DQK) + pm.gchunk);
+    if constexpr (DR > 0) {
+#pragma unroll
+      for (int kk = 0; kk < WR / 4; ++kk)
+        nr[kk] = ldg16(reinterpret_cast<const char*>(a.q + row_index(pr.row0 + 4 * TR::RPI * kk) * DQK + DM) + pr.gchunk);
+    }
+#pragma unroll
+    for (int kk = 0; kk < WY / 4; ++kk)
+      ny[kk] = ldg16(reinterpret_cast<const char*>(a.dy + row_index(py.row0 + 4 * TY::RPI * kk) * DV) + py.gchunk);
+    if (w < 2) {
+      const int64_t row = (int64_t)tok_lane * a.n1 + hrow + hh_row;
+      nst = ent < 0 ? (w == 0 ? INFINITY : 0.f) : (w == 0 ? a.lse2[row] : a.drow[row]);
+    }
+  };
+  auto write_stage = [&](int soff) {
+    const uint32_t stage = smem_lds + soff;
+#pragma unroll
+    for (int kk = 0; kk < WM / 4; ++kk) lds_st16_at(stage + OQM + (w + 4 * kk) * 1024 + 16 * lane, nm[kk]);
+    if constexpr (DR > 0) {
+#pragma unroll
+      for (int kk = 0; kk < WR / 4; ++kk) lds_st16_at(stage + OQR + (w + 4 * kk) * 1024 + 16 * lane, nr[kk]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < WY / 4; ++kk) lds_st16_at(stage + OY + (w + 4 * kk) * 1024 + 16 * lane, ny[kk]);
+    if (w < 2) lds_st4_at(stage + OL + 256 * w + 4 * lane, nst);
+  };
+
+  // ---- one step ------------------------------------------------------------------------
+  auto step = [&](int soff, int ent_cur) {
+    const uint32_t stage = smem_lds + soff;
+    const uint32_t statb = opaque(stage + OL + 4 * (32 * rh + 4 * g));  // lse2; drow at + 256
+    f32x4 lse[2], dr[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      lse[rt] = lds_f32x4_at(statb + 64 * rt);
+      dr[rt] = lds_f32x4_at(statb + 256 + 64 * rt);
+    }
+    constexpr int NS = KS + VS, PA = 3;
+    auto afrag = [&](int s, int rt) -> bf16x8 {
+      if (s < KSM) return lds_b128_at(stage + OQM + pm.rowA[s] + rt * 16 * TM::RB);
+      if (s < KS) return lds_b128_at(stage + OQR + pr.rowA[s - KSM] + rt * 16 * TR::RB);
+      return lds_b128_at(stage + OY + py.rowA[s - KS] + rt * 16 * TY::RB);
+    };
+    bf16x8 aring[PA][2];
+#pragma unroll
+    for (int i = 0; i < PA; ++i) { aring[i][0] = afrag(i, 0); aring[i][1] = afrag(i, 1); }
+    f32x4 S[2][2], D[2][2];  // [key tile][row tile]
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 a0 = aring[s % PA][0], a1 = aring[s % PA][1];
+      if (s + PA < NS) { aring[s % PA][0] = afrag(s + PA, 0); aring[s % PA][1] = afrag(s + PA, 1); }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (s < KS) {
+          S[t][0] = mfma_16x16x32(a0, Kf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][0]);
+          S[t][1] = mfma_16x16x32(a1, Kf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][1]);
+        } else {
+          D[t][0] = mfma_16x16x32(a0, Vf[t][s - KS], s == KS ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t][0]);
+          D[t][1] = mfma_16x16x32(a1, Vf[t][s - KS], s == KS ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t][1]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PA, 0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (s + PA < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    // P (keys past the block -> 0), then dS in place
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bool kvalid = 32 * kh + 16 * t + l16 < nk;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(S[t][rt][i] * a.scale_log2e - lse[rt][i]);
+          S[t][rt][i] = kvalid ? p : 0.f;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) D[t][rt][i] = S[t][rt][i] * (D[t][rt][i] - dr[rt][i]);
+    bf16x8 pa[2], da[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      pa[t] = pack8(S[t][0], S[t][1]);
+      da[t] = pack8(D[t][0], D[t][1]);
+      // dS^T tile: key 32kh + 16t + l16, rows 32rh + 4g + (0..3) and + 16 (8-byte writes)
+      const i16x8 d8 = __builtin_bit_cast(i16x8, da[t]);
+      const int key = 32 * kh + 16 * t + l16;
+      const int r0 = 32 * rh + 4 * g;
+      const uint32_t o0 = smem_lds + ODS + TD::off(key, r0 >> 3) + 2 * (r0 & 7);
+      const uint32_t o1 = smem_lds + ODS + TD::off(key, (r0 + 16) >> 3) + 2 * ((r0 + 16) & 7);
+      *reinterpret_cast<__attribute__((address_space(3))) i16x4*>((uintptr_t)o0) = i16x4{d8[0], d8[1], d8[2], d8[3]};
+      *reinterpret_cast<__attribute__((address_space(3))) i16x4*>((uintptr_t)o1) = i16x4{d8[4], d8[5], d8[6], d8[7]};
+    }
+    // dV += P^T dY, dK += dS^T Q
+    auto colfrag = [&](int j) -> bf16x8 {
+      uint32_t o, second;
+      if (j < NV) { o = stage + OY + py.colB[j]; second = 16 * TY::RB; }
+      else if (j < NV + NQM) { o = stage + OQM + pm.colB[j - NV]; second = 16 * TM::RB; }
+      else { o = stage + OQR + pr.colB[j - NV - NQM]; second = 16 * TR::RB; }
+      return join8(lds_tr16_at(o), lds_tr16_at(o + second));
+    };
+    constexpr int NJ = NV + NQ, PD = 4;
+    bf16x8 ring[PD];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) ring[i] = colfrag(i);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const bf16x8 bj = ring[j % PD];
+      if (j + PD < NJ) ring[j % PD] = colfrag(j + PD);
+      if (j < NV) {
+        dV[0][j] = mfma_16x16x32(pa[0], bj, dV[0][j]);
+        dV[1][j] = mfma_16x16x32(pa[1], bj, dV[1][j]);
+      } else {
+        dK[0][j - NV] = mfma_16x16x32(da[0], bj, dK[0][j - NV]);
+        dK[1][j - NV] = mfma_16x16x32(da[1], bj, dK[1][j - NV]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      if (j + PD < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+
+    // ---- dQ part: dQ_part^T (features x rows) = K^T dS^T over the 64 keys ------------
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's dS^T writes are done
+    barrier_no_vm_wait();                // every wave's dS^T is in LDS
+    f32x4 acc[NFW][4];
+#pragma unroll
+    for (int f = 0; f < NFW; ++f)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[f][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      bf16x8 kt[NFW], dt[4];
+#pragma unroll
+      for (int f = 0; f < NFW; ++f)
+        kt[f] = join8(lds_tr16_at(smem_lds + kcol[f][ks2][0]), lds_tr16_at(smem_lds + kcol[f][ks2][1]));
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const uint32_t o = smem_lds + dscol[rt] + ks2 * 32 * TD::RB;
+        dt[rt] = join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB));
+      }
+#pragma unroll
+      for (int f = 0; f < NFW; ++f)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[f][rt] = mfma_16x16x32(kt[f], dt[rt], acc[f][rt]);
+    }
+    // C tile (f, rt): lane holds row 16 rt + l16, features 16 (NFW w + f) + 4g .. +3
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int r = 16 * rt + l16;
+      const int ent = __shfl(ent_cur, r);
+      if (ent >= 0) {
+        const int t = ent / a.cnt, sl = ent - t * a.cnt;
+        uint16_t* dst = a.dq_part + ((((int64_t)t * a.n2 + kvh) * a.cnt + sl) * G + r % G) * DQK + 4 * g;
+#pragma unroll
+        for (int f = 0; f < NFW; ++f)
+          *reinterpret_cast<i16x4*>(dst + 16 * (NFW * w + f)) = pack4(acc[f][rt]);
+      }
+    }
+  };
+
+  // ---- step loop -----------------------------------------------------------------------
+  // Iteration st: barrier (stage st written; stage st+1 and the dS^T tile free), load stage
+  // st+1 into registers (its entries were read at iteration st-1), read the entries of step
+  // st+2, compute step st, write the registers into stage st+1.
+  int ent_cur = entry_of(0);
+  int ent_nx = nsteps > 1 ? entry_of(1) : -1;
+  __syncthreads();  // K tile in LDS
+  if (nsteps > 0) {
+    load_stage(ent_cur);
+    write_stage(0);
+  }
+  for (int st = 0; st < nsteps; ++st) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    barrier_no_vm_wait();
+    const bool more = st + 1 < nsteps;
+    if (more) load_stage(ent_nx);
+    const int ent_nx2 = st + 2 < nsteps ? entry_of(st + 2) : -1;
+    asm volatile("" ::: "memory");  // keep the loads ahead of the step
+    step((st & 1) * SB, ent_cur);
+    if (more) write_stage((~st & 1) * SB);
+    ent_cur = ent_nx;
+    ent_nx = ent_nx2;
+  }
+
+  // ---- epilogue: sum the two row halves, bf16 through LDS, 16-byte stores ------------
+  __syncthreads();
+  f32x4* part = reinterpret_cast<f32x4*>(smem);
+  if (rh == 1) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane] = dK[t][n];
+#pragma unroll
+      for (int n = 0; n < NV; ++n) part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane] = dV[t][n];
+    }
+  }
+  __syncthreads();
+  uint16_t* Ko = reinterpret_cast<uint16_t*>(smem + 2 * NACC * 1024);
+  uint16_t* Vo = Ko + 64 * DQK;
+  if (rh == 0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        const f32x4 o = part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Ko[(32 * kh + 16 * t + 4 * g + i) * DQK + 16 * n + l16] = f2bf((dK[t][n][i] + o[i]) * a.scale);
+      }
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        const f32x4 o = part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Vo[(32 * kh + 16 * t + 4 * g + i) * DV + 16 * n + l16] = f2bf(dV[t][n][i] + o[i]);
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int QCH = DQK / 8, YCH = DV / 8;
+  for (int idx = tid; idx < kRows * QCH; idx += 256) {
+    const int r = idx / QCH, c = idx - r * QCH;
+    if (r < nk) sts16(a.dk + ((k0 + r) * a.n2 + kvh) * DQK + 8 * c, *reinterpret_cast<const uint4*>(Ko + r * DQK + 8 * c));
+  }
+  for (int idx = tid; idx < kRows * YCH; idx += 256) {
+    const int r = idx / YCH, c = idx - r * YCH;
+    if (r < nk) sts16(a.dv + ((k0 + r) * a.n2 + kvh) * DV + 8 * c, *reinterpret_cast<const uint4*>(Vo + r * DV + 8 * c));
+  }
+}
+
+}  // namespace
+
+bool selected_kv64_supported(int d_qk, int d_v, int G, int bs) {
+  return (d_qk == 192 || d_qk == 128) && d_v == 128 && bs <= kRows && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+}
+
+hipError_t launch_selected_kv64(const SelArgs& a, hipStream_t s) {
+  SkvArgs k{};
+  k.q = (const uint16_t*)a.q; k.k = (const uint16_t*)a.k; k.v = (const uint16_t*)a.v; k.dy = (const uint16_t*)a.dy;
+  k.lse2 = a.lse2; k.drow = a.drow;
+  k.dk = (uint16_t*)a.dk; k.dv = (uint16_t*)a.dv; k.dq_part = (uint16_t*)a.dq_part;
+  k.cu_kv = a.cu_kv; k.blkoff = a.blkoff; k.offsets = a.offsets; k.list = a.list;
+  k.batch = a.batch; k.n1 = a.n1; k.n2 = a.n2; k.G = a.G; k.bs = a.bs; k.cnt = a.cnt; k.nblk_total = a.nblk_total;
+  k.scale = a.scale; k.scale_log2e = a.scale_log2e;
+  const dim3 grid((unsigned)(a.n2 * a.nblk_total));
+  if (grid.x == 0) return hipSuccess;
+  if (a.d_qk == 192 && a.d_v == 128) hipLaunchKernelGGL((sel_kv_kernel<128, 64, 128>), grid, dim3(256), 0, s, k);
+  else if (a.d_qk == 128 && a.d_v == 128) hipLaunchKernelGGL((sel_kv_kernel<128, 0, 128>), grid, dim3(256), 0, s, k);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace ab
