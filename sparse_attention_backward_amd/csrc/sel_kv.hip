@@ -18,8 +18,8 @@
 //   S = Q K^T, dP = dY V^T, P = exp2(S*scale*log2e - lse2), dS = P (dP - drow)
 //   dV += P^T dY, dK += dS^T Q                       (registers, summed over all entries)
 //   dS^T -> LDS, then dQ_part^T = K^T dS^T over the block's keys (K staged in LDS once):
-//   every wave owns a quarter of the feature columns for all 64 rows, and each lane
-//   stores 4 consecutive features of one row (bf16) to dq_part[t, kvh, slot, head, :].
+//   every wave owns half of the feature columns for 32 rows, and each lane stores 8
+//   consecutive features of one row (bf16, 16 bytes) to dq_part[t, kvh, slot, head, :].
 // dq_reduce_kernel then sums the slots of each (token, KV head) in slot order.  Every
 // output row has one writer; no floating-point atomics: deterministic.
 //
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   constexpr int KS = DQK / 32, VS = DV / 32, NQ = DQK / 16, NV = DV / 16;
   constexpr int KSM = DM / 32, NQM = DM / 16;
   constexpr int WM = DM / 8, WR = DR > 0 ? DR / 8 : 8, WY = DV / 8;
-  constexpr int NFW = NQ / 4;  // dQ-part feature tiles per wave
+  constexpr int NFH = NQ / 2;  // dQ-part feature tiles per wave (half of the features)
   using TM = RowTile<WM>;
   using TR = RowTile<WR>;
   using TY = RowTile<WY>;
@@ -178,26 +178,25 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
       }
     }
   }
-  // K^T column reads for the dQ product: wave w's feature tiles ft = NFW w + f, keys
-  // {4g + jj, 16 + 4g + jj} + 32 ks; dS^T column reads: rows 16 rt + .., same keys
-  uint32_t kcol[NFW][2][2];
+  // dQ product split: wave w owns feature half fh = w & 1 and rows 32 rh .. +31 of the
+  // step.  Its NFH feature tiles are permuted: in C tile f, lane group g holds features
+  // F0(f) + 8 g + 4 (f % 2) + (0..3) with F0(f) = fh DQK/2 + 32 (f / 2), so the tile pair
+  // (2j, 2j+1) gives each lane 8 consecutive features (one 16-byte store) and the four
+  // lane groups of a row cover 64 consecutive bytes.  The K^T column reads follow the
+  // permutation: 4-feature chunk qq of tile f starts at feature F0(f) + 8 qq + 4 (f % 2).
+  const int fh = w & 1;
+  uint32_t kcol[NFH][2][2];
   {
-    PartLanes<WM> km;
-    km.init(0, lane, 0);
-    PartLanes<WR> kr_;
-    if constexpr (DR > 0) kr_.init(0, lane, 0);
-    auto tile_base = [&](auto ftc) -> int {
-      constexpr int ft = decltype(ftc)::value;
-      if constexpr (ft < NQM) return OKM + km.colB[ft];
-      else return OKR + kr_.colB[ft - NQM];
-    };
-    static_for_i<NFW>([&](auto fc) {
+    const int jj = l16 >> 2, qq = l16 & 3;
+    static_for_i<NFH>([&](auto fc) {
       constexpr int f = decltype(fc)::value;
       int base = 0, rb = 0;
-      static_for_i<4>([&](auto wc) {  // pick wave w's tile with compile-time indices only
-        constexpr int ww = decltype(wc)::value;
-        constexpr int ft = NFW * ww + f;
-        if (w == ww) { base = tile_base(std::integral_constant<int, ft>{}); rb = ft < NQM ? TM::RB : TR::RB; }
+      static_for_i<2>([&](auto hc) {  // the feature half with compile-time tile choice
+        constexpr int F0 = decltype(hc)::value * (DQK / 2) + 32 * (f / 2);
+        if (fh == decltype(hc)::value) {
+          if constexpr (F0 < DM) { base = OKM + TM::off(4 * g + jj, F0 / 8 + qq) + 8 * (f % 2); rb = TM::RB; }
+          else { base = OKR + TR::off(4 * g + jj, (F0 - DM) / 8 + qq) + 8 * (f % 2); rb = TR::RB; }
+        }
       });
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
@@ -206,11 +205,11 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
       }
     });
   }
-  int dscol[4];
+  int dscol[2];
   {
     const int jj = l16 >> 2, qq = l16 & 3;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) dscol[rt] = ODS + TD::off(4 * g + jj, 2 * rt + (qq >> 1)) + 8 * (qq & 1);
+    for (int rr = 0; rr < 2; ++rr) dscol[rr] = ODS + TD::off(4 * g + jj, 2 * (2 * rh + rr) + (qq >> 1)) + 8 * (qq & 1);
   }
 
   f32x4 dK[2][NQ], dV[2][NV];
@@ -373,38 +372,38 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     // ---- dQ part: dQ_part^T (features x rows) = K^T dS^T over the 64 keys ------------
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's dS^T writes are done
     barrier_no_vm_wait();                // every wave's dS^T is in LDS
-    f32x4 acc[NFW][4];
+    f32x4 acc[NFH][2];
 #pragma unroll
-    for (int f = 0; f < NFW; ++f)
+    for (int f = 0; f < NFH; ++f)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[f][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rr = 0; rr < 2; ++rr) acc[f][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      bf16x8 kt[NFW], dt[4];
+      bf16x8 kt[NFH], dt[2];
 #pragma unroll
-      for (int f = 0; f < NFW; ++f)
+      for (int f = 0; f < NFH; ++f)
         kt[f] = join8(lds_tr16_at(smem_lds + kcol[f][ks2][0]), lds_tr16_at(smem_lds + kcol[f][ks2][1]));
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const uint32_t o = smem_lds + dscol[rt] + ks2 * 32 * TD::RB;
-        dt[rt] = join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB));
+      for (int rr = 0; rr < 2; ++rr) {
+        const uint32_t o = smem_lds + dscol[rr] + ks2 * 32 * TD::RB;
+        dt[rr] = join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB));
       }
 #pragma unroll
-      for (int f = 0; f < NFW; ++f)
+      for (int f = 0; f < NFH; ++f)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[f][rt] = mfma_16x16x32(kt[f], dt[rt], acc[f][rt]);
+        for (int rr = 0; rr < 2; ++rr) acc[f][rr] = mfma_16x16x32(kt[f], dt[rr], acc[f][rr]);
     }
-    // C tile (f, rt): lane holds row 16 rt + l16, features 16 (NFW w + f) + 4g .. +3
+    // C tile (f, rr): lane holds row 32 rh + 16 rr + l16 and the permuted features above
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int r = 16 * rt + l16;
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = 32 * rh + 16 * rr + l16;
       const int ent = __shfl(ent_cur, r);
       if (ent >= 0) {
         const int t = ent / a.cnt, sl = ent - t * a.cnt;
-        uint16_t* dst = a.dq_part + ((((int64_t)t * a.n2 + kvh) * a.cnt + sl) * G + r % G) * DQK + 4 * g;
+        uint16_t* dst = a.dq_part + ((((int64_t)t * a.n2 + kvh) * a.cnt + sl) * G + r % G) * DQK + fh * (DQK / 2) + 8 * g;
 #pragma unroll
-        for (int f = 0; f < NFW; ++f)
-          *reinterpret_cast<i16x4*>(dst + 16 * (NFW * w + f)) = pack4(acc[f][rt]);
+        for (int j = 0; j < NFH / 2; ++j)
+          *reinterpret_cast<bf16x8*>(dst + 32 * j) = pack8(acc[2 * j][rr], acc[2 * j + 1][rr]);
       }
     }
   };
