@@ -71,13 +71,14 @@ def stats_tensor(m, l):
 # Dense varlen form
 # ----------------------------------------------------------------------------
 
-def _causal_mask(n_q, n_k, causal):
-    """Visible[i, j]: query position i sees key position j of the same sequence."""
-    vis = np.ones((n_q, n_k), dtype=bool)
+def _causal_mask(qpos, n_q, n_k, causal):
+    """Visible[i, j]: the query at local position qpos[i] (of a sequence with n_q
+    queries) sees key position j of the same sequence."""
+    vis = np.ones((len(qpos), n_k), dtype=bool)
     if causal:
         if n_q != n_k:
             raise ValueError("causal attention needs equal query and KV lengths per sequence")
-        vis = np.tril(vis)
+        vis = np.arange(n_k)[None, :] <= np.asarray(qpos)[:, None]
     return vis
 
 
@@ -93,24 +94,35 @@ def _softmax_rows(S, vis):
     return P, m, l
 
 
-def _dense_blocks(cu_q, cu_kv, n1, n2):
-    """(q slice, kv slice, query head, KV head) for every sequence and query head."""
+def _dense_blocks(cu_q, cu_kv, n1, n2, causal, tokens=None):
+    """(query rows, kv slice, visibility mask, query head, KV head) for every
+    sequence and query head.  The query rows are the whole sequence, or only the
+    listed ``tokens`` that fall in it (ascending)."""
     G = n1 // n2
+    toks = None if tokens is None else np.unique(np.asarray(tokens, dtype=np.int64))
     for b in range(len(cu_q) - 1):
         qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_kv[b]), int(cu_kv[b + 1])
-        if qe == qs or ke == ks:
+        if toks is None:
+            rows = slice(qs, qe)
+            qpos = np.arange(qe - qs)
+        else:
+            rows = toks[(toks >= qs) & (toks < qe)]
+            qpos = rows - qs
+        if len(qpos) == 0 or ke == ks:
             continue
+        vis = _causal_mask(qpos, qe - qs, ke - ks, causal)
         for h in range(n1):
-            yield slice(qs, qe), slice(ks, ke), h, h // G
+            yield rows, slice(ks, ke), vis, h, h // G
 
 
 def forward_dense(query, key, value, cu_q, cu_kv, n1, n2, scale, causal,
-                  query_rope=None, key_rope=None):
+                  query_rope=None, key_rope=None, tokens=None):
     """Forward of the dense page's Formula section, one (sequence, head) at a time:
     S = Mask(Q K^T * scale), P = Softmax(S), Y = P V.
 
     Returns O [T1, N1, Dv], m [T1, N1], l [T1, N1] (float64).  Rows without a
-    visible key get O = 0, m = -inf, l = 0.
+    visible key get O = 0, m = -inf, l = 0.  ``tokens`` restricts the work to
+    those query tokens (the other rows are left as rows without a visible key).
     """
     Q = _cat_rope(query, query_rope)
     K = _cat_rope(key, key_rope)
@@ -119,20 +131,18 @@ def forward_dense(query, key, value, cu_q, cu_kv, n1, n2, scale, causal,
     O = np.zeros((T1, n1, V.shape[-1]))
     m = np.full((T1, n1), -np.inf)
     l = np.zeros((T1, n1))
-    for qsl, ksl, h, kvh in _dense_blocks(cu_q, cu_kv, n1, n2):
-        vis = _causal_mask(qsl.stop - qsl.start, ksl.stop - ksl.start, causal)
+    for qsl, ksl, vis, h, kvh in _dense_blocks(cu_q, cu_kv, n1, n2, causal, tokens):
         S = scale * (Q[qsl, h, :] @ K[ksl, kvh, :].T)
         P, m[qsl, h], l[qsl, h] = _softmax_rows(S, vis)
         O[qsl, h] = P @ V[ksl, kvh, :]
     return O, m, l
 
 
-def _dense_backward_core(Q, K, V, dY, cu_q, cu_kv, n1, n2, scale, causal, probs_and_D):
+def _dense_backward_core(Q, K, V, dY, cu_q, cu_kv, n1, n2, scale, causal, probs_and_D, tokens=None):
     dQ = np.zeros_like(Q)
     dK = np.zeros((K.shape[0], n2, K.shape[-1]))
     dV = np.zeros((V.shape[0], n2, V.shape[-1]))
-    for qsl, ksl, h, kvh in _dense_blocks(cu_q, cu_kv, n1, n2):
-        vis = _causal_mask(qsl.stop - qsl.start, ksl.stop - ksl.start, causal)
+    for qsl, ksl, vis, h, kvh in _dense_blocks(cu_q, cu_kv, n1, n2, causal, tokens):
         S = scale * (Q[qsl, h, :] @ K[ksl, kvh, :].T)
         dP = dY[qsl, h, :] @ V[ksl, kvh, :].T                    # dP = dY V^T
         P, D = probs_and_D(S, vis, dP, qsl, h)
@@ -148,11 +158,12 @@ def _split(x, d_main):
 
 
 def backward_dense(query, key, value, dy, cu_q, cu_kv, n1, n2, scale, causal,
-                   query_rope=None, key_rope=None):
+                   query_rope=None, key_rope=None, tokens=None):
     """Exact gradient for the dense form (P recomputed from the scores).
 
     Returns dq, dq_rope, dk, dk_rope, dv (float64; the rope parts have 0 columns
-    when no rope tensors are given).
+    when no rope tensors are given).  With ``tokens`` given, dQ rows of other
+    tokens stay 0 and dK / dV hold only the contributions of the listed tokens.
     """
     Q = _cat_rope(query, query_rope)
     K = _cat_rope(key, key_rope)
@@ -162,7 +173,7 @@ def backward_dense(query, key, value, dy, cu_q, cu_kv, n1, n2, scale, causal,
         P, _, _ = _softmax_rows(S, vis)
         return P, (P * dP).sum(axis=1)                           # D = sum_j P_j dP_j
 
-    dQ, dK, dV = _dense_backward_core(Q, K, V, dY, cu_q, cu_kv, n1, n2, scale, causal, exact)
+    dQ, dK, dV = _dense_backward_core(Q, K, V, dY, cu_q, cu_kv, n1, n2, scale, causal, exact, tokens)
     d_main = np.asarray(query).shape[-1]
     dq, dq_rope = _split(dQ, d_main)
     dk, dk_rope = _split(dK, d_main)
@@ -171,7 +182,7 @@ def backward_dense(query, key, value, dy, cu_q, cu_kv, n1, n2, scale, causal,
 
 def backward_dense_from_stats(query, key, value, out, dy, softmax_max, softmax_sum,
                               cu_q, cu_kv, n1, n2, scale, causal,
-                              query_rope=None, key_rope=None):
+                              query_rope=None, key_rope=None, tokens=None):
     """Diagnostic variant consuming the passed statistics and O:
     P = exp(s - m) / l from lane 0 of the stats, D = rowsum(dY * O)."""
     Q = _cat_rope(query, query_rope)
@@ -184,7 +195,7 @@ def backward_dense_from_stats(query, key, value, out, dy, softmax_max, softmax_s
         P = np.where(vis, np.exp(np.where(vis, S, 0.0) - m[qsl, h][:, None]), 0.0) / l[qsl, h][:, None]
         return P, (dY[qsl, h] * O[qsl, h]).sum(axis=1)
 
-    dQ, dK, dV = _dense_backward_core(Q, K, V, dY, cu_q, cu_kv, n1, n2, scale, causal, consume)
+    dQ, dK, dV = _dense_backward_core(Q, K, V, dY, cu_q, cu_kv, n1, n2, scale, causal, consume, tokens)
     d_main = np.asarray(query).shape[-1]
     dq, dq_rope = _split(dQ, d_main)
     dk, dk_rope = _split(dK, d_main)
@@ -256,8 +267,10 @@ def _selected_backward_core(Q, K, V, dY, topk, cu_q, cu_kv, n1, n2, scale, block
     G = n1 // n2
     seq = _seq_of_tokens(cu_q, T1)
     dQ = np.zeros_like(Q)
-    dK = np.zeros((K.shape[0], n2, K.shape[-1]))
-    dV = np.zeros((V.shape[0], n2, V.shape[-1]))
+    # written in full up front: the scatter below first-touches rows in random order,
+    # which is far slower than one sequential pass over a large array
+    dK = np.full((K.shape[0], n2, K.shape[-1]), 0.0)
+    dV = np.full((V.shape[0], n2, V.shape[-1]), 0.0)
     for t in _token_list(tokens, T1):
         ks = int(cu_kv[seq[t]])
         for kvh in range(n2):

@@ -1,0 +1,164 @@
+"""GPU parity at the full sizes of the benchmark workloads, in the launch
+configuration the benchmark times (same problem struct, same entry points, one
+workspace from the size query).
+
+The float64 oracle cannot run a whole full-size problem in seconds, so the test
+samples query tokens, and makes every other row inert instead of leaving it out:
+
+* a seeded sample of query tokens gets real O and softmax statistics from the
+  oracle forward;
+* every other row gets O = 0, softmaxSum = 1 and a softmaxMax far above every
+  score, so its probabilities exp(s - max) / sum are exactly 0, its
+  rowsum(dY * O) is 0, hence its dS is 0: the row contributes nothing anywhere.
+
+The GPU still runs the complete problem (every token, tile and list entry, the
+full inverted index and every kernel at its real grid), and must give
+* dQ of the sampled tokens equal to the oracle's (bf16 tolerances);
+* dQ of every other token exactly 0;
+* dK and dV, all rows, equal to the oracle's gradient restricted to the sampled
+  tokens (``tokens=`` mode of the oracle; the test suite pins that mode and this
+  inert-row construction against full oracle runs on small problems).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_attention_backward_amd as sab
+import workloads as W
+from helpers import assert_close, f64
+
+pytestmark = pytest.mark.gpu
+
+INERT_MAX = 3.0e4
+
+
+def _say(*a):
+    print("[fullsize]", *a, flush=True)
+
+
+def _sample_tokens(w, n):
+    rng = np.random.default_rng(1000 + w.seed)
+    return np.sort(rng.choice(w.T1, size=min(n, w.T1), replace=False)).astype(np.int64)
+
+
+def _inert_inputs(w, dev, toks, o_sub, m_sub, l_sub):
+    """O and the [T1, N1, 8] statistics: oracle values on the sampled rows, inert elsewhere."""
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    o = torch.zeros((w.T1, w.n1, w.d_v), dtype=dt, device=dev)
+    m = torch.full((w.T1, w.n1), INERT_MAX, dtype=torch.float32, device=dev)
+    l = torch.ones((w.T1, w.n1), dtype=torch.float32, device=dev)
+    idx = torch.from_numpy(toks).to(dev)
+    o[idx] = W.cast(o_sub, w.dtype).to(dev)
+    m[idx] = torch.from_numpy(np.asarray(m_sub, dtype=np.float64).astype(np.float32)).to(dev)
+    l[idx] = torch.from_numpy(np.asarray(l_sub, dtype=np.float64).astype(np.float32)).to(dev)
+    return o, m[..., None].expand(-1, -1, 8).contiguous(), l[..., None].expand(-1, -1, 8).contiguous()
+
+
+def _check_dq(name, w, dq, ref_rows, toks):
+    keep = torch.zeros(w.T1, dtype=torch.bool, device=dq.device)
+    keep[torch.from_numpy(toks).to(dq.device)] = True
+    assert_close(f"{w.name}:{name}[sampled]", f64(dq[keep]), ref_rows, w.dtype)
+    nz = int(torch.count_nonzero(dq[~keep]).item())
+    assert nz == 0, f"{w.name}:{name}: {nz} nonzero values in rows with zero gradient"
+
+
+def _run_dense(w, n_tok):
+    dev = torch.device("cuda", 0)
+    _say(w.name, "inputs")
+    x = W.make_inputs(w, device=dev, backend="torch")
+    toks = _sample_tokens(w, n_tok)
+    cpu = {k: (None if v is None else f64(v)) for k, v in x.items() if k in
+           ("query", "query_rope", "key", "key_rope", "value", "dy")}
+    _say(w.name, f"oracle forward on {len(toks)} tokens")
+    o, m, l = O.forward_dense(cpu["query"], cpu["key"], cpu["value"], w.cu_q, w.cu_kv, w.n1, w.n2, w.scale,
+                              w.causal, cpu["query_rope"], cpu["key_rope"], tokens=toks)
+    o, smax, ssum = _inert_inputs(w, dev, toks, o[toks], m[toks], l[toks])
+    prob = sab.Problem.dense(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, causal=w.causal,
+                             d_rope=w.d_rope, dtype=w.dtype)
+    outs = [torch.empty_like(x["query"]), torch.empty_like(x["query_rope"]) if w.d_rope else None,
+            torch.empty_like(x["key"]), torch.empty_like(x["key_rope"]) if w.d_rope else None,
+            torch.empty_like(x["value"])]
+    ws = torch.empty(max(1, sab.attn_bwd_workspace_size(prob)), dtype=torch.uint8, device=dev)
+    _say(w.name, "gpu backward")
+    sab.attn_bwd_dense_varlen(prob, x["query"], x["query_rope"], x["key"], x["key_rope"], x["value"], o, x["dy"],
+                              smax, ssum, *outs, ws, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    _say(w.name, "oracle backward")
+    ref = O.backward_dense(cpu["query"], cpu["key"], cpu["value"], cpu["dy"], w.cu_q, w.cu_kv, w.n1, w.n2, w.scale,
+                           w.causal, cpu["query_rope"], cpu["key_rope"], tokens=toks)
+    dq, dq_rope, dk, dk_rope, dv = outs
+    _check_dq("dq", w, dq, ref[0][toks], toks)
+    if w.d_rope:
+        _check_dq("dq_rope", w, dq_rope, ref[1][toks], toks)
+        assert_close(f"{w.name}:dk_rope", f64(dk_rope), ref[3], w.dtype)
+    assert_close(f"{w.name}:dk", f64(dk), ref[2], w.dtype)
+    assert_close(f"{w.name}:dv", f64(dv), ref[4], w.dtype)
+
+
+def _run_selected(w, n_tok, deterministic, repeat=False):
+    dev = torch.device("cuda", 0)
+    _say(w.name, "inputs")
+    x = W.make_inputs(w, device=dev, backend="torch")
+    toks = _sample_tokens(w, n_tok)
+    # Without a causal mask a token's result depends only on its own rows and its
+    # sequence's K / V: the oracle runs on the sampled tokens as a compact problem.
+    seq = np.searchsorted(np.asarray(w.cu_q), toks, side="right") - 1
+    cu_sub = np.concatenate([[0], np.cumsum(np.bincount(seq, minlength=w.batch))]).astype(np.int64)
+    idx = torch.from_numpy(toks).to(dev)
+    q_sub, dy_sub = f64(x["query"][idx]), f64(x["dy"][idx])
+    topk_sub = x["topk"][idx].cpu().numpy()
+    K, V = f64(x["key"]), f64(x["value"])
+    _say(w.name, f"oracle forward on {len(toks)} tokens")
+    o_sub, m_sub, l_sub = O.forward_selected(q_sub, K, V, topk_sub, cu_sub, w.cu_kv, w.n1, w.n2, w.scale,
+                                             w.block_size)
+    o, smax, ssum = _inert_inputs(w, dev, toks, o_sub, m_sub, l_sub)
+    prob = sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size, w.block_count,
+                                deterministic=deterministic)
+    ws = torch.empty(max(1, sab.attn_bwd_workspace_size(prob)), dtype=torch.uint8, device=dev)
+
+    def run():
+        outs = [torch.empty_like(x["query"]), torch.empty_like(x["key"]), torch.empty_like(x["value"])]
+        sab.attn_bwd_selected(prob, x["query"], x["key"], x["value"], o, x["dy"], smax, ssum, x["topk"], *outs, ws,
+                              stream=torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return outs
+
+    _say(w.name, f"gpu backward (deterministic={deterministic})")
+    dq, dk, dv = run()
+    if repeat:
+        _say(w.name, "gpu backward again")
+        dq2, dk2, dv2 = run()
+        for a, b, n in ((dq, dq2, "dq"), (dk, dk2, "dk"), (dv, dv2, "dv")):
+            assert torch.equal(a, b), f"{w.name}:{n} differs between two deterministic runs"
+        del dq2, dk2, dv2
+    del ws
+    _say(w.name, "oracle backward")
+    rq, rk, rv = O.backward_selected(q_sub, K, V, dy_sub, topk_sub, cu_sub, w.cu_kv, w.n1, w.n2, w.scale,
+                                     w.block_size)
+    _check_dq("dq", w, dq, rq, toks)
+    assert_close(f"{w.name}:dk", f64(dk), rk, w.dtype)
+    assert_close(f"{w.name}:dv", f64(dv), rv, w.dtype)
+
+
+@pytest.fixture(autouse=True)
+def _free_device_memory():
+    yield
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_dense_causal_rope():
+    _run_dense(W.config(2), 1024)
+
+
+def test_fullsize_selected_s32k():
+    _run_selected(W.config(3), 1024, deterministic=False)
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_fullsize_selected_varlen_zipf(deterministic):
+    _run_selected(W.config(4), 512, deterministic=deterministic, repeat=deterministic)
+
+
+def test_fullsize_selected_s128k():
+    _run_selected(W.config(5), 512, deterministic=False)

@@ -55,6 +55,8 @@ def test_dense_fp32_small_rope():
     dict(seqlens=(192, 96), block_size=32, block_count=3, n1=16, n2=2),
     dict(seqlens=(128, 128), block_size=16, block_count=5, n1=8, n2=1, d_qk=128, d_v=128),
     dict(seqlens=(200, 0, 64), seqlens_kv=(256, 128, 192), block_size=64, block_count=2, index_dist="zipf"),
+    # one query token against G = 16 heads and a 64-key block; single-block sequence
+    dict(seqlens=(1,), seqlens_kv=(64,), block_size=64, block_count=1, n1=16, n2=1),
 ])
 def test_selected(kw):
     _run(W.small_selected(**kw))

@@ -383,3 +383,76 @@ def test_token_subset_matches_full_run():
     only = O.backward_selected(c["q"], c["k"], c["v"], c["dy"], c["topk"], cq, ck, n1, n2, scale, bs,
                                tokens=range(sum(lq)))
     np.testing.assert_allclose(only[1], full[1], rtol=1e-13)
+
+
+def _inert_stats(m, l, o, tokens):
+    """Statistics and O for rows outside ``tokens`` that make those rows contribute
+    nothing: l = 1 and a maximum far above every score give P = exp(s - m) / l = 0,
+    and O = 0 gives rowsum(dY * O) = 0, hence dS = 0."""
+    keep = np.zeros(m.shape[0], dtype=bool)
+    keep[list(tokens)] = True
+    m, l, o = m.copy(), l.copy(), o.copy()
+    m[~keep] = 3.0e4
+    l[~keep] = 1.0
+    o[~keep] = 0.0
+    return m, l, o
+
+
+def test_dense_token_subset_is_additive():
+    """Rows of disjoint token subsets: forward rows and dQ rows equal the full run's,
+    and the dK / dV contributions of the two subsets add up to the full gradient."""
+    rng = np.random.default_rng(23)
+    lq, n1, n2, dr = (7, 0, 9), 4, 2, 3
+    c = _dense_case(rng, lq, lq, n1, n2, 6, dr, 5)
+    cq, scale = cu(lq), 0.41
+    args = (cq, cq, n1, n2, scale, True)
+    fo, fm, fl = O.forward_dense(c["q"], c["k"], c["v"], *args, c["qr"], c["kr"])
+    full = O.backward_dense(c["q"], c["k"], c["v"], c["dy"], *args, c["qr"], c["kr"])
+    A = [0, 3, 6, 8, 15]
+    B = sorted(set(range(sum(lq))) - set(A))
+    po, pm, pl = O.forward_dense(c["q"], c["k"], c["v"], *args, c["qr"], c["kr"], tokens=A)
+    np.testing.assert_allclose(po[A], fo[A], rtol=1e-13)
+    np.testing.assert_allclose(pm[A], fm[A], rtol=1e-13)
+    assert np.isneginf(pm[B]).all() and (pl[B] == 0).all() and (po[B] == 0).all()
+    ga = O.backward_dense(c["q"], c["k"], c["v"], c["dy"], *args, c["qr"], c["kr"], tokens=A)
+    gb = O.backward_dense(c["q"], c["k"], c["v"], c["dy"], *args, c["qr"], c["kr"], tokens=B)
+    for i in (0, 1):   # dq, dq_rope: row restriction
+        np.testing.assert_allclose(ga[i][A], full[i][A], rtol=1e-12, atol=1e-14)
+        assert (ga[i][B] == 0).all()
+    for i in (2, 3, 4):  # dk, dk_rope, dv: additivity over query rows
+        np.testing.assert_allclose(ga[i] + gb[i], full[i], rtol=1e-12, atol=1e-13)
+
+
+def test_inert_rows_contribute_nothing_dense():
+    """The construction of the full-size parity tests: rows outside the sampled tokens
+    get O = 0, l = 1 and a huge maximum; consuming those statistics the way the kernels
+    do gives exactly the gradient of the sampled rows alone."""
+    rng = np.random.default_rng(24)
+    lq, n1, n2, dr = (8, 6), 4, 2, 2
+    c = _dense_case(rng, lq, lq, n1, n2, 6, dr, 5)
+    cq, scale = cu(lq), 0.39
+    args = (cq, cq, n1, n2, scale, True)
+    toks = [1, 5, 9, 13]
+    o, m, l = O.forward_dense(c["q"], c["k"], c["v"], *args, c["qr"], c["kr"], tokens=toks)
+    m, l, o = _inert_stats(m, l, o, toks)
+    smax, ssum = m[..., None].repeat(8, -1), l[..., None].repeat(8, -1)
+    got = O.backward_dense_from_stats(c["q"], c["k"], c["v"], o, c["dy"], smax, ssum, *args, c["qr"], c["kr"])
+    want = O.backward_dense(c["q"], c["k"], c["v"], c["dy"], *args, c["qr"], c["kr"], tokens=toks)
+    for g, wv in zip(got, want):
+        np.testing.assert_allclose(g, wv, rtol=1e-10, atol=1e-12)
+
+
+def test_inert_rows_contribute_nothing_selected():
+    rng = np.random.default_rng(25)
+    lq, lk, n1, n2, bs, cnt = (6, 5), (8, 12), 4, 2, 2, 3
+    c = _selected_case(rng, lq, lk, n1, n2, 5, 4, bs, cnt)
+    cq, ck, scale = cu(lq), cu(lk), 0.45
+    args = (c["topk"], cq, ck, n1, n2, scale, bs)
+    toks = [0, 4, 7]
+    o, m, l = O.forward_selected(c["q"], c["k"], c["v"], *args, tokens=toks)
+    m, l, o = _inert_stats(m, l, o, toks)
+    smax, ssum = m[..., None].repeat(8, -1), l[..., None].repeat(8, -1)
+    got = O.backward_selected_from_stats(c["q"], c["k"], c["v"], o, c["dy"], smax, ssum, *args)
+    want = O.backward_selected(c["q"], c["k"], c["v"], c["dy"], *args, tokens=toks)
+    for g, wv in zip(got, want):
+        np.testing.assert_allclose(g, wv, rtol=1e-10, atol=1e-12)
