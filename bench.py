@@ -66,7 +66,7 @@ KERNEL_SOURCES = {
     "dense_dq": ("dense_dq_ds_kernel<", "dense_dq.hip"),
     "dense_dq_recompute": ("dense_dq_kernel<", "attn_q.hip"),
     "selected_kv_major": ("sel_kv_kernel<", "sel_kv.hip"),
-    "selected_dq_reduce": ("dq_reduce_kernel<", "attn_kv.hip"),
+    "selected_dq_reduce": ("dq_reduce_kernel<", "sel_reduce.hip"),
     "row_stats": ("preprocess_kernel<", "preprocess.hip"),
 }
 CSRC = os.path.join(ROOT, "sparse_attention_backward_amd", "csrc")

@@ -19,8 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattnbwd.so")
-SOURCES = ["api.hip", "preprocess.hip", "dense_fp32.hip", "attn_kv.hip", "dense_kv.hip", "dense_dq.hip",
-           "attn_q.hip", "index.hip", "sel_kv.hip"]
+SOURCES = ["api.hip", "preprocess.hip", "dense_fp32.hip", "dense_kv.hip", "dense_dq.hip", "attn_q.hip",
+           "index.hip", "sel_kv.hip", "sel_reduce.hip"]
 ARCH = os.environ.get("ATTN_BWD_ARCH", "gfx950")
 # Per-source code generation options.
 EXTRA = {}

@@ -474,8 +474,7 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   a.flag = at<int32_t>(workspace, pl.off_flag);
   a.dq_part = at<void>(workspace, pl.off_dq_part);
   if (timed("selected_index", s, [&] { return launch_selected_index(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
-  const bool kv64 = selected_kv64_supported(a.d_qk, a.d_v, a.G, a.bs);
-  if (timed("selected_kv_major", s, [&] { return kv64 ? launch_selected_kv64(a, s) : launch_selected_dkdv(a, s); }) !=
+  if (timed("selected_kv_major", s, [&] { return launch_selected_kv(a, s); }) !=
       hipSuccess)
     return ATTN_ERR_HIP;
   if (timed("selected_dq_reduce", s, [&] { return launch_selected_dq_reduce(a, s); }) != hipSuccess)

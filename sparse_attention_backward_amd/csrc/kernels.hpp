@@ -75,9 +75,7 @@ struct SelArgs {
 };
 bool selected_supported(int d_qk, int d_v, int G, int bs);
 hipError_t launch_selected_index(const SelArgs& a, hipStream_t s);
-hipError_t launch_selected_dkdv(const SelArgs& a, hipStream_t s);       // dK, dV and dQ partials (any block size)
-bool selected_kv64_supported(int d_qk, int d_v, int G, int bs);
-hipError_t launch_selected_kv64(const SelArgs& a, hipStream_t s);       // the same, blocks of <= 64 keys
+hipError_t launch_selected_kv(const SelArgs& a, hipStream_t s);         // dK, dV and the dQ partials
 hipError_t launch_selected_dq_reduce(const SelArgs& a, hipStream_t s);  // dQ = scale * sum of partials
 
 // ---- misc --------------------------------------------------------------------

@@ -10,11 +10,13 @@
 // per block instead: the inverted index lists, for each (KV head, block), the (token,
 // slot) entries that selected it in ascending order, and one workgroup owns the block.
 //
-// One workgroup (4 waves) owns a block of up to 64 key rows of one KV head.  Query rows
-// stream past in steps of 64 rows = 64 / G listed entries x the G query heads of the KV
-// head.  The waves form a 2 x 2 grid as in the dense KV-major kernel: wave w owns keys
-// 32(w&1) .. +31 (K and V resident in registers) and rows 32(w>>1) .. +31 of every step.
-// Per step:
+// One workgroup (4 waves) owns a block of up to KB = 64 or 128 key rows of one KV head.
+// Query rows stream past in steps of 64 rows = floor(64 / G) listed entries x the G query
+// heads of the KV head (rows past that product are padding and contribute nothing).
+// KB = 64: the waves form a 2 x 2 grid as in the dense KV-major kernel, wave w owning
+// keys 32(w&1) .. +31 and rows 32(w>>1) .. +31 of every step; KB = 128: wave w owns keys
+// 32w .. +31 and takes both 32-row halves of the step in turn.  K and V of a wave's keys
+// stay resident in registers.  Per step:
 //   S = Q K^T, dP = dY V^T, P = exp2(S*scale*log2e - lse2), dS = P (dP - drow)
 //   dV += P^T dY, dK += dS^T Q                       (registers, summed over all entries)
 //   dS^T -> LDS, then dQ_part^T = K^T dS^T over the block's keys (K staged in LDS once):
@@ -33,7 +35,7 @@ namespace ab {
 
 namespace {
 
-constexpr int kRows = 64;  // query rows per step, key rows per workgroup (block_size <= 64)
+constexpr int kRows = 64;  // query rows per step
 typedef __attribute__((address_space(3))) void lds_void;
 
 struct SkvArgs {
@@ -88,8 +90,10 @@ struct PartLanes {
   }
 };
 
-template <int DM, int DR, int DV>
+template <int DM, int DR, int DV, int KB>
 __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
+  static_assert(KB == 64 || KB == 128, "64 or 128 keys per workgroup");
+  constexpr int NRH = KB / 64;  // 32-row halves of a step taken by each wave
   constexpr int DQK = DM + DR;
   constexpr int KS = DQK / 32, VS = DV / 32, NQ = DQK / 16, NV = DV / 16;
   constexpr int KSM = DM / 32, NQM = DM / 16;
@@ -101,18 +105,20 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   using TD = RowTile<8>;       // dS^T tile: 64 keys x 64 rows
   constexpr int OQM = 0, OQR = TM::BYTES, OY = OQR + (DR > 0 ? TR::BYTES : 0);
   constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = ORW + 256;  // stage: QM, QR, Y, lse2, drow
-  constexpr int OKM = 2 * SB, OKR = OKM + TM::BYTES;                  // K tile (dQ product)
-  constexpr int ODS = OKR + (DR > 0 ? TR::BYTES : 0);                 // dS^T tile
+  constexpr int OKM = 2 * SB, OKR = OKM + NRH * TM::BYTES;            // K tile, KB rows (dQ product)
+  constexpr int ODS = OKR + (DR > 0 ? NRH * TR::BYTES : 0);           // dS^T tile, KB key rows
   constexpr int NACC = 2 * (NQ + NV);
-  constexpr int EPI = 2 * NACC * 1024 + 64 * (DQK + DV) * 2;
-  constexpr int MAIN = ODS + TD::BYTES;
+  constexpr int EPI = (NRH == 1 ? 2 * NACC * 1024 : 0) + KB * (DQK + DV) * 2;
+  constexpr int MAIN = ODS + NRH * TD::BYTES;
   constexpr int SMEM = MAIN > EPI ? MAIN : EPI;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = w & 1, rh = w >> 1;
+  const int kh = NRH == 1 ? (w & 1) : w;      // key group: keys 32 kh .. +31
+  const int rh0 = NRH == 1 ? (w >> 1) : 0;    // first 32-row half of the step
+  const int qh = w >> 1;                      // dQ product: rows 32 qh .. +31
   const int l16 = lane & 15, g = lane >> 4;
 
   // ---- work unit: (KV head, block) and its list of entries -------------------------
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   const int64_t k0 = a.cu_kv[b] + (int64_t)(rem - a.blkoff[b]) * a.bs;
   const int nk = a.bs;
   const int e_begin = a.offsets[u], e_end = a.offsets[u + 1];
-  const int G = a.G, TPS = kRows / G;
+  const int G = a.G, TPS = kRows / G;  // entries per step
   const int nsteps = (e_end - e_begin + TPS - 1) / TPS;
   const int hh_row = lane % G;  // head (within the group) of step row `lane`
 
@@ -151,31 +157,35 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   PartLanes<WM> pm;
   PartLanes<WR> pr;
   PartLanes<WY> py;
-  pm.init(w, lane, rh);
-  if constexpr (DR > 0) pr.init(w, lane, rh);
-  py.init(w, lane, rh);
+  pm.init(w, lane, rh0);
+  if constexpr (DR > 0) pr.init(w, lane, rh0);
+  py.init(w, lane, rh0);
   const uint32_t smem_lds = lds_addr(smem);
 
-  // K tile in LDS (RowTile layout, key rows; keys past the block repeat its last key)
+  // K tile in LDS (RowTile layout, KB key rows; keys past the block repeat its last key)
   {
     PartLanes<WM> km;
     km.init(w, lane, 0);
 #pragma unroll
-    for (int kk = 0; kk < WM / 4; ++kk) {
-      const int r = min(km.row0 + 4 * TM::RPI * kk, nk - 1);
-      const uint4 x = ldg16(reinterpret_cast<const char*>(a.k + ((k0 + r) * a.n2 + kvh) * DQK) + km.gchunk);
-      lds_st16_at(smem_lds + OKM + (w + 4 * kk) * 1024 + 16 * lane, x);
-    }
+    for (int hk = 0; hk < NRH; ++hk)
+#pragma unroll
+      for (int kk = 0; kk < WM / 4; ++kk) {
+        const int r = min(64 * hk + km.row0 + 4 * TM::RPI * kk, nk - 1);
+        const uint4 x = ldg16(reinterpret_cast<const char*>(a.k + ((k0 + r) * a.n2 + kvh) * DQK) + km.gchunk);
+        lds_st16_at(smem_lds + OKM + hk * TM::BYTES + (w + 4 * kk) * 1024 + 16 * lane, x);
+      }
     if constexpr (DR > 0) {
       PartLanes<WR> kr_;
       kr_.init(w, lane, 0);
 #pragma unroll
-      for (int kk = 0; kk < WR / 4; ++kk) {
-        const int r = min(kr_.row0 + 4 * TR::RPI * kk, nk - 1);
-        const uint4 x =
-            ldg16(reinterpret_cast<const char*>(a.k + ((k0 + r) * a.n2 + kvh) * DQK + DM) + kr_.gchunk);
-        lds_st16_at(smem_lds + OKR + (w + 4 * kk) * 1024 + 16 * lane, x);
-      }
+      for (int hk = 0; hk < NRH; ++hk)
+#pragma unroll
+        for (int kk = 0; kk < WR / 4; ++kk) {
+          const int r = min(64 * hk + kr_.row0 + 4 * TR::RPI * kk, nk - 1);
+          const uint4 x =
+              ldg16(reinterpret_cast<const char*>(a.k + ((k0 + r) * a.n2 + kvh) * DQK + DM) + kr_.gchunk);
+          lds_st16_at(smem_lds + OKR + hk * TR::BYTES + (w + 4 * kk) * 1024 + 16 * lane, x);
+        }
     }
   }
   // dQ product split: wave w owns feature half fh = w & 1 and rows 32 rh .. +31 of the
@@ -185,31 +195,27 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   // lane groups of a row cover 64 consecutive bytes.  The K^T column reads follow the
   // permutation: 4-feature chunk qq of tile f starts at feature F0(f) + 8 qq + 4 (f % 2).
   const int fh = w & 1;
-  uint32_t kcol[NFH][2][2];
+  uint32_t kcol[NFH];  // keys 4g + jj; + (32 ks + 16 h) rows at use
   {
     const int jj = l16 >> 2, qq = l16 & 3;
     static_for_i<NFH>([&](auto fc) {
       constexpr int f = decltype(fc)::value;
-      int base = 0, rb = 0;
+      int base = 0;
       static_for_i<2>([&](auto hc) {  // the feature half with compile-time tile choice
         constexpr int F0 = decltype(hc)::value * (DQK / 2) + 32 * (f / 2);
         if (fh == decltype(hc)::value) {
-          if constexpr (F0 < DM) { base = OKM + TM::off(4 * g + jj, F0 / 8 + qq) + 8 * (f % 2); rb = TM::RB; }
-          else { base = OKR + TR::off(4 * g + jj, (F0 - DM) / 8 + qq) + 8 * (f % 2); rb = TR::RB; }
+          if constexpr (F0 < DM) base = OKM + TM::off(4 * g + jj, F0 / 8 + qq) + 8 * (f % 2);
+          else base = OKR + TR::off(4 * g + jj, (F0 - DM) / 8 + qq) + 8 * (f % 2);
         }
       });
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        kcol[f][ks2][0] = base + ks2 * 32 * rb;
-        kcol[f][ks2][1] = base + ks2 * 32 * rb + 16 * rb;
-      }
+      kcol[f] = base;
     });
   }
   int dscol[2];
   {
     const int jj = l16 >> 2, qq = l16 & 3;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) dscol[rr] = ODS + TD::off(4 * g + jj, 2 * (2 * rh + rr) + (qq >> 1)) + 8 * (qq & 1);
+    for (int rr = 0; rr < 2; ++rr) dscol[rr] = ODS + TD::off(4 * g + jj, 2 * (2 * qh + rr) + (qq >> 1)) + 8 * (qq & 1);
   }
 
   f32x4 dK[2][NQ], dV[2][NV];
@@ -223,8 +229,9 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
 
   // ---- list entries: row `lane` of step st is entry e_begin + st * TPS + lane / G ------
   auto entry_of = [&](int st) -> int {
-    const int ei = e_begin + st * TPS + lane / G;
-    return ei < e_end ? a.list[ei] : -1;
+    const int slot = lane / G;  // entry slot of row `lane`; slots >= TPS are padding rows
+    const int ei = e_begin + st * TPS + slot;
+    return slot < TPS && ei < e_end ? a.list[ei] : -1;
   };
   const int first_entry = e_begin < e_end ? a.list[e_begin] : 0;  // stands in for missing rows
 
@@ -266,8 +273,13 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   };
 
   // ---- one step ------------------------------------------------------------------------
-  auto step = [&](int soff, int ent_cur) {
-    const uint32_t stage = smem_lds + soff;
+  // rows 32 (rh0 + hi) .. +31 of the step staged at `stage`: S, dP, P, dS, dS^T -> LDS,
+  // dV += P^T dY, dK += dS^T Q
+  auto half_step = [&](uint32_t stage, auto hic) {
+    constexpr int hi = decltype(hic)::value;
+    const int rh = rh0 + hi;
+    const uint32_t bm = stage + OQM + hi * 32 * TM::RB, br = stage + OQR + hi * 32 * TR::RB;
+    const uint32_t by = stage + OY + hi * 32 * TY::RB;
     const uint32_t statb = opaque(stage + OL + 4 * (32 * rh + 4 * g));  // lse2; drow at + 256
     f32x4 lse[2], dr[2];
 #pragma unroll
@@ -277,9 +289,9 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     }
     constexpr int NS = KS + VS, PA = 3;
     auto afrag = [&](int s, int rt) -> bf16x8 {
-      if (s < KSM) return lds_b128_at(stage + OQM + pm.rowA[s] + rt * 16 * TM::RB);
-      if (s < KS) return lds_b128_at(stage + OQR + pr.rowA[s - KSM] + rt * 16 * TR::RB);
-      return lds_b128_at(stage + OY + py.rowA[s - KS] + rt * 16 * TY::RB);
+      if (s < KSM) return lds_b128_at(bm + pm.rowA[s] + rt * 16 * TM::RB);
+      if (s < KS) return lds_b128_at(br + pr.rowA[s - KSM] + rt * 16 * TR::RB);
+      return lds_b128_at(by + py.rowA[s - KS] + rt * 16 * TY::RB);
     };
     bf16x8 aring[PA][2];
 #pragma unroll
@@ -341,9 +353,9 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     // dV += P^T dY, dK += dS^T Q
     auto colfrag = [&](int j) -> bf16x8 {
       uint32_t o, second;
-      if (j < NV) { o = stage + OY + py.colB[j]; second = 16 * TY::RB; }
-      else if (j < NV + NQM) { o = stage + OQM + pm.colB[j - NV]; second = 16 * TM::RB; }
-      else { o = stage + OQR + pr.colB[j - NV - NQM]; second = 16 * TR::RB; }
+      if (j < NV) { o = by + py.colB[j]; second = 16 * TY::RB; }
+      else if (j < NV + NQM) { o = bm + pm.colB[j - NV]; second = 16 * TM::RB; }
+      else { o = br + pr.colB[j - NV - NQM]; second = 16 * TR::RB; }
       return join8(lds_tr16_at(o), lds_tr16_at(o + second));
     };
     constexpr int NJ = NV + NQ, PD = 4;
@@ -369,23 +381,29 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
       if (j + PD < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
 
-    // ---- dQ part: dQ_part^T (features x rows) = K^T dS^T over the 64 keys ------------
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's dS^T writes are done
-    barrier_no_vm_wait();                // every wave's dS^T is in LDS
+  };
+
+  // dQ_part^T (features x rows) = K^T dS^T over the KB keys, for the feature half FH and
+  // rows 32 qh .. +31; every row with an entry stores its G x DQK share (bf16).
+  auto dq_part = [&](int ent_cur, auto fhc) {
+    constexpr int FH = decltype(fhc)::value;
     f32x4 acc[NFH][2];
 #pragma unroll
     for (int f = 0; f < NFH; ++f)
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) acc[f][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
+    for (int ks = 0; ks < KB / 32; ++ks) {
       bf16x8 kt[NFH], dt[2];
-#pragma unroll
-      for (int f = 0; f < NFH; ++f)
-        kt[f] = join8(lds_tr16_at(smem_lds + kcol[f][ks2][0]), lds_tr16_at(smem_lds + kcol[f][ks2][1]));
+      static_for_i<NFH>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        constexpr int rb = FH * (DQK / 2) + 32 * (f / 2) < DM ? TM::RB : TR::RB;
+        const uint32_t o = smem_lds + kcol[f] + ks * 32 * rb;
+        kt[f] = join8(lds_tr16_at(o), lds_tr16_at(o + 16 * rb));
+      });
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
-        const uint32_t o = smem_lds + dscol[rr] + ks2 * 32 * TD::RB;
+        const uint32_t o = smem_lds + dscol[rr] + ks * 32 * TD::RB;
         dt[rr] = join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB));
       }
 #pragma unroll
@@ -393,19 +411,28 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) acc[f][rr] = mfma_16x16x32(kt[f], dt[rr], acc[f][rr]);
     }
-    // C tile (f, rr): lane holds row 32 rh + 16 rr + l16 and the permuted features above
+    // C tile (f, rr): lane holds row 32 qh + 16 rr + l16 and the permuted features above
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-      const int r = 32 * rh + 16 * rr + l16;
+      const int r = 32 * qh + 16 * rr + l16;
       const int ent = __shfl(ent_cur, r);
       if (ent >= 0) {
         const int t = ent / a.cnt, sl = ent - t * a.cnt;
-        uint16_t* dst = a.dq_part + ((((int64_t)t * a.n2 + kvh) * a.cnt + sl) * G + r % G) * DQK + fh * (DQK / 2) + 8 * g;
+        uint16_t* dst = a.dq_part + ((((int64_t)t * a.n2 + kvh) * a.cnt + sl) * G + r % G) * DQK + FH * (DQK / 2) + 8 * g;
 #pragma unroll
         for (int j = 0; j < NFH / 2; ++j)
           *reinterpret_cast<bf16x8*>(dst + 32 * j) = pack8(acc[2 * j][rr], acc[2 * j + 1][rr]);
       }
     }
+  };
+
+  auto step = [&](int soff, int ent_cur) {
+    const uint32_t stage = smem_lds + soff;
+    static_for_i<NRH>([&](auto hic) { half_step(stage, hic); });
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's dS^T writes are done
+    barrier_no_vm_wait();                // every wave's dS^T is in LDS
+    if (fh) dq_part(ent_cur, std::integral_constant<int, 1>{});
+    else dq_part(ent_cur, std::integral_constant<int, 0>{});
   };
 
   // ---- step loop -----------------------------------------------------------------------
@@ -432,46 +459,55 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     ent_nx = ent_nx2;
   }
 
-  // ---- epilogue: sum the two row halves, bf16 through LDS, 16-byte stores ------------
+  // ---- epilogue: dK, dV to bf16 through LDS (KB = 64: the two row halves summed first),
+  // then 16-byte stores of whole rows ----------------------------------------------------
   __syncthreads();
-  f32x4* part = reinterpret_cast<f32x4*>(smem);
-  if (rh == 1) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int n = 0; n < NQ; ++n) part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane] = dK[t][n];
-#pragma unroll
-      for (int n = 0; n < NV; ++n) part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane] = dV[t][n];
-    }
-  }
-  __syncthreads();
-  uint16_t* Ko = reinterpret_cast<uint16_t*>(smem + 2 * NACC * 1024);
-  uint16_t* Vo = Ko + 64 * DQK;
-  if (rh == 0) {
+  uint16_t* Ko = reinterpret_cast<uint16_t*>(smem + (NRH == 1 ? 2 * NACC * 1024 : 0));
+  uint16_t* Vo = Ko + KB * DQK;
+  auto put = [&](auto&& other_k, auto&& other_v) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
-        const f32x4 o = part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane];
+        const f32x4 o = other_k(t, n);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           Ko[(32 * kh + 16 * t + 4 * g + i) * DQK + 16 * n + l16] = f2bf((dK[t][n][i] + o[i]) * a.scale);
       }
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
-        const f32x4 o = part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane];
+        const f32x4 o = other_v(t, n);
 #pragma unroll
         for (int i = 0; i < 4; ++i) Vo[(32 * kh + 16 * t + 4 * g + i) * DV + 16 * n + l16] = f2bf(dV[t][n][i] + o[i]);
       }
     }
+  };
+  if constexpr (NRH == 1) {
+    f32x4* part = reinterpret_cast<f32x4*>(smem);
+    if (rh0 == 1) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane] = dK[t][n];
+#pragma unroll
+        for (int n = 0; n < NV; ++n) part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane] = dV[t][n];
+      }
+    }
+    __syncthreads();
+    if (rh0 == 0)
+      put([&](int t, int n) { return part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane]; },
+          [&](int t, int n) { return part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane]; });
+  } else {
+    const auto zero = [](int, int) { return f32x4{0.f, 0.f, 0.f, 0.f}; };
+    put(zero, zero);
   }
   __syncthreads();
   constexpr int QCH = DQK / 8, YCH = DV / 8;
-  for (int idx = tid; idx < kRows * QCH; idx += 256) {
+  for (int idx = tid; idx < KB * QCH; idx += 256) {
     const int r = idx / QCH, c = idx - r * QCH;
     if (r < nk) sts16(a.dk + ((k0 + r) * a.n2 + kvh) * DQK + 8 * c, *reinterpret_cast<const uint4*>(Ko + r * DQK + 8 * c));
   }
-  for (int idx = tid; idx < kRows * YCH; idx += 256) {
+  for (int idx = tid; idx < KB * YCH; idx += 256) {
     const int r = idx / YCH, c = idx - r * YCH;
     if (r < nk) sts16(a.dv + ((k0 + r) * a.n2 + kvh) * DV + 8 * c, *reinterpret_cast<const uint4*>(Vo + r * DV + 8 * c));
   }
@@ -479,11 +515,12 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
 
 }  // namespace
 
-bool selected_kv64_supported(int d_qk, int d_v, int G, int bs) {
-  return (d_qk == 192 || d_qk == 128) && d_v == 128 && bs <= kRows && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+bool selected_supported(int d_qk, int d_v, int G, int bs) {
+  return (d_qk == 192 || d_qk == 128) && d_v == 128 && G >= 1 && G <= 32 && bs >= 16 && bs <= 128 && bs % 16 == 0;
 }
 
-hipError_t launch_selected_kv64(const SelArgs& a, hipStream_t s) {
+hipError_t launch_selected_kv(const SelArgs& a, hipStream_t s) {
+  if (!selected_supported(a.d_qk, a.d_v, a.G, a.bs)) return hipErrorInvalidValue;
   SkvArgs k{};
   k.q = (const uint16_t*)a.q; k.k = (const uint16_t*)a.k; k.v = (const uint16_t*)a.v; k.dy = (const uint16_t*)a.dy;
   k.lse2 = a.lse2; k.drow = a.drow;
@@ -493,9 +530,14 @@ hipError_t launch_selected_kv64(const SelArgs& a, hipStream_t s) {
   k.scale = a.scale; k.scale_log2e = a.scale_log2e;
   const dim3 grid((unsigned)(a.n2 * a.nblk_total));
   if (grid.x == 0) return hipSuccess;
-  if (a.d_qk == 192 && a.d_v == 128) hipLaunchKernelGGL((sel_kv_kernel<128, 64, 128>), grid, dim3(256), 0, s, k);
-  else if (a.d_qk == 128 && a.d_v == 128) hipLaunchKernelGGL((sel_kv_kernel<128, 0, 128>), grid, dim3(256), 0, s, k);
-  else return hipErrorInvalidValue;
+  const bool wide = a.bs > 64;
+  if (a.d_qk == 192) {
+    if (wide) hipLaunchKernelGGL((sel_kv_kernel<128, 64, 128, 128>), grid, dim3(256), 0, s, k);
+    else hipLaunchKernelGGL((sel_kv_kernel<128, 64, 128, 64>), grid, dim3(256), 0, s, k);
+  } else {
+    if (wide) hipLaunchKernelGGL((sel_kv_kernel<128, 0, 128, 128>), grid, dim3(256), 0, s, k);
+    else hipLaunchKernelGGL((sel_kv_kernel<128, 0, 128, 64>), grid, dim3(256), 0, s, k);
+  }
   return hipGetLastError();
 }
 

@@ -1,0 +1,114 @@
+// dQ of the selected form from the per-block partials left by the KV-major kernel.
+//
+// Page "NsaSelectedAttentionGrad", formula section: dQ = dS K / sqrt(d) over the gathered
+// rows, i.e. the sum over the selected blocks of each block's dS_block K_block.  The
+// KV-major kernel stores every block's share (bf16) at [t, kvh, slot, head, :]; this kernel
+// adds the slots of each (token, KV head) in slot order and scales:
+//   dQ[t, kvh G + h, :] = scale * sum_slot part[t, kvh, slot, h, :].
+// Fixed order, one writer per output row: deterministic.
+//
+// One wave per (token, KV head).  Lane l owns the 16-byte chunks l, l + 64, ... of the
+// G x DQK block (six per lane at G = 16, DQK = 192), and the slot loop takes two slots per
+// iteration so that twelve 16-byte loads per lane are in flight.  A slot whose topk id is
+// out of range was never written and is skipped: the ids are checked once, one ballot per
+// 64 slots.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ab {
+
+namespace {
+
+constexpr int kU = 6;  // chunks per lane per pass
+constexpr uint32_t kNegZero2 = 0x80008000u;  // two bf16 -0.0: x + (-0) == x for every x
+
+__device__ __forceinline__ void add_bf16x8(float* acc, const uint4& x) {
+  const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc[2 * j] += __uint_as_float(xv[j] << 16);
+    acc[2 * j + 1] += __uint_as_float(xv[j] & 0xffff0000u);
+  }
+}
+
+template <int DQK>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, uint16_t* dq, int64_t pairs, int n2,
+                                                        int n1, int G, int cnt, float scale, const int32_t* topk,
+                                                        const int64_t* cu_q, const int32_t* blkoff, int batch) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= pairs) return;  // whole wave
+  const int64_t t = pair / n2;
+  const int kvh = (int)(pair - t * n2);
+  const int b = seq_of(cu_q, batch, t);
+  const int nblk = blkoff[b + 1] - blkoff[b];
+  uint64_t valid[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int sl = 64 * h + lane;
+    bool ok = false;
+    if (sl < cnt) {
+      const int id = topk[pair * cnt + sl];
+      ok = id >= 0 && id < nblk;
+    }
+    valid[h] = __ballot(ok);
+  }
+  auto slot_ok = [&](int sl) -> bool { return (valid[sl >> 6] >> (sl & 63)) & 1; };
+  const int chunks = G * DQK / 8;
+  const int64_t slot_stride = (int64_t)G * DQK;
+  const uint16_t* src = part + pair * (int64_t)cnt * slot_stride;
+  uint16_t* out = dq + (t * n1 + (int64_t)kvh * G) * DQK;
+  for (int c0 = lane; c0 < chunks; c0 += 64 * kU) {
+    float acc[kU][8];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[u][j] = 0.f;
+    for (int sl = 0; sl < cnt; sl += 2) {
+      const bool v0 = slot_ok(sl), v1 = sl + 1 < cnt && slot_ok(sl + 1);
+      uint4 x0[kU], x1[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = c0 + 64 * u;
+        x0[u] = make_uint4(kNegZero2, kNegZero2, kNegZero2, kNegZero2);  // adds nothing, exactly
+        x1[u] = make_uint4(kNegZero2, kNegZero2, kNegZero2, kNegZero2);
+        if (v0 && c < chunks) x0[u] = ldg16(src + sl * slot_stride + 8 * c);
+        if (v1 && c < chunks) x1[u] = ldg16(src + (sl + 1) * slot_stride + 8 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) add_bf16x8(acc[u], x0[u]);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) add_bf16x8(acc[u], x1[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + 64 * u;
+      if (c < chunks) {
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = (uint32_t)f2bf(acc[u][2 * j] * scale) | ((uint32_t)f2bf(acc[u][2 * j + 1] * scale) << 16);
+        sts16(out + 8 * c, make_uint4(o[0], o[1], o[2], o[3]));
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_selected_dq_reduce(const SelArgs& a, hipStream_t s) {
+  const int64_t pairs = a.T1 * a.n2;
+  if (pairs == 0) return hipSuccess;
+  const dim3 grid((unsigned)((pairs + 3) / 4)), block(256);
+  if (a.d_qk == 192)
+    hipLaunchKernelGGL(dq_reduce_kernel<192>, grid, block, 0, s, (const uint16_t*)a.dq_part, (uint16_t*)a.dq, pairs,
+                       a.n2, a.n1, a.G, a.cnt, a.scale, a.topk, a.cu_q, a.blkoff, a.batch);
+  else if (a.d_qk == 128)
+    hipLaunchKernelGGL(dq_reduce_kernel<128>, grid, block, 0, s, (const uint16_t*)a.dq_part, (uint16_t*)a.dq, pairs,
+                       a.n2, a.n1, a.G, a.cnt, a.scale, a.topk, a.cu_q, a.blkoff, a.batch);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace ab

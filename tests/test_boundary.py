@@ -119,7 +119,7 @@ def test_dense_constraints(kw, want):
     (dict(n1=64, n2=1), INVALID),                            # G <= 32
     (dict(n1=256, n2=8), INVALID),                           # N1 <= 128
     (dict(n1=7, n2=2), INVALID),
-    (dict(n1=64, n2=2), UNSUPPORTED),                        # G = 32: valid, not built
+    (dict(n1=64, n2=2), OK),                                 # G = 32, the largest group
     (dict(d_v=192), UNSUPPORTED),                            # 192/192: valid, not built
     (dict(dtype="fp16"), UNSUPPORTED),
     (dict(dtype="fp32"), INVALID),

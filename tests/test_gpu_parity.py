@@ -55,6 +55,12 @@ def test_dense_fp32_small_rope():
     dict(seqlens=(192, 96), block_size=32, block_count=3, n1=16, n2=2),
     dict(seqlens=(128, 128), block_size=16, block_count=5, n1=8, n2=1, d_qk=128, d_v=128),
     dict(seqlens=(200, 0, 64), seqlens_kv=(256, 128, 192), block_size=64, block_count=2, index_dist="zipf"),
+    # largest group and gathered length the problem allows: G = 32, cnt * bs = 8064 < 8192
+    dict(seqlens=(40,), seqlens_kv=(8192,), block_size=128, block_count=63, n1=64, n2=2),
+    # G = 3 (steps of 21 tokens and a padding row); blocks of 96 keys (a partly used 128-key tile)
+    dict(seqlens=(96, 64), seqlens_kv=(384, 192), block_size=96, block_count=2, n1=6, n2=2),
+    # G = 12 with 32-key blocks
+    dict(seqlens=(70,), seqlens_kv=(256,), block_size=32, block_count=4, n1=24, n2=2),
     # one query token against G = 16 heads and a 64-key block; single-block sequence
     dict(seqlens=(1,), seqlens_kv=(64,), block_size=64, block_count=1, n1=16, n2=1),
 ])
