@@ -3,16 +3,26 @@
 // Page "NsaSelectedAttentionGrad", formula section: selectedKey = Gather(key, topkIndices[i]);
 // the gradient of a gather is a scatter-add (page "aclnnLightningIndexerGrad", formula:
 // dK = ScatterAdd(..., Indices)).  Instead of scattering with atomics, the index is
-// inverted so that each (KV head, block) owns the list of query tokens that selected it:
-//   1. count:  histogram of entries per key = (kv head, sequence block)      (int atomics)
-//   2. scan:   exclusive prefix sum of the counts -> offsets
-//   3. fill:   each entry e = (t, kv head, slot) writes t * cnt + slot at a claimed position
-//   4. sort:   each key's segment is sorted ascending, which removes the arbitrary order of
-//              step 3: the lists, and every sum taken over them, are deterministic.
-// Keys are numbered kv_head * nblk_total + blkoff[b] + id.  An id outside
-// [0, S2_b / block_size) is skipped (and raises the flag); steps 1 and 3 skip the same
-// entries, so the offsets and the filled lists agree.
+// inverted so that each (KV head, block) -- a key -- owns the list of its entries
+// t * cnt + slot in ascending order.  Keys are numbered kv_head * nblk_total + blkoff[b] + id.
+// An id outside [0, S2_b / block_size) is skipped (and raises the flag).
+//
+// Ordered path (a stable counting sort; used when the per-chunk count table fits the
+// scratch buffer and a key histogram fits in LDS):
+//   1. hist:    the entries are cut into chunks of consecutive entries; each chunk's key
+//               histogram (LDS) becomes one row of a [chunk][key] table
+//   2. column sum:  per key, the sum over chunks -> counts
+//   3. scan:        exclusive prefix sum of the counts -> offsets
+//   4. column scan: per key, offsets + running sum over chunks -> each (chunk, key) base
+//   5. fill:    one wave walks its chunk in entry order; an entry's position is its key's
+//               running base plus its rank among equal keys of the same 64 entries
+// Entry order is ascending t * cnt + slot within a key, so no sort is needed.
+// Fallback path: atomic count, scan, atomic fill, then an LDS / global bitonic sort of each
+// key's segment.  Both give the same lists.
+// Schedule: the keys ordered by list length, longest first (ties by key), so that the
+// workgroups with the longest lists start first; identity order when too many keys.
 // Integer work only: bitwise reproducible.
+#include <algorithm>
 #include <climits>
 
 #include "common.hpp"
@@ -23,6 +33,9 @@ namespace ab {
 namespace {
 
 constexpr int kSortCap = 16384;  // segments up to this length are sorted in LDS
+constexpr int kMaxLdsKeys = 16384;  // ordered path: key histogram in LDS (64 KiB)
+constexpr int kMaxChunks = 2048;
+constexpr int kSchedCap = 8192;     // keys sorted for the schedule in LDS (8 bytes each, 64 KiB)
 
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
@@ -147,6 +160,124 @@ __global__ __launch_bounds__(256) void idx_sort_kernel(const int32_t* offsets, i
   }
 }
 
+// ---- ordered path -------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void idx_hist_kernel(SelArgs a, int64_t total, int64_t chunk, int nkeys,
+                                                       int32_t* tab) {
+  extern __shared__ int32_t hist[];
+  for (int k = threadIdx.x; k < nkeys; k += 256) hist[k] = 0;
+  __syncthreads();
+  const int64_t e0 = (int64_t)blockIdx.x * chunk, e1 = min(total, e0 + chunk);
+  for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
+    int64_t t; int slot, key;
+    if (decode_entry(a, e, t, slot, key)) atomicAdd(&hist[key], 1);
+    else a.flag[0] = 1;
+  }
+  __syncthreads();
+  int32_t* row = tab + (int64_t)blockIdx.x * nkeys;
+  for (int k = threadIdx.x; k < nkeys; k += 256) row[k] = hist[k];
+}
+
+// Column pass over the [chunk][key] table: a workgroup takes 16 keys, and each of its 64
+// chunk lanes a contiguous range of at most 32 chunks (nchunks <= 2048).  SCAN = false:
+// counts[key] = sum over all chunks.  SCAN = true: every entry becomes offsets[key] plus the
+// sum of the entries of the earlier chunks (in place).
+template <bool SCAN>
+__global__ __launch_bounds__(1024) void idx_colpass_kernel(int32_t* tab, int nchunks, int nkeys, int32_t* counts,
+                                                           const int32_t* offsets) {
+  __shared__ int32_t part[64][16];
+  const int kq = threadIdx.x & 15, cl = threadIdx.x >> 4;
+  const int key = blockIdx.x * 16 + kq;
+  const bool kok = key < nkeys;
+  const int cpl = (nchunks + 63) / 64;
+  const int c0 = min(nchunks, cl * cpl), c1 = min(nchunks, c0 + cpl);
+  int32_t sum = 0;
+  if (kok)
+    for (int c = c0; c < c1; ++c) sum += tab[(int64_t)c * nkeys + key];
+  part[cl][kq] = sum;
+  __syncthreads();
+  int32_t before = 0;
+  for (int j = 0; j < cl; ++j) before += part[j][kq];
+  if (!kok) return;
+  if constexpr (!SCAN) {
+    if (cl == 63) counts[key] = before + sum;
+  } else {
+    int32_t run = offsets[key] + before;
+    for (int c = c0; c < c1; ++c) {
+      const int64_t i = (int64_t)c * nkeys + key;
+      const int32_t v = tab[i];
+      tab[i] = run;
+      run += v;
+    }
+  }
+}
+
+// One wave per chunk.  Per round of 64 consecutive entries: rank = number of lower lanes
+// with the same key; the highest lane of each key advances that key's base.
+__global__ __launch_bounds__(64) void idx_fill_ordered_kernel(SelArgs a, int64_t total, int64_t chunk, int nkeys,
+                                                              const int32_t* tab) {
+  extern __shared__ int32_t base[];
+  const int lane = threadIdx.x;
+  const int32_t* row = tab + (int64_t)blockIdx.x * nkeys;
+  for (int k = lane; k < nkeys; k += 64) base[k] = row[k];
+  __syncthreads();
+  const int64_t e0 = (int64_t)blockIdx.x * chunk, e1 = min(total, e0 + chunk);
+  for (int64_t r0 = e0; r0 < e1; r0 += 64) {
+    const int64_t e = r0 + lane;
+    int64_t t = 0; int slot = 0, key = -1;
+    if (e >= e1 || !decode_entry(a, e, t, slot, key)) key = -1;
+    int rank = 0;
+    bool last = true;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const int kj = __builtin_amdgcn_readlane(key, j);
+      if (kj == key) {
+        if (j < lane) ++rank;
+        if (j > lane) last = false;
+      }
+    }
+    int pos = 0;
+    if (key >= 0) pos = base[key] + rank;
+    __syncthreads();  // every lane has read its base before any is advanced
+    if (key >= 0) {
+      a.list[pos] = (int32_t)(t * a.cnt + slot);
+      if (last) base[key] = pos + 1;
+    }
+    __syncthreads();
+  }
+}
+
+// Schedule: keys by list length, longest first; ties in key order.  One workgroup.
+__global__ __launch_bounds__(1024) void idx_schedule_kernel(const int32_t* offsets, int nkeys, int32_t* sched) {
+  extern __shared__ uint64_t sk[];
+  int n = 1;
+  while (n < nkeys) n <<= 1;
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    // ascending order of (~length, key): longest first, then lower key
+    sk[i] = i < nkeys ? ((uint64_t)(0x7fffffff - (offsets[i + 1] - offsets[i])) << 32) | (uint32_t)i : ~0ull;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += 1024) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = sk[i], y = sk[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) { sk[i] = y; sk[ixj] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < nkeys; i += 1024) sched[i] = (int32_t)(uint32_t)sk[i];
+}
+
+__global__ __launch_bounds__(256) void idx_identity_kernel(int32_t* sched, int nkeys) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k < nkeys) sched[k] = k;
+}
+
 unsigned grid_for(int64_t n, int64_t per_block) {
   int64_t b = (n + per_block - 1) / per_block;
   return (unsigned)(b < 1 ? 1 : b);
@@ -162,21 +293,60 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Chunking of the ordered path: at most kMaxChunks chunks of a multiple of 64 entries,
+// and a count table no larger than the 2 * entries ints of the sort scratch buffer.
+// Returns 0 chunks when the ordered path does not apply.
+static void ordered_plan(int64_t total, int nkeys, int& nchunks, int64_t& chunk) {
+  nchunks = 0;
+  chunk = 0;
+  if (total <= 0 || nkeys <= 0 || nkeys > kMaxLdsKeys) return;
+  int64_t n = (total + 1023) / 1024;
+  n = std::min<int64_t>(n, kMaxChunks);
+  n = std::min<int64_t>(n, 2 * total / nkeys);
+  if (n < 1) return;
+  chunk = ((total + n - 1) / n + 63) / 64 * 64;
+  nchunks = (int)((total + chunk - 1) / chunk);
+}
+
 hipError_t launch_selected_index(const SelArgs& a, hipStream_t s) {
   const int nkeys = a.n2 * a.nblk_total;
   const int64_t total = a.T1 * a.n2 * a.cnt;
   hipError_t e = launch_fill_i32(a.flag, 1, 0, s);
   if (e != hipSuccess) return e;
-  e = launch_fill_i32(a.counts, nkeys, 0, s);
-  if (e != hipSuccess) return e;
   if (nkeys == 0) return hipSuccess;
-  if (total > 0) hipLaunchKernelGGL(idx_count_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, a, total);
-  hipLaunchKernelGGL(idx_scan_kernel, dim3(1), dim3(1024), 0, s, (const int32_t*)a.counts, a.offsets, a.cursor, nkeys);
-  if (total > 0) {
-    hipLaunchKernelGGL(idx_fill_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, a, total);
-    hipLaunchKernelGGL(idx_sort_kernel, dim3((unsigned)nkeys), dim3(256), 0, s, (const int32_t*)a.offsets, a.list,
-                       a.sort_scratch);
+  int nchunks;
+  int64_t chunk;
+  ordered_plan(total, nkeys, nchunks, chunk);
+  const unsigned kgrid = grid_for(nkeys, 256);
+  if (nchunks > 0) {
+    int32_t* tab = a.sort_scratch;
+    const size_t lds = 4 * (size_t)nkeys;
+    hipLaunchKernelGGL(idx_hist_kernel, dim3(nchunks), dim3(256), lds, s, a, total, chunk, nkeys, tab);
+    const dim3 cgrid((unsigned)((nkeys + 15) / 16));
+    hipLaunchKernelGGL(idx_colpass_kernel<false>, cgrid, dim3(1024), 0, s, tab, nchunks, nkeys, a.counts,
+                       (const int32_t*)nullptr);
+    hipLaunchKernelGGL(idx_scan_kernel, dim3(1), dim3(1024), 0, s, (const int32_t*)a.counts, a.offsets, a.cursor, nkeys);
+    hipLaunchKernelGGL(idx_colpass_kernel<true>, cgrid, dim3(1024), 0, s, tab, nchunks, nkeys, (int32_t*)nullptr,
+                       (const int32_t*)a.offsets);
+    hipLaunchKernelGGL(idx_fill_ordered_kernel, dim3(nchunks), dim3(64), lds, s, a, total, chunk, nkeys,
+                       (const int32_t*)tab);
+  } else {
+    e = launch_fill_i32(a.counts, nkeys, 0, s);
+    if (e != hipSuccess) return e;
+    if (total > 0) hipLaunchKernelGGL(idx_count_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, a, total);
+    hipLaunchKernelGGL(idx_scan_kernel, dim3(1), dim3(1024), 0, s, (const int32_t*)a.counts, a.offsets, a.cursor, nkeys);
+    if (total > 0) {
+      hipLaunchKernelGGL(idx_fill_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, a, total);
+      hipLaunchKernelGGL(idx_sort_kernel, dim3((unsigned)nkeys), dim3(256), 0, s, (const int32_t*)a.offsets, a.list,
+                         a.sort_scratch);
+    }
   }
+  // the schedule reuses the cursor array (the fill above is done with it)
+  if (nkeys <= kSchedCap)
+    hipLaunchKernelGGL(idx_schedule_kernel, dim3(1), dim3(1024), 8 * (size_t)(nkeys <= 1 ? 1 : 1 << (32 - __builtin_clz(nkeys - 1))),
+                       s, (const int32_t*)a.offsets, nkeys, a.cursor);
+  else
+    hipLaunchKernelGGL(idx_identity_kernel, dim3(kgrid), dim3(256), 0, s, a.cursor, nkeys);
   return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ struct SelArgs {
   // inverted index (workspace)
   int32_t* counts;          // [nkeys]      nkeys = n2 * nblk_total
   int32_t* offsets;         // [nkeys + 1]
-  int32_t* cursor;          // [nkeys]
+  int32_t* cursor;          // [nkeys] fill cursors, then the work order of the KV-major kernel
   int32_t* list;            // [T1 * n2 * cnt]  entries t * cnt + slot, sorted per key
   int32_t* sort_scratch;    // [2 * T1 * n2 * cnt]
   int32_t* flag;            // [1] raised on an out-of-range topk id

@@ -47,6 +47,7 @@ struct SkvArgs {
   const int32_t* blkoff;      // [B+1] blocks before each sequence
   const int32_t* offsets;     // inverted index: [n2 * nblk_total + 1]
   const int32_t* list;        // entries t * cnt + slot, ascending per (KV head, block)
+  const int32_t* sched;       // [n2 * nblk_total] work order: keys, longest list first
   int batch, n1, n2, G, bs, cnt, nblk_total;
   float scale, scale_log2e;
 };
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   const int l16 = lane & 15, g = lane >> 4;
 
   // ---- work unit: (KV head, block) and its list of entries -------------------------
-  const int u = blockIdx.x;
+  const int u = a.sched[blockIdx.x];
   const int kvh = u / a.nblk_total;
   const int rem = u - kvh * a.nblk_total;
   const int b = seq_of32(a.blkoff, a.batch, rem);
@@ -525,7 +526,7 @@ hipError_t launch_selected_kv(const SelArgs& a, hipStream_t s) {
   k.q = (const uint16_t*)a.q; k.k = (const uint16_t*)a.k; k.v = (const uint16_t*)a.v; k.dy = (const uint16_t*)a.dy;
   k.lse2 = a.lse2; k.drow = a.drow;
   k.dk = (uint16_t*)a.dk; k.dv = (uint16_t*)a.dv; k.dq_part = (uint16_t*)a.dq_part;
-  k.cu_kv = a.cu_kv; k.blkoff = a.blkoff; k.offsets = a.offsets; k.list = a.list;
+  k.cu_kv = a.cu_kv; k.blkoff = a.blkoff; k.offsets = a.offsets; k.list = a.list; k.sched = a.cursor;
   k.batch = a.batch; k.n1 = a.n1; k.n2 = a.n2; k.G = a.G; k.bs = a.bs; k.cnt = a.cnt; k.nblk_total = a.nblk_total;
   k.scale = a.scale; k.scale_log2e = a.scale_log2e;
   const dim3 grid((unsigned)(a.n2 * a.nblk_total));

@@ -61,6 +61,8 @@ def test_dense_fp32_small_rope():
     dict(seqlens=(96, 64), seqlens_kv=(384, 192), block_size=96, block_count=2, n1=6, n2=2),
     # G = 12 with 32-key blocks
     dict(seqlens=(70,), seqlens_kv=(256,), block_size=32, block_count=4, n1=24, n2=2),
+    # few entries over many blocks: the index build takes its atomic-fill-and-sort path
+    dict(seqlens=(8,), seqlens_kv=(2048,), block_size=16, block_count=2, n1=16, n2=1),
     # one query token against G = 16 heads and a 64-key block; single-block sequence
     dict(seqlens=(1,), seqlens_kv=(64,), block_size=64, block_count=1, n1=16, n2=1),
 ])
