@@ -130,9 +130,9 @@ def summarize_counters(dirs, calib_dir=None):
 # kernel -> the GEMMs it performs (for its roofline point)
 KERNEL_GEMMS = {
     "dense_kv_major": ("S", "dP", "dV", "dK"),
-    "dense_dq": ("S", "dP", "dQ"),
-    "selected_kv_major": ("S", "dP", "dV", "dK"),
-    "selected_dq": ("S", "dP", "dQ"),
+    "dense_dq": ("dQ",),
+    "dense_dq_recompute": ("S", "dP", "dQ"),
+    "selected_kv_major": ("S", "dP", "dV", "dK", "dQ"),
     "dense_fp32": ("S", "dP", "dV", "dQ", "dK", "S", "dP"),
 }
 
