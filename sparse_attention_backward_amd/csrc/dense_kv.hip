@@ -122,7 +122,8 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
   using TR = RowTile<WR>;
   using TY = RowTile<WY>;
   constexpr int OQM = 0, OQR = TM::BYTES, OY = OQR + (DR > 0 ? TR::BYTES : 0);
-  constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = ORW + 256;  // stage: QM, QR, Y, lse2, drow
+  // stage: QM, QR, Y, lse2, drow, and two 256-byte slots the other waves' stat values land in
+  constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = ORW + 256 + 512;
   constexpr int NACC = 2 * (NQ + NV);
   constexpr int EPI = 2 * NACC * 1024 + 64 * (DQK + DV) * 2;           // epilogue buffers
   constexpr int SMEM = 2 * SB > EPI ? 2 * SB : EPI;
@@ -204,10 +205,13 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
   const uint32_t smem_lds = lds_addr(smem);
   const uint32_t rs_m = (uint32_t)a.n1 * DM * 2, rs_r = (uint32_t)a.n1 * DR * 2, rs_y = (uint32_t)a.n1 * DV * 2;
 
-  // Registers holding the next stage: W / 4 16-byte chunks per lane per part, plus one
-  // lse2 (wave 0) or drow (wave 1) value per lane (row = lane).
-  uint4 nm[WM / 4], nr[WR / 4], ny[WY / 4];
-  float nst = 0.f;
+  // Registers holding a stage on its way to LDS: W / 4 16-byte chunks per lane per part,
+  // plus one lse2 (wave 0) or drow (wave 1) value per lane (row = lane).  Two sets, for
+  // the stages one and two steps ahead.
+  struct Regs {
+    uint4 m[WM / 4], r[WR / 4], y[WY / 4];
+    float st;
+  };
   auto load_part = [&](auto wtag, const auto& pl, uint4* dst, const char* gtile, uint32_t rs, int nvalid) {
     constexpr int W = decltype(wtag)::value;
     constexpr int RPI = RowTile<W>::RPI;
@@ -217,35 +221,34 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
       dst[k] = ldg16(gtile + __umul24((uint32_t)r, rs) + pl.gchunk);
     }
   };
-  auto load_stage = [&](int st) {
+  auto load_stage = [&](int st, Regs& X) {
     int hg, qt;
     step_tile(st, hg, qt);
     const int nvalid = min(kRows, S1 - qt * kRows);
     const int64_t rh0 = (qs + (int64_t)qt * kRows) * a.n1 + kvh * a.G + hg;  // (first row) * n1 + h
-    load_part(std::integral_constant<int, WM>{}, pm, nm, reinterpret_cast<const char*>(a.q + rh0 * DM), rs_m, nvalid);
+    load_part(std::integral_constant<int, WM>{}, pm, X.m, reinterpret_cast<const char*>(a.q + rh0 * DM), rs_m, nvalid);
     if constexpr (DR > 0)
-      load_part(std::integral_constant<int, WR>{}, pr, nr, reinterpret_cast<const char*>(a.q_rope + rh0 * DR), rs_r,
+      load_part(std::integral_constant<int, WR>{}, pr, X.r, reinterpret_cast<const char*>(a.q_rope + rh0 * DR), rs_r,
                 nvalid);
-    load_part(std::integral_constant<int, WY>{}, py, ny, reinterpret_cast<const char*>(a.dy + rh0 * DV), rs_y, nvalid);
-    if (w < 2) {
-      const int64_t lrow = rh0 + (int64_t)min(lane, nvalid - 1) * a.n1;
-      nst = w == 0 ? a.lse2[lrow] : a.drow[lrow];
-    }
+    load_part(std::integral_constant<int, WY>{}, py, X.y, reinterpret_cast<const char*>(a.dy + rh0 * DV), rs_y, nvalid);
+    // every wave issues the same number of loads (waves 2, 3 read a value they drop)
+    const int64_t lrow = rh0 + (int64_t)min(lane, nvalid - 1) * a.n1;
+    X.st = w == 1 ? a.drow[lrow] : a.lse2[lrow];
   };
-  auto write_stage = [&](int soff) {
+  auto write_stage = [&](int soff, const Regs& X) {
     const uint32_t stage = smem_lds + soff;
 #pragma unroll
     for (int k = 0; k < WM / 4; ++k)
-      lds_st16_at(stage + OQM + (w + 4 * k) * 1024 + 16 * lane, nm[k]);
+      lds_st16_at(stage + OQM + (w + 4 * k) * 1024 + 16 * lane, X.m[k]);
     if constexpr (DR > 0) {
 #pragma unroll
       for (int k = 0; k < WR / 4; ++k)
-        lds_st16_at(stage + OQR + (w + 4 * k) * 1024 + 16 * lane, nr[k]);
+        lds_st16_at(stage + OQR + (w + 4 * k) * 1024 + 16 * lane, X.r[k]);
     }
 #pragma unroll
     for (int k = 0; k < WY / 4; ++k)
-      lds_st16_at(stage + OY + (w + 4 * k) * 1024 + 16 * lane, ny[k]);
-    if (w < 2) lds_st4_at(stage + OL + 256 * w + 4 * lane, nst);
+      lds_st16_at(stage + OY + (w + 4 * k) * 1024 + 16 * lane, X.y[k]);
+    lds_st4_at(stage + OL + 256 * w + 4 * lane, X.st);  // waves 2, 3: unused slots
   };
 
   // dS of the previous step, stored at the start of the next one (see the loop)
@@ -378,17 +381,20 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     }
   };
 
+  // this lane's place in the dS^T block [64 keys][64 rows] of step st's (query tile, key
+  // tile kt0, head)
+  auto ds_ptr = [&](int st) -> uint16_t* {
+    int hg, qt;
+    step_tile(st, hg, qt);
+    const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt0 : (int64_t)qt * nkt + kt0);
+    return a.ds + (blk * a.n1 + kvh * a.G + hg) * (int64_t)(kRows * kRows) + (32 * kh + l16) * kRows + 32 * rh + 4 * g;
+  };
   auto step = [&](int st, int soff) {
     int hg, qt;
     step_tile(st, hg, qt);
-    const int h = kvh * a.G + hg;
     const int nvalid = min(kRows, S1 - qt * kRows);
     const bool diag = a.causal && qt == kt0;
-    // the block's dS^T: [64 keys][64 rows] of (query tile qt, key tile kt0, head h)
-    if constexpr (DS) {
-      const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt0 : (int64_t)qt * nkt + kt0);
-      dsp = a.ds + (blk * a.n1 + h) * (int64_t)(kRows * kRows) + (32 * kh + l16) * kRows + 32 * rh + 4 * g;
-    }
+    if constexpr (DS) dsp = ds_ptr(st);
     if (diag && kh > rh) {  // every key of this wave lies after every row: P = dS = 0
 #pragma unroll
       for (int t = 0; t < 2; ++t) dsv[t][0] = dsv[t][1] = i16x4{0, 0, 0, 0};
@@ -401,28 +407,49 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     // rows 32rh + 4g + (0..3) and + 16; keys 32kh + 16t + l16
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      st8(dsp + 16 * t * kRows, dsv[t][0]);
-      st8(dsp + 16 * t * kRows + 16, dsv[t][1]);
+      *reinterpret_cast<i16x4*>(dsp + 16 * t * kRows) = dsv[t][0];
+      *reinterpret_cast<i16x4*>(dsp + 16 * t * kRows + 16) = dsv[t][1];
     }
   };
 
   // Iteration st: barrier (stage st is written; stage st+1 is no longer read), store the
-  // dS of step st-1, load stage st+1 into registers, compute step st, then write the
-  // registers into stage st+1.  The loads have a whole step to arrive.
+  // dS of step st-1, compute step st, write the registers holding stage st+1 into LDS and
+  // reload them with stage st+3.  Stage k's loads are issued at the end of iteration k-3
+  // and wait at the end of iteration k-1: two steps to arrive.  Iterations alternate
+  // between the two register sets (the loop is unrolled by two).
+  // The memory operations of every iteration are the same: the dS store of the previous
+  // step (in iteration 0 and before it: zeros into step 0's block, which step 0's own
+  // store overwrites later), the wait for one register set, the loads into it (past the
+  // last step they repeat the last stage, which is never written to LDS).  So the waits
+  // the compiler places before each write_stage count exactly the newer operations and
+  // leave the other set in flight.
+  Regs ra, rb;
   if (nsteps > 0) {
-    load_stage(0);
-    write_stage(0);
+    if constexpr (DS) {
+      dsp = ds_ptr(0);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) dsv[t][0] = dsv[t][1] = i16x4{0, 0, 0, 0};
+    }
+    load_stage(0, ra);
+    write_stage(0, ra);
+    load_stage(min(1, nsteps - 1), ra);
+    if constexpr (DS) store_ds();
+    load_stage(min(2, nsteps - 1), rb);
   }
-  for (int st = 0; st < nsteps; ++st) {
+  auto iteration = [&](int st, Regs& X) {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
     barrier_no_vm_wait();
-    if (DS && st > 0) store_ds();
-    const bool more = st + 1 < nsteps;
-    if (more) load_stage(st + 1);
-    asm volatile("" ::: "memory");  // keep the loads ahead of the step
+    if constexpr (DS) store_ds();
     step(st, (st & 1) * SB);
-    if (more) write_stage((~st & 1) * SB);
+    if (st + 1 < nsteps) write_stage((~st & 1) * SB, X);
+    load_stage(min(st + 3, nsteps - 1), X);
+  };
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    iteration(st, ra);
+    iteration(st + 1, rb);
   }
+  if (st < nsteps) iteration(st, ra);
   if (DS && nsteps > 0) store_ds();
 
   // ---- epilogue: sum the two row halves, bf16 through LDS, 16-byte stores ------------
