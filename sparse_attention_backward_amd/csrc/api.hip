@@ -32,8 +32,9 @@ struct Plan {
   int B = 0, G = 0;
   int64_t T1 = 0, T2 = 0;
   // dense schedule
-  std::vector<int32_t> kv_tiles, q_tiles;
+  std::vector<int32_t> kv_tiles, kv_split, q_tiles;
   std::vector<int64_t> ds_base;
+  int kv_slots = 0;       // fp32 partial slots of split key tiles
   bool dense_ds = false;  // dQ from stored dS tiles (else recomputed)
   // selected
   std::vector<int32_t> blkoff;
@@ -44,45 +45,73 @@ struct Plan {
   size_t off_lse2 = 0, off_drow = 0;
   size_t off_counts = 0, off_offsets = 0, off_cursor = 0, off_list = 0, off_scratch = 0, off_flag = 0;
   size_t off_dq_part = 0;
-  size_t off_ds_base = 0, off_ds = 0;
+  size_t off_ds_base = 0, off_ds = 0, off_kvsplit = 0, off_kvpart = 0;
   size_t total = 0;
 };
 
 constexpr int kXcds = 8;                          // workgroups are dealt to the XCDs round-robin
+constexpr int kCus = 256;                         // compute units (sets the key-tile split size only)
 constexpr uint64_t kDenseDsAutoMax = 8ull << 30;  // stored dS above this size: recompute instead
 
 // Dense schedule tables.
-//  * Key tiles (sequence, key tile, KV head): the tiles of one (sequence, KV head) read the
-//    same query rows, so each such group goes to one XCD (groups dealt to the least loaded
-//    XCD, largest first) and its tiles share that XCD's L2.  Within an XCD tiles run
-//    heaviest first.  Slot p of the launch belongs to XCD p % 8; slots an XCD does not
-//    need are idle (-1).  The dealing affects speed only, never results.
-//  * Query tiles (sequence, query tile), heaviest first.
-//  * ds_base: (query tile, key tile) blocks before each sequence (stored-dS layout).
+//  * Work items of the KV-major kernel: (sequence, 128-key tile, KV head, query-tile range,
+//    partial slot).  A key tile's query tiles (from its diagonal on when causal) form one
+//    range, or, when that is more than about a half of a CU's fair share of the whole
+//    launch, several ranges whose fp32 partials the combine kernel adds (in range order).
+//    The items of one (sequence, KV head) read the same query rows, so each such group
+//    goes to one XCD (groups dealt to the least loaded XCD, largest first) and its items
+//    share that XCD's L2.  Within an XCD items run heaviest first.  Slot p of the launch
+//    belongs to XCD p % 8; slots an XCD does not need are idle (-1).  The dealing and
+//    the split affect speed only, never results.
+//  * Split tiles (sequence, 128-key tile, KV head, first slot, ranges) for the combine.
+//  * Query tiles (sequence, 64-row query tile), heaviest first.
+//  * ds_base: (query tile, 64-key tile) blocks before each sequence (stored-dS layout).
 void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
   const int B = pl.B;
   const int64_t* cq = p->cu_seqlens_q;
   const int64_t* ck = p->cu_seqlens_kv;
-  struct W { int64_t work; int32_t b, tile, kvh; };
-  std::vector<std::vector<W>> groups;  // per (sequence, KV head)
-  std::vector<int64_t> gwork;
+  struct W { int64_t work; int32_t b, tile, kvh, qa, qb, slot; };
+  struct T { int32_t b, tile, kvh, qlo, qhi; };
+  std::vector<T> tiles;
   std::vector<W> qv;
+  int64_t total = 0;
   pl.ds_base.assign(B + 1, 0);
   for (int b = 0; b < B; ++b) {
     const int64_t S1 = cq[b + 1] - cq[b], S2 = ck[b + 1] - ck[b];
     const int64_t nqt = (S1 + kDenseTile - 1) / kDenseTile, nkt = (S2 + kDenseTile - 1) / kDenseTile;
+    const int64_t nkt2 = (S2 + kDenseKeyTile - 1) / kDenseKeyTile;
     pl.ds_base[b + 1] = pl.ds_base[b] + (p->causal ? nqt * (nqt + 1) / 2 : nqt * nkt);
-    for (int h = 0; h < p->n2; ++h) {
-      std::vector<W> gl;
-      int64_t tot = 0;
-      for (int64_t t = 0; t < nkt; ++t) {
-        const int64_t work = (p->causal ? std::max<int64_t>(nqt - t, 0) : nqt) * pl.G;
-        gl.push_back({work, b, (int32_t)t, h});
-        tot += work;
+    for (int h = 0; h < p->n2; ++h)
+      for (int64_t t = 0; t < nkt2; ++t) {
+        const int64_t qlo = p->causal ? std::min<int64_t>(2 * t, nqt) : 0;
+        tiles.push_back({b, (int32_t)t, h, (int32_t)qlo, (int32_t)nqt});
+        total += (nqt - qlo) * pl.G;
       }
-      if (!gl.empty()) { groups.push_back(std::move(gl)); gwork.push_back(tot); }
+    for (int64_t t = 0; t < nqt; ++t) qv.push_back({p->causal ? std::min(t + 1, nkt) : nkt, b, (int32_t)t, 0, 0, 0, 0});
+  }
+  // split size in query tiles: about half of a CU's share of all steps
+  const int64_t target = std::max<int64_t>(2 * pl.G, (total + 2 * kCus - 1) / (2 * kCus));
+  const int64_t qchunk = std::max<int64_t>(1, target / pl.G);
+  std::vector<std::vector<W>> groups;  // per (sequence, KV head)
+  std::vector<int64_t> gwork;
+  pl.kv_split.clear();
+  pl.kv_slots = 0;
+  for (size_t i = 0; i < tiles.size(); ++i) {
+    const T& t = tiles[i];
+    if (i == 0 || t.b != tiles[i - 1].b || t.kvh != tiles[i - 1].kvh) { groups.emplace_back(); gwork.push_back(0); }
+    const int64_t nq = t.qhi - t.qlo;
+    const int64_t parts = nq > qchunk ? (nq + qchunk - 1) / qchunk : 1;
+    const int32_t slot0 = parts > 1 ? pl.kv_slots : -1;
+    if (parts > 1) {
+      pl.kv_split.insert(pl.kv_split.end(), {t.b, t.tile, t.kvh, slot0, (int32_t)parts});
+      pl.kv_slots += (int)parts;
     }
-    for (int64_t t = 0; t < nqt; ++t) qv.push_back({p->causal ? std::min(t + 1, nkt) : nkt, b, (int32_t)t, 0});
+    for (int64_t q = 0; q < parts; ++q) {
+      const int32_t qa = (int32_t)(t.qlo + nq * q / parts), qb = (int32_t)(t.qlo + nq * (q + 1) / parts);
+      const int64_t work = std::max<int64_t>((int64_t)(qb - qa) * pl.G, 1);
+      groups.back().push_back({work, t.b, t.tile, t.kvh, qa, qb, parts > 1 ? slot0 + (int32_t)q : -1});
+      gwork.back() += work;
+    }
   }
   std::vector<size_t> order(groups.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = i;
@@ -99,13 +128,14 @@ void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
     std::stable_sort(bin.begin(), bin.end(), [](const W& x, const W& y) { return x.work > y.work; });
     rounds = std::max(rounds, bin.size());
   }
+  pl.kv_tiles.clear();
   for (size_t r = 0; r < rounds; ++r)
     for (int x = 0; x < kXcds; ++x) {
       if (r < bins[x].size()) {
         const W& t = bins[x][r];
-        pl.kv_tiles.insert(pl.kv_tiles.end(), {t.b, t.tile, t.kvh});
+        pl.kv_tiles.insert(pl.kv_tiles.end(), {t.b, t.tile, t.kvh, t.qa, t.qb, t.slot});
       } else {
-        pl.kv_tiles.insert(pl.kv_tiles.end(), {-1, 0, 0});
+        pl.kv_tiles.insert(pl.kv_tiles.end(), {-1, 0, 0, 0, 0, -1});
       }
     }
   std::stable_sort(qv.begin(), qv.end(), [](const W& x, const W& y) { return x.work > y.work; });
@@ -189,6 +219,8 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   pl.off_tab1 = o;
   if (p->op == ATTN_OP_DENSE) {
     o += 4 * pl.kv_tiles.size();
+    pl.off_kvsplit = o;
+    o += 4 * pl.kv_split.size();
     pl.off_tab2 = o;
     o += 4 * pl.q_tiles.size();
     o = (o + 7) / 8 * 8;
@@ -216,6 +248,10 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   if (p->op == ATTN_OP_DENSE && pl.dense_ds) {
     pl.off_ds = o;
     o = align_up(o + (size_t)pl.ds_base[pl.B] * p->n1 * kDenseTile * kDenseTile * 2);
+  }
+  if (p->op == ATTN_OP_DENSE && p->dtype == ATTN_BF16 && pl.kv_slots > 0) {
+    pl.off_kvpart = o;
+    o = align_up(o + (size_t)pl.kv_slots * kDenseKvPartBytes);
   }
   pl.total = o;
   return ATTN_OK;
@@ -285,6 +321,7 @@ std::vector<uint8_t> pack_tables(const attn_bwd_problem_t* p, const Plan& pl) {
   std::memcpy(t.data() + pl.off_cu_kv, p->cu_seqlens_kv, 8 * (size_t)(pl.B + 1));
   if (p->op == ATTN_OP_DENSE) {
     if (!pl.kv_tiles.empty()) std::memcpy(t.data() + pl.off_tab1, pl.kv_tiles.data(), 4 * pl.kv_tiles.size());
+    if (!pl.kv_split.empty()) std::memcpy(t.data() + pl.off_kvsplit, pl.kv_split.data(), 4 * pl.kv_split.size());
     if (!pl.q_tiles.empty()) std::memcpy(t.data() + pl.off_tab2, pl.q_tiles.data(), 4 * pl.q_tiles.size());
     std::memcpy(t.data() + pl.off_ds_base, pl.ds_base.data(), 8 * pl.ds_base.size());
   } else {
@@ -408,7 +445,10 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, 
   a.q_tiles = at<const int32_t>(workspace, pl.off_tab2);
   a.ds_base = at<const int64_t>(workspace, pl.off_ds_base);
   a.ds = pl.dense_ds ? at<void>(workspace, pl.off_ds) : nullptr;
-  a.n_kv_tiles = (int)(pl.kv_tiles.size() / 3);
+  a.kv_split = at<const int32_t>(workspace, pl.off_kvsplit);
+  a.kv_part = pl.kv_slots > 0 ? at<void>(workspace, pl.off_kvpart) : nullptr;
+  a.n_kv_tiles = (int)(pl.kv_tiles.size() / 6);
+  a.n_kv_split = (int)(pl.kv_split.size() / 5);
   a.n_q_tiles = (int)(pl.q_tiles.size() / 2);
   a.batch = pl.B; a.n1 = p->n1; a.n2 = p->n2; a.G = pl.G;
   a.T1 = pl.T1; a.T2 = pl.T2;

@@ -4,31 +4,36 @@
 // Page "aclnnFlashAttentionUnpaddingScoreGradV3", Formula section: dV = P^T dY,
 // dK = dS^T Q / sqrt(d), dkRope = dS^T qRope / sqrt(d), with Q = [query, queryRope].
 //
-// One workgroup (4 waves) owns a 64-key tile of one sequence and KV head.  Query rows
-// stream past in steps of 64 rows: the query tiles from the last one down to the diagonal
-// (causal) or down to the first, each for the G query heads of the KV head in turn.
+// One workgroup (4 waves) owns a 128-key tile of one sequence and KV head, and a range of
+// its query tiles.  Query rows stream past in steps of 64 rows: the query tiles of the
+// range from the last one down, each for the G query heads of the KV head in turn.
 // Walking every key tile's list from the same end keeps the workgroups of one
-// (sequence, KV head) on the same query tile at the same time, so their row loads
-// share the L2.
+// (sequence, KV head) on the same query tile at the same time, so their row loads share
+// the L2.  A step's rows are loaded once for 128 keys (half the load and LDS-write
+// traffic per flop of a 64-key tile, and half the barriers).
 //
-// The waves form a 2 x 2 grid: wave w owns keys 32(w&1) .. +31 of the tile (K and V
-// resident in registers as MFMA B operands) and rows 32(w>>1) .. +31 of every step.
-// Per step and wave (32 rows x 32 keys):
+// Wave w owns keys 32w .. +31 of the tile (K and V resident in registers as MFMA B
+// operands) and takes the two 32-row halves of every step in turn.  Per half (32 rows x
+// 32 keys):
 //   S = Q K^T, dP = dY V^T       A operands: Q / dY rows from LDS (16-byte reads)
 //   P = exp2(S*scale*log2e - lse2), dS = P (dP - drow)   (masks: causal diagonal,
 //                                 ragged query tail, ragged key tail)
 //   dV += P^T dY, dK += dS^T Q   A operands: the P / dS C tiles repacked in registers;
 //                                 B operands: dY / Q columns (ds_read_b64_tr_b16)
-//   dS^T -> workspace (bf16), one 64 x 64 block per (query tile, key tile, head)
-// Each key row's dK / dV is the sum of the two row-half waves' registers, added once
-// through LDS at the end.  Every output row has one writer: no atomics, deterministic.
+//   dS^T -> workspace (bf16), one 64 x 64 block per (query tile, 64-key tile, head)
+// Causal: a wave's 32-key block against a 32-row block is skipped when it lies wholly
+// after the rows, masked on the diagonal, and complete otherwise.
+//
+// Key tiles with many query tiles are split into ranges (so that no workgroup runs far
+// longer than the average): each range leaves its fp32 dK / dV in a partial slot, in
+// register order, and dense_kv_combine_kernel adds the ranges of a tile in range order.
+// Every output row has one writer: no atomics, deterministic.
 //
 // Staging: a step's Q (query and queryRope parts), dY, lse2 and drow are loaded into
-// registers one step ahead (while the current step computes) and written to one of two
-// LDS stages at the end of the step.  (Global->LDS transfers were measured to slow the
-// LDS reads of the compute phases in proportion to the bytes they move.)  Each part is a
-// RowTile: every load instruction reads whole rows (full cache lines) and the chunk
-// swizzle keeps the LDS writes and the row / column reads conflict free.
+// registers two steps ahead (two register sets) and written to one of two LDS stages at
+// the end of the step before.  Each part is a RowTile: every load instruction reads whole
+// rows (full cache lines) and the chunk swizzle keeps the LDS writes and the row / column
+// reads conflict free.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,7 +41,8 @@ namespace ab {
 
 namespace {
 
-constexpr int kRows = 64;  // query rows per step, keys per workgroup
+constexpr int kRows = 64;                // query rows per step, rows / keys of a dS block
+constexpr int kKeys = kDenseKeyTile;     // keys per workgroup
 typedef __attribute__((address_space(3))) void lds_void;
 
 struct DkvArgs {
@@ -47,8 +53,11 @@ struct DkvArgs {
   uint16_t* dk; uint16_t* dk_rope; uint16_t* dv;
   uint16_t* ds;               // [block][head][64 keys][64 rows] bf16 (dS transposed)
   const int64_t* cu_q; const int64_t* cu_kv;
-  const int64_t* ds_base;     // [B + 1] (query tile, key tile) blocks before each sequence
-  const int32_t* tiles;       // [n][3] (sequence, key tile, KV head); sequence < 0: idle slot
+  const int64_t* ds_base;     // [B + 1] (query tile, 64-key tile) blocks before each sequence
+  const int32_t* tiles;       // [n][6] (sequence, 128-key tile, KV head, first / end query tile,
+                              // partial slot or -1); sequence < 0: idle slot
+  const int32_t* split;       // [n][5] (sequence, 128-key tile, KV head, first slot, parts)
+  float* part;                // fp32 partials, kDenseKvPartBytes per slot
   int n1, n2, G;
   int causal;
   float scale, scale_log2e;
@@ -73,11 +82,6 @@ __device__ __forceinline__ void barrier_no_vm_wait() {
 __device__ __forceinline__ uint32_t lds_addr(const void* lds) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
 }
-// 8-byte store issued as inline assembly, so that the compiler does not hold back the
-// next step's loads behind it.
-__device__ __forceinline__ void st8(void* dst, i16x4 v) {
-  asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(dst), "v"(v) : "memory");
-}
 
 template <int N, typename F, int I = 0>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -91,9 +95,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 //   loads: the wave fills 1 KB blocks i = w + 4k (k < W/4) of the part; lane l fills row
 //              (w + 4k) RPI + l / W, slot l % W, i.e. reads chunk (l % W) ^ swz(row) --
 //              the same chunk for every k, because 4 RPI rows is a multiple of 16.
-//   row reads (A operands): rows 32rh + 16rt + l16, chunk 4s + g.
-//   column reads (transposed, B operands): rows 32rh + 4g + jj (+16), chunk 2j + qq/2,
-//              half qq&1.
+//   row reads (A operands): rows 16rt + l16, chunk 4s + g (+32 rows for the second half).
+//   column reads (transposed, B operands): rows 4g + jj (+16), chunk 2j + qq/2, half qq&1
+//              (+32 rows for the second half).
 template <int W>
 struct PartLanes {
   using T = RowTile<W>;
@@ -112,6 +116,45 @@ struct PartLanes {
   }
 };
 
+// dK (scaled) / dV of this wave's 32 keys from the accumulators to bf16 rows through LDS
+// (Ko [128][DQK], Vo [128][DV] at smem), then 16-byte stores of the rows < nk.
+template <int DM, int DR, int DV>
+__device__ __forceinline__ void store_dkdv(const DkvArgs& a, char* smem, const f32x4 (&dK)[2][(DM + DR) / 16],
+                                           const f32x4 (&dV)[2][DV / 16], int w, int lane, int64_t k0, int nk,
+                                           int kvh) {
+  constexpr int DQK = DM + DR, NQ = DQK / 16, NV = DV / 16;
+  const int l16 = lane & 15, g = lane >> 4;
+  uint16_t* Ko = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Vo = Ko + kKeys * DQK;
+  __syncthreads();  // LDS free
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ko[(32 * w + 16 * t + 4 * g + i) * DQK + 16 * n + l16] = f2bf(dK[t][n][i] * a.scale);
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Vo[(32 * w + 16 * t + 4 * g + i) * DV + 16 * n + l16] = f2bf(dV[t][n][i]);
+  }
+  __syncthreads();
+  constexpr int QCH = DQK / 8, YCH = DV / 8;
+  const int tid = 64 * w + lane;
+  for (int idx = tid; idx < kKeys * QCH; idx += 256) {
+    const int r = idx / QCH, c = idx - r * QCH, d = 8 * c;
+    if (r < nk) {
+      const int64_t kr = (k0 + r) * a.n2 + kvh;
+      uint16_t* dst = d < DM ? a.dk + kr * DM + d : a.dk_rope + kr * DR + (d - DM);
+      sts16(dst, *reinterpret_cast<const uint4*>(Ko + r * DQK + d));
+    }
+  }
+  for (int idx = tid; idx < kKeys * YCH; idx += 256) {
+    const int r = idx / YCH, c = idx - r * YCH;
+    if (r < nk) sts16(a.dv + ((k0 + r) * a.n2 + kvh) * DV + 8 * c, *reinterpret_cast<const uint4*>(Vo + r * DV + 8 * c));
+  }
+}
+
 template <int DM, int DR, int DV, bool DS>
 __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
   constexpr int DQK = DM + DR;
@@ -121,42 +164,41 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
   using TM = RowTile<WM>;
   using TR = RowTile<WR>;
   using TY = RowTile<WY>;
-  constexpr int OQM = 0, OQR = TM::BYTES, OY = OQR + (DR > 0 ? TR::BYTES : 0);
   // stage: QM, QR, Y, lse2, drow, and two 256-byte slots the other waves' stat values land in
+  constexpr int OQM = 0, OQR = TM::BYTES, OY = OQR + (DR > 0 ? TR::BYTES : 0);
   constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = ORW + 256 + 512;
-  constexpr int NACC = 2 * (NQ + NV);
-  constexpr int EPI = 2 * NACC * 1024 + 64 * (DQK + DV) * 2;           // epilogue buffers
+  constexpr int EPI = kKeys * (DQK + DV) * 2;  // epilogue: bf16 output tiles
   constexpr int SMEM = 2 * SB > EPI ? 2 * SB : EPI;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static_assert(2 * (NQ + NV) * 16 * 256 <= kDenseKvPartBytes, "partial slot size");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = w & 1, rh = w >> 1;
   const int l16 = lane & 15, g = lane >> 4;
 
-  const int b = a.tiles[3 * blockIdx.x];
+  const int32_t* tl = a.tiles + 6 * blockIdx.x;
+  const int b = tl[0];
   if (b < 0) return;  // idle slot of the schedule
-  const int kt0 = a.tiles[3 * blockIdx.x + 1];
-  const int kvh = a.tiles[3 * blockIdx.x + 2];
+  const int kt0 = tl[1], kvh = tl[2], qa = tl[3], qb = tl[4], slot = tl[5];
   const int64_t ks = a.cu_kv[b];
   const int S2 = (int)(a.cu_kv[b + 1] - ks);
-  const int64_t k0 = ks + (int64_t)kt0 * kRows;
-  const int nk = min(kRows, S2 - kt0 * kRows);
-  const int nkt = (S2 + kRows - 1) / kRows;
+  const int64_t k0 = ks + (int64_t)kt0 * kKeys;
+  const int nk = min(kKeys, S2 - kt0 * kKeys);
+  const int nkt64 = (S2 + kRows - 1) / kRows;
   const int64_t qs = a.cu_q[b];
   const int S1 = (int)(a.cu_q[b + 1] - qs);
-  const int nqt = (S1 + kRows - 1) / kRows;
-  const int qt0 = a.causal ? min(kt0, nqt) : 0;
-  const int nq = nqt - qt0;
-  const int nsteps = a.G * nq;
+  const int nsteps = a.G * (qb - qa);
   const int64_t blk0 = a.ds_base[b];
+  const int kb = 4 * kt0 + w;          // this wave's 32-key block
+  const int kt64 = 2 * kt0 + (w >> 1);  // its 64-key tile (dS block column)
+  const bool idle = 32 * w >= nk;       // every key of this wave lies past the sequence
 
   // ---- resident keys: K and V as MFMA B operands ------------------------------------
   bf16x8 Kf[2][KS], Vf[2][VS];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int key = 32 * kh + 16 * t + l16;
+    const int key = 32 * w + 16 * t + l16;
     const bool valid = key < nk;
     const int64_t kr = (k0 + key) * a.n2 + kvh;
 #pragma unroll
@@ -174,8 +216,7 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     }
   }
   // The K / V loads are the only vector-memory operations the compiler tracks; waiting for
-  // them here keeps it from placing a full wait (which would also drain the transfers
-  // issued ahead) inside the step loop, where the registers are first used.
+  // them here keeps it from placing a full wait inside the step loop.
   wait_vmcnt<0>();
 
   f32x4 dK[2][NQ], dV[2][NV];
@@ -190,16 +231,16 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
   PartLanes<WM> pm;
   PartLanes<WR> pr;
   PartLanes<WY> py;
-  pm.init(w, lane, rh);
-  if constexpr (DR > 0) pr.init(w, lane, rh);
-  py.init(w, lane, rh);
+  pm.init(w, lane, 0);
+  if constexpr (DR > 0) pr.init(w, lane, 0);
+  py.init(w, lane, 0);
 
-  // step st -> (query tile qt, head hg): query tiles walked from the last one down, the G
-  // heads of a query tile back to back
+  // step st -> (query tile qt, head hg): the range's query tiles from the last one down,
+  // the G heads of a query tile back to back
   auto step_tile = [&](int st, int& hg, int& qt) {
     const int i = st / a.G;
     hg = st - i * a.G;
-    qt = nqt - 1 - i;
+    qt = qb - 1 - i;
   };
 
   const uint32_t smem_lds = lds_addr(smem);
@@ -251,17 +292,35 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     lds_st4_at(stage + OL + 256 * w + 4 * lane, X.st);  // waves 2, 3: unused slots
   };
 
-  // dS of the previous step, stored at the start of the next one (see the loop)
-  i16x4 dsv[2][2];
-  uint16_t* dsp = nullptr;
 
-  // One step.  Masks, all applied outside the MFMA stream: rows past the end of the
-  // sequence get lse2 = +inf (P = 0); on the causal diagonal a short wave-uniform fix-up
-  // zeroes P where key > row; keys past the end only matter for the stored dS, which is
-  // zeroed for them (their dK / dV rows are never written).
-  auto step_body = [&](int nvalid, bool diag, int soff) {
-    const uint32_t stage = smem_lds + soff;
-    const uint32_t statb = opaque(stage + OL + 4 * (32 * rh + 4 * g));  // lse2; drow at + 256
+  // One half step: rows 32 hi .. +31 of step st.  Masks, all applied outside the MFMA
+  // stream: rows past the end of the sequence get lse2 = +inf (P = 0); on the causal
+  // diagonal a short wave-uniform fix-up zeroes P where key > row; keys past the end only
+  // matter for the stored dS, which is zeroed for them (their dK / dV rows are never
+  // written).
+  auto half_step = [&](int st, uint32_t stage, auto hic) {
+    constexpr int hi = decltype(hic)::value;
+    int hg, qt;
+    step_tile(st, hg, qt);
+    const int rb = 2 * qt + hi;  // this half's 32-row block
+    uint16_t* dsp = nullptr;
+    if constexpr (DS) {
+      if (kt64 < nkt64 && (!a.causal || kt64 <= qt)) {  // the block exists
+        const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt64 : (int64_t)qt * nkt64 + kt64);
+        dsp = a.ds + (blk * a.n1 + kvh * a.G + hg) * (int64_t)(kRows * kRows) + (32 * (w & 1) + l16) * kRows +
+              32 * hi + 4 * g;
+      }
+    }
+    // a wave with no key in the sequence, or with every key after every row, contributes
+    // nothing and only writes zeros to its part of an existing dS block
+    const bool active = !idle && !(a.causal && kb > rb);
+    bf16x8 da[2] = {bf16x8{}, bf16x8{}};
+    if (active) {
+    const bool diag = a.causal && kb == rb;
+    const int nvalid = min(kRows, S1 - qt * kRows);
+    const uint32_t bm = stage + OQM + hi * 32 * TM::RB, br = stage + OQR + hi * 32 * TR::RB;
+    const uint32_t by = stage + OY + hi * 32 * TY::RB;
+    const uint32_t statb = opaque(stage + OL + 4 * (32 * hi + 4 * g));  // lse2; drow at + 256
 
     f32x4 lse[2], dr[2];
 #pragma unroll
@@ -273,16 +332,16 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lse[rt][i] = 32 * rh + 16 * rt + 4 * g + i < nvalid ? lse[rt][i] : INFINITY;
+        for (int i = 0; i < 4; ++i) lse[rt][i] = 32 * hi + 16 * rt + 4 * g + i < nvalid ? lse[rt][i] : INFINITY;
     }
     // S = Q K^T, dP = dY V^T.  k-steps s < KSM read the query part, KSM <= s < KS the rope
     // part, the rest dY; the A fragments of a k-step (both row tiles) serve both key tiles
     // and are read PA k-steps ahead.
     constexpr int NS = KS + VS, PA = 3;
     auto afrag = [&](int s, int rt) -> bf16x8 {
-      if (s < KSM) return lds_b128_at(stage + OQM + pm.rowA[s] + rt * 16 * TM::RB);
-      if (s < KS) return lds_b128_at(stage + OQR + pr.rowA[s - KSM] + rt * 16 * TR::RB);
-      return lds_b128_at(stage + OY + py.rowA[s - KS] + rt * 16 * TY::RB);
+      if (s < KSM) return lds_b128_at(bm + pm.rowA[s] + rt * 16 * TM::RB);
+      if (s < KS) return lds_b128_at(br + pr.rowA[s - KSM] + rt * 16 * TR::RB);
+      return lds_b128_at(by + py.rowA[s - KS] + rt * 16 * TY::RB);
     };
     bf16x8 aring[PA][2];
 #pragma unroll
@@ -318,10 +377,10 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[t][rt][i] = __builtin_amdgcn_exp2f(S[t][rt][i] * a.scale_log2e - lse[rt][i]);
-    if (diag && kh == rh) {
-      // keys 32kh + 16t + l16 against rows 32rh + 16rt + 4g + i: with kh == rh, tile pair
-      // (t, rt) = (1, 0) lies wholly after the diagonal, (0, 1) wholly before it, and on
-      // (0, 0) / (1, 1) the key lies after the row iff l16 - 4g > i
+    if (diag) {
+      // keys 32kb + 16t + l16 against rows 32kb + 16rt + 4g + i: tile pair (t, rt) = (1, 0)
+      // lies wholly after the diagonal, (0, 1) wholly before it, and on (0, 0) / (1, 1)
+      // the key lies after the row iff l16 - 4g > i
       const int dl = l16 - 4 * g;
       S[1][0] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -340,21 +399,17 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     // dV += P^T dY, dK += dS^T Q.  Items j < NV: dY columns 16j.. (dV); then the query and
     // rope columns (dK).  Each column fragment (two transposed reads) serves both key tiles
     // and is read PD items ahead of its MFMAs.
-    bf16x8 pa[2], da[2];
+    bf16x8 pa[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       pa[t] = pack8(S[t][0], S[t][1]);
       da[t] = pack8(D[t][0], D[t][1]);
-      const i16x8 dv8 = __builtin_bit_cast(i16x8, da[t]);
-      dsv[t][0] = i16x4{dv8[0], dv8[1], dv8[2], dv8[3]};
-      dsv[t][1] = i16x4{dv8[4], dv8[5], dv8[6], dv8[7]};
-      if (nk < kRows && 32 * kh + 16 * t + l16 >= nk) dsv[t][0] = dsv[t][1] = i16x4{0, 0, 0, 0};
     }
     auto colfrag = [&](int j) -> bf16x8 {
       uint32_t o, second;
-      if (j < NV) { o = stage + OY + py.colB[j]; second = 16 * TY::RB; }
-      else if (j < NV + NQM) { o = stage + OQM + pm.colB[j - NV]; second = 16 * TM::RB; }
-      else { o = stage + OQR + pr.colB[j - NV - NQM]; second = 16 * TR::RB; }
+      if (j < NV) { o = by + py.colB[j]; second = 16 * TY::RB; }
+      else if (j < NV + NQM) { o = bm + pm.colB[j - NV]; second = 16 * TM::RB; }
+      else { o = br + pr.colB[j - NV - NQM]; second = 16 * TR::RB; }
       return join8(lds_tr16_at(o), lds_tr16_at(o + second));
     };
     constexpr int NJ = NV + NQ, PD = 4;
@@ -379,68 +434,42 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
       if (j + PD < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
-  };
-
-  // this lane's place in the dS^T block [64 keys][64 rows] of step st's (query tile, key
-  // tile kt0, head)
-  auto ds_ptr = [&](int st) -> uint16_t* {
-    int hg, qt;
-    step_tile(st, hg, qt);
-    const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt0 : (int64_t)qt * nkt + kt0);
-    return a.ds + (blk * a.n1 + kvh * a.G + hg) * (int64_t)(kRows * kRows) + (32 * kh + l16) * kRows + 32 * rh + 4 * g;
-  };
-  auto step = [&](int st, int soff) {
-    int hg, qt;
-    step_tile(st, hg, qt);
-    const int nvalid = min(kRows, S1 - qt * kRows);
-    const bool diag = a.causal && qt == kt0;
-    if constexpr (DS) dsp = ds_ptr(st);
-    if (diag && kh > rh) {  // every key of this wave lies after every row: P = dS = 0
+    }  // active
+    if constexpr (DS) {
+      // dS^T rows (keys) 32(w&1) + 16t + l16 of the 64-key tile, columns (query rows)
+      // 32hi + 4g + (0..3) and + 16
+      if (dsp != nullptr)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) dsv[t][0] = dsv[t][1] = i16x4{0, 0, 0, 0};
-      return;
-    }
-    step_body(nvalid, diag, soff);
-  };
-
-  auto store_ds = [&]() {
-    // rows 32rh + 4g + (0..3) and + 16; keys 32kh + 16t + l16
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      *reinterpret_cast<i16x4*>(dsp + 16 * t * kRows) = dsv[t][0];
-      *reinterpret_cast<i16x4*>(dsp + 16 * t * kRows + 16) = dsv[t][1];
+      for (int t = 0; t < 2; ++t) {
+        const i16x8 d8 = __builtin_bit_cast(i16x8, da[t]);
+        i16x4 lo = i16x4{d8[0], d8[1], d8[2], d8[3]}, hv = i16x4{d8[4], d8[5], d8[6], d8[7]};
+        if (nk < kKeys && 32 * w + 16 * t + l16 >= nk) lo = hv = i16x4{0, 0, 0, 0};
+        *reinterpret_cast<i16x4*>(dsp + 16 * t * kRows) = lo;
+        *reinterpret_cast<i16x4*>(dsp + 16 * t * kRows + 16) = hv;
+      }
     }
   };
 
-  // Iteration st: barrier (stage st is written; stage st+1 is no longer read), store the
-  // dS of step st-1, compute step st, write the registers holding stage st+1 into LDS and
-  // reload them with stage st+3.  Stage k's loads are issued at the end of iteration k-3
-  // and wait at the end of iteration k-1: two steps to arrive.  Iterations alternate
-  // between the two register sets (the loop is unrolled by two).
-  // The memory operations of every iteration are the same: the dS store of the previous
-  // step (in iteration 0 and before it: zeros into step 0's block, which step 0's own
-  // store overwrites later), the wait for one register set, the loads into it (past the
-  // last step they repeat the last stage, which is never written to LDS).  So the waits
-  // the compiler places before each write_stage count exactly the newer operations and
-  // leave the other set in flight.
+  // Iteration st: barrier (stage st is written; stage st+1 is no longer read), the two
+  // half steps of step st (each storing its dS^T), then the registers holding stage st+1
+  // go to LDS and are reloaded with stage st+3.  Stage k's loads are issued at the end of
+  // iteration k-3 and wait at the end of iteration k-1: two steps to arrive.  Iterations
+  // alternate between the two register sets (the loop is unrolled by two).  Past the last
+  // step the loads repeat the last stage (never written to LDS), so that every iteration
+  // issues the same loads.
   Regs ra, rb;
   if (nsteps > 0) {
-    if constexpr (DS) {
-      dsp = ds_ptr(0);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) dsv[t][0] = dsv[t][1] = i16x4{0, 0, 0, 0};
-    }
     load_stage(0, ra);
     write_stage(0, ra);
     load_stage(min(1, nsteps - 1), ra);
-    if constexpr (DS) store_ds();
     load_stage(min(2, nsteps - 1), rb);
   }
   auto iteration = [&](int st, Regs& X) {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
     barrier_no_vm_wait();
-    if constexpr (DS) store_ds();
-    step(st, (st & 1) * SB);
+    const uint32_t stage = smem_lds + (st & 1) * SB;
+    half_step(st, stage, std::integral_constant<int, 0>{});
+    half_step(st, stage, std::integral_constant<int, 1>{});
     if (st + 1 < nsteps) write_stage((~st & 1) * SB, X);
     load_stage(min(st + 3, nsteps - 1), X);
   };
@@ -450,63 +479,67 @@ __global__ __launch_bounds__(256, 1) void dense_kv_kernel(DkvArgs a) {
     iteration(st + 1, rb);
   }
   if (st < nsteps) iteration(st, ra);
-  if (DS && nsteps > 0) store_ds();
 
-  // ---- epilogue: sum the two row halves, bf16 through LDS, 16-byte stores ------------
-  __syncthreads();
-  // partials of the rh = 1 waves: [kh][index][lane] as f32x4 (conflict-free)
-  f32x4* part = reinterpret_cast<f32x4*>(smem);
-  if (rh == 1) {
+  // ---- epilogue --------------------------------------------------------------------------
+  if (slot < 0) {
+    store_dkdv<DM, DR, DV>(a, smem, dK, dV, w, lane, k0, nk, kvh);
+  } else {
+    // fp32 partial in register order: [wave][register][lane] f32x4, coalesced 16-byte stores
+    f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(a.part) + (size_t)slot * kDenseKvPartBytes) +
+                 w * (2 * (NQ + NV)) * 64 + lane;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int n = 0; n < NQ; ++n) part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane] = dK[t][n];
+      for (int n = 0; n < NQ; ++n) dst[(t * (NQ + NV) + n) * 64] = dK[t][n];
 #pragma unroll
-      for (int n = 0; n < NV; ++n) part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane] = dV[t][n];
+      for (int n = 0; n < NV; ++n) dst[(t * (NQ + NV) + NQ + n) * 64] = dV[t][n];
     }
-  }
-  __syncthreads();
-  // output tiles, row-major: dK [64 keys][DQK], dV [64 keys][DV]
-  uint16_t* Ko = reinterpret_cast<uint16_t*>(smem + 2 * NACC * 1024);
-  uint16_t* Vo = Ko + 64 * DQK;
-  if (rh == 0) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int n = 0; n < NQ; ++n) {
-        const f32x4 o = part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Ko[(32 * kh + 16 * t + 4 * g + i) * DQK + 16 * n + l16] = f2bf((dK[t][n][i] + o[i]) * a.scale);
-      }
-#pragma unroll
-      for (int n = 0; n < NV; ++n) {
-        const f32x4 o = part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Vo[(32 * kh + 16 * t + 4 * g + i) * DV + 16 * n + l16] = f2bf(dV[t][n][i] + o[i]);
-      }
-    }
-  }
-  __syncthreads();
-  constexpr int QCH = DQK / 8, YCH = DV / 8;
-  for (int idx = tid; idx < kRows * QCH; idx += 256) {
-    const int r = idx / QCH, c = idx - r * QCH, d = 8 * c;
-    if (r < nk) {
-      const int64_t kr = (k0 + r) * a.n2 + kvh;
-      uint16_t* dst = d < DM ? a.dk + kr * DM + d : a.dk_rope + kr * DR + (d - DM);
-      sts16(dst, *reinterpret_cast<const uint4*>(Ko + r * DQK + d));
-    }
-  }
-  for (int idx = tid; idx < kRows * YCH; idx += 256) {
-    const int r = idx / YCH, c = idx - r * YCH;
-    if (r < nk) sts16(a.dv + ((k0 + r) * a.n2 + kvh) * DV + 8 * c, *reinterpret_cast<const uint4*>(Vo + r * DV + 8 * c));
   }
 }
 
+// dK / dV of a split key tile: the partials of its query ranges added in range order.
 template <int DM, int DR, int DV>
-hipError_t launch_kv(const DkvArgs& k, dim3 grid, bool ds, hipStream_t s) {
-  if (ds) hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, true>), grid, dim3(256), 0, s, k);
-  else hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, false>), grid, dim3(256), 0, s, k);
+__global__ __launch_bounds__(256, 1) void dense_kv_combine_kernel(DkvArgs a) {
+  constexpr int DQK = DM + DR, NQ = DQK / 16, NV = DV / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[kKeys * (DQK + DV) * 2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t* sp = a.split + 5 * blockIdx.x;
+  const int b = sp[0], kt0 = sp[1], kvh = sp[2], slot0 = sp[3], parts = sp[4];
+  const int64_t ks = a.cu_kv[b];
+  const int S2 = (int)(a.cu_kv[b + 1] - ks);
+  const int64_t k0 = ks + (int64_t)kt0 * kKeys;
+  const int nk = min(kKeys, S2 - kt0 * kKeys);
+  f32x4 dK[2][NQ], dV[2][NV];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) dK[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < NV; ++n) dV[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int p = 0; p < parts; ++p) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(a.part) +
+                                                      (size_t)(slot0 + p) * kDenseKvPartBytes) +
+                       w * (2 * (NQ + NV)) * 64 + lane;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) dK[t][n] += src[(t * (NQ + NV) + n) * 64];
+#pragma unroll
+      for (int n = 0; n < NV; ++n) dV[t][n] += src[(t * (NQ + NV) + NQ + n) * 64];
+    }
+  }
+  store_dkdv<DM, DR, DV>(a, smem, dK, dV, w, lane, k0, nk, kvh);
+}
+
+template <int DM, int DR, int DV>
+hipError_t launch_kv(const DkvArgs& k, int n_tiles, int n_split, bool ds, hipStream_t s) {
+  if (n_tiles > 0) {
+    if (ds) hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, true>), dim3(n_tiles), dim3(256), 0, s, k);
+    else hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, false>), dim3(n_tiles), dim3(256), 0, s, k);
+  }
+  if (n_split > 0) hipLaunchKernelGGL((dense_kv_combine_kernel<DM, DR, DV>), dim3(n_split), dim3(256), 0, s, k);
   return hipGetLastError();
 }
 
@@ -526,14 +559,14 @@ hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) {
   k.lse2 = a.lse2; k.drow = a.drow;
   k.dk = (uint16_t*)a.dk; k.dk_rope = (uint16_t*)a.dk_rope; k.dv = (uint16_t*)a.dv;
   k.ds = (uint16_t*)a.ds;
-  k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.ds_base = a.ds_base; k.tiles = a.kv_tiles;
+  k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.ds_base = a.ds_base;
+  k.tiles = a.kv_tiles; k.split = a.kv_split; k.part = (float*)a.kv_part;
   k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;
   k.causal = a.causal; k.scale = a.scale; k.scale_log2e = a.scale_log2e;
-  const dim3 grid(a.n_kv_tiles);
   const bool ds = a.ds != nullptr;
-  if (a.d_main == 128 && a.d_rope == 64 && a.d_v == 128) return launch_kv<128, 64, 128>(k, grid, ds, s);
-  if (a.d_main == 128 && a.d_rope == 0 && a.d_v == 128) return launch_kv<128, 0, 128>(k, grid, ds, s);
-  if (a.d_main == 64 && a.d_rope == 0 && a.d_v == 64) return launch_kv<64, 0, 64>(k, grid, ds, s);
+  if (a.d_main == 128 && a.d_rope == 64 && a.d_v == 128) return launch_kv<128, 64, 128>(k, a.n_kv_tiles, a.n_kv_split, ds, s);
+  if (a.d_main == 128 && a.d_rope == 0 && a.d_v == 128) return launch_kv<128, 0, 128>(k, a.n_kv_tiles, a.n_kv_split, ds, s);
+  if (a.d_main == 64 && a.d_rope == 0 && a.d_v == 64) return launch_kv<64, 0, 64>(k, a.n_kv_tiles, a.n_kv_split, ds, s);
   return hipErrorInvalidValue;
 }
 

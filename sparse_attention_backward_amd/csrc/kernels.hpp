@@ -31,17 +31,22 @@ struct DenseArgs {
   void* ds;                 // bf16 dS^T blocks [block][N1][64][64] (stored-dS mode), else null
   const int64_t* cu_q;      // [B+1]
   const int64_t* cu_kv;     // [B+1]
-  const int64_t* ds_base;   // [B+1] (query tile, key tile) blocks before each sequence
-  const int32_t* kv_tiles;  // [n_kv_tiles, 3] = (sequence, key tile, KV head), -1 = idle slot
+  const int64_t* ds_base;   // [B+1] (query tile, 64-key tile) blocks before each sequence
+  const int32_t* kv_tiles;  // [n_kv_tiles, 6] = (sequence, 128-key tile, KV head, first query tile,
+                            //  end query tile, partial slot or -1); sequence -1 = idle slot
+  const int32_t* kv_split;  // [n_kv_split, 5] = (sequence, 128-key tile, KV head, first slot, parts)
+  void* kv_part;            // fp32 partial dK / dV of split key tiles, 160 KiB per slot
   const int32_t* q_tiles;   // [n_q_tiles, 2]  = (sequence, query tile), heaviest first
-  int n_kv_tiles, n_q_tiles;
+  int n_kv_tiles, n_kv_split, n_q_tiles;
   int batch, n1, n2, G;
   int64_t T1, T2;
   int d_main, d_rope, d_v;  // head dims: query/key main part, rope part, value
   float scale, scale_log2e;
   int causal;
 };
-constexpr int kDenseTile = 64;  // query and key tile length of the bf16 dense kernels
+constexpr int kDenseTile = 64;      // query tile and dS block length of the bf16 dense kernels
+constexpr int kDenseKeyTile = 128;  // keys per workgroup of the bf16 dense KV-major kernel
+constexpr int kDenseKvPartBytes = 256 * 40 * 16;  // one fp32 partial: 4 waves x 64 lanes x 40 f32x4
 bool dense_bf16_supported(int d_main, int d_rope, int d_v);
 hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s);     // KV-major dK, dV (+ dS when a.ds)
 hipError_t launch_dense_dq_from_ds(const DenseArgs& a, hipStream_t s);  // dQ = scale dS K from stored dS
