@@ -192,23 +192,43 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
       barrier_no_vm_wait();  // tile kt is in LDS; the other stage is free
       const uint32_t stage = smem_lds + (kt & 1) * SB;
       if (kt + 1 < nkt_run) issue(kt + 1, (~kt & 1) * SB);
+      // 2 HP column fragments of dS^T (items i = (ks2, hh, rt)) and, per ks2, NF column
+      // fragments of K.  The dS^T fragments run PD items ahead of their MFMAs; the K
+      // fragments of ks2 = 1 are read during ks2 = 0.
+      auto kfrag = [&](int f, int ks2) -> bf16x8 {
+        return join8(lds_tr16_at(stage + kcol[f][ks2][0]), lds_tr16_at(stage + kcol[f][ks2][1]));
+      };
+      auto dfrag = [&](int i) -> bf16x8 {
+        const int ks2 = i / (2 * HP), hh = (i / 2) % HP, rt = i % 2;
+        const uint32_t o = stage + OD + hh * TD::BYTES + dsA[rt] + ks2 * 32 * TD::RB;
+        return join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB));
+      };
+      constexpr int NI = 4 * HP, PD = 3;
+      bf16x8 kb0[NF], kb1[NF], dring[PD];
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        // K column fragments of this wave's feature tiles (keys 32 ks2 ..)
-        bf16x8 kb[NF];
+      for (int f = 0; f < NF; ++f) kb0[f] = kfrag(f, 0);
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
-          kb[f] = join8(lds_tr16_at(stage + kcol[f][ks2][0]), lds_tr16_at(stage + kcol[f][ks2][1]));
+      for (int i = 0; i < PD; ++i) dring[i] = dfrag(i);
 #pragma unroll
-        for (int hh = 0; hh < HP; ++hh) {
+      for (int i = 0; i < NI; ++i) {
+        const bf16x8 da = dring[i % PD];
+        if (i + PD < NI) dring[i % PD] = dfrag(i + PD);
+        if (i == 0) {
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            const uint32_t o = stage + OD + hh * TD::BYTES + dsA[rt] + ks2 * 32 * TD::RB;
-            const bf16x8 da = join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB));
-#pragma unroll
-            for (int f = 0; f < NF; ++f) acc[hh][rt][f] = mfma_16x16x32(da, kb[f], acc[hh][rt][f]);
-          }
+          for (int f = 0; f < NF; ++f) kb1[f] = kfrag(f, 1);
         }
+        const int hh = (i / 2) % HP, rt = i % 2;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[hh][rt][f] = mfma_16x16x32(da, i < 2 * HP ? kb0[f] : kb1[f], acc[hh][rt][f]);
+      }
+      // schedule: the first reads, then per item its MFMAs followed by the reads of the item
+      // PD ahead (and after item 0 the K fragments of ks2 = 1)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NF + 2 * PD, 0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
+        if (i + PD < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NF, 0);
       }
     }
 
