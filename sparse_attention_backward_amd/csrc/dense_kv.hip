@@ -534,12 +534,13 @@ __global__ __launch_bounds__(256, 1) void dense_kv_combine_kernel(DkvArgs a) {
 }
 
 template <int DM, int DR, int DV>
-hipError_t launch_kv(const DkvArgs& k, int n_tiles, int n_split, bool ds, hipStream_t s) {
-  if (n_tiles > 0) {
+hipError_t launch_kv(const DkvArgs& k, int n_tiles, int n_split, bool ds, bool combine, hipStream_t s) {
+  if (!combine && n_tiles > 0) {
     if (ds) hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, true>), dim3(n_tiles), dim3(256), 0, s, k);
     else hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, false>), dim3(n_tiles), dim3(256), 0, s, k);
   }
-  if (n_split > 0) hipLaunchKernelGGL((dense_kv_combine_kernel<DM, DR, DV>), dim3(n_split), dim3(256), 0, s, k);
+  if (combine && n_split > 0)
+    hipLaunchKernelGGL((dense_kv_combine_kernel<DM, DR, DV>), dim3(n_split), dim3(256), 0, s, k);
   return hipGetLastError();
 }
 
@@ -550,7 +551,7 @@ bool dense_bf16_supported(int d_main, int d_rope, int d_v) {
          (d_main == 64 && d_rope == 0 && d_v == 64);
 }
 
-hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) {
+static hipError_t launch_dense_kv_any(const DenseArgs& a, bool combine, hipStream_t s) {
   if (a.n_kv_tiles == 0) return hipSuccess;
   DkvArgs k{};
   k.q = (const uint16_t*)a.q; k.q_rope = (const uint16_t*)a.q_rope;
@@ -564,10 +565,16 @@ hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) {
   k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;
   k.causal = a.causal; k.scale = a.scale; k.scale_log2e = a.scale_log2e;
   const bool ds = a.ds != nullptr;
-  if (a.d_main == 128 && a.d_rope == 64 && a.d_v == 128) return launch_kv<128, 64, 128>(k, a.n_kv_tiles, a.n_kv_split, ds, s);
-  if (a.d_main == 128 && a.d_rope == 0 && a.d_v == 128) return launch_kv<128, 0, 128>(k, a.n_kv_tiles, a.n_kv_split, ds, s);
-  if (a.d_main == 64 && a.d_rope == 0 && a.d_v == 64) return launch_kv<64, 0, 64>(k, a.n_kv_tiles, a.n_kv_split, ds, s);
+  if (a.d_main == 128 && a.d_rope == 64 && a.d_v == 128)
+    return launch_kv<128, 64, 128>(k, a.n_kv_tiles, a.n_kv_split, ds, combine, s);
+  if (a.d_main == 128 && a.d_rope == 0 && a.d_v == 128)
+    return launch_kv<128, 0, 128>(k, a.n_kv_tiles, a.n_kv_split, ds, combine, s);
+  if (a.d_main == 64 && a.d_rope == 0 && a.d_v == 64) return launch_kv<64, 0, 64>(k, a.n_kv_tiles, a.n_kv_split, ds, combine, s);
   return hipErrorInvalidValue;
 }
+
+hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) { return launch_dense_kv_any(a, false, s); }
+
+hipError_t launch_dense_kv_combine(const DenseArgs& a, hipStream_t s) { return launch_dense_kv_any(a, true, s); }
 
 }  // namespace ab
