@@ -425,8 +425,10 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
         const i16x8 d8 = __builtin_bit_cast(i16x8, da[t]);
         i16x4 lo = i16x4{d8[0], d8[1], d8[2], d8[3]}, hv = i16x4{d8[4], d8[5], d8[6], d8[7]};
         if (nk < kKeys && 32 * p + 16 * t + l16 >= nk) lo = hv = i16x4{0, 0, 0, 0};
-        *reinterpret_cast<i16x4*>(dsp + 16 * t * kRows) = lo;
-        *reinterpret_cast<i16x4*>(dsp + 16 * t * kRows + 16) = hv;
+        // streaming stores: the dS blocks are read back only by the next kernel, so they
+        // should not push the query rows that other key tiles still read out of the L2
+        __builtin_nontemporal_store(lo, reinterpret_cast<i16x4*>(dsp + 16 * t * kRows));
+        __builtin_nontemporal_store(hv, reinterpret_cast<i16x4*>(dsp + 16 * t * kRows + 16));
       }
     };
 
