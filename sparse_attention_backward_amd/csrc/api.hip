@@ -70,7 +70,7 @@ void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
   const int B = pl.B;
   const int64_t* cq = p->cu_seqlens_q;
   const int64_t* ck = p->cu_seqlens_kv;
-  struct W { int64_t work; int32_t b, tile, kvh, qa, qb, slot; };
+  struct W { int64_t work; int32_t b, tile, kvh, qa, qb, slot, part, group; };
   struct T { int32_t b, tile, kvh, qlo, qhi; };
   std::vector<T> tiles;
   std::vector<W> qv;
@@ -87,9 +87,12 @@ void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
         tiles.push_back({b, (int32_t)t, h, (int32_t)qlo, (int32_t)nqt});
         total += (nqt - qlo) * pl.G;
       }
-    for (int64_t t = 0; t < nqt; ++t) qv.push_back({p->causal ? std::min(t + 1, nkt) : nkt, b, (int32_t)t, 0, 0, 0, 0});
+    for (int64_t t = 0; t < nqt; ++t) qv.push_back({p->causal ? std::min(t + 1, nkt) : nkt, b, (int32_t)t, 0, 0, 0, 0, 0, 0});
   }
-  // split size in query tiles: about half of a CU's share of all steps
+  // Split size in query tiles: about half of a CU's share of all steps.  The ranges are cut at
+  // the same query tiles for every key tile of a (sequence, KV head) -- counted from the last
+  // query tile down -- so that the parts that run together walk the same query rows and share
+  // them in the L2.
   const int64_t target = std::max<int64_t>(2 * pl.G, (total + 2 * kCus - 1) / (2 * kCus));
   const int64_t qchunk = std::max<int64_t>(1, target / pl.G);
   std::vector<std::vector<W>> groups;  // per (sequence, KV head)
@@ -107,9 +110,11 @@ void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
       pl.kv_slots += (int)parts;
     }
     for (int64_t q = 0; q < parts; ++q) {
-      const int32_t qa = (int32_t)(t.qlo + nq * q / parts), qb = (int32_t)(t.qlo + nq * (q + 1) / parts);
+      const int32_t qb = (int32_t)(t.qhi - q * qchunk);
+      const int32_t qa = parts > 1 ? (int32_t)std::max<int64_t>(t.qlo, qb - qchunk) : (int32_t)t.qlo;
       const int64_t work = std::max<int64_t>((int64_t)(qb - qa) * pl.G, 1);
-      groups.back().push_back({work, t.b, t.tile, t.kvh, qa, qb, parts > 1 ? slot0 + (int32_t)q : -1});
+      groups.back().push_back({work, t.b, t.tile, t.kvh, qa, qb, parts > 1 ? slot0 + (int32_t)q : -1, (int32_t)q,
+                               (int32_t)(groups.size() - 1)});
       gwork.back() += work;
     }
   }
@@ -124,8 +129,13 @@ void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
     bins[x].insert(bins[x].end(), groups[gi].begin(), groups[gi].end());
   }
   size_t rounds = 0;
+  // longest first; among equal lengths, the parts of one group and one range together
   for (auto& bin : bins) {
-    std::stable_sort(bin.begin(), bin.end(), [](const W& x, const W& y) { return x.work > y.work; });
+    std::stable_sort(bin.begin(), bin.end(), [](const W& x, const W& y) {
+      if (x.work != y.work) return x.work > y.work;
+      if (x.group != y.group) return x.group < y.group;
+      return x.part < y.part;
+    });
     rounds = std::max(rounds, bin.size());
   }
   pl.kv_tiles.clear();
