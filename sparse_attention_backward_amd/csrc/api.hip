@@ -268,7 +268,10 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
 }
 
 // ---- pinned staging ring for the per-call tables --------------------------------
-// A slot is reused only after the copy that last read it has executed (its event).
+// The tables are written to a pinned host slot and copied into the workspace by the first
+// kernel of the call (the row-statistics kernel reads the slot directly).  A slot is reused
+// only after that kernel has executed (the event recorded behind it); the device's ring lock
+// is held from choosing the slot until the event is recorded.
 struct StagingSlot {
   void* host = nullptr;
   size_t cap = 0;
@@ -283,47 +286,68 @@ struct DeviceStaging {
 std::mutex g_staging_mu;
 std::map<int, DeviceStaging*> g_staging;
 
-hipError_t upload_tables(const std::vector<uint8_t>& bytes, void* dst, hipStream_t s) {
-  if (bytes.empty()) return hipSuccess;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  DeviceStaging* ds;
-  {
-    std::lock_guard<std::mutex> lk(g_staging_mu);
-    auto it = g_staging.find(dev);
-    if (it == g_staging.end()) it = g_staging.emplace(dev, new DeviceStaging).first;
-    ds = it->second;
+class TableStage {
+ public:
+  ~TableStage() {
+    if (lock_.owns_lock()) lock_.unlock();
   }
-  std::lock_guard<std::mutex> lk(ds->mu);
-  StagingSlot& sl = ds->slots[ds->next];
-  ds->next = (ds->next + 1) % 4;
-  if (sl.pending) {
-    e = hipEventSynchronize(sl.ev);
+  // Copy bytes (zero-padded to a multiple of 16) into a free slot.
+  hipError_t stage(const std::vector<uint8_t>& bytes) {
+    if (bytes.empty()) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    sl.pending = false;
+    DeviceStaging* ds;
+    {
+      std::lock_guard<std::mutex> lk(g_staging_mu);
+      auto it = g_staging.find(dev);
+      if (it == g_staging.end()) it = g_staging.emplace(dev, new DeviceStaging).first;
+      ds = it->second;
+    }
+    lock_ = std::unique_lock<std::mutex>(ds->mu);
+    StagingSlot& sl = ds->slots[ds->next];
+    ds->next = (ds->next + 1) % 4;
+    if (sl.pending) {
+      e = hipEventSynchronize(sl.ev);
+      if (e != hipSuccess) return e;
+      sl.pending = false;
+    }
+    if (!sl.ev) {
+      e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+    const size_t padded = (bytes.size() + 15) / 16 * 16;
+    if (sl.cap < padded) {
+      if (sl.host) (void)hipHostFree(sl.host);
+      sl.host = nullptr;
+      sl.cap = 0;
+      const size_t cap = std::max<size_t>(padded, 4096);
+      e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
+      if (e != hipSuccess) return e;
+      sl.cap = cap;
+    }
+    std::memcpy(sl.host, bytes.data(), bytes.size());
+    std::memset(static_cast<uint8_t*>(sl.host) + bytes.size(), 0, padded - bytes.size());
+    slot_ = &sl;
+    n16_ = (int64_t)(padded / 16);
+    return hipSuccess;
   }
-  if (!sl.ev) {
-    e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
+  const void* src() const { return slot_ ? slot_->host : nullptr; }
+  int64_t n16() const { return n16_; }
+  // After the launch of the kernel that reads the slot: the slot is busy until it has run.
+  hipError_t commit(hipStream_t s) {
+    if (!slot_) return hipSuccess;
+    const hipError_t e = hipEventRecord(slot_->ev, s);
+    if (e == hipSuccess) slot_->pending = true;
+    lock_.unlock();
+    return e;
   }
-  if (sl.cap < bytes.size()) {
-    if (sl.host) (void)hipHostFree(sl.host);
-    sl.host = nullptr;
-    sl.cap = 0;
-    const size_t cap = std::max<size_t>(bytes.size(), 4096);
-    e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
-    if (e != hipSuccess) return e;
-    sl.cap = cap;
-  }
-  std::memcpy(sl.host, bytes.data(), bytes.size());
-  e = hipMemcpyAsync(dst, sl.host, bytes.size(), hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(sl.ev, s);
-  if (e != hipSuccess) return e;
-  sl.pending = true;
-  return hipSuccess;
-}
+
+ private:
+  std::unique_lock<std::mutex> lock_;
+  StagingSlot* slot_ = nullptr;
+  int64_t n16_ = 0;
+};
 
 std::vector<uint8_t> pack_tables(const attn_bwd_problem_t* p, const Plan& pl) {
   std::vector<uint8_t> t(pl.table_bytes, 0);
@@ -437,13 +461,17 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, 
   if (!has_q && !has_k) return ATTN_OK;
 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if (upload_tables(pack_tables(p, pl), workspace, s) != hipSuccess) return ATTN_ERR_HIP;
+  TableStage tables;
+  if (tables.stage(pack_tables(p, pl)) != hipSuccess) return ATTN_ERR_HIP;
 
   PreArgs pa{};
   pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
   pa.lse2 = at<float>(workspace, pl.off_lse2); pa.drow = at<float>(workspace, pl.off_drow);
   pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = p->dtype == ATTN_BF16;
+  pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
+  pa.tab_n16 = tables.n16();
   if (timed("row_stats", s, [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
 
   DenseArgs a{};
   a.q = q; a.q_rope = q_rope; a.k = k; a.k_rope = k_rope; a.v = v; a.dy = dy;
@@ -500,13 +528,17 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   if (!has_q && !has_k) return ATTN_OK;
 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if (upload_tables(pack_tables(p, pl), workspace, s) != hipSuccess) return ATTN_ERR_HIP;
+  TableStage tables;
+  if (tables.stage(pack_tables(p, pl)) != hipSuccess) return ATTN_ERR_HIP;
 
   PreArgs pa{};
   pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
   pa.lse2 = at<float>(workspace, pl.off_lse2); pa.drow = at<float>(workspace, pl.off_drow);
   pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = 1;
+  pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
+  pa.tab_n16 = tables.n16();
   if (timed("row_stats", s, [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
 
   SelArgs a{};
   a.q = q; a.k = k; a.v = v; a.dy = dy; a.lse2 = pa.lse2; a.drow = pa.drow; a.topk = topk_indices;

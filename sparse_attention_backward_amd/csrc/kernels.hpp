@@ -18,6 +18,9 @@ struct PreArgs {
   int64_t rows;           // T1 * N1
   int dv;
   int is_bf16;
+  const uint4* tab_src;   // the call's tables in pinned host memory (read by the kernel) ...
+  uint4* tab_dst;         // ... copied to the start of the workspace: tab_n16 16-byte words
+  int64_t tab_n16;
 };
 hipError_t launch_preprocess(const PreArgs& a, hipStream_t s);
 

@@ -1,4 +1,5 @@
-// Row statistics for the backward pass (both forms).
+// Row statistics for the backward pass (both forms); the same launch also copies the call's
+// tables (schedule, sequence offsets) from pinned host memory into the workspace.
 //
 // For every query row (t, h):
 //   lse2 = (softmaxMax + ln softmaxSum) * log2(e), so that P = exp2(s * scale * log2(e) - lse2)
@@ -36,8 +37,11 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
   const int sub = lane % LPR;
-  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  // the call's tables: pinned host memory -> workspace (read by the kernels that follow)
+  const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nthreads = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = gtid; i < a.tab_n16; i += nthreads) a.tab_dst[i] = a.tab_src[i];
+  const int64_t wave = gtid >> 6;
+  const int64_t nwaves = nthreads >> 6;
   for (int64_t base = wave * RPW; base < a.rows; base += nwaves * RPW) {
     const int64_t row = base + lane / LPR;
     float acc = 0.f;
@@ -79,7 +83,7 @@ static hipError_t launch_pre_t(const PreArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_preprocess(const PreArgs& a, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
+  if (a.rows == 0 && a.tab_n16 == 0) return hipSuccess;
   return a.is_bf16 ? launch_pre_t<uint16_t>(a, s) : launch_pre_t<float>(a, s);
 }
 
