@@ -497,12 +497,13 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, 
   if (p->dtype == ATTN_FP32)
     return timed("dense_fp32", s, [&] { return launch_dense_fp32(a, s); }) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   if (timed("dense_kv_major", s, [&] { return launch_dense_kv_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
-  if (a.n_kv_split > 0 &&
-      timed("dense_kv_combine", s, [&] { return launch_dense_kv_combine(a, s); }) != hipSuccess)
-    return ATTN_ERR_HIP;
   if (pl.dense_ds) {
+    // one launch: the split key tiles' dK / dV, then dQ = dS K
     if (timed("dense_dq", s, [&] { return launch_dense_dq_from_ds(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
   } else {
+    if (a.n_kv_split > 0 &&
+        timed("dense_kv_combine", s, [&] { return launch_dense_kv_combine(a, s); }) != hipSuccess)
+      return ATTN_ERR_HIP;
     if (timed("dense_dq_recompute", s, [&] { return launch_dense_dq_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
   }
   return ATTN_OK;

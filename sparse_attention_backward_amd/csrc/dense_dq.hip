@@ -14,6 +14,10 @@
 // tiles (RowTile layout: whole-row transfers, conflict-free column reads).  Keys are
 // taken in the order {4g + j, 16 + 4g + j} on both sides.  Fixed loop order, no atomics:
 // deterministic.
+//
+// The same launch also finishes the key tiles that the KV-major kernel split into query
+// ranges (both depend only on that kernel): its first n_split workgroups each add the fp32
+// partials of one split key tile in range order and write its dK (scaled) and dV rows.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -34,6 +38,12 @@ struct DqArgs {
   int n1, n2, G;
   int causal;
   float scale;
+  int n_q_tiles;                // workgroups n_split + (query tile, KV head) with kvh-major order
+  // split key tiles of the KV-major kernel
+  const int32_t* split;         // [n_split][5] (sequence, 128-key tile, KV head, first slot, parts)
+  const float* part;            // fp32 partials, kDenseKvPartBytes per slot, [pair][register][lane]
+  uint16_t* dk; uint16_t* dk_rope; uint16_t* dv;
+  int n_split;
 };
 
 template <int N>
@@ -84,6 +94,69 @@ struct KeyPartLanes {
   }
 };
 
+// dK / dV of split key tile sidx: the partials of its ranges added in range order, then bf16
+// rows through LDS (dK [128][DQK] scaled, dV [128][DV]) and 16-byte stores of rows < nk.
+template <int DM, int DR, int DV>
+__device__ __forceinline__ void combine_split_tile(const DqArgs& a, int sidx, char* smem) {
+  constexpr int DQK = DM + DR, NQ = DQK / 16, NV = DV / 16, KEYS = kDenseKeyTile;
+  static_assert(KEYS * (DQK + DV) * 2 <= 160 * 1024, "output tiles");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int32_t* sp = a.split + 5 * sidx;
+  const int b = sp[0], kt0 = sp[1], kvh = sp[2], slot0 = sp[3], parts = sp[4];
+  const int64_t ks = a.cu_kv[b];
+  const int S2 = (int)(a.cu_kv[b + 1] - ks);
+  const int64_t k0 = ks + (int64_t)kt0 * KEYS;
+  const int nk = min(KEYS, S2 - kt0 * KEYS);
+  f32x4 dK[2][NQ], dV[2][NV];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) dK[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < NV; ++n) dV[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int q = 0; q < parts; ++q) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(a.part) +
+                                                      (size_t)(slot0 + q) * kDenseKvPartBytes) +
+                       w * (2 * (NQ + NV)) * 64 + lane;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) dK[t][n] += src[(t * (NQ + NV) + n) * 64];
+#pragma unroll
+      for (int n = 0; n < NV; ++n) dV[t][n] += src[(t * (NQ + NV) + NQ + n) * 64];
+    }
+  }
+  uint16_t* Ko = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Vo = Ko + KEYS * DQK;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * w + 16 * t + 4 * g + i;
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) Ko[r * DQK + 16 * n + l16] = f2bf(dK[t][n][i] * a.scale);
+#pragma unroll
+      for (int n = 0; n < NV; ++n) Vo[r * DV + 16 * n + l16] = f2bf(dV[t][n][i]);
+    }
+  __syncthreads();
+  constexpr int QCH = DQK / 8, YCH = DV / 8;
+  for (int idx = tid; idx < KEYS * QCH; idx += 256) {
+    const int r = idx / QCH, c = idx - r * QCH, d = 8 * c;
+    if (r < nk) {
+      const int64_t kr = (k0 + r) * a.n2 + kvh;
+      uint16_t* dst = d < DM ? a.dk + kr * DM + d : a.dk_rope + kr * DR + (d - DM);
+      sts16(dst, *reinterpret_cast<const uint4*>(Ko + r * DQK + d));
+    }
+  }
+  for (int idx = tid; idx < KEYS * YCH; idx += 256) {
+    const int r = idx / YCH, c = idx - r * YCH;
+    if (r < nk) sts16(a.dv + ((k0 + r) * a.n2 + kvh) * DV + 8 * c, *reinterpret_cast<const uint4*>(Vo + r * DV + 8 * c));
+  }
+}
+
 template <int DM, int DR, int HP>
 __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
   constexpr int DQK = DM + DR;
@@ -96,15 +169,22 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
   constexpr int SB = OD + HP * TD::BYTES;                    // one stage
   static_assert(2 * SB <= 160 * 1024, "two stages must fit in LDS");
   static_assert(HP * kT * DQK * 2 <= 2 * SB, "output tiles must fit");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * SB];
+  constexpr int SMEM = 2 * SB > kDenseKeyTile * (DQK + DM) * 2 ? 2 * SB : kDenseKeyTile * (DQK + DM) * 2;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  if ((int)blockIdx.x < a.n_split) {  // a split key tile of the KV-major kernel (DV = DM)
+    combine_split_tile<DM, DR, DM>(a, blockIdx.x, smem);
+    return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fh = w & 1, rh = w >> 1;
   const int l16 = lane & 15, g = lane >> 4, jj = l16 >> 2, qq = l16 & 3;
 
-  const int b = a.tiles[2 * blockIdx.x], qt = a.tiles[2 * blockIdx.x + 1];
-  const int kvh = blockIdx.y;
+  const int wg = (int)blockIdx.x - a.n_split;
+  const int kvh = wg / a.n_q_tiles, qi = wg - kvh * a.n_q_tiles;
+  const int b = a.tiles[2 * qi], qt = a.tiles[2 * qi + 1];
   const int64_t qs = a.cu_q[b], ks = a.cu_kv[b];
   const int S1 = (int)(a.cu_q[b + 1] - qs), S2 = (int)(a.cu_kv[b + 1] - ks);
   const int nkt = (S2 + kT - 1) / kT;
@@ -269,8 +349,9 @@ hipError_t launch_hp(const DqArgs& k, int G, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_dense_dq_from_ds(const DenseArgs& a, hipStream_t s) {
-  if (a.n_q_tiles == 0) return hipSuccess;
+static hipError_t launch_dq_any(const DenseArgs& a, bool with_dq, hipStream_t s) {
+  const int n_q = with_dq ? a.n_q_tiles : 0;
+  if (n_q == 0 && a.n_kv_split == 0) return hipSuccess;
   DqArgs k{};
   k.k = (const uint16_t*)a.k; k.k_rope = (const uint16_t*)a.k_rope;
   k.ds = (const uint16_t*)a.ds;
@@ -278,11 +359,21 @@ hipError_t launch_dense_dq_from_ds(const DenseArgs& a, hipStream_t s) {
   k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.ds_base = a.ds_base; k.tiles = a.q_tiles;
   k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;
   k.causal = a.causal; k.scale = a.scale;
-  const dim3 grid(a.n_q_tiles, a.n2);
+  k.n_q_tiles = n_q;
+  k.split = a.kv_split; k.part = (const float*)a.kv_part;
+  k.dk = (uint16_t*)a.dk; k.dk_rope = (uint16_t*)a.dk_rope; k.dv = (uint16_t*)a.dv;
+  k.n_split = a.n_kv_split;
+  const dim3 grid(a.n_kv_split + n_q * a.n2);
   if (a.d_main == 128 && a.d_rope == 64) return launch_hp<128, 64>(k, a.G, grid, s);
   if (a.d_main == 128 && a.d_rope == 0) return launch_hp<128, 0>(k, a.G, grid, s);
   if (a.d_main == 64 && a.d_rope == 0) return launch_hp<64, 0>(k, a.G, grid, s);
   return hipErrorInvalidValue;
 }
+
+// dQ from the stored dS, together with the split key tiles of the KV-major kernel
+hipError_t launch_dense_dq_from_ds(const DenseArgs& a, hipStream_t s) { return launch_dq_any(a, true, s); }
+
+// the split key tiles alone (dQ recomputed elsewhere)
+hipError_t launch_dense_kv_combine(const DenseArgs& a, hipStream_t s) { return launch_dq_any(a, false, s); }
 
 }  // namespace ab

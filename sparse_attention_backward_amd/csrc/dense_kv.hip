@@ -29,7 +29,8 @@
 //
 // Key tiles with many query tiles are split into ranges (so that no workgroup runs far
 // longer than the average): each range leaves its fp32 dK / dV in a partial slot, in
-// register order, and dense_kv_combine_kernel adds the ranges of a tile in range order.
+// register order, and the first workgroups of the dQ launch add the ranges of a tile in
+// range order.
 // Every output row has one writer: no atomics, deterministic.
 //
 // Staging: a step's Q (query and queryRope parts), dY, lse2 and drow go from global memory
@@ -564,55 +565,10 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
                                 reinterpret_cast<const uint16_t*>(smem) + kKeys * DQK, tid, 512, k0, nk, kvh);
 }
 
-// dK / dV of a split key tile: the partials of its query ranges added in range order.
 template <int DM, int DR, int DV>
-__global__ __launch_bounds__(256, 1) void dense_kv_combine_kernel(DkvArgs a) {
-  constexpr int DQK = DM + DR, NQ = DQK / 16, NV = DV / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[kKeys * (DQK + DV) * 2];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t* sp = a.split + 5 * blockIdx.x;
-  const int b = sp[0], kt0 = sp[1], kvh = sp[2], slot0 = sp[3], parts = sp[4];
-  const int64_t ks = a.cu_kv[b];
-  const int S2 = (int)(a.cu_kv[b + 1] - ks);
-  const int64_t k0 = ks + (int64_t)kt0 * kKeys;
-  const int nk = min(kKeys, S2 - kt0 * kKeys);
-  f32x4 dK[2][NQ], dV[2][NV];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) dK[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int n = 0; n < NV; ++n) dV[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int p = 0; p < parts; ++p) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(a.part) +
-                                                      (size_t)(slot0 + p) * kDenseKvPartBytes) +
-                       w * (2 * (NQ + NV)) * 64 + lane;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int n = 0; n < NQ; ++n) dK[t][n] += src[(t * (NQ + NV) + n) * 64];
-#pragma unroll
-      for (int n = 0; n < NV; ++n) dV[t][n] += src[(t * (NQ + NV) + NQ + n) * 64];
-    }
-  }
-  uint16_t* Ko = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Vo = Ko + kKeys * DQK;
-  acc_to_lds<DQK>(Ko, dK, w, lane, a.scale);
-  acc_to_lds<DV>(Vo, dV, w, lane, 1.f);
-  __syncthreads();
-  tiles_to_global<DM, DR, DV>(a, Ko, Vo, tid, 256, k0, nk, kvh);
-}
-
-template <int DM, int DR, int DV>
-hipError_t launch_kv(const DkvArgs& k, int n_tiles, int n_split, bool ds, bool combine, hipStream_t s) {
-  if (!combine && n_tiles > 0) {
-    if (ds) hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, true>), dim3(n_tiles), dim3(512), 0, s, k);
-    else hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, false>), dim3(n_tiles), dim3(512), 0, s, k);
-  }
-  if (combine && n_split > 0)
-    hipLaunchKernelGGL((dense_kv_combine_kernel<DM, DR, DV>), dim3(n_split), dim3(256), 0, s, k);
+hipError_t launch_kv(const DkvArgs& k, int n_tiles, bool ds, hipStream_t s) {
+  if (ds) hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, true>), dim3(n_tiles), dim3(512), 0, s, k);
+  else hipLaunchKernelGGL((dense_kv_kernel<DM, DR, DV, false>), dim3(n_tiles), dim3(512), 0, s, k);
   return hipGetLastError();
 }
 
@@ -623,7 +579,7 @@ bool dense_bf16_supported(int d_main, int d_rope, int d_v) {
          (d_main == 64 && d_rope == 0 && d_v == 64);
 }
 
-static hipError_t launch_dense_kv_any(const DenseArgs& a, bool combine, hipStream_t s) {
+hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) {
   if (a.n_kv_tiles == 0) return hipSuccess;
   DkvArgs k{};
   k.q = (const uint16_t*)a.q; k.q_rope = (const uint16_t*)a.q_rope;
@@ -638,15 +594,12 @@ static hipError_t launch_dense_kv_any(const DenseArgs& a, bool combine, hipStrea
   k.causal = a.causal; k.scale = a.scale; k.scale_log2e = a.scale_log2e;
   const bool ds = a.ds != nullptr;
   if (a.d_main == 128 && a.d_rope == 64 && a.d_v == 128)
-    return launch_kv<128, 64, 128>(k, a.n_kv_tiles, a.n_kv_split, ds, combine, s);
+    return launch_kv<128, 64, 128>(k, a.n_kv_tiles, ds, s);
   if (a.d_main == 128 && a.d_rope == 0 && a.d_v == 128)
-    return launch_kv<128, 0, 128>(k, a.n_kv_tiles, a.n_kv_split, ds, combine, s);
-  if (a.d_main == 64 && a.d_rope == 0 && a.d_v == 64) return launch_kv<64, 0, 64>(k, a.n_kv_tiles, a.n_kv_split, ds, combine, s);
+    return launch_kv<128, 0, 128>(k, a.n_kv_tiles, ds, s);
+  if (a.d_main == 64 && a.d_rope == 0 && a.d_v == 64) return launch_kv<64, 0, 64>(k, a.n_kv_tiles, ds, s);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) { return launch_dense_kv_any(a, false, s); }
-
-hipError_t launch_dense_kv_combine(const DenseArgs& a, hipStream_t s) { return launch_dense_kv_any(a, true, s); }
 
 }  // namespace ab

@@ -52,8 +52,8 @@ constexpr int kDenseKeyTile = 128;  // keys per workgroup of the bf16 dense KV-m
 constexpr int kDenseKvPartBytes = 256 * 40 * 16;  // one fp32 partial: 4 waves x 64 lanes x 40 f32x4
 bool dense_bf16_supported(int d_main, int d_rope, int d_v);
 hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s);     // KV-major dK, dV (+ dS when a.ds)
-hipError_t launch_dense_kv_combine(const DenseArgs& a, hipStream_t s);  // dK, dV of split key tiles
-hipError_t launch_dense_dq_from_ds(const DenseArgs& a, hipStream_t s);  // dQ = scale dS K from stored dS
+hipError_t launch_dense_kv_combine(const DenseArgs& a, hipStream_t s);  // dK, dV of split key tiles alone
+hipError_t launch_dense_dq_from_ds(const DenseArgs& a, hipStream_t s);  // split key tiles + dQ = scale dS K
 hipError_t launch_dense_dq_bf16(const DenseArgs& a, hipStream_t s);     // query-major dQ, recomputing S, dP
 constexpr int kDenseTileF32 = 64;
 hipError_t launch_dense_fp32(const DenseArgs& a, hipStream_t s);
