@@ -103,16 +103,16 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Per-lane addressing of one staged part (a RowTile of W chunks per row).
-//   transfers: wave w (of 8) fills 1 KB blocks i = w + 8k (k < W/8) of the part; lane l
+//   transfers: S wave w (of 4) fills 1 KB blocks i = w + 4k (k < W/4) of the part; lane l
 //              fills row i RPI + l / W, slot l % W, i.e. reads chunk (l % W) ^ swz(row) --
-//              the same chunk for every k, because 8 RPI rows is a multiple of 16.
+//              the same chunk for every k, because 4 RPI rows is a multiple of 16.
 //   row reads (A operands): rows 16rt + l16, chunk 4s + g (+32 rows for the second half).
 //   column reads (transposed, B operands): rows 4g + jj (+16), chunk 2j + qq/2, half qq&1
 //              (+32 rows for the second half).
 template <int W>
 struct PartLanes {
   using T = RowTile<W>;
-  static_assert(W % 8 == 0, "whole blocks per wave");
+  static_assert(W % 4 == 0, "whole blocks per wave");
   int row0;          // transfer row for k = 0
   uint32_t gchunk;   // byte offset of the chunk this lane reads within its row
   __device__ __forceinline__ void init(int w, int lane) {
@@ -218,16 +218,18 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
   if constexpr (DR > 0) pr.init(w, lane);
   py.init(w, lane);
 
-  // Transfers of step st into the stage at LDS address stage: this wave's blocks of each
-  // part (rows past the end of the sequence repeat its last row), and the lse2 (wave 0) or
-  // drow (wave 1) values of the 64 rows.
+  // Transfers of step st into the stage at LDS address stage, issued by the S waves only
+  // (so that the dP waves never wait for vector-memory counts and their dS stores stay in
+  // flight across barriers): this wave's blocks of each part (rows past the end of the
+  // sequence repeat its last row), and the lse2 (wave 0) or drow (wave 1) values of the 64
+  // rows.
   auto issue_part = [&](auto wtag, const auto& pl, const char* gtile, uint32_t rs, uint32_t lds_part, int nvalid) {
     constexpr int W = decltype(wtag)::value;
     constexpr int RPI = RowTile<W>::RPI;
-    static_for<W / 8>([&](auto kc) {
+    static_for<W / 4>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      const int r = min(pl.row0 + 8 * RPI * k, nvalid - 1);
-      dma16<8192 * k>(gtile + __umul24((uint32_t)r, rs) + pl.gchunk, lds_part + w * 1024);
+      const int r = min(pl.row0 + 4 * RPI * k, nvalid - 1);
+      dma16<4096 * k>(gtile + __umul24((uint32_t)r, rs) + pl.gchunk, lds_part + w * 1024);
     });
   };
   auto issue_stage = [&](int st, uint32_t stage) {
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
     return !idle && !(a.causal && kb > rb);
   };
 
-  if (nsteps > 0) issue_stage(0, smem_lds);
+  if (nsteps > 0 && swave) issue_stage(0, smem_lds);
 
   if (swave) {
     // ---------------- S waves: S, P, dV -------------------------------------------------
@@ -418,35 +420,48 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
 #pragma unroll
       for (int n = 0; n < NQ; ++n) dK[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // dS^T of one half step: rows (keys) 32(p&1) + 16t + l16 of the 64-key tile, columns
-    // (query rows) 32hi + 4g + (0..3) and + 16; zeros for keys past the end of the sequence
-    auto store_ds = [&](uint16_t* dsp, const bf16x8 (&da)[2]) {
+    // dS^T of one step: rows (keys) 32(p&1) + 16t + l16 of the 64-key tile, all 64 columns
+    // (query rows).  After half step hi a lane holds, per key tile, the 4-column pieces
+    // 8hi + g (columns 32hi + 4g ..) and 8hi + 4 + g (+16).  One lane swap between rows g and
+    // g ^ 1 of the wave (v_permlane16_swap: an even row keeps its first operand and receives
+    // the odd row's first; an odd row receives the even row's second and keeps its own)
+    // leaves every lane two adjacent pieces, 16 bytes: pieces 8hi + {g, g + 1} for even g,
+    // 8hi + {g + 3, g + 4} for odd g, so the four lanes of a key row write 64 contiguous bytes
+    // per half.  Zeros for keys past the end of the sequence.
+    auto pair_pieces = [&](const bf16x8& d) -> u32x4 {
+      const u32x4 v = __builtin_bit_cast(u32x4, d);
+      const auto s0 = __builtin_amdgcn_permlane16_swap(v[0], v[2], false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(v[1], v[3], false, false);
+      return u32x4{s0[0], s1[0], s0[1], s1[1]};
+    };
+    const int piece_col = (g & 1) ? 4 * g + 12 : 4 * g;
+    auto store_ds = [&](uint16_t* row, const u32x4 (&c0)[2], const u32x4 (&c1)[2]) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const i16x8 d8 = __builtin_bit_cast(i16x8, da[t]);
-        i16x4 lo = i16x4{d8[0], d8[1], d8[2], d8[3]}, hv = i16x4{d8[4], d8[5], d8[6], d8[7]};
-        if (nk < kKeys && 32 * p + 16 * t + l16 >= nk) lo = hv = i16x4{0, 0, 0, 0};
+        u32x4 x0 = c0[t], x1 = c1[t];
+        if (nk < kKeys && 32 * p + 16 * t + l16 >= nk) x0 = x1 = u32x4{0u, 0u, 0u, 0u};
         // streaming stores: the dS blocks are read back only by the next kernel, so they
         // should not push the query rows that other key tiles still read out of the L2
-        __builtin_nontemporal_store(lo, reinterpret_cast<i16x4*>(dsp + 16 * t * kRows));
-        __builtin_nontemporal_store(hv, reinterpret_cast<i16x4*>(dsp + 16 * t * kRows + 16));
+        __builtin_nontemporal_store(x0, reinterpret_cast<u32x4*>(row + 16 * t * kRows + piece_col));
+        __builtin_nontemporal_store(x1, reinterpret_cast<u32x4*>(row + 16 * t * kRows + 32 + piece_col));
       }
     };
 
-    // A half step leaves its dS (zero where the pair's block is skipped) in da and the
-    // address of its part of the dS^T block, or nullptr when no block exists, in dsp.
-    auto dp_half = [&](int st, uint32_t stage, auto hic, uint16_t*& dsp, bf16x8 (&da)[2]) {
+    // The dS^T row of this lane's key in the block of step st, or nullptr when no block
+    // exists (causal: the key tile lies after the query tile).
+    auto ds_row = [&](int st) -> uint16_t* {
+      int hg, qt;
+      step_tile(st, hg, qt);
+      if (!(kt64 < nkt64 && (!a.causal || kt64 <= qt))) return nullptr;
+      const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt64 : (int64_t)qt * nkt64 + kt64);
+      return a.ds + (blk * a.n1 + kvh * a.G + hg) * (int64_t)(kRows * kRows) + (32 * (p & 1) + l16) * kRows;
+    };
+
+    // A half step leaves its dS in da: zero where the pair's block is skipped.
+    auto dp_half = [&](int st, uint32_t stage, auto hic, bf16x8 (&da)[2]) {
       constexpr int hi = decltype(hic)::value;
       int hg, qt, rb;
       const bool active = half_active(st, hi, hg, qt, rb);
-      dsp = nullptr;
-      if constexpr (DS) {
-        if (kt64 < nkt64 && (!a.causal || kt64 <= qt)) {  // the block exists
-          const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt64 : (int64_t)qt * nkt64 + kt64);
-          dsp = a.ds + (blk * a.n1 + kvh * a.G + hg) * (int64_t)(kRows * kRows) + (32 * (p & 1) + l16) * kRows +
-                32 * hi + 4 * g;
-        }
-      }
       da[0] = da[1] = bf16x8{};
       if (!active) return;
       const uint32_t bm = stage + OQM + hi * 32 * TM::RB, br = stage + OQR + hi * 32 * TR::RB;
@@ -519,31 +534,32 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       }
     };
 
-    // Iteration st handles step st - 1.  The dS stores of its second half step are issued
-    // after the next barrier, so that the wait before that barrier does not stall on stores
-    // issued just before it.
-    uint16_t* dsp_pend = nullptr;
-    bf16x8 da_pend[2] = {bf16x8{}, bf16x8{}};
+    // Iteration st handles step st - 1 and stores its dS^T rows at the end.  The barrier
+    // waits only for this wave's LDS accesses: its stores stay in flight.
     for (int st = 0; st <= nsteps; ++st) {
-      barrier_all_done();
-      if (st + 1 < nsteps) issue_stage(st + 1, stage_of(st + 1));
-      if constexpr (DS) {
-        if (dsp_pend != nullptr) store_ds(dsp_pend, da_pend);
-      }
-      dsp_pend = nullptr;
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       if (st > 0) {
         const uint32_t stage = stage_of(st - 1);
-        uint16_t* dsp;
         bf16x8 da[2];
-        dp_half(st - 1, stage, std::integral_constant<int, 0>{}, dsp, da);
+        u32x4 c0[2], c1[2];
+        dp_half(st - 1, stage, std::integral_constant<int, 0>{}, da);
         if constexpr (DS) {
-          if (dsp != nullptr) store_ds(dsp, da);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) c0[t] = pair_pieces(da[t]);
         }
-        dp_half(st - 1, stage, std::integral_constant<int, 1>{}, dsp_pend, da_pend);
+        dp_half(st - 1, stage, std::integral_constant<int, 1>{}, da);
+        if constexpr (DS) {
+          uint16_t* row = ds_row(st - 1);
+          if (row != nullptr) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) c1[t] = pair_pieces(da[t]);
+            store_ds(row, c0, c1);
+          }
+        }
       }
-    }
-    if constexpr (DS) {
-      if (dsp_pend != nullptr) store_ds(dsp_pend, da_pend);
     }
 
     // ---- epilogue: dK (scaled) ----
