@@ -94,56 +94,53 @@ struct KeyPartLanes {
   }
 };
 
-// dK / dV of split key tile sidx: the partials of its ranges added in range order, then bf16
-// rows through LDS (dK [128][DQK] scaled, dV [128][DV]) and 16-byte stores of rows < nk.
+// dK / dV of split key tile sidx: the partials of its ranges added in range order (waves
+// 0-3: dK of key pair w, waves 4-7: dV of key pair w - 4), then bf16 rows through LDS
+// (dK [128][DQK] scaled, dV [128][DV]) and 16-byte stores of rows < nk.
 template <int DM, int DR, int DV>
 __device__ __forceinline__ void combine_split_tile(const DqArgs& a, int sidx, char* smem) {
   constexpr int DQK = DM + DR, NQ = DQK / 16, NV = DV / 16, KEYS = kDenseKeyTile;
   static_assert(KEYS * (DQK + DV) * 2 <= 160 * 1024, "output tiles");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, g = lane >> 4;
+  const int pr = w & 3, l16 = lane & 15, g = lane >> 4;
   const int32_t* sp = a.split + 5 * sidx;
   const int b = sp[0], kt0 = sp[1], kvh = sp[2], slot0 = sp[3], parts = sp[4];
   const int64_t ks = a.cu_kv[b];
   const int S2 = (int)(a.cu_kv[b + 1] - ks);
   const int64_t k0 = ks + (int64_t)kt0 * KEYS;
   const int nk = min(KEYS, S2 - kt0 * KEYS);
-  f32x4 dK[2][NQ], dV[2][NV];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) dK[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int n = 0; n < NV; ++n) dV[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int q = 0; q < parts; ++q) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(a.part) +
-                                                      (size_t)(slot0 + q) * kDenseKvPartBytes) +
-                       w * (2 * (NQ + NV)) * 64 + lane;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int n = 0; n < NQ; ++n) dK[t][n] += src[(t * (NQ + NV) + n) * 64];
-#pragma unroll
-      for (int n = 0; n < NV; ++n) dV[t][n] += src[(t * (NQ + NV) + NQ + n) * 64];
-    }
-  }
   uint16_t* Ko = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Vo = Ko + KEYS * DQK;
+  // one kind of accumulator per wave: N tiles at register offset R of the pair's slot region
+  auto sum_parts = [&](auto nc, auto rc, uint16_t* tile, int D, float sc) {
+    constexpr int N = decltype(nc)::value, R = decltype(rc)::value;
+    f32x4 acc[2][N];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 32 * w + 16 * t + 4 * g + i;
+      for (int n = 0; n < N; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < parts; ++q) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(a.part) +
+                                                        (size_t)(slot0 + q) * kDenseKvPartBytes) +
+                         pr * (2 * (NQ + NV)) * 64 + lane;
 #pragma unroll
-      for (int n = 0; n < NQ; ++n) Ko[r * DQK + 16 * n + l16] = f2bf(dK[t][n][i] * a.scale);
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int n = 0; n < NV; ++n) Vo[r * DV + 16 * n + l16] = f2bf(dV[t][n][i]);
+        for (int n = 0; n < N; ++n) acc[t][n] += src[(t * (NQ + NV) + R + n) * 64];
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < N; ++n) tile[(32 * pr + 16 * t + 4 * g + i) * D + 16 * n + l16] = f2bf(acc[t][n][i] * sc);
+  };
+  if (w < 4) sum_parts(std::integral_constant<int, NQ>{}, std::integral_constant<int, 0>{}, Ko, DQK, a.scale);
+  else sum_parts(std::integral_constant<int, NV>{}, std::integral_constant<int, NQ>{}, Vo, DV, 1.f);
   __syncthreads();
   constexpr int QCH = DQK / 8, YCH = DV / 8;
-  for (int idx = tid; idx < KEYS * QCH; idx += 256) {
+  for (int idx = tid; idx < KEYS * QCH; idx += 512) {
     const int r = idx / QCH, c = idx - r * QCH, d = 8 * c;
     if (r < nk) {
       const int64_t kr = (k0 + r) * a.n2 + kvh;
@@ -151,17 +148,22 @@ __device__ __forceinline__ void combine_split_tile(const DqArgs& a, int sidx, ch
       sts16(dst, *reinterpret_cast<const uint4*>(Ko + r * DQK + d));
     }
   }
-  for (int idx = tid; idx < KEYS * YCH; idx += 256) {
+  for (int idx = tid; idx < KEYS * YCH; idx += 512) {
     const int r = idx / YCH, c = idx - r * YCH;
     if (r < nk) sts16(a.dv + ((k0 + r) * a.n2 + kvh) * DV + 8 * c, *reinterpret_cast<const uint4*>(Vo + r * DV + 8 * c));
   }
 }
 
+// 8 waves: WPH = 8 / HP waves per head; within a head, wave (rs, fh) takes query rows
+// 16 RT rs .. (RT = HP row tiles of 16, R = 4 / HP row groups) and feature half fh.  Each
+// dS^T column fragment (A operand) serves the NF feature tiles of the wave, each K column
+// fragment (B operand) its RT row tiles.
 template <int DM, int DR, int HP>
-__global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
+__global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
   constexpr int DQK = DM + DR;
   constexpr int NQ = DQK / 16, NF = NQ / 2, NQM = DM / 16;  // feature tiles: all / per wave / key part
   constexpr int WM = DM / 8, WR = DR > 0 ? DR / 8 : 8;
+  constexpr int WPH = 8 / HP, RT = HP;                     // waves per head, row tiles per wave
   using TM = RowTile<WM>;
   using TR = RowTile<WR>;
   using TD = RowTile<8>;                                     // dS^T block: 64 keys x 64 rows
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int fh = w & 1, rh = w >> 1;
+  const int hh = w / WPH, fh = w & 1, rs = (w % WPH) >> 1;
   const int l16 = lane & 15, g = lane >> 4, jj = l16 >> 2, qq = l16 & 3;
 
   const int wg = (int)blockIdx.x - a.n_split;
@@ -219,23 +221,24 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
       kcol[f][ks2][1] = base + ks2 * 32 * rb + 16 * rb;
     }
   });
-  // dS^T column reads of this wave's row tiles rt: rows (columns of the block) 16(2rh + rt)..
-  int dsA[2];
+  // dS^T column reads of this wave's row tiles rt: rows (columns of the block) 16(RT rs + rt)..
+  int dsA[RT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) dsA[rt] = TD::off(4 * g + jj, 2 * (2 * rh + rt) + (qq >> 1)) + 8 * (qq & 1);
+  for (int rt = 0; rt < RT; ++rt) dsA[rt] = TD::off(4 * g + jj, 2 * (RT * rs + rt) + (qq >> 1)) + 8 * (qq & 1);
 
   const uint32_t rs_m = (uint32_t)a.n2 * DM * 2, rs_r = (uint32_t)a.n2 * DR * 2;
 
   for (int hp0 = 0; hp0 < a.G; hp0 += HP) {
     const int h0 = kvh * a.G + hp0;  // first query head of this pass
 
+    // transfers: wave w fills 1 KB blocks w + 8k of each part
     auto issue_part = [&](auto wtag, const auto& pl, const char* gtile, uint32_t rs, uint32_t lds_part, int nrows) {
       constexpr int W = decltype(wtag)::value;
       constexpr int RPI = RowTile<W>::RPI;
-      static_for<W / 4>([&](auto kc) {
+      static_for<W / 8>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
-        const int r = min(pl.row0 + 4 * RPI * k, nrows - 1);
-        dma16<4096 * k>(gtile + __umul24((uint32_t)r, rs) + pl.gchunk, lds_part + w * 1024);
+        const int r = min(pl.row0 + 8 * RPI * k, nrows - 1);
+        dma16<8192 * k>(gtile + __umul24((uint32_t)r, rs) + pl.gchunk, lds_part + w * 1024);
       });
     };
     // issue(): the K tile (both parts) and the HP dS^T blocks of key tile kt
@@ -251,19 +254,17 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
       const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt : (int64_t)qt * nkt + kt);
       const char* dblk = reinterpret_cast<const char*>(a.ds + (blk * a.n1 + h0) * (kT * kT));
       static_for<HP>([&](auto hc) {
-        constexpr int hh = decltype(hc)::value;
-        issue_part(std::integral_constant<int, 8>{}, pd, dblk + hh * (kT * kT * 2), kT * 2,
-                   stage + OD + hh * TD::BYTES, kT);
+        constexpr int hx = decltype(hc)::value;
+        issue_part(std::integral_constant<int, 8>{}, pd, dblk + hx * (kT * kT * 2), kT * 2,
+                   stage + OD + hx * TD::BYTES, kT);
       });
     };
 
-    f32x4 acc[HP][2][NF];
+    f32x4 acc[RT][NF];
 #pragma unroll
-    for (int hh = 0; hh < HP; ++hh)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int f = 0; f < NF; ++f) acc[hh][rt][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < NF; ++f) acc[rt][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     __syncthreads();  // the previous pass's output tiles have been read
     if (nkt_run > 0) issue(0, 0);
@@ -272,18 +273,17 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
       barrier_no_vm_wait();  // tile kt is in LDS; the other stage is free
       const uint32_t stage = smem_lds + (kt & 1) * SB;
       if (kt + 1 < nkt_run) issue(kt + 1, (~kt & 1) * SB);
-      // 2 HP column fragments of dS^T (items i = (ks2, hh, rt)) and, per ks2, NF column
-      // fragments of K.  The dS^T fragments run PD items ahead of their MFMAs; the K
-      // fragments of ks2 = 1 are read during ks2 = 0.
+      // items i = (ks2, rt): one dS^T column fragment each, PD items ahead of its MFMAs; per
+      // ks2, NF column fragments of K (those of ks2 = 1 read during ks2 = 0)
       auto kfrag = [&](int f, int ks2) -> bf16x8 {
         return join8(lds_tr16_at(stage + kcol[f][ks2][0]), lds_tr16_at(stage + kcol[f][ks2][1]));
       };
       auto dfrag = [&](int i) -> bf16x8 {
-        const int ks2 = i / (2 * HP), hh = (i / 2) % HP, rt = i % 2;
+        const int ks2 = i / RT, rt = i % RT;
         const uint32_t o = stage + OD + hh * TD::BYTES + dsA[rt] + ks2 * 32 * TD::RB;
         return join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB));
       };
-      constexpr int NI = 4 * HP, PD = 3;
+      constexpr int NI = 2 * RT, PD = NI < 3 ? NI : 3;
       bf16x8 kb0[NF], kb1[NF], dring[PD];
 #pragma unroll
       for (int f = 0; f < NF; ++f) kb0[f] = kfrag(f, 0);
@@ -297,9 +297,9 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
 #pragma unroll
           for (int f = 0; f < NF; ++f) kb1[f] = kfrag(f, 1);
         }
-        const int hh = (i / 2) % HP, rt = i % 2;
+        const int rt = i % RT;
 #pragma unroll
-        for (int f = 0; f < NF; ++f) acc[hh][rt][f] = mfma_16x16x32(da, i < 2 * HP ? kb0[f] : kb1[f], acc[hh][rt][f]);
+        for (int f = 0; f < NF; ++f) acc[rt][f] = mfma_16x16x32(da, i < RT ? kb0[f] : kb1[f], acc[rt][f]);
       }
       // schedule: the first reads, then per item its MFMAs followed by the reads of the item
       // PD ahead (and after item 0 the K fragments of ks2 = 1)
@@ -314,26 +314,25 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
 
     // ---- epilogue: bf16 through LDS (row-major [64 rows][DQK] per head), 16-byte stores
     __syncthreads();
-#pragma unroll
-    for (int hh = 0; hh < HP; ++hh) {
+    {
       uint16_t* O = reinterpret_cast<uint16_t*>(smem) + hh * kT * DQK;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int f = 0; f < NF; ++f)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            O[(32 * rh + 16 * rt + 4 * g + i) * DQK + 16 * (fh * NF + f) + l16] = f2bf(acc[hh][rt][f][i] * a.scale);
+            O[(16 * (RT * rs + rt) + 4 * g + i) * DQK + 16 * (fh * NF + f) + l16] = f2bf(acc[rt][f][i] * a.scale);
     }
     __syncthreads();
     constexpr int QCH = DQK / 8;
-    for (int idx = tid; idx < HP * kT * QCH; idx += 256) {
-      const int hh = idx / (kT * QCH), rem = idx - hh * (kT * QCH);
+    for (int idx = tid; idx < HP * kT * QCH; idx += 512) {
+      const int hx = idx / (kT * QCH), rem = idx - hx * (kT * QCH);
       const int r = rem / QCH, c = rem - r * QCH, d = 8 * c;
       if (r < nvalid) {
-        const int64_t qr = (qs + (int64_t)qt * kT + r) * a.n1 + h0 + hh;
+        const int64_t qr = (qs + (int64_t)qt * kT + r) * a.n1 + h0 + hx;
         uint16_t* dst = d < DM ? a.dq + qr * DM + d : a.dq_rope + qr * DR + (d - DM);
-        sts16(dst, *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(smem) + (hh * kT + r) * DQK + d));
+        sts16(dst, *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(smem) + (hx * kT + r) * DQK + d));
       }
     }
   }
@@ -341,9 +340,9 @@ __global__ __launch_bounds__(256, 1) void dense_dq_ds_kernel(DqArgs a) {
 
 template <int DM, int DR>
 hipError_t launch_hp(const DqArgs& k, int G, dim3 grid, hipStream_t s) {
-  if (G % 4 == 0) hipLaunchKernelGGL((dense_dq_ds_kernel<DM, DR, 4>), grid, dim3(256), 0, s, k);
-  else if (G % 2 == 0) hipLaunchKernelGGL((dense_dq_ds_kernel<DM, DR, 2>), grid, dim3(256), 0, s, k);
-  else hipLaunchKernelGGL((dense_dq_ds_kernel<DM, DR, 1>), grid, dim3(256), 0, s, k);
+  if (G % 4 == 0) hipLaunchKernelGGL((dense_dq_ds_kernel<DM, DR, 4>), grid, dim3(512), 0, s, k);
+  else if (G % 2 == 0) hipLaunchKernelGGL((dense_dq_ds_kernel<DM, DR, 2>), grid, dim3(512), 0, s, k);
+  else hipLaunchKernelGGL((dense_dq_ds_kernel<DM, DR, 1>), grid, dim3(512), 0, s, k);
   return hipGetLastError();
 }
 
