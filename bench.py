@@ -63,7 +63,6 @@ def flops_per_pair(w: W.Workload, gemms=("S", "dP", "dV", "dQ", "dK")) -> int:
 # library timing name -> (kernel symbol prefix in profiler output, kernel source file)
 KERNEL_SOURCES = {
     "dense_kv_major": ("dense_kv_kernel<", "dense_kv.hip"),
-    "dense_kv_combine": ("dense_dq_ds_kernel<", "dense_dq.hip"),
     "dense_dq": ("dense_dq_ds_kernel<", "dense_dq.hip"),
     "dense_dq_recompute": ("dense_dq_kernel<", "attn_q.hip"),
     "selected_kv_major": ("sel_kv_kernel<", "sel_kv.hip"),
