@@ -108,6 +108,15 @@ __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast
 
 __device__ __forceinline__ void sts16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// Non-temporal 16-byte accesses, for data read or written once (not worth keeping in the caches).
+__device__ __forceinline__ uint4 ldg16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void sts16_stream(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+
 // Bank-conflict-free LDS tile of bf16 rows, C columns, no padding (64 banks x 4 B).
 // The 16-byte chunk c of row r is stored at chunk c ^ h(r).  h is chosen so that
 //   * a ds_read_b128 over 16 consecutive rows at one column chunk, and

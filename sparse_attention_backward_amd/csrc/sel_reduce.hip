@@ -11,7 +11,7 @@
 // G x DQK block (six per lane at G = 16, DQK = 192), and the slot loop takes two slots per
 // iteration so that twelve 16-byte loads per lane are in flight.  A slot whose topk id is
 // out of range was never written and is skipped: the ids are checked once, one ballot per
-// 64 slots.
+// 64 slots.  Shares and dQ are touched once: streaming (non-temporal) loads and stores.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -72,8 +72,8 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, ui
         const int c = c0 + 64 * u;
         x0[u] = make_uint4(kNegZero2, kNegZero2, kNegZero2, kNegZero2);  // adds nothing, exactly
         x1[u] = make_uint4(kNegZero2, kNegZero2, kNegZero2, kNegZero2);
-        if (v0 && c < chunks) x0[u] = ldg16(src + sl * slot_stride + 8 * c);
-        if (v1 && c < chunks) x1[u] = ldg16(src + (sl + 1) * slot_stride + 8 * c);
+        if (v0 && c < chunks) x0[u] = ldg16_stream(src + sl * slot_stride + 8 * c);
+        if (v1 && c < chunks) x1[u] = ldg16_stream(src + (sl + 1) * slot_stride + 8 * c);
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) add_bf16x8(acc[u], x0[u]);
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, ui
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           o[j] = (uint32_t)f2bf(acc[u][2 * j] * scale) | ((uint32_t)f2bf(acc[u][2 * j + 1] * scale) << 16);
-        sts16(out + 8 * c, make_uint4(o[0], o[1], o[2], o[3]));
+        sts16_stream(out + 8 * c, make_uint4(o[0], o[1], o[2], o[3]));
       }
     }
   }
