@@ -38,7 +38,7 @@ struct DqArgs {
   int n1, n2, G;
   int causal;
   float scale;
-  int n_q_tiles;                // workgroups n_split + (query tile, KV head) with kvh-major order
+  int n_q_tiles;                // workgroups: n_split, then (query tile, KV head), KV head fastest
   // split key tiles of the KV-major kernel
   const int32_t* split;         // [n_split][5] (sequence, 128-key tile, KV head, first slot, parts)
   const float* part;            // fp32 partials, kDenseKvPartBytes per slot, [pair][register][lane]
@@ -184,8 +184,11 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
   const int hh = w / WPH, fh = w & 1, rs = (w % WPH) >> 1;
   const int l16 = lane & 15, g = lane >> 4, jj = l16 >> 2, qq = l16 & 3;
 
+  // query tiles longest first (the table's order), the KV heads of one query tile together:
+  // longest-first over the whole grid, and with n2 = 8 each XCD (workgroup i runs on XCD
+  // i mod 8) keeps one KV head's K tiles in its L2
   const int wg = (int)blockIdx.x - a.n_split;
-  const int kvh = wg / a.n_q_tiles, qi = wg - kvh * a.n_q_tiles;
+  const int qi = wg / a.n2, kvh = wg - qi * a.n2;
   const int b = a.tiles[2 * qi], qt = a.tiles[2 * qi + 1];
   const int64_t qs = a.cu_q[b], ks = a.cu_kv[b];
   const int S1 = (int)(a.cu_q[b + 1] - qs), S2 = (int)(a.cu_kv[b + 1] - ks);
