@@ -173,11 +173,11 @@ struct RowTile {
   static constexpr int RB = 16 * W;        // bytes per row
   static constexpr int RPI = 1024 / RB;    // rows per transfer instruction
   static constexpr int BYTES = 64 * RB;
-  __device__ __forceinline__ static int swz(int r) {
+  __host__ __device__ static constexpr int swz(int r) {
     if constexpr (W == 16) return 2 * (r & 7) + ((r >> 3) & 1);
     else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
   }
-  __device__ __forceinline__ static int off(int r, int c) { return r * RB + 16 * (c ^ swz(r)); }
+  __host__ __device__ static constexpr int off(int r, int c) { return r * RB + 16 * (c ^ swz(r)); }
 };
 
 // Sequence of a packed row: largest b with cu[b] <= row (cu has B + 1 entries).

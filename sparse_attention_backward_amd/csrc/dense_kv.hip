@@ -84,6 +84,13 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
                ::"v"(src), "s"(lds), "i"(MOFF) : "memory", "m0", "scc");
 }
 
+// The same from base + voff (a wave-uniform 64-bit base and a per-lane 32-bit offset)
+template <int MOFF>
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(voff), "s"(base), "s"(lds), "i"(MOFF) : "memory", "m0", "scc");
+}
+
 // 4 bytes per lane from global memory into LDS at M0 = lds, + 4 * lane
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -119,10 +126,24 @@ struct PartLanes {
     row0 = w * T::RPI + lane / W;
     gchunk = 16u * (uint32_t)((lane % W) ^ T::swz(row0));
   }
-  __device__ __forceinline__ static int rowA(int lane, int s) { return T::off(lane & 15, 4 * s + (lane >> 4)); }
-  __device__ __forceinline__ static int colB(int lane, int j) {
+  __host__ __device__ static constexpr int rowA(int lane, int s) { return T::off(lane & 15, 4 * s + (lane >> 4)); }
+  __host__ __device__ static constexpr int colB(int lane, int j) {
     const int l16 = lane & 15, g = lane >> 4;
     return T::off(4 * g + (l16 >> 2), 2 * j + ((l16 & 3) >> 1)) + 8 * (l16 & 1);
+  }
+  // swz only XORs the chunk index with a value of the row, so the reads of k-step s and of
+  // column group j differ from those of s = 0 / j = 0 in bits 5-7 alone: rowA(l, s) =
+  // rowA(l, 0) ^ 64 s and colB(l, j) = colB(l, 0) ^ 32 j.  With a 256-byte aligned base,
+  // base + rowA(l, s) = (base + rowA(l, 0)) ^ 64 s: one address per part and stage, one XOR
+  // per fragment, and the row-tile / half offsets go into the instruction's offset field.
+  static constexpr bool xor_steps() {
+    for (int lane = 0; lane < 64; ++lane) {
+      for (int s = 0; s < W / 4; ++s)
+        if (rowA(lane, s) != (rowA(lane, 0) ^ (64 * s)) || rowA(lane, 0) >= 16 * T::RB) return false;
+      for (int j = 0; j < W / 2; ++j)
+        if (colB(lane, j) != (colB(lane, 0) ^ (32 * j)) || colB(lane, 0) >= 16 * T::RB) return false;
+    }
+    return true;
   }
 };
 
@@ -175,6 +196,9 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
   constexpr int EPI = kKeys * (DQK + DV) * 2;  // epilogue: bf16 output tiles
   constexpr int SMEM = OX + XBYTES > EPI ? OX + XBYTES : EPI;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static_assert(SB % 256 == 0 && OQR % 256 == 0 && OY % 256 == 0, "part bases keep bits 0-7 clear");
+  static_assert(PartLanes<WM>::xor_steps() && PartLanes<WR>::xor_steps() && PartLanes<WY>::xor_steps(),
+                "fragment offsets differ by XOR constants");
   static_assert(2 * (NQ + NV) * 16 * 256 <= kDenseKvPartBytes, "partial slot size");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
@@ -217,33 +241,45 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
   pm.init(w, lane);
   if constexpr (DR > 0) pr.init(w, lane);
   py.init(w, lane);
+  const uint32_t vo_m = (uint32_t)pm.row0 * rs_m + pm.gchunk, vo_y = (uint32_t)py.row0 * rs_y + py.gchunk;
+  const uint32_t vo_r = DR > 0 ? (uint32_t)pr.row0 * rs_r + pr.gchunk : 0u;
 
   // Transfers of step st into the stage at LDS address stage, issued by the S waves only
   // (so that the dP waves never wait for vector-memory counts and their dS stores stay in
   // flight across barriers): this wave's blocks of each part (rows past the end of the
   // sequence repeat its last row), and the lse2 (wave 0) or drow (wave 1) values of the 64
   // rows.
-  auto issue_part = [&](auto wtag, const auto& pl, const char* gtile, uint32_t rs, uint32_t lds_part, int nvalid) {
+  // With every row of the step in the sequence, transfer k reads rows 4 RPI k further on: a
+  // wave-uniform base and the lane's fixed offset voff (no per-transfer vector arithmetic).
+  auto issue_part = [&](auto wtag, const auto& pl, uint32_t voff, const char* gtile, uint32_t rs, uint32_t lds_part,
+                        int nvalid) {
     constexpr int W = decltype(wtag)::value;
     constexpr int RPI = RowTile<W>::RPI;
-    static_for<W / 4>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      const int r = min(pl.row0 + 4 * RPI * k, nvalid - 1);
-      dma16<4096 * k>(gtile + __umul24((uint32_t)r, rs) + pl.gchunk, lds_part + w * 1024);
-    });
+    if (nvalid == kRows) {
+      static_for<W / 4>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        dma16s<4096 * k>(voff, gtile + (size_t)(4 * RPI * k) * rs, lds_part + w * 1024);
+      });
+    } else {
+      static_for<W / 4>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        const int r = min(pl.row0 + 4 * RPI * k, nvalid - 1);
+        dma16<4096 * k>(gtile + __umul24((uint32_t)r, rs) + pl.gchunk, lds_part + w * 1024);
+      });
+    }
   };
   auto issue_stage = [&](int st, uint32_t stage) {
     int hg, qt;
     step_tile(st, hg, qt);
     const int nvalid = min(kRows, S1 - qt * kRows);
     const int64_t rh0 = (qs + (int64_t)qt * kRows) * a.n1 + kvh * a.G + hg;  // (first row) * n1 + h
-    issue_part(std::integral_constant<int, WM>{}, pm, reinterpret_cast<const char*>(a.q + rh0 * DM), rs_m, stage + OQM,
-               nvalid);
+    issue_part(std::integral_constant<int, WM>{}, pm, vo_m, reinterpret_cast<const char*>(a.q + rh0 * DM), rs_m,
+               stage + OQM, nvalid);
     if constexpr (DR > 0)
-      issue_part(std::integral_constant<int, WR>{}, pr, reinterpret_cast<const char*>(a.q_rope + rh0 * DR), rs_r,
+      issue_part(std::integral_constant<int, WR>{}, pr, vo_r, reinterpret_cast<const char*>(a.q_rope + rh0 * DR), rs_r,
                  stage + OQR, nvalid);
-    issue_part(std::integral_constant<int, WY>{}, py, reinterpret_cast<const char*>(a.dy + rh0 * DV), rs_y, stage + OY,
-               nvalid);
+    issue_part(std::integral_constant<int, WY>{}, py, vo_y, reinterpret_cast<const char*>(a.dy + rh0 * DV), rs_y,
+               stage + OY, nvalid);
     if (w < 2) {
       const int64_t lrow = rh0 + (int64_t)min(lane, nvalid - 1) * a.n1;
       dma4(w == 0 ? a.lse2 + lrow : a.drow + lrow, stage + OL + 256 * w);
@@ -288,8 +324,8 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       if (!half_active(st, hi, hg, qt, rb)) return;
       const bool diag = a.causal && kb == rb;
       const int nvalid = min(kRows, S1 - qt * kRows);
-      const uint32_t bm = stage + OQM + hi * 32 * TM::RB, br = stage + OQR + hi * 32 * TR::RB;
-      const uint32_t by = stage + OY + hi * 32 * TY::RB;
+      const uint32_t vm = stage + OQM + PartLanes<WM>::rowA(lane, 0), vr = stage + OQR + PartLanes<WR>::rowA(lane, 0);
+      const uint32_t vy = stage + OY + PartLanes<WY>::colB(lane, 0);
       const uint32_t statb = opaque(stage + OL + 4 * (32 * hi + 4 * g));
       f32x4 lse[2];
 #pragma unroll
@@ -304,8 +340,8 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       // fragments of a k-step (both row tiles) serve both key tiles and are read PA ahead
       constexpr int PA = 3;
       auto afrag = [&](int s, int rt) -> bf16x8 {
-        if (s < KSM) return lds_b128_at(bm + PartLanes<WM>::rowA(lane, s) + rt * 16 * TM::RB);
-        return lds_b128_at(br + PartLanes<WR>::rowA(lane, s - KSM) + rt * 16 * TR::RB);
+        if (s < KSM) return lds_b128_at((vm ^ (64u * s)) + (32 * hi + 16 * rt) * TM::RB);
+        return lds_b128_at((vr ^ (64u * (s - KSM))) + (32 * hi + 16 * rt) * TR::RB);
       };
       bf16x8 aring[PA][2];
 #pragma unroll
@@ -354,8 +390,8 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       lds_st16_at(xs + 1024, __builtin_bit_cast(uint4, pa[1]));
       // dV += P^T dY: column fragments of dY (two transposed reads each), PD items ahead
       auto colfrag = [&](int j) -> bf16x8 {
-        const uint32_t o = by + PartLanes<WY>::colB(lane, j);
-        return join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TY::RB));
+        const uint32_t o = vy ^ (32u * j);
+        return join8(lds_tr16_at(o + 32 * hi * TY::RB), lds_tr16_at(o + (32 * hi + 16) * TY::RB));
       };
       constexpr int PD = 4;
       bf16x8 ring[PD];
@@ -464,8 +500,8 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       const bool active = half_active(st, hi, hg, qt, rb);
       da[0] = da[1] = bf16x8{};
       if (!active) return;
-      const uint32_t bm = stage + OQM + hi * 32 * TM::RB, br = stage + OQR + hi * 32 * TR::RB;
-      const uint32_t by = stage + OY + hi * 32 * TY::RB;
+      const uint32_t vm = stage + OQM + PartLanes<WM>::colB(lane, 0), vr = stage + OQR + PartLanes<WR>::colB(lane, 0);
+      const uint32_t vy = stage + OY + PartLanes<WY>::rowA(lane, 0);
       const uint32_t statb = opaque(stage + OL + 256 + 4 * (32 * hi + 4 * g));
       const uint32_t xs = xslot(st, hi) + 16 * lane;
       const bf16x8 p0 = lds_b128_at(xs), p1 = lds_b128_at(xs + 1024);
@@ -474,9 +510,7 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       for (int rt = 0; rt < 2; ++rt) dr[rt] = lds_f32x4_at(statb + 64 * rt);
       // dP = dY V^T over VS k-steps of dY rows
       constexpr int PA = 2;
-      auto afrag = [&](int s, int rt) -> bf16x8 {
-        return lds_b128_at(by + PartLanes<WY>::rowA(lane, s) + rt * 16 * TY::RB);
-      };
+      auto afrag = [&](int s, int rt) -> bf16x8 { return lds_b128_at((vy ^ (64u * s)) + (32 * hi + 16 * rt) * TY::RB); };
       bf16x8 aring[PA][2];
 #pragma unroll
       for (int i = 0; i < PA; ++i) { aring[i][0] = afrag(i, 0); aring[i][1] = afrag(i, 1); }
@@ -510,10 +544,12 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       }
       // dK += dS^T Q: column fragments of the query part, then of the rope part
       auto colfrag = [&](int j) -> bf16x8 {
-        uint32_t o, second;
-        if (j < NQM) { o = bm + PartLanes<WM>::colB(lane, j); second = 16 * TM::RB; }
-        else { o = br + PartLanes<WR>::colB(lane, j - NQM); second = 16 * TR::RB; }
-        return join8(lds_tr16_at(o), lds_tr16_at(o + second));
+        if (j < NQM) {
+          const uint32_t o = vm ^ (32u * j);
+          return join8(lds_tr16_at(o + 32 * hi * TM::RB), lds_tr16_at(o + (32 * hi + 16) * TM::RB));
+        }
+        const uint32_t o = vr ^ (32u * (j - NQM));
+        return join8(lds_tr16_at(o + 32 * hi * TR::RB), lds_tr16_at(o + (32 * hi + 16) * TR::RB));
       };
       constexpr int PD = 3;
       bf16x8 ring[PD];
