@@ -437,6 +437,9 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
     }
   } else {
     // ---------------- dP waves: dP, dS, dK (one step behind) ----------------------------
+    // The dP waves carry the longer part of a step (their dS arithmetic and stores); the S
+    // waves wait at the barrier meanwhile, so the dP waves get issue priority on the SIMD.
+    __builtin_amdgcn_s_setprio(3);
     bf16x8 Vf[2][VS];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
