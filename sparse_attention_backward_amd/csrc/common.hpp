@@ -178,7 +178,38 @@ struct RowTile {
     else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
   }
   __host__ __device__ static constexpr int off(int r, int c) { return r * RB + 16 * (c ^ swz(r)); }
+
+  // Per-lane offsets of the MFMA operand reads (l16 = lane & 15, g = lane >> 4):
+  //   rowA(lane, s): A operand rows l16 at chunk 4s + g (16-byte reads; +16 RB for row tile 1);
+  //   colB(lane, j): transposed B operand, rows 4g + l16/4 at chunk 2j + (l16&3)/2, half l16&1
+  //                  (8-byte reads; +16 RB for the second 16 rows);
+  //   colK(lane, m): the same rows at chunk 4m + (l16&3) (a B operand whose four 4-column
+  //                  pieces are chunks 4m .. 4m + 3).
+  // swz only XORs the chunk index with a value of the row, so the reads of k-step s, column
+  // group j or chunk group m differ from those of 0 in bits 5-7 alone: rowA(l, s) =
+  // rowA(l, 0) ^ 64 s, colB(l, j) = colB(l, 0) ^ 32 j, colK(l, m) = colK(l, 0) ^ 64 m (checked
+  // by xor_steps).  Bits 0-7 of a 256-byte aligned base are zero, so base + rowA(l, s) =
+  // (base + rowA(l, 0)) ^ 64 s: one address per part and stage and one XOR per fragment,
+  // with the row offsets in the instruction's offset field.
+  __host__ __device__ static constexpr int rowA(int lane, int s) { return off(lane & 15, 4 * s + (lane >> 4)); }
+  __host__ __device__ static constexpr int colB(int lane, int j) {
+    return off(4 * (lane >> 4) + ((lane & 15) >> 2), 2 * j + ((lane & 3) >> 1)) + 8 * (lane & 1);
+  }
+  __host__ __device__ static constexpr int colK(int lane, int m) {
+    return off(4 * (lane >> 4) + ((lane & 15) >> 2), 4 * m + (lane & 3));
+  }
+  static constexpr bool xor_steps() {
+    for (int lane = 0; lane < 64; ++lane) {
+      if (rowA(lane, 0) >= 16 * RB || colB(lane, 0) >= 16 * RB || colK(lane, 0) >= 16 * RB) return false;
+      for (int s = 0; s < W / 4; ++s)
+        if (rowA(lane, s) != (rowA(lane, 0) ^ (64 * s)) || colK(lane, s) != (colK(lane, 0) ^ (64 * s))) return false;
+      for (int j = 0; j < W / 2; ++j)
+        if (colB(lane, j) != (colB(lane, 0) ^ (32 * j))) return false;
+    }
+    return true;
+  }
 };
+static_assert(RowTile<8>::xor_steps() && RowTile<16>::xor_steps(), "operand offsets differ by XOR constants");
 
 // Sequence of a packed row: largest b with cu[b] <= row (cu has B + 1 entries).
 __device__ __forceinline__ int seq_of(const int64_t* cu, int batch, int64_t row) {

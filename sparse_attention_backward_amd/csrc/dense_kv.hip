@@ -126,25 +126,8 @@ struct PartLanes {
     row0 = w * T::RPI + lane / W;
     gchunk = 16u * (uint32_t)((lane % W) ^ T::swz(row0));
   }
-  __host__ __device__ static constexpr int rowA(int lane, int s) { return T::off(lane & 15, 4 * s + (lane >> 4)); }
-  __host__ __device__ static constexpr int colB(int lane, int j) {
-    const int l16 = lane & 15, g = lane >> 4;
-    return T::off(4 * g + (l16 >> 2), 2 * j + ((l16 & 3) >> 1)) + 8 * (l16 & 1);
-  }
-  // swz only XORs the chunk index with a value of the row, so the reads of k-step s and of
-  // column group j differ from those of s = 0 / j = 0 in bits 5-7 alone: rowA(l, s) =
-  // rowA(l, 0) ^ 64 s and colB(l, j) = colB(l, 0) ^ 32 j.  With a 256-byte aligned base,
-  // base + rowA(l, s) = (base + rowA(l, 0)) ^ 64 s: one address per part and stage, one XOR
-  // per fragment, and the row-tile / half offsets go into the instruction's offset field.
-  static constexpr bool xor_steps() {
-    for (int lane = 0; lane < 64; ++lane) {
-      for (int s = 0; s < W / 4; ++s)
-        if (rowA(lane, s) != (rowA(lane, 0) ^ (64 * s)) || rowA(lane, 0) >= 16 * T::RB) return false;
-      for (int j = 0; j < W / 2; ++j)
-        if (colB(lane, j) != (colB(lane, 0) ^ (32 * j)) || colB(lane, 0) >= 16 * T::RB) return false;
-    }
-    return true;
-  }
+  __host__ __device__ static constexpr int rowA(int lane, int s) { return T::rowA(lane, s); }
+  __host__ __device__ static constexpr int colB(int lane, int j) { return T::colB(lane, j); }
 };
 
 // Accumulators of one kind (dK: S = 0 unused, or dV) of this pair's 32 keys to bf16 rows
@@ -197,8 +180,6 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
   constexpr int SMEM = OX + XBYTES > EPI ? OX + XBYTES : EPI;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   static_assert(SB % 256 == 0 && OQR % 256 == 0 && OY % 256 == 0, "part bases keep bits 0-7 clear");
-  static_assert(PartLanes<WM>::xor_steps() && PartLanes<WR>::xor_steps() && PartLanes<WY>::xor_steps(),
-                "fragment offsets differ by XOR constants");
   static_assert(2 * (NQ + NV) * 16 * 256 <= kDenseKvPartBytes, "partial slot size");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 

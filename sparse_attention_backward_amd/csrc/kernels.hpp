@@ -79,7 +79,7 @@ struct SelArgs {
   int32_t* sort_scratch;    // [2 * T1 * n2 * cnt]
   int32_t* flag;            // [1] raised on an out-of-range topk id
   float* dkdv_acc;          // [T2, n2, d_qk + d_v] fp32, atomic mode only
-  void* dq_part;            // [T1, n2, cnt, G, d_qk] bf16: each block's share of dQ
+  void* dq_part;            // [T1, cnt, n2, G, d_qk] bf16: each block's share of dQ
   int64_t T2;
 };
 bool selected_supported(int d_qk, int d_v, int G, int bs);

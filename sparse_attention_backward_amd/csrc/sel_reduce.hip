@@ -2,9 +2,10 @@
 //
 // Page "NsaSelectedAttentionGrad", formula section: dQ = dS K / sqrt(d) over the gathered
 // rows, i.e. the sum over the selected blocks of each block's dS_block K_block.  The
-// KV-major kernel stores every block's share (bf16) at [t, kvh, slot, head, :]; this kernel
-// adds the slots of each (token, KV head) in slot order and scales:
-//   dQ[t, kvh G + h, :] = scale * sum_slot part[t, kvh, slot, h, :].
+// KV-major kernel stores every block's share (bf16) at [t, slot, kvh, head, :] (the list entry
+// t cnt + slot times n2, plus kvh: no division in the store address); this kernel adds the
+// slots of each (token, KV head) in slot order and scales:
+//   dQ[t, kvh G + h, :] = scale * sum_slot part[t, slot, kvh, h, :].
 // Fixed order, one writer per output row: deterministic.
 //
 // One wave per (token, KV head).  Lane l owns the 16-byte chunks l, l + 64, ... of the
@@ -55,8 +56,8 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, ui
   }
   auto slot_ok = [&](int sl) -> bool { return (valid[sl >> 6] >> (sl & 63)) & 1; };
   const int chunks = G * DQK / 8;
-  const int64_t slot_stride = (int64_t)G * DQK;
-  const uint16_t* src = part + pair * (int64_t)cnt * slot_stride;
+  const int64_t slot_stride = (int64_t)n2 * G * DQK;
+  const uint16_t* src = part + (t * cnt * n2 + kvh) * (int64_t)G * DQK;
   uint16_t* out = dq + (t * n1 + (int64_t)kvh * G) * DQK;
   for (int c0 = lane; c0 < chunks; c0 += 64 * kU) {
     float acc[kU][8];
