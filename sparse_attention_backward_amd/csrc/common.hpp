@@ -31,6 +31,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -52,6 +54,9 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
 // instruction's immediate offset.
 __device__ __forceinline__ bf16x8 lds_b128_at(uint32_t addr) {
   return *reinterpret_cast<const lds_bf16x8*>((uintptr_t)addr);
+}
+__device__ __forceinline__ f16x8 lds_f16x8_at(uint32_t addr) {
+  return *reinterpret_cast<const lds_f16x8*>((uintptr_t)addr);
 }
 __device__ __forceinline__ f32x4 lds_f32x4_at(uint32_t addr) {
   return *reinterpret_cast<const lds_f32x4*>((uintptr_t)addr);

@@ -363,12 +363,20 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
           S[1][1][i] = after ? 0.f : S[1][1][i];
         }
       }
+      // P as bf16 for this wave's dV product and as f16 (more mantissa, and the dP wave's
+      // mixed-precision multiply takes f16 halves directly) for the exchange
       bf16x8 pa[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) pa[t] = pack8(S[t][0], S[t][1]);
       const uint32_t xs = xslot(st, hi) + 16 * lane;
-      lds_st16_at(xs, __builtin_bit_cast(uint4, pa[0]));
-      lds_st16_at(xs + 1024, __builtin_bit_cast(uint4, pa[1]));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint32_t h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          h[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(S[t][q >> 1][2 * (q & 1)], S[t][q >> 1][2 * (q & 1) + 1]));
+        lds_st16_at(xs + 1024 * t, make_uint4(h[0], h[1], h[2], h[3]));
+      }
       // dV += P^T dY: column fragments of dY (two transposed reads each), PD items ahead
       auto colfrag = [&](int j) -> bf16x8 {
         const uint32_t o = vy ^ (32u * j);
@@ -488,10 +496,10 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       const uint32_t vy = stage + OY + PartLanes<WY>::rowA(lane, 0);
       const uint32_t statb = opaque(stage + OL + 256 + 4 * (32 * hi + 4 * g));
       const uint32_t xs = xslot(st, hi) + 16 * lane;
-      const bf16x8 p0 = lds_b128_at(xs), p1 = lds_b128_at(xs + 1024);
-      f32x4 dr[2];
+      const f16x8 p0 = lds_f16x8_at(xs), p1 = lds_f16x8_at(xs + 1024);
+      f32x4 ndr[2];  // the dP accumulators start at -drow, so they end at dP - drow
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) dr[rt] = lds_f32x4_at(statb + 64 * rt);
+      for (int rt = 0; rt < 2; ++rt) ndr[rt] = -lds_f32x4_at(statb + 64 * rt);
       // dP = dY V^T over VS k-steps of dY rows
       constexpr int PA = 2;
       auto afrag = [&](int s, int rt) -> bf16x8 { return lds_b128_at((vy ^ (64u * s)) + (32 * hi + 16 * rt) * TY::RB); };
@@ -505,8 +513,8 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
         if (s + PA < VS) { aring[s % PA][0] = afrag(s + PA, 0); aring[s % PA][1] = afrag(s + PA, 1); }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          D[t][0] = mfma_16x16x32(a0, Vf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t][0]);
-          D[t][1] = mfma_16x16x32(a1, Vf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t][1]);
+          D[t][0] = mfma_16x16x32(a0, Vf[t][s], s == 0 ? ndr[0] : D[t][0]);
+          D[t][1] = mfma_16x16x32(a1, Vf[t][s], s == 0 ? ndr[1] : D[t][1]);
         }
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * PA + 2, 0);
@@ -515,15 +523,15 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         if (s + PA < VS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      // dS = P (dP - drow); P is the S wave's bf16 tile, in the same lane layout
-      const bf16x8 pp[2] = {p0, p1};
+      // dS = P (dP - drow); P is the S wave's f16 tile, in the same lane layout
+      const f16x8 pp[2] = {p0, p1};
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         f32x4 ds[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ds[rt][i] = (float)pp[t][4 * rt + i] * (D[t][rt][i] - dr[rt][i]);
+          for (int i = 0; i < 4; ++i) ds[rt][i] = __builtin_fmaf((float)pp[t][4 * rt + i], D[t][rt][i], 0.f);
         da[t] = pack8(ds[0], ds[1]);
       }
       // dK += dS^T Q: column fragments of the query part, then of the rope part
