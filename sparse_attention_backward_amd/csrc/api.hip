@@ -42,7 +42,7 @@ struct Plan {
   int64_t entries = 0;
   // workspace layout (byte offsets)
   size_t off_cu_q = 0, off_cu_kv = 0, off_tab1 = 0, off_tab2 = 0, table_bytes = 0;
-  size_t off_lse2 = 0, off_drow = 0;
+  size_t off_lse2 = 0, off_ndrow = 0;
   size_t off_counts = 0, off_offsets = 0, off_cursor = 0, off_list = 0, off_scratch = 0, off_flag = 0;
   size_t off_dq_part = 0;
   size_t off_ds_base = 0, off_ds = 0, off_kvsplit = 0, off_kvpart = 0;
@@ -244,7 +244,7 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   o = align_up(o);
   const size_t rows = (size_t)pl.T1 * p->n1;
   pl.off_lse2 = o; o = align_up(o + 4 * rows);
-  pl.off_drow = o; o = align_up(o + 4 * rows);
+  pl.off_ndrow = o; o = align_up(o + 4 * rows);
   if (p->op == ATTN_OP_SELECTED) {
     const size_t nkeys = (size_t)p->n2 * pl.nblk_total;
     pl.off_counts = o;  o = align_up(o + 4 * nkeys);
@@ -466,7 +466,7 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, 
 
   PreArgs pa{};
   pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
-  pa.lse2 = at<float>(workspace, pl.off_lse2); pa.drow = at<float>(workspace, pl.off_drow);
+  pa.lse2 = at<float>(workspace, pl.off_lse2); pa.ndrow = at<float>(workspace, pl.off_ndrow);
   pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = p->dtype == ATTN_BF16;
   pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
   pa.tab_n16 = tables.n16();
@@ -475,7 +475,7 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, 
 
   DenseArgs a{};
   a.q = q; a.q_rope = q_rope; a.k = k; a.k_rope = k_rope; a.v = v; a.dy = dy;
-  a.lse2 = pa.lse2; a.drow = pa.drow;
+  a.lse2 = pa.lse2; a.ndrow = pa.ndrow;
   a.dq = dq; a.dq_rope = dq_rope; a.dk = dk; a.dk_rope = dk_rope; a.dv = dv;
   a.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
   a.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
@@ -534,7 +534,7 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
 
   PreArgs pa{};
   pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
-  pa.lse2 = at<float>(workspace, pl.off_lse2); pa.drow = at<float>(workspace, pl.off_drow);
+  pa.lse2 = at<float>(workspace, pl.off_lse2); pa.ndrow = at<float>(workspace, pl.off_ndrow);
   pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = 1;
   pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
   pa.tab_n16 = tables.n16();
@@ -542,7 +542,7 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   if (tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
 
   SelArgs a{};
-  a.q = q; a.k = k; a.v = v; a.dy = dy; a.lse2 = pa.lse2; a.drow = pa.drow; a.topk = topk_indices;
+  a.q = q; a.k = k; a.v = v; a.dy = dy; a.lse2 = pa.lse2; a.ndrow = pa.ndrow; a.topk = topk_indices;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
   a.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);

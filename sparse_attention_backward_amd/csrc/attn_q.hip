@@ -24,7 +24,7 @@ struct QArgs {
   const uint16_t* q; const uint16_t* q_rope;
   const uint16_t* k; const uint16_t* k_rope;
   const uint16_t* v; const uint16_t* dy;
-  const float* lse2; const float* drow;
+  const float* lse2; const float* ndrow;
   uint16_t* dq; uint16_t* dq_rope;
   const int64_t* cu_q; const int64_t* cu_kv;
   const int32_t* tiles;  // (sequence, query tile)
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     Yf[s] = __builtin_bit_cast(bf16x8, x);
   }
   const float lse = rvalid ? a.lse2[qrow] : INFINITY;
-  const float dr = rvalid ? a.drow[qrow] : 0.f;
+  const float ndr = rvalid ? a.ndrow[qrow] : 0.f;
 
   f32x4 dQ[NQ];
 #pragma unroll
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int key = kt * kKeys + 16 * c + 4 * g + i;
         float p = __builtin_amdgcn_exp2f(ST[c][i] * a.scale_log2e - lse);
         if (key >= S2 || (a.causal && key > rloc)) p = 0.f;
-        ST[c][i] = p * (PT[c][i] - dr);
+        ST[c][i] = p * (PT[c][i] + ndr);
       }
     }
     // dQ += dS K over the two 32-key halves; K column fragments PD2 items ahead
@@ -185,7 +185,7 @@ hipError_t launch_dense_dq_bf16(const DenseArgs& a, hipStream_t s) {
   k.q = (const uint16_t*)a.q; k.q_rope = (const uint16_t*)a.q_rope;
   k.k = (const uint16_t*)a.k; k.k_rope = (const uint16_t*)a.k_rope;
   k.v = (const uint16_t*)a.v; k.dy = (const uint16_t*)a.dy;
-  k.lse2 = a.lse2; k.drow = a.drow;
+  k.lse2 = a.lse2; k.ndrow = a.ndrow;
   k.dq = (uint16_t*)a.dq; k.dq_rope = (uint16_t*)a.dq_rope;
   k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.tiles = a.q_tiles;
   k.batch = a.batch; k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;

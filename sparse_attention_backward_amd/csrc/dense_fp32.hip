@@ -49,7 +49,7 @@ __global__ __launch_bounds__(64) void dense_kv_fp32(DenseArgs a) {
       for (int d = 0; d < dqk; ++d) s = fmaf(qk_elem(q, qr, i, a.n1, h, a.d_main, a.d_rope, d), Kj[d], s);
       for (int d = 0; d < dv; ++d) dp = fmaf(dy[(i * a.n1 + h) * dv + d], Vj[d], dp);
       p = exp2f(s * a.scale_log2e - a.lse2[i * a.n1 + h]);
-      ds = p * (dp - a.drow[i * a.n1 + h]);
+      ds = p * (dp + a.ndrow[i * a.n1 + h]);
     }
     p_s[tid] = p;
     ds_s[tid] = ds;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64) void dense_dq_fp32(DenseArgs a) {
   const int64_t kend = a.causal ? (ks + iloc + 1 < ke ? ks + iloc + 1 : ke) : ke;
   for (int d = tid; d < dqk; d += 64) Qi[d] = qk_elem(q, qr, i, a.n1, h, a.d_main, a.d_rope, d);
   for (int d = tid; d < dv; d += 64) Yi[d] = dy[(i * a.n1 + h) * dv + d];
-  const float lse2 = a.lse2[i * a.n1 + h], drow = a.drow[i * a.n1 + h];
+  const float lse2 = a.lse2[i * a.n1 + h], ndrow = a.ndrow[i * a.n1 + h];
   __syncthreads();
   float acc[kF32MaxD / 64];
 #pragma unroll
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(64) void dense_dq_fp32(DenseArgs a) {
       for (int d = 0; d < dqk; ++d) s = fmaf(Qi[d], qk_elem(k, kr, j, a.n2, kvh, a.d_main, a.d_rope, d), s);
       for (int d = 0; d < dv; ++d) dp = fmaf(Yi[d], v[(j * a.n2 + kvh) * dv + d], dp);
       const float p = exp2f(s * a.scale_log2e - lse2);
-      ds = p * (dp - drow);
+      ds = p * (dp + ndrow);
     }
     ds_s[tid] = ds;
     __syncthreads();

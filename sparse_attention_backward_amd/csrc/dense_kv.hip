@@ -33,7 +33,7 @@
 // range order.
 // Every output row has one writer: no atomics, deterministic.
 //
-// Staging: a step's Q (query and queryRope parts), dY, lse2 and drow go from global memory
+// Staging: a step's Q (query and queryRope parts), dY, lse2 and ndrow go from global memory
 // straight into one of three LDS stages (global_load_lds), issued one step ahead; the
 // stage of step s is read by the S waves in iteration s and by the dP waves in iteration
 // s + 1.  Each part is a RowTile: every transfer instruction reads whole rows (full cache
@@ -54,7 +54,7 @@ struct DkvArgs {
   const uint16_t* q; const uint16_t* q_rope;
   const uint16_t* k; const uint16_t* k_rope;
   const uint16_t* v; const uint16_t* dy;
-  const float* lse2; const float* drow;
+  const float* lse2; const float* ndrow;
   uint16_t* dk; uint16_t* dk_rope; uint16_t* dv;
   uint16_t* ds;               // [block][head][64 keys][64 rows] bf16 (dS transposed)
   const int64_t* cu_q; const int64_t* cu_kv;
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
   using TM = RowTile<WM>;
   using TR = RowTile<WR>;
   using TY = RowTile<WY>;
-  // stage: QM, QR, Y, lse2 (64 floats), drow (64 floats); three stages, then the P
+  // stage: QM, QR, Y, lse2 (64 floats), ndrow (64 floats); three stages, then the P
   // exchange: [step parity][pair][half] 2 KB (two 1 KB arrays of 16 bytes per lane)
   constexpr int OQM = 0, OQR = TM::BYTES, OY = OQR + (DR > 0 ? TR::BYTES : 0);
   constexpr int OL = OY + TY::BYTES, SB = OL + 512;
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
   // Transfers of step st into the stage at LDS address stage, issued by the S waves only
   // (so that the dP waves never wait for vector-memory counts and their dS stores stay in
   // flight across barriers): this wave's blocks of each part (rows past the end of the
-  // sequence repeat its last row), and the lse2 (wave 0) or drow (wave 1) values of the 64
+  // sequence repeat its last row), and the lse2 (wave 0) or ndrow (wave 1) values of the 64
   // rows.
   // With every row of the step in the sequence, transfer k reads rows 4 RPI k further on: a
   // wave-uniform base and the lane's fixed offset voff (no per-transfer vector arithmetic).
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
                stage + OY, nvalid);
     if (w < 2) {
       const int64_t lrow = rh0 + (int64_t)min(lane, nvalid - 1) * a.n1;
-      dma4(w == 0 ? a.lse2 + lrow : a.drow + lrow, stage + OL + 256 * w);
+      dma4(w == 0 ? a.lse2 + lrow : a.ndrow + lrow, stage + OL + 256 * w);
     }
   };
   auto stage_of = [&](int st) { return smem_lds + (uint32_t)(st % 3) * SB; };
@@ -497,9 +497,9 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       const uint32_t statb = opaque(stage + OL + 256 + 4 * (32 * hi + 4 * g));
       const uint32_t xs = xslot(st, hi) + 16 * lane;
       const f16x8 p0 = lds_f16x8_at(xs), p1 = lds_f16x8_at(xs + 1024);
-      f32x4 ndr[2];  // the dP accumulators start at -drow, so they end at dP - drow
+      f32x4 ndr[2];  // the dP accumulators start at ndrow = -drow, so they end at dP - drow
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) ndr[rt] = -lds_f32x4_at(statb + 64 * rt);
+      for (int rt = 0; rt < 2; ++rt) ndr[rt] = lds_f32x4_at(statb + 64 * rt);
       // dP = dY V^T over VS k-steps of dY rows
       constexpr int PA = 2;
       auto afrag = [&](int s, int rt) -> bf16x8 { return lds_b128_at((vy ^ (64u * s)) + (32 * hi + 16 * rt) * TY::RB); };
@@ -629,7 +629,7 @@ hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) {
   k.q = (const uint16_t*)a.q; k.q_rope = (const uint16_t*)a.q_rope;
   k.k = (const uint16_t*)a.k; k.k_rope = (const uint16_t*)a.k_rope;
   k.v = (const uint16_t*)a.v; k.dy = (const uint16_t*)a.dy;
-  k.lse2 = a.lse2; k.drow = a.drow;
+  k.lse2 = a.lse2; k.ndrow = a.ndrow;
   k.dk = (uint16_t*)a.dk; k.dk_rope = (uint16_t*)a.dk_rope; k.dv = (uint16_t*)a.dv;
   k.ds = (uint16_t*)a.ds;
   k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.ds_base = a.ds_base;

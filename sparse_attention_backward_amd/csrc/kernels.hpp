@@ -7,14 +7,14 @@
 
 namespace ab {
 
-// ---- row statistics: lse2 = (m + ln l) * log2(e), drow = rowsum(dY * O) -------
+// ---- row statistics: lse2 = (m + ln l) * log2(e), ndrow = -rowsum(dY * O) ------
 struct PreArgs {
   const void* out;        // [rows, dv] bf16 or fp32
   const void* dy;         // [rows, dv]
   const float* smax;      // [rows, 8]
   const float* ssum;      // [rows, 8]
   float* lse2;            // [rows]
-  float* drow;            // [rows]
+  float* ndrow;           // [rows]
   int64_t rows;           // T1 * N1
   int dv;
   int is_bf16;
@@ -29,7 +29,7 @@ struct DenseArgs {
   const void* q;  const void* q_rope;
   const void* k;  const void* k_rope;
   const void* v;  const void* dy;
-  const float* lse2; const float* drow;
+  const float* lse2; const float* ndrow;
   void* dq; void* dq_rope; void* dk; void* dk_rope; void* dv;
   void* ds;                 // bf16 dS^T blocks [block][N1][64][64] (stored-dS mode), else null
   const int64_t* cu_q;      // [B+1]
@@ -61,7 +61,7 @@ hipError_t launch_dense_fp32(const DenseArgs& a, hipStream_t s);
 // ---- selected (NSA) ----------------------------------------------------------
 struct SelArgs {
   const void* q; const void* k; const void* v; const void* dy;
-  const float* lse2; const float* drow;
+  const float* lse2; const float* ndrow;
   const int32_t* topk;      // [T1, N2, cnt]
   void* dq; void* dk; void* dv;
   const int64_t* cu_q;      // [B+1]

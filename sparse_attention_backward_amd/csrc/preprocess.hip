@@ -5,7 +5,8 @@
 //   lse2 = (softmaxMax + ln softmaxSum) * log2(e), so that P = exp2(s * scale * log2(e) - lse2)
 //          reproduces exp(s * scale - m) / l; a row with l = 0 (no visible key) gets +inf,
 //          which makes every P of that row 0.
-//   drow = sum_d dY[t,h,d] * O[t,h,d], which equals rowsum(P * dP) because O = P V.
+//   ndrow = -sum_d dY[t,h,d] * O[t,h,d], minus rowsum(P * dP) because O = P V; stored negated
+//          so that a dP accumulator started at ndrow ends at dP - rowsum(P * dP).
 // softmaxMax / softmaxSum are [T, N, 8] float32 with identical lanes; lane 0 is read.
 // HBM-bound: 2 * d_v * sizeof(T) + 64 bytes moved per row (the stats rows are 32 B
 // each but a 4-byte read of each touches one 32-byte sector).
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (sub == 0 && row < a.rows) {
-      a.drow[row] = acc;
+      a.ndrow[row] = -acc;
       const float m = a.smax[row * 8], l = a.ssum[row * 8];
       a.lse2[row] = (l > 0.f && m > -INFINITY) ? (m + logf(l)) * kLog2e : INFINITY;
     }

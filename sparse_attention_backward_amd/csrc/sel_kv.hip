@@ -41,7 +41,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 struct SkvArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* dy;
-  const float* lse2; const float* drow;
+  const float* lse2; const float* ndrow;
   uint16_t* dk; uint16_t* dv;
   uint16_t* dq_part;          // [T1, cnt, n2, G, DQK] bf16
   const int64_t* cu_kv;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   using TY = RowTile<WY>;
   using TD = RowTile<8>;       // dS^T tile: 64 keys x 64 rows
   constexpr int OQM = 0, OQR = TM::BYTES, OY = OQR + (DR > 0 ? TR::BYTES : 0);
-  constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = ORW + 256;  // stage: QM, QR, Y, lse2, drow
+  constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = ORW + 256;  // stage: QM, QR, Y, lse2, ndrow
   constexpr int OKM = 2 * SB, OKR = OKM + NRH * TM::BYTES;            // K tile, KB rows (dQ product)
   constexpr int ODS = OKR + (DR > 0 ? NRH * TR::BYTES : 0);           // dS^T tile, KB key rows
   constexpr int NACC = 2 * (NQ + NV);
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
       ny[kk] = ldg16(reinterpret_cast<const char*>(a.dy + row_index(py.row0 + 4 * TY::RPI * kk) * DV) + py.gchunk);
     if (w < 2) {
       const int64_t row = (int64_t)tok_lane * a.n1 + hrow + hh_row;
-      nst = ent < 0 ? (w == 0 ? INFINITY : 0.f) : (w == 0 ? a.lse2[row] : a.drow[row]);
+      nst = ent < 0 ? (w == 0 ? INFINITY : 0.f) : (w == 0 ? a.lse2[row] : a.ndrow[row]);
     }
   };
   auto write_stage = [&](int soff) {
@@ -271,12 +271,12 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     // lane bases of this wave's first row half (256-byte aligned part bases; see RowTile)
     const uint32_t vm = stage + OQM + rh0 * 32 * TM::RB, vr = stage + OQR + rh0 * 32 * TR::RB;
     const uint32_t vy = stage + OY + rh0 * 32 * TY::RB;
-    const uint32_t statb = opaque(stage + OL + 4 * (32 * rh + 4 * g));  // lse2; drow at + 256
-    f32x4 lse[2], dr[2];
+    const uint32_t statb = opaque(stage + OL + 4 * (32 * rh + 4 * g));  // lse2; ndrow at + 256
+    f32x4 lse[2], ndr[2];  // ndrow = -drow: the dP accumulators start there and end at dP - drow
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       lse[rt] = lds_f32x4_at(statb + 64 * rt);
-      dr[rt] = lds_f32x4_at(statb + 256 + 64 * rt);
+      ndr[rt] = lds_f32x4_at(statb + 256 + 64 * rt);
     }
     constexpr int NS = KS + VS, PA = 3;
     const uint32_t am = vm + TM::rowA(lane, 0), ar = vr + TR::rowA(lane, 0), ay = vy + TY::rowA(lane, 0);
@@ -299,8 +299,8 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
           S[t][0] = mfma_16x16x32(a0, Kf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][0]);
           S[t][1] = mfma_16x16x32(a1, Kf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][1]);
         } else {
-          D[t][0] = mfma_16x16x32(a0, Vf[t][s - KS], s == KS ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t][0]);
-          D[t][1] = mfma_16x16x32(a1, Vf[t][s - KS], s == KS ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t][1]);
+          D[t][0] = mfma_16x16x32(a0, Vf[t][s - KS], s == KS ? ndr[0] : D[t][0]);
+          D[t][1] = mfma_16x16x32(a1, Vf[t][s - KS], s == KS ? ndr[1] : D[t][1]);
         }
       }
     }
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) D[t][rt][i] = S[t][rt][i] * (D[t][rt][i] - dr[rt][i]);
+        for (int i = 0; i < 4; ++i) D[t][rt][i] = S[t][rt][i] * D[t][rt][i];
     bf16x8 pa[2], da[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -528,7 +528,7 @@ template <int KB>
 hipError_t launch_keys(const SelArgs& a, hipStream_t s) {
   SkvArgs k{};
   k.q = (const uint16_t*)a.q; k.k = (const uint16_t*)a.k; k.v = (const uint16_t*)a.v; k.dy = (const uint16_t*)a.dy;
-  k.lse2 = a.lse2; k.drow = a.drow;
+  k.lse2 = a.lse2; k.ndrow = a.ndrow;
   k.dk = (uint16_t*)a.dk; k.dv = (uint16_t*)a.dv; k.dq_part = (uint16_t*)a.dq_part;
   k.cu_kv = a.cu_kv; k.blkoff = a.blkoff; k.offsets = a.offsets; k.list = a.list; k.sched = a.cursor;
   k.batch = a.batch; k.n1 = a.n1; k.n2 = a.n2; k.G = a.G; k.bs = a.bs; k.cnt = a.cnt; k.nblk_total = a.nblk_total;
