@@ -204,20 +204,25 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
   pm.init(w, lane);
   if constexpr (DR > 0) pr.init(w, lane);
   pd.init(w, lane);
-  // K column reads of this wave's feature tiles ft = fh NF + f, resolved now so that the
-  // step loop indexes only by compile-time f: [f][ks2][first / second read]
+  // dQ^T = K^T dS^T: the K^T fragments are the A operands, so a C tile holds features by lane
+  // group and query rows by lane.  This wave's NF feature tiles are permuted: in tile f, lane
+  // group g holds features F0(f) + 8 g + 4 (f % 2) + (0..3), F0(f) = fh DQK/2 + 32 (f / 2), so
+  // the tile pair (2j, 2j + 1) gives each lane 8 consecutive features of one row (one 16-byte
+  // store, straight from registers).  The K column reads follow: piece qq of tile f is chunk
+  // group F0(f) / 32 of the K tile (RowTile::colK) plus 8 (f % 2) bytes.  Resolved now so that
+  // the step loop indexes only by compile-time f: [f][ks2][first / second read].
   uint32_t kcol[NF][2][2];
-  auto tile_base = [&](auto ftc) -> int {  // compile-time feature tile
-    constexpr int ft = decltype(ftc)::value;
-    if constexpr (ft < NQM) return OKM + pm.colB[ft];
-    else return OKR + pr.colB[ft - NQM];
-  };
   static_for<NF>([&](auto fc) {
     constexpr int f = decltype(fc)::value;
-    constexpr int rb0 = f < NQM ? TM::RB : TR::RB, rb1 = NF + f < NQM ? TM::RB : TR::RB;
-    const int b0 = tile_base(std::integral_constant<int, f>{});
-    const int b1 = tile_base(std::integral_constant<int, NF + f>{});
-    const int base = fh ? b1 : b0, rb = fh ? rb1 : rb0;
+    constexpr int F0a = 32 * (f / 2), F0b = DQK / 2 + 32 * (f / 2);  // fh = 0 / 1
+    auto tile = [&](auto F0c) -> int {
+      constexpr int F0 = decltype(F0c)::value;
+      if constexpr (F0 < DM) return OKM + TM::colK(lane, F0 / 32) + 8 * (f % 2);
+      else return OKR + TR::colK(lane, (F0 - DM) / 32) + 8 * (f % 2);
+    };
+    constexpr int rba = F0a < DM ? TM::RB : TR::RB, rbb = F0b < DM ? TM::RB : TR::RB;
+    const int base = fh ? tile(std::integral_constant<int, F0b>{}) : tile(std::integral_constant<int, F0a>{});
+    const int rb = fh ? rbb : rba;
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       kcol[f][ks2][0] = base + ks2 * 32 * rb;
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
       });
     };
 
-    f32x4 acc[RT][NF];
+    f32x4 acc[RT][NF];  // C tile (f, rt) of dQ^T
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
         }
         const int rt = i % RT;
 #pragma unroll
-        for (int f = 0; f < NF; ++f) acc[rt][f] = mfma_16x16x32(da, i < RT ? kb0[f] : kb1[f], acc[rt][f]);
+        for (int f = 0; f < NF; ++f) acc[rt][f] = mfma_16x16x32(i < RT ? kb0[f] : kb1[f], da, acc[rt][f]);
       }
       // schedule: the first reads, then per item its MFMAs followed by the reads of the item
       // PD ahead (and after item 0 the K fragments of ks2 = 1)
@@ -315,27 +320,22 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
       }
     }
 
-    // ---- epilogue: bf16 through LDS (row-major [64 rows][DQK] per head), 16-byte stores
-    __syncthreads();
-    {
-      uint16_t* O = reinterpret_cast<uint16_t*>(smem) + hh * kT * DQK;
+    // ---- epilogue: lane l16 of row tile rt holds row 16 (RT rs + rt) + l16 of head hh and,
+    // per tile pair j, features F0(2j) + 8 g .. + 7: one 16-byte store each
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            O[(16 * (RT * rs + rt) + 4 * g + i) * DQK + 16 * (fh * NF + f) + l16] = f2bf(acc[rt][f][i] * a.scale);
-    }
-    __syncthreads();
-    constexpr int QCH = DQK / 8;
-    for (int idx = tid; idx < HP * kT * QCH; idx += 512) {
-      const int hx = idx / (kT * QCH), rem = idx - hx * (kT * QCH);
-      const int r = rem / QCH, c = rem - r * QCH, d = 8 * c;
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = 16 * (RT * rs + rt) + l16;
       if (r < nvalid) {
-        const int64_t qr = (qs + (int64_t)qt * kT + r) * a.n1 + h0 + hx;
-        uint16_t* dst = d < DM ? a.dq + qr * DM + d : a.dq_rope + qr * DR + (d - DM);
-        sts16(dst, *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(smem) + (hx * kT + r) * DQK + d));
+        const int64_t qr = (qs + (int64_t)qt * kT + r) * a.n1 + h0 + hh;
+#pragma unroll
+        for (int jp = 0; jp < NF / 2; ++jp) {
+          f32x4 lo = acc[rt][2 * jp], hi = acc[rt][2 * jp + 1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { lo[i] *= a.scale; hi[i] *= a.scale; }
+          const int d = fh * (DQK / 2) + 32 * jp + 8 * g;
+          uint16_t* dst = d < DM ? a.dq + qr * DM + d : a.dq_rope + qr * DR + (d - DM);
+          *reinterpret_cast<bf16x8*>(dst) = pack8(lo, hi);
+        }
       }
     }
   }
