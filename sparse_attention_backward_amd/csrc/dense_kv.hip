@@ -319,7 +319,7 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       }
       // S = Q K^T: k-steps s < KSM over the query part, the rest over the rope part; the A
       // fragments of a k-step (both row tiles) serve both key tiles and are read PA ahead
-      constexpr int PA = 3;
+      constexpr int PA = 2;
       auto afrag = [&](int s, int rt) -> bf16x8 {
         if (s < KSM) return lds_b128_at((vm ^ (64u * s)) + (32 * hi + 16 * rt) * TM::RB);
         return lds_b128_at((vr ^ (64u * (s - KSM))) + (32 * hi + 16 * rt) * TR::RB);
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) ndr[rt] = lds_f32x4_at(statb + 64 * rt);
       // dP = dY V^T over VS k-steps of dY rows
-      constexpr int PA = 2;
+      constexpr int PA = 3;
       auto afrag = [&](int s, int rt) -> bf16x8 { return lds_b128_at((vy ^ (64u * s)) + (32 * hi + 16 * rt) * TY::RB); };
       bf16x8 aring[PA][2];
 #pragma unroll
