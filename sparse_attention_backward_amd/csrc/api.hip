@@ -56,8 +56,8 @@ constexpr uint64_t kDenseDsAutoMax = 8ull << 30;  // stored dS above this size: 
 // Dense schedule tables.
 //  * Work items of the KV-major kernel: (sequence, 128-key tile, KV head, query-tile range,
 //    partial slot).  A key tile's query tiles (from its diagonal on when causal) form one
-//    range, or, when that is more than about a half of a CU's fair share of the whole
-//    launch, several ranges whose fp32 partials the combine kernel adds (in range order).
+//    range, or, when that is more than about 4/5 of a CU's fair share of the whole
+//    launch, several ranges whose fp32 partials the dQ launch adds first (in range order).
 //    The items of one (sequence, KV head) read the same query rows, so each such group
 //    goes to one XCD (groups dealt to the least loaded XCD, largest first) and its items
 //    share that XCD's L2.  Within an XCD items run heaviest first.  Slot p of the launch
@@ -89,11 +89,13 @@ void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
       }
     for (int64_t t = 0; t < nqt; ++t) qv.push_back({p->causal ? std::min(t + 1, nkt) : nkt, b, (int32_t)t, 0, 0, 0, 0, 0, 0});
   }
-  // Split size in query tiles: about half of a CU's share of all steps.  The ranges are cut at
+  // Split size in query tiles: about 4/5 of a CU's share of all steps (a steady-state sweep of
+  // 1/2 .. 2 shares on the dense workload: longer ranges stretch the KV-major tail, shorter ones
+  // add split tiles whose partials the dQ launch must add).  The ranges are cut at
   // the same query tiles for every key tile of a (sequence, KV head) -- counted from the last
   // query tile down -- so that the parts that run together walk the same query rows and share
   // them in the L2.
-  const int64_t target = std::max<int64_t>(2 * pl.G, (total + 2 * kCus - 1) / (2 * kCus));
+  const int64_t target = std::max<int64_t>(2 * pl.G, (4 * total + 5 * kCus - 1) / (5 * kCus));
   const int64_t qchunk = std::max<int64_t>(1, target / pl.G);
   std::vector<std::vector<W>> groups;  // per (sequence, KV head)
   std::vector<int64_t> gwork;
