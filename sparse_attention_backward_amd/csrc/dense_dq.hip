@@ -5,11 +5,13 @@
 // kernel, which leaves one transposed 64 x 64 bf16 block per (query tile, key tile, head)
 // in the workspace; this kernel is then a plain product, with no recomputation of S or dP.
 //
-// One workgroup (4 waves) owns a 64-row query tile of HP query heads that share a KV head
+// One workgroup (8 waves) owns a 64-row query tile of HP query heads that share a KV head
 // (all G heads, in passes of HP).  Per key tile it stages the K tile (key and keyRope
-// parts) and the HP dS^T blocks in LDS (double buffered, global->LDS transfers one tile
-// ahead) and accumulates dQ += dS K.  The waves form a 2 x 2 grid: rows 32(w>>1) .. +31
-// and feature columns (DQK/2)(w&1) .. of every head.  Both operands are read with
+// parts) and the HP dS^T blocks in LDS through global->LDS transfers and accumulates
+// dQ += dS K.  The K tile is re-read by every query tile of its KV head and mostly comes
+// from L2, so two K stages (one tile ahead) suffice; the dS^T blocks are read once from
+// HBM, so they rotate through three stages, issued two tiles ahead.  Each wave owns one
+// head, a group of rows and one half of the features.  Both operands are read with
 // ds_read_b64_tr_b16: the contraction runs over keys, which are the rows of both staged
 // tiles (RowTile layout: whole-row transfers, conflict-free column reads).  Keys are
 // taken in the order {4g + j, 16 + 4g + j} on both sides.  Fixed loop order, no atomics:
@@ -65,6 +67,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* lds) {
 template <int MOFF>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(src), "s"(lds), "i"(MOFF) : "memory", "m0", "scc");
+}
+// the same with the non-temporal hint, for data read once (dS): it does not displace the
+// K tiles that later query tiles re-read from L2
+template <int MOFF>
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                ::"v"(src), "s"(lds), "i"(MOFF) : "memory", "m0", "scc");
 }
 
@@ -167,11 +176,11 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
   using TM = RowTile<WM>;
   using TR = RowTile<WR>;
   using TD = RowTile<8>;                                     // dS^T block: 64 keys x 64 rows
-  constexpr int OKM = 0, OKR = TM::BYTES, OD = OKR + (DR > 0 ? TR::BYTES : 0);
-  constexpr int SB = OD + HP * TD::BYTES;                    // one stage
-  static_assert(2 * SB <= 160 * 1024, "two stages must fit in LDS");
-  static_assert(HP * kT * DQK * 2 <= 2 * SB, "output tiles must fit");
-  constexpr int SMEM = 2 * SB > kDenseKeyTile * (DQK + DM) * 2 ? 2 * SB : kDenseKeyTile * (DQK + DM) * 2;
+  constexpr int OKM = 0, OKR = TM::BYTES, KB = OKR + (DR > 0 ? TR::BYTES : 0);  // one K stage
+  constexpr int DB = HP * TD::BYTES;                         // one dS^T stage
+  constexpr int OD = 2 * KB;                                 // K stages 0, 1, then dS^T stages 0..2
+  constexpr int STAGES = OD + 3 * DB;
+  constexpr int SMEM = STAGES > kDenseKeyTile * (DQK + DM) * 2 ? STAGES : kDenseKeyTile * (DQK + DM) * 2;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   if ((int)blockIdx.x < a.n_split) {  // a split key tile of the KV-major kernel (DV = DM)
@@ -240,31 +249,39 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
     const int h0 = kvh * a.G + hp0;  // first query head of this pass
 
     // transfers: wave w fills 1 KB blocks w + 8k of each part
-    auto issue_part = [&](auto wtag, const auto& pl, const char* gtile, uint32_t rs, uint32_t lds_part, int nrows) {
+    auto issue_part = [&](auto wtag, auto nttag, const auto& pl, const char* gtile, uint32_t rs, uint32_t lds_part,
+                          int nrows) {
       constexpr int W = decltype(wtag)::value;
+      constexpr bool NTL = decltype(nttag)::value;
       constexpr int RPI = RowTile<W>::RPI;
       static_for<W / 8>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         const int r = min(pl.row0 + 8 * RPI * k, nrows - 1);
-        dma16<8192 * k>(gtile + __umul24((uint32_t)r, rs) + pl.gchunk, lds_part + w * 1024);
+        const char* src = gtile + __umul24((uint32_t)r, rs) + pl.gchunk;
+        if constexpr (NTL) dma16_nt<8192 * k>(src, lds_part + w * 1024);
+        else dma16<8192 * k>(src, lds_part + w * 1024);
       });
     };
-    // issue(): the K tile (both parts) and the HP dS^T blocks of key tile kt
-    auto issue = [&](int kt, int soff) {
+    // the K tile (both parts) of key tile kt, into K stage kt & 1
+    auto issue_k = [&](int kt) {
       const int nk = min(kT, S2 - kt * kT);
       const int64_t kr0 = (ks + (int64_t)kt * kT) * a.n2 + kvh;
-      const uint32_t stage = smem_lds + soff;
-      issue_part(std::integral_constant<int, WM>{}, pm, reinterpret_cast<const char*>(a.k + kr0 * DM), rs_m,
+      const uint32_t stage = smem_lds + (kt & 1) * KB;
+      issue_part(std::integral_constant<int, WM>{}, std::false_type{}, pm, reinterpret_cast<const char*>(a.k + kr0 * DM), rs_m,
                  stage + OKM, nk);
       if constexpr (DR > 0)
-        issue_part(std::integral_constant<int, WR>{}, pr, reinterpret_cast<const char*>(a.k_rope + kr0 * DR), rs_r,
+        issue_part(std::integral_constant<int, WR>{}, std::false_type{}, pr, reinterpret_cast<const char*>(a.k_rope + kr0 * DR), rs_r,
                    stage + OKR, nk);
+    };
+    // the HP dS^T blocks of key tile kt, into dS^T stage kt mod 3: HP transfers per wave
+    auto issue_d = [&](int kt) {
+      const uint32_t stage = smem_lds + OD + (kt % 3) * DB;
       const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt : (int64_t)qt * nkt + kt);
       const char* dblk = reinterpret_cast<const char*>(a.ds + (blk * a.n1 + h0) * (kT * kT));
       static_for<HP>([&](auto hc) {
         constexpr int hx = decltype(hc)::value;
-        issue_part(std::integral_constant<int, 8>{}, pd, dblk + hx * (kT * kT * 2), kT * 2,
-                   stage + OD + hx * TD::BYTES, kT);
+        issue_part(std::integral_constant<int, 8>{}, std::true_type{}, pd, dblk + hx * (kT * kT * 2), kT * 2,
+                   stage + hx * TD::BYTES, kT);
       });
     };
 
@@ -274,13 +291,23 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[rt][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();  // the previous pass's output tiles have been read
-    if (nkt_run > 0) issue(0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave is done with the previous pass's stages
+    // issue order K0 D0 D1, then per step kt: K(kt+1) D(kt+2).  At the top of step kt the
+    // transfers issued after those of tile kt are at most D(kt+1), HP per wave (in-order
+    // completion of vector loads).
+    if (nkt_run > 0) {
+      issue_k(0);
+      issue_d(0);
+    }
+    if (nkt_run > 1) issue_d(1);
     for (int kt = 0; kt < nkt_run; ++kt) {
-      wait_vmcnt<0>();
-      barrier_no_vm_wait();  // tile kt is in LDS; the other stage is free
-      const uint32_t stage = smem_lds + (kt & 1) * SB;
-      if (kt + 1 < nkt_run) issue(kt + 1, (~kt & 1) * SB);
+      if (kt + 1 < nkt_run) wait_vmcnt<HP>();
+      else wait_vmcnt<0>();
+      barrier_no_vm_wait();  // tile kt is in LDS; stages of tile kt - 1 are free
+      const uint32_t stage = smem_lds + (kt & 1) * KB, dstage = smem_lds + OD + (kt % 3) * DB;
+      if (kt + 1 < nkt_run) issue_k(kt + 1);
+      if (kt + 2 < nkt_run) issue_d(kt + 2);
       // items i = (ks2, rt): one dS^T column fragment each, PD items ahead of its MFMAs; per
       // ks2, NF column fragments of K (those of ks2 = 1 read during ks2 = 0)
       auto kfrag = [&](int f, int ks2) -> bf16x8 {
@@ -288,7 +315,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
       };
       auto dfrag = [&](int i) -> bf16x8 {
         const int ks2 = i / RT, rt = i % RT;
-        const uint32_t o = stage + OD + hh * TD::BYTES + dsA[rt] + ks2 * 32 * TD::RB;
+        const uint32_t o = dstage + hh * TD::BYTES + dsA[rt] + ks2 * 32 * TD::RB;
         return join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB));
       };
       constexpr int NI = 2 * RT, PD = NI < 3 ? NI : 3;
