@@ -267,11 +267,11 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
       const int nk = min(kT, S2 - kt * kT);
       const int64_t kr0 = (ks + (int64_t)kt * kT) * a.n2 + kvh;
       const uint32_t stage = smem_lds + (kt & 1) * KB;
-      issue_part(std::integral_constant<int, WM>{}, std::false_type{}, pm, reinterpret_cast<const char*>(a.k + kr0 * DM), rs_m,
-                 stage + OKM, nk);
+      issue_part(std::integral_constant<int, WM>{}, std::false_type{}, pm,
+                 reinterpret_cast<const char*>(a.k + kr0 * DM), rs_m, stage + OKM, nk);
       if constexpr (DR > 0)
-        issue_part(std::integral_constant<int, WR>{}, std::false_type{}, pr, reinterpret_cast<const char*>(a.k_rope + kr0 * DR), rs_r,
-                   stage + OKR, nk);
+        issue_part(std::integral_constant<int, WR>{}, std::false_type{}, pr,
+                   reinterpret_cast<const char*>(a.k_rope + kr0 * DR), rs_r, stage + OKR, nk);
     };
     // the HP dS^T blocks of key tile kt, into dS^T stage kt mod 3: HP transfers per wave
     auto issue_d = [&](int kt) {
