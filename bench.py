@@ -1,14 +1,18 @@
 #!/usr/bin/env python3
 """Attention-backward throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-extra] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--no-extra] [--no-cpu-baseline]
 
-A step is one complete C-ABI call (row statistics, schedule upload, every kernel)
-over one batch of synthetic input already resident in HBM.  The default workload
-is the dense varlen bf16 case (causal, rope split, GQA 32/8, D 128+64 / 128, four
-sequences with seeded lengths); --workload 3/4/5 selects a selected-attention case.
+A step is one complete C-ABI call (row statistics, schedule upload, index, every kernel)
+over one batch of synthetic input already resident in HBM.  The headline workload is
+the largest single-GPU one, selected bf16 at S = 128K (N1 64, N2 4, D 192 / 128, blocks
+of 64, 32 per token); `extra` holds one line each for the dense varlen bf16 workload
+(causal, rope 128 + 64, GQA 32/8, four seeded lengths), selected at S = 32K, and the
+Zipf-skewed varlen selected workload in both determinism settings.
 `value` is algorithmic TFLOP/s: attended (query row, key row) pairs x 2(3 D_qk + 2 D_v),
 causal pairs only (the five GEMMs S, dP, dV, dQ, dK; recomputation is not counted).
+Before the warmup calls every workload repeats its call for --prewarm-ms of GPU time, so
+that the timed calls run at the sustained clock.
 
 O and the softmax statistics fed to the timed call are produced once, before timing,
 by a plain fp32 torch forward on the GPU (input preparation only).  The float64
@@ -83,23 +87,28 @@ def kernel_source_hash(name: str) -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(name: str, workload: str):
-    """HBM bytes per launch recorded in profiles/traffic_<kernel>_<workload>.md (FETCH_SIZE + WRITE_SIZE,
-    each scaled by the copy-kernel calibration), or None when absent or taken from other kernel source."""
-    path = os.path.join(PROFILES, f"traffic_{name}_{workload}.md")
+def recorded_counters(name: str, workload: str) -> dict:
+    """Counter figures recorded for a kernel on a workload in profiles/counters_<kernel>_<workload>.md
+    (lines "- key: value"): HBM traffic per launch (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
+    calibration) and MFMA busy percentage.  Empty when the record is absent or was taken from other kernel
+    source (sha256 of the kernel's sources)."""
+    path = os.path.join(PROFILES, f"counters_{name}_{workload}.md")
     if not os.path.exists(path) or name not in KERNEL_SOURCES:
-        return None
+        return {}
     vals = {}
     for line in open(path):
         if ":" in line and line.strip().startswith("- "):
             k, v = line.strip()[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
     if vals.get("source_sha256") != kernel_source_hash(name):
-        return None
-    try:
-        return int(vals["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return {}
+    out = {}
+    for k, conv in (("traffic_bytes_per_launch", int), ("mfma_busy_pct", float)):
+        try:
+            out[k] = conv(vals[k])
+        except (KeyError, ValueError):
+            pass
+    return out
 
 
 def summarize_counters(dirs, calib_dir=None):
@@ -181,7 +190,7 @@ def gpu_forward(w: W.Workload, x):
         Q, K, V = x["query"], x["key"], x["value"]
         n = w.block_count * w.block_size
         ar = torch.arange(w.block_size, device=dev)
-        chunk = max(1, int(1.5e8 // (w.n2 * n * (w.d_qk + w.d_v))))
+        chunk = max(1, int(1.5e9 // (w.n2 * n * (w.d_qk + w.d_v))))
         cq, ck = w.cu_q, w.cu_kv
         for b in range(w.batch):
             qs, qe, ks = int(cq[b]), int(cq[b + 1]), int(ck[b])
@@ -211,19 +220,27 @@ def gpu_forward(w: W.Workload, x):
 # timed run
 # ----------------------------------------------------------------------------
 
-def run_workload(w: W.Workload, steps: int, warmup: int, deterministic=False):
+def make_problem(w: W.Workload, deterministic=False, window_tokens=0):
+    if w.form == "dense":
+        return sab.Problem.dense(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, causal=w.causal,
+                                 d_rope=w.d_rope, dtype=w.dtype, deterministic=deterministic)
+    return sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size,
+                                w.block_count, deterministic=deterministic, window_tokens=window_tokens)
+
+
+def run_workload(w: W.Workload, steps: int, warmup: int, deterministic=False, window_tokens=0, prewarm_ms=300.0):
+    """Time `steps` complete calls after a clock pre-warm (calls repeated until `prewarm_ms` of GPU time
+    have passed) and `warmup` untimed calls.  Returns the inputs, ms per call, the library's per-kernel
+    totals over the timed calls, and the pre-warm actually spent."""
     dev = torch.device("cuda", 0)
     x = W.make_inputs(w, device=dev, backend="torch")
     o, smax, ssum = gpu_forward(w, x)
+    prob = make_problem(w, deterministic, window_tokens)
     if w.form == "dense":
-        prob = sab.Problem.dense(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, causal=w.causal,
-                                 d_rope=w.d_rope, dtype=w.dtype, deterministic=deterministic)
         outs = [torch.empty_like(x["query"]), torch.empty_like(x["query_rope"]) if w.d_rope else None,
                 torch.empty_like(x["key"]), torch.empty_like(x["key_rope"]) if w.d_rope else None,
                 torch.empty_like(x["value"])]
     else:
-        prob = sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size,
-                                    w.block_count, deterministic=deterministic)
         outs = [torch.empty_like(x["query"]), torch.empty_like(x["key"]), torch.empty_like(x["value"])]
     ws = torch.empty(max(1, sab.attn_bwd_workspace_size(prob)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -236,6 +253,22 @@ def run_workload(w: W.Workload, steps: int, warmup: int, deterministic=False):
             sab.attn_bwd_selected(prob, x["query"], x["key"], x["value"], o, x["dy"], smax, ssum, x["topk"],
                                   *outs, ws, stream=stream)
 
+    # The GPU raises its clock over the first tens of milliseconds of sustained work: repeat the
+    # call until prewarm_ms have passed (measured with events, in batches), then the warmup calls.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    spent, batch = 0.0, 1
+    while spent < prewarm_ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(batch):
+            step()
+        b.record(stream)
+        b.synchronize()
+        spent += a.elapsed_time(b)
+        batch = min(batch * 2, 64)
+        if time.perf_counter() - t0 > 60:
+            break
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -251,47 +284,87 @@ def run_workload(w: W.Workload, steps: int, warmup: int, deterministic=False):
     sab.attn_bwd_profiling(False)
     ms = start.elapsed_time(end) / steps
     kernels = sab.attn_bwd_profile_read()
-    return x, ms, kernels
+    return x, ms, kernels, spent
 
 
-def selected_kv_bytes(w: W.Workload) -> int:
-    """Algorithmic HBM bytes of one selected KV-major launch: per (token, KV head, selected block)
-    the G query rows of Q and dY gathered (G (D_qk + D_v) bf16) with their lse2 / ndrow (2 G fp32)
-    and the block's dQ share written (G D_qk bf16); once per launch K and V read and dK and dV
-    written (bf16)."""
-    entries = w.T1 * w.n2 * w.block_count
-    per_entry = w.G * (w.d_qk + w.d_v) * 2 + 2 * w.G * 4 + w.G * w.d_qk * 2
-    return entries * per_entry + 2 * w.T2 * w.n2 * (w.d_qk + w.d_v) * 2
+def algorithmic_bytes(w: W.Workload) -> int:
+    """HBM bytes the call must move at the least: every input read once and every output written once."""
+    e = 2 if w.dtype == "bf16" else 4
+    dqk = w.d_qk + w.d_rope
+    by = w.T1 * w.n1 * dqk * e * 2                      # Q (+ queryRope) in, dQ (+ dqRope) out
+    by += w.T2 * w.n2 * (dqk + w.d_v) * e * 2           # K (+ keyRope), V in; dK (+ dkRope), dV out
+    by += 2 * w.T1 * w.n1 * w.d_v * e                   # O, dY
+    by += 2 * w.T1 * w.n1 * 8 * 4                       # softmaxMax, softmaxSum [T1, N1, 8] fp32
+    if w.form == "selected":
+        by += w.T1 * w.n2 * w.block_count * 4           # topkIndices
+    return by
 
 
-def roofline_for(w: W.Workload, kernels: dict):
+def roofline_for(w: W.Workload, kernels: dict, steps: int, call_ms: float):
+    """Roofline point of the dominant kernel (largest time per call): its algorithmic GEMM flops per call
+    (attended pairs x 2 x the widths of the GEMMs it performs) over its time per call, against the bf16
+    MFMA peak (fp32 config: against the fp32 vector peak).  `hbm_view`: the call's algorithmic bytes
+    (inputs read and outputs written once) over the call time, against 8 TB/s.  `traffic`: HBM bytes of
+    the kernel per launch from the recorded rocprofv3 counters (null when absent or stale)."""
     name = max(kernels, key=lambda k: kernels[k][0])
     tot_ms, n = kernels[name]
-    avg_ms = tot_ms / max(n, 1)
-    if name == "selected_kv_major":
-        # HBM-bound: with uniformly random block choices every (token, block) pair is a fresh
-        # gather and a fresh share; the MFMA view is kept beside it
-        by = selected_kv_bytes(w)
-        achieved = by / (avg_ms * 1e-3) / 1e9
-        fl = attended_pairs(w) * flops_per_pair(w, KERNEL_GEMMS[name])
-        return {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": recorded_traffic(name, w.name), "avg_ms": avg_ms,
-                "bytes_per_launch": by, "mfma_tflops": fl / (avg_ms * 1e-3) / 1e12,
-                "mfma_frac": fl / (avg_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-    pairs = attended_pairs(w)
+    per_call_ms = tot_ms / max(steps, 1)
+    launches = n / max(steps, 1)
     gemms = KERNEL_GEMMS.get(name)
-    if gemms is None:  # non-GEMM kernel: report bytes against HBM
-        return {"kernel": name, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": None, "traffic": None, "avg_ms": avg_ms}
-    fl = pairs * flops_per_pair(w, gemms)
-    achieved = fl / (avg_ms * 1e-3) / 1e12
-    traffic = recorded_traffic(name, w.name)
-    if w.dtype == "fp32":
-        return {"kernel": name, "bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": traffic, "avg_ms": avg_ms,
-                "flop_per_launch": fl}
-    return {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "avg_ms": avg_ms, "flop_per_launch": fl}
+    rec = recorded_counters(name, w.name)
+    ab_bytes = algorithmic_bytes(w)
+    out = {"kernel": name, "avg_ms": tot_ms / max(n, 1), "launches_per_call": launches,
+           "ms_per_call": per_call_ms}
+    if gemms is None:
+        out.update({"bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": None})
+    else:
+        fl = attended_pairs(w) * flops_per_pair(w, gemms)
+        achieved = fl / (per_call_ms * 1e-3) / 1e12
+        if w.dtype == "fp32":
+            out.update({"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                        "frac": achieved / PEAK_FP32_VALU_TFLOPS})
+        else:
+            out.update({"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": achieved / PEAK_BF16_TFLOPS})
+        out["flop_per_call"] = fl
+        out["flop_per_launch"] = fl / max(launches, 1e-9)
+    traffic = rec.get("traffic_bytes_per_launch")
+    out["traffic"] = traffic
+    if traffic is not None:
+        out["traffic_per_call"] = traffic * launches
+        out["traffic_vs_algorithmic_call_bytes"] = traffic * launches / ab_bytes
+    if "mfma_busy_pct" in rec:
+        out["mfma_busy_pct_counter"] = rec["mfma_busy_pct"]
+    out["hbm_view"] = {"algorithmic_bytes_per_call": ab_bytes,
+                       "achieved_gbs": ab_bytes / (call_ms * 1e-3) / 1e9,
+                       "frac": ab_bytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    return out
+
+
+def measure(wl: int, steps: int, warmup: int, deterministic=False, window_tokens=0, prewarm_ms=300.0):
+    """One bench record for workload `wl`: value, timing, roofline and per-kernel times."""
+    w = W.config(wl)
+    x, ms, kernels, spent = run_workload(w, steps, warmup, deterministic, window_tokens, prewarm_ms)
+    total_flops = attended_pairs(w) * flops_per_pair(w)
+    value = total_flops / (ms * 1e-3) / 1e12
+    rec = {
+        "workload": w.name,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(ms, 4),
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "config": {"workload": w.name, "form": w.form, "seqlens": list(w.seqlens_q), "n1": w.n1, "n2": w.n2,
+                   "d_qk": w.d_qk, "d_rope": w.d_rope, "d_v": w.d_v, "causal": w.causal,
+                   "block_size": w.block_size, "block_count": w.block_count, "index_dist": w.index_dist,
+                   "deterministic": bool(deterministic), "window_tokens": int(window_tokens),
+                   "algorithmic_tflop_per_step": total_flops / 1e12},
+        "roofline": roofline_for(w, kernels, steps, ms),
+        "kernels_ms_per_call": {k: round(v[0] / steps, 4) for k, v in kernels.items()},
+        "kernel_launches_per_call": {k: v[1] / steps for k, v in kernels.items()},
+        "prewarm_ms": round(spent, 1),
+    }
+    return w, x, rec
 
 
 # ----------------------------------------------------------------------------
@@ -355,16 +428,21 @@ def cpu_baseline(w: W.Workload, x, budget_s=12.0):
 
 # ----------------------------------------------------------------------------
 
+EXTRA_RUNS = ((2, False), (3, False), (4, False), (4, True))  # (workload, deterministic) beside the headline
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # 50 untimed calls (~30 ms of the dense workload) let the GPU reach its sustained clock: with
-    # 3 the timed calls still ran during the ramp and measured ~11% slower
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=2, help="workload number 1..5 (default 2: dense bf16)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prewarm-ms", type=float, default=300.0,
+                    help="GPU time spent repeating the call before the warmup calls (clock ramp)")
+    ap.add_argument("--workload", type=int, default=5,
+                    help="headline workload 1..5 (default 5: selected bf16 at S = 128K, the largest)")
     ap.add_argument("--deterministic", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the secondary selected-attention measurement")
+    ap.add_argument("--window-tokens", type=int, default=0, help="selected: query tokens per window (0 automatic)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 5 times (counter calibration)")
@@ -372,7 +450,7 @@ def main(argv=None):
                     help="print per-kernel mean counters of rocprofv3 --pmc output directories and exit "
                          "(with --calibration DIR: also the copy kernel's FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--calibration", metavar="DIR")
-    ap.add_argument("--source-hash", metavar="KERNEL", help="print the kernel source hash used by traffic records")
+    ap.add_argument("--source-hash", metavar="KERNEL", help="print the kernel source hash used by counter records")
     args = ap.parse_args(argv)
     if args.summarize_counters:
         print(json.dumps(summarize_counters(args.summarize_counters, args.calibration), indent=1))
@@ -397,42 +475,45 @@ def main(argv=None):
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
         return 0
 
-    w = W.config(args.workload)
-    x, ms, kernels = run_workload(w, args.steps, args.warmup, args.deterministic)
-    total_flops = attended_pairs(w) * flops_per_pair(w)
-    value = total_flops / (ms * 1e-3) / 1e12
+    w, x, rec = measure(args.workload, args.steps, args.warmup, args.deterministic, args.window_tokens,
+                        args.prewarm_ms)
     line = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": rec["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": rec["dtype"],
         "data": "synthetic",
-        "config": {"workload": w.name, "form": w.form, "seqlens": list(w.seqlens_q), "n1": w.n1, "n2": w.n2,
-                   "d_qk": w.d_qk, "d_rope": w.d_rope, "d_v": w.d_v, "causal": w.causal,
-                   "block_size": w.block_size, "block_count": w.block_count, "index_dist": w.index_dist,
-                   "deterministic": bool(args.deterministic), "algorithmic_tflop_per_step": total_flops / 1e12},
-        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": roofline_for(w, kernels),
-        "kernels_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in kernels.items()},
+        "config": rec["config"],
+        "pct_bf16_peak": rec["pct_bf16_peak"],
+        "roofline": rec["roofline"],
+        "kernels_ms_per_call": rec["kernels_ms_per_call"],
+        "kernel_launches_per_call": rec["kernel_launches_per_call"],
+        "prewarm_ms": rec["prewarm_ms"],
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x)
     del x
     torch.cuda.empty_cache()
-    if not args.no_extra and args.workload == 2:
-        w3 = W.config(3)
-        x3, ms3, k3 = run_workload(w3, max(3, args.steps // 10), max(2, args.warmup // 10))
-        v3 = attended_pairs(w3) * flops_per_pair(w3) / (ms3 * 1e-3) / 1e12
-        line["extra"] = {"workload": w3.name, "tflops": round(v3, 3), "ms_per_step": round(ms3, 3),
-                         "pct_bf16_peak": round(100 * v3 / PEAK_BF16_TFLOPS, 2), "roofline": roofline_for(w3, k3),
-                         "kernels_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in k3.items()}}
+    if not args.no_extra:
+        extra = []
+        for wl, det in EXTRA_RUNS:
+            if wl == args.workload and det == args.deterministic:
+                continue
+            # the dense workload's calls are short: time more of them
+            k = args.steps * 10 if W.config(wl).form == "dense" else args.steps
+            _, xe, re_ = measure(wl, k, args.warmup, det, 0, args.prewarm_ms)
+            re_["steps"] = k
+            extra.append(re_)
+            del xe
+            torch.cuda.empty_cache()
+        line["extra"] = extra
     print(json.dumps(line), flush=True)
     return 0
 

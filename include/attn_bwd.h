@@ -106,6 +106,15 @@ typedef struct {
                                      dS storage); 0 = automatic: 1 while the dS storage is at
                                      most 8 GiB, else 2.  Both give results within the same
                                      tolerance and are deterministic.                          */
+  int32_t sel_window_tokens;      /* selected only (0 for dense): the backward runs over windows
+                                     of at most this many consecutive query tokens, one after
+                                     the other, so that the per-block dQ shares of one window
+                                     (block_count * n1 * d_qk bf16 per token) fit the workspace;
+                                     0 = automatic: the largest windows whose shares take at most
+                                     64 GiB.  A smaller value shrinks the workspace (and costs
+                                     time: each window reloads every block and carries its fp32
+                                     dK / dV sums).  Any value gives results within the same
+                                     tolerance; deterministic.                                  */
 } attn_bwd_problem_t;
 
 /* Validate `p` and return the workspace size in bytes for its execute call.

@@ -48,6 +48,7 @@ class attn_bwd_problem_t(ctypes.Structure):
         ("scale", c_double), ("causal", c_int32),
         ("block_size", c_int32), ("block_count", c_int32),
         ("deterministic", c_int32), ("dkdv_atomic", c_int32), ("dense_dq_mode", c_int32),
+        ("sel_window_tokens", c_int32),
     ]
 
 
@@ -111,7 +112,8 @@ class Problem:
     """attn_bwd_problem_t plus the host cu_seqlens arrays it points to (kept alive here)."""
 
     def __init__(self, op, dtype, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, d_rope=0, causal=False,
-                 block_size=0, block_count=0, deterministic=False, dkdv_atomic=False, dense_dq_mode=0):
+                 block_size=0, block_count=0, deterministic=False, dkdv_atomic=False, dense_dq_mode=0,
+                 window_tokens=0):
         cu_q = [int(x) for x in cu_q]
         cu_kv = [int(x) for x in cu_kv]
         self.cu_q_arr = (c_int64 * len(cu_q))(*cu_q)
@@ -123,7 +125,7 @@ class Problem:
             n1=n1, n2=n2, d_qk=d_qk, d_rope=d_rope, d_v=d_v, scale=float(scale), causal=int(bool(causal)),
             block_size=block_size, block_count=block_count,
             deterministic=int(bool(deterministic)), dkdv_atomic=int(bool(dkdv_atomic)),
-            dense_dq_mode=int(dense_dq_mode))
+            dense_dq_mode=int(dense_dq_mode), sel_window_tokens=int(window_tokens))
         self.T1, self.T2 = cu_q[-1], cu_kv[-1]
 
     @classmethod
@@ -136,10 +138,11 @@ class Problem:
 
     @classmethod
     def selected(cls, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, block_size, block_count, deterministic=False,
-                 dkdv_atomic=False, dtype="bf16"):
+                 dkdv_atomic=False, dtype="bf16", window_tokens=0):
+        """window_tokens: query tokens per window (field sel_window_tokens; 0 automatic)."""
         return cls(ATTN_OP_SELECTED, {"bf16": ATTN_BF16, "fp32": ATTN_FP32, "fp16": ATTN_FP16}[dtype], cu_q,
                    cu_kv, n1, n2, d_qk, d_v, scale, block_size=block_size, block_count=block_count,
-                   deterministic=deterministic, dkdv_atomic=dkdv_atomic)
+                   deterministic=deterministic, dkdv_atomic=dkdv_atomic, window_tokens=window_tokens)
 
     @property
     def ref(self):

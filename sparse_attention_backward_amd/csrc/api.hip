@@ -40,11 +40,13 @@ struct Plan {
   std::vector<int32_t> blkoff;
   int nblk_total = 0;
   int64_t entries = 0;
+  int nwin = 1;              // windows of query tokens (dQ shares of one window in the workspace)
+  int64_t win_tokens = 0;
   // workspace layout (byte offsets)
   size_t off_cu_q = 0, off_cu_kv = 0, off_tab1 = 0, off_tab2 = 0, table_bytes = 0;
   size_t off_lse2 = 0, off_ndrow = 0;
   size_t off_counts = 0, off_offsets = 0, off_cursor = 0, off_list = 0, off_scratch = 0, off_flag = 0;
-  size_t off_dq_part = 0;
+  size_t off_dq_part = 0, off_wofs = 0, off_kvacc = 0;
   size_t off_ds_base = 0, off_ds = 0, off_kvsplit = 0, off_kvpart = 0;
   size_t total = 0;
 };
@@ -52,6 +54,11 @@ struct Plan {
 constexpr int kXcds = 8;                          // workgroups are dealt to the XCDs round-robin
 constexpr int kCus = 256;                         // compute units (sets the key-tile split size only)
 constexpr uint64_t kDenseDsAutoMax = 8ull << 30;  // stored dS above this size: recompute instead
+// Selected: the dQ shares of one window take at most this much workspace.  Windows cost time
+// (per window every block's K / V is loaded again and its fp32 dK / dV sums are saved and
+// restored; with skewed ids each window's longest list runs alone), so they are made as long
+// as the cap allows; the caller can ask for shorter ones (sel_window_tokens).
+constexpr uint64_t kSelShareMax = 64ull << 30;
 
 // Dense schedule tables.
 //  * Work items of the KV-major kernel: (sequence, 128-key tile, KV head, query-tile range,
@@ -193,7 +200,7 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     const int dqk = p->d_qk + p->d_rope;
     if (p->dtype == ATTN_BF16 && !dense_bf16_supported(p->d_qk, p->d_rope, p->d_v)) return ATTN_ERR_UNSUPPORTED;
     if (p->dtype == ATTN_FP32 && (dqk > 256 || p->d_v > 256)) return ATTN_ERR_UNSUPPORTED;
-    if (p->dense_dq_mode < 0 || p->dense_dq_mode > 2) return ATTN_ERR_INVALID;
+    if (p->dense_dq_mode < 0 || p->dense_dq_mode > 2 || p->sel_window_tokens != 0) return ATTN_ERR_INVALID;
     plan_dense_schedule(p, pl);
   } else {
     if (p->dtype == ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
@@ -222,6 +229,15 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     pl.entries = pl.T1 * p->n2 * cnt;
     if (pl.entries >= (int64_t(1) << 31) || (int64_t)p->n2 * pl.nblk_total >= (int64_t(1) << 31))
       return ATTN_ERR_UNSUPPORTED;
+    // Windows of query tokens: the shares of one window (cnt N1 d_qk bf16 per token) stay within
+    // kSelShareMax; the caller may ask for smaller windows.  Windows are of equal length but
+    // the last.
+    if (p->sel_window_tokens < 0) return ATTN_ERR_INVALID;
+    const uint64_t share_per_token = (uint64_t)cnt * p->n1 * p->d_qk * 2;
+    int64_t w = std::max<int64_t>(1, (int64_t)(kSelShareMax / share_per_token));
+    if (p->sel_window_tokens > 0) w = std::min<int64_t>(w, p->sel_window_tokens);
+    pl.nwin = (int)std::max<int64_t>(1, (pl.T1 + w - 1) / w);
+    pl.win_tokens = std::max<int64_t>(1, (pl.T1 + pl.nwin - 1) / pl.nwin);
   }
 
   // ---- workspace layout ----
@@ -255,7 +271,12 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     pl.off_list = o;    o = align_up(o + 4 * (size_t)pl.entries);
     pl.off_scratch = o; o = align_up(o + 8 * (size_t)pl.entries);
     pl.off_flag = o;    o = align_up(o + 4);
-    pl.off_dq_part = o; o = align_up(o + 2 * (size_t)pl.entries * pl.G * p->d_qk);
+    pl.off_dq_part = o;
+    o = align_up(o + 2 * (size_t)std::min<int64_t>(pl.win_tokens, pl.T1) * p->block_count * p->n1 * p->d_qk);
+    if (pl.nwin > 1) {
+      pl.off_wofs = o;  o = align_up(o + 4 * nkeys * (size_t)(pl.nwin + 1));
+      pl.off_kvacc = o; o = align_up(o + 4 * nkeys * (size_t)sel_kv_keys(p->block_size) * (p->d_qk + p->d_v));
+    }
   }
   if (p->op == ATTN_OP_DENSE && pl.dense_ds) {
     pl.off_ds = o;
@@ -561,12 +582,23 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   a.sort_scratch = at<int32_t>(workspace, pl.off_scratch);
   a.flag = at<int32_t>(workspace, pl.off_flag);
   a.dq_part = at<void>(workspace, pl.off_dq_part);
-  if (timed("selected_index", s, [&] { return launch_selected_index(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
-  if (timed("selected_kv_major", s, [&] { return launch_selected_kv(a, s); }) !=
-      hipSuccess)
+  a.nwin = pl.nwin;
+  a.win_tokens = pl.win_tokens;
+  a.wofs = pl.nwin > 1 ? at<int32_t>(workspace, pl.off_wofs) : nullptr;
+  a.kvacc = pl.nwin > 1 ? at<float>(workspace, pl.off_kvacc) : nullptr;
+  if (timed("selected_index", s, [&] {
+        const hipError_t e = launch_selected_index(a, s);
+        return e != hipSuccess ? e : launch_selected_window_offsets(a, s);
+      }) != hipSuccess)
     return ATTN_ERR_HIP;
-  if (timed("selected_dq_reduce", s, [&] { return launch_selected_dq_reduce(a, s); }) != hipSuccess)
-    return ATTN_ERR_HIP;
+  for (int w = 0; w < pl.nwin; ++w) {
+    a.win = w;
+    a.t0 = std::min<int64_t>(pl.T1, (int64_t)w * pl.win_tokens);
+    a.t1 = std::min<int64_t>(pl.T1, a.t0 + pl.win_tokens);
+    if (timed("selected_kv_major", s, [&] { return launch_selected_kv(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+    if (timed("selected_dq_reduce", s, [&] { return launch_selected_dq_reduce(a, s); }) != hipSuccess)
+      return ATTN_ERR_HIP;
+  }
   return ATTN_OK;
 }
 

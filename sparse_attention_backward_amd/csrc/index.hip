@@ -278,6 +278,29 @@ __global__ __launch_bounds__(256) void idx_identity_kernel(int32_t* sched, int n
   if (k < nkeys) sched[k] = k;
 }
 
+// Window offsets: for every key and window boundary w (0..nwin), the first position of the
+// key's list whose entry t cnt + slot has t >= w win_tokens (lists are ascending), found by
+// binary search.  wofs[key][0] = offsets[key], wofs[key][nwin] = offsets[key + 1].
+__global__ __launch_bounds__(256) void idx_window_kernel(const int32_t* offsets, const int32_t* list, int32_t* wofs,
+                                                         int nkeys, int nwin, int64_t win_tokens, int64_t T1,
+                                                         int cnt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)nkeys * (nwin + 1)) return;
+  const int key = (int)(i / (nwin + 1)), w = (int)(i - (int64_t)key * (nwin + 1));
+  int lo = offsets[key], hi = offsets[key + 1];
+  if (w == nwin) {
+    wofs[i] = hi;
+    return;
+  }
+  const int64_t target = min((int64_t)w * win_tokens, T1) * cnt;  // first entry of window w
+  while (lo < hi) {  // first position with list[pos] >= target
+    const int mid = lo + ((hi - lo) >> 1);
+    if ((int64_t)list[mid] < target) lo = mid + 1;
+    else hi = mid;
+  }
+  wofs[i] = lo;
+}
+
 unsigned grid_for(int64_t n, int64_t per_block) {
   int64_t b = (n + per_block - 1) / per_block;
   return (unsigned)(b < 1 ? 1 : b);
@@ -290,6 +313,15 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_selected_window_offsets(const SelArgs& a, hipStream_t s) {
+  const int nkeys = a.n2 * a.nblk_total;
+  if (a.nwin <= 1 || nkeys == 0) return hipSuccess;
+  const int64_t n = (int64_t)nkeys * (a.nwin + 1);
+  hipLaunchKernelGGL(idx_window_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, (const int32_t*)a.offsets,
+                     (const int32_t*)a.list, a.wofs, nkeys, a.nwin, a.win_tokens, a.T1, a.cnt);
   return hipGetLastError();
 }
 

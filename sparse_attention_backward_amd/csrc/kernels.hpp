@@ -78,12 +78,23 @@ struct SelArgs {
   int32_t* list;            // [T1 * n2 * cnt]  entries t * cnt + slot, sorted per key
   int32_t* sort_scratch;    // [2 * T1 * n2 * cnt]
   int32_t* flag;            // [1] raised on an out-of-range topk id
-  float* dkdv_acc;          // [T2, n2, d_qk + d_v] fp32, atomic mode only
-  void* dq_part;            // [T1, cnt, n2, G, d_qk] bf16: each block's share of dQ
+  void* dq_part;            // [W, cnt, n2, G, d_qk] bf16: each block's share of dQ, for the W query
+                            // tokens of the current window
   int64_t T2;
+  // query-token windows: the KV-major pass and the dQ reduction run once per window of
+  // win_tokens consecutive query tokens, so the share buffer holds one window
+  int nwin;                 // number of windows (1: the whole problem at once)
+  int64_t win_tokens;       // tokens per window (the last may be shorter)
+  int32_t* wofs;            // [n2 * nblk_total, nwin + 1] first list position of each window (nwin > 1)
+  float* kvacc;             // fp32 dK / dV accumulators of every (KV head, block) between windows (nwin > 1):
+                            // sel_kv_keys(bs) * (d_qk + d_v) floats per (KV head, block), in register order
+  int win;                  // current window
+  int64_t t0, t1;           // its query tokens [t0, t1)
 };
 bool selected_supported(int d_qk, int d_v, int G, int bs);
+inline int sel_kv_keys(int bs) { return bs > 64 ? 128 : 64; }  // keys per KV-major workgroup
 hipError_t launch_selected_index(const SelArgs& a, hipStream_t s);
+hipError_t launch_selected_window_offsets(const SelArgs& a, hipStream_t s);  // wofs from the lists (nwin > 1)
 hipError_t launch_selected_kv(const SelArgs& a, hipStream_t s);         // dK, dV and the dQ partials
 hipError_t launch_selected_dq_reduce(const SelArgs& a, hipStream_t s);  // dQ = scale * sum of partials
 

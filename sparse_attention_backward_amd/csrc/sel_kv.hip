@@ -21,10 +21,16 @@
 //   dV += P^T dY, dK += dS^T Q                       (registers, summed over all entries)
 //   dS^T -> LDS, then dQ_part^T = K^T dS^T over the block's keys (K staged in LDS once):
 //   every wave owns half of the feature columns for 32 rows, and each lane stores 8
-//   consecutive features of one row (bf16, 16 bytes) to dq_part[t, slot, kvh, head, :], whose
-//   row index is (list entry t cnt + slot) n2 + kvh.
+//   consecutive features of one row (bf16, 16 bytes) to dq_part[t - t0, slot, kvh, head, :],
+//   whose row index is (list entry t cnt + slot - t0 cnt) n2 + kvh.
 // dq_reduce_kernel then sums the slots of each (token, KV head) in slot order.  Every
 // output row has one writer; no floating-point atomics: deterministic.
+//
+// Windows: the query tokens are cut into windows [t0, t1) so that the dQ shares of one
+// window fit a bounded buffer; each window is one launch of this kernel and one of the
+// reduction.  Since a list is ascending in t, a window's entries are a contiguous part
+// of it (wofs).  Between windows the fp32 dK / dV accumulators of every block are kept in
+// kvacc (the first window starts from zero, the last one writes the bf16 outputs).
 //
 // Row staging as in the dense KV-major kernel: coalesced whole-row loads into registers
 // one step ahead, written to one of two swizzled LDS stages.  The list entries of a step
@@ -43,13 +49,17 @@ struct SkvArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* dy;
   const float* lse2; const float* ndrow;
   uint16_t* dk; uint16_t* dv;
-  uint16_t* dq_part;          // [T1, cnt, n2, G, DQK] bf16
+  uint16_t* dq_part;          // [window tokens, cnt, n2, G, DQK] bf16
   const int64_t* cu_kv;
   const int32_t* blkoff;      // [B+1] blocks before each sequence
   const int32_t* offsets;     // inverted index: [n2 * nblk_total + 1]
   const int32_t* list;        // entries t * cnt + slot, ascending per (KV head, block)
   const int32_t* sched;       // [n2 * nblk_total] work order: keys, longest list first
+  const int32_t* wofs;        // [n2 * nblk_total, nwin + 1] list position where each window starts
+  float* kvacc;               // fp32 dK / dV of every key between windows, KB (DQK + DV) per key
   int batch, n1, n2, G, bs, cnt, nblk_total;
+  int nwin, win;              // windows of query tokens; this launch takes window `win`
+  int e_lo;                   // first list entry (t cnt + slot) of the window: share row 0
   float scale, scale_log2e;
 };
 
@@ -125,7 +135,12 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   const int b = seq_of32(a.blkoff, a.batch, rem);
   const int64_t k0 = a.cu_kv[b] + (int64_t)(rem - a.blkoff[b]) * a.bs;
   const int nk = a.bs;
-  const int e_begin = a.offsets[u], e_end = a.offsets[u + 1];
+  // the entries of this window: a contiguous part of the (ascending) list
+  const int e_begin = a.nwin > 1 ? a.wofs[(int64_t)u * (a.nwin + 1) + a.win] : a.offsets[u];
+  const int e_end = a.nwin > 1 ? a.wofs[(int64_t)u * (a.nwin + 1) + a.win + 1] : a.offsets[u + 1];
+  const bool first_win = a.win == 0, last_win = a.win == a.nwin - 1;
+  // a window between the first and the last with no entry leaves the accumulators as they are
+  if (e_begin == e_end && !first_win && !last_win) return;  // whole workgroup
   const int G = a.G, TPS = kRows / G;  // entries per step
   const int nsteps = (e_end - e_begin + TPS - 1) / TPS;
   const int hh_row = lane % G;  // head (within the group) of step row `lane`
@@ -208,13 +223,21 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     }
   }
 
+  // dK / dV accumulators: zero, or (after the first window) the key's running sums; with
+  // KB = 64 the two row-half waves of a key group were added at the end of the previous
+  // window, and the first of them continues from that sum.
+  // kvacc layout per key: [key group kh][t][NQ dK tiles, NV dV tiles][lane] f32x4
   f32x4 dK[2][NQ], dV[2][NV];
+  f32x4* const accu = reinterpret_cast<f32x4*>(a.kvacc) + (int64_t)u * (KB / 32) * NACC * 64;
+  const bool resume = !first_win && (NRH != 1 || rh0 == 0);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) dK[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NQ; ++n)
+      dK[t][n] = resume ? accu[(kh * NACC + t * (NQ + NV) + n) * 64 + lane] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int n = 0; n < NV; ++n) dV[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NV; ++n)
+      dV[t][n] = resume ? accu[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // ---- list entries: row `lane` of step st is entry e_begin + st * TPS + lane / G ------
@@ -418,7 +441,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
       const int r = 32 * qh + 16 * rr + l16;
       const int ent = __shfl(ent_cur, r);
       if (ent >= 0) {
-        uint16_t* dst = a.dq_part + (((int64_t)ent * a.n2 + kvh) * G + rmod[rr]) * DQK + FH * (DQK / 2) + 8 * g;
+        uint16_t* dst = a.dq_part + (((int64_t)(ent - a.e_lo) * a.n2 + kvh) * G + rmod[rr]) * DQK + FH * (DQK / 2) + 8 * g;
 #pragma unroll
         for (int j = 0; j < NFH / 2; ++j)
           *reinterpret_cast<bf16x8*>(dst + 32 * j) = pack8(acc[2 * j][rr], acc[2 * j + 1][rr]);
@@ -460,7 +483,17 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   }
 
   // ---- epilogue: dK, dV to bf16 through LDS (KB = 64: the two row halves summed first),
-  // then 16-byte stores of whole rows ----------------------------------------------------
+  // then 16-byte stores of whole rows; before the last window, the fp32 sums go to kvacc ----
+  const bool keep = !last_win;
+  auto keep_acc = [&](auto&& other_k, auto&& other_v) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) accu[(kh * NACC + t * (NQ + NV) + n) * 64 + lane] = dK[t][n] + other_k(t, n);
+#pragma unroll
+      for (int n = 0; n < NV; ++n) accu[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane] = dV[t][n] + other_v(t, n);
+    }
+  };
   __syncthreads();
   uint16_t* Ko = reinterpret_cast<uint16_t*>(smem + (NRH == 1 ? 2 * NACC * 1024 : 0));
   uint16_t* Vo = Ko + KB * DQK;
@@ -494,13 +527,18 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
       }
     }
     __syncthreads();
-    if (rh0 == 0)
-      put([&](int t, int n) { return part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane]; },
-          [&](int t, int n) { return part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane]; });
+    const auto ok = [&](int t, int n) { return part[(kh * NACC + t * (NQ + NV) + n) * 64 + lane]; };
+    const auto ov = [&](int t, int n) { return part[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane]; };
+    if (rh0 == 0) {
+      if (keep) keep_acc(ok, ov);
+      else put(ok, ov);
+    }
   } else {
     const auto zero = [](int, int) { return f32x4{0.f, 0.f, 0.f, 0.f}; };
-    put(zero, zero);
+    if (keep) keep_acc(zero, zero);
+    else put(zero, zero);
   }
+  if (keep) return;  // whole workgroup
   __syncthreads();
   constexpr int QCH = DQK / 8, YCH = DV / 8;
   for (int idx = tid; idx < KB * QCH; idx += 256) {
@@ -531,6 +569,7 @@ hipError_t launch_keys(const SelArgs& a, hipStream_t s) {
   k.lse2 = a.lse2; k.ndrow = a.ndrow;
   k.dk = (uint16_t*)a.dk; k.dv = (uint16_t*)a.dv; k.dq_part = (uint16_t*)a.dq_part;
   k.cu_kv = a.cu_kv; k.blkoff = a.blkoff; k.offsets = a.offsets; k.list = a.list; k.sched = a.cursor;
+  k.wofs = a.wofs; k.kvacc = a.kvacc; k.nwin = a.nwin; k.win = a.win; k.e_lo = (int)(a.t0 * a.cnt);
   k.batch = a.batch; k.n1 = a.n1; k.n2 = a.n2; k.G = a.G; k.bs = a.bs; k.cnt = a.cnt; k.nblk_total = a.nblk_total;
   k.scale = a.scale; k.scale_log2e = a.scale_log2e;
   const dim3 grid((unsigned)(a.n2 * a.nblk_total));

@@ -2,9 +2,10 @@
 //
 // Page "NsaSelectedAttentionGrad", formula section: dQ = dS K / sqrt(d) over the gathered
 // rows, i.e. the sum over the selected blocks of each block's dS_block K_block.  The
-// KV-major kernel stores every block's share (bf16) at [t, slot, kvh, head, :] (the list entry
-// t cnt + slot times n2, plus kvh: no division in the store address); this kernel adds the
-// slots of each (token, KV head) in slot order and scales:
+// KV-major kernel stores every block's share (bf16) at [t - t0, slot, kvh, head, :] for the
+// tokens [t0, t1) of the current window (the list entry t cnt + slot, less t0 cnt, times n2,
+// plus kvh: no division in the store address); this kernel adds the slots of each (token,
+// KV head) of the window in slot order and scales:
 //   dQ[t, kvh G + h, :] = scale * sum_slot part[t, slot, kvh, h, :].
 // Fixed order, one writer per output row: deterministic.
 //
@@ -33,14 +34,15 @@ __device__ __forceinline__ void add_bf16x8(float* acc, const uint4& x) {
 }
 
 template <int DQK>
-__global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, uint16_t* dq, int64_t pairs, int n2,
-                                                        int n1, int G, int cnt, float scale, const int32_t* topk,
-                                                        const int64_t* cu_q, const int32_t* blkoff, int batch) {
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, uint16_t* dq, int64_t t0, int64_t pairs,
+                                                        int n2, int n1, int G, int cnt, float scale,
+                                                        const int32_t* topk, const int64_t* cu_q,
+                                                        const int32_t* blkoff, int batch) {
   const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= pairs) return;  // whole wave
-  const int64_t t = pair / n2;
-  const int kvh = (int)(pair - t * n2);
+  const int64_t wpair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // within the window
+  if (wpair >= pairs) return;  // whole wave
+  const int64_t tw = wpair / n2, t = t0 + tw, pair = t0 * n2 + wpair;
+  const int kvh = (int)(wpair - tw * n2);
   const int b = seq_of(cu_q, batch, t);
   const int nblk = blkoff[b + 1] - blkoff[b];
   uint64_t valid[2];
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, ui
   auto slot_ok = [&](int sl) -> bool { return (valid[sl >> 6] >> (sl & 63)) & 1; };
   const int chunks = G * DQK / 8;
   const int64_t slot_stride = (int64_t)n2 * G * DQK;
-  const uint16_t* src = part + (t * cnt * n2 + kvh) * (int64_t)G * DQK;
+  const uint16_t* src = part + (tw * cnt * n2 + kvh) * (int64_t)G * DQK;
   uint16_t* out = dq + (t * n1 + (int64_t)kvh * G) * DQK;
   for (int c0 = lane; c0 < chunks; c0 += 64 * kU) {
     float acc[kU][8];
@@ -98,14 +100,14 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, ui
 }  // namespace
 
 hipError_t launch_selected_dq_reduce(const SelArgs& a, hipStream_t s) {
-  const int64_t pairs = a.T1 * a.n2;
+  const int64_t pairs = (a.t1 - a.t0) * a.n2;  // (token, KV head) pairs of the window
   if (pairs == 0) return hipSuccess;
   const dim3 grid((unsigned)((pairs + 3) / 4)), block(256);
   if (a.d_qk == 192)
-    hipLaunchKernelGGL(dq_reduce_kernel<192>, grid, block, 0, s, (const uint16_t*)a.dq_part, (uint16_t*)a.dq, pairs,
+    hipLaunchKernelGGL(dq_reduce_kernel<192>, grid, block, 0, s, (const uint16_t*)a.dq_part, (uint16_t*)a.dq, a.t0, pairs,
                        a.n2, a.n1, a.G, a.cnt, a.scale, a.topk, a.cu_q, a.blkoff, a.batch);
   else if (a.d_qk == 128)
-    hipLaunchKernelGGL(dq_reduce_kernel<128>, grid, block, 0, s, (const uint16_t*)a.dq_part, (uint16_t*)a.dq, pairs,
+    hipLaunchKernelGGL(dq_reduce_kernel<128>, grid, block, 0, s, (const uint16_t*)a.dq_part, (uint16_t*)a.dq, a.t0, pairs,
                        a.n2, a.n1, a.G, a.cnt, a.scale, a.topk, a.cu_q, a.blkoff, a.batch);
   else
     return hipErrorInvalidValue;

@@ -67,21 +67,21 @@ def oracle_backward(w: W.Workload, x):
     return {"dq": dq, "dk": dk, "dv": dv}
 
 
-def problem_for(w: W.Workload, deterministic=None, dq_mode=0):
+def problem_for(w: W.Workload, deterministic=None, dq_mode=0, window_tokens=0):
     import sparse_attention_backward_amd as sab
     det = w.deterministic if deterministic is None else deterministic
     if w.form == "dense":
         return sab.Problem.dense(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, causal=w.causal,
                                  d_rope=w.d_rope, dtype=w.dtype, deterministic=det, dq_mode=dq_mode)
     return sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size, w.block_count,
-                                deterministic=det)
+                                deterministic=det, window_tokens=window_tokens)
 
 
-def gpu_backward(w: W.Workload, x, o, smax, ssum, device="cuda", deterministic=None, dq_mode=0):
+def gpu_backward(w: W.Workload, x, o, smax, ssum, device="cuda", deterministic=None, dq_mode=0, window_tokens=0):
     """Run the library on the GPU; returns the output tensors (on the device)."""
     import sparse_attention_backward_amd as sab
     dev = lambda t: None if t is None else t.to(device).contiguous()  # noqa: E731
-    prob = problem_for(w, deterministic, dq_mode)
+    prob = problem_for(w, deterministic, dq_mode, window_tokens)
     if w.form == "dense":
         outs = sab.dense_backward(prob, dev(x["query"]), dev(x["query_rope"]), dev(x["key"]), dev(x["key_rope"]),
                                   dev(x["value"]), dev(o), dev(x["dy"]), dev(smax), dev(ssum))

@@ -196,3 +196,48 @@ def test_dense_dq_mode_field():
     p = selected()
     p.s.dense_dq_mode = 1
     assert status_ws(p)[0] == INVALID
+
+
+# ---- selected workspace bound -------------------------------------------------------------
+SHARE_CAP = 64 << 30   # dQ shares of one window: at most 64 GiB (then more windows)
+
+
+def _selected_ws_bound(T1, T2, n1, n2, d_qk, d_v, bs, cnt):
+    """Workspace the selected call may take: the share cap plus terms linear in the inputs --
+    12 B per topk entry (list, sort scratch), the per-block fp32 dK / dV sums carried between
+    windows (at most 64 / 128 keys per block), the row statistics (8 B per query row) and the
+    index tables (12 B per block and KV head), with 1 MiB of slack for tables and alignment."""
+    entries = T1 * n2 * cnt
+    keys = n2 * (T2 // bs)
+    kb = 128 if bs > 64 else 64
+    return SHARE_CAP + 12 * entries + 4 * keys * kb * (d_qk + d_v) + 8 * T1 * n1 + 12 * keys + (1 << 20)
+
+
+@pytest.mark.parametrize("S,n1,n2,bs,cnt,d_qk,d_v", [
+    (128 << 10, 128, 4, 16, 128, 192, 128),      # longest sequence, most heads, most blocks of the smallest size
+    (128 << 10, 128, 128, 64, 64, 192, 128),      # G = 1
+    (128 << 10, 64, 2, 128, 63, 192, 128),        # cnt * bs = 8064, the largest gather
+    (128 << 10, 96, 3, 32, 100, 128, 128),
+])
+def test_selected_workspace_bounded_at_extreme_shapes(S, n1, n2, bs, cnt, d_qk, d_v):
+    entries = S * n2 * cnt
+    p = selected(cu_q=[0, S], cu_kv=[0, S], n1=n1, n2=n2, d_qk=d_qk, d_v=d_v, block_size=bs, block_count=cnt)
+    st, n = status_ws(p)
+    if entries >= 1 << 31:   # list entries are 32-bit: such problems are refused, not mis-sized
+        assert st == UNSUPPORTED
+        return
+    assert st == OK
+    assert n <= _selected_ws_bound(S, S, n1, n2, d_qk, d_v, bs, cnt), n
+    full_shares = S * cnt * n1 * d_qk * 2
+    if full_shares > SHARE_CAP:
+        assert n < full_shares  # the shares of the whole problem would not fit: windows
+
+
+def test_selected_window_tokens_shrink_the_workspace():
+    big = status_ws(selected())[1]
+    small = status_ws(selected(window_tokens=16))[1]
+    assert small < big
+    assert status_ws(selected(window_tokens=-1))[0] == INVALID
+    d = dense()
+    d.s.sel_window_tokens = 5   # a selected-only field: must be 0 for dense problems
+    assert status_ws(d)[0] == INVALID

@@ -10,11 +10,12 @@ from helpers import (assert_close, check_against_oracle, f64, gpu_backward, orac
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, deterministic=None, dq_mode=0):
+def _run(w, deterministic=None, dq_mode=0, window_tokens=0):
     x = W.make_inputs(w)
     o, smax, ssum = oracle_forward(w, x)
-    print(f"[parity] {w.name} seqlens={w.seqlens_q}/{w.seqlens_kv} n1={w.n1} n2={w.n2} dq_mode={dq_mode}", flush=True)
-    got = gpu_backward(w, x, o, smax, ssum, deterministic=deterministic, dq_mode=dq_mode)
+    print(f"[parity] {w.name} seqlens={w.seqlens_q}/{w.seqlens_kv} n1={w.n1} n2={w.n2} dq_mode={dq_mode} "
+          f"window_tokens={window_tokens}", flush=True)
+    got = gpu_backward(w, x, o, smax, ssum, deterministic=deterministic, dq_mode=dq_mode, window_tokens=window_tokens)
     ref = oracle_backward(w, x)
     check_against_oracle(w, got, ref)
     return x, got, ref
@@ -68,6 +69,35 @@ def test_dense_fp32_small_rope():
 ])
 def test_selected(kw):
     _run(W.small_selected(**kw))
+
+
+# Windows of query tokens: the dQ shares are formed and summed one window at a time and the
+# dK / dV accumulators carried between windows in fp32.  Ragged windows (the last shorter), a
+# window shorter than a step's entries, windows that cross a sequence boundary, and blocks
+# that no token of a middle window selected.
+@pytest.mark.parametrize("window_tokens,kw", [
+    (37, dict(seqlens=(256, 384), block_size=64, block_count=3)),
+    (100, dict(seqlens=(256, 512), block_size=128, block_count=2)),
+    (3, dict(seqlens=(40, 9), seqlens_kv=(512, 256), block_size=64, block_count=2, n1=16, n2=1)),
+    (64, dict(seqlens=(200, 0, 64), seqlens_kv=(256, 128, 192), block_size=64, block_count=2, index_dist="zipf")),
+    (50, dict(seqlens=(96, 64), seqlens_kv=(384, 192), block_size=96, block_count=2, n1=6, n2=2)),
+])
+def test_selected_windows(window_tokens, kw):
+    _run(W.small_selected(**kw), window_tokens=window_tokens)
+
+
+def test_selected_windows_match_single_window():
+    """dQ does not depend on the windows (same shares, same slot order); dK / dV only through
+    the fp32 summation order."""
+    w = W.small_selected(seqlens=(256, 384), block_size=64, block_count=4, index_dist="zipf")
+    x = W.make_inputs(w)
+    o, smax, ssum = oracle_forward(w, x)
+    a = gpu_backward(w, x, o, smax, ssum, deterministic=True)
+    b = gpu_backward(w, x, o, smax, ssum, deterministic=True, window_tokens=41)
+    assert torch.equal(a["dq"], b["dq"])
+    for n in ("dk", "dv"):
+        d = (a[n].double() - b[n].double()).abs().max().item()
+        assert d <= 1e-2 * a[n].double().abs().max().item(), (n, d)
 
 
 def test_selected_duplicate_ids():
