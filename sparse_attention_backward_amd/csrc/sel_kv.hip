@@ -223,21 +223,14 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     }
   }
 
-  // dK / dV accumulators: zero, or (after the first window) the key's running sums; with
-  // KB = 64 the two row-half waves of a key group were added at the end of the previous
-  // window, and the first of them continues from that sum.
-  // kvacc layout per key: [key group kh][t][NQ dK tiles, NV dV tiles][lane] f32x4
+  // dK / dV accumulators of this window (the sums of earlier windows are added at the end)
   f32x4 dK[2][NQ], dV[2][NV];
-  f32x4* const accu = reinterpret_cast<f32x4*>(a.kvacc) + (int64_t)u * (KB / 32) * NACC * 64;
-  const bool resume = !first_win && (NRH != 1 || rh0 == 0);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
-    for (int n = 0; n < NQ; ++n)
-      dK[t][n] = resume ? accu[(kh * NACC + t * (NQ + NV) + n) * 64 + lane] : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NQ; ++n) dK[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int n = 0; n < NV; ++n)
-      dV[t][n] = resume ? accu[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane] : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NV; ++n) dV[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // ---- list entries: row `lane` of step st is entry e_begin + st * TPS + lane / G ------
@@ -483,15 +476,26 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   }
 
   // ---- epilogue: dK, dV to bf16 through LDS (KB = 64: the two row halves summed first),
-  // then 16-byte stores of whole rows; before the last window, the fp32 sums go to kvacc ----
+  // then 16-byte stores of whole rows.  With several windows the fp32 sums of the earlier
+  // windows are added (in this fixed order: row half 0, row half 1, earlier windows), and
+  // before the last window the result goes back to kvacc instead.
+  // kvacc layout per key: [key group kh][t][NQ dK tiles, NV dV tiles][lane] f32x4
+  f32x4* const accu = reinterpret_cast<f32x4*>(a.kvacc) + (int64_t)u * (KB / 32) * NACC * 64;
   const bool keep = !last_win;
+  auto prev = [&](int i) { return first_win ? f32x4{0.f, 0.f, 0.f, 0.f} : accu[i * 64 + lane]; };
   auto keep_acc = [&](auto&& other_k, auto&& other_v) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int n = 0; n < NQ; ++n) accu[(kh * NACC + t * (NQ + NV) + n) * 64 + lane] = dK[t][n] + other_k(t, n);
+      for (int n = 0; n < NQ; ++n) {
+        const int i = kh * NACC + t * (NQ + NV) + n;
+        accu[i * 64 + lane] = dK[t][n] + other_k(t, n) + prev(i);
+      }
 #pragma unroll
-      for (int n = 0; n < NV; ++n) accu[(kh * NACC + t * (NQ + NV) + NQ + n) * 64 + lane] = dV[t][n] + other_v(t, n);
+      for (int n = 0; n < NV; ++n) {
+        const int i = kh * NACC + t * (NQ + NV) + NQ + n;
+        accu[i * 64 + lane] = dV[t][n] + other_v(t, n) + prev(i);
+      }
     }
   };
   __syncthreads();
@@ -503,15 +507,18 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
         const f32x4 o = other_k(t, n);
+        const f32x4 e = prev(kh * NACC + t * (NQ + NV) + n);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          Ko[(32 * kh + 16 * t + 4 * g + i) * DQK + 16 * n + l16] = f2bf((dK[t][n][i] + o[i]) * a.scale);
+          Ko[(32 * kh + 16 * t + 4 * g + i) * DQK + 16 * n + l16] = f2bf((dK[t][n][i] + o[i] + e[i]) * a.scale);
       }
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
         const f32x4 o = other_v(t, n);
+        const f32x4 e = prev(kh * NACC + t * (NQ + NV) + NQ + n);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Vo[(32 * kh + 16 * t + 4 * g + i) * DV + 16 * n + l16] = f2bf(dV[t][n][i] + o[i]);
+        for (int i = 0; i < 4; ++i)
+          Vo[(32 * kh + 16 * t + 4 * g + i) * DV + 16 * n + l16] = f2bf(dV[t][n][i] + o[i] + e[i]);
       }
     }
   };
