@@ -135,6 +135,30 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p,
                                     void* workspace, uint64_t workspace_bytes,
                                     void* hip_stream);
 
+/* Size of the fixed device scratch array behind attn_bwd_dense_varlen_noalloc (64 MiB). */
+#define ATTN_BWD_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* attn_bwd_dense_varlen without a workspace, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, layouts and results are those of attn_bwd_dense_varlen; the workspace is a
+ * fixed array of ATTN_BWD_NOALLOC_SCRATCH_BYTES in the library's device code, one per GPU,
+ * held from the library's load until the process ends.  The call allocates nothing: no
+ * hipMalloc / hipFree / pinned host memory and no events (the per-kernel timing of
+ * attn_bwd_profiling does not see it); its schedule tables are copied from pageable host
+ * memory with hipMemcpyAsync on `hip_stream`.  With dense_dq_mode = 0 it picks the stored-dS
+ * mode when that plan fits the array, else the recompute mode.
+ * Returns ATTN_ERR_WORKSPACE (nothing enqueued) when the problem needs more than the array
+ * (the workspace-size query gives the need); the other codes as attn_bwd_dense_varlen.
+ * Every call on one GPU uses the same array: calls that overlap on one GPU (other streams,
+ * other host threads) race and give wrong results; calls ordered on one stream are safe. */
+attn_status_t attn_bwd_dense_varlen_noalloc(const attn_bwd_problem_t* p,
+                                            const void* q, const void* q_rope,
+                                            const void* k, const void* k_rope,
+                                            const void* v, const void* out, const void* dy,
+                                            const float* softmax_max, const float* softmax_sum,
+                                            void* dq, void* dq_rope, void* dk, void* dk_rope, void* dv,
+                                            void* hip_stream);
+
 /* Selected (NSA) backward (page "NsaSelectedAttentionGrad").  p->op must be
  * ATTN_OP_SELECTED, p->dtype ATTN_BF16.  The page lists attentionOut as optional;
  * this build requires it (NULL -> ATTN_ERR_UNSUPPORTED). */

@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "AttnError", "Problem", "LIB_PATH", "lib",
-    "attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_selected",
+    "attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_dense_varlen_noalloc", "attn_bwd_selected",
     "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version",
     "attn_bwd_profiling", "attn_bwd_profile_reset", "attn_bwd_profile_read",
     "dense_backward", "selected_backward", "EXPORTED_SYMBOLS",
@@ -34,7 +34,10 @@ ATTN_OK, ATTN_ERR_NULLPTR, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORK
 ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
 ATTN_OP_DENSE, ATTN_OP_SELECTED = 0, 1
 
-EXPORTED_SYMBOLS = ("attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_selected",
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_BWD_NOALLOC_SCRATCH_BYTES
+
+EXPORTED_SYMBOLS = ("attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_dense_varlen_noalloc",
+                    "attn_bwd_selected",
                     "attn_bwd_check_index_flag", "attn_bwd_profiling", "attn_bwd_profile_reset",
                     "attn_bwd_profile_read", "attn_bwd_status_string", "attn_bwd_version")
 
@@ -62,6 +65,9 @@ def _load():
     L.attn_bwd_dense_varlen.argtypes = [P] + [c_void_p] * 7 + [c_void_p, c_void_p] + [c_void_p] * 5 + \
         [c_void_p, c_uint64, c_void_p]
     L.attn_bwd_dense_varlen.restype = c_int32
+    L.attn_bwd_dense_varlen_noalloc.argtypes = [P] + [c_void_p] * 7 + [c_void_p, c_void_p] + [c_void_p] * 5 + \
+        [c_void_p]
+    L.attn_bwd_dense_varlen_noalloc.restype = c_int32
     L.attn_bwd_selected.argtypes = [P] + [c_void_p] * 5 + [c_void_p, c_void_p, c_void_p] + [c_void_p] * 3 + \
         [c_void_p, c_uint64, c_void_p]
     L.attn_bwd_selected.restype = c_int32
@@ -188,6 +194,14 @@ def attn_bwd_dense_varlen(problem, q, q_rope, k, k_rope, v, out, dy, softmax_max
                                    _ptr(dy), _ptr(softmax_max), _ptr(softmax_sum), _ptr(dq), _ptr(dq_rope), _ptr(dk),
                                    _ptr(dk_rope), _ptr(dv), _ptr(workspace), wb, _stream(stream))
     _check(st, "attn_bwd_dense_varlen")
+
+
+def attn_bwd_dense_varlen_noalloc(problem, q, q_rope, k, k_rope, v, out, dy, softmax_max, softmax_sum,
+                                  dq, dq_rope, dk, dk_rope, dv, stream=None):
+    st = _L().attn_bwd_dense_varlen_noalloc(problem.ref, _ptr(q), _ptr(q_rope), _ptr(k), _ptr(k_rope), _ptr(v),
+                                           _ptr(out), _ptr(dy), _ptr(softmax_max), _ptr(softmax_sum), _ptr(dq),
+                                           _ptr(dq_rope), _ptr(dk), _ptr(dk_rope), _ptr(dv), _stream(stream))
+    _check(st, "attn_bwd_dense_varlen_noalloc")
 
 
 def attn_bwd_selected(problem, q, k, v, out, dy, softmax_max, softmax_sum, topk_indices, dq, dk, dv,

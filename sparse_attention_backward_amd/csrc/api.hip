@@ -432,6 +432,116 @@ bool misaligned(const void* ptr) { return ptr && (reinterpret_cast<uintptr_t>(pt
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off); }
 
+// Pointer checks of the dense call (after validate_and_plan).
+attn_status_t dense_check_pointers(const attn_bwd_problem_t* p, const Plan& pl, const void* q, const void* q_rope,
+                                   const void* k, const void* k_rope, const void* v, const void* out, const void* dy,
+                                   const float* softmax_max, const float* softmax_sum, void* dq, void* dq_rope,
+                                   void* dk, void* dk_rope, void* dv) {
+  if (p->op != ATTN_OP_DENSE) return ATTN_ERR_INVALID;
+  const bool has_q = pl.T1 > 0, has_k = pl.T2 > 0;
+  if (has_q && (!q || !out || !dy || !softmax_max || !softmax_sum || !dq)) return ATTN_ERR_NULLPTR;
+  if (has_k && (!k || !v || !dk || !dv)) return ATTN_ERR_NULLPTR;
+  if (p->d_rope > 0) {
+    if ((has_q && (!q_rope || !dq_rope)) || (has_k && (!k_rope || !dk_rope))) return ATTN_ERR_NULLPTR;
+  } else if (q_rope || k_rope || dq_rope || dk_rope) {
+    return ATTN_ERR_INVALID;
+  }
+  for (const void* ptr : {q, q_rope, k, k_rope, v, out, dy, (const void*)softmax_max, (const void*)softmax_sum,
+                          (const void*)dq, (const void*)dq_rope, (const void*)dk, (const void*)dk_rope, (const void*)dv})
+    if (misaligned(ptr)) return ATTN_ERR_INVALID;
+  return ATTN_OK;
+}
+
+// Enqueue the dense backward with `workspace` (pl.total bytes, 256-byte aligned).  no_alloc: the
+// tables are copied with hipMemcpyAsync from pageable host memory (the pinned staging ring
+// allocates on first use) and the per-kernel timing, which creates events, is bypassed.
+attn_status_t dense_launch(const attn_bwd_problem_t* p, const Plan& pl, const void* q, const void* q_rope,
+                           const void* k, const void* k_rope, const void* v, const void* out, const void* dy,
+                           const float* softmax_max, const float* softmax_sum, void* dq, void* dq_rope, void* dk,
+                           void* dk_rope, void* dv, void* workspace, hipStream_t s, bool no_alloc) {
+  if (pl.T1 == 0 && pl.T2 == 0) return ATTN_OK;
+  auto run = [&](const char* name, auto&& launch) -> hipError_t { return no_alloc ? launch() : timed(name, s, launch); };
+  TableStage tables;
+  const std::vector<uint8_t> tab = pack_tables(p, pl);
+  if (no_alloc) {
+    // pageable source: the copy has taken the bytes when the call returns
+    if (!tab.empty() && hipMemcpyAsync(workspace, tab.data(), tab.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+  } else if (tables.stage(tab) != hipSuccess) {
+    return ATTN_ERR_HIP;
+  }
+
+  PreArgs pa{};
+  pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
+  pa.lse2 = at<float>(workspace, pl.off_lse2); pa.ndrow = at<float>(workspace, pl.off_ndrow);
+  pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = p->dtype == ATTN_BF16;
+  pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
+  pa.tab_n16 = no_alloc ? 0 : tables.n16();
+  if (run("row_stats", [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (!no_alloc && tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
+
+  DenseArgs a{};
+  a.q = q; a.q_rope = q_rope; a.k = k; a.k_rope = k_rope; a.v = v; a.dy = dy;
+  a.lse2 = pa.lse2; a.ndrow = pa.ndrow;
+  a.dq = dq; a.dq_rope = dq_rope; a.dk = dk; a.dk_rope = dk_rope; a.dv = dv;
+  a.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
+  a.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
+  a.kv_tiles = at<const int32_t>(workspace, pl.off_tab1);
+  a.q_tiles = at<const int32_t>(workspace, pl.off_tab2);
+  a.ds_base = at<const int64_t>(workspace, pl.off_ds_base);
+  a.ds = pl.dense_ds ? at<void>(workspace, pl.off_ds) : nullptr;
+  a.kv_split = at<const int32_t>(workspace, pl.off_kvsplit);
+  a.kv_part = pl.kv_slots > 0 ? at<void>(workspace, pl.off_kvpart) : nullptr;
+  a.n_kv_tiles = (int)(pl.kv_tiles.size() / 6);
+  a.n_kv_split = (int)(pl.kv_split.size() / 5);
+  a.n_q_tiles = (int)(pl.q_tiles.size() / 2);
+  a.batch = pl.B; a.n1 = p->n1; a.n2 = p->n2; a.G = pl.G;
+  a.T1 = pl.T1; a.T2 = pl.T2;
+  a.d_main = p->d_qk; a.d_rope = p->d_rope; a.d_v = p->d_v;
+  a.scale = (float)p->scale;
+  a.scale_log2e = (float)(p->scale * 1.4426950408889634);
+  a.causal = p->causal;
+  if (p->dtype == ATTN_FP32)
+    return run("dense_fp32", [&] { return launch_dense_fp32(a, s); }) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  if (run("dense_kv_major", [&] { return launch_dense_kv_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (pl.dense_ds) {
+    // one launch: the split key tiles' dK / dV, then dQ = dS K
+    if (run("dense_dq", [&] { return launch_dense_dq_from_ds(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  } else {
+    if (a.n_kv_split > 0 && run("dense_kv_combine", [&] { return launch_dense_kv_combine(a, s); }) != hipSuccess)
+      return ATTN_ERR_HIP;
+    if (run("dense_dq_recompute", [&] { return launch_dense_dq_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+// ---- fixed scratch for attn_bwd_dense_varlen_noalloc --------------------------------------
+// Device memory beyond the inputs and outputs for callers that cannot allocate: one array per
+// GPU, held from module load to process end.  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per device (with that
+// device current), and is kept here.
+constexpr size_t kNoAllocScratch = ATTN_BWD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratch];
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & (kAlign - 1))) return hipErrorInvalidValue;
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -467,69 +577,41 @@ attn_status_t attn_bwd_dense_varlen(const attn_bwd_problem_t* p, const void* q, 
   Plan pl;
   attn_status_t st = validate_and_plan(p, pl);
   if (st != ATTN_OK) return st;
-  if (p->op != ATTN_OP_DENSE) return ATTN_ERR_INVALID;
-  const bool has_q = pl.T1 > 0, has_k = pl.T2 > 0;
-  if (has_q && (!q || !out || !dy || !softmax_max || !softmax_sum || !dq)) return ATTN_ERR_NULLPTR;
-  if (has_k && (!k || !v || !dk || !dv)) return ATTN_ERR_NULLPTR;
-  if (p->d_rope > 0) {
-    if ((has_q && (!q_rope || !dq_rope)) || (has_k && (!k_rope || !dk_rope))) return ATTN_ERR_NULLPTR;
-  } else if (q_rope || k_rope || dq_rope || dk_rope) {
-    return ATTN_ERR_INVALID;
-  }
-  for (const void* ptr : {q, q_rope, k, k_rope, v, out, dy, (const void*)softmax_max, (const void*)softmax_sum,
-                          (const void*)dq, (const void*)dq_rope, (const void*)dk, (const void*)dk_rope, (const void*)dv})
-    if (misaligned(ptr)) return ATTN_ERR_INVALID;
+  st = dense_check_pointers(p, pl, q, q_rope, k, k_rope, v, out, dy, softmax_max, softmax_sum, dq, dq_rope, dk,
+                            dk_rope, dv);
+  if (st != ATTN_OK) return st;
   if (!workspace || workspace_bytes < pl.total || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
     return ATTN_ERR_WORKSPACE;
-  if (!has_q && !has_k) return ATTN_OK;
+  return dense_launch(p, pl, q, q_rope, k, k_rope, v, out, dy, softmax_max, softmax_sum, dq, dq_rope, dk, dk_rope,
+                      dv, workspace, static_cast<hipStream_t>(hip_stream), false);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  TableStage tables;
-  if (tables.stage(pack_tables(p, pl)) != hipSuccess) return ATTN_ERR_HIP;
-
-  PreArgs pa{};
-  pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
-  pa.lse2 = at<float>(workspace, pl.off_lse2); pa.ndrow = at<float>(workspace, pl.off_ndrow);
-  pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = p->dtype == ATTN_BF16;
-  pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
-  pa.tab_n16 = tables.n16();
-  if (timed("row_stats", s, [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
-  if (tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
-
-  DenseArgs a{};
-  a.q = q; a.q_rope = q_rope; a.k = k; a.k_rope = k_rope; a.v = v; a.dy = dy;
-  a.lse2 = pa.lse2; a.ndrow = pa.ndrow;
-  a.dq = dq; a.dq_rope = dq_rope; a.dk = dk; a.dk_rope = dk_rope; a.dv = dv;
-  a.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
-  a.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
-  a.kv_tiles = at<const int32_t>(workspace, pl.off_tab1);
-  a.q_tiles = at<const int32_t>(workspace, pl.off_tab2);
-  a.ds_base = at<const int64_t>(workspace, pl.off_ds_base);
-  a.ds = pl.dense_ds ? at<void>(workspace, pl.off_ds) : nullptr;
-  a.kv_split = at<const int32_t>(workspace, pl.off_kvsplit);
-  a.kv_part = pl.kv_slots > 0 ? at<void>(workspace, pl.off_kvpart) : nullptr;
-  a.n_kv_tiles = (int)(pl.kv_tiles.size() / 6);
-  a.n_kv_split = (int)(pl.kv_split.size() / 5);
-  a.n_q_tiles = (int)(pl.q_tiles.size() / 2);
-  a.batch = pl.B; a.n1 = p->n1; a.n2 = p->n2; a.G = pl.G;
-  a.T1 = pl.T1; a.T2 = pl.T2;
-  a.d_main = p->d_qk; a.d_rope = p->d_rope; a.d_v = p->d_v;
-  a.scale = (float)p->scale;
-  a.scale_log2e = (float)(p->scale * 1.4426950408889634);
-  a.causal = p->causal;
-  if (p->dtype == ATTN_FP32)
-    return timed("dense_fp32", s, [&] { return launch_dense_fp32(a, s); }) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-  if (timed("dense_kv_major", s, [&] { return launch_dense_kv_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
-  if (pl.dense_ds) {
-    // one launch: the split key tiles' dK / dV, then dQ = dS K
-    if (timed("dense_dq", s, [&] { return launch_dense_dq_from_ds(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
-  } else {
-    if (a.n_kv_split > 0 &&
-        timed("dense_kv_combine", s, [&] { return launch_dense_kv_combine(a, s); }) != hipSuccess)
-      return ATTN_ERR_HIP;
-    if (timed("dense_dq_recompute", s, [&] { return launch_dense_dq_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+attn_status_t attn_bwd_dense_varlen_noalloc(const attn_bwd_problem_t* p, const void* q, const void* q_rope,
+                                            const void* k, const void* k_rope, const void* v, const void* out,
+                                            const void* dy, const float* softmax_max, const float* softmax_sum,
+                                            void* dq, void* dq_rope, void* dk, void* dk_rope, void* dv,
+                                            void* hip_stream) {
+  Plan pl;
+  attn_status_t st = validate_and_plan(p, pl);
+  if (st != ATTN_OK) return st;
+  // dQ mode 0 (automatic): stored dS when its plan fits the scratch array, else recomputation
+  attn_bwd_problem_t q2;
+  if (p->op == ATTN_OP_DENSE && p->dtype == ATTN_BF16 && p->dense_dq_mode == 0 && pl.total > kNoAllocScratch) {
+    q2 = *p;
+    q2.dense_dq_mode = 2;
+    p = &q2;
+    pl = Plan();
+    st = validate_and_plan(p, pl);
+    if (st != ATTN_OK) return st;
   }
-  return ATTN_OK;
+  st = dense_check_pointers(p, pl, q, q_rope, k, k_rope, v, out, dy, softmax_max, softmax_sum, dq, dq_rope, dk,
+                            dk_rope, dv);
+  if (st != ATTN_OK) return st;
+  if (pl.total > kNoAllocScratch) return ATTN_ERR_WORKSPACE;
+  void* scratch_ptr = nullptr;
+  if (noalloc_scratch(&scratch_ptr) != hipSuccess) return ATTN_ERR_HIP;
+  return dense_launch(p, pl, q, q_rope, k, k_rope, v, out, dy, softmax_max, softmax_sum, dq, dq_rope, dk, dk_rope,
+                      dv, scratch_ptr, static_cast<hipStream_t>(hip_stream), true);
 }
 
 attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, const void* k, const void* v,

@@ -241,3 +241,12 @@ def test_selected_window_tokens_shrink_the_workspace():
     d = dense()
     d.s.sel_window_tokens = 5   # a selected-only field: must be 0 for dense problems
     assert status_ws(d)[0] == INVALID
+
+
+def test_noalloc_refuses_problems_beyond_the_scratch_array_on_the_host():
+    """The size check of attn_bwd_dense_varlen_noalloc runs before any device call."""
+    p = dense(cu_q=[0, 300000], cu_kv=[0, 300000], n1=32, n2=8, dq_mode=2)
+    st, n = status_ws(p)
+    assert st == OK and n > sab.NOALLOC_SCRATCH_BYTES
+    args = [FAKE] * 14
+    assert sab.lib.attn_bwd_dense_varlen_noalloc(p.ref, *args, None) == WORKSPACE
