@@ -74,11 +74,12 @@ typedef enum {
 } attn_status_t;
 
 typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1, ATTN_FP32 = 2 } attn_dtype_t;
-typedef enum { ATTN_OP_DENSE = 0, ATTN_OP_SELECTED = 1 } attn_op_t;
+typedef enum { ATTN_OP_DENSE = 0, ATTN_OP_SELECTED = 1, ATTN_OP_SELECTED_FWD = 2 } attn_op_t;
 
 typedef struct {
   int32_t op;                     /* attn_op_t                                              */
-  int32_t dtype;                  /* dense: ATTN_BF16 or ATTN_FP32; selected: ATTN_BF16    */
+  int32_t dtype;                  /* dense: ATTN_BF16 or ATTN_FP32; selected (backward and
+                                     forward): ATTN_BF16 or ATTN_FP16                         */
   int32_t batch;                  /* B >= 1                                                 */
   const int64_t* cu_seqlens_q;    /* HOST [B+1]: 0, then running sums of query lengths;
                                      a length may be 0 (dense constraints allow S = 0)     */
@@ -160,14 +161,36 @@ attn_status_t attn_bwd_dense_varlen_noalloc(const attn_bwd_problem_t* p,
                                             void* hip_stream);
 
 /* Selected (NSA) backward (page "NsaSelectedAttentionGrad").  p->op must be
- * ATTN_OP_SELECTED, p->dtype ATTN_BF16.  The page lists attentionOut as optional;
- * this build requires it (NULL -> ATTN_ERR_UNSUPPORTED). */
+ * ATTN_OP_SELECTED, p->dtype ATTN_BF16 or ATTN_FP16 (all tensors but the float32 statistics
+ * and the int32 ids in that type).  The page lists attentionOut as optional: with out == NULL
+ * the row term rowsum(P * dP) is formed by an extra query-major pass over the gathered key and
+ * value rows (P from the passed statistics, dP = dY V^T) instead of rowsum(dY * O); the
+ * gradients are the same up to rounding. */
 attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p,
                                 const void* q, const void* k, const void* v,
                                 const void* out, const void* dy,
                                 const float* softmax_max, const float* softmax_sum,
                                 const int32_t* topk_indices,
                                 void* dq, void* dk, void* dv,
+                                void* workspace, uint64_t workspace_bytes,
+                                void* hip_stream);
+
+/* Selected (NSA) forward, the producer of the backward's attentionOut, softmaxMax and
+ * softmaxSum (page "NsaSelectedAttentionGrad", parameter table: the forward's output and
+ * intermediate outputs).  For every query token and KV head its G query heads attend to the
+ * rows that topk_indices gathers (Gather(key, ids), Gather(value, ids), formula section):
+ *   s = scale * Q K^T,  m = max s,  l = sum exp(s - m),  out = sum exp(s - m) V / l,
+ * softmax_max = m and softmax_sum = l, each written to all 8 lanes of [T1, N1, 8] float32.
+ * p->op must be ATTN_OP_SELECTED_FWD with the constraints of the selected backward;
+ * attn_bwd_workspace_size(p) gives its (small) workspace: the sequence tables and the index
+ * flag.  q [T1, N1, d_qk], k [T2, N2, d_qk], v [T2, N2, d_v], out [T1, N1, d_v] in p->dtype
+ * (bf16 or fp16).  A repeated id counts twice; an out-of-range id is skipped and raises the
+ * flag (attn_bwd_check_index_flag with this workspace).  A row whose ids are all out of
+ * range gets out = 0, m = -inf, l = 0. */
+attn_status_t attn_fwd_selected(const attn_bwd_problem_t* p,
+                                const void* q, const void* k, const void* v,
+                                const int32_t* topk_indices,
+                                void* out, float* softmax_max, float* softmax_sum,
                                 void* workspace, uint64_t workspace_bytes,
                                 void* hip_stream);
 

@@ -23,21 +23,21 @@ import torch
 __all__ = [
     "AttnError", "Problem", "LIB_PATH", "lib",
     "attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_dense_varlen_noalloc", "attn_bwd_selected",
-    "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version",
+    "attn_fwd_selected", "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version",
     "attn_bwd_profiling", "attn_bwd_profile_reset", "attn_bwd_profile_read",
-    "dense_backward", "selected_backward", "EXPORTED_SYMBOLS",
+    "dense_backward", "selected_backward", "selected_forward", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_NULLPTR, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
 ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
-ATTN_OP_DENSE, ATTN_OP_SELECTED = 0, 1
+ATTN_OP_DENSE, ATTN_OP_SELECTED, ATTN_OP_SELECTED_FWD = 0, 1, 2
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_BWD_NOALLOC_SCRATCH_BYTES
 
 EXPORTED_SYMBOLS = ("attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_dense_varlen_noalloc",
-                    "attn_bwd_selected",
+                    "attn_bwd_selected", "attn_fwd_selected",
                     "attn_bwd_check_index_flag", "attn_bwd_profiling", "attn_bwd_profile_reset",
                     "attn_bwd_profile_read", "attn_bwd_status_string", "attn_bwd_version")
 
@@ -71,6 +71,8 @@ def _load():
     L.attn_bwd_selected.argtypes = [P] + [c_void_p] * 5 + [c_void_p, c_void_p, c_void_p] + [c_void_p] * 3 + \
         [c_void_p, c_uint64, c_void_p]
     L.attn_bwd_selected.restype = c_int32
+    L.attn_fwd_selected.argtypes = [P] + [c_void_p] * 7 + [c_void_p, c_uint64, c_void_p]
+    L.attn_fwd_selected.restype = c_int32
     L.attn_bwd_check_index_flag.argtypes = [P, c_void_p, POINTER(c_int32), c_void_p]
     L.attn_bwd_check_index_flag.restype = c_int32
     L.attn_bwd_profiling.argtypes = [c_int32]
@@ -144,9 +146,11 @@ class Problem:
 
     @classmethod
     def selected(cls, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, block_size, block_count, deterministic=False,
-                 dkdv_atomic=False, dtype="bf16", window_tokens=0):
-        """window_tokens: query tokens per window (field sel_window_tokens; 0 automatic)."""
-        return cls(ATTN_OP_SELECTED, {"bf16": ATTN_BF16, "fp32": ATTN_FP32, "fp16": ATTN_FP16}[dtype], cu_q,
+                 dkdv_atomic=False, dtype="bf16", window_tokens=0, forward=False):
+        """window_tokens: query tokens per window (field sel_window_tokens; 0 automatic).
+        forward: the problem of attn_fwd_selected (op ATTN_OP_SELECTED_FWD)."""
+        return cls(ATTN_OP_SELECTED_FWD if forward else ATTN_OP_SELECTED,
+                   {"bf16": ATTN_BF16, "fp32": ATTN_FP32, "fp16": ATTN_FP16}[dtype], cu_q,
                    cu_kv, n1, n2, d_qk, d_v, scale, block_size=block_size, block_count=block_count,
                    deterministic=deterministic, dkdv_atomic=dkdv_atomic, window_tokens=window_tokens)
 
@@ -211,6 +215,26 @@ def attn_bwd_selected(problem, q, k, v, out, dy, softmax_max, softmax_sum, topk_
                                _ptr(softmax_sum), _ptr(topk_indices), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                wb, _stream(stream))
     _check(st, "attn_bwd_selected")
+
+
+def attn_fwd_selected(problem, q, k, v, topk_indices, out, softmax_max, softmax_sum, workspace,
+                      workspace_bytes=None, stream=None):
+    wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = _L().attn_fwd_selected(problem.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(topk_indices), _ptr(out),
+                               _ptr(softmax_max), _ptr(softmax_sum), _ptr(workspace), wb, _stream(stream))
+    _check(st, "attn_fwd_selected")
+
+
+def selected_forward(problem, q, k, v, topk_indices, workspace=None, stream=None):
+    """Allocate out [T1, N1, d_v] and the [T1, N1, 8] statistics (and the workspace unless given)
+    and run attn_fwd_selected.  Returns out, softmax_max, softmax_sum."""
+    T1, n1, dv = q.shape[0], q.shape[1], v.shape[-1]
+    out = torch.empty((T1, n1, dv), dtype=q.dtype, device=q.device)
+    smax = torch.empty((T1, n1, 8), dtype=torch.float32, device=q.device)
+    ssum = torch.empty((T1, n1, 8), dtype=torch.float32, device=q.device)
+    ws = workspace if workspace is not None else _workspace(problem, q.device)
+    attn_fwd_selected(problem, q, k, v, topk_indices, out, smax, ssum, ws, stream=stream)
+    return out, smax, ssum
 
 
 def attn_bwd_check_index_flag(problem, workspace, stream=None) -> bool:

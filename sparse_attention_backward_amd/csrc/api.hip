@@ -166,7 +166,7 @@ void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
 
 attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   if (!p) return ATTN_ERR_NULLPTR;
-  if (p->op != ATTN_OP_DENSE && p->op != ATTN_OP_SELECTED) return ATTN_ERR_INVALID;
+  if (p->op != ATTN_OP_DENSE && p->op != ATTN_OP_SELECTED && p->op != ATTN_OP_SELECTED_FWD) return ATTN_ERR_INVALID;
   if (p->batch < 1) return ATTN_ERR_INVALID;
   if (!p->cu_seqlens_q || !p->cu_seqlens_kv) return ATTN_ERR_NULLPTR;
   const int B = p->batch;
@@ -203,8 +203,8 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     if (p->dense_dq_mode < 0 || p->dense_dq_mode > 2 || p->sel_window_tokens != 0) return ATTN_ERR_INVALID;
     plan_dense_schedule(p, pl);
   } else {
-    if (p->dtype == ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
-    if (p->dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+    // selected backward and forward: BFLOAT16 or FLOAT16 (parameter table)
+    if (p->dtype != ATTN_BF16 && p->dtype != ATTN_FP16) return ATTN_ERR_INVALID;
     if (p->d_rope != 0 || p->causal != 0 || p->dense_dq_mode != 0) return ATTN_ERR_INVALID;
     // D is 192 or 128 (K and V may differ); N1, N2 in 1..128; G in 1..32
     if ((p->d_qk != 128 && p->d_qk != 192) || (p->d_v != 128 && p->d_v != 192)) return ATTN_ERR_INVALID;
@@ -260,6 +260,11 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   }
   pl.table_bytes = o;
   o = align_up(o);
+  if (p->op == ATTN_OP_SELECTED_FWD) {  // the forward needs the tables and the index flag only
+    pl.off_flag = o;
+    pl.total = align_up(o + 4);
+    return ATTN_OK;
+  }
   const size_t rows = (size_t)pl.T1 * p->n1;
   pl.off_lse2 = o; o = align_up(o + 4 * rows);
   pl.off_ndrow = o; o = align_up(o + 4 * rows);
@@ -474,7 +479,7 @@ attn_status_t dense_launch(const attn_bwd_problem_t* p, const Plan& pl, const vo
   PreArgs pa{};
   pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
   pa.lse2 = at<float>(workspace, pl.off_lse2); pa.ndrow = at<float>(workspace, pl.off_ndrow);
-  pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = p->dtype == ATTN_BF16;
+  pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.elem = p->dtype == ATTN_BF16 ? 0 : 2;
   pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
   pa.tab_n16 = no_alloc ? 0 : tables.n16();
   if (run("row_stats", [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
@@ -623,7 +628,8 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   if (st != ATTN_OK) return st;
   if (p->op != ATTN_OP_SELECTED) return ATTN_ERR_INVALID;
   const bool has_q = pl.T1 > 0, has_k = pl.T2 > 0;
-  if (has_q && !out) return ATTN_ERR_UNSUPPORTED;  // attentionOut is optional on the page; required here
+  // attentionOut is optional (parameter table): without it rowsum(P * dP) is formed from the
+  // gathered rows by a query-major pass instead of rowsum(dY * O)
   if (has_q && (!q || !dy || !softmax_max || !softmax_sum || !topk_indices || !dq)) return ATTN_ERR_NULLPTR;
   if (has_k && (!k || !v || !dk || !dv)) return ATTN_ERR_NULLPTR;
   for (const void* ptr : {q, k, v, out, dy, (const void*)softmax_max, (const void*)softmax_sum,
@@ -640,11 +646,24 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   PreArgs pa{};
   pa.out = out; pa.dy = dy; pa.smax = softmax_max; pa.ssum = softmax_sum;
   pa.lse2 = at<float>(workspace, pl.off_lse2); pa.ndrow = at<float>(workspace, pl.off_ndrow);
-  pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.is_bf16 = 1;
+  pa.rows = pl.T1 * p->n1; pa.dv = p->d_v; pa.elem = p->dtype == ATTN_FP16 ? 1 : 0;
   pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
   pa.tab_n16 = tables.n16();
   if (timed("row_stats", s, [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
   if (tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
+  if (!out && has_q) {
+    SelFwdArgs f{};
+    f.q = q; f.k = k; f.v = v; f.dy = dy; f.topk = topk_indices;
+    f.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
+    f.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
+    f.lse2 = pa.lse2; f.ndrow = pa.ndrow;
+    f.flag = nullptr;  // the index build below checks the ids and raises the flag
+    f.batch = pl.B; f.n1 = p->n1; f.n2 = p->n2; f.G = pl.G; f.d_qk = p->d_qk; f.d_v = p->d_v;
+    f.bs = p->block_size; f.cnt = p->block_count; f.T1 = pl.T1;
+    f.scale_log2e = (float)(p->scale * 1.4426950408889634);
+    f.is_f16 = p->dtype == ATTN_FP16;
+    if (timed("selected_row_stat", s, [&] { return launch_selected_drow(f, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  }
 
   SelArgs a{};
   a.q = q; a.k = k; a.v = v; a.dy = dy; a.lse2 = pa.lse2; a.ndrow = pa.ndrow; a.topk = topk_indices;
@@ -668,6 +687,7 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   a.win_tokens = pl.win_tokens;
   a.wofs = pl.nwin > 1 ? at<int32_t>(workspace, pl.off_wofs) : nullptr;
   a.kvacc = pl.nwin > 1 ? at<float>(workspace, pl.off_kvacc) : nullptr;
+  a.is_f16 = p->dtype == ATTN_FP16;
   if (timed("selected_index", s, [&] {
         const hipError_t e = launch_selected_index(a, s);
         return e != hipSuccess ? e : launch_selected_window_offsets(a, s);
@@ -684,13 +704,51 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   return ATTN_OK;
 }
 
+attn_status_t attn_fwd_selected(const attn_bwd_problem_t* p, const void* q, const void* k, const void* v,
+                                const int32_t* topk_indices, void* out, float* softmax_max, float* softmax_sum,
+                                void* workspace, uint64_t workspace_bytes, void* hip_stream) {
+  Plan pl;
+  attn_status_t st = validate_and_plan(p, pl);
+  if (st != ATTN_OK) return st;
+  if (p->op != ATTN_OP_SELECTED_FWD) return ATTN_ERR_INVALID;
+  const bool has_q = pl.T1 > 0;
+  if (has_q && (!q || !k || !v || !topk_indices || !out || !softmax_max || !softmax_sum)) return ATTN_ERR_NULLPTR;
+  for (const void* ptr : {q, k, v, (const void*)topk_indices, (const void*)out, (const void*)softmax_max,
+                          (const void*)softmax_sum})
+    if (misaligned(ptr)) return ATTN_ERR_INVALID;
+  if (!workspace || workspace_bytes < pl.total || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return ATTN_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  int32_t* flag = at<int32_t>(workspace, pl.off_flag);
+  if (launch_fill_i32(flag, 1, 0, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (!has_q) return ATTN_OK;
+  TableStage tables;
+  if (tables.stage(pack_tables(p, pl)) != hipSuccess) return ATTN_ERR_HIP;
+  PreArgs pa{};  // no rows: the launch only copies the tables into the workspace
+  pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
+  pa.tab_n16 = tables.n16();
+  if (timed("tables", s, [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
+  SelFwdArgs f{};
+  f.q = q; f.k = k; f.v = v; f.topk = topk_indices;
+  f.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
+  f.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
+  f.o = out; f.smax = softmax_max; f.ssum = softmax_sum; f.flag = flag;
+  f.batch = pl.B; f.n1 = p->n1; f.n2 = p->n2; f.G = pl.G; f.d_qk = p->d_qk; f.d_v = p->d_v;
+  f.bs = p->block_size; f.cnt = p->block_count; f.T1 = pl.T1;
+  f.scale_log2e = (float)(p->scale * 1.4426950408889634);
+  f.is_f16 = p->dtype == ATTN_FP16;
+  return timed("selected_forward", s, [&] { return launch_selected_forward(f, s); }) == hipSuccess ? ATTN_OK
+                                                                                                    : ATTN_ERR_HIP;
+}
+
 attn_status_t attn_bwd_check_index_flag(const attn_bwd_problem_t* p, const void* workspace, int32_t* raised,
                                         void* hip_stream) {
   if (!raised || !workspace) return ATTN_ERR_NULLPTR;
   Plan pl;
   attn_status_t st = validate_and_plan(p, pl);
   if (st != ATTN_OK) return st;
-  if (p->op != ATTN_OP_SELECTED) return ATTN_ERR_INVALID;
+  if (p->op != ATTN_OP_SELECTED && p->op != ATTN_OP_SELECTED_FWD) return ATTN_ERR_INVALID;
   int32_t h = 0;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   if (hipMemcpyAsync(&h, static_cast<const uint8_t*>(workspace) + pl.off_flag, 4, hipMemcpyDeviceToHost, s) !=

@@ -109,6 +109,48 @@ __device__ __forceinline__ i16x4 pack4(f32x4 v) {
   return __builtin_bit_cast(i16x4, r);
 }
 
+// ---- element types: bf16 and fp16 operands of the 16x16x32 MFMA, fp32 accumulation ----
+template <typename T>
+struct Mma;
+template <>
+struct Mma<__bf16> {
+  typedef bf16x8 v8;
+  static __device__ __forceinline__ f32x4 run(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<_Float16> {
+  typedef f16x8 v8;
+  static __device__ __forceinline__ f32x4 run(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <typename T, typename X>
+__device__ __forceinline__ typename Mma<T>::v8 as_v8(X x) {
+  return __builtin_bit_cast(typename Mma<T>::v8, x);
+}
+// Eight floats (two C tiles' four values each) as one operand, round to nearest even.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::v8 pack8t(f32x4 lo, f32x4 hi) {
+  typename Mma<T>::v8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (T)lo[i];
+    r[4 + i] = (T)hi[i];
+  }
+  return r;
+}
+// float -> the 16-bit pattern of T (round to nearest even), and back
+template <typename T>
+__device__ __forceinline__ uint16_t f2t(float f) {
+  return __builtin_bit_cast(uint16_t, (T)f);
+}
+template <typename T>
+__device__ __forceinline__ float t2f(uint16_t x) {
+  return (float)__builtin_bit_cast(T, x);
+}
+
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 __device__ __forceinline__ void sts16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }

@@ -9,7 +9,7 @@ namespace ab {
 
 // ---- row statistics: lse2 = (m + ln l) * log2(e), ndrow = -rowsum(dY * O) ------
 struct PreArgs {
-  const void* out;        // [rows, dv] bf16 or fp32
+  const void* out;        // [rows, dv] bf16, fp16 or fp32; null: ndrow is not written
   const void* dy;         // [rows, dv]
   const float* smax;      // [rows, 8]
   const float* ssum;      // [rows, 8]
@@ -17,7 +17,7 @@ struct PreArgs {
   float* ndrow;           // [rows]
   int64_t rows;           // T1 * N1
   int dv;
-  int is_bf16;
+  int elem;               // element type of out / dy: 0 bf16, 1 fp16, 2 fp32
   const uint4* tab_src;   // the call's tables in pinned host memory (read by the kernel) ...
   uint4* tab_dst;         // ... copied to the start of the workspace: tab_n16 16-byte words
   int64_t tab_n16;
@@ -90,6 +90,7 @@ struct SelArgs {
                             // sel_kv_keys(bs) * (d_qk + d_v) floats per (KV head, block), in register order
   int win;                  // current window
   int64_t t0, t1;           // its query tokens [t0, t1)
+  int is_f16;               // element type of the tensors and shares: 0 bf16, 1 fp16
 };
 bool selected_supported(int d_qk, int d_v, int G, int bs);
 inline int sel_kv_keys(int bs) { return bs > 64 ? 128 : 64; }  // keys per KV-major workgroup
@@ -97,6 +98,25 @@ hipError_t launch_selected_index(const SelArgs& a, hipStream_t s);
 hipError_t launch_selected_window_offsets(const SelArgs& a, hipStream_t s);  // wofs from the lists (nwin > 1)
 hipError_t launch_selected_kv(const SelArgs& a, hipStream_t s);         // dK, dV and the dQ partials
 hipError_t launch_selected_dq_reduce(const SelArgs& a, hipStream_t s);  // dQ = scale * sum of partials
+
+// ---- selected (NSA), query-major: forward, and the row statistic without attentionOut ----
+struct SelFwdArgs {
+  const void* q; const void* k; const void* v; const void* dy;  // dy: row-statistic pass only
+  const int32_t* topk;      // [T1, N2, cnt]
+  const int64_t* cu_q;      // [B+1] (device)
+  const int64_t* cu_kv;     // [B+1] (device)
+  void* o;                  // forward: O [T1, N1, d_v]
+  float* smax; float* ssum; // forward: [T1, N1, 8] softmaxMax, softmaxSum
+  const float* lse2;        // row-statistic pass: [T1 * N1] (m + ln l) log2 e
+  float* ndrow;             // row-statistic pass: [T1 * N1] -sum_j P_j dP_j
+  int32_t* flag;            // raised on an out-of-range topk id (may be null)
+  int batch, n1, n2, G, d_qk, d_v, bs, cnt;
+  int64_t T1;
+  float scale_log2e;
+  int is_f16;               // element type: 0 bf16, 1 fp16
+};
+hipError_t launch_selected_forward(const SelFwdArgs& a, hipStream_t s);  // O, softmaxMax, softmaxSum
+hipError_t launch_selected_drow(const SelFwdArgs& a, hipStream_t s);     // ndrow without O
 
 // ---- misc --------------------------------------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);  // kernel, not a memset node

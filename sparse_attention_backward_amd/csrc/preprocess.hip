@@ -6,7 +6,8 @@
 //          reproduces exp(s * scale - m) / l; a row with l = 0 (no visible key) gets +inf,
 //          which makes every P of that row 0.
 //   ndrow = -sum_d dY[t,h,d] * O[t,h,d], minus rowsum(P * dP) because O = P V; stored negated
-//          so that a dP accumulator started at ndrow ends at dP - rowsum(P * dP).
+//          so that a dP accumulator started at ndrow ends at dP - rowsum(P * dP).  Not written
+//          when O is not given (the selected form then forms it from P and dP).
 // softmaxMax / softmaxSum are [T, N, 8] float32 with identical lanes; lane 0 is read.
 // HBM-bound: 2 * d_v * sizeof(T) + 64 bytes moved per row (the stats rows are 32 B
 // each but a 4-byte read of each touches one 32-byte sector).
@@ -22,6 +23,17 @@ __device__ __forceinline__ float dot16(uint4 a, uint4 b, uint16_t) {
   for (int i = 0; i < 4; ++i) {
     s += __uint_as_float(av[i] << 16) * __uint_as_float(bv[i] << 16);
     s += __uint_as_float(av[i] & 0xffff0000u) * __uint_as_float(bv[i] & 0xffff0000u);
+  }
+  return s;
+}
+
+__device__ __forceinline__ float dot16(uint4 a, uint4 b, _Float16) {
+  float s = 0.f;
+  const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s += t2f<_Float16>((uint16_t)(av[i] & 0xffffu)) * t2f<_Float16>((uint16_t)(bv[i] & 0xffffu));
+    s += t2f<_Float16>((uint16_t)(av[i] >> 16)) * t2f<_Float16>((uint16_t)(bv[i] >> 16));
   }
   return s;
 }
@@ -46,7 +58,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
   for (int64_t base = wave * RPW; base < a.rows; base += nwaves * RPW) {
     const int64_t row = base + lane / LPR;
     float acc = 0.f;
-    if (row < a.rows) {
+    if (row < a.rows && a.out) {
       const T* o = reinterpret_cast<const T*>(a.out) + row * a.dv;
       const T* d = reinterpret_cast<const T*>(a.dy) + row * a.dv;
       for (int c = sub * VEC; c < a.dv; c += LPR * VEC) acc += dot16(ldg16(o + c), ldg16(d + c), T());
@@ -54,7 +66,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (sub == 0 && row < a.rows) {
-      a.ndrow[row] = -acc;
+      if (a.out) a.ndrow[row] = -acc;  // without O the row statistic comes from another pass
       const float m = a.smax[row * 8], l = a.ssum[row * 8];
       a.lse2[row] = (l > 0.f && m > -INFINITY) ? (m + logf(l)) * kLog2e : INFINITY;
     }
@@ -85,7 +97,8 @@ static hipError_t launch_pre_t(const PreArgs& a, hipStream_t s) {
 
 hipError_t launch_preprocess(const PreArgs& a, hipStream_t s) {
   if (a.rows == 0 && a.tab_n16 == 0) return hipSuccess;
-  return a.is_bf16 ? launch_pre_t<uint16_t>(a, s) : launch_pre_t<float>(a, s);
+  if (a.elem == 1) return launch_pre_t<_Float16>(a, s);
+  return a.elem == 2 ? launch_pre_t<float>(a, s) : launch_pre_t<uint16_t>(a, s);
 }
 
 }  // namespace ab

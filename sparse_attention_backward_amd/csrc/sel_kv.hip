@@ -1,6 +1,6 @@
 // Selected (NSA) backward, KV-major: dK and dV of one selected block in registers, and the
-// block's share of dQ for every (token, slot) that selected it (bf16 MFMA, fp32
-// accumulation).
+// block's share of dQ for every (token, slot) that selected it (bf16 or fp16 MFMA, fp32
+// accumulation; P and dS are rounded to the element type for their products).
 //
 // Page "NsaSelectedAttentionGrad", formula section: each query token gathers
 // selectedBlockCount blocks of selectedBlockSize key / value rows through topkIndices
@@ -49,7 +49,7 @@ struct SkvArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* dy;
   const float* lse2; const float* ndrow;
   uint16_t* dk; uint16_t* dv;
-  uint16_t* dq_part;          // [window tokens, cnt, n2, G, DQK] bf16
+  uint16_t* dq_part;          // [window tokens, cnt, n2, G, DQK] in the element type
   const int64_t* cu_kv;
   const int32_t* blkoff;      // [B+1] blocks before each sequence
   const int32_t* offsets;     // inverted index: [n2 * nblk_total + 1]
@@ -95,8 +95,9 @@ struct PartLanes {
   }
 };
 
-template <int DM, int DR, int DV, int KB>
+template <typename T, int DM, int DR, int DV, int KB>
 __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
+  using V8 = typename Mma<T>::v8;
   static_assert(KB == 64 || KB == 128, "64 or 128 keys per workgroup");
   constexpr int NRH = KB / 64;  // 32-row halves of a step taken by each wave
   constexpr int DQK = DM + DR;
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   const int hh_row = lane % G;  // head (within the group) of step row `lane`
 
   // ---- resident keys: K and V as MFMA B operands; K also staged in LDS for dQ --------
-  bf16x8 Kf[2][KS], Vf[2][VS];
+  V8 Kf[2][KS], Vf[2][VS];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int key = 32 * kh + 16 * t + l16;
@@ -156,13 +157,13 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     for (int s = 0; s < KS; ++s) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (valid) x = ldg16(a.k + kr * DQK + 32 * s + 8 * g);
-      Kf[t][s] = __builtin_bit_cast(bf16x8, x);
+      Kf[t][s] = as_v8<T>(x);
     }
 #pragma unroll
     for (int s = 0; s < VS; ++s) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (valid) x = ldg16(a.v + kr * DV + 32 * s + 8 * g);
-      Vf[t][s] = __builtin_bit_cast(bf16x8, x);
+      Vf[t][s] = as_v8<T>(x);
     }
   }
 
@@ -296,27 +297,27 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     }
     constexpr int NS = KS + VS, PA = 3;
     const uint32_t am = vm + TM::rowA(lane, 0), ar = vr + TR::rowA(lane, 0), ay = vy + TY::rowA(lane, 0);
-    auto afrag = [&](int s, int rt) -> bf16x8 {
-      if (s < KSM) return lds_b128_at((am ^ (64u * s)) + (32 * hi + 16 * rt) * TM::RB);
-      if (s < KS) return lds_b128_at((ar ^ (64u * (s - KSM))) + (32 * hi + 16 * rt) * TR::RB);
-      return lds_b128_at((ay ^ (64u * (s - KS))) + (32 * hi + 16 * rt) * TY::RB);
+    auto afrag = [&](int s, int rt) -> V8 {
+      if (s < KSM) return as_v8<T>(lds_b128_at((am ^ (64u * s)) + (32 * hi + 16 * rt) * TM::RB));
+      if (s < KS) return as_v8<T>(lds_b128_at((ar ^ (64u * (s - KSM))) + (32 * hi + 16 * rt) * TR::RB));
+      return as_v8<T>(lds_b128_at((ay ^ (64u * (s - KS))) + (32 * hi + 16 * rt) * TY::RB));
     };
-    bf16x8 aring[PA][2];
+    V8 aring[PA][2];
 #pragma unroll
     for (int i = 0; i < PA; ++i) { aring[i][0] = afrag(i, 0); aring[i][1] = afrag(i, 1); }
     f32x4 S[2][2], D[2][2];  // [key tile][row tile]
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const bf16x8 a0 = aring[s % PA][0], a1 = aring[s % PA][1];
+      const V8 a0 = aring[s % PA][0], a1 = aring[s % PA][1];
       if (s + PA < NS) { aring[s % PA][0] = afrag(s + PA, 0); aring[s % PA][1] = afrag(s + PA, 1); }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         if (s < KS) {
-          S[t][0] = mfma_16x16x32(a0, Kf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][0]);
-          S[t][1] = mfma_16x16x32(a1, Kf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][1]);
+          S[t][0] = Mma<T>::run(a0, Kf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][0]);
+          S[t][1] = Mma<T>::run(a1, Kf[t][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][1]);
         } else {
-          D[t][0] = mfma_16x16x32(a0, Vf[t][s - KS], s == KS ? ndr[0] : D[t][0]);
-          D[t][1] = mfma_16x16x32(a1, Vf[t][s - KS], s == KS ? ndr[1] : D[t][1]);
+          D[t][0] = Mma<T>::run(a0, Vf[t][s - KS], s == KS ? ndr[0] : D[t][0]);
+          D[t][1] = Mma<T>::run(a1, Vf[t][s - KS], s == KS ? ndr[1] : D[t][1]);
         }
       }
     }
@@ -350,11 +351,11 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) D[t][rt][i] = S[t][rt][i] * D[t][rt][i];
-    bf16x8 pa[2], da[2];
+    V8 pa[2], da[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      pa[t] = pack8(S[t][0], S[t][1]);
-      da[t] = pack8(D[t][0], D[t][1]);
+      pa[t] = pack8t<T>(S[t][0], S[t][1]);
+      da[t] = pack8t<T>(D[t][0], D[t][1]);
       // dS^T tile: key 32kh + 16t + l16, rows 32rh + 4g + (0..3) and + 16 (8-byte writes)
       const i16x8 d8 = __builtin_bit_cast(i16x8, da[t]);
       const int key = 32 * kh + 16 * t + l16;
@@ -366,28 +367,28 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     }
     // dV += P^T dY, dK += dS^T Q
     const uint32_t cm = vm + TM::colB(lane, 0), cr = vr + TR::colB(lane, 0), cy = vy + TY::colB(lane, 0);
-    auto colfrag = [&](int j) -> bf16x8 {
+    auto colfrag = [&](int j) -> V8 {
       uint32_t o;
       int rb;
       if (j < NV) { o = cy ^ (32u * j); rb = TY::RB; }
       else if (j < NV + NQM) { o = cm ^ (32u * (j - NV)); rb = TM::RB; }
       else { o = cr ^ (32u * (j - NV - NQM)); rb = TR::RB; }
-      return join8(lds_tr16_at(o + 32 * hi * rb), lds_tr16_at(o + (32 * hi + 16) * rb));
+      return as_v8<T>(join8(lds_tr16_at(o + 32 * hi * rb), lds_tr16_at(o + (32 * hi + 16) * rb)));
     };
     constexpr int NJ = NV + NQ, PD = 4;
-    bf16x8 ring[PD];
+    V8 ring[PD];
 #pragma unroll
     for (int i = 0; i < PD; ++i) ring[i] = colfrag(i);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const bf16x8 bj = ring[j % PD];
+      const V8 bj = ring[j % PD];
       if (j + PD < NJ) ring[j % PD] = colfrag(j + PD);
       if (j < NV) {
-        dV[0][j] = mfma_16x16x32(pa[0], bj, dV[0][j]);
-        dV[1][j] = mfma_16x16x32(pa[1], bj, dV[1][j]);
+        dV[0][j] = Mma<T>::run(pa[0], bj, dV[0][j]);
+        dV[1][j] = Mma<T>::run(pa[1], bj, dV[1][j]);
       } else {
-        dK[0][j - NV] = mfma_16x16x32(da[0], bj, dK[0][j - NV]);
-        dK[1][j - NV] = mfma_16x16x32(da[1], bj, dK[1][j - NV]);
+        dK[0][j - NV] = Mma<T>::run(da[0], bj, dK[0][j - NV]);
+        dK[1][j - NV] = Mma<T>::run(da[1], bj, dK[1][j - NV]);
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 1);
@@ -410,23 +411,23 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
       for (int rr = 0; rr < 2; ++rr) acc[f][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KB / 32; ++ks) {
-      bf16x8 kt[NFH], dt[2];
+      V8 kt[NFH], dt[2];
       static_for_i<NFH>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
         constexpr int F0 = FH * (DQK / 2) + 32 * (f / 2);
         constexpr int rb = F0 < DM ? TM::RB : TR::RB;
         const uint32_t o = (F0 < DM ? kcm ^ (64u * (F0 / 32)) : kcr ^ (64u * ((F0 - DM) / 32))) + 8 * (f % 2) + ks * 32 * rb;
-        kt[f] = join8(lds_tr16_at(o), lds_tr16_at(o + 16 * rb));
+        kt[f] = as_v8<T>(join8(lds_tr16_at(o), lds_tr16_at(o + 16 * rb)));
       });
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const uint32_t o = smem_lds + dscol[rr] + ks * 32 * TD::RB;
-        dt[rr] = join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB));
+        dt[rr] = as_v8<T>(join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TD::RB)));
       }
 #pragma unroll
       for (int f = 0; f < NFH; ++f)
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) acc[f][rr] = mfma_16x16x32(kt[f], dt[rr], acc[f][rr]);
+        for (int rr = 0; rr < 2; ++rr) acc[f][rr] = Mma<T>::run(kt[f], dt[rr], acc[f][rr]);
     }
     // C tile (f, rr): lane holds row 32 qh + 16 rr + l16 and the permuted features above
 #pragma unroll
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
         uint16_t* dst = a.dq_part + (((int64_t)(ent - a.e_lo) * a.n2 + kvh) * G + rmod[rr]) * DQK + FH * (DQK / 2) + 8 * g;
 #pragma unroll
         for (int j = 0; j < NFH / 2; ++j)
-          *reinterpret_cast<bf16x8*>(dst + 32 * j) = pack8(acc[2 * j][rr], acc[2 * j + 1][rr]);
+          *reinterpret_cast<V8*>(dst + 32 * j) = pack8t<T>(acc[2 * j][rr], acc[2 * j + 1][rr]);
       }
     }
   };
@@ -510,7 +511,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
         const f32x4 e = prev(kh * NACC + t * (NQ + NV) + n);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          Ko[(32 * kh + 16 * t + 4 * g + i) * DQK + 16 * n + l16] = f2bf((dK[t][n][i] + o[i] + e[i]) * a.scale);
+          Ko[(32 * kh + 16 * t + 4 * g + i) * DQK + 16 * n + l16] = f2t<T>((dK[t][n][i] + o[i] + e[i]) * a.scale);
       }
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
         const f32x4 e = prev(kh * NACC + t * (NQ + NV) + NQ + n);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          Vo[(32 * kh + 16 * t + 4 * g + i) * DV + 16 * n + l16] = f2bf(dV[t][n][i] + o[i] + e[i]);
+          Vo[(32 * kh + 16 * t + 4 * g + i) * DV + 16 * n + l16] = f2t<T>(dV[t][n][i] + o[i] + e[i]);
       }
     }
   };
@@ -580,8 +581,13 @@ hipError_t launch_keys(const SelArgs& a, hipStream_t s) {
   k.batch = a.batch; k.n1 = a.n1; k.n2 = a.n2; k.G = a.G; k.bs = a.bs; k.cnt = a.cnt; k.nblk_total = a.nblk_total;
   k.scale = a.scale; k.scale_log2e = a.scale_log2e;
   const dim3 grid((unsigned)(a.n2 * a.nblk_total));
-  if (a.d_qk == 192) hipLaunchKernelGGL((sel_kv_kernel<128, 64, 128, KB>), grid, dim3(256), 0, s, k);
-  else hipLaunchKernelGGL((sel_kv_kernel<128, 0, 128, KB>), grid, dim3(256), 0, s, k);
+  if (a.is_f16) {
+    if (a.d_qk == 192) hipLaunchKernelGGL((sel_kv_kernel<_Float16, 128, 64, 128, KB>), grid, dim3(256), 0, s, k);
+    else hipLaunchKernelGGL((sel_kv_kernel<_Float16, 128, 0, 128, KB>), grid, dim3(256), 0, s, k);
+  } else {
+    if (a.d_qk == 192) hipLaunchKernelGGL((sel_kv_kernel<__bf16, 128, 64, 128, KB>), grid, dim3(256), 0, s, k);
+    else hipLaunchKernelGGL((sel_kv_kernel<__bf16, 128, 0, 128, KB>), grid, dim3(256), 0, s, k);
+  }
   return hipGetLastError();
 }
 

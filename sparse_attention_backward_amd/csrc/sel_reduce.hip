@@ -22,18 +22,19 @@ namespace ab {
 namespace {
 
 constexpr int kU = 6;  // chunks per lane per pass
-constexpr uint32_t kNegZero2 = 0x80008000u;  // two bf16 -0.0: x + (-0) == x for every x
+constexpr uint32_t kNegZero2 = 0x80008000u;  // two -0.0 (bf16 and fp16 alike): x + (-0) == x for every x
 
-__device__ __forceinline__ void add_bf16x8(float* acc, const uint4& x) {
+template <typename T>
+__device__ __forceinline__ void add_x8(float* acc, const uint4& x) {
   const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    acc[2 * j] += __uint_as_float(xv[j] << 16);
-    acc[2 * j + 1] += __uint_as_float(xv[j] & 0xffff0000u);
+    acc[2 * j] += t2f<T>((uint16_t)(xv[j] & 0xffffu));
+    acc[2 * j + 1] += t2f<T>((uint16_t)(xv[j] >> 16));
   }
 }
 
-template <int DQK>
+template <typename T, int DQK>
 __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, uint16_t* dq, int64_t t0, int64_t pairs,
                                                         int n2, int n1, int G, int cnt, float scale,
                                                         const int32_t* topk, const int64_t* cu_q,
@@ -79,9 +80,9 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, ui
         if (v1 && c < chunks) x1[u] = ldg16_stream(src + (sl + 1) * slot_stride + 8 * c);
       }
 #pragma unroll
-      for (int u = 0; u < kU; ++u) add_bf16x8(acc[u], x0[u]);
+      for (int u = 0; u < kU; ++u) add_x8<T>(acc[u], x0[u]);
 #pragma unroll
-      for (int u = 0; u < kU; ++u) add_bf16x8(acc[u], x1[u]);
+      for (int u = 0; u < kU; ++u) add_x8<T>(acc[u], x1[u]);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, ui
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          o[j] = (uint32_t)f2bf(acc[u][2 * j] * scale) | ((uint32_t)f2bf(acc[u][2 * j + 1] * scale) << 16);
+          o[j] = (uint32_t)f2t<T>(acc[u][2 * j] * scale) | ((uint32_t)f2t<T>(acc[u][2 * j + 1] * scale) << 16);
         sts16_stream(out + 8 * c, make_uint4(o[0], o[1], o[2], o[3]));
       }
     }
@@ -103,14 +104,21 @@ hipError_t launch_selected_dq_reduce(const SelArgs& a, hipStream_t s) {
   const int64_t pairs = (a.t1 - a.t0) * a.n2;  // (token, KV head) pairs of the window
   if (pairs == 0) return hipSuccess;
   const dim3 grid((unsigned)((pairs + 3) / 4)), block(256);
-  if (a.d_qk == 192)
-    hipLaunchKernelGGL(dq_reduce_kernel<192>, grid, block, 0, s, (const uint16_t*)a.dq_part, (uint16_t*)a.dq, a.t0, pairs,
-                       a.n2, a.n1, a.G, a.cnt, a.scale, a.topk, a.cu_q, a.blkoff, a.batch);
-  else if (a.d_qk == 128)
-    hipLaunchKernelGGL(dq_reduce_kernel<128>, grid, block, 0, s, (const uint16_t*)a.dq_part, (uint16_t*)a.dq, a.t0, pairs,
-                       a.n2, a.n1, a.G, a.cnt, a.scale, a.topk, a.cu_q, a.blkoff, a.batch);
-  else
+  const uint16_t* part = (const uint16_t*)a.dq_part;
+  uint16_t* dq = (uint16_t*)a.dq;
+#define AB_DQ_REDUCE(T, D)                                                                                   \
+  hipLaunchKernelGGL((dq_reduce_kernel<T, D>), grid, block, 0, s, part, dq, a.t0, pairs, a.n2, a.n1, a.G, a.cnt, \
+                     a.scale, a.topk, a.cu_q, a.blkoff, a.batch)
+  if (a.d_qk == 192) {
+    if (a.is_f16) AB_DQ_REDUCE(_Float16, 192);
+    else AB_DQ_REDUCE(__bf16, 192);
+  } else if (a.d_qk == 128) {
+    if (a.is_f16) AB_DQ_REDUCE(_Float16, 128);
+    else AB_DQ_REDUCE(__bf16, 128);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef AB_DQ_REDUCE
   return hipGetLastError();
 }
 

@@ -15,6 +15,10 @@ import workloads as W
 BF16_REL_L2 = 1e-2
 BF16_MAX_ABS = 2e-2   # times max |ref|
 FP32_REL_L2 = 1e-4
+# fp16 (no bar is stated for it): the bf16 bar scaled by the ratio of the unit roundoffs,
+# 2^-11 / 2^-8, with a factor 2 for the P and dS operands rounded to fp16 before their products
+FP16_REL_L2 = 2.5e-3
+FP16_MAX_ABS = 5e-3
 
 
 def f64(t):
@@ -35,6 +39,12 @@ def assert_close(name, got, ref, dtype):
     mref = np.abs(ref).max()
     if dtype == "fp32":
         assert rel <= FP32_REL_L2 or (nref == 0 and err <= 1e-6), f"{name}: rel L2 {rel:.3e} > {FP32_REL_L2}"
+    elif dtype == "fp16":
+        if nref == 0:
+            assert mx <= 1e-6, f"{name}: expected zeros, max |x| = {mx:.3e}"
+            return
+        assert rel <= FP16_REL_L2, f"{name}: rel L2 {rel:.3e} > {FP16_REL_L2}"
+        assert mx <= FP16_MAX_ABS * mref, f"{name}: max abs {mx:.3e} > {FP16_MAX_ABS} * {mref:.3e}"
     else:
         if nref == 0:
             assert mx <= 1e-6, f"{name}: expected zeros, max |x| = {mx:.3e}"
@@ -74,11 +84,12 @@ def problem_for(w: W.Workload, deterministic=None, dq_mode=0, window_tokens=0):
         return sab.Problem.dense(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, causal=w.causal,
                                  d_rope=w.d_rope, dtype=w.dtype, deterministic=det, dq_mode=dq_mode)
     return sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size, w.block_count,
-                                deterministic=det, window_tokens=window_tokens)
+                                deterministic=det, window_tokens=window_tokens, dtype=w.dtype)
 
 
 def gpu_backward(w: W.Workload, x, o, smax, ssum, device="cuda", deterministic=None, dq_mode=0, window_tokens=0):
-    """Run the library on the GPU; returns the output tensors (on the device)."""
+    """Run the library on the GPU; returns the output tensors (on the device).  o = None: the
+    selected call without attentionOut."""
     import sparse_attention_backward_amd as sab
     dev = lambda t: None if t is None else t.to(device).contiguous()  # noqa: E731
     prob = problem_for(w, deterministic, dq_mode, window_tokens)

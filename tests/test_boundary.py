@@ -20,7 +20,7 @@ FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced by the
 
 def header_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:attn_status_t|const char\*)\s+(attn_bwd_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:attn_status_t|const char\*)\s+(attn_(?:bwd|fwd)_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -121,8 +121,8 @@ def test_dense_constraints(kw, want):
     (dict(n1=7, n2=2), INVALID),
     (dict(n1=64, n2=2), OK),                                 # G = 32, the largest group
     (dict(d_v=192), UNSUPPORTED),                            # 192/192: valid, not built
-    (dict(dtype="fp16"), UNSUPPORTED),
-    (dict(dtype="fp32"), INVALID),
+    (dict(dtype="fp16"), OK),                                 # FLOAT16 (parameter table)
+    (dict(dtype="fp32"), INVALID),                           # not a dtype of the selected page
     (dict(cu_q=[0, 256, 640 + (128 << 10)], cu_kv=[0, 256, 640 + (128 << 10)]), INVALID),  # S <= 128K
 ])
 def test_selected_constraints(kw, want):
@@ -138,14 +138,12 @@ def test_selected_rejects_rope_and_causal():
     assert status_ws(p)[0] == INVALID
 
 
-def test_selected_requires_attention_out_and_pointers():
+def test_selected_pointers():
     p = selected()
     n = sab.attn_bwd_workspace_size(p)
     L = sab.lib
     args = [FAKE] * 11
-    # out == NULL: the page lists attentionOut as optional; this build requires it
-    a = list(args); a[3] = None
-    assert L.attn_bwd_selected(p.ref, *a, FAKE, n, None) == UNSUPPORTED
+    # out == NULL is allowed (attentionOut is optional); the other inputs are required
     a = list(args); a[7] = None   # topk
     assert L.attn_bwd_selected(p.ref, *a, FAKE, n, None) == NULLPTR
     assert L.attn_bwd_selected(p.ref, *args, None, n, None) == WORKSPACE
@@ -250,3 +248,20 @@ def test_noalloc_refuses_problems_beyond_the_scratch_array_on_the_host():
     assert st == OK and n > sab.NOALLOC_SCRATCH_BYTES
     args = [FAKE] * 14
     assert sab.lib.attn_bwd_dense_varlen_noalloc(p.ref, *args, None) == WORKSPACE
+
+
+def test_selected_forward_validation():
+    """attn_fwd_selected: op ATTN_OP_SELECTED_FWD, the selected constraints, a small workspace
+    (tables and the index flag, independent of the backward's index and shares)."""
+    fw = selected(forward=True)
+    st, n = status_ws(fw)
+    assert st == OK and 0 < n < 4096
+    assert status_ws(selected(forward=True, block_size=24))[0] == INVALID
+    L = sab.lib
+    args = [FAKE] * 7
+    assert L.attn_fwd_selected(selected().ref, *args, FAKE, n, None) == INVALID      # backward problem
+    a = list(args); a[3] = None   # topk
+    assert L.attn_fwd_selected(fw.ref, *a, FAKE, n, None) == NULLPTR
+    assert L.attn_fwd_selected(fw.ref, *args, FAKE, n - 1, None) == WORKSPACE
+    a = list(args); a[4] = FAKE + 4  # misaligned out
+    assert L.attn_fwd_selected(fw.ref, *a, FAKE, n, None) == INVALID

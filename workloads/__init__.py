@@ -32,7 +32,7 @@ __all__ = ["Workload", "config", "CONFIGS", "make_inputs", "cast", "small_dense"
 class Workload:
     name: str
     form: str                      # "dense" or "selected"
-    dtype: str                     # "bf16" or "fp32"
+    dtype: str                     # "bf16", "fp16" or "fp32"
     seqlens_q: tuple
     seqlens_kv: tuple
     n1: int
@@ -114,10 +114,10 @@ def small_dense(seqlens=(200, 130), n1=8, n2=2, d_qk=128, d_rope=64, d_v=128, dt
 
 
 def small_selected(seqlens=(256, 384), n1=32, n2=2, d_qk=192, d_v=128, block_size=64,
-                   block_count=3, index_dist="uniform", seed=13, seqlens_kv=None):
+                   block_count=3, index_dist="uniform", seed=13, seqlens_kv=None, dtype="bf16"):
     """A multi-block selected case small enough for the oracle."""
     kv = tuple(seqlens_kv) if seqlens_kv is not None else tuple(seqlens)
-    return Workload("selected-small", "selected", "bf16", tuple(seqlens), kv, n1, n2, d_qk, d_v,
+    return Workload(f"selected-small-{dtype}", "selected", dtype, tuple(seqlens), kv, n1, n2, d_qk, d_v,
                     1.0 / math.sqrt(d_qk), block_size=block_size, block_count=block_count,
                     index_dist=index_dist, seed=seed)
 
@@ -126,14 +126,14 @@ def small_selected(seqlens=(256, 384), n1=32, n2=2, d_qk=192, d_v=128, block_siz
 # dtype casts
 # ----------------------------------------------------------------------------
 
-_TORCH_DTYPES = {"bf16": torch.bfloat16, "fp32": torch.float32}
+_TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 
 def cast(x, dtype: str, device="cpu"):
     """float64 / float32 array or tensor -> torch tensor of the workload dtype
     (round to nearest even)."""
     t = torch.as_tensor(x)
-    if t.dtype == torch.float64 and dtype == "bf16":
+    if t.dtype == torch.float64 and dtype in ("bf16", "fp16"):
         t = t.to(torch.float32)
     return t.to(device=device, dtype=_TORCH_DTYPES[dtype]).contiguous()
 
