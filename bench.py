@@ -14,10 +14,11 @@ causal pairs only (the five GEMMs S, dP, dV, dQ, dK; recomputation is not counte
 Before the warmup calls every workload repeats its call for --prewarm-ms of GPU time, so
 that the timed calls run at the sustained clock.
 
-O and the softmax statistics fed to the timed call are produced once, before timing,
-by a plain fp32 torch forward on the GPU (input preparation only).  The float64
-oracle runs only in the CPU-baseline leg, on a bounded sample of the same workload.
-Prints one JSON line.
+O and the softmax statistics fed to the timed call are produced once, before timing:
+for the selected workloads by the library's own forward (attn_fwd_selected, which
+the extra lines also time on its own), for the dense one by a plain fp32 torch
+forward on the GPU.  The float64 oracle runs only in the CPU-baseline leg, on a
+bounded sample of the same workload.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -60,18 +61,19 @@ def attended_pairs(w: W.Workload) -> int:
 
 def flops_per_pair(w: W.Workload, gemms=("S", "dP", "dV", "dQ", "dK")) -> int:
     dqk, dv = w.d_qk + w.d_rope, w.d_v
-    width = {"S": dqk, "dP": dv, "dV": dv, "dQ": dqk, "dK": dqk}
+    width = {"S": dqk, "dP": dv, "dV": dv, "dQ": dqk, "dK": dqk, "O": dv}
     return 2 * sum(width[g] for g in gemms)
 
 
-# library timing name -> (kernel symbol prefix in profiler output, kernel source file)
+# library timing name -> (kernel identifier in profiler output, plain or mangled; kernel source file)
 KERNEL_SOURCES = {
-    "dense_kv_major": ("dense_kv_kernel<", "dense_kv.hip"),
-    "dense_dq": ("dense_dq_ds_kernel<", "dense_dq.hip"),
-    "dense_dq_recompute": ("dense_dq_kernel<", "attn_q.hip"),
-    "selected_kv_major": ("sel_kv_kernel<", "sel_kv.hip"),
-    "selected_dq_reduce": ("dq_reduce_kernel<", "sel_reduce.hip"),
-    "row_stats": ("preprocess_kernel<", "preprocess.hip"),
+    "dense_kv_major": ("dense_kv_kernel", "dense_kv.hip"),
+    "dense_dq": ("dense_dq_ds_kernel", "dense_dq.hip"),
+    "dense_dq_recompute": ("dense_dq_kernel", "attn_q.hip"),
+    "selected_kv_major": ("sel_kv_kernel", "sel_kv.hip"),
+    "selected_dq_reduce": ("dq_reduce_kernel", "sel_reduce.hip"),
+    "selected_forward": ("sel_fwd_kernel", "sel_fwd.hip"),
+    "row_stats": ("preprocess_kernel", "preprocess.hip"),
 }
 CSRC = os.path.join(ROOT, "sparse_attention_backward_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -143,6 +145,7 @@ KERNEL_GEMMS = {
     "dense_dq_recompute": ("S", "dP", "dQ"),
     "selected_kv_major": ("S", "dP", "dV", "dK", "dQ"),
     "dense_fp32": ("S", "dP", "dV", "dQ", "dK", "S", "dP"),
+    "selected_forward": ("S", "O"),
 }
 
 
@@ -156,14 +159,16 @@ def _cat(a, b):
 
 @torch.no_grad()
 def gpu_forward(w: W.Workload, x):
-    """O (workload dtype) and [T1, N1, 8] fp32 softmax max / sum of the forward."""
+    """O (workload dtype) and [T1, N1, 8] fp32 softmax max / sum of the forward: for the dense
+    workloads a plain fp32 torch forward per sequence, for the selected ones the library's
+    attn_fwd_selected."""
     dev = x["query"].device
     T1 = w.T1
-    O = torch.zeros((T1, w.n1, w.d_v), device=dev, dtype=torch.float32)
-    m = torch.full((T1, w.n1), -math.inf, device=dev)
-    l = torch.zeros((T1, w.n1), device=dev)
     G = w.G
     if w.form == "dense":
+        O = torch.zeros((T1, w.n1, w.d_v), device=dev, dtype=torch.float32)
+        m = torch.full((T1, w.n1), -math.inf, device=dev)
+        l = torch.zeros((T1, w.n1), device=dev)
         Q = _cat(x["query"], x["query_rope"]).float()
         K = _cat(x["key"], x["key_rope"]).float()
         V = x["value"].float()
@@ -187,29 +192,12 @@ def gpu_forward(w: W.Workload, x):
             l[qs:qe] = lb.transpose(0, 1)
             del S, P
     else:
-        Q, K, V = x["query"], x["key"], x["value"]
-        n = w.block_count * w.block_size
-        ar = torch.arange(w.block_size, device=dev)
-        chunk = max(1, int(1.5e9 // (w.n2 * n * (w.d_qk + w.d_v))))
-        cq, ck = w.cu_q, w.cu_kv
-        for b in range(w.batch):
-            qs, qe, ks = int(cq[b]), int(cq[b + 1]), int(ck[b])
-            for t0 in range(qs, qe, chunk):
-                t1 = min(qe, t0 + chunk)
-                ids = x["topk"][t0:t1].long()                                           # [C, N2, cnt]
-                rows = (ks + ids[..., None] * w.block_size + ar).reshape(t1 - t0, w.n2, n)
-                hh = torch.arange(w.n2, device=dev)[None, :, None].expand_as(rows)
-                Ks = K[rows, hh].float()                                                 # [C, N2, n, D]
-                Vs = V[rows, hh].float()
-                Qg = Q[t0:t1].float().reshape(t1 - t0, w.n2, G, w.d_qk)
-                S = torch.matmul(Qg, Ks.transpose(-1, -2).contiguous()) * w.scale       # [C, N2, G, n]
-                mb = S.amax(-1)
-                P = torch.exp(S - mb[..., None])
-                lb = P.sum(-1)
-                O[t0:t1] = torch.matmul(P / lb[..., None], Vs).reshape(t1 - t0, w.n1, w.d_v)
-                m[t0:t1] = mb.reshape(t1 - t0, w.n1)
-                l[t0:t1] = lb.reshape(t1 - t0, w.n1)
-                del Ks, Vs, S, P
+        # the library's own selected forward (one launch; its parity is tested against the oracle)
+        prob = sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size,
+                                    w.block_count, dtype=w.dtype, forward=True)
+        out, smax, ssum = sab.selected_forward(prob, x["query"], x["key"], x["value"], x["topk"])
+        torch.cuda.synchronize()
+        return out, smax, ssum
     smax = m[..., None].expand(T1, w.n1, 8).contiguous()
     ssum = l[..., None].expand(T1, w.n1, 8).contiguous()
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -428,7 +416,67 @@ def cpu_baseline(w: W.Workload, x, budget_s=12.0):
 
 # ----------------------------------------------------------------------------
 
+def measure_forward(wl: int, steps: int, warmup: int, prewarm_ms=300.0):
+    """The selected forward (attn_fwd_selected) on workload `wl`: its own record, with the two
+    GEMMs S and O = P V (2 (D_qk + D_v) flop per attended pair) as the algorithmic work."""
+    w = W.config(wl)
+    dev = torch.device("cuda", 0)
+    x = W.make_inputs(w, device=dev, backend="torch")
+    prob = sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size,
+                                w.block_count, dtype=w.dtype, forward=True)
+    ws = torch.empty(max(1, sab.attn_bwd_workspace_size(prob)), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.T1, w.n1, w.d_v), dtype=x["query"].dtype, device=dev)
+    smax = torch.empty((w.T1, w.n1, 8), dtype=torch.float32, device=dev)
+    ssum = torch.empty_like(smax)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sab.attn_fwd_selected(prob, x["query"], x["key"], x["value"], x["topk"], out, smax, ssum, ws, stream=stream)
+
+    torch.cuda.synchronize()
+    spent, t0 = 0.0, time.perf_counter()
+    while spent < prewarm_ms and time.perf_counter() - t0 < 60:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        spent += a.elapsed_time(b)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    sab.attn_bwd_profile_reset()
+    sab.attn_bwd_profiling(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    sab.attn_bwd_profiling(False)
+    ms = a.elapsed_time(b) / steps
+    kernels = sab.attn_bwd_profile_read()
+    fl = attended_pairs(w) * flops_per_pair(w, ("S", "O"))
+    tot_ms, n = kernels["selected_forward"]
+    kms = tot_ms / steps
+    # what the query-major design moves: the gathered key and value rows, per (token, KV head, key row)
+    gather = w.T1 * w.n2 * w.block_count * w.block_size * (w.d_qk + w.d_v) * (2 if w.dtype != "fp32" else 4)
+    rec = {"workload": w.name, "pass": "forward", "value": round(fl / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+           "ms_per_step": round(ms, 4), "steps": steps,
+           "pct_bf16_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "roofline": {"kernel": "selected_forward", "bound": "mfma", "avg_ms": tot_ms / max(n, 1),
+                        "achieved": fl / (kms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": fl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop_per_launch": fl,
+                        "traffic": recorded_counters("selected_forward", w.name).get("traffic_bytes_per_launch"),
+                        "gather_bytes_per_launch": gather, "gather_gbs": gather / (kms * 1e-3) / 1e9},
+           "prewarm_ms": round(spent, 1)}
+    del x, out, smax, ssum, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
 EXTRA_RUNS = ((2, False), (3, False), (4, False), (4, True))  # (workload, deterministic) beside the headline
+FORWARD_RUNS = (5, 3)  # selected forward measured on these workloads
 
 
 def main(argv=None):
@@ -513,6 +561,8 @@ def main(argv=None):
             extra.append(re_)
             del xe
             torch.cuda.empty_cache()
+        for wl in FORWARD_RUNS:
+            extra.append(measure_forward(wl, max(3, args.steps // 2), args.warmup, args.prewarm_ms))
         line["extra"] = extra
     print(json.dumps(line), flush=True)
     return 0

@@ -194,6 +194,22 @@ attn_status_t attn_fwd_selected(const attn_bwd_problem_t* p,
                                 void* workspace, uint64_t workspace_bytes,
                                 void* hip_stream);
 
+/* Diagnostic: build only the inverted index of a selected problem (the first stage of
+ * attn_bwd_selected) and copy it out, so that it can be checked entry by entry.
+ * Keys are (KV head, block) pairs numbered kvh * NB + (blocks of the earlier sequences) + id,
+ * NB = the total number of blocks over all sequences (S2_b / block_size summed).
+ *   offsets [N2 * NB + 1]   key k's list is lists[offsets[k] .. offsets[k + 1])
+ *   lists   [T1 * N2 * block_count]  entries t * block_count + slot, ascending within a key;
+ *                           only offsets[N2 * NB] of them are written (out-of-range ids are left
+ *                           out and raise the flag)
+ *   order   [N2 * NB]       the keys in the order the KV-major pass takes them (longest list
+ *                           first, ties by key; identity order above 8192 keys)
+ * All three are device buffers owned by the caller; `workspace` as for attn_bwd_selected.
+ * Asynchronous on `hip_stream`; p->op must be ATTN_OP_SELECTED. */
+attn_status_t attn_bwd_selected_index(const attn_bwd_problem_t* p, const int32_t* topk_indices,
+                                      int32_t* offsets, int32_t* lists, int32_t* order,
+                                      void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
 /* Read (synchronously, on `hip_stream`) the device flag that a selected call raises
  * when it meets a topk id outside [0, S2_b / block_size).  Writes 1 to *raised when
  * the flag is set, 0 otherwise.  `workspace` is the one passed to that call. */

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "AttnError", "Problem", "LIB_PATH", "lib",
     "attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_dense_varlen_noalloc", "attn_bwd_selected",
-    "attn_fwd_selected", "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version",
+    "attn_fwd_selected", "attn_bwd_selected_index", "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version",
     "attn_bwd_profiling", "attn_bwd_profile_reset", "attn_bwd_profile_read",
     "dense_backward", "selected_backward", "selected_forward", "EXPORTED_SYMBOLS",
 ]
@@ -37,7 +37,7 @@ ATTN_OP_DENSE, ATTN_OP_SELECTED, ATTN_OP_SELECTED_FWD = 0, 1, 2
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_BWD_NOALLOC_SCRATCH_BYTES
 
 EXPORTED_SYMBOLS = ("attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_dense_varlen_noalloc",
-                    "attn_bwd_selected", "attn_fwd_selected",
+                    "attn_bwd_selected", "attn_fwd_selected", "attn_bwd_selected_index",
                     "attn_bwd_check_index_flag", "attn_bwd_profiling", "attn_bwd_profile_reset",
                     "attn_bwd_profile_read", "attn_bwd_status_string", "attn_bwd_version")
 
@@ -73,6 +73,8 @@ def _load():
     L.attn_bwd_selected.restype = c_int32
     L.attn_fwd_selected.argtypes = [P] + [c_void_p] * 7 + [c_void_p, c_uint64, c_void_p]
     L.attn_fwd_selected.restype = c_int32
+    L.attn_bwd_selected_index.argtypes = [P] + [c_void_p] * 4 + [c_void_p, c_uint64, c_void_p]
+    L.attn_bwd_selected_index.restype = c_int32
     L.attn_bwd_check_index_flag.argtypes = [P, c_void_p, POINTER(c_int32), c_void_p]
     L.attn_bwd_check_index_flag.restype = c_int32
     L.attn_bwd_profiling.argtypes = [c_int32]
@@ -235,6 +237,14 @@ def selected_forward(problem, q, k, v, topk_indices, workspace=None, stream=None
     ws = workspace if workspace is not None else _workspace(problem, q.device)
     attn_fwd_selected(problem, q, k, v, topk_indices, out, smax, ssum, ws, stream=stream)
     return out, smax, ssum
+
+
+def attn_bwd_selected_index(problem, topk_indices, offsets, lists, order, workspace, workspace_bytes=None,
+                            stream=None):
+    wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = _L().attn_bwd_selected_index(problem.ref, _ptr(topk_indices), _ptr(offsets), _ptr(lists), _ptr(order),
+                                     _ptr(workspace), wb, _stream(stream))
+    _check(st, "attn_bwd_selected_index")
 
 
 def attn_bwd_check_index_flag(problem, workspace, stream=None) -> bool:

@@ -742,6 +742,45 @@ attn_status_t attn_fwd_selected(const attn_bwd_problem_t* p, const void* q, cons
                                                                                                     : ATTN_ERR_HIP;
 }
 
+attn_status_t attn_bwd_selected_index(const attn_bwd_problem_t* p, const int32_t* topk_indices, int32_t* offsets,
+                                      int32_t* lists, int32_t* order, void* workspace, uint64_t workspace_bytes,
+                                      void* hip_stream) {
+  Plan pl;
+  attn_status_t st = validate_and_plan(p, pl);
+  if (st != ATTN_OK) return st;
+  if (p->op != ATTN_OP_SELECTED) return ATTN_ERR_INVALID;
+  if (!offsets || !order || (pl.entries > 0 && (!topk_indices || !lists))) return ATTN_ERR_NULLPTR;
+  if (!workspace || workspace_bytes < pl.total || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return ATTN_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  TableStage tables;
+  if (tables.stage(pack_tables(p, pl)) != hipSuccess) return ATTN_ERR_HIP;
+  PreArgs pa{};  // no rows: the launch only copies the tables into the workspace
+  pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
+  pa.tab_n16 = tables.n16();
+  if (launch_preprocess(pa, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
+  SelArgs a{};
+  a.topk = topk_indices;
+  a.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
+  a.blkoff = at<const int32_t>(workspace, pl.off_tab1);
+  a.batch = pl.B; a.n2 = p->n2; a.cnt = p->block_count; a.nblk_total = pl.nblk_total; a.T1 = pl.T1;
+  a.counts = at<int32_t>(workspace, pl.off_counts);
+  a.offsets = at<int32_t>(workspace, pl.off_offsets);
+  a.cursor = at<int32_t>(workspace, pl.off_cursor);
+  a.list = at<int32_t>(workspace, pl.off_list);
+  a.sort_scratch = at<int32_t>(workspace, pl.off_scratch);
+  a.flag = at<int32_t>(workspace, pl.off_flag);
+  if (launch_selected_index(a, s) != hipSuccess) return ATTN_ERR_HIP;
+  const size_t nkeys = (size_t)p->n2 * pl.nblk_total;
+  if (hipMemcpyAsync(offsets, a.offsets, 4 * (nkeys + 1), hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(order, a.cursor, 4 * nkeys, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return ATTN_ERR_HIP;
+  if (pl.entries > 0 && hipMemcpyAsync(lists, a.list, 4 * (size_t)pl.entries, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
 attn_status_t attn_bwd_check_index_flag(const attn_bwd_problem_t* p, const void* workspace, int32_t* raised,
                                         void* hip_stream) {
   if (!raised || !workspace) return ATTN_ERR_NULLPTR;

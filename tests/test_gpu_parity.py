@@ -144,3 +144,34 @@ def test_selected_gradient_sums_on_gpu_outputs():
             assert np.abs(sk).max() <= 2e-2 * np.abs(dk[ks:ke, h]).sum(axis=0).max() + 1e-6
             want = dy[qs:qe, h * G:(h + 1) * G].sum(axis=(0, 1))
             np.testing.assert_allclose(dv[ks:ke, h].sum(axis=0), want, rtol=2e-2, atol=2e-2 * np.abs(want).max())
+
+
+def test_selected_out_of_range_id_raises_flag_and_spares_other_rows():
+    """An out-of-range id is skipped by every kernel (no contribution) and raises the flag that
+    attn_bwd_check_index_flag reads.  dQ rows of the other tokens are unaffected and match the
+    oracle (which is given a valid id in that slot: dQ of a token depends on its own ids only)."""
+    import sparse_attention_backward_amd as sab
+    w = W.small_selected(seqlens=(128, 64), seqlens_kv=(256, 192), block_size=64, block_count=2, n1=16, n2=2)
+    x = W.make_inputs(w)
+    bad = x["topk"].clone()
+    bad[7, 1, 0] = 4          # sequence 0 has 4 blocks
+    dev = torch.device("cuda", 0)
+    o, smax, ssum = oracle_forward(w, x)
+    prob = sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size, w.block_count)
+    ws = torch.empty(sab.attn_bwd_workspace_size(prob), dtype=torch.uint8, device=dev)
+    g = lambda t: t.to(dev).contiguous()  # noqa: E731
+    dq, dk, dv = sab.selected_backward(prob, g(x["query"]), g(x["key"]), g(x["value"]), g(o), g(x["dy"]), g(smax),
+                                       g(ssum), g(bad), workspace=ws)
+    torch.cuda.synchronize()
+    assert sab.attn_bwd_check_index_flag(prob, ws)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    ref = oracle_backward(w, x)
+    keep = np.ones(w.T1, dtype=bool)
+    keep[7] = False
+    assert_close("other tokens' dq", f64(dq)[keep], ref["dq"][keep], "bf16")
+    # a clean call on the same workspace clears the flag
+    sab.selected_backward(prob, g(x["query"]), g(x["key"]), g(x["value"]), g(o), g(x["dy"]), g(smax), g(ssum),
+                          g(x["topk"]), workspace=ws)
+    torch.cuda.synchronize()
+    assert not sab.attn_bwd_check_index_flag(prob, ws)
