@@ -75,15 +75,23 @@ typedef enum {
 
 typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1, ATTN_FP32 = 2 } attn_dtype_t;
 typedef enum { ATTN_OP_DENSE = 0, ATTN_OP_SELECTED = 1, ATTN_OP_SELECTED_FWD = 2 } attn_op_t;
+typedef enum { ATTN_LAYOUT_TND = 0, ATTN_LAYOUT_BSND = 1 } attn_layout_t;
 
 typedef struct {
   int32_t op;                     /* attn_op_t                                              */
   int32_t dtype;                  /* dense: ATTN_BF16 or ATTN_FP32; selected (backward and
                                      forward): ATTN_BF16 or ATTN_FP16                         */
   int32_t batch;                  /* B >= 1                                                 */
-  const int64_t* cu_seqlens_q;    /* HOST [B+1]: 0, then running sums of query lengths;
+  int32_t layout;                 /* attn_layout_t.  TND: sequences of their own lengths,
+                                     given by cu_seqlens_q / cu_seqlens_kv.  BSND (selected
+                                     backward and forward only; the dense page takes TND):
+                                     [B, S, N, D] with every sequence seq_len_q queries and
+                                     seq_len_kv keys long -- the same memory as TND with equal
+                                     lengths; the cu_seqlens pointers must be NULL.          */
+  const int64_t* cu_seqlens_q;    /* TND: HOST [B+1]: 0, then running sums of query lengths;
                                      a length may be 0 (dense constraints allow S = 0)     */
-  const int64_t* cu_seqlens_kv;   /* HOST [B+1]: same for key/value lengths                */
+  const int64_t* cu_seqlens_kv;   /* TND: HOST [B+1]: same for key/value lengths           */
+  int64_t seq_len_q, seq_len_kv;  /* BSND: S of query and of key / value (0 for TND)        */
   int32_t n1, n2;                 /* query / KV heads, n1 % n2 == 0                         */
   int32_t d_qk;                   /* head dim of query / key (the non-rope part)            */
   int32_t d_rope;                 /* dense: head dim of queryRope / keyRope (0 = none);

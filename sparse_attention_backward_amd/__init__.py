@@ -33,6 +33,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnbwd.
 ATTN_OK, ATTN_ERR_NULLPTR, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
 ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
 ATTN_OP_DENSE, ATTN_OP_SELECTED, ATTN_OP_SELECTED_FWD = 0, 1, 2
+ATTN_LAYOUT_TND, ATTN_LAYOUT_BSND = 0, 1
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_BWD_NOALLOC_SCRATCH_BYTES
 
@@ -44,8 +45,9 @@ EXPORTED_SYMBOLS = ("attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bw
 
 class attn_bwd_problem_t(ctypes.Structure):
     _fields_ = [
-        ("op", c_int32), ("dtype", c_int32), ("batch", c_int32),
+        ("op", c_int32), ("dtype", c_int32), ("batch", c_int32), ("layout", c_int32),
         ("cu_seqlens_q", POINTER(c_int64)), ("cu_seqlens_kv", POINTER(c_int64)),
+        ("seq_len_q", c_int64), ("seq_len_kv", c_int64),
         ("n1", c_int32), ("n2", c_int32),
         ("d_qk", c_int32), ("d_rope", c_int32), ("d_v", c_int32),
         ("scale", c_double), ("causal", c_int32),
@@ -123,15 +125,22 @@ class Problem:
 
     def __init__(self, op, dtype, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, d_rope=0, causal=False,
                  block_size=0, block_count=0, deterministic=False, dkdv_atomic=False, dense_dq_mode=0,
-                 window_tokens=0):
+                 window_tokens=0, bsnd=None):
+        """bsnd = (B, S1, S2): the BSND layout (cu_q / cu_kv are then ignored and passed as NULL)."""
+        if bsnd is not None:
+            B, S1, S2 = (int(v) for v in bsnd)
+            cu_q = [b * S1 for b in range(B + 1)]
+            cu_kv = [b * S2 for b in range(B + 1)]
         cu_q = [int(x) for x in cu_q]
         cu_kv = [int(x) for x in cu_kv]
         self.cu_q_arr = (c_int64 * len(cu_q))(*cu_q)
         self.cu_kv_arr = (c_int64 * len(cu_kv))(*cu_kv)
+        null = ctypes.cast(None, POINTER(c_int64))
         self.s = attn_bwd_problem_t(
-            op=op, dtype=dtype, batch=len(cu_q) - 1,
-            cu_seqlens_q=ctypes.cast(self.cu_q_arr, POINTER(c_int64)),
-            cu_seqlens_kv=ctypes.cast(self.cu_kv_arr, POINTER(c_int64)),
+            op=op, dtype=dtype, batch=len(cu_q) - 1, layout=ATTN_LAYOUT_BSND if bsnd else ATTN_LAYOUT_TND,
+            cu_seqlens_q=null if bsnd else ctypes.cast(self.cu_q_arr, POINTER(c_int64)),
+            cu_seqlens_kv=null if bsnd else ctypes.cast(self.cu_kv_arr, POINTER(c_int64)),
+            seq_len_q=bsnd[1] if bsnd else 0, seq_len_kv=bsnd[2] if bsnd else 0,
             n1=n1, n2=n2, d_qk=d_qk, d_rope=d_rope, d_v=d_v, scale=float(scale), causal=int(bool(causal)),
             block_size=block_size, block_count=block_count,
             deterministic=int(bool(deterministic)), dkdv_atomic=int(bool(dkdv_atomic)),
@@ -148,13 +157,14 @@ class Problem:
 
     @classmethod
     def selected(cls, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, block_size, block_count, deterministic=False,
-                 dkdv_atomic=False, dtype="bf16", window_tokens=0, forward=False):
+                 dkdv_atomic=False, dtype="bf16", window_tokens=0, forward=False, bsnd=None):
         """window_tokens: query tokens per window (field sel_window_tokens; 0 automatic).
-        forward: the problem of attn_fwd_selected (op ATTN_OP_SELECTED_FWD)."""
+        forward: the problem of attn_fwd_selected (op ATTN_OP_SELECTED_FWD).
+        bsnd = (B, S1, S2): BSND layout instead of TND (cu_q / cu_kv ignored)."""
         return cls(ATTN_OP_SELECTED_FWD if forward else ATTN_OP_SELECTED,
                    {"bf16": ATTN_BF16, "fp32": ATTN_FP32, "fp16": ATTN_FP16}[dtype], cu_q,
                    cu_kv, n1, n2, d_qk, d_v, scale, block_size=block_size, block_count=block_count,
-                   deterministic=deterministic, dkdv_atomic=dkdv_atomic, window_tokens=window_tokens)
+                   deterministic=deterministic, dkdv_atomic=dkdv_atomic, window_tokens=window_tokens, bsnd=bsnd)
 
     @property
     def ref(self):

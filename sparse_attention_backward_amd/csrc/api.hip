@@ -31,6 +31,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
   int B = 0, G = 0;
   int64_t T1 = 0, T2 = 0;
+  std::vector<int64_t> cuq, cukv;  // sequence offsets: the caller's (TND) or derived (BSND)
   // dense schedule
   std::vector<int32_t> kv_tiles, kv_split, q_tiles;
   std::vector<int64_t> ds_base;
@@ -75,8 +76,8 @@ constexpr uint64_t kSelShareMax = 64ull << 30;
 //  * ds_base: (query tile, 64-key tile) blocks before each sequence (stored-dS layout).
 void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
   const int B = pl.B;
-  const int64_t* cq = p->cu_seqlens_q;
-  const int64_t* ck = p->cu_seqlens_kv;
+  const int64_t* cq = pl.cuq.data();
+  const int64_t* ck = pl.cukv.data();
   struct W { int64_t work; int32_t b, tile, kvh, qa, qb, slot, part, group; };
   struct T { int32_t b, tile, kvh, qlo, qhi; };
   std::vector<T> tiles;
@@ -168,10 +169,31 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   if (!p) return ATTN_ERR_NULLPTR;
   if (p->op != ATTN_OP_DENSE && p->op != ATTN_OP_SELECTED && p->op != ATTN_OP_SELECTED_FWD) return ATTN_ERR_INVALID;
   if (p->batch < 1) return ATTN_ERR_INVALID;
-  if (!p->cu_seqlens_q || !p->cu_seqlens_kv) return ATTN_ERR_NULLPTR;
   const int B = p->batch;
-  const int64_t* cq = p->cu_seqlens_q;
-  const int64_t* ck = p->cu_seqlens_kv;
+  if (p->layout == ATTN_LAYOUT_TND) {
+    if (!p->cu_seqlens_q || !p->cu_seqlens_kv) return ATTN_ERR_NULLPTR;
+    if (p->seq_len_q != 0 || p->seq_len_kv != 0) return ATTN_ERR_INVALID;
+    pl.cuq.assign(p->cu_seqlens_q, p->cu_seqlens_q + B + 1);
+    pl.cukv.assign(p->cu_seqlens_kv, p->cu_seqlens_kv + B + 1);
+  } else if (p->layout == ATTN_LAYOUT_BSND) {
+    // [B, S, N, D]: every sequence has seq_len_q queries and seq_len_kv keys, back to back --
+    // the TND layout with equal lengths (layouts of the selected and indexer pages)
+    if (p->op == ATTN_OP_DENSE) return ATTN_ERR_INVALID;  // the dense page takes TND only
+    if (p->cu_seqlens_q || p->cu_seqlens_kv) return ATTN_ERR_INVALID;
+    if (p->seq_len_q < 0 || p->seq_len_kv < 0 || p->seq_len_q > (int64_t(1) << 40) / B ||
+        p->seq_len_kv > (int64_t(1) << 40) / B)
+      return ATTN_ERR_INVALID;
+    pl.cuq.resize(B + 1);
+    pl.cukv.resize(B + 1);
+    for (int b = 0; b <= B; ++b) {
+      pl.cuq[b] = (int64_t)b * p->seq_len_q;
+      pl.cukv[b] = (int64_t)b * p->seq_len_kv;
+    }
+  } else {
+    return ATTN_ERR_INVALID;
+  }
+  const int64_t* cq = pl.cuq.data();
+  const int64_t* ck = pl.cukv.data();
   if (cq[0] != 0 || ck[0] != 0) return ATTN_ERR_INVALID;
   for (int b = 0; b < B; ++b)
     if (cq[b + 1] < cq[b] || ck[b + 1] < ck[b]) return ATTN_ERR_INVALID;
@@ -379,8 +401,8 @@ class TableStage {
 
 std::vector<uint8_t> pack_tables(const attn_bwd_problem_t* p, const Plan& pl) {
   std::vector<uint8_t> t(pl.table_bytes, 0);
-  std::memcpy(t.data() + pl.off_cu_q, p->cu_seqlens_q, 8 * (size_t)(pl.B + 1));
-  std::memcpy(t.data() + pl.off_cu_kv, p->cu_seqlens_kv, 8 * (size_t)(pl.B + 1));
+  std::memcpy(t.data() + pl.off_cu_q, pl.cuq.data(), 8 * (size_t)(pl.B + 1));
+  std::memcpy(t.data() + pl.off_cu_kv, pl.cukv.data(), 8 * (size_t)(pl.B + 1));
   if (p->op == ATTN_OP_DENSE) {
     if (!pl.kv_tiles.empty()) std::memcpy(t.data() + pl.off_tab1, pl.kv_tiles.data(), 4 * pl.kv_tiles.size());
     if (!pl.kv_split.empty()) std::memcpy(t.data() + pl.off_kvsplit, pl.kv_split.data(), 4 * pl.kv_split.size());

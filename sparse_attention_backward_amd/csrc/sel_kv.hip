@@ -209,11 +209,8 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   // permutation: 4-feature piece qq of tile f starts at feature F0(f) + 8 qq + 4 (f % 2),
   // i.e. chunk group F0(f) / 32 of the K tile (RowTile::colK) plus 8 (f % 2) bytes.
   const int fh = w & 1;
-  // The two K-tile bases stay opaque to the optimizer: with their values visible, the
-  // 128-key kernel's dQ shares came out wrong (deterministically, depending on code
-  // generation only; the cause is not pinned down and the parity tests cover both widths).
-  const uint32_t kcm = opaque(smem_lds + OKM + TM::colK(lane, 0));
-  const uint32_t kcr = opaque(smem_lds + OKR + TR::colK(lane, 0));
+  const uint32_t kcm = smem_lds + OKM + TM::colK(lane, 0);
+  const uint32_t kcr = smem_lds + OKR + TR::colK(lane, 0);
   int dscol[2], rmod[2];  // column reads of the dS^T tile; head of dQ-product rows 32 qh + 16 rr + l16
   {
     const int jj = l16 >> 2, qq = l16 & 3;

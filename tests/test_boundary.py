@@ -265,3 +265,30 @@ def test_selected_forward_validation():
     assert L.attn_fwd_selected(fw.ref, *args, FAKE, n - 1, None) == WORKSPACE
     a = list(args); a[4] = FAKE + 4  # misaligned out
     assert L.attn_fwd_selected(fw.ref, *a, FAKE, n, None) == INVALID
+
+
+def test_bsnd_layout_is_tnd_with_equal_lengths():
+    """BSND ([B, S, N, D], the non-TND layout of the selected page): the same workspace as
+    the TND problem with B sequences of S queries and S2 keys; TND only for the dense form."""
+    B, S1, S2 = 3, 192, 256
+    cu_q, cu_kv = [b * S1 for b in range(B + 1)], [b * S2 for b in range(B + 1)]
+    tnd = selected(cu_q=cu_q, cu_kv=cu_kv)
+    bsnd = selected(cu_q=[0], cu_kv=[0], bsnd=(B, S1, S2))
+    assert status_ws(bsnd) == status_ws(tnd)
+    fw = selected(cu_q=[0], cu_kv=[0], bsnd=(B, S1, S2), forward=True)
+    assert status_ws(fw)[0] == OK
+    d = dense()
+    d.s.layout = sab.ATTN_LAYOUT_BSND
+    d.s.cu_seqlens_q = ctypes.cast(None, ctypes.POINTER(ctypes.c_int64))
+    d.s.cu_seqlens_kv = ctypes.cast(None, ctypes.POINTER(ctypes.c_int64))
+    d.s.seq_len_q = d.s.seq_len_kv = 64
+    assert status_ws(d)[0] == INVALID
+    bad = selected(cu_q=[0], cu_kv=[0], bsnd=(B, S1, S2))
+    bad.s.cu_seqlens_q = tnd.s.cu_seqlens_q        # BSND takes no sequence offsets
+    assert status_ws(bad)[0] == INVALID
+    t2 = selected(cu_q=cu_q, cu_kv=cu_kv)
+    t2.s.seq_len_q = 5                             # TND takes no BSND lengths
+    assert status_ws(t2)[0] == INVALID
+    t3 = selected(cu_q=cu_q, cu_kv=cu_kv)
+    t3.s.layout = 7
+    assert status_ws(t3)[0] == INVALID

@@ -109,3 +109,28 @@ def test_selected_forward_out_of_range_id_raises_flag():
                                     w.cu_q, w.cu_kv, w.n1, w.n2, w.scale, w.block_size, tokens=t5)
     assert_close("out-of-range row", f64(out[5]), o1[5], "bf16")
     _check_stats("out-of-range row", smax[5:6], ssum[5:6], m1[5:6], l1[5:6])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_selected_bsnd_layout_matches_tnd(dtype):
+    """BSND inputs are TND inputs with equal lengths: forward and backward give the same bits."""
+    B, S1, S2 = 3, 96, 256
+    w = W.small_selected(seqlens=(S1,) * B, seqlens_kv=(S2,) * B, block_size=32, block_count=3, n1=16, n2=2,
+                         dtype=dtype)
+    x = W.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    g = lambda t: t.to(dev).contiguous()  # noqa: E731
+    res = []
+    for bsnd in (None, (B, S1, S2)):
+        fw = sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size, w.block_count,
+                                  dtype=dtype, forward=True, bsnd=bsnd)
+        out, smax, ssum = sab.selected_forward(fw, g(x["query"]), g(x["key"]), g(x["value"]), g(x["topk"]))
+        bw = sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size, w.block_count,
+                                  dtype=dtype, bsnd=bsnd)
+        grads = sab.selected_backward(bw, g(x["query"]), g(x["key"]), g(x["value"]), out, g(x["dy"]), smax, ssum,
+                                      g(x["topk"]))
+        torch.cuda.synchronize()
+        res.append((out, smax, ssum) + tuple(grads))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+    check_against_oracle(w, dict(zip(("dq", "dk", "dv"), res[1][3:])), oracle_backward(w, x))
