@@ -30,6 +30,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
   repeated column (literal Gather); gradients from both copies add up.
 * Causal: key j of a sequence is visible to query i of the same sequence when
   j <= i (local positions); it requires equal query and KV lengths.
+* The other masks (causal with unequal lengths, windows of preTokens / nextTokens):
+  BandMask below; its alignment and window are the reading of sparse modes whose
+  definitions the dense page only links to.
 * A query row with no visible key produces O = 0 and zero gradients.
 
 The backward recomputes P from the scores (it does not consume the passed
@@ -42,7 +45,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "forward_dense", "backward_dense", "backward_dense_from_stats",
+    "BandMask", "forward_dense", "backward_dense", "backward_dense_from_stats",
     "forward_selected", "backward_selected", "backward_selected_from_stats",
     "selected_key_rows", "stats_tensor",
 ]
@@ -71,9 +74,32 @@ def stats_tensor(m, l):
 # Dense varlen form
 # ----------------------------------------------------------------------------
 
+class BandMask:
+    """A mask on the relative position of key and query (the dense page names sparse modes
+    with preTokens / nextTokens and causal variants, but their definitions are not on the
+    pages; this is the reading taken).  Key j (position in its sequence) is visible to query i
+    when  i + off - pre <= j <= i + off + next,  where off = 0 aligns the first query with the
+    first key ("top_left") and off = S2 - S1 aligns the last query with the last key
+    ("bottom_right").  pre = inf, next = 0 is causal attention under that alignment."""
+
+    def __init__(self, pre, next, align="top_left"):
+        if align not in ("top_left", "bottom_right"):
+            raise ValueError(align)
+        self.pre, self.next, self.align = pre, next, align
+
+    def visible(self, qpos, n_q, n_k):
+        off = 0 if self.align == "top_left" else n_k - n_q
+        i = np.asarray(qpos, dtype=np.float64)[:, None]
+        j = np.arange(n_k, dtype=np.float64)[None, :]
+        return (j >= i + off - self.pre) & (j <= i + off + self.next)
+
+
 def _causal_mask(qpos, n_q, n_k, causal):
     """Visible[i, j]: the query at local position qpos[i] (of a sequence with n_q
-    queries) sees key position j of the same sequence."""
+    queries) sees key position j of the same sequence.  causal: False, True (key j
+    visible iff j <= i; equal lengths), or a BandMask."""
+    if isinstance(causal, BandMask):
+        return causal.visible(qpos, n_q, n_k)
     vis = np.ones((len(qpos), n_k), dtype=bool)
     if causal:
         if n_q != n_k:

@@ -456,3 +456,97 @@ def test_inert_rows_contribute_nothing_selected():
     want = O.backward_selected(c["q"], c["k"], c["v"], c["dy"], *args, tokens=toks)
     for g, wv in zip(got, want):
         np.testing.assert_allclose(g, wv, rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# band / alignment masks (BandMask): causal with unequal lengths, preTokens / nextTokens
+# ----------------------------------------------------------------------------
+
+INF = float("inf")
+BANDS = [
+    ("causal-bottom-right, S1 < S2", (4, 3), (7, 5), OA.BandMask(INF, 0, "bottom_right")),
+    ("causal-bottom-right, S1 > S2 (rows with no key)", (6, 2), (3, 2), OA.BandMask(INF, 0, "bottom_right")),
+    ("causal-top-left, S1 < S2", (4, 3), (7, 5), OA.BandMask(INF, 0, "top_left")),
+    ("band pre 2 next 1, bottom-right", (5, 4), (6, 4), OA.BandMask(2, 1, "bottom_right")),
+    ("band pre 0 next 3, top-left", (5,), (5,), OA.BandMask(0, 3, "top_left")),
+]
+
+
+@pytest.mark.parametrize("name,lq,lk,mask", BANDS, ids=[b[0] for b in BANDS])
+def test_band_mask_backward_matches_finite_differences(name, lq, lk, mask):
+    rng = np.random.default_rng(21)
+    n1, n2, dr = 4, 2, 2
+    c = _dense_case(rng, lq, lk, n1, n2, 5, dr, 4)
+    cq, ck, scale = cu(lq), cu(lk), 0.43
+
+    def loss():
+        o, _, _ = O.forward_dense(c["q"], c["k"], c["v"], cq, ck, n1, n2, scale, mask, c["qr"], c["kr"])
+        return float((c["dy"] * o).sum())
+
+    dq, dqr, dk, dkr, dv = O.backward_dense(c["q"], c["k"], c["v"], c["dy"], cq, ck, n1, n2, scale, mask,
+                                            c["qr"], c["kr"])
+    assert_fd(dq, fd_grad(loss, c["q"]))
+    assert_fd(dk, fd_grad(loss, c["k"]))
+    assert_fd(dv, fd_grad(loss, c["v"]))
+    assert_fd(dkr, fd_grad(loss, c["kr"]))
+
+
+def _torch_band_loss(q, k, v, dy, lq, lk, n1, n2, scale, lo_rel, hi_rel, bottom_right):
+    """Naive attention with the mask built by torch.tril / triu diagonals (independent of BandMask):
+    visible iff lo <= j - i <= hi with lo, hi shifted by S2 - S1 when aligned bottom-right."""
+    G = n1 // n2
+    total = q.new_zeros(())
+    cq, ck = cu(lq), cu(lk)
+    for b in range(len(lq)):
+        s1, s2 = lq[b], lk[b]
+        off = s2 - s1 if bottom_right else 0
+        keep = torch.ones(s1, s2, dtype=torch.bool).tril(off + hi_rel) & torch.ones(s1, s2, dtype=torch.bool).triu(
+            off + lo_rel)
+        Qb = q[cq[b]:cq[b + 1]].transpose(0, 1)
+        Kb = k[ck[b]:ck[b + 1]].transpose(0, 1).repeat_interleave(G, 0)
+        Vb = v[ck[b]:ck[b + 1]].transpose(0, 1).repeat_interleave(G, 0)
+        S = torch.matmul(Qb, Kb.transpose(1, 2).contiguous()) * scale
+        S = S.masked_fill(~keep, float("-inf"))
+        P = torch.softmax(S, -1).nan_to_num(0.0)   # a row with no visible key: P = 0
+        total = total + (dy[cq[b]:cq[b + 1]] * torch.matmul(P, Vb).transpose(0, 1)).sum()
+    return total
+
+
+@pytest.mark.parametrize("lo_rel,hi_rel,bottom_right,lq,lk", [
+    (-1000, 0, True, (9, 5), (13, 5)),
+    (-1000, 0, True, (8,), (5,)),
+    (-3, 2, True, (7, 6), (9, 6)),
+    (-2, 4, False, (7,), (10,)),
+])
+def test_band_mask_matches_torch_autograd(lo_rel, hi_rel, bottom_right, lq, lk):
+    rng = np.random.default_rng(22)
+    n1, n2, scale = 4, 2, 0.31
+    c = _dense_case(rng, lq, lk, n1, n2, 8, 0, 6)
+    ts = {k: torch.tensor(v, requires_grad=True) for k, v in c.items()}
+    _torch_band_loss(ts["q"], ts["k"], ts["v"], ts["dy"], lq, lk, n1, n2, scale, lo_rel, hi_rel,
+                     bottom_right).backward()
+    mask = OA.BandMask(-lo_rel, hi_rel, "bottom_right" if bottom_right else "top_left")
+    dq, _, dk, _, dv = O.backward_dense(c["q"], c["k"], c["v"], c["dy"], cu(lq), cu(lk), n1, n2, scale, mask)
+    for mine, name in zip((dq, dk, dv), ("q", "k", "v")):
+        np.testing.assert_allclose(mine, ts[name].grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_band_mask_special_cases():
+    """Equal lengths: both alignments of causal are the causal mask; a window wider than the
+    sequences is no mask; a bottom-right causal row before the first key has no key at all."""
+    rng = np.random.default_rng(23)
+    lq = (6, 4)
+    c = _dense_case(rng, lq, lq, 2, 1, 4, 0, 3)
+    ref = O.forward_dense(c["q"], c["k"], c["v"], cu(lq), cu(lq), 2, 1, 0.5, True)
+    for align in ("top_left", "bottom_right"):
+        got = O.forward_dense(c["q"], c["k"], c["v"], cu(lq), cu(lq), 2, 1, 0.5, OA.BandMask(INF, 0, align))
+        for a, b in zip(got, ref):
+            np.testing.assert_array_equal(a, b)
+    full = O.forward_dense(c["q"], c["k"], c["v"], cu(lq), cu(lq), 2, 1, 0.5, False)
+    wide = O.forward_dense(c["q"], c["k"], c["v"], cu(lq), cu(lq), 2, 1, 0.5, OA.BandMask(100, 100))
+    for a, b in zip(wide, full):
+        np.testing.assert_array_equal(a, b)
+    o, m, l = O.forward_dense(c["q"][:6], c["k"][:4], c["v"][:4], cu((6,)), cu((4,)), 2, 1, 0.5,
+                              OA.BandMask(INF, 0, "bottom_right"))
+    assert (o[:2] == 0).all() and np.isneginf(m[:2]).all() and (l[:2] == 0).all()   # rows 0, 1: no key
+    assert (l[2:] > 0).all()
