@@ -98,8 +98,19 @@ typedef struct {
                                      selected: must be 0                                    */
   int32_t d_v;                    /* head dim of value / out / dy                           */
   double scale;                   /* scaleValue: the factor written 1/sqrt(d) on the pages  */
-  int32_t causal;                 /* dense: 1 = key j visible to query i iff j <= i within
-                                     the sequence (needs equal q / kv lengths); selected: 0 */
+  int32_t causal;                 /* dense: 1 = key j visible to query i iff j <= i + off
+                                     (positions within the sequence; off from mask_align);
+                                     selected: 0                                            */
+  int32_t mask_align;             /* dense, causal or band: 0 = off 0 (first query aligned with
+                                     the first key), 1 = off S2_b - S1_b (last query aligned
+                                     with the last key); the same when the lengths are equal */
+  int32_t band;                   /* dense: 1 = window mask: key j visible to query i iff
+                                     i + off - pre_tokens <= j <= i + off + next_tokens
+                                     (excludes causal).  The dense page names sparse modes with
+                                     preTokens / nextTokens; their definitions are not on it,
+                                     this is the reading taken.  Rows that see no key get
+                                     zero gradients.                                         */
+  int64_t pre_tokens, next_tokens;/* band only (0 otherwise); |value| <= 2^30, pre + next >= 0 */
   int32_t block_size;             /* selected: selectedBlockSize (<= 128, multiple of 16)  */
   int32_t block_count;            /* selected: selectedBlockCount (1..128, count*size < 8192)*/
   int32_t deterministic;          /* 1 = bitwise reproducible                               */

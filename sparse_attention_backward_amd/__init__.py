@@ -50,7 +50,8 @@ class attn_bwd_problem_t(ctypes.Structure):
         ("seq_len_q", c_int64), ("seq_len_kv", c_int64),
         ("n1", c_int32), ("n2", c_int32),
         ("d_qk", c_int32), ("d_rope", c_int32), ("d_v", c_int32),
-        ("scale", c_double), ("causal", c_int32),
+        ("scale", c_double), ("causal", c_int32), ("mask_align", c_int32), ("band", c_int32),
+        ("pre_tokens", c_int64), ("next_tokens", c_int64),
         ("block_size", c_int32), ("block_count", c_int32),
         ("deterministic", c_int32), ("dkdv_atomic", c_int32), ("dense_dq_mode", c_int32),
         ("sel_window_tokens", c_int32),
@@ -125,7 +126,7 @@ class Problem:
 
     def __init__(self, op, dtype, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, d_rope=0, causal=False,
                  block_size=0, block_count=0, deterministic=False, dkdv_atomic=False, dense_dq_mode=0,
-                 window_tokens=0, bsnd=None):
+                 window_tokens=0, bsnd=None, mask_align=0, band=None):
         """bsnd = (B, S1, S2): the BSND layout (cu_q / cu_kv are then ignored and passed as NULL)."""
         if bsnd is not None:
             B, S1, S2 = (int(v) for v in bsnd)
@@ -142,6 +143,8 @@ class Problem:
             cu_seqlens_kv=null if bsnd else ctypes.cast(self.cu_kv_arr, POINTER(c_int64)),
             seq_len_q=bsnd[1] if bsnd else 0, seq_len_kv=bsnd[2] if bsnd else 0,
             n1=n1, n2=n2, d_qk=d_qk, d_rope=d_rope, d_v=d_v, scale=float(scale), causal=int(bool(causal)),
+            mask_align=int(mask_align), band=int(band is not None),
+            pre_tokens=int(band[0]) if band is not None else 0, next_tokens=int(band[1]) if band is not None else 0,
             block_size=block_size, block_count=block_count,
             deterministic=int(bool(deterministic)), dkdv_atomic=int(bool(dkdv_atomic)),
             dense_dq_mode=int(dense_dq_mode), sel_window_tokens=int(window_tokens))
@@ -149,11 +152,12 @@ class Problem:
 
     @classmethod
     def dense(cls, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, causal=False, d_rope=0, dtype="bf16",
-              deterministic=False, dq_mode=0):
-        """dq_mode: 0 automatic, 1 stored dS, 2 recompute (field dense_dq_mode of the C struct)."""
+              deterministic=False, dq_mode=0, align=0, band=None):
+        """dq_mode: 0 automatic, 1 stored dS, 2 recompute (field dense_dq_mode of the C struct).
+        align: 0 top-left, 1 bottom-right (field mask_align); band = (pre_tokens, next_tokens)."""
         return cls(ATTN_OP_DENSE, {"bf16": ATTN_BF16, "fp32": ATTN_FP32, "fp16": ATTN_FP16}[dtype], cu_q, cu_kv,
                    n1, n2, d_qk, d_v, scale, d_rope=d_rope, causal=causal, deterministic=deterministic,
-                   dense_dq_mode=dq_mode)
+                   dense_dq_mode=dq_mode, mask_align=align, band=band)
 
     @classmethod
     def selected(cls, cu_q, cu_kv, n1, n2, d_qk, d_v, scale, block_size, block_count, deterministic=False,

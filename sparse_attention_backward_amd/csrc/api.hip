@@ -34,7 +34,10 @@ struct Plan {
   std::vector<int64_t> cuq, cukv;  // sequence offsets: the caller's (TND) or derived (BSND)
   // dense schedule
   std::vector<int32_t> kv_tiles, kv_split, q_tiles;
-  std::vector<int64_t> ds_base;
+  std::vector<int32_t> qt_base, qt_kr;  // query tiles before each sequence; key-tile range of each
+  std::vector<int64_t> qt_blk;          // first stored dS block of each query tile
+  int64_t ds_blocks = 0;
+  int lo_rel = -kBandInf, hi_rel = kBandInf;  // dense mask (dense_band); +-kBandInf: unbounded
   int kv_slots = 0;       // fp32 partial slots of split key tiles
   bool dense_ds = false;  // dQ from stored dS tiles (else recomputed)
   // selected
@@ -48,7 +51,7 @@ struct Plan {
   size_t off_lse2 = 0, off_ndrow = 0;
   size_t off_counts = 0, off_offsets = 0, off_cursor = 0, off_list = 0, off_scratch = 0, off_flag = 0;
   size_t off_dq_part = 0, off_wofs = 0, off_kvacc = 0;
-  size_t off_ds_base = 0, off_ds = 0, off_kvsplit = 0, off_kvpart = 0;
+  size_t off_qt_base = 0, off_qt_blk = 0, off_qt_kr = 0, off_ds = 0, off_kvsplit = 0, off_kvpart = 0;
   size_t total = 0;
 };
 
@@ -83,19 +86,36 @@ void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
   std::vector<T> tiles;
   std::vector<W> qv;
   int64_t total = 0;
-  pl.ds_base.assign(B + 1, 0);
+  pl.qt_base.assign(B + 1, 0);
+  pl.qt_blk.clear();
+  pl.qt_kr.clear();
+  pl.ds_blocks = 0;
   for (int b = 0; b < B; ++b) {
     const int64_t S1 = cq[b + 1] - cq[b], S2 = ck[b + 1] - ck[b];
-    const int64_t nqt = (S1 + kDenseTile - 1) / kDenseTile, nkt = (S2 + kDenseTile - 1) / kDenseTile;
+    const int64_t nqt = (S1 + kDenseTile - 1) / kDenseTile;
     const int64_t nkt2 = (S2 + kDenseKeyTile - 1) / kDenseKeyTile;
-    pl.ds_base[b + 1] = pl.ds_base[b] + (p->causal ? nqt * (nqt + 1) / 2 : nqt * nkt);
+    int lo, hi;
+    dense_band(pl.lo_rel, pl.hi_rel, p->mask_align, S1, S2, lo, hi);
+    pl.qt_base[b + 1] = pl.qt_base[b] + (int32_t)nqt;
+    // per query tile: the 64-key tiles with a visible key, and their stored dS blocks
+    for (int64_t t = 0; t < nqt; ++t) {
+      int klo, khi;
+      dense_key_tiles(lo, hi, kDenseTile * t, std::min<int64_t>(kDenseTile * (t + 1), S1), S2, kDenseTile, klo, khi);
+      pl.qt_blk.push_back(pl.ds_blocks);
+      pl.qt_kr.push_back(klo);
+      pl.qt_kr.push_back(khi);
+      pl.ds_blocks += khi - klo;
+      qv.push_back({khi - klo, b, (int32_t)t, 0, 0, 0, 0, 0, 0});
+    }
+    // per 128-key tile and KV head: the query tiles with a row that sees one of its keys
     for (int h = 0; h < p->n2; ++h)
       for (int64_t t = 0; t < nkt2; ++t) {
-        const int64_t qlo = p->causal ? std::min<int64_t>(2 * t, nqt) : 0;
-        tiles.push_back({b, (int32_t)t, h, (int32_t)qlo, (int32_t)nqt});
-        total += (nqt - qlo) * pl.G;
+        int qlo, qhi;
+        dense_row_tiles(lo, hi, kDenseKeyTile * t, std::min<int64_t>(kDenseKeyTile * (t + 1), S2), S1, kDenseTile, qlo,
+                        qhi);
+        tiles.push_back({b, (int32_t)t, h, (int32_t)qlo, (int32_t)qhi});
+        total += (int64_t)(qhi - qlo) * pl.G;
       }
-    for (int64_t t = 0; t < nqt; ++t) qv.push_back({p->causal ? std::min(t + 1, nkt) : nkt, b, (int32_t)t, 0, 0, 0, 0, 0, 0});
   }
   // Split size in query tiles: about 4/5 of a CU's share of all steps (a steady-state sweep of
   // 1/2 .. 2 shares on the dense workload: longer ranges stretch the KV-major tail, shorter ones
@@ -160,7 +180,7 @@ void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
     }
   std::stable_sort(qv.begin(), qv.end(), [](const W& x, const W& y) { return x.work > y.work; });
   for (auto& x : qv) { pl.q_tiles.push_back(x.b); pl.q_tiles.push_back(x.tile); }
-  const uint64_t ds_bytes = (uint64_t)pl.ds_base[B] * p->n1 * kDenseTile * kDenseTile * 2;
+  const uint64_t ds_bytes = (uint64_t)pl.ds_blocks * p->n1 * kDenseTile * kDenseTile * 2;
   pl.dense_ds = p->dtype == ATTN_BF16 &&
                 (p->dense_dq_mode == 1 || (p->dense_dq_mode == 0 && ds_bytes <= kDenseDsAutoMax));
 }
@@ -200,7 +220,8 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   if (p->n1 < 1 || p->n2 < 1 || p->n1 % p->n2 != 0) return ATTN_ERR_INVALID;
   if (p->d_qk < 1 || p->d_v < 1 || p->d_rope < 0) return ATTN_ERR_INVALID;
   if (!std::isfinite(p->scale)) return ATTN_ERR_INVALID;
-  if ((p->causal != 0 && p->causal != 1) || (p->deterministic != 0 && p->deterministic != 1) ||
+  if ((p->causal != 0 && p->causal != 1) || (p->band != 0 && p->band != 1) ||
+      (p->mask_align != 0 && p->mask_align != 1) || (p->deterministic != 0 && p->deterministic != 1) ||
       (p->dkdv_atomic != 0 && p->dkdv_atomic != 1))
     return ATTN_ERR_INVALID;
   pl.B = B;
@@ -216,9 +237,21 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     if (p->d_v > p->d_qk) return ATTN_ERR_INVALID;
     if (p->d_qk + p->d_rope > 768 || p->n1 > 256) return ATTN_ERR_INVALID;
     if (pl.T1 > kDenseMaxT || pl.T2 > kDenseMaxT) return ATTN_ERR_INVALID;
-    if (p->causal)
-      for (int b = 0; b < B; ++b)
-        if (cq[b + 1] - cq[b] != ck[b + 1] - ck[b]) return ATTN_ERR_INVALID;
+    // masks on the relative position: causal (aligned top-left or bottom-right when the
+    // lengths differ) or a window of pre_tokens / next_tokens around the aligned diagonal
+    if (p->causal && p->band) return ATTN_ERR_INVALID;
+    if (p->band) {
+      if (p->pre_tokens < -kBandInf || p->pre_tokens > kBandInf || p->next_tokens < -kBandInf ||
+          p->next_tokens > kBandInf || p->pre_tokens + p->next_tokens < 0)
+        return ATTN_ERR_INVALID;
+      pl.lo_rel = p->pre_tokens >= kBandInf ? -kBandInf : (int)-p->pre_tokens;
+      pl.hi_rel = p->next_tokens >= kBandInf ? kBandInf : (int)p->next_tokens;
+    } else if (p->pre_tokens != 0 || p->next_tokens != 0) {
+      return ATTN_ERR_INVALID;
+    } else if (p->causal) {
+      pl.lo_rel = -kBandInf;
+      pl.hi_rel = 0;
+    }
     const int dqk = p->d_qk + p->d_rope;
     if (p->dtype == ATTN_BF16 && !dense_bf16_supported(p->d_qk, p->d_rope, p->d_v)) return ATTN_ERR_UNSUPPORTED;
     if (p->dtype == ATTN_FP32 && (dqk > 256 || p->d_v > 256)) return ATTN_ERR_UNSUPPORTED;
@@ -227,7 +260,9 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   } else {
     // selected backward and forward: BFLOAT16 or FLOAT16 (parameter table)
     if (p->dtype != ATTN_BF16 && p->dtype != ATTN_FP16) return ATTN_ERR_INVALID;
-    if (p->d_rope != 0 || p->causal != 0 || p->dense_dq_mode != 0) return ATTN_ERR_INVALID;
+    if (p->d_rope != 0 || p->causal != 0 || p->dense_dq_mode != 0 || p->band != 0 || p->mask_align != 0 ||
+        p->pre_tokens != 0 || p->next_tokens != 0)
+      return ATTN_ERR_INVALID;
     // D is 192 or 128 (K and V may differ); N1, N2 in 1..128; G in 1..32
     if ((p->d_qk != 128 && p->d_qk != 192) || (p->d_v != 128 && p->d_v != 192)) return ATTN_ERR_INVALID;
     if (p->n1 > 128 || p->n2 > 128 || pl.G > 32) return ATTN_ERR_INVALID;
@@ -273,9 +308,13 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     o += 4 * pl.kv_split.size();
     pl.off_tab2 = o;
     o += 4 * pl.q_tiles.size();
+    pl.off_qt_base = o;
+    o += 4 * pl.qt_base.size();
+    pl.off_qt_kr = o;
+    o += 4 * pl.qt_kr.size();
     o = (o + 7) / 8 * 8;
-    pl.off_ds_base = o;
-    o += 8 * pl.ds_base.size();
+    pl.off_qt_blk = o;
+    o += 8 * pl.qt_blk.size();
   } else {
     o += 4 * pl.blkoff.size();
     pl.off_tab2 = o;
@@ -307,7 +346,7 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   }
   if (p->op == ATTN_OP_DENSE && pl.dense_ds) {
     pl.off_ds = o;
-    o = align_up(o + (size_t)pl.ds_base[pl.B] * p->n1 * kDenseTile * kDenseTile * 2);
+    o = align_up(o + (size_t)pl.ds_blocks * p->n1 * kDenseTile * kDenseTile * 2);
   }
   if (p->op == ATTN_OP_DENSE && p->dtype == ATTN_BF16 && pl.kv_slots > 0) {
     pl.off_kvpart = o;
@@ -407,7 +446,9 @@ std::vector<uint8_t> pack_tables(const attn_bwd_problem_t* p, const Plan& pl) {
     if (!pl.kv_tiles.empty()) std::memcpy(t.data() + pl.off_tab1, pl.kv_tiles.data(), 4 * pl.kv_tiles.size());
     if (!pl.kv_split.empty()) std::memcpy(t.data() + pl.off_kvsplit, pl.kv_split.data(), 4 * pl.kv_split.size());
     if (!pl.q_tiles.empty()) std::memcpy(t.data() + pl.off_tab2, pl.q_tiles.data(), 4 * pl.q_tiles.size());
-    std::memcpy(t.data() + pl.off_ds_base, pl.ds_base.data(), 8 * pl.ds_base.size());
+    std::memcpy(t.data() + pl.off_qt_base, pl.qt_base.data(), 4 * pl.qt_base.size());
+    if (!pl.qt_kr.empty()) std::memcpy(t.data() + pl.off_qt_kr, pl.qt_kr.data(), 4 * pl.qt_kr.size());
+    if (!pl.qt_blk.empty()) std::memcpy(t.data() + pl.off_qt_blk, pl.qt_blk.data(), 8 * pl.qt_blk.size());
   } else {
     std::memcpy(t.data() + pl.off_tab1, pl.blkoff.data(), 4 * pl.blkoff.size());
   }
@@ -515,7 +556,9 @@ attn_status_t dense_launch(const attn_bwd_problem_t* p, const Plan& pl, const vo
   a.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
   a.kv_tiles = at<const int32_t>(workspace, pl.off_tab1);
   a.q_tiles = at<const int32_t>(workspace, pl.off_tab2);
-  a.ds_base = at<const int64_t>(workspace, pl.off_ds_base);
+  a.qt_base = at<const int32_t>(workspace, pl.off_qt_base);
+  a.qt_kr = at<const int32_t>(workspace, pl.off_qt_kr);
+  a.qt_blk = at<const int64_t>(workspace, pl.off_qt_blk);
   a.ds = pl.dense_ds ? at<void>(workspace, pl.off_ds) : nullptr;
   a.kv_split = at<const int32_t>(workspace, pl.off_kvsplit);
   a.kv_part = pl.kv_slots > 0 ? at<void>(workspace, pl.off_kvpart) : nullptr;
@@ -527,7 +570,8 @@ attn_status_t dense_launch(const attn_bwd_problem_t* p, const Plan& pl, const vo
   a.d_main = p->d_qk; a.d_rope = p->d_rope; a.d_v = p->d_v;
   a.scale = (float)p->scale;
   a.scale_log2e = (float)(p->scale * 1.4426950408889634);
-  a.causal = p->causal;
+  a.mask_on = p->causal || p->band;
+  a.lo_rel = pl.lo_rel; a.hi_rel = pl.hi_rel; a.align = p->mask_align;
   if (p->dtype == ATTN_FP32)
     return run("dense_fp32", [&] { return launch_dense_fp32(a, s); }) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   if (run("dense_kv_major", [&] { return launch_dense_kv_bf16(a, s); }) != hipSuccess) return ATTN_ERR_HIP;

@@ -29,7 +29,7 @@ struct QArgs {
   const int64_t* cu_q; const int64_t* cu_kv;
   const int32_t* tiles;  // (sequence, query tile)
   int batch, n1, n2, G, d_main, d_rope, d_v;
-  int causal;
+  int lo_rel, hi_rel, align;  // mask on j - i (dense_band)
   float scale, scale_log2e;
 };
 
@@ -75,9 +75,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int n = 0; n < NQ; ++n) dQ[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int nkt = a.causal ? qt + 1 : (S2 + kKeys - 1) / kKeys;
-  const int nkt_all = (S2 + kKeys - 1) / kKeys;
-  if (nkt > nkt_all) nkt = nkt_all;
+  // key tiles [klo, khi) hold every key some row of this tile sees: lo <= j - i <= hi
+  int lo, hi, klo, khi;
+  dense_band(a.lo_rel, a.hi_rel, a.align, S1, S2, lo, hi);
+  dense_key_tiles(lo, hi, (int64_t)qt * kKeys, min((qt + 1) * kKeys, S1), S2, kKeys, klo, khi);
 
   // key-tile loads: thread serves row my_r = tid / 4 and chunks my_c + 4k
   const int my_r = tid >> 2, my_c = tid & 3;
@@ -99,15 +100,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  if (nkt > 0) prefetch(0);
-  for (int kt = 0; kt < nkt; ++kt) {
+  if (khi > klo) prefetch(klo);
+  for (int kt = klo; kt < khi; ++kt) {
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < KPT; ++k) sts16(&Ks[SK::off(my_r, 8 * (my_c + 4 * k))], pk[k]);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) sts16(&Vs[SV::off(my_r, 8 * (my_c + 4 * k))], pv[k]);
     __syncthreads();
-    if (kt + 1 < nkt) prefetch(kt + 1);
+    if (kt + 1 < khi) prefetch(kt + 1);
 
     // S^T, dP^T: items i = (k-step gi, key sub-tile c); A fragments PD1 items ahead
     constexpr int NI1 = 4 * (KS + VS), PD1 = 4;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int i = 0; i < 4; ++i) {
         const int key = kt * kKeys + 16 * c + 4 * g + i;
         float p = __builtin_amdgcn_exp2f(ST[c][i] * a.scale_log2e - lse);
-        if (key >= S2 || (a.causal && key > rloc)) p = 0.f;
+        if (key >= S2 || key - rloc < lo || key - rloc > hi) p = 0.f;
         ST[c][i] = p * (PT[c][i] + ndr);
       }
     }
@@ -190,7 +191,8 @@ hipError_t launch_dense_dq_bf16(const DenseArgs& a, hipStream_t s) {
   k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.tiles = a.q_tiles;
   k.batch = a.batch; k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;
   k.d_main = a.d_main; k.d_rope = a.d_rope; k.d_v = a.d_v;
-  k.causal = a.causal; k.scale = a.scale; k.scale_log2e = a.scale_log2e;
+  k.lo_rel = a.mask_on ? a.lo_rel : -kBandInf; k.hi_rel = a.mask_on ? a.hi_rel : kBandInf; k.align = a.align;
+  k.scale = a.scale; k.scale_log2e = a.scale_log2e;
   const dim3 grid(a.n_q_tiles, a.n1);
   const int dqk = a.d_main + a.d_rope;
   if (dqk == 192 && a.d_v == 128) hipLaunchKernelGGL((dense_dq_kernel<192, 128>), grid, dim3(256), 0, s, k);

@@ -35,10 +35,11 @@ struct DqArgs {
   const uint16_t* ds;           // [block][head][64 keys][64 rows]
   uint16_t* dq; uint16_t* dq_rope;
   const int64_t* cu_q; const int64_t* cu_kv;
-  const int64_t* ds_base;       // [B + 1]
+  const int32_t* qt_base;       // [B + 1] query tiles before each sequence
+  const int64_t* qt_blk;        // first stored block of each query tile
+  const int32_t* qt_kr;         // [query tiles][2] its 64-key tiles [lo, hi)
   const int32_t* tiles;         // [n][2] (sequence, query tile)
   int n1, n2, G;
-  int causal;
   float scale;
   int n_q_tiles;                // workgroups: n_split, then (query tile, KV head), KV head fastest
   // split key tiles of the KV-major kernel
@@ -201,10 +202,12 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
   const int b = a.tiles[2 * qi], qt = a.tiles[2 * qi + 1];
   const int64_t qs = a.cu_q[b], ks = a.cu_kv[b];
   const int S1 = (int)(a.cu_q[b + 1] - qs), S2 = (int)(a.cu_kv[b + 1] - ks);
-  const int nkt = (S2 + kT - 1) / kT;
-  const int nkt_run = a.causal ? min(qt + 1, nkt) : nkt;
+  // the query tile's key tiles [klo, klo + nkt_run), whose dS blocks start at block blk0
+  const int gq = a.qt_base[b] + qt;
+  const int klo = a.qt_kr[2 * gq];
+  const int nkt_run = a.qt_kr[2 * gq + 1] - klo;
   const int nvalid = min(kT, S1 - qt * kT);
-  const int64_t blk0 = a.ds_base[b];
+  const int64_t blk0 = a.qt_blk[gq];
   const uint32_t smem_lds = lds_addr(smem);
 
   KeyPartLanes<WM> pm;
@@ -262,10 +265,10 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
         else dma16<8192 * k>(src, lds_part + w * 1024);
       });
     };
-    // the K tile (both parts) of key tile kt, into K stage kt & 1
+    // the K tile (both parts) of the range's key tile kt (key tile klo + kt), into K stage kt & 1
     auto issue_k = [&](int kt) {
-      const int nk = min(kT, S2 - kt * kT);
-      const int64_t kr0 = (ks + (int64_t)kt * kT) * a.n2 + kvh;
+      const int nk = min(kT, S2 - (klo + kt) * kT);
+      const int64_t kr0 = (ks + (int64_t)(klo + kt) * kT) * a.n2 + kvh;
       const uint32_t stage = smem_lds + (kt & 1) * KB;
       issue_part(std::integral_constant<int, WM>{}, std::false_type{}, pm,
                  reinterpret_cast<const char*>(a.k + kr0 * DM), rs_m, stage + OKM, nk);
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_ds_kernel(DqArgs a) {
     // the HP dS^T blocks of key tile kt, into dS^T stage kt mod 3: HP transfers per wave
     auto issue_d = [&](int kt) {
       const uint32_t stage = smem_lds + OD + (kt % 3) * DB;
-      const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt : (int64_t)qt * nkt + kt);
+      const int64_t blk = blk0 + kt;
       const char* dblk = reinterpret_cast<const char*>(a.ds + (blk * a.n1 + h0) * (kT * kT));
       static_for<HP>([&](auto hc) {
         constexpr int hx = decltype(hc)::value;
@@ -385,9 +388,10 @@ static hipError_t launch_dq_any(const DenseArgs& a, bool with_dq, hipStream_t s)
   k.k = (const uint16_t*)a.k; k.k_rope = (const uint16_t*)a.k_rope;
   k.ds = (const uint16_t*)a.ds;
   k.dq = (uint16_t*)a.dq; k.dq_rope = (uint16_t*)a.dq_rope;
-  k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.ds_base = a.ds_base; k.tiles = a.q_tiles;
+  k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.qt_base = a.qt_base; k.qt_blk = a.qt_blk; k.qt_kr = a.qt_kr;
+  k.tiles = a.q_tiles;
   k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;
-  k.causal = a.causal; k.scale = a.scale;
+  k.scale = a.scale;
   k.n_q_tiles = n_q;
   k.split = a.kv_split; k.part = (const float*)a.kv_part;
   k.dk = (uint16_t*)a.dk; k.dk_rope = (uint16_t*)a.dk_rope; k.dv = (uint16_t*)a.dv;

@@ -37,8 +37,12 @@ __global__ __launch_bounds__(64) void dense_kv_fp32(DenseArgs a) {
   float dk[kF32MaxD / 64], dvv[kF32MaxD / 64];
 #pragma unroll
   for (int c = 0; c < kF32MaxD / 64; ++c) dk[c] = dvv[c] = 0.f;
-  const int64_t i0 = a.causal ? qs + jloc : qs;
-  const int64_t R = (qe > i0 ? qe - i0 : 0) * a.G;
+  // query rows that see key j: lo <= j - i <= hi
+  int lo, hi;
+  dense_band(a.lo_rel, a.hi_rel, a.align, qe - qs, a.cu_kv[b + 1] - a.cu_kv[b], lo, hi);
+  const int64_t ia = jloc - hi > 0 ? jloc - hi : 0, ib = jloc - lo < qe - qs ? jloc - lo + 1 : qe - qs;
+  const int64_t i0 = qs + ia;
+  const int64_t R = (ib > ia ? ib - ia : 0) * a.G;
   for (int64_t r0 = 0; r0 < R; r0 += 64) {
     float p = 0.f, ds = 0.f;
     const int64_t r = r0 + tid;
@@ -90,7 +94,11 @@ __global__ __launch_bounds__(64) void dense_dq_fp32(DenseArgs a) {
   const int b = seq_of(a.cu_q, a.batch, i);
   const int64_t iloc = i - a.cu_q[b];
   const int64_t ks = a.cu_kv[b], ke = a.cu_kv[b + 1];
-  const int64_t kend = a.causal ? (ks + iloc + 1 < ke ? ks + iloc + 1 : ke) : ke;
+  // keys that query i sees: lo <= j - i <= hi
+  int lo, hi;
+  dense_band(a.lo_rel, a.hi_rel, a.align, a.cu_q[b + 1] - a.cu_q[b], ke - ks, lo, hi);
+  const int64_t kbeg = iloc + lo > 0 ? ks + iloc + lo : ks;
+  const int64_t kend = iloc + hi < ke - ks ? ks + iloc + hi + 1 : ke;
   for (int d = tid; d < dqk; d += 64) Qi[d] = qk_elem(q, qr, i, a.n1, h, a.d_main, a.d_rope, d);
   for (int d = tid; d < dv; d += 64) Yi[d] = dy[(i * a.n1 + h) * dv + d];
   const float lse2 = a.lse2[i * a.n1 + h], ndrow = a.ndrow[i * a.n1 + h];
@@ -98,7 +106,7 @@ __global__ __launch_bounds__(64) void dense_dq_fp32(DenseArgs a) {
   float acc[kF32MaxD / 64];
 #pragma unroll
   for (int c = 0; c < kF32MaxD / 64; ++c) acc[c] = 0.f;
-  for (int64_t j0 = ks; j0 < kend; j0 += 64) {
+  for (int64_t j0 = kbeg; j0 < kend; j0 += 64) {
     const int64_t j = j0 + tid;
     float ds = 0.f;
     if (j < kend) {

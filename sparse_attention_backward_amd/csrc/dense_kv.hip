@@ -15,7 +15,8 @@
 // between them (two waves per SIMD, one of each kind, so that one wave's LDS waits and
 // exponentials overlap the other's matrix work):
 //   S wave (w < 4), K resident:   S = Q K^T; P = exp2(S*scale*log2e - lse2) with the masks
-//                                 (causal diagonal, ragged query tail); P -> LDS;
+//                                 (edges of the causal / window mask, ragged query tail);
+//                                 P -> LDS;
 //                                 dV += P^T dY
 //   dP wave (w >= 4), V resident: dP = dY V^T; dS = P (dP - drow) with P from LDS;
 //                                 dS^T -> workspace (bf16, one 64 x 64 block per (query
@@ -24,8 +25,9 @@
 // tiles repacked in registers; B operands of dV / dK: dY / Q columns (ds_read_b64_tr_b16).
 // Each kind does 2*(D_qk + D_v) flop per (row, key) pair.  The dP waves work one step
 // behind the S waves: step s's P, written before barrier s + 1, is read after it.
-// Causal: a 32-key block against a 32-row block is skipped when it lies wholly after the
-// rows, masked on the diagonal, and complete otherwise.
+// Masks (causal, windows): a 32-key block against a 32-row block is skipped when none of its
+// pairs is visible, masked element by element when it crosses an edge of the mask, and
+// complete otherwise.
 //
 // Key tiles with many query tiles are split into ranges (so that no workgroup runs far
 // longer than the average): each range leaves its fp32 dK / dV in a partial slot, in
@@ -58,13 +60,15 @@ struct DkvArgs {
   uint16_t* dk; uint16_t* dk_rope; uint16_t* dv;
   uint16_t* ds;               // [block][head][64 keys][64 rows] bf16 (dS transposed)
   const int64_t* cu_q; const int64_t* cu_kv;
-  const int64_t* ds_base;     // [B + 1] (query tile, 64-key tile) blocks before each sequence
+  const int32_t* qt_base;     // [B + 1] query tiles before each sequence
+  const int64_t* qt_blk;      // first stored dS block of each query tile
+  const int32_t* qt_kr;       // [query tiles][2] its 64-key tiles [lo, hi)
   const int32_t* tiles;       // [n][6] (sequence, 128-key tile, KV head, first / end query tile,
                               // partial slot or -1); sequence < 0: idle slot
   const int32_t* split;       // [n][5] (sequence, 128-key tile, KV head, first slot, parts)
   float* part;                // fp32 partials, kDenseKvPartBytes per slot
   int n1, n2, G;
-  int causal;
+  int lo_rel, hi_rel, align;  // mask on j - i (dense_band); unbounded without a mask
   float scale, scale_log2e;
 };
 
@@ -201,7 +205,8 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
   const int64_t qs = a.cu_q[b];
   const int S1 = (int)(a.cu_q[b + 1] - qs);
   const int nsteps = a.G * (qb - qa);
-  const int64_t blk0 = a.ds_base[b];
+  int mlo, mhi;  // key j visible to query i iff mlo <= j - i <= mhi (positions in the sequence)
+  dense_band(a.lo_rel, a.hi_rel, a.align, S1, S2, mlo, mhi);
   const int kb = 4 * kt0 + p;           // this pair's 32-key block
   const int kt64 = 2 * kt0 + (p >> 1);  // its 64-key tile (dS block column)
   const bool idle = 32 * p >= nk;       // every key of this pair lies past the sequence
@@ -268,11 +273,13 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
   };
   auto stage_of = [&](int st) { return smem_lds + (uint32_t)(st % 3) * SB; };
   auto xslot = [&](int st, int hi) { return smem_lds + OX + (uint32_t)((((st & 1) * 4 + p) * 2 + hi) * 2048); };
-  // the pair's 32-key block against the 32-row block of half hi of step st
-  auto half_active = [&](int st, int hi, int& hg, int& qt, int& rb) {
+  // the pair's 32-key block against the 32-row block of half hh of step st: skipped when no
+  // (key, row) pair of it is visible (j - i spans 32 (kb - rb) - 31 .. + 31)
+  auto half_active = [&](int st, int hh, int& hg, int& qt, int& rb) {
     step_tile(st, hg, qt);
-    rb = 2 * qt + hi;
-    return !idle && !(a.causal && kb > rb);
+    rb = 2 * qt + hh;
+    const int d0 = 32 * (kb - rb);
+    return !idle && d0 + 31 >= mlo && d0 - 31 <= mhi;
   };
 
   if (nsteps > 0 && swave) issue_stage(0, smem_lds);
@@ -303,7 +310,8 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
       constexpr int hi = decltype(hic)::value;
       int hg, qt, rb;
       if (!half_active(st, hi, hg, qt, rb)) return;
-      const bool diag = a.causal && kb == rb;
+      const int d0 = 32 * (kb - rb);
+      const bool edge = d0 - 31 < mlo || d0 + 31 > mhi;  // the block crosses an edge of the mask
       const int nvalid = min(kRows, S1 - qt * kRows);
       const uint32_t vm = stage + OQM + PartLanes<WM>::rowA(lane, 0), vr = stage + OQR + PartLanes<WR>::rowA(lane, 0);
       const uint32_t vy = stage + OY + PartLanes<WY>::colB(lane, 0);
@@ -350,18 +358,18 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) S[t][rt][i] = __builtin_amdgcn_exp2f(S[t][rt][i] * a.scale_log2e - lse[rt][i]);
-      if (diag) {
-        // keys 32kb + 16t + l16 against rows 32kb + 16rt + 4g + i: tile pair (t, rt) = (1, 0)
-        // lies wholly after the diagonal, (0, 1) wholly before it, and on (0, 0) / (1, 1)
-        // the key lies after the row iff l16 - 4g > i
-        const int dl = l16 - 4 * g;
-        S[1][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (edge) {
+        // key 32kb + 16t + l16 against row 32rb + 16rt + 4g + i: j - i = d0 + 16(t - rt) + l16 - 4g - i
+        const int dl = d0 + l16 - 4 * g;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool after = dl > i;
-          S[0][0][i] = after ? 0.f : S[0][0][i];
-          S[1][1][i] = after ? 0.f : S[1][1][i];
-        }
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int d = dl + 16 * (t - rt) - i;
+              S[t][rt][i] = (d < mlo || d > mhi) ? 0.f : S[t][rt][i];
+            }
       }
       // P as bf16 for this wave's dV product and as f16 (more mantissa, and the dP wave's
       // mixed-precision multiply takes f16 halves directly) for the exchange
@@ -476,12 +484,14 @@ __global__ __launch_bounds__(512, 1) void dense_kv_kernel(DkvArgs a) {
     };
 
     // The dS^T row of this lane's key in the block of step st, or nullptr when no block
-    // exists (causal: the key tile lies after the query tile).
+    // exists (no key of the 64-key tile is visible to a row of the query tile).
     auto ds_row = [&](int st) -> uint16_t* {
       int hg, qt;
       step_tile(st, hg, qt);
-      if (!(kt64 < nkt64 && (!a.causal || kt64 <= qt))) return nullptr;
-      const int64_t blk = blk0 + (a.causal ? (int64_t)qt * (qt + 1) / 2 + kt64 : (int64_t)qt * nkt64 + kt64);
+      const int gq = a.qt_base[b] + qt;
+      const int klo = a.qt_kr[2 * gq], khi = a.qt_kr[2 * gq + 1];
+      if (!(kt64 < nkt64 && kt64 >= klo && kt64 < khi)) return nullptr;
+      const int64_t blk = a.qt_blk[gq] + (kt64 - klo);
       return a.ds + (blk * a.n1 + kvh * a.G + hg) * (int64_t)(kRows * kRows) + (32 * (p & 1) + l16) * kRows;
     };
 
@@ -632,10 +642,11 @@ hipError_t launch_dense_kv_bf16(const DenseArgs& a, hipStream_t s) {
   k.lse2 = a.lse2; k.ndrow = a.ndrow;
   k.dk = (uint16_t*)a.dk; k.dk_rope = (uint16_t*)a.dk_rope; k.dv = (uint16_t*)a.dv;
   k.ds = (uint16_t*)a.ds;
-  k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.ds_base = a.ds_base;
+  k.cu_q = a.cu_q; k.cu_kv = a.cu_kv; k.qt_base = a.qt_base; k.qt_blk = a.qt_blk; k.qt_kr = a.qt_kr;
   k.tiles = a.kv_tiles; k.split = a.kv_split; k.part = (float*)a.kv_part;
   k.n1 = a.n1; k.n2 = a.n2; k.G = a.G;
-  k.causal = a.causal; k.scale = a.scale; k.scale_log2e = a.scale_log2e;
+  k.lo_rel = a.mask_on ? a.lo_rel : -kBandInf; k.hi_rel = a.mask_on ? a.hi_rel : kBandInf; k.align = a.align;
+  k.scale = a.scale; k.scale_log2e = a.scale_log2e;
   const bool ds = a.ds != nullptr;
   if (a.d_main == 128 && a.d_rope == 64 && a.d_v == 128)
     return launch_kv<128, 64, 128>(k, a.n_kv_tiles, ds, s);

@@ -25,6 +25,36 @@ struct PreArgs {
 hipError_t launch_preprocess(const PreArgs& a, hipStream_t s);
 
 // ---- dense varlen ------------------------------------------------------------
+// Masks on the relative position d = j - i of key j and query i (positions in their
+// sequence): key j is visible to query i iff lo <= d <= hi.  No mask: lo = -kBandInf,
+// hi = kBandInf; causal: hi = off; window of preTokens / nextTokens: lo = off - pre,
+// hi = off + next; off = 0 aligns the first query with the first key, off = S2 - S1 the
+// last query with the last key.  The schedule (host) and the kernels use these helpers.
+constexpr int kBandInf = 1 << 30;
+__host__ __device__ inline void dense_band(int lo_rel, int hi_rel, int align, int64_t S1, int64_t S2, int& lo,
+                                           int& hi) {
+  const int off = align ? (int)(S2 - S1) : 0;
+  lo = lo_rel <= -kBandInf ? -kBandInf : lo_rel + off;
+  hi = hi_rel >= kBandInf ? kBandInf : hi_rel + off;
+}
+// Tiles [tlo, thi) of `tile` keys holding a key visible to some query row in [i0, i1) (an empty
+// range gives tlo = thi = 0).
+__host__ __device__ inline void dense_key_tiles(int lo, int hi, int64_t i0, int64_t i1, int64_t S2, int tile,
+                                                int& tlo, int& thi) {
+  const int64_t a = i0 + lo > 0 ? i0 + lo : 0, b = (i1 - 1) + hi < S2 - 1 ? (i1 - 1) + hi : S2 - 1;
+  if (i1 <= i0 || S2 <= 0 || a > b) { tlo = thi = 0; return; }
+  tlo = (int)(a / tile);
+  thi = (int)(b / tile) + 1;
+}
+// Tiles [tlo, thi) of `tile` query rows holding a row that sees some key in [j0, j1).
+__host__ __device__ inline void dense_row_tiles(int lo, int hi, int64_t j0, int64_t j1, int64_t S1, int tile,
+                                                int& tlo, int& thi) {
+  const int64_t a = j0 - hi > 0 ? j0 - hi : 0, b = (j1 - 1) - lo < S1 - 1 ? (j1 - 1) - lo : S1 - 1;
+  if (j1 <= j0 || S1 <= 0 || a > b) { tlo = thi = 0; return; }
+  tlo = (int)(a / tile);
+  thi = (int)(b / tile) + 1;
+}
+
 struct DenseArgs {
   const void* q;  const void* q_rope;
   const void* k;  const void* k_rope;
@@ -34,7 +64,11 @@ struct DenseArgs {
   void* ds;                 // bf16 dS^T blocks [block][N1][64][64] (stored-dS mode), else null
   const int64_t* cu_q;      // [B+1]
   const int64_t* cu_kv;     // [B+1]
-  const int64_t* ds_base;   // [B+1] (query tile, 64-key tile) blocks before each sequence
+  // stored dS blocks: query tile q (global index qt_base[b] + local tile) has 64-key tiles
+  // [qt_kr[2q], qt_kr[2q + 1]), whose blocks start at block qt_blk[q]
+  const int32_t* qt_base;   // [B+1] query tiles before each sequence
+  const int64_t* qt_blk;    // [query tiles]
+  const int32_t* qt_kr;     // [query tiles][2]
   const int32_t* kv_tiles;  // [n_kv_tiles, 6] = (sequence, 128-key tile, KV head, first query tile,
                             //  end query tile, partial slot or -1); sequence -1 = idle slot
   const int32_t* kv_split;  // [n_kv_split, 5] = (sequence, 128-key tile, KV head, first slot, parts)
@@ -45,7 +79,8 @@ struct DenseArgs {
   int64_t T1, T2;
   int d_main, d_rope, d_v;  // head dims: query/key main part, rope part, value
   float scale, scale_log2e;
-  int causal;
+  int mask_on;              // a mask applies (causal or window); lo_rel / hi_rel / align as in dense_band
+  int lo_rel, hi_rel, align;
 };
 constexpr int kDenseTile = 64;      // query tile and dS block length of the bf16 dense kernels
 constexpr int kDenseKeyTile = 128;  // keys per workgroup of the bf16 dense KV-major kernel

@@ -89,7 +89,14 @@ def test_null_arguments():
     (dict(n1=6, n2=4), INVALID),                            # Nq / Nkv integer
     (dict(n1=512, n2=2), INVALID),                          # N <= 256
     (dict(d_qk=512, d_rope=512), INVALID),                  # D <= 768
-    (dict(cu_q=[0, 100, 160], cu_kv=[0, 100, 164]), INVALID),  # causal needs equal lengths
+    (dict(cu_q=[0, 100, 160], cu_kv=[0, 100, 164]), OK),   # causal with unequal lengths: aligned
+    (dict(cu_q=[0, 100, 160], cu_kv=[0, 100, 164], align=1), OK),
+    (dict(align=2), INVALID),
+    (dict(causal=False, band=(16, 0)), OK),                 # window of pre / next tokens
+    (dict(causal=False, band=(-3, 2), align=1), INVALID),   # empty window: pre + next < 0
+    (dict(causal=False, band=(3, -2)), OK),
+    (dict(causal=True, band=(16, 0)), INVALID),             # causal and window exclude each other
+    (dict(causal=False, band=((1 << 30) + 1, 0)), INVALID),
     (dict(cu_q=[1, 100, 164]), INVALID),                    # cu starts at 0
     (dict(cu_q=[0, 100, 90], cu_kv=[0, 100, 90]), INVALID),  # non-decreasing
     (dict(cu_q=[0, (1 << 20) + 1], cu_kv=[0, (1 << 20) + 1]), INVALID),  # T <= 1M
@@ -292,3 +299,13 @@ def test_bsnd_layout_is_tnd_with_equal_lengths():
     t3 = selected(cu_q=cu_q, cu_kv=cu_kv)
     t3.s.layout = 7
     assert status_ws(t3)[0] == INVALID
+
+
+def test_mask_fields_are_dense_only():
+    for field, val in (("band", 1), ("mask_align", 1), ("pre_tokens", 3), ("next_tokens", 3)):
+        p = selected()
+        setattr(p.s, field, val)
+        assert status_ws(p)[0] == INVALID, field
+    d = dense(causal=False)
+    d.s.pre_tokens = 4   # window sizes without the window flag
+    assert status_ws(d)[0] == INVALID

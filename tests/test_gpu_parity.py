@@ -45,6 +45,31 @@ def test_dense_bf16_noncausal_unequal_lengths(dq_mode):
     _run(w, dq_mode=dq_mode)
 
 
+# Masks on the relative position (causal aligned top-left or bottom-right when the lengths
+# differ, windows of pre / next tokens): blocks skipped, blocks crossing an edge masked per
+# element, rows that see no key (zero gradients), keys no row sees (zero dK / dV).
+MASKS = [
+    dict(seqlens=(150, 70), seqlens_kv=(200, 70), causal=True, mask_align=1),       # S1 < S2, bottom-right
+    dict(seqlens=(200, 64), seqlens_kv=(90, 64), causal=True, mask_align=1),        # S1 > S2: keyless rows
+    dict(seqlens=(120,), seqlens_kv=(210,), causal=True, mask_align=0),             # top-left, S1 < S2
+    dict(seqlens=(190, 77), causal=False, band=(40, 5)),                            # window, equal lengths
+    dict(seqlens=(130, 96), seqlens_kv=(160, 50), causal=False, band=(17, 33), mask_align=1),
+    dict(seqlens=(140,), seqlens_kv=(100,), causal=False, band=(0, 0)),              # the diagonal only
+    dict(seqlens=(100,), causal=False, band=(5, -3), mask_align=1),                  # a window off the diagonal
+]
+
+
+@pytest.mark.parametrize("dq_mode", [1, 2])
+@pytest.mark.parametrize("kw", MASKS)
+def test_dense_bf16_masks(kw, dq_mode):
+    _run(W.small_dense(n1=8, n2=2, **kw), dq_mode=dq_mode)
+
+
+@pytest.mark.parametrize("kw", MASKS[:2] + MASKS[4:5])
+def test_dense_fp32_masks(kw):
+    _run(W.small_dense(n1=4, n2=2, d_qk=64, d_rope=32, d_v=64, dtype="fp32", **kw))
+
+
 def test_dense_fp32_small_rope():
     w = W.small_dense(seqlens=(70, 33), n1=4, n2=2, d_qk=64, d_rope=32, d_v=64, dtype="fp32")
     _run(w)

@@ -42,6 +42,8 @@ class Workload:
     scale: float
     d_rope: int = 0                # dense only: queryRope / keyRope head dim
     causal: bool = False
+    mask_align: int = 0            # dense masks: 0 top-left, 1 bottom-right alignment
+    band: tuple = None             # dense: (pre_tokens, next_tokens) window, or None
     block_size: int = 0            # selected only
     block_count: int = 0
     index_dist: str = "uniform"    # "uniform" or "zipf"
@@ -105,12 +107,13 @@ CONFIGS = (1, 2, 3, 4, 5)
 
 
 def small_dense(seqlens=(200, 130), n1=8, n2=2, d_qk=128, d_rope=64, d_v=128, dtype="bf16",
-                causal=True, seed=11, scale=None):
+                causal=True, seed=11, scale=None, seqlens_kv=None, mask_align=0, band=None):
     """A multi-tile dense case with a ragged tail, small enough for the oracle."""
     d = d_qk + d_rope
-    return Workload(f"dense-small-{dtype}", "dense", dtype, tuple(seqlens), tuple(seqlens), n1, n2,
+    kv = tuple(seqlens_kv) if seqlens_kv is not None else tuple(seqlens)
+    return Workload(f"dense-small-{dtype}", "dense", dtype, tuple(seqlens), kv, n1, n2,
                     d_qk, d_v, scale if scale is not None else 1.0 / math.sqrt(d), d_rope=d_rope,
-                    causal=causal, seed=seed)
+                    causal=causal, mask_align=mask_align, band=band, seed=seed)
 
 
 def small_selected(seqlens=(256, 384), n1=32, n2=2, d_qk=192, d_v=128, block_size=64,
