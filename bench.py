@@ -73,6 +73,7 @@ KERNEL_SOURCES = {
     "selected_kv_major": ("sel_kv_kernel", "sel_kv.hip"),
     "selected_dq_reduce": ("dq_reduce_kernel", "sel_reduce.hip"),
     "selected_forward": ("sel_fwd_kernel", "sel_fwd.hip"),
+    "indexer_query_major": ("idx_bwd_kernel", "indexer.hip"),
     "row_stats": ("preprocess_kernel", "preprocess.hip"),
 }
 CSRC = os.path.join(ROOT, "sparse_attention_backward_amd", "csrc")
@@ -475,6 +476,61 @@ def measure_forward(wl: int, steps: int, warmup: int, prewarm_ms=300.0):
     return rec
 
 
+def measure_indexer(deterministic: bool, steps: int, warmup: int, prewarm_ms=300.0):
+    """The lightning-indexer backward (attn_bwd_indexer) on its 8K workload: three GEMMs per
+    (token, key head, selected key) -- S = Q K^T, dQ = R K, dK shares = R^T Q -- i.e.
+    2 x 3 x G x D flop per (token, key head, slot)."""
+    w = W.indexer_config()
+    dev = torch.device("cuda", 0)
+    x = W.make_indexer_inputs(w, device=dev, backend="torch")
+    prob = sab.Problem.indexer(w.cu_q, w.cu_kv, w.n1, w.n2, w.topk, d=w.d, deterministic=deterministic)
+    ws = torch.empty(max(1, sab.attn_bwd_workspace_size(prob)), dtype=torch.uint8, device=dev)
+    dq, dk, dw = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["weights"])
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sab.attn_bwd_indexer(prob, x["q"], x["k"], x["weights"], x["dy"], x["indices"], dq, dk, dw, ws, stream=stream)
+
+    torch.cuda.synchronize()
+    spent, t0 = 0.0, time.perf_counter()
+    while spent < prewarm_ms and time.perf_counter() - t0 < 60:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        spent += a.elapsed_time(b)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    sab.attn_bwd_profile_reset()
+    sab.attn_bwd_profiling(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    sab.attn_bwd_profiling(False)
+    ms = a.elapsed_time(b) / steps
+    kernels = sab.attn_bwd_profile_read()
+    fl = w.T1 * w.n1 * w.topk * w.d * 6
+    tot_ms, n = kernels["indexer_query_major"]
+    kms = tot_ms / steps
+    rec = {"workload": w.name, "pass": "indexer backward", "deterministic": deterministic,
+           "value": round(fl / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
+           "steps": steps, "pct_bf16_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "roofline": {"kernel": "indexer_query_major", "bound": "mfma", "avg_ms": tot_ms / max(n, 1),
+                        "achieved": fl / (kms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": fl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop_per_call": fl,
+                        "traffic": recorded_counters("indexer_query_major", w.name).get("traffic_bytes_per_launch")},
+           "kernels_ms_per_call": {k: round(v[0] / steps, 4) for k, v in kernels.items()},
+           "prewarm_ms": round(spent, 1)}
+    del x, ws, dq, dk, dw
+    torch.cuda.empty_cache()
+    return rec
+
+
 EXTRA_RUNS = ((2, False), (3, False), (4, False), (4, True))  # (workload, deterministic) beside the headline
 FORWARD_RUNS = (5, 3)  # selected forward measured on these workloads
 
@@ -491,6 +547,8 @@ def main(argv=None):
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--window-tokens", type=int, default=0, help="selected: query tokens per window (0 automatic)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' lines")
+    ap.add_argument("--indexer-only", action="store_true",
+                    help="only the lightning-indexer backward lines (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 5 times (counter calibration)")
@@ -523,6 +581,10 @@ def main(argv=None):
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
         return 0
 
+    if args.indexer_only:
+        print(json.dumps([measure_indexer(det, args.steps, args.warmup, args.prewarm_ms) for det in (False, True)]),
+              flush=True)
+        return 0
     w, x, rec = measure(args.workload, args.steps, args.warmup, args.deterministic, args.window_tokens,
                         args.prewarm_ms)
     line = {
@@ -563,6 +625,8 @@ def main(argv=None):
             torch.cuda.empty_cache()
         for wl in FORWARD_RUNS:
             extra.append(measure_forward(wl, max(3, args.steps // 2), args.warmup, args.prewarm_ms))
+        for det in (False, True):
+            extra.append(measure_indexer(det, args.steps, args.warmup, args.prewarm_ms))
         line["extra"] = extra
     print(json.dumps(line), flush=True)
     return 0

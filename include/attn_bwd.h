@@ -74,7 +74,7 @@ typedef enum {
 } attn_status_t;
 
 typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1, ATTN_FP32 = 2 } attn_dtype_t;
-typedef enum { ATTN_OP_DENSE = 0, ATTN_OP_SELECTED = 1, ATTN_OP_SELECTED_FWD = 2 } attn_op_t;
+typedef enum { ATTN_OP_DENSE = 0, ATTN_OP_SELECTED = 1, ATTN_OP_SELECTED_FWD = 2, ATTN_OP_INDEXER = 3 } attn_op_t;
 typedef enum { ATTN_LAYOUT_TND = 0, ATTN_LAYOUT_BSND = 1 } attn_layout_t;
 
 typedef struct {
@@ -228,6 +228,31 @@ attn_status_t attn_fwd_selected(const attn_bwd_problem_t* p,
 attn_status_t attn_bwd_selected_index(const attn_bwd_problem_t* p, const int32_t* topk_indices,
                                       int32_t* offsets, int32_t* lists, int32_t* order,
                                       void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
+/* Lightning-indexer backward (page "aclnnLightningIndexerGrad", formula section):
+ *   S = ReLU(Q . Gather(K, Indices)),  Y = dy * Weights,  dW = Reduce(S * dy),
+ *   dQ = ReluGrad(Y, S) . Gather(K, Indices),  dK = ScatterAdd(ReluGrad(Y, S) . Q, Indices).
+ * The page's shape table is lost in its text; the readings taken: for query token t, key
+ * head n2 and the G = n1 / n2 query heads h of n2 (h / G = n2),
+ *   S[t, h, k] = max(0, sum_d Q[t, h, d] K[idx, n2, d])  with idx = cu_kv[b] + indices[t, n2, k],
+ *   Y[t, h, k] = dy[t, n2, k] * weights[t, h],  ReluGrad(Y, S) = Y where S > 0, else 0,
+ *   dW[t, h] = sum_k S[t, h, k] dy[t, n2, k]; no scale factor.
+ * p->op = ATTN_OP_INDEXER, p->dtype = ATTN_BF16, d_qk = D = 128, d_v = 0, block_size = 1,
+ * block_count = topK (1 .. 128K, and every sequence with queries has at least topK keys),
+ * G <= 64, B <= 1024, layout TND or BSND.  Tensors (bf16): q [T1, n1, 128], k [T2, n2, 128],
+ * weights [T1, n1], dy [T1, n2, topK]; indices int32 [T1, n2, topK] (key positions inside
+ * the token's sequence; a repeated index counts twice; an out-of-range one contributes
+ * nothing and raises the flag of attn_bwd_check_index_flag); outputs dq [T1, n1, 128],
+ * dk [T2, n2, 128], dweights [T1, n1].  deterministic = 0 (the page's default): dK by fp32
+ * atomics; deterministic = 1: each (token, key head, slot)'s share of dK is kept and the
+ * shares of a key row are added in ascending (token, slot) order through an inverted index,
+ * over windows of query tokens whose shares take at most 8 GiB (sel_window_tokens caps the
+ * window further).  dQ and dW have one writer per row in both modes. */
+attn_status_t attn_bwd_indexer(const attn_bwd_problem_t* p,
+                               const void* q, const void* k, const void* weights, const void* dy,
+                               const int32_t* indices,
+                               void* dq, void* dk, void* dweights,
+                               void* workspace, uint64_t workspace_bytes, void* hip_stream);
 
 /* Read (synchronously, on `hip_stream`) the device flag that a selected call raises
  * when it meets a topk id outside [0, S2_b / block_size).  Writes 1 to *raised when

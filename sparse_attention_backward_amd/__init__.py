@@ -23,22 +23,22 @@ import torch
 __all__ = [
     "AttnError", "Problem", "LIB_PATH", "lib",
     "attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_dense_varlen_noalloc", "attn_bwd_selected",
-    "attn_fwd_selected", "attn_bwd_selected_index", "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version",
+    "attn_fwd_selected", "attn_bwd_selected_index", "attn_bwd_indexer", "attn_bwd_check_index_flag", "attn_bwd_status_string", "attn_bwd_version",
     "attn_bwd_profiling", "attn_bwd_profile_reset", "attn_bwd_profile_read",
-    "dense_backward", "selected_backward", "selected_forward", "EXPORTED_SYMBOLS",
+    "dense_backward", "selected_backward", "selected_forward", "indexer_backward", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_NULLPTR, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
 ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
-ATTN_OP_DENSE, ATTN_OP_SELECTED, ATTN_OP_SELECTED_FWD = 0, 1, 2
+ATTN_OP_DENSE, ATTN_OP_SELECTED, ATTN_OP_SELECTED_FWD, ATTN_OP_INDEXER = 0, 1, 2, 3
 ATTN_LAYOUT_TND, ATTN_LAYOUT_BSND = 0, 1
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_BWD_NOALLOC_SCRATCH_BYTES
 
 EXPORTED_SYMBOLS = ("attn_bwd_workspace_size", "attn_bwd_dense_varlen", "attn_bwd_dense_varlen_noalloc",
-                    "attn_bwd_selected", "attn_fwd_selected", "attn_bwd_selected_index",
+                    "attn_bwd_selected", "attn_fwd_selected", "attn_bwd_selected_index", "attn_bwd_indexer",
                     "attn_bwd_check_index_flag", "attn_bwd_profiling", "attn_bwd_profile_reset",
                     "attn_bwd_profile_read", "attn_bwd_status_string", "attn_bwd_version")
 
@@ -78,6 +78,8 @@ def _load():
     L.attn_fwd_selected.restype = c_int32
     L.attn_bwd_selected_index.argtypes = [P] + [c_void_p] * 4 + [c_void_p, c_uint64, c_void_p]
     L.attn_bwd_selected_index.restype = c_int32
+    L.attn_bwd_indexer.argtypes = [P] + [c_void_p] * 8 + [c_void_p, c_uint64, c_void_p]
+    L.attn_bwd_indexer.restype = c_int32
     L.attn_bwd_check_index_flag.argtypes = [P, c_void_p, POINTER(c_int32), c_void_p]
     L.attn_bwd_check_index_flag.restype = c_int32
     L.attn_bwd_profiling.argtypes = [c_int32]
@@ -170,6 +172,13 @@ class Problem:
                    cu_kv, n1, n2, d_qk, d_v, scale, block_size=block_size, block_count=block_count,
                    deterministic=deterministic, dkdv_atomic=dkdv_atomic, window_tokens=window_tokens, bsnd=bsnd)
 
+    @classmethod
+    def indexer(cls, cu_q, cu_kv, n1, n2, topk, d=128, deterministic=False, window_tokens=0, bsnd=None):
+        """The lightning-indexer backward's problem (op ATTN_OP_INDEXER): topk indices per
+        (token, key head), head dim d, bf16."""
+        return cls(ATTN_OP_INDEXER, ATTN_BF16, cu_q, cu_kv, n1, n2, d, 0, 1.0, block_size=1, block_count=topk,
+                   deterministic=deterministic, window_tokens=window_tokens, bsnd=bsnd)
+
     @property
     def ref(self):
         return ctypes.byref(self.s)
@@ -259,6 +268,22 @@ def attn_bwd_selected_index(problem, topk_indices, offsets, lists, order, worksp
     st = _L().attn_bwd_selected_index(problem.ref, _ptr(topk_indices), _ptr(offsets), _ptr(lists), _ptr(order),
                                      _ptr(workspace), wb, _stream(stream))
     _check(st, "attn_bwd_selected_index")
+
+
+def attn_bwd_indexer(problem, q, k, weights, dy, indices, dq, dk, dweights, workspace, workspace_bytes=None,
+                     stream=None):
+    wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = _L().attn_bwd_indexer(problem.ref, _ptr(q), _ptr(k), _ptr(weights), _ptr(dy), _ptr(indices), _ptr(dq),
+                              _ptr(dk), _ptr(dweights), _ptr(workspace), wb, _stream(stream))
+    _check(st, "attn_bwd_indexer")
+
+
+def indexer_backward(problem, q, k, weights, dy, indices, workspace=None, stream=None):
+    """Allocate dq, dk, dweights (and the workspace unless given) and run attn_bwd_indexer."""
+    dq, dk, dw = torch.empty_like(q), torch.empty_like(k), torch.empty_like(weights)
+    ws = workspace if workspace is not None else _workspace(problem, q.device)
+    attn_bwd_indexer(problem, q, k, weights, dy, indices, dq, dk, dw, ws, stream=stream)
+    return dq, dk, dw
 
 
 def attn_bwd_check_index_flag(problem, workspace, stream=None) -> bool:

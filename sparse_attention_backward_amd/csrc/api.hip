@@ -50,7 +50,7 @@ struct Plan {
   size_t off_cu_q = 0, off_cu_kv = 0, off_tab1 = 0, off_tab2 = 0, table_bytes = 0;
   size_t off_lse2 = 0, off_ndrow = 0;
   size_t off_counts = 0, off_offsets = 0, off_cursor = 0, off_list = 0, off_scratch = 0, off_flag = 0;
-  size_t off_dq_part = 0, off_wofs = 0, off_kvacc = 0;
+  size_t off_dq_part = 0, off_wofs = 0, off_kvacc = 0, off_dkacc = 0, off_contrib = 0;
   size_t off_qt_base = 0, off_qt_blk = 0, off_qt_kr = 0, off_ds = 0, off_kvsplit = 0, off_kvpart = 0;
   size_t total = 0;
 };
@@ -63,6 +63,7 @@ constexpr uint64_t kDenseDsAutoMax = 8ull << 30;  // stored dS above this size: 
 // restored; with skewed ids each window's longest list runs alone), so they are made as long
 // as the cap allows; the caller can ask for shorter ones (sel_window_tokens).
 constexpr uint64_t kSelShareMax = 64ull << 30;
+constexpr uint64_t kIdxContribMax = 8ull << 30;  // indexer, deterministic: dK shares of one window at most
 
 // Dense schedule tables.
 //  * Work items of the KV-major kernel: (sequence, 128-key tile, KV head, query-tile range,
@@ -187,7 +188,8 @@ void plan_dense_schedule(const attn_bwd_problem_t* p, Plan& pl) {
 
 attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   if (!p) return ATTN_ERR_NULLPTR;
-  if (p->op != ATTN_OP_DENSE && p->op != ATTN_OP_SELECTED && p->op != ATTN_OP_SELECTED_FWD) return ATTN_ERR_INVALID;
+  if (p->op != ATTN_OP_DENSE && p->op != ATTN_OP_SELECTED && p->op != ATTN_OP_SELECTED_FWD && p->op != ATTN_OP_INDEXER)
+    return ATTN_ERR_INVALID;
   if (p->batch < 1) return ATTN_ERR_INVALID;
   const int B = p->batch;
   if (p->layout == ATTN_LAYOUT_TND) {
@@ -218,7 +220,7 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   for (int b = 0; b < B; ++b)
     if (cq[b + 1] < cq[b] || ck[b + 1] < ck[b]) return ATTN_ERR_INVALID;
   if (p->n1 < 1 || p->n2 < 1 || p->n1 % p->n2 != 0) return ATTN_ERR_INVALID;
-  if (p->d_qk < 1 || p->d_v < 1 || p->d_rope < 0) return ATTN_ERR_INVALID;
+  if (p->d_qk < 1 || (p->d_v < 1 && p->op != ATTN_OP_INDEXER) || p->d_rope < 0) return ATTN_ERR_INVALID;
   if (!std::isfinite(p->scale)) return ATTN_ERR_INVALID;
   if ((p->causal != 0 && p->causal != 1) || (p->band != 0 && p->band != 1) ||
       (p->mask_align != 0 && p->mask_align != 1) || (p->deterministic != 0 && p->deterministic != 1) ||
@@ -257,6 +259,35 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     if (p->dtype == ATTN_FP32 && (dqk > 256 || p->d_v > 256)) return ATTN_ERR_UNSUPPORTED;
     if (p->dense_dq_mode < 0 || p->dense_dq_mode > 2 || p->sel_window_tokens != 0) return ATTN_ERR_INVALID;
     plan_dense_schedule(p, pl);
+  } else if (p->op == ATTN_OP_INDEXER) {
+    // lightning-indexer backward (readings of the page's lost shape table: bf16, D = 128,
+    // G <= 64, topK key tokens of the token's own sequence, S up to 128K, B up to 1024)
+    if (p->dtype != ATTN_BF16) return p->dtype == ATTN_FP16 || p->dtype == ATTN_FP32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
+    if (p->d_rope != 0 || p->causal != 0 || p->dense_dq_mode != 0 || p->band != 0 || p->mask_align != 0 ||
+        p->pre_tokens != 0 || p->next_tokens != 0 || p->d_v != 0 || p->block_size != 1 || p->dkdv_atomic != 0)
+      return ATTN_ERR_INVALID;
+    if (B > 1024 || p->n1 > 128 || pl.G > 64) return ATTN_ERR_INVALID;
+    const int topk = p->block_count;
+    if (topk < 1 || topk > kSelMaxS) return ATTN_ERR_INVALID;
+    pl.blkoff.assign(B + 1, 0);
+    for (int b = 0; b < B; ++b) {
+      const int64_t S1 = cq[b + 1] - cq[b], S2 = ck[b + 1] - ck[b];
+      if (S1 > kSelMaxS || S2 > kSelMaxS) return ATTN_ERR_INVALID;
+      if (S1 > 0 && S2 < topk) return ATTN_ERR_INVALID;  // S_K from topK up
+      pl.blkoff[b + 1] = (int32_t)ck[b + 1];  // one index = one key token
+    }
+    pl.nblk_total = (int)pl.T2;
+    if (!indexer_supported(p->d_qk, pl.G)) return ATTN_ERR_UNSUPPORTED;
+    pl.entries = pl.T1 * p->n2 * topk;
+    if (pl.entries >= (int64_t(1) << 31) || (int64_t)p->n2 * pl.T2 >= (int64_t(1) << 31)) return ATTN_ERR_UNSUPPORTED;
+    // deterministic mode: the fp32 dK shares of one window of query tokens take at most
+    // kIdxContribMax; windows of equal length but the last
+    if (p->sel_window_tokens < 0) return ATTN_ERR_INVALID;
+    const uint64_t per_token = (uint64_t)p->n2 * topk * p->d_qk * 4;
+    int64_t w = std::max<int64_t>(1, (int64_t)(kIdxContribMax / per_token));
+    if (p->sel_window_tokens > 0) w = std::min<int64_t>(w, p->sel_window_tokens);
+    pl.nwin = (int)std::max<int64_t>(1, (pl.T1 + w - 1) / w);
+    pl.win_tokens = std::max<int64_t>(1, (pl.T1 + pl.nwin - 1) / pl.nwin);
   } else {
     // selected backward and forward: BFLOAT16 or FLOAT16 (parameter table)
     if (p->dtype != ATTN_BF16 && p->dtype != ATTN_FP16) return ATTN_ERR_INVALID;
@@ -324,6 +355,23 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   if (p->op == ATTN_OP_SELECTED_FWD) {  // the forward needs the tables and the index flag only
     pl.off_flag = o;
     pl.total = align_up(o + 4);
+    return ATTN_OK;
+  }
+  if (p->op == ATTN_OP_INDEXER) {
+    const size_t nkeys = (size_t)p->n2 * pl.T2;
+    pl.off_flag = o;  o = align_up(o + 4);
+    pl.off_dkacc = o; o = align_up(o + 4 * nkeys * (size_t)p->d_qk);
+    if (p->deterministic) {
+      pl.off_counts = o;  o = align_up(o + 4 * nkeys);
+      pl.off_offsets = o; o = align_up(o + 4 * (nkeys + 1));
+      pl.off_cursor = o;  o = align_up(o + 4 * nkeys);
+      pl.off_list = o;    o = align_up(o + 4 * (size_t)pl.entries);
+      pl.off_scratch = o; o = align_up(o + 8 * (size_t)pl.entries);
+      pl.off_contrib = o;
+      o = align_up(o + 4 * (size_t)std::min<int64_t>(pl.win_tokens, pl.T1) * p->n2 * p->block_count * p->d_qk);
+      if (pl.nwin > 1) { pl.off_wofs = o; o = align_up(o + 4 * nkeys * (size_t)(pl.nwin + 1)); }
+    }
+    pl.total = o;
     return ATTN_OK;
   }
   const size_t rows = (size_t)pl.T1 * p->n1;
@@ -847,13 +895,89 @@ attn_status_t attn_bwd_selected_index(const attn_bwd_problem_t* p, const int32_t
   return ATTN_OK;
 }
 
+attn_status_t attn_bwd_indexer(const attn_bwd_problem_t* p, const void* q, const void* k, const void* weights,
+                               const void* dy, const int32_t* indices, void* dq, void* dk, void* dweights,
+                               void* workspace, uint64_t workspace_bytes, void* hip_stream) {
+  Plan pl;
+  attn_status_t st = validate_and_plan(p, pl);
+  if (st != ATTN_OK) return st;
+  if (p->op != ATTN_OP_INDEXER) return ATTN_ERR_INVALID;
+  const bool has_q = pl.T1 > 0, has_k = pl.T2 > 0;
+  if (has_q && (!q || !weights || !dy || !indices || !dq || !dweights)) return ATTN_ERR_NULLPTR;
+  if (has_k && (!k || !dk)) return ATTN_ERR_NULLPTR;
+  for (const void* ptr : {q, k, (const void*)dq, (const void*)dk}) if (misaligned(ptr)) return ATTN_ERR_INVALID;
+  for (const void* ptr : {weights, dy, (const void*)dweights, (const void*)indices})  // 2- and 4-byte elements
+    if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 3u)) return ATTN_ERR_INVALID;
+  if (!workspace || workspace_bytes < pl.total || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return ATTN_ERR_WORKSPACE;
+  if (!has_q && !has_k) return ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  TableStage tables;
+  if (tables.stage(pack_tables(p, pl)) != hipSuccess) return ATTN_ERR_HIP;
+  PreArgs pa{};  // no rows: the launch only copies the tables into the workspace
+  pa.tab_src = static_cast<const uint4*>(tables.src()); pa.tab_dst = static_cast<uint4*>(workspace);
+  pa.tab_n16 = tables.n16();
+  if (timed("tables", s, [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
+  IdxArgs a{};
+  a.q = q; a.k = k; a.weights = weights; a.dy = dy; a.indices = indices;
+  a.dq = dq; a.dk = dk; a.dweights = dweights;
+  a.dk_acc = at<float>(workspace, pl.off_dkacc);
+  a.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
+  a.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
+  a.flag = at<int32_t>(workspace, pl.off_flag);
+  a.batch = pl.B; a.n1 = p->n1; a.n2 = p->n2; a.G = pl.G; a.d = p->d_qk; a.topk = p->block_count;
+  a.T1 = pl.T1; a.T2 = pl.T2;
+  a.atomic = !p->deterministic;
+  a.nkeys = (int64_t)p->n2 * pl.T2;
+  if (launch_fill_i32(a.flag, 1, 0, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (timed("indexer_zero", s, [&] { return launch_indexer_zero(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  if (a.atomic) {
+    a.unit0 = 0;
+    a.unit1 = pl.T1 * p->n2;
+    if (timed("indexer_query_major", s, [&] { return launch_indexer_qm(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+  } else {
+    // the inverted index of the indices (one key per index) for the ordered dK sums
+    SelArgs x{};
+    x.topk = indices; x.cu_q = a.cu_q; x.blkoff = at<const int32_t>(workspace, pl.off_tab1);
+    x.batch = pl.B; x.n2 = p->n2; x.cnt = p->block_count; x.nblk_total = pl.nblk_total; x.T1 = pl.T1;
+    x.counts = at<int32_t>(workspace, pl.off_counts);
+    x.offsets = at<int32_t>(workspace, pl.off_offsets);
+    x.cursor = at<int32_t>(workspace, pl.off_cursor);
+    x.list = at<int32_t>(workspace, pl.off_list);
+    x.sort_scratch = at<int32_t>(workspace, pl.off_scratch);
+    x.flag = a.flag;
+    x.nwin = pl.nwin; x.win_tokens = pl.win_tokens;
+    x.wofs = pl.nwin > 1 ? at<int32_t>(workspace, pl.off_wofs) : nullptr;
+    if (timed("indexer_index", s, [&] {
+          const hipError_t e = launch_selected_index(x, s);
+          return e != hipSuccess ? e : launch_selected_window_offsets(x, s);
+        }) != hipSuccess)
+      return ATTN_ERR_HIP;
+    a.offsets = x.offsets; a.list = x.list; a.wofs = x.wofs; a.nwin = pl.nwin;
+    a.contrib = at<float>(workspace, pl.off_contrib);
+    for (int w = 0; w < pl.nwin; ++w) {
+      a.win = w;
+      const int64_t t0 = std::min<int64_t>(pl.T1, (int64_t)w * pl.win_tokens);
+      const int64_t t1 = std::min<int64_t>(pl.T1, t0 + pl.win_tokens);
+      a.unit0 = t0 * p->n2;
+      a.unit1 = t1 * p->n2;
+      if (timed("indexer_query_major", s, [&] { return launch_indexer_qm(a, s); }) != hipSuccess) return ATTN_ERR_HIP;
+      if (timed("indexer_dk_reduce", s, [&] { return launch_indexer_dk_reduce(a, s); }) != hipSuccess)
+        return ATTN_ERR_HIP;
+    }
+  }
+  return timed("indexer_dk_cast", s, [&] { return launch_indexer_dk_cast(a, s); }) == hipSuccess ? ATTN_OK
+                                                                                                  : ATTN_ERR_HIP;
+}
+
 attn_status_t attn_bwd_check_index_flag(const attn_bwd_problem_t* p, const void* workspace, int32_t* raised,
                                         void* hip_stream) {
   if (!raised || !workspace) return ATTN_ERR_NULLPTR;
   Plan pl;
   attn_status_t st = validate_and_plan(p, pl);
   if (st != ATTN_OK) return st;
-  if (p->op != ATTN_OP_SELECTED && p->op != ATTN_OP_SELECTED_FWD) return ATTN_ERR_INVALID;
+  if (p->op == ATTN_OP_DENSE) return ATTN_ERR_INVALID;
   int32_t h = 0;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   if (hipMemcpyAsync(&h, static_cast<const uint8_t*>(workspace) + pl.off_flag, 4, hipMemcpyDeviceToHost, s) !=

@@ -1,0 +1,317 @@
+// Lightning-indexer backward (page "aclnnLightningIndexerGrad", formula section):
+//   S  = ReLU(Q . Gather(K, Indices))          per query token t, key head n2, selected key k
+//   Y  = dy * Weights                          Y[t, h, k] = dy[t, n2, k] W[t, h]
+//   dW = Reduce(S * dy)                        dW[t, h] = sum_k S[t, h, k] dy[t, n2, k]
+//   dQ = ReluGrad(Y, S) . Gather(K, Indices)   R = Y where S > 0, else 0
+//   dK = ScatterAdd(ReluGrad(Y, S) . Q, Indices)
+// for the G = N1 / N2 query heads h of key head n2.
+//
+// Query-major: one workgroup (4 waves) per (token, key head).  The G heads are the columns
+// of the MFMA tiles (G padded to 16, 32 or 64; padding heads carry zero weights), and the
+// topK selected keys pass in chunks of 64, 16 per wave:
+//   S^T (keys x heads)  = K (A: the wave's 16 gathered key rows, 16 bytes per lane straight
+//                         from global memory) x Q^T (B: the head rows, resident);
+//   R^T                 = where(S^T > 0, dy W, 0); dW += S^T dy per head (lane);
+//   dQ^T (feat x heads) += K^T (A: column reads of the key rows, staged in LDS) x R^T (B: the
+//                         C tile as it stands, k = the 16 keys);
+//   C^T (feat x keys)   = Q^T (A: column reads of the Q tile in LDS) x R (B: column reads of
+//                         R^T written to LDS as [head][key]);  C is the key rows' share of dK.
+// C goes either to an fp32 accumulator with atomics (non-deterministic mode, the page's
+// default) or, row by row, to a contribution buffer indexed by (token, key head, slot) that
+// a second kernel sums over each key's inverted-index list in ascending order
+// (deterministic).  dQ (the four waves' partials added in LDS) and dW have one writer each.
+// An out-of-range index contributes nothing and raises the flag.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ab {
+
+namespace {
+
+constexpr int kIdxD = 128;    // head dim
+constexpr int kIdxChunk = 64; // keys per chunk (16 per wave)
+
+__device__ __forceinline__ float group_sum4(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+template <int NHT, bool ATOMIC>
+__global__ __launch_bounds__(256) void idx_bwd_kernel(IdxArgs a) {
+  constexpr int D = kIdxD, KS = D / 32, NF = D / 16;
+  constexpr int GP = 16 * NHT;                 // padded head count
+  using TQ = RowTile<D / 8>;                   // Q tile / key sub-tiles: rows of 256 bytes
+  constexpr int OQ = 0;                        // Q tile: GP rows (64-row tile)
+  constexpr int OK = TQ::BYTES;                // key rows: 4 waves x 16 rows (one 64-row tile)
+  constexpr int OR = OK + TQ::BYTES;           // R^T as [head][16 keys] bf16 per wave: GP x 32 bytes
+  constexpr int RB = GP * 32;
+  constexpr int SMEM_MAIN = OR + 4 * RB;
+  constexpr int SMEM_RED = 2 * NF * NHT * 64 * 16;  // dQ partials of two waves at a time
+  constexpr int SMEM = SMEM_MAIN > SMEM_RED ? SMEM_MAIN : SMEM_RED;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t unit = a.unit0 + blockIdx.x;     // (token, key head)
+  const int64_t t = unit / a.n2;
+  const int kvh = (int)(unit - t * a.n2);
+  const int b = seq_of(a.cu_q, a.batch, t);
+  const int64_t kv0 = a.cu_kv[b];
+  const int S2 = (int)(a.cu_kv[b + 1] - kv0);
+  const int G = a.G;
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  const uint16_t* wts = static_cast<const uint16_t*>(a.weights);
+  const uint16_t* dyp = static_cast<const uint16_t*>(a.dy);
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const int64_t qrow0 = t * a.n1 + (int64_t)kvh * G;  // first query head of the group
+
+  // Q tile in LDS (rows = heads, zero rows for padding heads) and Q^T B operands in registers
+  for (int i = tid; i < GP * (D / 8); i += 256) {
+    const int r = i / (D / 8), c = i % (D / 8);
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (r < G) x = ldg16(q + (qrow0 + r) * D + 8 * c);
+    lds_st16_at(smem_lds + OQ + TQ::off(r, c), x);
+  }
+  bf16x8 Qf[NHT][KS];
+  float wv[NHT];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int h = 16 * ht + l16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      Qf[ht][s] = __builtin_bit_cast(bf16x8, h < G ? ldg16(q + (qrow0 + h) * D + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0));
+    wv[ht] = h < G ? bf2f(wts[qrow0 + h]) : 0.f;
+  }
+  f32x4 dQ[NF][NHT];
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) dQ[f][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dW[NHT];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) dW[ht] = 0.f;
+  __syncthreads();  // Q tile in LDS
+
+  const uint32_t ksub = smem_lds + OK + 16 * w * TQ::RB;    // this wave's 16 key rows
+  const uint32_t rt = smem_lds + OR + w * RB;               // this wave's R^T [head][key]
+  const int32_t* ids = a.indices + unit * a.topk;
+  const uint16_t* dyrow = dyp + unit * a.topk;
+
+  for (int c0 = 0; c0 < a.topk; c0 += kIdxChunk) {
+    // this lane's key (for the A operand and the stores): slot c0 + 16 w + l16
+    const int slot = c0 + 16 * w + l16;
+    const int id = slot < a.topk ? ids[slot] : -1;
+    const bool kvalid = slot < a.topk && id >= 0 && id < S2;
+    if (slot < a.topk && !kvalid && a.flag) a.flag[0] = 1;
+    const int64_t krow = (kv0 + (kvalid ? id : 0)) * a.n2 + kvh;
+    uint4 kx[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kx[s] = kvalid ? ldg16(k + krow * D + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
+    // dy of the keys 4 g .. 4 g + 3 of the wave's 16 (the rows of this lane's S^T values)
+    float dyk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sl = c0 + 16 * w + 4 * g + j;
+      dyk[j] = sl < a.topk ? bf2f(dyrow[sl]) : 0.f;
+    }
+    // key rows into LDS: lane (l16, g) holds chunks 4 s + g of key row l16
+#pragma unroll
+    for (int s = 0; s < KS; ++s) lds_st16_at(ksub + TQ::off(l16, 4 * s + g), kx[s]);
+    // S^T = K Q^T
+    f32x4 St[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mfma_16x16x32(__builtin_bit_cast(bf16x8, kx[s]), Qf[ht][s], acc);
+      St[ht] = acc;
+    }
+    // R^T, dW, and R^T -> LDS as [head][key] (8 bytes: keys 4 g .. + 3 of head 16 ht + l16)
+    i16x4 Rb[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      f32x4 r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float s = St[ht][j];
+        dW[ht] += fmaxf(s, 0.f) * dyk[j];
+        r[j] = s > 0.f ? dyk[j] * wv[ht] : 0.f;
+      }
+      Rb[ht] = pack4(r);
+      *reinterpret_cast<__attribute__((address_space(3))) i16x4*>((uintptr_t)(rt + (16 * ht + l16) * 32 + 8 * g)) = Rb[ht];
+    }
+    asm volatile("" ::: "memory");  // LDS writes of this wave come before its transposed reads
+    // dQ^T += K^T R^T (k = the 16 keys: 4 per lane group)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const i16x4 kt = lds_tr16_at(ksub + TQ::colB(lane, f));
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) dQ[f][ht] = mfma_16x16x16(kt, Rb[ht], dQ[f][ht]);
+    }
+    // C^T = Q^T R (k = heads, 16 per step): this wave's 16 keys' shares of dK
+    i16x4 rk[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) rk[ht] = lds_tr16_at(rt + (16 * ht + 4 * g + (l16 >> 2)) * 32 + 8 * (l16 & 3));
+    // the C tile of feature tile f: lane holds key l16 of the wave, features 16 f + 4 g + (0..3)
+    const int cslot = c0 + 16 * w + l16;
+    const int cid = cslot < a.topk ? ids[cslot] : -1;
+    const bool cvalid = cslot < a.topk && cid >= 0 && cid < S2;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+        acc = mfma_16x16x16(lds_tr16_at(smem_lds + OQ + 16 * ht * TQ::RB + TQ::colB(lane, f)), rk[ht], acc);
+      if (cvalid) {
+        if constexpr (ATOMIC) {
+          float* dst = a.dk_acc + ((kv0 + cid) * a.n2 + kvh) * D + 16 * f + 4 * g;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) atomicAdd(dst + j, acc[j]);
+        } else {
+          float* dst = a.contrib + ((unit - a.unit0) * a.topk + cslot) * D + 16 * f + 4 * g;
+          *reinterpret_cast<f32x4*>(dst) = acc;
+        }
+      }
+    }
+    asm volatile("" ::: "memory");  // this chunk's LDS reads come before the next chunk's writes
+  }
+
+  // ---- dW: per head, over the lane groups and the four waves ----
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const float s = group_sum4(dW[ht]);
+    if (g == 0) red[w * GP + 16 * ht + l16] = s;
+  }
+  __syncthreads();
+  if (tid < G) {
+    const float s = (red[tid] + red[GP + tid]) + (red[2 * GP + tid] + red[3 * GP + tid]);
+    static_cast<uint16_t*>(a.dweights)[qrow0 + tid] = f2bf(s);
+  }
+  __syncthreads();
+  // ---- dQ: the four waves' partials added in LDS (waves 2, 3 then 1), then stored ----
+  // lane holds head 16 ht + l16, features 16 f + 4 g + (0..3) of tile (f, ht)
+  f32x4* part = reinterpret_cast<f32x4*>(smem);
+  auto pidx = [&](int f, int ht) { return (f * NHT + ht) * 64 + lane; };
+  if (w >= 2) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) part[(w - 2) * NF * NHT * 64 + pidx(f, ht)] = dQ[f][ht];
+  }
+  __syncthreads();
+  if (w < 2) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) dQ[f][ht] += part[w * NF * NHT * 64 + pidx(f, ht)];
+  }
+  __syncthreads();
+  if (w == 1) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) part[pidx(f, ht)] = dQ[f][ht];
+  }
+  __syncthreads();
+  if (w == 0) {
+    uint16_t* dq = static_cast<uint16_t*>(a.dq);
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + l16;
+      if (h >= G) continue;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const f32x4 v = dQ[f][ht] + part[pidx(f, ht)];
+        const uint2 o = make_uint2((uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                                   (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16));
+        *reinterpret_cast<uint2*>(dq + (qrow0 + h) * D + 16 * f + 4 * g) = o;
+      }
+    }
+  }
+}
+
+// Deterministic dK: one wave per key row (token j, key head); its list holds the entries
+// t topK + slot that selected it, ascending; the window's entries are added in that order to
+// the fp32 accumulator (two features per lane).
+__global__ __launch_bounds__(256) void idx_dk_reduce_kernel(IdxArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t key = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (key >= a.nkeys) return;  // whole wave
+  const int kvh = (int)(key / a.T2);
+  const int64_t j = key - (int64_t)kvh * a.T2;
+  const int e0 = a.nwin > 1 ? a.wofs[key * (a.nwin + 1) + a.win] : a.offsets[key];
+  const int e1 = a.nwin > 1 ? a.wofs[key * (a.nwin + 1) + a.win + 1] : a.offsets[key + 1];
+  if (e0 == e1) return;
+  float2 acc = *reinterpret_cast<const float2*>(a.dk_acc + (j * a.n2 + kvh) * kIdxD + 2 * lane);
+  for (int e = e0; e < e1; ++e) {
+    const int ent = a.list[e];  // t topK + slot
+    const int64_t t = ent / a.topk, slot = ent - t * a.topk;
+    const int64_t u = t * a.n2 + kvh - a.unit0;
+    const float2 c = *reinterpret_cast<const float2*>(a.contrib + (u * a.topk + slot) * kIdxD + 2 * lane);
+    acc.x += c.x;
+    acc.y += c.y;
+  }
+  *reinterpret_cast<float2*>(a.dk_acc + (j * a.n2 + kvh) * kIdxD + 2 * lane) = acc;
+}
+
+__global__ __launch_bounds__(256) void idx_dk_cast_kernel(const float* acc, uint16_t* dk, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dk[i] = f2bf(acc[i]);
+}
+
+__global__ __launch_bounds__(256) void idx_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+unsigned grid_of(int64_t n, int64_t per) {
+  int64_t g = (n + per - 1) / per;
+  return (unsigned)(g < 1 ? 1 : (g > 65536 ? 65536 : g));
+}
+
+}  // namespace
+
+bool indexer_supported(int d, int G) { return d == kIdxD && G >= 1 && G <= 64; }
+
+hipError_t launch_indexer_zero(const IdxArgs& a, hipStream_t s) {
+  const int64_t n = a.T2 * a.n2 * kIdxD;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(idx_zero_kernel, dim3(grid_of(n, 256)), dim3(256), 0, s, a.dk_acc, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_qm(const IdxArgs& a, hipStream_t s) {
+  const int64_t units = a.unit1 - a.unit0;
+  if (units <= 0) return hipSuccess;
+  if (!indexer_supported(a.d, a.G)) return hipErrorInvalidValue;
+  const IdxArgs& k = a;  // workgroup i takes unit unit0 + i
+  const dim3 grid((unsigned)units), block(256);
+  const int nht = a.G <= 16 ? 1 : (a.G <= 32 ? 2 : 4);
+#define AB_IDX(NHT)                                                                                            \
+  do {                                                                                                         \
+    if (a.atomic) hipLaunchKernelGGL((idx_bwd_kernel<NHT, true>), grid, block, 0, s, k);                       \
+    else hipLaunchKernelGGL((idx_bwd_kernel<NHT, false>), grid, block, 0, s, k);                               \
+  } while (0)
+  if (nht == 1) AB_IDX(1);
+  else if (nht == 2) AB_IDX(2);
+  else AB_IDX(4);
+#undef AB_IDX
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_dk_reduce(const IdxArgs& a, hipStream_t s) {
+  if (a.nkeys == 0) return hipSuccess;
+  hipLaunchKernelGGL(idx_dk_reduce_kernel, dim3(grid_of(a.nkeys, 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_dk_cast(const IdxArgs& a, hipStream_t s) {
+  const int64_t n = a.T2 * a.n2 * kIdxD;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(idx_dk_cast_kernel, dim3(grid_of(n, 256)), dim3(256), 0, s, (const float*)a.dk_acc,
+                     (uint16_t*)a.dk, n);
+  return hipGetLastError();
+}
+
+}  // namespace ab

@@ -153,6 +153,33 @@ struct SelFwdArgs {
 hipError_t launch_selected_forward(const SelFwdArgs& a, hipStream_t s);  // O, softmaxMax, softmaxSum
 hipError_t launch_selected_drow(const SelFwdArgs& a, hipStream_t s);     // ndrow without O
 
+// ---- lightning-indexer backward ------------------------------------------------
+struct IdxArgs {
+  const void* q;            // [T1, N1, D] bf16
+  const void* k;            // [T2, N2, D] bf16
+  const void* weights;      // [T1, N1] bf16
+  const void* dy;           // [T1, N2, topk] bf16
+  const int32_t* indices;   // [T1, N2, topk] key positions in the token's sequence
+  void* dq; void* dk; void* dweights;
+  float* dk_acc;            // [T2, N2, D] fp32 accumulator of dK
+  float* contrib;           // deterministic mode: [units of the window, topk, D] fp32 shares of dK
+  const int64_t* cu_q; const int64_t* cu_kv;
+  int32_t* flag;            // raised on an out-of-range index
+  int batch, n1, n2, G, d, topk;
+  int64_t T1, T2;
+  int64_t unit0, unit1;     // (token, key head) units t N2 + n2 of this launch
+  int atomic;               // 1: dK by fp32 atomics; 0: contributions + ordered reduction
+  // inverted index (deterministic mode): keys kvh T2 + j, lists of entries t topk + slot
+  const int32_t* offsets; const int32_t* list; const int32_t* wofs;
+  int64_t nkeys;
+  int nwin, win;
+};
+bool indexer_supported(int d, int G);
+hipError_t launch_indexer_zero(const IdxArgs& a, hipStream_t s);       // dk_acc = 0
+hipError_t launch_indexer_qm(const IdxArgs& a, hipStream_t s);         // dQ, dW and the dK shares
+hipError_t launch_indexer_dk_reduce(const IdxArgs& a, hipStream_t s);  // deterministic: shares -> dk_acc
+hipError_t launch_indexer_dk_cast(const IdxArgs& a, hipStream_t s);    // dk_acc -> dK (bf16)
+
 // ---- misc --------------------------------------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);  // kernel, not a memset node
 

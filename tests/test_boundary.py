@@ -309,3 +309,33 @@ def test_mask_fields_are_dense_only():
     d = dense(causal=False)
     d.s.pre_tokens = 4   # window sizes without the window flag
     assert status_ws(d)[0] == INVALID
+
+
+def _indexer(**kw):
+    base = dict(cu_q=[0, 96, 160], cu_kv=[0, 160, 290], n1=16, n2=1, topk=40)
+    base.update(kw)
+    return sab.Problem.indexer(base.pop("cu_q"), base.pop("cu_kv"), base.pop("n1"), base.pop("n2"), base.pop("topk"),
+                               **base)
+
+
+def test_indexer_validation():
+    assert status_ws(_indexer())[0] == OK
+    assert status_ws(_indexer(topk=200))[0] == INVALID            # a sequence holds fewer keys than topK
+    assert status_ws(_indexer(d=64))[0] == UNSUPPORTED           # D = 128 only
+    assert status_ws(_indexer(n1=128, n2=1))[0] == INVALID       # G <= 64
+    assert status_ws(_indexer(n1=6, n2=4))[0] == INVALID
+    p = _indexer()
+    p.s.block_size = 2
+    assert status_ws(p)[0] == INVALID                            # one key per index
+    p = _indexer()
+    p.s.dtype = sab.ATTN_FP16
+    assert status_ws(p)[0] == UNSUPPORTED
+    small = status_ws(_indexer(deterministic=True, window_tokens=8))[1]
+    big = status_ws(_indexer(deterministic=True))[1]
+    assert status_ws(_indexer())[1] < small < big                # the shares buffer is per window
+    args = [FAKE] * 8
+    n = status_ws(_indexer())[1]
+    assert sab.lib.attn_bwd_indexer(_indexer().ref, *args, FAKE, n - 1, None) == WORKSPACE
+    a = list(args); a[4] = None
+    assert sab.lib.attn_bwd_indexer(_indexer().ref, *a, FAKE, n, None) == NULLPTR
+    assert sab.lib.attn_bwd_indexer(selected().ref, *args, FAKE, n, None) == INVALID

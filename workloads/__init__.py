@@ -25,7 +25,8 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "config", "CONFIGS", "make_inputs", "cast", "small_dense", "small_selected"]
+__all__ = ["Workload", "config", "CONFIGS", "make_inputs", "cast", "small_dense", "small_selected",
+           "IndexerWorkload", "indexer_config", "small_indexer", "make_indexer_inputs"]
 
 
 @dataclass(frozen=True)
@@ -217,4 +218,85 @@ def make_inputs(w: Workload, device="cpu", backend="numpy"):
         out["topk"] = topk
     out["cu_q"] = torch.from_numpy(w.cu_q)
     out["cu_kv"] = torch.from_numpy(w.cu_kv)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# lightning-indexer backward inputs
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class IndexerWorkload:
+    name: str
+    seqlens_q: tuple
+    seqlens_kv: tuple
+    n1: int
+    n2: int
+    topk: int
+    d: int = 128
+    seed: int = 0
+
+    @property
+    def batch(self):
+        return len(self.seqlens_q)
+
+    @property
+    def T1(self):
+        return int(sum(self.seqlens_q))
+
+    @property
+    def T2(self):
+        return int(sum(self.seqlens_kv))
+
+    @property
+    def G(self):
+        return self.n1 // self.n2
+
+    @property
+    def cu_q(self):
+        return np.concatenate([[0], np.cumsum(self.seqlens_q)]).astype(np.int64)
+
+    @property
+    def cu_kv(self):
+        return np.concatenate([[0], np.cumsum(self.seqlens_kv)]).astype(np.int64)
+
+
+def indexer_config() -> IndexerWorkload:
+    """An indexer backward of one 8K sequence: 64 query heads over one key head, D 128, the
+    top 2048 keys of each token (seed 6)."""
+    return IndexerWorkload("indexer-bf16-S8K-N64-topk2048", (8192,), (8192,), 64, 1, 2048, seed=6)
+
+
+def small_indexer(seqlens=(96, 64), seqlens_kv=(160, 130), n1=16, n2=1, topk=40, seed=17):
+    return IndexerWorkload("indexer-small", tuple(seqlens), tuple(seqlens_kv), n1, n2, topk, seed=seed)
+
+
+def make_indexer_inputs(w: IndexerWorkload, device="cpu", backend="numpy"):
+    """q [T1, N1, D], k [T2, N2, D], weights [T1, N1], dy [T1, N2, topk] ~ N(0, 1) in bf16;
+    indices [T1, N2, topk] int32: topk distinct key positions of the token's own sequence,
+    uniform (prefix of a random permutation), drawn per (token, key head) in that order."""
+    T1, T2 = w.T1, w.T2
+    if backend == "numpy":
+        rng = np.random.default_rng([w.seed, 2])
+        draw = lambda shape: cast(_normal_np(rng, shape), "bf16", device)  # noqa: E731
+    else:
+        gen = torch.Generator(device=device)
+        gen.manual_seed(int(w.seed))
+        draw = lambda shape: _normal_torch(gen, shape, device).to(torch.bfloat16)  # noqa: E731
+    out = {"q": draw((T1, w.n1, w.d)), "k": draw((T2, w.n2, w.d)), "weights": draw((T1, w.n1)),
+           "dy": draw((T1, w.n2, w.topk))}
+    idx = torch.empty((T1, w.n2, w.topk), dtype=torch.int32, device=device)
+    cu_q, cu_kv = w.cu_q, w.cu_kv
+    for b in range(w.batch):
+        qs, qe = int(cu_q[b]), int(cu_q[b + 1])
+        n = int(cu_kv[b + 1] - cu_kv[b])
+        rows = (qe - qs) * w.n2
+        if rows == 0:
+            continue
+        if backend == "numpy":
+            ids = torch.from_numpy(_topk_rows_np(rng, rows, n, w.topk, "uniform", 0.0))
+        else:
+            ids = _topk_rows_torch(gen, rows, n, w.topk, "uniform", 0.0, device)
+        idx[qs:qe] = ids.to(device).reshape(qe - qs, w.n2, w.topk)
+    out["indices"] = idx
     return out
