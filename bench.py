@@ -476,14 +476,14 @@ def measure_forward(wl: int, steps: int, warmup: int, prewarm_ms=300.0):
     return rec
 
 
-def measure_indexer(deterministic: bool, steps: int, warmup: int, prewarm_ms=300.0):
+def measure_indexer(dk_atomic: bool, steps: int, warmup: int, prewarm_ms=300.0):
     """The lightning-indexer backward (attn_bwd_indexer) on its 8K workload: three GEMMs per
     (token, key head, selected key) -- S = Q K^T, dQ = R K, dK shares = R^T Q -- i.e.
     2 x 3 x G x D flop per (token, key head, slot)."""
     w = W.indexer_config()
     dev = torch.device("cuda", 0)
     x = W.make_indexer_inputs(w, device=dev, backend="torch")
-    prob = sab.Problem.indexer(w.cu_q, w.cu_kv, w.n1, w.n2, w.topk, d=w.d, deterministic=deterministic)
+    prob = sab.Problem.indexer(w.cu_q, w.cu_kv, w.n1, w.n2, w.topk, d=w.d, dk_atomic=dk_atomic)
     ws = torch.empty(max(1, sab.attn_bwd_workspace_size(prob)), dtype=torch.uint8, device=dev)
     dq, dk, dw = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["weights"])
     stream = torch.cuda.current_stream()
@@ -517,7 +517,7 @@ def measure_indexer(deterministic: bool, steps: int, warmup: int, prewarm_ms=300
     fl = w.T1 * w.n1 * w.topk * w.d * 6
     tot_ms, n = kernels["indexer_query_major"]
     kms = tot_ms / steps
-    rec = {"workload": w.name, "pass": "indexer backward", "deterministic": deterministic,
+    rec = {"workload": w.name, "pass": "indexer backward", "dk": "fp32 atomics" if dk_atomic else "ordered sums",
            "value": round(fl / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
            "steps": steps, "pct_bf16_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
            "roofline": {"kernel": "indexer_query_major", "bound": "mfma", "avg_ms": tot_ms / max(n, 1),
@@ -582,7 +582,7 @@ def main(argv=None):
         return 0
 
     if args.indexer_only:
-        print(json.dumps([measure_indexer(det, args.steps, args.warmup, args.prewarm_ms) for det in (False, True)]),
+        print(json.dumps([measure_indexer(a, args.steps, args.warmup, args.prewarm_ms) for a in (False, True)]),
               flush=True)
         return 0
     w, x, rec = measure(args.workload, args.steps, args.warmup, args.deterministic, args.window_tokens,
@@ -625,8 +625,8 @@ def main(argv=None):
             torch.cuda.empty_cache()
         for wl in FORWARD_RUNS:
             extra.append(measure_forward(wl, max(3, args.steps // 2), args.warmup, args.prewarm_ms))
-        for det in (False, True):
-            extra.append(measure_indexer(det, args.steps, args.warmup, args.prewarm_ms))
+        for atomic in (False, True):
+            extra.append(measure_indexer(atomic, args.steps, args.warmup, args.prewarm_ms))
         line["extra"] = extra
     print(json.dumps(line), flush=True)
     return 0

@@ -51,9 +51,9 @@
  *
  * Determinism: with deterministic = 1 the outputs are bitwise identical for
  * identical inputs, problem and device.  Both pages say the default is
- * non-deterministic and determinism can be enabled; every kernel behind this
- * interface happens to be deterministic in both modes unless
- * `dkdv_atomic` is set (see below).
+ * non-deterministic and determinism can be enabled; every path behind this
+ * interface is deterministic in both modes except the indexer's dK with
+ * `dkdv_atomic` = 1 (see below).
  */
 #ifndef ATTN_BWD_H_
 #define ATTN_BWD_H_
@@ -114,10 +114,14 @@ typedef struct {
   int32_t block_size;             /* selected: selectedBlockSize (<= 128, multiple of 16)  */
   int32_t block_count;            /* selected: selectedBlockCount (1..128, count*size < 8192)*/
   int32_t deterministic;          /* 1 = bitwise reproducible                               */
-  int32_t dkdv_atomic;            /* selected only: 1 = scatter dK/dV with fp32 atomics from
-                                     the query-major pass (non-deterministic; needs a larger
-                                     workspace); 0 = inverted-index KV-major pass.
-                                     Ignored (treated as 0) when deterministic = 1.          */
+  int32_t dkdv_atomic;            /* indexer: 1 = scatter dK with fp32 atomics from the
+                                     query-major pass (non-deterministic, smaller workspace);
+                                     0 = sum each key row's shares in a fixed order through an
+                                     inverted index (faster on the 8K / topK 2048 workload:
+                                     7.8 ms against 27.5 ms).  Ignored (treated as 0) when
+                                     deterministic = 1.  Selected and selected-forward: reserved,
+                                     1 with deterministic = 0 returns ATTN_ERR_UNSUPPORTED.
+                                     Dense: must be 0.                                        */
   int32_t dense_dq_mode;          /* dense bf16 only (0 for every other problem): how dQ is
                                      formed.  1 = the KV-major pass stores dS (bf16, 8 KiB per
                                      64 x 64 (query tile, key tile) block and query head, in the
@@ -243,11 +247,12 @@ attn_status_t attn_bwd_selected_index(const attn_bwd_problem_t* p, const int32_t
  * weights [T1, n1], dy [T1, n2, topK]; indices int32 [T1, n2, topK] (key positions inside
  * the token's sequence; a repeated index counts twice; an out-of-range one contributes
  * nothing and raises the flag of attn_bwd_check_index_flag); outputs dq [T1, n1, 128],
- * dk [T2, n2, 128], dweights [T1, n1].  deterministic = 0 (the page's default): dK by fp32
- * atomics; deterministic = 1: each (token, key head, slot)'s share of dK is kept and the
- * shares of a key row are added in ascending (token, slot) order through an inverted index,
- * over windows of query tokens whose shares take at most 8 GiB (sel_window_tokens caps the
- * window further).  dQ and dW have one writer per row in both modes. */
+ * dk [T2, n2, 128], dweights [T1, n1].  dK: by default each (token, key head, slot)'s fp32
+ * share of dK is kept and the shares of a key row are added in ascending (token, slot) order
+ * through an inverted index, over windows of query tokens whose shares take at most 8 GiB
+ * (sel_window_tokens caps the window further) -- deterministic whatever `deterministic` says;
+ * dkdv_atomic = 1 with deterministic = 0 scatters the shares with fp32 atomics instead.
+ * dQ and dW have one writer per row in every mode. */
 attn_status_t attn_bwd_indexer(const attn_bwd_problem_t* p,
                                const void* q, const void* k, const void* weights, const void* dy,
                                const int32_t* indices,

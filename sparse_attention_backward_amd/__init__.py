@@ -173,11 +173,13 @@ class Problem:
                    deterministic=deterministic, dkdv_atomic=dkdv_atomic, window_tokens=window_tokens, bsnd=bsnd)
 
     @classmethod
-    def indexer(cls, cu_q, cu_kv, n1, n2, topk, d=128, deterministic=False, window_tokens=0, bsnd=None):
+    def indexer(cls, cu_q, cu_kv, n1, n2, topk, d=128, deterministic=False, window_tokens=0, bsnd=None,
+                dk_atomic=False):
         """The lightning-indexer backward's problem (op ATTN_OP_INDEXER): topk indices per
-        (token, key head), head dim d, bf16."""
+        (token, key head), head dim d, bf16.  dk_atomic (with deterministic False): dK by fp32
+        atomics instead of the ordered sums."""
         return cls(ATTN_OP_INDEXER, ATTN_BF16, cu_q, cu_kv, n1, n2, d, 0, 1.0, block_size=1, block_count=topk,
-                   deterministic=deterministic, window_tokens=window_tokens, bsnd=bsnd)
+                   deterministic=deterministic, dkdv_atomic=dk_atomic, window_tokens=window_tokens, bsnd=bsnd)
 
     @property
     def ref(self):

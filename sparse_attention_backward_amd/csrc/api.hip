@@ -46,6 +46,7 @@ struct Plan {
   int64_t entries = 0;
   int nwin = 1;              // windows of query tokens (dQ shares of one window in the workspace)
   int64_t win_tokens = 0;
+  bool idx_atomic = false;    // indexer: dK by fp32 atomics (asked for, non-deterministic)
   // workspace layout (byte offsets)
   size_t off_cu_q = 0, off_cu_kv = 0, off_tab1 = 0, off_tab2 = 0, table_bytes = 0;
   size_t off_lse2 = 0, off_ndrow = 0;
@@ -257,15 +258,17 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     const int dqk = p->d_qk + p->d_rope;
     if (p->dtype == ATTN_BF16 && !dense_bf16_supported(p->d_qk, p->d_rope, p->d_v)) return ATTN_ERR_UNSUPPORTED;
     if (p->dtype == ATTN_FP32 && (dqk > 256 || p->d_v > 256)) return ATTN_ERR_UNSUPPORTED;
-    if (p->dense_dq_mode < 0 || p->dense_dq_mode > 2 || p->sel_window_tokens != 0) return ATTN_ERR_INVALID;
+    if (p->dense_dq_mode < 0 || p->dense_dq_mode > 2 || p->sel_window_tokens != 0 || p->dkdv_atomic != 0)
+      return ATTN_ERR_INVALID;
     plan_dense_schedule(p, pl);
   } else if (p->op == ATTN_OP_INDEXER) {
     // lightning-indexer backward (readings of the page's lost shape table: bf16, D = 128,
     // G <= 64, topK key tokens of the token's own sequence, S up to 128K, B up to 1024)
     if (p->dtype != ATTN_BF16) return p->dtype == ATTN_FP16 || p->dtype == ATTN_FP32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
     if (p->d_rope != 0 || p->causal != 0 || p->dense_dq_mode != 0 || p->band != 0 || p->mask_align != 0 ||
-        p->pre_tokens != 0 || p->next_tokens != 0 || p->d_v != 0 || p->block_size != 1 || p->dkdv_atomic != 0)
+        p->pre_tokens != 0 || p->next_tokens != 0 || p->d_v != 0 || p->block_size != 1)
       return ATTN_ERR_INVALID;
+    pl.idx_atomic = p->dkdv_atomic != 0 && p->deterministic == 0;
     if (B > 1024 || p->n1 > 128 || pl.G > 64) return ATTN_ERR_INVALID;
     const int topk = p->block_count;
     if (topk < 1 || topk > kSelMaxS) return ATTN_ERR_INVALID;
@@ -361,7 +364,7 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     const size_t nkeys = (size_t)p->n2 * pl.T2;
     pl.off_flag = o;  o = align_up(o + 4);
     pl.off_dkacc = o; o = align_up(o + 4 * nkeys * (size_t)p->d_qk);
-    if (p->deterministic) {
+    if (!pl.idx_atomic) {
       pl.off_counts = o;  o = align_up(o + 4 * nkeys);
       pl.off_offsets = o; o = align_up(o + 4 * (nkeys + 1));
       pl.off_cursor = o;  o = align_up(o + 4 * nkeys);
@@ -928,7 +931,7 @@ attn_status_t attn_bwd_indexer(const attn_bwd_problem_t* p, const void* q, const
   a.flag = at<int32_t>(workspace, pl.off_flag);
   a.batch = pl.B; a.n1 = p->n1; a.n2 = p->n2; a.G = pl.G; a.d = p->d_qk; a.topk = p->block_count;
   a.T1 = pl.T1; a.T2 = pl.T2;
-  a.atomic = !p->deterministic;
+  a.atomic = pl.idx_atomic;
   a.nkeys = (int64_t)p->n2 * pl.T2;
   if (launch_fill_i32(a.flag, 1, 0, s) != hipSuccess) return ATTN_ERR_HIP;
   if (timed("indexer_zero", s, [&] { return launch_indexer_zero(a, s); }) != hipSuccess) return ATTN_ERR_HIP;

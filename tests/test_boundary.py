@@ -330,11 +330,20 @@ def test_indexer_validation():
     p = _indexer()
     p.s.dtype = sab.ATTN_FP16
     assert status_ws(p)[0] == UNSUPPORTED
-    small = status_ws(_indexer(deterministic=True, window_tokens=8))[1]
-    big = status_ws(_indexer(deterministic=True))[1]
-    assert status_ws(_indexer())[1] < small < big                # the shares buffer is per window
+    small = status_ws(_indexer(window_tokens=8))[1]
+    big = status_ws(_indexer())[1]
+    atomic = status_ws(_indexer(dk_atomic=True))[1]
+    assert atomic < small < big                                  # the shares buffer is per window
+    assert status_ws(_indexer(deterministic=True))[1] == big
+    assert status_ws(_indexer(deterministic=True, dk_atomic=True))[1] == big   # atomics off when deterministic
+    d = dense()
+    d.s.dkdv_atomic = 1
+    assert status_ws(d)[0] == INVALID
+    s = selected()
+    s.s.dkdv_atomic = 1
+    assert status_ws(s)[0] == UNSUPPORTED
     args = [FAKE] * 8
-    n = status_ws(_indexer())[1]
+    n = big
     assert sab.lib.attn_bwd_indexer(_indexer().ref, *args, FAKE, n - 1, None) == WORKSPACE
     a = list(args); a[4] = None
     assert sab.lib.attn_bwd_indexer(_indexer().ref, *a, FAKE, n, None) == NULLPTR

@@ -1,5 +1,6 @@
 """GPU parity of the lightning-indexer backward (attn_bwd_indexer) against the float64 oracle
-(oracle/indexer.py), in both determinism modes.
+(oracle/indexer.py), in its three modes: ordered dK sums (deterministic 0 or 1) and fp32
+atomics (dk_atomic).
 
 The ReLU mask is a decision taken on S: the kernel forms S in fp32 from bf16 inputs, the
 oracle in float64, so a score within rounding of 0 could fall on different sides.  Such
@@ -37,15 +38,15 @@ def _inputs(w):
     return x
 
 
-def _run(w, deterministic, window_tokens=0, x=None):
+def _run(w, deterministic, window_tokens=0, x=None, dk_atomic=False):
     x = x if x is not None else _inputs(w)
     dev = torch.device("cuda", 0)
     g = lambda t: t.to(dev).contiguous()  # noqa: E731
     prob = sab.Problem.indexer(w.cu_q, w.cu_kv, w.n1, w.n2, w.topk, deterministic=deterministic,
-                               window_tokens=window_tokens)
+                               window_tokens=window_tokens, dk_atomic=dk_atomic)
     ws = torch.empty(max(1, sab.attn_bwd_workspace_size(prob)), dtype=torch.uint8, device=dev)
     print(f"[indexer] seqlens={w.seqlens_q}/{w.seqlens_kv} n1={w.n1} n2={w.n2} topk={w.topk} "
-          f"det={deterministic} window_tokens={window_tokens}", flush=True)
+          f"det={deterministic} atomic={dk_atomic} window_tokens={window_tokens}", flush=True)
     dq, dk, dw = sab.indexer_backward(prob, g(x["q"]), g(x["k"]), g(x["weights"]), g(x["dy"]), g(x["indices"]), ws)
     torch.cuda.synchronize()
     return x, (dq, dk, dw), sab.attn_bwd_check_index_flag(prob, ws)
@@ -69,11 +70,11 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("mode", ["default", "deterministic", "atomic"])
 @pytest.mark.parametrize("kw", SHAPES)
-def test_indexer(kw, deterministic):
+def test_indexer(kw, mode):
     w = W.small_indexer(**kw)
-    x, got, raised = _run(w, deterministic)
+    x, got, raised = _run(w, mode == "deterministic", dk_atomic=mode == "atomic")
     assert not raised
     _check(w, x, got)
 
@@ -99,8 +100,8 @@ def test_indexer_repeated_and_out_of_range_indices():
     _check(w, x, got)
     bad = {k: v.clone() for k, v in x.items()}
     bad["indices"][7, 0, 3] = 100                          # sequence of 100 keys
-    for det in (False, True):
-        _, got, raised = _run(w, det, x=bad)
+    for det, atomic in ((False, True), (True, False)):
+        _, got, raised = _run(w, det, x=bad, dk_atomic=atomic)
         assert raised
         for t in got:
             assert torch.isfinite(t.float()).all()
