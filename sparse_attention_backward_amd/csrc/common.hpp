@@ -28,6 +28,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
@@ -60,6 +61,9 @@ __device__ __forceinline__ f16x8 lds_f16x8_at(uint32_t addr) {
 }
 __device__ __forceinline__ f32x4 lds_f32x4_at(uint32_t addr) {
   return *reinterpret_cast<const lds_f32x4*>((uintptr_t)addr);
+}
+__device__ __forceinline__ float lds_f32_at(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>((uintptr_t)addr);
 }
 __device__ __forceinline__ i16x4 lds_tr16_at(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>((uintptr_t)addr));

@@ -37,7 +37,7 @@ __device__ __forceinline__ float group_sum4(float x) {
 }
 
 template <int NHT, bool ATOMIC>
-__global__ __launch_bounds__(256) void idx_bwd_kernel(IdxArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void idx_bwd_kernel(IdxArgs a) {
   constexpr int D = kIdxD, KS = D / 32, NF = D / 16;
   constexpr int GP = 16 * NHT;                 // padded head count
   using TQ = RowTile<D / 8>;                   // Q tile / key sub-tiles: rows of 256 bytes
@@ -66,21 +66,18 @@ __global__ __launch_bounds__(256) void idx_bwd_kernel(IdxArgs a) {
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const int64_t qrow0 = t * a.n1 + (int64_t)kvh * G;  // first query head of the group
 
-  // Q tile in LDS (rows = heads, zero rows for padding heads) and Q^T B operands in registers
+  // Q tile in LDS (rows = heads, zero rows for padding heads): the B operands of S^T (row
+  // reads) and the A operands of C^T (column reads)
   for (int i = tid; i < GP * (D / 8); i += 256) {
     const int r = i / (D / 8), c = i % (D / 8);
     uint4 x = make_uint4(0, 0, 0, 0);
     if (r < G) x = ldg16(q + (qrow0 + r) * D + 8 * c);
     lds_st16_at(smem_lds + OQ + TQ::off(r, c), x);
   }
-  bf16x8 Qf[NHT][KS];
   float wv[NHT];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
     const int h = 16 * ht + l16;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      Qf[ht][s] = __builtin_bit_cast(bf16x8, h < G ? ldg16(q + (qrow0 + h) * D + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0));
     wv[ht] = h < G ? bf2f(wts[qrow0 + h]) : 0.f;
   }
   f32x4 dQ[NF][NHT];
@@ -124,7 +121,9 @@ __global__ __launch_bounds__(256) void idx_bwd_kernel(IdxArgs a) {
     for (int ht = 0; ht < NHT; ++ht) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) acc = mfma_16x16x32(__builtin_bit_cast(bf16x8, kx[s]), Qf[ht][s], acc);
+      for (int s = 0; s < KS; ++s)
+        acc = mfma_16x16x32(__builtin_bit_cast(bf16x8, kx[s]), lds_b128_at(smem_lds + OQ + 16 * ht * TQ::RB + TQ::rowA(lane, s)),
+                            acc);
       St[ht] = acc;
     }
     // R^T, dW, and R^T -> LDS as [head][key] (8 bytes: keys 4 g .. + 3 of head 16 ht + l16)
@@ -153,24 +152,42 @@ __global__ __launch_bounds__(256) void idx_bwd_kernel(IdxArgs a) {
     i16x4 rk[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) rk[ht] = lds_tr16_at(rt + (16 * ht + 4 * g + (l16 >> 2)) * 32 + 8 * (l16 & 3));
-    // the C tile of feature tile f: lane holds key l16 of the wave, features 16 f + 4 g + (0..3)
+    // The C tiles go out through this wave's key-row slot of LDS (4 KiB, free once the dQ
+    // product has read it), 64 features at a time as [16 keys][16 chunks of 16 B] with chunk c
+    // of row r at c ^ r, so that every global store or atomic covers whole key rows instead
+    // of 16 rows x 64 bytes.  C tile of feature tile f: lane holds key l16 of the wave,
+    // features 16 f + 4 g + (0..3).
     const int cslot = c0 + 16 * w + l16;
     const int cid = cslot < a.topk ? ids[cslot] : -1;
-    const bool cvalid = cslot < a.topk && cid >= 0 && cid < S2;
+    const int cvalid = cslot < a.topk && cid >= 0 && cid < S2;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht)
-        acc = mfma_16x16x16(lds_tr16_at(smem_lds + OQ + 16 * ht * TQ::RB + TQ::colB(lane, f)), rk[ht], acc);
-      if (cvalid) {
-        if constexpr (ATOMIC) {
-          float* dst = a.dk_acc + ((kv0 + cid) * a.n2 + kvh) * D + 16 * f + 4 * g;
+      for (int f4 = 0; f4 < 4; ++f4) {
+        const int f = 4 * hf + f4;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) atomicAdd(dst + j, acc[j]);
-        } else {
-          float* dst = a.contrib + ((unit - a.unit0) * a.topk + cslot) * D + 16 * f + 4 * g;
-          *reinterpret_cast<f32x4*>(dst) = acc;
+        for (int ht = 0; ht < NHT; ++ht)
+          acc = mfma_16x16x16(lds_tr16_at(smem_lds + OQ + 16 * ht * TQ::RB + TQ::colB(lane, f)), rk[ht], acc);
+        lds_st16_at(ksub + l16 * 256 + 16 * ((4 * f4 + g) ^ l16), __builtin_bit_cast(uint4, acc));
+      }
+      if constexpr (ATOMIC) {
+        // one key row per instruction: lane = feature 64 hf + lane
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rid = __shfl(cid, r);
+          const float v = lds_f32_at(ksub + r * 256 + 16 * ((lane >> 2) ^ r) + 4 * (lane & 3));
+          if (__shfl(cvalid, r)) atomicAdd(a.dk_acc + ((kv0 + rid) * a.n2 + kvh) * D + 64 * hf + lane, v);
+        }
+      } else {
+        // four key rows per instruction: lane = row 4 i + lane / 16, chunk lane % 16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * i + (lane >> 4), c = lane & 15;
+          const f32x4 v = lds_f32x4_at(ksub + r * 256 + 16 * (c ^ r));
+          const int sl = c0 + 16 * w + r;
+          if (sl < a.topk)
+            sts16_stream(a.contrib + ((unit - a.unit0) * a.topk + sl) * D + 64 * hf + 4 * c, __builtin_bit_cast(uint4, v));
         }
       }
     }
@@ -246,13 +263,27 @@ __global__ __launch_bounds__(256) void idx_dk_reduce_kernel(IdxArgs a) {
   const int e1 = a.nwin > 1 ? a.wofs[key * (a.nwin + 1) + a.win + 1] : a.offsets[key + 1];
   if (e0 == e1) return;
   float2 acc = *reinterpret_cast<const float2*>(a.dk_acc + (j * a.n2 + kvh) * kIdxD + 2 * lane);
-  for (int e = e0; e < e1; ++e) {
-    const int ent = a.list[e];  // t topK + slot
+  // the share of list entry `ent` (t topK + slot): read once, so not kept in the caches
+  auto share = [&](int ent) {
     const int64_t t = ent / a.topk, slot = ent - t * a.topk;
     const int64_t u = t * a.n2 + kvh - a.unit0;
-    const float2 c = *reinterpret_cast<const float2*>(a.contrib + (u * a.topk + slot) * kIdxD + 2 * lane);
-    acc.x += c.x;
-    acc.y += c.y;
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(a.contrib + (u * a.topk + slot) * kIdxD + 2 * lane));
+  };
+  int e = e0;
+  for (; e + 8 <= e1; e += 8) {  // eight loads in flight, added in list order
+    f32x2 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = share(a.list[e + i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc.x += c[i][0];
+      acc.y += c[i][1];
+    }
+  }
+  for (; e < e1; ++e) {
+    const f32x2 c = share(a.list[e]);
+    acc.x += c[0];
+    acc.y += c[1];
   }
   *reinterpret_cast<float2*>(a.dk_acc + (j * a.n2 + kvh) * kIdxD + 2 * lane) = acc;
 }
