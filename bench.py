@@ -72,7 +72,7 @@ KERNEL_SOURCES = {
     "dense_dq_recompute": ("dense_dq_kernel", "attn_q.hip"),
     "selected_kv_major": ("sel_kv_kernel", "sel_kv.hip"),
     "selected_dq_reduce": ("dq_reduce_kernel", "sel_reduce.hip"),
-    "selected_forward": ("sel_fwd_kernel", "sel_fwd.hip"),
+    "selected_forward": ("sel_fwd_kv_kernel", "sel_fwd_kv.hip"),
     "indexer_query_major": ("idx_bwd_kernel", "indexer.hip"),
     "row_stats": ("preprocess_kernel", "preprocess.hip"),
 }
@@ -460,16 +460,21 @@ def measure_forward(wl: int, steps: int, warmup: int, prewarm_ms=300.0):
     fl = attended_pairs(w) * flops_per_pair(w, ("S", "O"))
     tot_ms, n = kernels["selected_forward"]
     kms = tot_ms / steps
-    # what the query-major design moves: the gathered key and value rows, per (token, KV head, key row)
-    gather = w.T1 * w.n2 * w.block_count * w.block_size * (w.d_qk + w.d_v) * (2 if w.dtype != "fp32" else 4)
+    launches = n / max(steps, 1)
+    # what the KV-major pass moves per (token, KV head, slot): the G query rows gathered and the
+    # entry's partial (G d_v elements + G (m_b, l_b)) written
+    e = 2 if w.dtype != "fp32" else 4
+    gather = w.T1 * w.n2 * w.block_count * w.G * (w.d_qk * e + w.d_v * e + 8)
     rec = {"workload": w.name, "pass": "forward", "value": round(fl / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
            "ms_per_step": round(ms, 4), "steps": steps,
            "pct_bf16_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
            "roofline": {"kernel": "selected_forward", "bound": "mfma", "avg_ms": tot_ms / max(n, 1),
                         "achieved": fl / (kms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": fl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop_per_launch": fl,
+                        "frac": fl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop_per_launch": fl / max(launches, 1e-9),
+                        "launches_per_call": launches,
                         "traffic": recorded_counters("selected_forward", w.name).get("traffic_bytes_per_launch"),
-                        "gather_bytes_per_launch": gather, "gather_gbs": gather / (kms * 1e-3) / 1e9},
+                        "kv_pass_bytes_per_call": gather, "kv_pass_gbs": gather / (kms * 1e-3) / 1e9},
+           "kernels_ms_per_call": {k: round(v[0] / steps, 4) for k, v in kernels.items()},
            "prewarm_ms": round(spent, 1)}
     del x, out, smax, ssum, ws
     torch.cuda.empty_cache()
@@ -549,6 +554,8 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' lines")
     ap.add_argument("--indexer-only", action="store_true",
                     help="only the lightning-indexer backward lines (for profiling runs)")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="only the selected forward lines (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 5 times (counter calibration)")
@@ -581,6 +588,10 @@ def main(argv=None):
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
         return 0
 
+    if args.forward_only:
+        print(json.dumps([measure_forward(wl, args.steps, args.warmup, args.prewarm_ms) for wl in FORWARD_RUNS]),
+              flush=True)
+        return 0
     if args.indexer_only:
         print(json.dumps([measure_indexer(a, args.steps, args.warmup, args.prewarm_ms) for a in (False, True)]),
               flush=True)

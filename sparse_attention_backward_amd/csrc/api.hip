@@ -49,7 +49,7 @@ struct Plan {
   bool idx_atomic = false;    // indexer: dK by fp32 atomics (asked for, non-deterministic)
   // workspace layout (byte offsets)
   size_t off_cu_q = 0, off_cu_kv = 0, off_tab1 = 0, off_tab2 = 0, table_bytes = 0;
-  size_t off_lse2 = 0, off_ndrow = 0;
+  size_t off_lse2 = 0, off_ndrow = 0, off_ml = 0;
   size_t off_counts = 0, off_offsets = 0, off_cursor = 0, off_list = 0, off_scratch = 0, off_flag = 0;
   size_t off_dq_part = 0, off_wofs = 0, off_kvacc = 0, off_dkacc = 0, off_contrib = 0;
   size_t off_qt_base = 0, off_qt_blk = 0, off_qt_kr = 0, off_ds = 0, off_kvsplit = 0, off_kvpart = 0;
@@ -320,11 +320,13 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     pl.entries = pl.T1 * p->n2 * cnt;
     if (pl.entries >= (int64_t(1) << 31) || (int64_t)p->n2 * pl.nblk_total >= (int64_t(1) << 31))
       return ATTN_ERR_UNSUPPORTED;
-    // Windows of query tokens: the shares of one window (cnt N1 d_qk bf16 per token) stay within
+    // Windows of query tokens: the backward's dQ shares of one window (cnt N1 d_qk elements per
+    // token), or the forward's partials (cnt N1 (d_v elements + 8 bytes) per token), stay within
     // kSelShareMax; the caller may ask for smaller windows.  Windows are of equal length but
     // the last.
     if (p->sel_window_tokens < 0) return ATTN_ERR_INVALID;
-    const uint64_t share_per_token = (uint64_t)cnt * p->n1 * p->d_qk * 2;
+    const uint64_t share_per_token = p->op == ATTN_OP_SELECTED_FWD ? (uint64_t)cnt * p->n1 * (p->d_v * 2 + 8)
+                                                                   : (uint64_t)cnt * p->n1 * p->d_qk * 2;
     int64_t w = std::max<int64_t>(1, (int64_t)(kSelShareMax / share_per_token));
     if (p->sel_window_tokens > 0) w = std::min<int64_t>(w, p->sel_window_tokens);
     pl.nwin = (int)std::max<int64_t>(1, (pl.T1 + w - 1) / w);
@@ -355,9 +357,19 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
   }
   pl.table_bytes = o;
   o = align_up(o);
-  if (p->op == ATTN_OP_SELECTED_FWD) {  // the forward needs the tables and the index flag only
-    pl.off_flag = o;
-    pl.total = align_up(o + 4);
+  if (p->op == ATTN_OP_SELECTED_FWD) {  // the inverted index and the partials of one window
+    const size_t nkeys = (size_t)p->n2 * pl.nblk_total;
+    const size_t prow = (size_t)std::min<int64_t>(pl.win_tokens, pl.T1) * p->block_count * p->n1;  // (entry, head)
+    pl.off_flag = o;    o = align_up(o + 4);
+    pl.off_counts = o;  o = align_up(o + 4 * nkeys);
+    pl.off_offsets = o; o = align_up(o + 4 * (nkeys + 1));
+    pl.off_cursor = o;  o = align_up(o + 4 * nkeys);
+    pl.off_list = o;    o = align_up(o + 4 * (size_t)pl.entries);
+    pl.off_scratch = o; o = align_up(o + 8 * (size_t)pl.entries);
+    pl.off_dq_part = o; o = align_up(o + 2 * prow * p->d_v);  // O_b / l_b
+    pl.off_ml = o;      o = align_up(o + 8 * prow);           // (m_b, l_b)
+    if (pl.nwin > 1) { pl.off_wofs = o; o = align_up(o + 4 * nkeys * (size_t)(pl.nwin + 1)); }
+    pl.total = o;
     return ATTN_OK;
   }
   if (p->op == ATTN_OP_INDEXER) {
@@ -846,17 +858,48 @@ attn_status_t attn_fwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   pa.tab_n16 = tables.n16();
   if (timed("tables", s, [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
   if (tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
+  // the inverted index of the ids: the KV-major pass walks each block's list
+  SelArgs x{};
+  x.topk = topk_indices;
+  x.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
+  x.blkoff = at<const int32_t>(workspace, pl.off_tab1);
+  x.batch = pl.B; x.n2 = p->n2; x.cnt = p->block_count; x.nblk_total = pl.nblk_total; x.T1 = pl.T1;
+  x.counts = at<int32_t>(workspace, pl.off_counts);
+  x.offsets = at<int32_t>(workspace, pl.off_offsets);
+  x.cursor = at<int32_t>(workspace, pl.off_cursor);
+  x.list = at<int32_t>(workspace, pl.off_list);
+  x.sort_scratch = at<int32_t>(workspace, pl.off_scratch);
+  x.flag = flag;
+  x.nwin = pl.nwin; x.win_tokens = pl.win_tokens;
+  x.wofs = pl.nwin > 1 ? at<int32_t>(workspace, pl.off_wofs) : nullptr;
+  if (timed("selected_index", s, [&] {
+        const hipError_t e = launch_selected_index(x, s);
+        return e != hipSuccess ? e : launch_selected_window_offsets(x, s);
+      }) != hipSuccess)
+    return ATTN_ERR_HIP;
   SelFwdArgs f{};
   f.q = q; f.k = k; f.v = v; f.topk = topk_indices;
-  f.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
+  f.cu_q = x.cu_q;
   f.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
   f.o = out; f.smax = softmax_max; f.ssum = softmax_sum; f.flag = flag;
   f.batch = pl.B; f.n1 = p->n1; f.n2 = p->n2; f.G = pl.G; f.d_qk = p->d_qk; f.d_v = p->d_v;
   f.bs = p->block_size; f.cnt = p->block_count; f.T1 = pl.T1;
   f.scale_log2e = (float)(p->scale * 1.4426950408889634);
   f.is_f16 = p->dtype == ATTN_FP16;
-  return timed("selected_forward", s, [&] { return launch_selected_forward(f, s); }) == hipSuccess ? ATTN_OK
-                                                                                                    : ATTN_ERR_HIP;
+  f.blkoff = x.blkoff; f.offsets = x.offsets; f.list = x.list; f.sched = x.cursor; f.wofs = x.wofs;
+  f.nblk_total = pl.nblk_total; f.nwin = pl.nwin;
+  f.part_o = at<void>(workspace, pl.off_dq_part);
+  f.part_ml = at<float2>(workspace, pl.off_ml);
+  for (int w = 0; w < pl.nwin; ++w) {
+    f.win = w;
+    f.t0 = std::min<int64_t>(pl.T1, (int64_t)w * pl.win_tokens);
+    f.t1 = std::min<int64_t>(pl.T1, f.t0 + pl.win_tokens);
+    if (timed("selected_forward", s, [&] { return launch_selected_forward_kv(f, s); }) != hipSuccess)
+      return ATTN_ERR_HIP;
+    if (timed("selected_forward_combine", s, [&] { return launch_selected_forward_combine(f, s); }) != hipSuccess)
+      return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
 }
 
 attn_status_t attn_bwd_selected_index(const attn_bwd_problem_t* p, const int32_t* topk_indices, int32_t* offsets,

@@ -134,7 +134,7 @@ hipError_t launch_selected_window_offsets(const SelArgs& a, hipStream_t s);  // 
 hipError_t launch_selected_kv(const SelArgs& a, hipStream_t s);         // dK, dV and the dQ partials
 hipError_t launch_selected_dq_reduce(const SelArgs& a, hipStream_t s);  // dQ = scale * sum of partials
 
-// ---- selected (NSA), query-major: forward, and the row statistic without attentionOut ----
+// ---- selected (NSA) forward (KV-major + combine), and the row statistic without attentionOut ----
 struct SelFwdArgs {
   const void* q; const void* k; const void* v; const void* dy;  // dy: row-statistic pass only
   const int32_t* topk;      // [T1, N2, cnt]
@@ -149,9 +149,20 @@ struct SelFwdArgs {
   int64_t T1;
   float scale_log2e;
   int is_f16;               // element type: 0 bf16, 1 fp16
+  // KV-major forward: the inverted index of the selected backward, and per-entry partials
+  const int32_t* blkoff;    // [B+1] blocks before each sequence
+  const int32_t* offsets;   // [n2 * nblk_total + 1]
+  const int32_t* list;      // entries t * cnt + slot, ascending per key
+  const int32_t* sched;     // work order of the keys
+  const int32_t* wofs;      // [n2 * nblk_total, nwin + 1] (nwin > 1)
+  int nblk_total, nwin, win;
+  int64_t t0, t1;           // query tokens of the current window
+  void* part_o;             // [W * cnt * n2][d_v / 16][G][16] O_b / l_b of each entry of the window (element type)
+  float2* part_ml;          // [W * cnt * n2, G] (m_b, l_b), log2 domain
 };
-hipError_t launch_selected_forward(const SelFwdArgs& a, hipStream_t s);  // O, softmaxMax, softmaxSum
-hipError_t launch_selected_drow(const SelFwdArgs& a, hipStream_t s);     // ndrow without O
+hipError_t launch_selected_drow(const SelFwdArgs& a, hipStream_t s);     // ndrow without O (query-major)
+hipError_t launch_selected_forward_kv(const SelFwdArgs& a, hipStream_t s);       // per-entry partials
+hipError_t launch_selected_forward_combine(const SelFwdArgs& a, hipStream_t s);  // O, softmaxMax, softmaxSum
 
 // ---- lightning-indexer backward ------------------------------------------------
 struct IdxArgs {

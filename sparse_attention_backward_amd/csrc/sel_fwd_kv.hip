@@ -1,0 +1,355 @@
+// Selected (NSA) attention forward, KV-major with per-block partial softmax.
+//
+// Page "NsaSelectedAttentionGrad": the backward consumes attentionOut, softmaxMax and
+// softmaxSum, the forward's outputs; for query token t and KV head n2 the G query heads
+// attend to the selectedBlockCount blocks that topkIndices[t, n2] gathers:
+//   s = scale Q K^T,  m = max s,  l = sum exp(s - m),  O = sum exp(s - m) V / l.
+// The softmax over the gathered rows splits over the blocks: with each block's own
+// m_b = max of its scores, l_b = sum exp(s - m_b) and O_b = sum exp(s - m_b) V / l_b,
+//   m = max_b m_b,  l = sum_b l_b exp(m_b - m),  O = sum_b (l_b exp(m_b - m) / l) O_b.
+//
+// Pass 1 (sel_fwd_kv_kernel): one workgroup per (KV head, block), that block's K and V rows
+// resident in LDS; the block's list of (token, slot) entries (the inverted index, ascending)
+// is dealt to the four waves, each entry to one wave.  Per entry the G heads' query rows are
+// gathered straight into registers as the B operand (the next entry's rows load while the
+// current one computes), and the heads are the MFMA columns:
+//   S^T (keys x heads) = K (A: row reads of the K tile) x Q^T,
+//   m_b, P^T = exp2(S^T scale log2 e - m_b), l_b per head (column),
+//   O_b^T (features x heads) = V^T (A: column reads of the V tile) x P^T / l_b.
+// O_b (element type) and (m_b, l_b) (fp32, log2 domain) are stored as the entry's partial,
+// row (entry - first entry of the window) N2 + KV head.  Per entry this moves the query rows
+// (G D_qk elements) and a partial of G D_v elements, instead of gathering the block's
+// bs (D_qk + D_v) elements of K and V for every entry.
+// Pass 2 (sel_fwd_combine_kernel): one wave per (token, KV head): the cnt partials merged
+// in slot order into O, softmaxMax (natural units) and softmaxSum.  Slots whose id
+// is out of range have no partial (the index build skipped them and raised the flag).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ab {
+
+namespace {
+
+__device__ __forceinline__ float max4(f32x4 v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
+__device__ __forceinline__ float sum4(f32x4 v) { return (v[0] + v[1]) + (v[2] + v[3]); }
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (T)x) | ((uint32_t)__builtin_bit_cast(uint16_t, (T)y) << 16);
+}
+
+constexpr int kDv = 128;
+
+template <typename T, int DQK, int NHT, int KB>
+__global__ __launch_bounds__(256) void sel_fwd_kv_kernel(SelFwdArgs a) {
+  using V8 = typename Mma<T>::v8;
+  constexpr int DM = 128, DR = DQK - DM;
+  constexpr int KS = DQK / 32, NF = kDv / 16, NKT = KB / 16, NT = KB / 64;
+  using TM = RowTile<16>;  // 128-feature rows: the K main part and V
+  using TR = RowTile<8>;   // 64-feature rows: the K part past 128
+  constexpr int OKM = 0, OKR = OKM + NT * TM::BYTES, OV = OKR + (DR > 0 ? NT * TR::BYTES : 0);
+  constexpr int SMEM = OV + NT * TM::BYTES;
+  static_assert(DR == 0 || DR == 64, "query / key head dim 128 or 192");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int u = a.sched[blockIdx.x];  // key: KV head nblk_total + block
+  const int kvh = u / a.nblk_total;
+  const int rem = u - kvh * a.nblk_total;
+  const int b = seq_of32(a.blkoff, a.batch, rem);
+  const int64_t k0 = a.cu_kv[b] + (int64_t)(rem - a.blkoff[b]) * a.bs;
+  const int e_begin = a.nwin > 1 ? a.wofs[(int64_t)u * (a.nwin + 1) + a.win] : a.offsets[u];
+  const int e_end = a.nwin > 1 ? a.wofs[(int64_t)u * (a.nwin + 1) + a.win + 1] : a.offsets[u + 1];
+  if (e_begin == e_end) return;  // whole workgroup
+  const int nkt = a.bs / 16;     // key tiles of the block (bs is a multiple of 16)
+  const int G = a.G;
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+
+  // K and V rows of the block into LDS; rows past the block are zero
+  {
+    constexpr int CK = DQK / 8, CV = kDv / 8;  // 16-byte chunks per row
+    for (int i = tid; i < KB * (CK + CV); i += 256) {
+      const int r = i / (CK + CV), c = i - r * (CK + CV);
+      const int64_t kr = (k0 + r) * a.n2 + kvh;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (c < CK) {
+        if (r < a.bs) x = ldg16(k + kr * DQK + 8 * c);
+        const uint32_t dst = c < 16 ? OKM + (r >> 6) * TM::BYTES + TM::off(r & 63, c)
+                                    : OKR + (r >> 6) * TR::BYTES + TR::off(r & 63, c - 16);
+        lds_st16_at(smem_lds + dst, x);
+      } else {
+        if (r < a.bs) x = ldg16(v + kr * kDv + 8 * (c - CK));
+        lds_st16_at(smem_lds + OV + (r >> 6) * TM::BYTES + TM::off(r & 63, c - CK), x);
+      }
+    }
+  }
+  __syncthreads();
+
+  // query rows of entry e (token t = list / cnt) as B operands: column = head 16 ht + l16,
+  // k = features 32 s + 8 g .. + 7
+  auto load_q = [&](int e, V8 (&Qf)[NHT][KS]) {
+    const int ent = a.list[e];
+    const int64_t t = ent / a.cnt;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + l16;
+      const int64_t row = t * a.n1 + (int64_t)kvh * G + h;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        Qf[ht][s] = as_v8<T>(h < G ? ldg16(q + row * DQK + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0));
+    }
+  };
+
+  const int e_lo = (int)(a.t0 * a.cnt);  // first entry of the window
+  int e = e_begin + wave;
+  V8 Qc[NHT][KS];
+  if (e < e_end) load_q(e, Qc);
+  for (; e < e_end; e += 4) {
+    V8 Qn[NHT][KS];
+    if (e + 4 < e_end) load_q(e + 4, Qn);
+    // S^T tiles: key tile kt holds keys 16 kt + 4 g + (0..3) of the lane's head column
+    f32x4 S[NKT][NHT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (kt < nkt) {
+        const uint32_t km = smem_lds + OKM + (kt >> 2) * TM::BYTES + 16 * (kt & 3) * TM::RB;
+        const uint32_t kr = smem_lds + OKR + (kt >> 2) * TR::BYTES + 16 * (kt & 3) * TR::RB;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const V8 ka = s < 4 ? as_v8<T>(lds_b128_at(km + TM::rowA(lane, s)))
+                              : as_v8<T>(lds_b128_at(kr + TR::rowA(lane, s - 4)));
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = Mma<T>::run(ka, Qc[ht][s], S[kt][ht]);
+        }
+      }
+    }
+    // block-local softmax per head column (log2 domain)
+    float mb[NHT], lb[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+        if (kt < nkt) mx = fmaxf(mx, max4(S[kt][ht] * a.scale_log2e));
+      mx = group_max(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        if (kt < nkt) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) S[kt][ht][j] = __builtin_amdgcn_exp2f(S[kt][ht][j] * a.scale_log2e - mx);
+          sum += sum4(S[kt][ht]);
+        } else {
+          S[kt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      mb[ht] = mx;
+      lb[ht] = group_sum(sum);
+    }
+    // O_b^T = V^T P^T over the block: k-step kk covers keys 32 kk .. +31 (tiles 2 kk, 2 kk + 1)
+    f32x4 O[NHT][NF];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) O[ht][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKT / 2; ++kk) {
+      if (2 * kk < nkt) {
+        V8 pb[NHT];
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) pb[ht] = pack8t<T>(S[2 * kk][ht], S[2 * kk + 1][ht]);
+        const uint32_t vt = smem_lds + OV + (kk >> 1) * TM::BYTES + 32 * (kk & 1) * TM::RB;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const uint32_t o = vt + TM::colB(lane, f);
+          const V8 va = __builtin_bit_cast(V8, join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TM::RB)));
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) O[ht][f] = Mma<T>::run(va, pb[ht], O[ht][f]);
+        }
+      }
+    }
+    // the entry's partial O_b / l_b as [feature tile f][head][16 features] (lane: features
+    // 16 f + 4 g .. + 3 of its head), so that one store covers G x 32 contiguous bytes; m_b, l_b
+    const int ent = a.list[e];
+    const int64_t r = (int64_t)(ent - e_lo) * a.n2 + kvh;
+    T* po = static_cast<T*>(a.part_o) + r * G * kDv;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + l16;
+      if (h < G) {
+        const float inv = 1.f / lb[ht];  // <= 1: l_b includes the maximum's own term, 1
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const uint2 w = make_uint2(pack2<T>(O[ht][f][0] * inv, O[ht][f][1] * inv),
+                                     pack2<T>(O[ht][f][2] * inv, O[ht][f][3] * inv));
+          *reinterpret_cast<uint2*>(po + (f * G + h) * 16 + 4 * g) = w;
+        }
+        if (g == 0) a.part_ml[r * G + h] = make_float2(mb[ht], lb[ht]);
+      }
+    }
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) Qc[ht][s] = Qn[ht][s];
+  }
+}
+
+// One wave per (token, KV head) of the window.  Lane l owns the 16-byte chunks l, l + 64,
+// ... of the G x d_v block in the partials' order (chunk c: feature tile f = c / 2G, head
+// (c mod 2G) / 2, features 16 f + 8 (c mod 2) .. + 7) and merges
+// the slots in order with a running maximum (online softmax over the blocks); two slots per
+// iteration keep eight 16-byte partial loads per lane in flight.  Slots whose id is out of
+// range have no partial: one ballot per 64 slots marks the valid ones.
+constexpr int kCU = 4;  // chunks per lane per pass
+
+template <typename T>
+__global__ __launch_bounds__(256) void sel_fwd_combine_kernel(SelFwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wu = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // unit within the window
+  if (wu >= (a.t1 - a.t0) * a.n2) return;                           // whole wave
+  const int64_t unit = a.t0 * a.n2 + wu;
+  const int64_t t = unit / a.n2;
+  const int kvh = (int)(unit - t * a.n2);
+  const int b = seq_of(a.cu_q, a.batch, t);
+  const int nblk = (int)((a.cu_kv[b + 1] - a.cu_kv[b]) / a.bs);
+  uint64_t valid[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int sl = 64 * hh + lane;
+    bool ok = false;
+    if (sl < a.cnt) {
+      const int id = a.topk[unit * a.cnt + sl];
+      ok = id >= 0 && id < nblk;
+    }
+    valid[hh] = __ballot(ok);
+  }
+  auto slot_ok = [&](int sl) -> bool { return sl < a.cnt && ((valid[sl >> 6] >> (sl & 63)) & 1); };
+  const int G = a.G, chunks = G * (kDv / 8);
+  const int64_t r0 = (t - a.t0) * a.cnt;  // the token's first entry in the window
+  const T* po = static_cast<const T*>(a.part_o);
+  for (int c0 = lane; c0 < chunks; c0 += 64 * kCU) {
+    float acc[kCU][8], m[kCU], l[kCU];
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      m[u] = -INFINITY;
+      l[u] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[u][j] = 0.f;
+    }
+    for (int sl = 0; sl < a.cnt; sl += 2) {
+      uint4 x[2][kCU];
+      float2 ml[2][kCU];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const bool ok = slot_ok(sl + d);
+        const int64_t r = ((r0 + sl + d) * a.n2 + kvh) * G;  // (entry, head 0) row
+#pragma unroll
+        for (int u = 0; u < kCU; ++u) {
+          const int c = c0 + 64 * u;
+          x[d][u] = make_uint4(0, 0, 0, 0);
+          ml[d][u] = make_float2(-INFINITY, 0.f);
+          if (ok && c < chunks) {
+            x[d][u] = ldg16_stream(po + r * kDv + 8 * c);
+            ml[d][u] = a.part_ml[r + (c % (2 * G)) / 2];
+          }
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        if (!slot_ok(sl + d)) continue;
+#pragma unroll
+        for (int u = 0; u < kCU; ++u) {
+          const float mn = fmaxf(m[u], ml[d][u].x);
+          const float sc = __builtin_amdgcn_exp2f(m[u] - mn);  // 0 before the first valid slot
+          const float w = ml[d][u].y * __builtin_amdgcn_exp2f(ml[d][u].x - mn);
+          const uint32_t xs[4] = {x[d][u].x, x[d][u].y, x[d][u].z, x[d][u].w};
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            acc[u][2 * q2] = acc[u][2 * q2] * sc + w * t2f<T>((uint16_t)(xs[q2] & 0xffffu));
+            acc[u][2 * q2 + 1] = acc[u][2 * q2 + 1] * sc + w * t2f<T>((uint16_t)(xs[q2] >> 16));
+          }
+          l[u] = l[u] * sc + w;
+          m[u] = mn;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      const int c = c0 + 64 * u;
+      if (c >= chunks) continue;
+      const int f = c / (2 * G), h = (c % (2 * G)) / 2, half = c & 1;
+      const float inv = l[u] > 0.f ? 1.f / l[u] : 0.f;
+      const int64_t row = t * a.n1 + (int64_t)kvh * G + h;
+      const uint4 y = make_uint4(pack2<T>(acc[u][0] * inv, acc[u][1] * inv), pack2<T>(acc[u][2] * inv, acc[u][3] * inv),
+                                 pack2<T>(acc[u][4] * inv, acc[u][5] * inv), pack2<T>(acc[u][6] * inv, acc[u][7] * inv));
+      sts16_stream(static_cast<T*>(a.o) + row * kDv + 16 * f + 8 * half, y);
+      if (f == 0 && half == 0) {
+        // statistics in natural units: m = m2 ln 2, l as summed; no valid block: -inf, 0
+        const float mn = l[u] > 0.f ? m[u] * 0.6931471805599453f : -INFINITY;
+        const float lv = l[u];
+        *reinterpret_cast<f32x4*>(a.smax + row * 8) = f32x4{mn, mn, mn, mn};
+        *reinterpret_cast<f32x4*>(a.smax + row * 8 + 4) = f32x4{mn, mn, mn, mn};
+        *reinterpret_cast<f32x4*>(a.ssum + row * 8) = f32x4{lv, lv, lv, lv};
+        *reinterpret_cast<f32x4*>(a.ssum + row * 8 + 4) = f32x4{lv, lv, lv, lv};
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_kv_t(const SelFwdArgs& a, hipStream_t s) {
+  const int nkeys = a.n2 * a.nblk_total;
+  if (nkeys == 0) return hipSuccess;
+  const dim3 grid((unsigned)nkeys), block(256);
+  const bool two = a.G > 16, wide = a.bs > 64;
+#define AB_FWD_KV(DQK)                                                                                \
+  do {                                                                                                \
+    if (two) {                                                                                        \
+      if (wide) hipLaunchKernelGGL((sel_fwd_kv_kernel<T, DQK, 2, 128>), grid, block, 0, s, a);        \
+      else hipLaunchKernelGGL((sel_fwd_kv_kernel<T, DQK, 2, 64>), grid, block, 0, s, a);              \
+    } else {                                                                                          \
+      if (wide) hipLaunchKernelGGL((sel_fwd_kv_kernel<T, DQK, 1, 128>), grid, block, 0, s, a);        \
+      else hipLaunchKernelGGL((sel_fwd_kv_kernel<T, DQK, 1, 64>), grid, block, 0, s, a);              \
+    }                                                                                                 \
+  } while (0)
+  if (a.d_qk == 192) AB_FWD_KV(192);
+  else AB_FWD_KV(128);
+#undef AB_FWD_KV
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_combine_t(const SelFwdArgs& a, hipStream_t s) {
+  const int64_t units = (a.t1 - a.t0) * a.n2;
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sel_fwd_combine_kernel<T>, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_selected_forward_kv(const SelFwdArgs& a, hipStream_t s) {
+  if (!selected_supported(a.d_qk, a.d_v, a.G, a.bs)) return hipErrorInvalidValue;
+  return a.is_f16 ? launch_kv_t<_Float16>(a, s) : launch_kv_t<__bf16>(a, s);
+}
+
+hipError_t launch_selected_forward_combine(const SelFwdArgs& a, hipStream_t s) {
+  return a.is_f16 ? launch_combine_t<_Float16>(a, s) : launch_combine_t<__bf16>(a, s);
+}
+
+}  // namespace ab

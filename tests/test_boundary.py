@@ -258,11 +258,16 @@ def test_noalloc_refuses_problems_beyond_the_scratch_array_on_the_host():
 
 
 def test_selected_forward_validation():
-    """attn_fwd_selected: op ATTN_OP_SELECTED_FWD, the selected constraints, a small workspace
-    (tables and the index flag, independent of the backward's index and shares)."""
+    """attn_fwd_selected: op ATTN_OP_SELECTED_FWD, the selected constraints, a workspace of the
+    inverted index and one partial per (entry, head): d_v elements + (m_b, l_b)."""
     fw = selected(forward=True)
     st, n = status_ws(fw)
-    assert st == OK and 0 < n < 4096
+    T1, cnt, n1, n2, d_v = 640, 3, 32, 2, 128
+    partials = T1 * cnt * n1 * (2 * d_v + 8)
+    index = 12 * T1 * n2 * cnt            # list and sort scratch
+    assert st == OK and partials + index <= n <= partials + index + (1 << 16)
+    small = selected(forward=True, window_tokens=100)
+    assert status_ws(small)[1] < n        # windows of query tokens bound the partials
     assert status_ws(selected(forward=True, block_size=24))[0] == INVALID
     L = sab.lib
     args = [FAKE] * 7
