@@ -217,13 +217,16 @@ def make_problem(w: W.Workload, deterministic=False, window_tokens=0):
                                 w.block_count, deterministic=deterministic, window_tokens=window_tokens)
 
 
-def run_workload(w: W.Workload, steps: int, warmup: int, deterministic=False, window_tokens=0, prewarm_ms=300.0):
+def run_workload(w: W.Workload, steps: int, warmup: int, deterministic=False, window_tokens=0, prewarm_ms=300.0,
+                 with_out=True):
     """Time `steps` complete calls after a clock pre-warm (calls repeated until `prewarm_ms` of GPU time
     have passed) and `warmup` untimed calls.  Returns the inputs, ms per call, the library's per-kernel
     totals over the timed calls, and the pre-warm actually spent."""
     dev = torch.device("cuda", 0)
     x = W.make_inputs(w, device=dev, backend="torch")
     o, smax, ssum = gpu_forward(w, x)
+    if not with_out:  # the selected call without attentionOut (the row statistic from the gathered rows)
+        o = None
     prob = make_problem(w, deterministic, window_tokens)
     if w.form == "dense":
         outs = [torch.empty_like(x["query"]), torch.empty_like(x["query_rope"]) if w.d_rope else None,
@@ -330,10 +333,10 @@ def roofline_for(w: W.Workload, kernels: dict, steps: int, call_ms: float):
     return out
 
 
-def measure(wl: int, steps: int, warmup: int, deterministic=False, window_tokens=0, prewarm_ms=300.0):
+def measure(wl: int, steps: int, warmup: int, deterministic=False, window_tokens=0, prewarm_ms=300.0, with_out=True):
     """One bench record for workload `wl`: value, timing, roofline and per-kernel times."""
     w = W.config(wl)
-    x, ms, kernels, spent = run_workload(w, steps, warmup, deterministic, window_tokens, prewarm_ms)
+    x, ms, kernels, spent = run_workload(w, steps, warmup, deterministic, window_tokens, prewarm_ms, with_out)
     total_flops = attended_pairs(w) * flops_per_pair(w)
     value = total_flops / (ms * 1e-3) / 1e12
     rec = {
@@ -347,6 +350,7 @@ def measure(wl: int, steps: int, warmup: int, deterministic=False, window_tokens
                    "d_qk": w.d_qk, "d_rope": w.d_rope, "d_v": w.d_v, "causal": w.causal,
                    "block_size": w.block_size, "block_count": w.block_count, "index_dist": w.index_dist,
                    "deterministic": bool(deterministic), "window_tokens": int(window_tokens),
+                   "attention_out": bool(with_out),
                    "algorithmic_tflop_per_step": total_flops / 1e12},
         "roofline": roofline_for(w, kernels, steps, ms),
         "kernels_ms_per_call": {k: round(v[0] / steps, 4) for k, v in kernels.items()},
@@ -537,6 +541,7 @@ def measure_indexer(dk_atomic: bool, steps: int, warmup: int, prewarm_ms=300.0):
 
 
 EXTRA_RUNS = ((2, False), (3, False), (4, False), (4, True))  # (workload, deterministic) beside the headline
+NO_OUT_RUNS = (3,)  # the selected backward without attentionOut, measured on these workloads
 FORWARD_RUNS = (5, 3)  # selected forward measured on these workloads
 
 
@@ -556,6 +561,8 @@ def main(argv=None):
                     help="only the lightning-indexer backward lines (for profiling runs)")
     ap.add_argument("--forward-only", action="store_true",
                     help="only the selected forward lines (for profiling runs)")
+    ap.add_argument("--no-out", action="store_true",
+                    help="selected headline without attentionOut (the row statistic from the gathered rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 5 times (counter calibration)")
@@ -597,7 +604,7 @@ def main(argv=None):
               flush=True)
         return 0
     w, x, rec = measure(args.workload, args.steps, args.warmup, args.deterministic, args.window_tokens,
-                        args.prewarm_ms)
+                        args.prewarm_ms, with_out=not args.no_out)
     line = {
         "metric": METRIC,
         "value": rec["value"],
@@ -631,6 +638,12 @@ def main(argv=None):
             k = args.steps * 10 if W.config(wl).form == "dense" else args.steps
             _, xe, re_ = measure(wl, k, args.warmup, det, 0, args.prewarm_ms)
             re_["steps"] = k
+            extra.append(re_)
+            del xe
+            torch.cuda.empty_cache()
+        for wl in NO_OUT_RUNS:
+            _, xe, re_ = measure(wl, args.steps, args.warmup, False, 0, args.prewarm_ms, with_out=False)
+            re_["pass"] = "backward without attentionOut"
             extra.append(re_)
             del xe
             torch.cuda.empty_cache()

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattnbwd.so")
 SOURCES = ["api.hip", "preprocess.hip", "dense_fp32.hip", "dense_kv.hip", "dense_dq.hip", "attn_q.hip",
-           "index.hip", "sel_kv.hip", "sel_reduce.hip", "sel_drow.hip", "sel_fwd_kv.hip", "indexer.hip"]
+           "index.hip", "sel_kv.hip", "sel_reduce.hip", "sel_fwd_kv.hip", "indexer.hip"]
 ARCH = os.environ.get("ATTN_BWD_ARCH", "gfx950")
 # Compilation units: (object name, source, extra options).  sel_kv.hip is compiled twice,
 # once per key-block width.  The 64-key kernels run one wave per SIMD with every register in

@@ -758,7 +758,7 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   if (p->op != ATTN_OP_SELECTED) return ATTN_ERR_INVALID;
   const bool has_q = pl.T1 > 0, has_k = pl.T2 > 0;
   // attentionOut is optional (parameter table): without it rowsum(P * dP) is formed from the
-  // gathered rows by a query-major pass instead of rowsum(dY * O)
+  // gathered rows by a KV-major pass instead of rowsum(dY * O)
   if (has_q && (!q || !dy || !softmax_max || !softmax_sum || !topk_indices || !dq)) return ATTN_ERR_NULLPTR;
   if (has_k && (!k || !v || !dk || !dv)) return ATTN_ERR_NULLPTR;
   for (const void* ptr : {q, k, v, out, dy, (const void*)softmax_max, (const void*)softmax_sum,
@@ -780,20 +780,6 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
   pa.tab_n16 = tables.n16();
   if (timed("row_stats", s, [&] { return launch_preprocess(pa, s); }) != hipSuccess) return ATTN_ERR_HIP;
   if (tables.commit(s) != hipSuccess) return ATTN_ERR_HIP;
-  if (!out && has_q) {
-    SelFwdArgs f{};
-    f.q = q; f.k = k; f.v = v; f.dy = dy; f.topk = topk_indices;
-    f.cu_q = at<const int64_t>(workspace, pl.off_cu_q);
-    f.cu_kv = at<const int64_t>(workspace, pl.off_cu_kv);
-    f.lse2 = pa.lse2; f.ndrow = pa.ndrow;
-    f.flag = nullptr;  // the index build below checks the ids and raises the flag
-    f.batch = pl.B; f.n1 = p->n1; f.n2 = p->n2; f.G = pl.G; f.d_qk = p->d_qk; f.d_v = p->d_v;
-    f.bs = p->block_size; f.cnt = p->block_count; f.T1 = pl.T1;
-    f.scale_log2e = (float)(p->scale * 1.4426950408889634);
-    f.is_f16 = p->dtype == ATTN_FP16;
-    if (timed("selected_row_stat", s, [&] { return launch_selected_drow(f, s); }) != hipSuccess) return ATTN_ERR_HIP;
-  }
-
   SelArgs a{};
   a.q = q; a.k = k; a.v = v; a.dy = dy; a.lse2 = pa.lse2; a.ndrow = pa.ndrow; a.topk = topk_indices;
   a.dq = dq; a.dk = dk; a.dv = dv;
@@ -822,6 +808,31 @@ attn_status_t attn_bwd_selected(const attn_bwd_problem_t* p, const void* q, cons
         return e != hipSuccess ? e : launch_selected_window_offsets(a, s);
       }) != hipSuccess)
     return ATTN_ERR_HIP;
+  if (!out && has_q) {
+    // rowsum(P dP) over the gathered rows, KV-major over the same index and windows; the
+    // per-entry sums use the share buffer before the backward's first window does
+    SelFwdArgs f{};
+    f.q = q; f.k = k; f.v = v; f.dy = dy; f.topk = topk_indices;
+    f.cu_q = a.cu_q; f.cu_kv = a.cu_kv;
+    f.lse2 = pa.lse2; f.ndrow = pa.ndrow;
+    f.batch = pl.B; f.n1 = p->n1; f.n2 = p->n2; f.G = pl.G; f.d_qk = p->d_qk; f.d_v = p->d_v;
+    f.bs = p->block_size; f.cnt = p->block_count; f.T1 = pl.T1;
+    f.scale_log2e = a.scale_log2e;
+    f.is_f16 = a.is_f16;
+    f.blkoff = a.blkoff; f.offsets = a.offsets; f.list = a.list; f.sched = a.cursor; f.wofs = a.wofs;
+    f.nblk_total = pl.nblk_total; f.nwin = pl.nwin;
+    f.part_d = static_cast<float*>(a.dq_part);
+    for (int w = 0; w < pl.nwin; ++w) {
+      f.win = w;
+      f.t0 = std::min<int64_t>(pl.T1, (int64_t)w * pl.win_tokens);
+      f.t1 = std::min<int64_t>(pl.T1, f.t0 + pl.win_tokens);
+      if (timed("selected_row_stat", s, [&] {
+            const hipError_t e = launch_selected_drow_kv(f, s);
+            return e != hipSuccess ? e : launch_selected_drow_combine(f, s);
+          }) != hipSuccess)
+        return ATTN_ERR_HIP;
+    }
+  }
   for (int w = 0; w < pl.nwin; ++w) {
     a.win = w;
     a.t0 = std::min<int64_t>(pl.T1, (int64_t)w * pl.win_tokens);

@@ -159,10 +159,12 @@ struct SelFwdArgs {
   int64_t t0, t1;           // query tokens of the current window
   void* part_o;             // [W * cnt * n2][d_v / 16][G][16] O_b / l_b of each entry of the window (element type)
   float2* part_ml;          // [W * cnt * n2, G] (m_b, l_b), log2 domain
+  float* part_d;            // row statistic: [W * cnt, N1] each entry's sum of P dP per head
 };
-hipError_t launch_selected_drow(const SelFwdArgs& a, hipStream_t s);     // ndrow without O (query-major)
 hipError_t launch_selected_forward_kv(const SelFwdArgs& a, hipStream_t s);       // per-entry partials
 hipError_t launch_selected_forward_combine(const SelFwdArgs& a, hipStream_t s);  // O, softmaxMax, softmaxSum
+hipError_t launch_selected_drow_kv(const SelFwdArgs& a, hipStream_t s);          // per-entry sums of P dP
+hipError_t launch_selected_drow_combine(const SelFwdArgs& a, hipStream_t s);     // ndrow without O
 
 // ---- lightning-indexer backward ------------------------------------------------
 struct IdxArgs {

@@ -48,42 +48,43 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
 
 constexpr int kDv = 128;
 
-template <typename T, int DQK, int NHT, int KB>
-__global__ __launch_bounds__(256) void sel_fwd_kv_kernel(SelFwdArgs a) {
-  using V8 = typename Mma<T>::v8;
-  constexpr int DM = 128, DR = DQK - DM;
-  constexpr int KS = DQK / 32, NF = kDv / 16, NKT = KB / 16, NT = KB / 64;
+// LDS of a KV-major workgroup: the block's K rows (main 128 features, then the rest) and V
+// rows, KB rows each (64-row RowTiles), rows past the block zero.
+template <int DQK, int KB>
+struct KvTiles {
+  static constexpr int DR = DQK - 128, NT = KB / 64;
   using TM = RowTile<16>;  // 128-feature rows: the K main part and V
   using TR = RowTile<8>;   // 64-feature rows: the K part past 128
-  constexpr int OKM = 0, OKR = OKM + NT * TM::BYTES, OV = OKR + (DR > 0 ? NT * TR::BYTES : 0);
-  constexpr int SMEM = OV + NT * TM::BYTES;
+  static constexpr int OKM = 0, OKR = OKM + NT * TM::BYTES, OV = OKR + (DR > 0 ? NT * TR::BYTES : 0);
+  static constexpr int SMEM = OV + NT * TM::BYTES;
   static_assert(DR == 0 || DR == 64, "query / key head dim 128 or 192");
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, g = lane >> 4;
-  const int u = a.sched[blockIdx.x];  // key: KV head nblk_total + block
-  const int kvh = u / a.nblk_total;
-  const int rem = u - kvh * a.nblk_total;
-  const int b = seq_of32(a.blkoff, a.batch, rem);
-  const int64_t k0 = a.cu_kv[b] + (int64_t)(rem - a.blkoff[b]) * a.bs;
-  const int e_begin = a.nwin > 1 ? a.wofs[(int64_t)u * (a.nwin + 1) + a.win] : a.offsets[u];
-  const int e_end = a.nwin > 1 ? a.wofs[(int64_t)u * (a.nwin + 1) + a.win + 1] : a.offsets[u + 1];
-  if (e_begin == e_end) return;  // whole workgroup
-  const int nkt = a.bs / 16;     // key tiles of the block (bs is a multiple of 16)
-  const int G = a.G;
-  const T* q = static_cast<const T*>(a.q);
-  const T* k = static_cast<const T*>(a.k);
-  const T* v = static_cast<const T*>(a.v);
-  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  // the work unit of workgroup blockIdx.x: key u = KV head nblk_total + block, its first
+  // key row k0 and the window's part [e_begin, e_end) of its list
+  struct Unit {
+    int kvh, e_begin, e_end;
+    int64_t k0;
+  };
+  static __device__ __forceinline__ Unit unit(const SelFwdArgs& a) {
+    Unit w;
+    const int u = a.sched[blockIdx.x];
+    w.kvh = u / a.nblk_total;
+    const int rem = u - w.kvh * a.nblk_total;
+    const int b = seq_of32(a.blkoff, a.batch, rem);
+    w.k0 = a.cu_kv[b] + (int64_t)(rem - a.blkoff[b]) * a.bs;
+    w.e_begin = a.nwin > 1 ? a.wofs[(int64_t)u * (a.nwin + 1) + a.win] : a.offsets[u];
+    w.e_end = a.nwin > 1 ? a.wofs[(int64_t)u * (a.nwin + 1) + a.win + 1] : a.offsets[u + 1];
+    return w;
+  }
 
-  // K and V rows of the block into LDS; rows past the block are zero
-  {
+  template <typename T>
+  static __device__ __forceinline__ void stage(const SelFwdArgs& a, const Unit& w, uint32_t smem_lds) {
     constexpr int CK = DQK / 8, CV = kDv / 8;  // 16-byte chunks per row
-    for (int i = tid; i < KB * (CK + CV); i += 256) {
+    const T* k = static_cast<const T*>(a.k);
+    const T* v = static_cast<const T*>(a.v);
+    for (int i = threadIdx.x; i < KB * (CK + CV); i += 256) {
       const int r = i / (CK + CV), c = i - r * (CK + CV);
-      const int64_t kr = (k0 + r) * a.n2 + kvh;
+      const int64_t kr = (w.k0 + r) * a.n2 + w.kvh;
       uint4 x = make_uint4(0, 0, 0, 0);
       if (c < CK) {
         if (r < a.bs) x = ldg16(k + kr * DQK + 8 * c);
@@ -96,6 +97,41 @@ __global__ __launch_bounds__(256) void sel_fwd_kv_kernel(SelFwdArgs a) {
       }
     }
   }
+
+  // S^T tile kt (keys 16 kt .. + 15 as rows, the 16 head columns of Qf) += K Q^T
+  template <typename T, int NHT, int KS>
+  static __device__ __forceinline__ void scores(uint32_t smem_lds, int kt, int lane,
+                                                const typename Mma<T>::v8 (&Qf)[NHT][KS], f32x4 (&S)[NHT]) {
+    const uint32_t km = smem_lds + OKM + (kt >> 2) * TM::BYTES + 16 * (kt & 3) * TM::RB;
+    const uint32_t kr = smem_lds + OKR + (kt >> 2) * TR::BYTES + 16 * (kt & 3) * TR::RB;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const auto ka = s < 4 ? as_v8<T>(lds_b128_at(km + TM::rowA(lane, s))) : as_v8<T>(lds_b128_at(kr + TR::rowA(lane, s - 4)));
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) S[ht] = Mma<T>::run(ka, Qf[ht][s], S[ht]);
+    }
+  }
+};
+
+template <typename T, int DQK, int NHT, int KB>
+__global__ __launch_bounds__(256) void sel_fwd_kv_kernel(SelFwdArgs a) {
+  using V8 = typename Mma<T>::v8;
+  using L = KvTiles<DQK, KB>;
+  using TM = typename L::TM;
+  constexpr int KS = DQK / 32, NF = kDv / 16, NKT = KB / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[L::SMEM];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const typename L::Unit wu = L::unit(a);
+  const int kvh = wu.kvh, e_begin = wu.e_begin, e_end = wu.e_end;
+  if (e_begin == e_end) return;  // whole workgroup
+  const int nkt = a.bs / 16;     // key tiles of the block (bs is a multiple of 16)
+  const int G = a.G;
+  const T* q = static_cast<const T*>(a.q);
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  L::template stage<T>(a, wu, smem_lds);
   __syncthreads();
 
   // query rows of entry e (token t = list / cnt) as B operands: column = head 16 ht + l16,
@@ -126,17 +162,7 @@ __global__ __launch_bounds__(256) void sel_fwd_kv_kernel(SelFwdArgs a) {
     for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (kt < nkt) {
-        const uint32_t km = smem_lds + OKM + (kt >> 2) * TM::BYTES + 16 * (kt & 3) * TM::RB;
-        const uint32_t kr = smem_lds + OKR + (kt >> 2) * TR::BYTES + 16 * (kt & 3) * TR::RB;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const V8 ka = s < 4 ? as_v8<T>(lds_b128_at(km + TM::rowA(lane, s)))
-                              : as_v8<T>(lds_b128_at(kr + TR::rowA(lane, s - 4)));
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = Mma<T>::run(ka, Qc[ht][s], S[kt][ht]);
-        }
-      }
+      if (kt < nkt) L::template scores<T, NHT, KS>(smem_lds, kt, lane, Qc, S[kt]);
     }
     // block-local softmax per head column (log2 domain)
     float mb[NHT], lb[NHT];
@@ -173,7 +199,7 @@ __global__ __launch_bounds__(256) void sel_fwd_kv_kernel(SelFwdArgs a) {
         V8 pb[NHT];
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) pb[ht] = pack8t<T>(S[2 * kk][ht], S[2 * kk + 1][ht]);
-        const uint32_t vt = smem_lds + OV + (kk >> 1) * TM::BYTES + 32 * (kk & 1) * TM::RB;
+        const uint32_t vt = smem_lds + L::OV + (kk >> 1) * TM::BYTES + 32 * (kk & 1) * TM::RB;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           const uint32_t o = vt + TM::colB(lane, f);
@@ -207,6 +233,126 @@ __global__ __launch_bounds__(256) void sel_fwd_kv_kernel(SelFwdArgs a) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) Qc[ht][s] = Qn[ht][s];
   }
+}
+
+// The backward's row statistic without attentionOut, KV-major like the forward: per entry
+// the G heads' query and dY rows are gathered as B operands, P^T = exp2(S^T scale log2 e -
+// lse2) from the passed statistics, dP^T (keys x heads) = V (A: row reads of the V tile) x
+// dY^T, and the entry's partial drow of each head, sum over the block's keys of P dP, is
+// stored at (entry - first entry of the window) N1 + KV head G + head.
+template <typename T, int DQK, int NHT, int KB>
+__global__ __launch_bounds__(256) void sel_drow_kv_kernel(SelFwdArgs a) {
+  using V8 = typename Mma<T>::v8;
+  using L = KvTiles<DQK, KB>;
+  using TM = typename L::TM;
+  constexpr int KS = DQK / 32, VS = kDv / 32, NKT = KB / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[L::SMEM];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const typename L::Unit wu = L::unit(a);
+  const int kvh = wu.kvh, e_begin = wu.e_begin, e_end = wu.e_end;
+  if (e_begin == e_end) return;  // whole workgroup
+  const int nkt = a.bs / 16;
+  const int G = a.G;
+  const T* q = static_cast<const T*>(a.q);
+  const T* dy = static_cast<const T*>(a.dy);
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  L::template stage<T>(a, wu, smem_lds);
+  __syncthreads();
+
+  // query and dY rows of entry e as B operands (column = head 16 ht + l16), and lse2 per head
+  auto load = [&](int e, V8 (&Qf)[NHT][KS], V8 (&Yf)[NHT][VS], float (&lse)[NHT]) {
+    const int64_t t = a.list[e] / a.cnt;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + l16;
+      const int64_t row = t * a.n1 + (int64_t)kvh * G + h;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        Qf[ht][s] = as_v8<T>(h < G ? ldg16(q + row * DQK + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+      for (int s = 0; s < VS; ++s)
+        Yf[ht][s] = as_v8<T>(h < G ? ldg16(dy + row * kDv + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0));
+      lse[ht] = h < G ? a.lse2[row] : INFINITY;
+    }
+  };
+
+  const int e_lo = (int)(a.t0 * a.cnt);
+  int e = e_begin + wave;
+  V8 Qc[NHT][KS], Yc[NHT][VS];
+  float lc[NHT];
+  if (e < e_end) load(e, Qc, Yc, lc);
+  for (; e < e_end; e += 4) {
+    V8 Qn[NHT][KS], Yn[NHT][VS];
+    float ln[NHT];
+    if (e + 4 < e_end) load(e + 4, Qn, Yn, ln);
+    float acc[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) acc[ht] = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      if (kt < nkt) {
+        f32x4 S[NHT], D[NHT];
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) S[ht] = D[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+        L::template scores<T, NHT, KS>(smem_lds, kt, lane, Qc, S);
+        const uint32_t vm = smem_lds + L::OV + (kt >> 2) * TM::BYTES + 16 * (kt & 3) * TM::RB;
+#pragma unroll
+        for (int s = 0; s < VS; ++s) {
+          const V8 va = as_v8<T>(lds_b128_at(vm + TM::rowA(lane, s)));
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) D[ht] = Mma<T>::run(va, Yc[ht][s], D[ht]);
+        }
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[ht] += __builtin_amdgcn_exp2f(S[ht][j] * a.scale_log2e - lc[ht]) * D[ht][j];
+      }
+    }
+    const int64_t r = (int64_t)(a.list[e] - e_lo) * a.n1 + (int64_t)kvh * G;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + l16;
+      const float d = group_sum(acc[ht]);
+      if (h < G && g == 0) a.part_d[r + h] = d;
+    }
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) Qc[ht][s] = Qn[ht][s];
+#pragma unroll
+      for (int s = 0; s < VS; ++s) Yc[ht][s] = Yn[ht][s];
+      lc[ht] = ln[ht];
+    }
+  }
+}
+
+// ndrow of each query row (token, head) of the window: minus the sum of its entries'
+// partials in slot order (eight loads in flight); slots with an out-of-range id have none.
+__global__ __launch_bounds__(256) void sel_drow_combine_kernel(SelFwdArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // row (t - t0) N1 + head
+  if (i >= (a.t1 - a.t0) * a.n1) return;
+  const int64_t tw = i / a.n1, t = a.t0 + tw;
+  const int hg = (int)(i - tw * a.n1), kvh = hg / a.G;
+  const int b = seq_of(a.cu_q, a.batch, t);
+  const int nblk = (int)((a.cu_kv[b + 1] - a.cu_kv[b]) / a.bs);
+  const int32_t* ids = a.topk + (t * a.n2 + kvh) * a.cnt;
+  const float* src = a.part_d + tw * a.cnt * a.n1 + hg;  // slot sl at + sl N1
+  float acc = 0.f;
+  for (int s0 = 0; s0 < a.cnt; s0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sl = s0 + j;
+      const int id = sl < a.cnt ? ids[sl] : -1;
+      x[j] = id >= 0 && id < nblk ? src[(int64_t)sl * a.n1] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += x[j];
+  }
+  a.ndrow[t * a.n1 + hg] = -acc;
 }
 
 // One wave per (token, KV head) of the window.  Lane l owns the 16-byte chunks l, l + 64,
@@ -311,25 +457,31 @@ __global__ __launch_bounds__(256) void sel_fwd_combine_kernel(SelFwdArgs a) {
   }
 }
 
-template <typename T>
+template <typename T, bool DROW>
 hipError_t launch_kv_t(const SelFwdArgs& a, hipStream_t s) {
   const int nkeys = a.n2 * a.nblk_total;
   if (nkeys == 0) return hipSuccess;
   const dim3 grid((unsigned)nkeys), block(256);
   const bool two = a.G > 16, wide = a.bs > 64;
-#define AB_FWD_KV(DQK)                                                                                \
+#define AB_KV(DQK, NHT, KB)                                                                           \
+  do {                                                                                                \
+    if (DROW) hipLaunchKernelGGL((sel_drow_kv_kernel<T, DQK, NHT, KB>), grid, block, 0, s, a);        \
+    else hipLaunchKernelGGL((sel_fwd_kv_kernel<T, DQK, NHT, KB>), grid, block, 0, s, a);              \
+  } while (0)
+#define AB_KV_D(DQK)                                                                                  \
   do {                                                                                                \
     if (two) {                                                                                        \
-      if (wide) hipLaunchKernelGGL((sel_fwd_kv_kernel<T, DQK, 2, 128>), grid, block, 0, s, a);        \
-      else hipLaunchKernelGGL((sel_fwd_kv_kernel<T, DQK, 2, 64>), grid, block, 0, s, a);              \
+      if (wide) AB_KV(DQK, 2, 128);                                                                   \
+      else AB_KV(DQK, 2, 64);                                                                         \
     } else {                                                                                          \
-      if (wide) hipLaunchKernelGGL((sel_fwd_kv_kernel<T, DQK, 1, 128>), grid, block, 0, s, a);        \
-      else hipLaunchKernelGGL((sel_fwd_kv_kernel<T, DQK, 1, 64>), grid, block, 0, s, a);              \
+      if (wide) AB_KV(DQK, 1, 128);                                                                   \
+      else AB_KV(DQK, 1, 64);                                                                         \
     }                                                                                                 \
   } while (0)
-  if (a.d_qk == 192) AB_FWD_KV(192);
-  else AB_FWD_KV(128);
-#undef AB_FWD_KV
+  if (a.d_qk == 192) AB_KV_D(192);
+  else AB_KV_D(128);
+#undef AB_KV_D
+#undef AB_KV
   return hipGetLastError();
 }
 
@@ -345,7 +497,19 @@ hipError_t launch_combine_t(const SelFwdArgs& a, hipStream_t s) {
 
 hipError_t launch_selected_forward_kv(const SelFwdArgs& a, hipStream_t s) {
   if (!selected_supported(a.d_qk, a.d_v, a.G, a.bs)) return hipErrorInvalidValue;
-  return a.is_f16 ? launch_kv_t<_Float16>(a, s) : launch_kv_t<__bf16>(a, s);
+  return a.is_f16 ? launch_kv_t<_Float16, false>(a, s) : launch_kv_t<__bf16, false>(a, s);
+}
+
+hipError_t launch_selected_drow_kv(const SelFwdArgs& a, hipStream_t s) {
+  if (!selected_supported(a.d_qk, a.d_v, a.G, a.bs)) return hipErrorInvalidValue;
+  return a.is_f16 ? launch_kv_t<_Float16, true>(a, s) : launch_kv_t<__bf16, true>(a, s);
+}
+
+hipError_t launch_selected_drow_combine(const SelFwdArgs& a, hipStream_t s) {
+  const int64_t rows = (a.t1 - a.t0) * a.n1;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sel_drow_combine_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_selected_forward_combine(const SelFwdArgs& a, hipStream_t s) {
