@@ -23,6 +23,12 @@
 // Pass 2 (sel_fwd_combine_kernel): one wave per (token, KV head): the cnt partials merged
 // in slot order into O, softmaxMax (natural units) and softmaxSum.  Slots whose id
 // is out of range have no partial (the index build skipped them and raised the flag).
+//
+// The same two passes give the backward's row statistic when attentionOut is not passed
+// (the page lists it as optional): drow = sum_j P_j dP_j over the gathered rows, with P from
+// the passed statistics and dP = dY V^T, per entry in sel_drow_kv_kernel (query and dY rows
+// gathered, 10 KB per entry at G = 16, instead of the block's K and V rows) and summed over
+// the slots in order by sel_drow_combine_kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 
