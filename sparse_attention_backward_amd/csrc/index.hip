@@ -41,17 +41,21 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n, in
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
-__device__ __forceinline__ bool decode_entry(const SelArgs& a, int64_t e, int64_t& t, int& slot, int& key) {
+// entry e = (t n2 + kvh) cnt + slot with topk value id
+__device__ __forceinline__ bool decode_id(const SelArgs& a, int64_t e, int id, int64_t& t, int& slot, int& key) {
   slot = (int)(e % a.cnt);
   const int64_t tn = e / a.cnt;
   const int kvh = (int)(tn % a.n2);
   t = tn / a.n2;
   const int b = seq_of(a.cu_q, a.batch, t);
   const int nblk = a.blkoff[b + 1] - a.blkoff[b];
-  const int id = a.topk[e];
   if (id < 0 || id >= nblk) return false;
   key = kvh * a.nblk_total + a.blkoff[b] + id;
   return true;
+}
+
+__device__ __forceinline__ bool decode_entry(const SelArgs& a, int64_t e, int64_t& t, int& slot, int& key) {
+  return decode_id(a, e, a.topk[e], t, slot, key);
 }
 
 __global__ __launch_bounds__(256) void idx_count_kernel(SelArgs a, int64_t total) {
@@ -213,7 +217,9 @@ __global__ __launch_bounds__(1024) void idx_colpass_kernel(int32_t* tab, int nch
 }
 
 // One wave per chunk.  Per round of 64 consecutive entries: rank = number of lower lanes
-// with the same key; the highest lane of each key advances that key's base.
+// with the same key; the highest lane of each key advances that key's base.  The lanes of
+// one key are found bit by bit (one ballot per key bit); the next round's ids are loaded
+// while a round is placed.
 __global__ __launch_bounds__(64) void idx_fill_ordered_kernel(SelArgs a, int64_t total, int64_t chunk, int nkeys,
                                                               const int32_t* tab) {
   extern __shared__ int32_t base[];
@@ -221,21 +227,24 @@ __global__ __launch_bounds__(64) void idx_fill_ordered_kernel(SelArgs a, int64_t
   const int32_t* row = tab + (int64_t)blockIdx.x * nkeys;
   for (int k = lane; k < nkeys; k += 64) base[k] = row[k];
   __syncthreads();
+  const int kbits = nkeys > 1 ? 32 - __builtin_clz(nkeys - 1) : 0;
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
   const int64_t e0 = (int64_t)blockIdx.x * chunk, e1 = min(total, e0 + chunk);
+  int id_next = e0 + lane < e1 ? a.topk[e0 + lane] : -1;
   for (int64_t r0 = e0; r0 < e1; r0 += 64) {
     const int64_t e = r0 + lane;
+    const int id = id_next;
+    id_next = e + 64 < e1 ? a.topk[e + 64] : -1;
     int64_t t = 0; int slot = 0, key = -1;
-    if (e >= e1 || !decode_entry(a, e, t, slot, key)) key = -1;
-    int rank = 0;
-    bool last = true;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const int kj = __builtin_amdgcn_readlane(key, j);
-      if (kj == key) {
-        if (j < lane) ++rank;
-        if (j > lane) last = false;
-      }
+    if (e >= e1 || !decode_id(a, e, id, t, slot, key)) key = -1;
+    uint64_t same = __ballot(key >= 0);
+    for (int bit = 0; bit < kbits; ++bit) {
+      const bool one = (key >> bit) & 1;
+      const uint64_t bb = __ballot(one);
+      same &= one ? bb : ~bb;
     }
+    const int rank = __popcll(same & below);
+    const bool last = (same >> lane) <= 1;  // no higher lane holds the key
     int pos = 0;
     if (key >= 0) pos = base[key] + rank;
     __syncthreads();  // every lane has read its base before any is advanced
