@@ -42,7 +42,11 @@
  * library allocates no device memory.  Outputs are fully overwritten (KV rows that
  * no query attends receive 0).  Work is enqueued on `hip_stream` (NULL = default
  * stream) and returns before it completes; inputs, outputs and workspace must stay
- * valid until the stream reaches that point.
+ * valid until the stream reaches that point.  The small per-call tables (sequence
+ * offsets, work lists) pass through a ring of four pinned host slots per device: the
+ * first call on a device, and a call whose tables outgrow its slot, allocate pinned
+ * host memory (held until the process ends); a call waits on the host only when the
+ * slot it takes still serves a call four calls back that the GPU has not reached.
  *
  * Errors: every check runs before anything is enqueued; on failure nothing is
  * enqueued and no output is touched.  Out-of-range topk ids are caller errors: the

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -522,7 +523,7 @@ std::vector<uint8_t> pack_tables(const attn_bwd_problem_t* p, const Plan& pl) {
 struct ProfRec { const char* name; hipEvent_t a, b; };
 struct ProfTotal { const char* name; double ms; int64_t n; };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
 std::vector<ProfRec> g_prof_pending;
 std::vector<ProfTotal> g_prof_totals;
 std::vector<hipEvent_t> g_prof_pool;
@@ -541,7 +542,7 @@ hipEvent_t prof_event() {
 // Run one launcher; while profiling is on, bracket it with events on the stream.
 template <typename F>
 hipError_t timed(const char* name, hipStream_t s, F&& launch) {
-  if (!g_prof_on) return launch();
+  if (!g_prof_on.load(std::memory_order_relaxed)) return launch();
   hipEvent_t a, b;
   {
     std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -1047,7 +1048,7 @@ attn_status_t attn_bwd_check_index_flag(const attn_bwd_problem_t* p, const void*
 
 attn_status_t attn_bwd_profiling(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = enable != 0;
+  g_prof_on.store(enable != 0, std::memory_order_relaxed);
   return ATTN_OK;
 }
 
