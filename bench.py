@@ -7,8 +7,10 @@ A step is one complete C-ABI call (row statistics, schedule upload, index, every
 over one batch of synthetic input already resident in HBM.  The headline workload is
 the largest single-GPU one, selected bf16 at S = 128K (N1 64, N2 4, D 192 / 128, blocks
 of 64, 32 per token); `extra` holds one line each for the dense varlen bf16 workload
-(causal, rope 128 + 64, GQA 32/8, four seeded lengths), selected at S = 32K, and the
-Zipf-skewed varlen selected workload in both determinism settings.
+(causal, rope 128 + 64, GQA 32/8, four seeded lengths), selected at S = 32K, the
+Zipf-skewed varlen selected workload in both determinism settings, the selected backward
+at S = 32K without attentionOut, the selected forward at S = 128K and S = 32K, and the
+lightning-indexer backward (one 8K sequence, 64 heads, topK 2048) with either dK mode.
 `value` is algorithmic TFLOP/s: attended (query row, key row) pairs x 2(3 D_qk + 2 D_v),
 causal pairs only (the five GEMMs S, dP, dV, dQ, dK; recomputation is not counted).
 Before the warmup calls every workload repeats its call for --prewarm-ms of GPU time, so
@@ -73,7 +75,11 @@ KERNEL_SOURCES = {
     "selected_kv_major": ("sel_kv_kernel", "sel_kv.hip"),
     "selected_dq_reduce": ("dq_reduce_kernel", "sel_reduce.hip"),
     "selected_forward": ("sel_fwd_kv_kernel", "sel_fwd_kv.hip"),
+    "selected_forward_combine": ("sel_fwd_combine_kernel", "sel_fwd_kv.hip"),
+    "selected_row_stat": ("sel_drow_kv_kernel", "sel_fwd_kv.hip"),
+    "selected_index": ("idx_fill_ordered_kernel", "index.hip"),
     "indexer_query_major": ("idx_bwd_kernel", "indexer.hip"),
+    "indexer_dk_reduce": ("idx_dk_reduce_kernel", "indexer.hip"),
     "row_stats": ("preprocess_kernel", "preprocess.hip"),
 }
 CSRC = os.path.join(ROOT, "sparse_attention_backward_amd", "csrc")
@@ -485,6 +491,11 @@ def measure_forward(wl: int, steps: int, warmup: int, prewarm_ms=300.0):
     return rec
 
 
+def indexer_record_name(w, dk_atomic: bool) -> str:
+    """Workload name of the indexer's counter records: the two dK modes run different kernels."""
+    return f"{w.name}-{'atomic' if dk_atomic else 'ordered'}"
+
+
 def measure_indexer(dk_atomic: bool, steps: int, warmup: int, prewarm_ms=300.0):
     """The lightning-indexer backward (attn_bwd_indexer) on its 8K workload: three GEMMs per
     (token, key head, selected key) -- S = Q K^T, dQ = R K, dK shares = R^T Q -- i.e.
@@ -530,9 +541,11 @@ def measure_indexer(dk_atomic: bool, steps: int, warmup: int, prewarm_ms=300.0):
            "value": round(fl / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
            "steps": steps, "pct_bf16_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
            "roofline": {"kernel": "indexer_query_major", "bound": "mfma", "avg_ms": tot_ms / max(n, 1),
+                        "launches_per_call": n / max(steps, 1),
                         "achieved": fl / (kms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": fl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop_per_call": fl,
-                        "traffic": recorded_counters("indexer_query_major", w.name).get("traffic_bytes_per_launch")},
+                        "traffic": recorded_counters("indexer_query_major", indexer_record_name(w, dk_atomic))
+                        .get("traffic_bytes_per_launch")},
            "kernels_ms_per_call": {k: round(v[0] / steps, 4) for k, v in kernels.items()},
            "prewarm_ms": round(spent, 1)}
     del x, ws, dq, dk, dw
@@ -559,8 +572,12 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' lines")
     ap.add_argument("--indexer-only", action="store_true",
                     help="only the lightning-indexer backward lines (for profiling runs)")
+    ap.add_argument("--indexer-mode", choices=("both", "ordered", "atomic"), default="both",
+                    help="with --indexer-only: which dK mode(s) to run")
     ap.add_argument("--forward-only", action="store_true",
                     help="only the selected forward lines (for profiling runs)")
+    ap.add_argument("--forward-workload", type=int, default=0,
+                    help="with --forward-only: this workload alone (0: all forward workloads)")
     ap.add_argument("--no-out", action="store_true",
                     help="selected headline without attentionOut (the row statistic from the gathered rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -596,12 +613,12 @@ def main(argv=None):
         return 0
 
     if args.forward_only:
-        print(json.dumps([measure_forward(wl, args.steps, args.warmup, args.prewarm_ms) for wl in FORWARD_RUNS]),
-              flush=True)
+        wls = (args.forward_workload,) if args.forward_workload else FORWARD_RUNS
+        print(json.dumps([measure_forward(wl, args.steps, args.warmup, args.prewarm_ms) for wl in wls]), flush=True)
         return 0
     if args.indexer_only:
-        print(json.dumps([measure_indexer(a, args.steps, args.warmup, args.prewarm_ms) for a in (False, True)]),
-              flush=True)
+        modes = {"both": (False, True), "ordered": (False,), "atomic": (True,)}[args.indexer_mode]
+        print(json.dumps([measure_indexer(a, args.steps, args.warmup, args.prewarm_ms) for a in modes]), flush=True)
         return 0
     w, x, rec = measure(args.workload, args.steps, args.warmup, args.deterministic, args.window_tokens,
                         args.prewarm_ms, with_out=not args.no_out)
