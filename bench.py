@@ -339,6 +339,12 @@ def roofline_for(w: W.Workload, kernels: dict, steps: int, call_ms: float):
     return out
 
 
+def progress(rec: dict) -> None:
+    """One line on stderr as each measured record completes."""
+    print(f"[bench] {rec.get('workload')} {rec.get('pass', 'backward')}: {rec.get('ms_per_step')} ms per call",
+          file=sys.stderr, flush=True)
+
+
 def measure(wl: int, steps: int, warmup: int, deterministic=False, window_tokens=0, prewarm_ms=300.0, with_out=True):
     """One bench record for workload `wl`: value, timing, roofline and per-kernel times."""
     w = W.config(wl)
@@ -363,6 +369,7 @@ def measure(wl: int, steps: int, warmup: int, deterministic=False, window_tokens
         "kernel_launches_per_call": {k: v[1] / steps for k, v in kernels.items()},
         "prewarm_ms": round(spent, 1),
     }
+    progress(rec)
     return w, x, rec
 
 
@@ -488,6 +495,7 @@ def measure_forward(wl: int, steps: int, warmup: int, prewarm_ms=300.0):
            "prewarm_ms": round(spent, 1)}
     del x, out, smax, ssum, ws
     torch.cuda.empty_cache()
+    progress(rec)
     return rec
 
 
@@ -550,6 +558,7 @@ def measure_indexer(dk_atomic: bool, steps: int, warmup: int, prewarm_ms=300.0):
            "prewarm_ms": round(spent, 1)}
     del x, ws, dq, dk, dw
     torch.cuda.empty_cache()
+    progress(rec)
     return rec
 
 
