@@ -134,3 +134,41 @@ def test_selected_bsnd_layout_matches_tnd(dtype):
     for a, b in zip(*res):
         assert torch.equal(a, b)
     check_against_oracle(w, dict(zip(("dq", "dk", "dv"), res[1][3:])), oracle_backward(w, x))
+
+
+@pytest.mark.parametrize("window_tokens", [37, 100])
+def test_selected_forward_windows_match_single_window(window_tokens):
+    """Windows of query tokens (the partials of one window at a time): each entry's partial and
+    each token's merge are the same computations, so the bits do not change."""
+    w = W.small_selected(seqlens=(256, 130), seqlens_kv=(256, 192), block_size=64, block_count=3, index_dist="zipf")
+    x = W.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    g = lambda t: t.to(dev).contiguous()  # noqa: E731
+    res = []
+    for wt in (0, window_tokens):
+        fw = sab.Problem.selected(w.cu_q, w.cu_kv, w.n1, w.n2, w.d_qk, w.d_v, w.scale, w.block_size, w.block_count,
+                                  forward=True, window_tokens=wt)
+        res.append(sab.selected_forward(fw, g(x["query"]), g(x["key"]), g(x["value"]), g(x["topk"])))
+        torch.cuda.synchronize()
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+    o, m, l = O.forward_selected(f64(x["query"]), f64(x["key"]), f64(x["value"]), x["topk"].numpy(), w.cu_q,
+                                 w.cu_kv, w.n1, w.n2, w.scale, w.block_size)
+    assert_close(f"{w.name}:out windows", f64(res[1][0]), o, w.dtype)
+    _check_stats(w.name, res[1][1], res[1][2], m, l)
+
+
+def test_selected_backward_without_out_windows_match_single_window():
+    """The row statistic without attentionOut runs over the backward's windows: its sums do not
+    depend on them, so dQ keeps its bits; dK / dV differ only by the fp32 order of the windows'
+    partial sums."""
+    w = W.small_selected(seqlens=(256, 130), seqlens_kv=(256, 192), block_size=64, block_count=3)
+    x = W.make_inputs(w)
+    _, smax, ssum = oracle_forward(w, x)
+    a = gpu_backward(w, x, None, smax, ssum, deterministic=True)
+    b = gpu_backward(w, x, None, smax, ssum, deterministic=True, window_tokens=41)
+    assert torch.equal(a["dq"], b["dq"])
+    for n in ("dk", "dv"):
+        d = (a[n].double() - b[n].double()).abs().max().item()
+        assert d <= 1e-2 * a[n].double().abs().max().item(), (n, d)
+    check_against_oracle(w, b, oracle_backward(w, x))
