@@ -251,10 +251,11 @@ attn_status_t attn_bwd_selected_index(const attn_bwd_problem_t* p, const int32_t
  * weights [T1, n1], dy [T1, n2, topK]; indices int32 [T1, n2, topK] (key positions inside
  * the token's sequence; a repeated index counts twice; an out-of-range one contributes
  * nothing and raises the flag of attn_bwd_check_index_flag); outputs dq [T1, n1, 128],
- * dk [T2, n2, 128], dweights [T1, n1].  dK: by default each (token, key head, slot)'s fp32
- * share of dK is kept and the shares of a key row are added in ascending (token, slot) order
- * through an inverted index, over windows of query tokens whose shares take at most 8 GiB
- * (sel_window_tokens caps the window further) -- deterministic whatever `deterministic` says;
+ * dk [T2, n2, 128], dweights [T1, n1].  dK: by default each (token, key head, slot)'s share
+ * of dK is kept (rounded to bf16) and the shares of a key row are added in fp32 in ascending
+ * (token, slot) order through an inverted index, over windows of query tokens whose shares
+ * take at most 8 GiB (sel_window_tokens caps the window further) -- deterministic whatever
+ * `deterministic` says;
  * dkdv_atomic = 1 with deterministic = 0 scatters the shares with fp32 atomics instead.
  * dQ and dW have one writer per row in every mode. */
 attn_status_t attn_bwd_indexer(const attn_bwd_problem_t* p,

@@ -65,7 +65,7 @@ constexpr uint64_t kDenseDsAutoMax = 8ull << 30;  // stored dS above this size: 
 // restored; with skewed ids each window's longest list runs alone), so they are made as long
 // as the cap allows; the caller can ask for shorter ones (sel_window_tokens).
 constexpr uint64_t kSelShareMax = 64ull << 30;
-constexpr uint64_t kIdxContribMax = 8ull << 30;  // indexer, deterministic: dK shares of one window at most
+constexpr uint64_t kIdxContribMax = 8ull << 30;  // indexer, ordered dK: bf16 dK shares of one window at most
 
 // Dense schedule tables.
 //  * Work items of the KV-major kernel: (sequence, 128-key tile, KV head, query-tile range,
@@ -287,7 +287,7 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     // deterministic mode: the fp32 dK shares of one window of query tokens take at most
     // kIdxContribMax; windows of equal length but the last
     if (p->sel_window_tokens < 0) return ATTN_ERR_INVALID;
-    const uint64_t per_token = (uint64_t)p->n2 * topk * p->d_qk * 4;
+    const uint64_t per_token = (uint64_t)p->n2 * topk * p->d_qk * 2;
     int64_t w = std::max<int64_t>(1, (int64_t)(kIdxContribMax / per_token));
     if (p->sel_window_tokens > 0) w = std::min<int64_t>(w, p->sel_window_tokens);
     pl.nwin = (int)std::max<int64_t>(1, (pl.T1 + w - 1) / w);
@@ -384,7 +384,7 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
       pl.off_list = o;    o = align_up(o + 4 * (size_t)pl.entries);
       pl.off_scratch = o; o = align_up(o + 8 * (size_t)pl.entries);
       pl.off_contrib = o;
-      o = align_up(o + 4 * (size_t)std::min<int64_t>(pl.win_tokens, pl.T1) * p->n2 * p->block_count * p->d_qk);
+      o = align_up(o + 2 * (size_t)std::min<int64_t>(pl.win_tokens, pl.T1) * p->n2 * p->block_count * p->d_qk);
       if (pl.nwin > 1) { pl.off_wofs = o; o = align_up(o + 4 * nkeys * (size_t)(pl.nwin + 1)); }
     }
     pl.total = o;
@@ -1013,7 +1013,7 @@ attn_status_t attn_bwd_indexer(const attn_bwd_problem_t* p, const void* q, const
         }) != hipSuccess)
       return ATTN_ERR_HIP;
     a.offsets = x.offsets; a.list = x.list; a.wofs = x.wofs; a.nwin = pl.nwin;
-    a.contrib = at<float>(workspace, pl.off_contrib);
+    a.contrib = at<uint16_t>(workspace, pl.off_contrib);
     for (int w = 0; w < pl.nwin; ++w) {
       a.win = w;
       const int64_t t0 = std::min<int64_t>(pl.T1, (int64_t)w * pl.win_tokens);

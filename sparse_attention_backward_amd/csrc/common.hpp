@@ -69,6 +69,7 @@ __device__ __forceinline__ i16x4 lds_tr16_at(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>((uintptr_t)addr));
 }
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 __device__ __forceinline__ void lds_st16_at(uint32_t addr, uint4 v) {
   *reinterpret_cast<lds_u32x4*>((uintptr_t)addr) = u32x4{v.x, v.y, v.z, v.w};

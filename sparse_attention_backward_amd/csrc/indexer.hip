@@ -12,15 +12,17 @@
 //   S^T (keys x heads)  = K (A: the wave's 16 gathered key rows, 16 bytes per lane straight
 //                         from global memory) x Q^T (B: the head rows, resident);
 //   R^T                 = where(S^T > 0, dy W, 0); dW += S^T dy per head (lane);
-//   dQ^T (feat x heads) += K^T (A: column reads of the key rows, staged in LDS) x R^T (B: the
-//                         C tile as it stands, k = the 16 keys);
+//   dQ^T (feat x heads) += K^T (A: column reads of the key rows, staged in LDS) x R^T (B: read
+//                         back from LDS), each wave over its quarter of the features and all
+//                         64 keys of the chunk, 16 (one wave's) per k-step;
 //   C^T (feat x keys)   = Q^T (A: column reads of the Q tile in LDS) x R (B: column reads of
 //                         R^T written to LDS as [head][key]);  C is the key rows' share of dK.
-// C goes either to an fp32 accumulator with atomics (non-deterministic mode, the page's
-// default) or, row by row, to a contribution buffer indexed by (token, key head, slot) that
-// a second kernel sums over each key's inverted-index list in ascending order
-// (deterministic).  dQ (the four waves' partials added in LDS) and dW have one writer each.
-// An out-of-range index contributes nothing and raises the flag.
+// C goes either, row by row, to a share buffer indexed by (token, key head, slot), rounded
+// to bf16, that a second kernel sums in fp32 over each key's inverted-index list in
+// ascending order (deterministic; the default), or to an fp32 accumulator with atomics.  The
+// next chunk's key rows, ids and dy load while a chunk computes.  dQ (each wave its own
+// features) and dW (the four waves' sums added in LDS) have one writer each.  An
+// out-of-range index contributes nothing and raises the flag.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,16 +40,15 @@ __device__ __forceinline__ float group_sum4(float x) {
 
 template <int NHT, bool ATOMIC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void idx_bwd_kernel(IdxArgs a) {
-  constexpr int D = kIdxD, KS = D / 32, NF = D / 16;
+  constexpr int D = kIdxD, KS = D / 32;
+  constexpr int NFQ = D / 64;                  // dQ feature tiles of a wave: features 32 w .. + 31
   constexpr int GP = 16 * NHT;                 // padded head count
   using TQ = RowTile<D / 8>;                   // Q tile / key sub-tiles: rows of 256 bytes
   constexpr int OQ = 0;                        // Q tile: GP rows (64-row tile)
   constexpr int OK = TQ::BYTES;                // key rows: 4 waves x 16 rows (one 64-row tile)
   constexpr int OR = OK + TQ::BYTES;           // R^T as [head][16 keys] bf16 per wave: GP x 32 bytes
   constexpr int RB = GP * 32;
-  constexpr int SMEM_MAIN = OR + 4 * RB;
-  constexpr int SMEM_RED = 2 * NF * NHT * 64 * 16;  // dQ partials of two waves at a time
-  constexpr int SMEM = SMEM_MAIN > SMEM_RED ? SMEM_MAIN : SMEM_RED;
+  constexpr int SMEM = OR + 4 * RB;
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -80,41 +81,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     const int h = 16 * ht + l16;
     wv[ht] = h < G ? bf2f(wts[qrow0 + h]) : 0.f;
   }
-  f32x4 dQ[NF][NHT];
+  // dQ^T of this wave's features 32 w .. + 31 (tiles 2 w, 2 w + 1) over every key of the chunk
+  f32x4 dQ[NFQ][NHT];
 #pragma unroll
-  for (int f = 0; f < NF; ++f)
+  for (int f = 0; f < NFQ; ++f)
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) dQ[f][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
   float dW[NHT];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) dW[ht] = 0.f;
-  __syncthreads();  // Q tile in LDS
 
   const uint32_t ksub = smem_lds + OK + 16 * w * TQ::RB;    // this wave's 16 key rows
   const uint32_t rt = smem_lds + OR + w * RB;               // this wave's R^T [head][key]
   const int32_t* ids = a.indices + unit * a.topk;
   const uint16_t* dyrow = dyp + unit * a.topk;
 
-  for (int c0 = 0; c0 < a.topk; c0 += kIdxChunk) {
-    // this lane's key (for the A operand and the stores): slot c0 + 16 w + l16
-    const int slot = c0 + 16 * w + l16;
-    const int id = slot < a.topk ? ids[slot] : -1;
-    const bool kvalid = slot < a.topk && id >= 0 && id < S2;
-    if (slot < a.topk && !kvalid && a.flag) a.flag[0] = 1;
-    const int64_t krow = (kv0 + (kvalid ? id : 0)) * a.n2 + kvh;
+  // the gathered inputs of chunk c0: this lane's key row (slot c0 + 16 w + l16) 16 bytes per
+  // k-step, and dy of the keys 4 g .. 4 g + 3 of the wave's 16 (the rows of its S^T values)
+  struct ChunkIn {
     uint4 kx[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) kx[s] = kvalid ? ldg16(k + krow * D + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
-    // dy of the keys 4 g .. 4 g + 3 of the wave's 16 (the rows of this lane's S^T values)
     float dyk[4];
+    int id;
+  };
+  auto load_chunk = [&](int c0, ChunkIn& in) {
+    const int slot = c0 + 16 * w + l16;
+    in.id = slot < a.topk ? ids[slot] : -1;
+    const bool kvalid = slot < a.topk && in.id >= 0 && in.id < S2;
+    const int64_t krow = (kv0 + (kvalid ? in.id : 0)) * a.n2 + kvh;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) in.kx[s] = kvalid ? ldg16(k + krow * D + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int sl = c0 + 16 * w + 4 * g + j;
-      dyk[j] = sl < a.topk ? bf2f(dyrow[sl]) : 0.f;
+      in.dyk[j] = sl < a.topk ? bf2f(dyrow[sl]) : 0.f;
     }
+  };
+  ChunkIn cur;
+  load_chunk(0, cur);
+  __syncthreads();  // Q tile in LDS
+
+  for (int c0 = 0; c0 < a.topk; c0 += kIdxChunk) {
+    const int slot = c0 + 16 * w + l16;
+    const bool kvalid = slot < a.topk && cur.id >= 0 && cur.id < S2;
+    if (slot < a.topk && !kvalid && a.flag) a.flag[0] = 1;
     // key rows into LDS: lane (l16, g) holds chunks 4 s + g of key row l16
 #pragma unroll
-    for (int s = 0; s < KS; ++s) lds_st16_at(ksub + TQ::off(l16, 4 * s + g), kx[s]);
+    for (int s = 0; s < KS; ++s) lds_st16_at(ksub + TQ::off(l16, 4 * s + g), cur.kx[s]);
     // S^T = K Q^T
     f32x4 St[NHT];
 #pragma unroll
@@ -122,44 +134,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        acc = mfma_16x16x32(__builtin_bit_cast(bf16x8, kx[s]), lds_b128_at(smem_lds + OQ + 16 * ht * TQ::RB + TQ::rowA(lane, s)),
-                            acc);
+        acc = mfma_16x16x32(__builtin_bit_cast(bf16x8, cur.kx[s]),
+                            lds_b128_at(smem_lds + OQ + 16 * ht * TQ::RB + TQ::rowA(lane, s)), acc);
       St[ht] = acc;
     }
     // R^T, dW, and R^T -> LDS as [head][key] (8 bytes: keys 4 g .. + 3 of head 16 ht + l16)
-    i16x4 Rb[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       f32x4 r;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float s = St[ht][j];
-        dW[ht] += fmaxf(s, 0.f) * dyk[j];
-        r[j] = s > 0.f ? dyk[j] * wv[ht] : 0.f;
+        const float sv = St[ht][j];
+        dW[ht] += fmaxf(sv, 0.f) * cur.dyk[j];
+        r[j] = sv > 0.f ? cur.dyk[j] * wv[ht] : 0.f;
       }
-      Rb[ht] = pack4(r);
-      *reinterpret_cast<__attribute__((address_space(3))) i16x4*>((uintptr_t)(rt + (16 * ht + l16) * 32 + 8 * g)) = Rb[ht];
+      *reinterpret_cast<__attribute__((address_space(3))) i16x4*>((uintptr_t)(rt + (16 * ht + l16) * 32 + 8 * g)) = pack4(r);
     }
-    asm volatile("" ::: "memory");  // LDS writes of this wave come before its transposed reads
-    // dQ^T += K^T R^T (k = the 16 keys: 4 per lane group)
+    // the next chunk's inputs load while this one computes
+    ChunkIn nxt;
+    if (c0 + kIdxChunk < a.topk) load_chunk(c0 + kIdxChunk, nxt);
+    __syncthreads();  // every wave's key rows and R^T in LDS
+    // dQ^T (features 32 w .. + 31) += K^T R^T over the 64 keys, 16 (one wave's) per k-step
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const i16x4 kt = lds_tr16_at(ksub + TQ::colB(lane, f));
+    for (int ks = 0; ks < 4; ++ks) {
+      i16x4 rb[NHT];
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) dQ[f][ht] = mfma_16x16x16(kt, Rb[ht], dQ[f][ht]);
+      for (int ht = 0; ht < NHT; ++ht)
+        rb[ht] = *reinterpret_cast<const __attribute__((address_space(3))) i16x4*>(
+            (uintptr_t)(smem_lds + OR + ks * RB + (16 * ht + l16) * 32 + 8 * g));
+#pragma unroll
+      for (int f = 0; f < NFQ; ++f) {
+        const i16x4 kt = lds_tr16_at(smem_lds + OK + 16 * ks * TQ::RB + TQ::colB(lane, NFQ * w + f));
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) dQ[f][ht] = mfma_16x16x16(kt, rb[ht], dQ[f][ht]);
+      }
     }
+    __syncthreads();  // every wave is done with the key rows and R^T of this chunk
     // C^T = Q^T R (k = heads, 16 per step): this wave's 16 keys' shares of dK
     i16x4 rk[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) rk[ht] = lds_tr16_at(rt + (16 * ht + 4 * g + (l16 >> 2)) * 32 + 8 * (l16 & 3));
-    // The C tiles go out through this wave's key-row slot of LDS (4 KiB, free once the dQ
-    // product has read it), 64 features at a time as [16 keys][16 chunks of 16 B] with chunk c
-    // of row r at c ^ r, so that every global store or atomic covers whole key rows instead
-    // of 16 rows x 64 bytes.  C tile of feature tile f: lane holds key l16 of the wave,
-    // features 16 f + 4 g + (0..3).
-    const int cslot = c0 + 16 * w + l16;
-    const int cid = cslot < a.topk ? ids[cslot] : -1;
-    const int cvalid = cslot < a.topk && cid >= 0 && cid < S2;
+    // The C tiles go out through this wave's key-row slot of LDS (4 KiB, free now that every
+    // wave's dQ product has read it), 64 features at a time as [16 keys][16 chunks of 16 B]
+    // with chunk c of row r at c ^ r, so that every global store or atomic covers whole key
+    // rows instead of 16 rows x 64 bytes.  C tile of feature tile f: lane holds key l16 of
+    // the wave, features 16 f + 4 g + (0..3).
+    const int cid = cur.id;
+    const int cvalid = kvalid;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -180,72 +201,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
           if (__shfl(cvalid, r)) atomicAdd(a.dk_acc + ((kv0 + rid) * a.n2 + kvh) * D + 64 * hf + lane, v);
         }
       } else {
-        // four key rows per instruction: lane = row 4 i + lane / 16, chunk lane % 16
+        // four key rows per instruction: lane = row 4 i + lane / 16, chunk lane % 16; the
+        // share leaves as bf16 (8 bytes per lane, 128 contiguous bytes per row half)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * i + (lane >> 4), c = lane & 15;
           const f32x4 v = lds_f32x4_at(ksub + r * 256 + 16 * (c ^ r));
           const int sl = c0 + 16 * w + r;
-          if (sl < a.topk)
-            sts16_stream(a.contrib + ((unit - a.unit0) * a.topk + sl) * D + 64 * hf + 4 * c, __builtin_bit_cast(uint4, v));
+          if (sl < a.topk) {
+            const u32x2 x = {(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                             (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(a.contrib + ((unit - a.unit0) * a.topk + sl) * D + 64 * hf + 4 * c));
+          }
         }
       }
     }
     asm volatile("" ::: "memory");  // this chunk's LDS reads come before the next chunk's writes
+    cur = nxt;
   }
 
-  // ---- dW: per head, over the lane groups and the four waves ----
+  // ---- dW: per head, over the lane groups and the four waves (in the Q tile's space, once
+  // every wave has done its last C^T product) ----
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
-    const float s = group_sum4(dW[ht]);
-    if (g == 0) red[w * GP + 16 * ht + l16] = s;
+    const float sv = group_sum4(dW[ht]);
+    if (g == 0) red[w * GP + 16 * ht + l16] = sv;
   }
   __syncthreads();
   if (tid < G) {
-    const float s = (red[tid] + red[GP + tid]) + (red[2 * GP + tid] + red[3 * GP + tid]);
-    static_cast<uint16_t*>(a.dweights)[qrow0 + tid] = f2bf(s);
+    const float sv = (red[tid] + red[GP + tid]) + (red[2 * GP + tid] + red[3 * GP + tid]);
+    static_cast<uint16_t*>(a.dweights)[qrow0 + tid] = f2bf(sv);
   }
-  __syncthreads();
-  // ---- dQ: the four waves' partials added in LDS (waves 2, 3 then 1), then stored ----
-  // lane holds head 16 ht + l16, features 16 f + 4 g + (0..3) of tile (f, ht)
-  f32x4* part = reinterpret_cast<f32x4*>(smem);
-  auto pidx = [&](int f, int ht) { return (f * NHT + ht) * 64 + lane; };
-  if (w >= 2) {
+  // ---- dQ: this wave's features, every head; lane holds head 16 ht + l16, features
+  // 32 w + 16 f + 4 g + (0..3) ----
+  uint16_t* dq = static_cast<uint16_t*>(a.dq);
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int h = 16 * ht + l16;
+    if (h >= G) continue;
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) part[(w - 2) * NF * NHT * 64 + pidx(f, ht)] = dQ[f][ht];
-  }
-  __syncthreads();
-  if (w < 2) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) dQ[f][ht] += part[w * NF * NHT * 64 + pidx(f, ht)];
-  }
-  __syncthreads();
-  if (w == 1) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) part[pidx(f, ht)] = dQ[f][ht];
-  }
-  __syncthreads();
-  if (w == 0) {
-    uint16_t* dq = static_cast<uint16_t*>(a.dq);
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      const int h = 16 * ht + l16;
-      if (h >= G) continue;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const f32x4 v = dQ[f][ht] + part[pidx(f, ht)];
-        const uint2 o = make_uint2((uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
-                                   (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16));
-        *reinterpret_cast<uint2*>(dq + (qrow0 + h) * D + 16 * f + 4 * g) = o;
-      }
+    for (int f = 0; f < NFQ; ++f) {
+      const f32x4 v = dQ[f][ht];
+      const uint2 o = make_uint2((uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                                 (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16));
+      *reinterpret_cast<uint2*>(dq + (qrow0 + h) * D + 16 * (NFQ * w + f) + 4 * g) = o;
     }
   }
 }
@@ -267,15 +268,16 @@ __global__ __launch_bounds__(256) void idx_dk_reduce_kernel(IdxArgs a) {
   auto share = [&](int ent) {
     const int64_t t = ent / a.topk, slot = ent - t * a.topk;
     const int64_t u = t * a.n2 + kvh - a.unit0;
-    return __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(a.contrib + (u * a.topk + slot) * kIdxD + 2 * lane));
+    const uint32_t x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.contrib + (u * a.topk + slot) * kIdxD + 2 * lane));
+    return f32x2{bf2f((uint16_t)(x & 0xffffu)), bf2f((uint16_t)(x >> 16))};
   };
   int e = e0;
-  for (; e + 8 <= e1; e += 8) {  // eight loads in flight, added in list order
-    f32x2 c[8];
+  for (; e + 16 <= e1; e += 16) {  // sixteen loads in flight, added in list order
+    f32x2 c[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = share(a.list[e + i]);
+    for (int i = 0; i < 16; ++i) c[i] = share(a.list[e + i]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
       acc.x += c[i][0];
       acc.y += c[i][1];
     }

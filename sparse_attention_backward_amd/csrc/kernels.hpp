@@ -175,7 +175,7 @@ struct IdxArgs {
   const int32_t* indices;   // [T1, N2, topk] key positions in the token's sequence
   void* dq; void* dk; void* dweights;
   float* dk_acc;            // [T2, N2, D] fp32 accumulator of dK
-  float* contrib;           // deterministic mode: [units of the window, topk, D] fp32 shares of dK
+  uint16_t* contrib;        // ordered mode: [units of the window, topk, D] bf16 shares of dK
   const int64_t* cu_q; const int64_t* cu_kv;
   int32_t* flag;            // raised on an out-of-range index
   int batch, n1, n2, G, d, topk;
