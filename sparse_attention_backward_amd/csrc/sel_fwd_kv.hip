@@ -119,8 +119,17 @@ struct KvTiles {
   }
 };
 
+// Waves per SIMD the forward's register allocation aims at: the entries' gathers are hidden
+// by occupancy, so the one-head-tile 64-key form is squeezed to four (nine registers spill,
+// and it still measured faster than three: 33.8 against 37.9 ms per launch at S = 128K).  The
+// row-statistic kernel holds dY rows as well and stays at its own allocation (three waves;
+// squeezed to four it spilled 28 registers and ran 5.2 against 3.2 ms at S = 32K).
+template <int NHT, int KB>
+constexpr int kv_waves() { return NHT == 1 && KB == 64 ? 4 : (NHT == 2 && KB == 128 ? 1 : 2); }
+
 template <typename T, int DQK, int NHT, int KB>
-__global__ __launch_bounds__(256) void sel_fwd_kv_kernel(SelFwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kv_waves<NHT, KB>()))) void sel_fwd_kv_kernel(
+    SelFwdArgs a) {
   using V8 = typename Mma<T>::v8;
   using L = KvTiles<DQK, KB>;
   using TM = typename L::TM;
