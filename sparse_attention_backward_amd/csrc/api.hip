@@ -401,8 +401,8 @@ attn_status_t validate_and_plan(const attn_bwd_problem_t* p, Plan& pl) {
     pl.off_list = o;    o = align_up(o + 4 * (size_t)pl.entries);
     pl.off_scratch = o; o = align_up(o + 8 * (size_t)pl.entries);
     pl.off_flag = o;    o = align_up(o + 4);
-    pl.off_dq_part = o;
-    o = align_up(o + 2 * (size_t)std::min<int64_t>(pl.win_tokens, pl.T1) * p->block_count * p->n1 * p->d_qk);
+    pl.off_dq_part = o;  // the shares of one window, then one (token, KV head) row group of scratch
+    o = align_up(o + 2 * ((size_t)std::min<int64_t>(pl.win_tokens, pl.T1) * p->block_count * p->n1 + pl.G) * p->d_qk);
     if (pl.nwin > 1) {
       pl.off_wofs = o;  o = align_up(o + 4 * nkeys * (size_t)(pl.nwin + 1));
       pl.off_kvacc = o; o = align_up(o + 4 * nkeys * (size_t)sel_kv_keys(p->block_size) * (p->d_qk + p->d_v));

@@ -32,9 +32,10 @@
 // of it (wofs).  Between windows the fp32 dK / dV accumulators of every block are kept in
 // kvacc (the first window starts from zero, the last one writes the bf16 outputs).
 //
-// Row staging as in the dense KV-major kernel: coalesced whole-row loads into registers
-// one step ahead, written to one of two swizzled LDS stages.  The list entries of a step
-// are read two steps ahead; lanes exchange row tokens with __shfl.
+// Row staging: each transfer instruction reads whole rows straight into one of two swizzled
+// LDS stages (global_load_lds), the rows of step st + 2 as soon as step st no longer needs
+// its stage; the list entries go the same way four steps ahead, and lanes exchange row
+// tokens with __shfl.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -50,6 +51,8 @@ struct SkvArgs {
   const float* lse2; const float* ndrow;
   uint16_t* dk; uint16_t* dv;
   uint16_t* dq_part;          // [window tokens, cnt, n2, G, DQK] in the element type
+  int trash_row;              // first of G share rows after those of the window: rows without an
+                              // entry store there (never read), so every step issues the same stores
   const int64_t* cu_kv;
   const int32_t* blkoff;      // [B+1] blocks before each sequence
   const int32_t* offsets;     // inverted index: [n2 * nblk_total + 1]
@@ -68,6 +71,23 @@ __device__ __forceinline__ void barrier_no_vm_wait() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// 16 bytes per lane from global memory into LDS at (M0 = lds + MOFF) + 16 * lane
+template <int MOFF>
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(src), "s"(lds), "i"(MOFF) : "memory", "m0", "scc");
+}
+
+// 4 bytes per lane from global memory into LDS at M0 = lds, + 4 * lane
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt operand for vmcnt(n) lgkmcnt(0), export count not waited for
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
+static_assert(wait_vm_lgkm0(63) == 0xc07f && wait_vm_lgkm0(0) == 0x0070, "s_waitcnt encoding");
 
 template <int N, typename F, int I = 0>
 __device__ __forceinline__ void static_for_i(F&& f) {
@@ -110,12 +130,15 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   using TY = RowTile<WY>;
   using TD = RowTile<8>;       // dS^T tile: 64 keys x 64 rows
   constexpr int OQM = 0, OQR = TM::BYTES, OY = OQR + (DR > 0 ? TR::BYTES : 0);
-  constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = ORW + 256;  // stage: QM, QR, Y, lse2, ndrow
+  // stage: QM, QR, Y, then 4 x 256 bytes of row statistics (lse2 from wave 0, ndrow from wave
+  // 1; waves 2 and 3 load the same rows into the other two slots, which nothing reads)
+  constexpr int OL = OY + TY::BYTES, ORW = OL + 256, SB = OL + 1024;
   constexpr int OKM = 2 * SB, OKR = OKM + NRH * TM::BYTES;            // K tile, KB rows (dQ product)
   constexpr int ODS = OKR + (DR > 0 ? NRH * TR::BYTES : 0);           // dS^T tile, KB key rows
+  constexpr int OENT = ODS + NRH * TD::BYTES;                          // per wave: 4 steps of list entries
   constexpr int NACC = 2 * (NQ + NV);
   constexpr int EPI = (NRH == 1 ? 2 * NACC * 1024 : 0) + KB * (DQK + DV) * 2;
-  constexpr int MAIN = ODS + NRH * TD::BYTES;
+  constexpr int MAIN = OENT + 4 * 1024;
   constexpr int SMEM = MAIN > EPI ? MAIN : EPI;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   static_assert(SB % 256 == 0 && OQR % 256 == 0 && OY % 256 == 0 && OKM % 256 == 0 && OKR % 256 == 0,
@@ -232,54 +255,87 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   }
 
   // ---- list entries: row `lane` of step st is entry e_begin + st * TPS + lane / G ------
-  auto entry_of = [&](int st) -> int {
+  // (-1 for padding rows and rows past the list)
+  auto row_has = [&](int st) -> bool {
     const int slot = lane / G;  // entry slot of row `lane`; slots >= TPS are padding rows
-    const int ei = e_begin + st * TPS + slot;
-    return slot < TPS && ei < e_end ? a.list[ei] : -1;
+    return slot < TPS && e_begin + st * TPS + slot < e_end;
   };
+  auto entry_of = [&](int st) -> int { return row_has(st) ? a.list[e_begin + st * TPS + lane / G] : -1; };
   const int first_entry = e_begin < e_end ? a.list[e_begin] : 0;  // stands in for missing rows
+  // rows of step st that have an entry: a prefix of the step (entry-major rows)
+  auto rows_valid = [&](int st) -> int { return min(TPS, e_end - e_begin - st * TPS) * G; };
 
-  // ---- staging: registers for the next stage ------------------------------------------
-  uint4 nm[WM / 4], nr[WR / 4], ny[WY / 4];
-  float nst = 0.f;
-  const int64_t hrow = (int64_t)kvh * G;  // first query head of the group
-  auto load_stage = [&](int ent) {  // ent: this lane's entry for its row (row = lane) of the step
+  // ---- staging ------------------------------------------------------------------------
+  // Every transfer goes from global memory straight into LDS (global_load_lds), so that no
+  // registers hold a stage and the rows of step st + 2 are requested as soon as the stage
+  // of step st is free (after the waves' S / dP products of step st), about 1.25 steps
+  // before they are used.  The list entries travel the same way, 4 steps ahead, into a
+  // 4-slot ring of this wave (lane = row of the step).  All transfers and stores of a step
+  // are issued whatever the step (rows past the list read the first entry's rows, entries
+  // past it the first entry), so the number of vector-memory operations each wave issues
+  // per step is fixed and the wait before a step counts exactly what may stay in flight.
+  const uint32_t ring = smem_lds + OENT + 1024 * w;
+  // Rows this lane transfers for the stage being prepared, as row indices t n1 + h of the
+  // [T1, n1, D] tensors (below 2^28: T1 is at most 2M and N1 at most 128): the row tokens
+  // are exchanged between lanes (LDS permutes, issued together).
+  int rim[WM / 4], rir[WR / 4], riy[WY / 4], rist = 0;
+  auto prep_rows = [&](int ent) {  // ent: this lane's entry for its row (row = lane) of the step
     const int tok_lane = (ent >= 0 ? ent : first_entry) / a.cnt;
-    // element offset of (row r of the step) in a [T1, n1, D] tensor, without the D factor
-    auto row_index = [&](int r) -> int64_t { return (int64_t)__shfl(tok_lane, r) * a.n1 + hrow + r % G; };
+    int tm[WM / 4], tr[WR / 4], ty[WY / 4];
 #pragma unroll
-    for (int kk = 0; kk < WM / 4; ++kk)
-      nm[kk] = ldg16(reinterpret_cast<const char*>(a.q + row_index(pm.row0 + 4 * TM::RPI * kk) * DQK) + pm.gchunk);
+    for (int kk = 0; kk < WM / 4; ++kk) tm[kk] = __shfl(tok_lane, pm.row0 + 4 * TM::RPI * kk);
     if constexpr (DR > 0) {
 #pragma unroll
-      for (int kk = 0; kk < WR / 4; ++kk)
-        nr[kk] = ldg16(reinterpret_cast<const char*>(a.q + row_index(pr.row0 + 4 * TR::RPI * kk) * DQK + DM) + pr.gchunk);
+      for (int kk = 0; kk < WR / 4; ++kk) tr[kk] = __shfl(tok_lane, pr.row0 + 4 * TR::RPI * kk);
     }
 #pragma unroll
-    for (int kk = 0; kk < WY / 4; ++kk)
-      ny[kk] = ldg16(reinterpret_cast<const char*>(a.dy + row_index(py.row0 + 4 * TY::RPI * kk) * DV) + py.gchunk);
-    if (w < 2) {
-      const int64_t row = (int64_t)tok_lane * a.n1 + hrow + hh_row;
-      nst = ent < 0 ? (w == 0 ? INFINITY : 0.f) : (w == 0 ? a.lse2[row] : a.ndrow[row]);
-    }
-  };
-  auto write_stage = [&](int soff) {
-    const uint32_t stage = smem_lds + soff;
+    for (int kk = 0; kk < WY / 4; ++kk) ty[kk] = __shfl(tok_lane, py.row0 + 4 * TY::RPI * kk);
+    const int h0 = kvh * G;
 #pragma unroll
-    for (int kk = 0; kk < WM / 4; ++kk) lds_st16_at(stage + OQM + (w + 4 * kk) * 1024 + 16 * lane, nm[kk]);
+    for (int kk = 0; kk < WM / 4; ++kk) rim[kk] = tm[kk] * a.n1 + h0 + (pm.row0 + 4 * TM::RPI * kk) % G;
     if constexpr (DR > 0) {
 #pragma unroll
-      for (int kk = 0; kk < WR / 4; ++kk) lds_st16_at(stage + OQR + (w + 4 * kk) * 1024 + 16 * lane, nr[kk]);
+      for (int kk = 0; kk < WR / 4; ++kk) rir[kk] = tr[kk] * a.n1 + h0 + (pr.row0 + 4 * TR::RPI * kk) % G;
     }
 #pragma unroll
-    for (int kk = 0; kk < WY / 4; ++kk) lds_st16_at(stage + OY + (w + 4 * kk) * 1024 + 16 * lane, ny[kk]);
-    if (w < 2) lds_st4_at(stage + OL + 256 * w + 4 * lane, nst);
+    for (int kk = 0; kk < WY / 4; ++kk) riy[kk] = ty[kk] * a.n1 + h0 + (py.row0 + 4 * TY::RPI * kk) % G;
+    rist = tok_lane * a.n1 + h0 + hh_row;
   };
+  // the rows found by prep_rows into the stage at `stage`: this wave's 1 KB blocks of each
+  // part, and the row statistic (lse2 for even waves, ndrow for odd) of the 64 rows
+  auto issue_stage = [&](uint32_t stage) {
+    static_for_i<WM / 4>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      dma16<4096 * kk>(reinterpret_cast<const char*>(a.q + (int64_t)rim[kk] * DQK) + pm.gchunk, stage + OQM + 1024 * w);
+    });
+    if constexpr (DR > 0) {
+      static_for_i<WR / 4>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        dma16<4096 * kk>(reinterpret_cast<const char*>(a.q + (int64_t)rir[kk] * DQK + DM) + pr.gchunk,
+                         stage + OQR + 1024 * w);
+      });
+    }
+    static_for_i<WY / 4>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      dma16<4096 * kk>(reinterpret_cast<const char*>(a.dy + (int64_t)riy[kk] * DV) + py.gchunk, stage + OY + 1024 * w);
+    });
+    dma4(((w & 1) ? a.ndrow : a.lse2) + rist, stage + OL + 256 * w);
+  };
+  // the list entries of step st into ring slot st % 4 (entries past the list read the first)
+  auto issue_entries = [&](int st) {
+    dma4(a.list + (row_has(st) ? e_begin + st * TPS + lane / G : e_begin), ring + 256 * (st & 3));
+  };
+  auto ring_entry = [&](int st) -> int {
+    const int e = __builtin_bit_cast(int, lds_f32_at(ring + 256 * (st & 3) + 4 * lane));
+    return row_has(st) ? e : -1;
+  };
+  // vector-memory operations per step: the stage's transfers, the entries, the dQ-share stores
+  constexpr int NSO = WM / 4 + (DR > 0 ? WR / 4 : 0) + WY / 4 + 1, NST = NFH;
 
   // ---- one step ------------------------------------------------------------------------
-  // rows 32 (rh0 + hi) .. +31 of the step staged at `stage`: S, dP, P, dS, dS^T -> LDS,
-  // dV += P^T dY, dK += dS^T Q
-  auto half_step = [&](uint32_t stage, auto hic) {
+  // rows 32 (rh0 + hi) .. +31 of the step staged at `stage`, whose first nvr rows have an
+  // entry: S, dP, P, dS, dS^T -> LDS, dV += P^T dY, dK += dS^T Q
+  auto half_step = [&](uint32_t stage, auto hic, int nvr) {
     constexpr int hi = decltype(hic)::value;
     const int rh = rh0 + hi;
     // lane bases of this wave's first row half (256-byte aligned part bases; see RowTile)
@@ -291,6 +347,16 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     for (int rt = 0; rt < 2; ++rt) {
       lse[rt] = lds_f32x4_at(statb + 64 * rt);
       ndr[rt] = lds_f32x4_at(statb + 256 + 64 * rt);
+    }
+    if (nvr < kRows) {  // rows without an entry (their rows are the first entry's): P = 0, no drow
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool pad = 32 * rh + 16 * rt + 4 * g + i >= nvr;
+          lse[rt][i] = pad ? INFINITY : lse[rt][i];
+          ndr[rt][i] = pad ? 0.f : ndr[rt][i];
+        }
     }
     constexpr int NS = KS + VS, PA = 3;
     const uint32_t am = vm + TM::rowA(lane, 0), ar = vr + TR::rowA(lane, 0), ay = vy + TY::rowA(lane, 0);
@@ -398,10 +464,9 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   };
 
   // dQ_part^T (features x rows) = K^T dS^T over the KB keys, for the feature half FH and
-  // rows 32 qh .. +31; every row with an entry stores its G x DQK share (bf16).
-  auto dq_part = [&](int ent_cur, auto fhc) {
+  // rows 32 qh .. +31
+  auto dq_prod = [&](f32x4 (&acc)[NFH][2], auto fhc) {
     constexpr int FH = decltype(fhc)::value;
-    f32x4 acc[NFH][2];
 #pragma unroll
     for (int f = 0; f < NFH; ++f)
 #pragma unroll
@@ -426,52 +491,67 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) acc[f][rr] = Mma<T>::run(kt[f], dt[rr], acc[f][rr]);
     }
-    // C tile (f, rr): lane holds row 32 qh + 16 rr + l16 and the permuted features above
+  };
+  // every row with an entry stores its share (G x DQK in the element type); C tile (f, rr):
+  // the lane holds row 32 qh + 16 rr + l16 and the permuted features above (feature half fh)
+  auto dq_store = [&](int ent_cur, const f32x4 (&acc)[NFH][2]) {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int r = 32 * qh + 16 * rr + l16;
       const int ent = __shfl(ent_cur, r);
-      if (ent >= 0) {
-        uint16_t* dst = a.dq_part + (((int64_t)(ent - a.e_lo) * a.n2 + kvh) * G + rmod[rr]) * DQK + FH * (DQK / 2) + 8 * g;
+      // share row (below 2^28: the shares of a window take at most 64 GiB)
+      const int srow = (ent >= 0 ? ((ent - a.e_lo) * a.n2 + kvh) * G : a.trash_row) + rmod[rr];
+      uint16_t* dst = a.dq_part + (int64_t)srow * DQK + fh * (DQK / 2) + 8 * g;
 #pragma unroll
-        for (int j = 0; j < NFH / 2; ++j)
-          *reinterpret_cast<V8*>(dst + 32 * j) = pack8t<T>(acc[2 * j][rr], acc[2 * j + 1][rr]);
-      }
+      for (int j = 0; j < NFH / 2; ++j)
+        *reinterpret_cast<V8*>(dst + 32 * j) = pack8t<T>(acc[2 * j][rr], acc[2 * j + 1][rr]);
     }
   };
 
-  auto step = [&](int soff, int ent_cur) {
-    const uint32_t stage = smem_lds + soff;
-    static_for_i<NRH>([&](auto hic) { half_step(stage, hic); });
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's dS^T writes are done
-    barrier_no_vm_wait();                // every wave's dS^T is in LDS
-    if (fh) dq_part(ent_cur, std::integral_constant<int, 1>{});
-    else dq_part(ent_cur, std::integral_constant<int, 0>{});
+  // step st: the S / dP products, then (the stage being free) the transfers of step st + 2
+  // and the entries of step st + 4, then the dQ product and the shares
+  auto step = [&](int st, int ent_cur) {
+    const uint32_t stage = smem_lds + (st & 1) * SB;
+    const int nvr = rows_valid(st);
+    static_for_i<NRH>([&](auto hic) { half_step(stage, hic, nvr); });
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's stage reads and dS^T writes are done
+    barrier_no_vm_wait();                // every wave's dS^T is in LDS; stage st is free
+    issue_stage(stage);                  // rows prepared at the top of the step
+    issue_entries(st + 4);
+    f32x4 acc[NFH][2];
+    if (fh) dq_prod(acc, std::integral_constant<int, 1>{});
+    else dq_prod(acc, std::integral_constant<int, 0>{});
+    dq_store(ent_cur, acc);  // after the join: one store sequence
   };
 
   // ---- step loop -----------------------------------------------------------------------
-  // Iteration st: barrier (stage st written; stage st+1 and the dS^T tile free), load stage
-  // st+1 into registers (its entries were read at iteration st-1), read the entries of step
-  // st+2, compute step st, write the registers into stage st+1.
-  int ent_cur = entry_of(0);
-  int ent_nx = nsteps > 1 ? entry_of(1) : -1;
+  // Before step st the stage of step st and the entries of step st + 2 must have arrived.
+  // This wave issued after them, in order: at step 0 the stage of step 1; at step 1 the
+  // operations of step 0; later the shares of step st - 2 and the operations of step st - 1
+  // (see step): that many may stay in flight.
   __syncthreads();  // K tile in LDS
   if (nsteps > 0) {
-    load_stage(ent_cur);
-    write_stage(0);
+    // ring slots 0, 1 from registers, 2, 3 by transfer; the stages of steps 0 and 1
+    const int e0 = entry_of(0), e1 = entry_of(1);
+    lds_st4_at(ring + 4 * lane, __builtin_bit_cast(float, e0));
+    lds_st4_at(ring + 256 + 4 * lane, __builtin_bit_cast(float, e1));
+    issue_entries(2);
+    issue_entries(3);
+    prep_rows(e0);
+    issue_stage(smem_lds);
+    prep_rows(e1);
+    issue_stage(smem_lds + SB);
   }
   for (int st = 0; st < nsteps; ++st) {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    if (st >= 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NST + NSO + 1));
+    else if (st == 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NST + NSO + 1));
+    else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NSO));
     barrier_no_vm_wait();
-    const bool more = st + 1 < nsteps;
-    if (more) load_stage(ent_nx);
-    const int ent_nx2 = st + 2 < nsteps ? entry_of(st + 2) : -1;
-    asm volatile("" ::: "memory");  // keep the loads ahead of the step
-    step((st & 1) * SB, ent_cur);
-    if (more) write_stage((~st & 1) * SB);
-    ent_cur = ent_nx;
-    ent_nx = ent_nx2;
+    const int ent_cur = ring_entry(st);
+    prep_rows(ring_entry(st + 2));
+    step(st, ent_cur);
   }
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // no transfer into LDS left in flight
 
   // ---- epilogue: dK, dV to bf16 through LDS (KB = 64: the two row halves summed first),
   // then 16-byte stores of whole rows.  With several windows the fp32 sums of the earlier
@@ -573,6 +653,7 @@ hipError_t launch_keys(const SelArgs& a, hipStream_t s) {
   k.q = (const uint16_t*)a.q; k.k = (const uint16_t*)a.k; k.v = (const uint16_t*)a.v; k.dy = (const uint16_t*)a.dy;
   k.lse2 = a.lse2; k.ndrow = a.ndrow;
   k.dk = (uint16_t*)a.dk; k.dv = (uint16_t*)a.dv; k.dq_part = (uint16_t*)a.dq_part;
+  k.trash_row = (int)(std::min<int64_t>(a.win_tokens, a.T1) * a.cnt * a.n1);
   k.cu_kv = a.cu_kv; k.blkoff = a.blkoff; k.offsets = a.offsets; k.list = a.list; k.sched = a.cursor;
   k.wofs = a.wofs; k.kvacc = a.kvacc; k.nwin = a.nwin; k.win = a.win; k.e_lo = (int)(a.t0 * a.cnt);
   k.batch = a.batch; k.n1 = a.n1; k.n2 = a.n2; k.G = a.G; k.bs = a.bs; k.cnt = a.cnt; k.nblk_total = a.nblk_total;
