@@ -23,13 +23,13 @@ SOURCES = ["api.hip", "preprocess.hip", "dense_fp32.hip", "dense_kv.hip", "dense
            "index.hip", "sel_kv.hip", "sel_reduce.hip", "sel_fwd_kv.hip", "indexer.hip"]
 ARCH = os.environ.get("ATTN_BWD_ARCH", "gfx950")
 # Compilation units: (object name, source, extra options).  sel_kv.hip is compiled twice,
-# once per key-block width.  The 64-key kernels run one wave per SIMD with every register in
-# use; asking for MFMA results in VGPRs keeps their score, dS and dQ-product accumulators
-# out of the AGPRs (fewer register moves; 3% faster at S = 32K), while the 128-key kernels
-# measured slower with it.
+# once per key-block width.  Both run one wave per SIMD; asking for MFMA results in VGPRs
+# keeps their score, dS and dQ-product accumulators out of the AGPRs and saves the register
+# moves between the two files (64 keys: 3% faster at S = 32K; 128 keys: 508 -> 415
+# registers, 4% faster on the Zipf workload).
 UNITS = [(os.path.splitext(s)[0], s, []) for s in SOURCES if s != "sel_kv.hip"] + [
     ("sel_kv_b64", "sel_kv.hip", ["-DSEL_KV_KEYS=64", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
-    ("sel_kv_b128", "sel_kv.hip", ["-DSEL_KV_KEYS=128"]),
+    ("sel_kv_b128", "sel_kv.hip", ["-DSEL_KV_KEYS=128", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
 ]
 
 

@@ -198,7 +198,12 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   py.init(w, lane);
   const uint32_t smem_lds = lds_addr(smem);
 
-  // K tile in LDS (RowTile layout, KB key rows; keys past the block repeat its last key)
+  // K tile in LDS (RowTile layout, KB key rows; keys past the block repeat its last key).
+  // The dQ product reads it by columns, every lane the same 8-byte half of its chunk; two
+  // rows whose swizzles differ by 2 (bit 1 of swz, see khalf) would read the same chunks,
+  // so on the rows with that bit set the two halves of every chunk are swapped.
+  auto khalf = [](auto tile, int r) -> int { return (decltype(tile)::swz(r) >> 1) & 1; };
+  auto half_swap = [](uint4 x, int sw) -> uint4 { return sw ? make_uint4(x.z, x.w, x.x, x.y) : x; };
   {
     PartLanes<WM> km;
     km.init(w, lane);
@@ -206,9 +211,10 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     for (int hk = 0; hk < NRH; ++hk)
 #pragma unroll
       for (int kk = 0; kk < WM / 4; ++kk) {
-        const int r = min(64 * hk + km.row0 + 4 * TM::RPI * kk, nk - 1);
+        const int rl = 64 * hk + km.row0 + 4 * TM::RPI * kk;  // row of the tile
+        const int r = min(rl, nk - 1);
         const uint4 x = ldg16(reinterpret_cast<const char*>(a.k + ((k0 + r) * a.n2 + kvh) * DQK) + km.gchunk);
-        lds_st16_at(smem_lds + OKM + hk * TM::BYTES + (w + 4 * kk) * 1024 + 16 * lane, x);
+        lds_st16_at(smem_lds + OKM + hk * TM::BYTES + (w + 4 * kk) * 1024 + 16 * lane, half_swap(x, khalf(TM{}, rl)));
       }
     if constexpr (DR > 0) {
       PartLanes<WR> kr_;
@@ -217,10 +223,11 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
       for (int hk = 0; hk < NRH; ++hk)
 #pragma unroll
         for (int kk = 0; kk < WR / 4; ++kk) {
-          const int r = min(64 * hk + kr_.row0 + 4 * TR::RPI * kk, nk - 1);
+          const int rl = 64 * hk + kr_.row0 + 4 * TR::RPI * kk;
+          const int r = min(rl, nk - 1);
           const uint4 x =
               ldg16(reinterpret_cast<const char*>(a.k + ((k0 + r) * a.n2 + kvh) * DQK + DM) + kr_.gchunk);
-          lds_st16_at(smem_lds + OKR + hk * TR::BYTES + (w + 4 * kk) * 1024 + 16 * lane, x);
+          lds_st16_at(smem_lds + OKR + hk * TR::BYTES + (w + 4 * kk) * 1024 + 16 * lane, half_swap(x, khalf(TR{}, rl)));
         }
     }
   }
@@ -230,10 +237,13 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   // (2j, 2j+1) gives each lane 8 consecutive features (one 16-byte store) and the four
   // lane groups of a row cover 64 consecutive bytes.  The K^T column reads follow the
   // permutation: 4-feature piece qq of tile f starts at feature F0(f) + 8 qq + 4 (f % 2),
-  // i.e. chunk group F0(f) / 32 of the K tile (RowTile::colK) plus 8 (f % 2) bytes.
+  // i.e. chunk group F0(f) / 32 of the K tile (RowTile::colK) plus 8 (f % 2) bytes, that
+  // half swapped on the lane's row if khalf says so (the row parity a lane reads is the
+  // same for every tile, k-step and +16 rows).
   const int fh = w & 1;
   const uint32_t kcm = smem_lds + OKM + TM::colK(lane, 0);
   const uint32_t kcr = smem_lds + OKR + TR::colK(lane, 0);
+  const uint32_t khm = 8u * khalf(TM{}, 4 * g + (l16 >> 2)), khr = 8u * khalf(TR{}, 4 * g + (l16 >> 2));
   int dscol[2], rmod[2];  // column reads of the dS^T tile; head of dQ-product rows 32 qh + 16 rr + l16
   {
     const int jj = l16 >> 2, qq = l16 & 3;
@@ -478,7 +488,8 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
         constexpr int f = decltype(fc)::value;
         constexpr int F0 = FH * (DQK / 2) + 32 * (f / 2);
         constexpr int rb = F0 < DM ? TM::RB : TR::RB;
-        const uint32_t o = (F0 < DM ? kcm ^ (64u * (F0 / 32)) : kcr ^ (64u * ((F0 - DM) / 32))) + 8 * (f % 2) + ks * 32 * rb;
+        const uint32_t o = (F0 < DM ? (kcm ^ (64u * (F0 / 32))) + ((8u * (f % 2)) ^ khm)
+                                    : (kcr ^ (64u * ((F0 - DM) / 32))) + ((8u * (f % 2)) ^ khr)) + ks * 32 * rb;
         kt[f] = as_v8<T>(join8(lds_tr16_at(o), lds_tr16_at(o + 16 * rb)));
       });
 #pragma unroll
