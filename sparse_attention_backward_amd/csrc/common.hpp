@@ -169,20 +169,19 @@ __device__ __forceinline__ void sts16_stream(void* p, uint4 v) {
   __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
 }
 
-// Bank-conflict-free LDS tile of bf16 rows, C columns, no padding (64 banks x 4 B).
-// The 16-byte chunk c of row r is stored at chunk c ^ h(r).  h is chosen so that
-//   * a ds_read_b128 over 16 consecutive rows at one column chunk, and
-//   * a ds_read_b64_tr_b16 over 8 consecutive rows x 32 contiguous bytes
-// both touch 64 distinct banks.  A row of C/2 words starts at bank 32*(r&1) when
-// C/2 = 32 (mod 64) and at bank 0 when C/2 = 0 (mod 64); h makes up the rest.
+// LDS tile of bf16 rows, C columns, no padding.  The 16-byte chunk c of row r is stored at
+// chunk c ^ h(r), with h the RowTile swizzle below (2 (r & 7), or 2 ((r >> 1) & 3) for rows
+// of 32 (mod 64) words): a ds_read_b128 over 16 consecutive rows at one column chunk and a
+// ds_read_b64_tr_b16 over 8 consecutive rows x 32 contiguous bytes run at the LDS's linear
+// rate (measured; see RowTile).
 template <int C>
 struct Swz {
   static_assert(C % 64 == 0, "swizzled rows hold a multiple of 64 bf16");
   static constexpr int W = C / 2;
   static_assert(W % 64 == 32 || (W % 64 == 0 && C % 128 == 0), "unsupported row length");
   __device__ __forceinline__ static int h(int r) {
-    if constexpr (W % 64 == 32) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
-    else return 2 * (r & 7) + ((r >> 3) & 1);
+    if constexpr (W % 64 == 32) return 2 * ((r >> 1) & 3);
+    else return 2 * (r & 7);
   }
   // element offset of (row r, column col); columns col..col+k stay contiguous while
   // they lie in one 8-element chunk
@@ -213,12 +212,17 @@ struct SwzCursor {
 // global->LDS transfers that each move 1024 contiguous LDS bytes = RPI = 64 / W whole rows
 // (lane l: row l / W, slot l % W).  Chunk c of row r sits in slot c ^ swz(r); the lane that
 // fills a slot reads the matching chunk, so every transfer reads whole rows (full cache
-// lines).  swz makes both kinds of read conflict free:
-//   * 16 consecutive rows (16-aligned) at one chunk (ds_read_b128 of a 16-row A operand):
-//     the slots are distinct (W = 16), resp. distinct within each row parity (W = 8, where
-//     even and odd rows start 32 banks apart);
-//   * 8 consecutive rows (8-aligned) x chunks {2j, 2j + 1} (ds_read_b64_tr_b16): the 16
-//     (row, chunk) pairs land in distinct slots, resp. distinct within each row parity.
+// lines).  swz(r) = 2 (r & 7) for 256-byte rows and 2 ((r >> 1) & 3) for 128-byte rows
+// (the XOR never touches chunk bit 0).  Measured on gfx950 (LDS cycles per instruction,
+// rocprofv3 SQ_LDS_IDX_ACTIVE / SQ_INSTS_LDS, with the operand offsets below):
+//   * the A-operand ds_read_b128 (16 rows at one chunk per lane group) takes 4 cycles, the
+//     rate of a linear 1 KiB read; folding row bit 3 into chunk bit 0 as well makes it
+//     2-way bank conflicted (8 cycles);
+//   * the transposed ds_read_b64_tr_b16 of colB (8 rows x 32 contiguous bytes) takes 2
+//     cycles, the rate of a linear 512-byte read;
+//   * colK, four chunks of a row at one 8-byte half per lane, is 2-way conflicted (4
+//     cycles) whatever the XOR, unless the rows with bit 1 of swz set keep their chunk
+//     halves swapped (2 cycles).
 template <int W>
 struct RowTile {
   static_assert(W == 8 || W == 16, "rows of 128 or 256 bytes");
@@ -226,8 +230,8 @@ struct RowTile {
   static constexpr int RPI = 1024 / RB;    // rows per transfer instruction
   static constexpr int BYTES = 64 * RB;
   __host__ __device__ static constexpr int swz(int r) {
-    if constexpr (W == 16) return 2 * (r & 7) + ((r >> 3) & 1);
-    else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+    if constexpr (W == 16) return 2 * (r & 7);
+    else return 2 * ((r >> 1) & 3);
   }
   __host__ __device__ static constexpr int off(int r, int c) { return r * RB + 16 * (c ^ swz(r)); }
 
