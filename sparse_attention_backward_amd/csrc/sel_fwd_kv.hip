@@ -108,11 +108,14 @@ struct KvTiles {
   template <typename T, int NHT, int KS>
   static __device__ __forceinline__ void scores(uint32_t smem_lds, int kt, int lane,
                                                 const typename Mma<T>::v8 (&Qf)[NHT][KS], f32x4 (&S)[NHT]) {
-    const uint32_t km = smem_lds + OKM + (kt >> 2) * TM::BYTES + 16 * (kt & 3) * TM::RB;
-    const uint32_t kr = smem_lds + OKR + (kt >> 2) * TR::BYTES + 16 * (kt & 3) * TR::RB;
+    // one lane address per part and key tile, the k-steps by XOR (the tile bases are 256-byte
+    // aligned, see RowTile): kept opaque so that the compiler does not hold one register per
+    // (tile, k-step) across the entry loop
+    const uint32_t km = opaque(smem_lds + OKM + (kt >> 2) * TM::BYTES + 16 * (kt & 3) * TM::RB + TM::rowA(lane, 0));
+    const uint32_t kr = opaque(smem_lds + OKR + (kt >> 2) * TR::BYTES + 16 * (kt & 3) * TR::RB + TR::rowA(lane, 0));
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const auto ka = s < 4 ? as_v8<T>(lds_b128_at(km + TM::rowA(lane, s))) : as_v8<T>(lds_b128_at(kr + TR::rowA(lane, s - 4)));
+      const auto ka = s < 4 ? as_v8<T>(lds_b128_at(km ^ (64u * s))) : as_v8<T>(lds_b128_at(kr ^ (64u * (s - 4))));
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) S[ht] = Mma<T>::run(ka, Qf[ht][s], S[ht]);
     }
@@ -120,10 +123,10 @@ struct KvTiles {
 };
 
 // Waves per SIMD the forward's register allocation aims at: the entries' gathers are hidden
-// by occupancy, so the one-head-tile 64-key form is squeezed to four (nine registers spill,
-// and it still measured faster than three: 33.8 against 37.9 ms per launch at S = 128K).  The
-// row-statistic kernel holds dY rows as well and stays at its own allocation (three waves;
-// squeezed to four it spilled 28 registers and ran 5.2 against 3.2 ms at S = 32K).
+// by occupancy, so the one-head-tile 64-key form runs four (106 registers, since the LDS
+// operand addresses are formed by XOR at each use instead of one register per tile and
+// k-step).  The row-statistic kernel holds dY rows as well and stays at its own allocation
+// (three waves, 140 registers; squeezed to four it spills and measured 2% slower).
 template <int NHT, int KB>
 constexpr int kv_waves() { return NHT == 1 && KB == 64 ? 4 : (NHT == 2 && KB == 128 ? 1 : 2); }
 
@@ -202,45 +205,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kv_waves<NH
       mb[ht] = mx;
       lb[ht] = group_sum(sum);
     }
-    // O_b^T = V^T P^T over the block: k-step kk covers keys 32 kk .. +31 (tiles 2 kk, 2 kk + 1)
-    f32x4 O[NHT][NF];
+    // O_b^T = V^T P^T over the block: k-step kk covers keys 32 kk .. +31 (tiles 2 kk, 2 kk + 1).
+    // P^T is packed first (the scores are then dead) and the features are taken in two halves,
+    // each stored as soon as it is done: fewer live registers at four waves per SIMD.
+    V8 pb[NKT / 2][NHT];
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht)
+    for (int kk = 0; kk < NKT / 2; ++kk)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) O[ht][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < NKT / 2; ++kk) {
-      if (2 * kk < nkt) {
-        V8 pb[NHT];
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) pb[ht] = pack8t<T>(S[2 * kk][ht], S[2 * kk + 1][ht]);
-        const uint32_t vt = smem_lds + L::OV + (kk >> 1) * TM::BYTES + 32 * (kk & 1) * TM::RB;
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const uint32_t o = vt + TM::colB(lane, f);
-          const V8 va = __builtin_bit_cast(V8, join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TM::RB)));
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) O[ht][f] = Mma<T>::run(va, pb[ht], O[ht][f]);
-        }
-      }
-    }
+      for (int ht = 0; ht < NHT; ++ht) pb[kk][ht] = pack8t<T>(S[2 * kk][ht], S[2 * kk + 1][ht]);
     // the entry's partial O_b / l_b as [feature tile f][head][16 features] (lane: features
     // 16 f + 4 g .. + 3 of its head), so that one store covers G x 32 contiguous bytes; m_b, l_b
     const int ent = a.list[e];
     const int64_t r = (int64_t)(ent - e_lo) * a.n2 + kvh;
     T* po = static_cast<T*>(a.part_o) + r * G * kDv;
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      const int h = 16 * ht + l16;
-      if (h < G) {
-        const float inv = 1.f / lb[ht];  // <= 1: l_b includes the maximum's own term, 1
+    for (int fh = 0; fh < 2; ++fh) {
+      constexpr int NFH = NF / 2;
+      f32x4 O[NHT][NFH];
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const uint2 w = make_uint2(pack2<T>(O[ht][f][0] * inv, O[ht][f][1] * inv),
-                                     pack2<T>(O[ht][f][2] * inv, O[ht][f][3] * inv));
-          *reinterpret_cast<uint2*>(po + (f * G + h) * 16 + 4 * g) = w;
+      for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int f = 0; f < NFH; ++f) O[ht][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NKT / 2; ++kk) {
+        if (2 * kk < nkt) {
+          const uint32_t vt = opaque(smem_lds + L::OV + (kk >> 1) * TM::BYTES + 32 * (kk & 1) * TM::RB + TM::colB(lane, 0));
+#pragma unroll
+          for (int f = 0; f < NFH; ++f) {
+            const uint32_t o = vt ^ (32u * (NFH * fh + f));
+            const V8 va = __builtin_bit_cast(V8, join8(lds_tr16_at(o), lds_tr16_at(o + 16 * TM::RB)));
+#pragma unroll
+            for (int ht = 0; ht < NHT; ++ht) O[ht][f] = Mma<T>::run(va, pb[kk][ht], O[ht][f]);
+          }
         }
-        if (g == 0) a.part_ml[r * G + h] = make_float2(mb[ht], lb[ht]);
+      }
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        const int h = 16 * ht + l16;
+        if (h < G) {
+          const float inv = 1.f / lb[ht];  // <= 1: l_b includes the maximum's own term, 1
+#pragma unroll
+          for (int f = 0; f < NFH; ++f) {
+            const uint2 w = make_uint2(pack2<T>(O[ht][f][0] * inv, O[ht][f][1] * inv),
+                                       pack2<T>(O[ht][f][2] * inv, O[ht][f][3] * inv));
+            *reinterpret_cast<uint2*>(po + ((NFH * fh + f) * G + h) * 16 + 4 * g) = w;
+          }
+          if (fh == 0 && g == 0) a.part_ml[r * G + h] = make_float2(mb[ht], lb[ht]);
+        }
       }
     }
 #pragma unroll
