@@ -229,8 +229,11 @@ attn_status_t attn_fwd_selected(const attn_bwd_problem_t* p,
  *   lists   [T1 * N2 * block_count]  entries t * block_count + slot, ascending within a key;
  *                           only offsets[N2 * NB] of them are written (out-of-range ids are left
  *                           out and raise the flag)
- *   order   [N2 * NB]       the keys in the order the KV-major pass takes them (longest list
- *                           first, ties by key; identity order above 8192 keys)
+ *   order   [N2 * NB]       the keys in the order the KV-major pass takes them: by length
+ *                           class, then by key.  With t_0 = the longest list's length and
+ *                           t_(k+1) = floor(4 t_k / 5), the class is the least k < 31 with
+ *                           length > t_(k+1), else 31; class 0 first (identity order above
+ *                           8192 keys)
  * All three are device buffers owned by the caller; `workspace` as for attn_bwd_selected.
  * Asynchronous on `hip_stream`; p->op must be ATTN_OP_SELECTED. */
 attn_status_t attn_bwd_selected_index(const attn_bwd_problem_t* p, const int32_t* topk_indices,

@@ -19,8 +19,17 @@
 // Entry order is ascending t * cnt + slot within a key, so no sort is needed.
 // Fallback path: atomic count, scan, atomic fill, then an LDS / global bitonic sort of each
 // key's segment.  Both give the same lists.
-// Schedule: the keys ordered by list length, longest first (ties by key), so that the
-// workgroups with the longest lists start first; identity order when too many keys.
+// Schedule: the keys in classes of list length, each class about 4/5 as long as the one before
+// it -- with thresholds t_0 = the longest length, t_(k+1) = floor(4 t_k / 5), class k holds the
+// lengths in (t_(k+1), t_k], 32 classes, the last also holding every shorter list -- longest
+// class first, and in key order within a class.  The workgroups with the longest lists start
+// first (the late ones are short, as in longest-first order), and those running at the same
+// time mostly belong to one KV head (and, for varlen batches, one sequence): lists drawn from
+// one distribution whose spread is below a fifth of the longest fall into one class.  Such
+// workgroups gather the same query rows -- a token's Q/dY rows for one KV head are read by
+// every block it chose -- and when those blocks run together the repeated reads are served
+// from the caches instead of HBM.
+// Identity order (which is head-major too) when there are too many keys.
 // Integer work only: bitwise reproducible.
 #include <algorithm>
 #include <climits>
@@ -256,14 +265,31 @@ __global__ __launch_bounds__(64) void idx_fill_ordered_kernel(SelArgs a, int64_t
   }
 }
 
-// Schedule: keys by list length, longest first; ties in key order.  One workgroup.
+// Schedule: keys by length class, longest class first; key order within a class.  One
+// workgroup.
+constexpr int kSchedClasses = 32;
+__device__ int length_class(int len, int longest) {
+  int t = longest;
+  for (int k = 0; k < kSchedClasses - 1; ++k) {
+    t = (int)((int64_t)t * 4 / 5);
+    if (len > t) return k;
+  }
+  return kSchedClasses - 1;
+}
 __global__ __launch_bounds__(1024) void idx_schedule_kernel(const int32_t* offsets, int nkeys, int32_t* sched) {
   extern __shared__ uint64_t sk[];
+  __shared__ int longest;
+  if (threadIdx.x == 0) longest = 0;
+  __syncthreads();
+  int mx = 0;
+  for (int i = threadIdx.x; i < nkeys; i += 1024) mx = max(mx, offsets[i + 1] - offsets[i]);
+  atomicMax(&longest, mx);
+  __syncthreads();
   int n = 1;
   while (n < nkeys) n <<= 1;
   for (int i = threadIdx.x; i < n; i += 1024) {
-    // ascending order of (~length, key): longest first, then lower key
-    sk[i] = i < nkeys ? ((uint64_t)(0x7fffffff - (offsets[i + 1] - offsets[i])) << 32) | (uint32_t)i : ~0ull;
+    // ascending order of (class, key); class 0 holds the longest lists
+    sk[i] = i < nkeys ? ((uint64_t)length_class(offsets[i + 1] - offsets[i], longest) << 32) | (uint32_t)i : ~0ull;
   }
   __syncthreads();
   for (int k = 2; k <= n; k <<= 1) {

@@ -57,7 +57,7 @@ struct SkvArgs {
   const int32_t* blkoff;      // [B+1] blocks before each sequence
   const int32_t* offsets;     // inverted index: [n2 * nblk_total + 1]
   const int32_t* list;        // entries t * cnt + slot, ascending per (KV head, block)
-  const int32_t* sched;       // [n2 * nblk_total] work order: keys, longest list first
+  const int32_t* sched;       // [n2 * nblk_total] work order: keys by length class, then key
   const int32_t* wofs;        // [n2 * nblk_total, nwin + 1] list position where each window starts
   float* kvacc;               // fp32 dK / dV of every key between windows, KB (DQK + DV) per key
   int batch, n1, n2, G, bs, cnt, nblk_total;

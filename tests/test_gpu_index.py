@@ -32,7 +32,20 @@ def expected_index(w, topk):
     counts = np.bincount(kv, minlength=n2 * NB)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     keys = np.arange(n2 * NB)
-    order = np.lexsort((keys, -counts)).astype(np.int32) if n2 * NB <= 8192 else keys.astype(np.int32)
+    # length classes: thresholds t_0 = longest, t_(k+1) = floor(4 t_k / 5); the least k < 31 with
+    # length > t_(k+1), else 31; ordered by class, then key
+    longest = int(counts.max(initial=0))
+
+    def length_class(n):
+        t = longest
+        for k in range(31):
+            t = t * 4 // 5
+            if n > t:
+                return k
+        return 31
+
+    cls = np.array([length_class(int(n)) for n in counts], dtype=np.int64)
+    order = np.lexsort((keys, cls)).astype(np.int32) if n2 * NB <= 8192 else keys.astype(np.int32)
     return offsets, lists, order, bool((~valid).any())
 
 
