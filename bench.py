@@ -67,30 +67,32 @@ def flops_per_pair(w: W.Workload, gemms=("S", "dP", "dV", "dQ", "dK")) -> int:
     return 2 * sum(width[g] for g in gemms)
 
 
-# library timing name -> (kernel identifier in profiler output, plain or mangled; kernel source file)
+# library timing name -> (kernel identifier in profiler output, plain or mangled; the source files
+# whose text decides its traffic: the kernel's own, and index.hip for the KV-major passes, whose
+# work order it computes)
 KERNEL_SOURCES = {
-    "dense_kv_major": ("dense_kv_kernel", "dense_kv.hip"),
-    "dense_dq": ("dense_dq_ds_kernel", "dense_dq.hip"),
-    "dense_dq_recompute": ("dense_dq_kernel", "attn_q.hip"),
-    "selected_kv_major": ("sel_kv_kernel", "sel_kv.hip"),
-    "selected_dq_reduce": ("dq_reduce_kernel", "sel_reduce.hip"),
-    "selected_forward": ("sel_fwd_kv_kernel", "sel_fwd_kv.hip"),
-    "selected_forward_combine": ("sel_fwd_combine_kernel", "sel_fwd_kv.hip"),
-    "selected_row_stat": ("sel_drow_kv_kernel", "sel_fwd_kv.hip"),
-    "selected_index": ("idx_fill_ordered_kernel", "index.hip"),
-    "indexer_query_major": ("idx_bwd_kernel", "indexer.hip"),
-    "indexer_dk_reduce": ("idx_dk_reduce_kernel", "indexer.hip"),
-    "row_stats": ("preprocess_kernel", "preprocess.hip"),
+    "dense_kv_major": ("dense_kv_kernel", ("dense_kv.hip",)),
+    "dense_dq": ("dense_dq_ds_kernel", ("dense_dq.hip",)),
+    "dense_dq_recompute": ("dense_dq_kernel", ("attn_q.hip",)),
+    "selected_kv_major": ("sel_kv_kernel", ("sel_kv.hip", "index.hip")),
+    "selected_dq_reduce": ("dq_reduce_kernel", ("sel_reduce.hip",)),
+    "selected_forward": ("sel_fwd_kv_kernel", ("sel_fwd_kv.hip", "index.hip")),
+    "selected_forward_combine": ("sel_fwd_combine_kernel", ("sel_fwd_kv.hip",)),
+    "selected_row_stat": ("sel_drow_kv_kernel", ("sel_fwd_kv.hip", "index.hip")),
+    "selected_index": ("idx_fill_ordered_kernel", ("index.hip",)),
+    "indexer_query_major": ("idx_bwd_kernel", ("indexer.hip",)),
+    "indexer_dk_reduce": ("idx_dk_reduce_kernel", ("indexer.hip",)),
+    "row_stats": ("preprocess_kernel", ("preprocess.hip",)),
 }
 CSRC = os.path.join(ROOT, "sparse_attention_backward_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash(name: str) -> str:
-    """sha256 over the kernel's source file and the shared headers it includes."""
+    """sha256 over the kernel's source files and the shared headers they include."""
     import hashlib
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[name][1], "common.hpp", "kernels.hpp"):
+    for f in (*KERNEL_SOURCES[name][1], "common.hpp", "kernels.hpp"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
