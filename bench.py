@@ -74,8 +74,8 @@ KERNEL_SOURCES = {
     "dense_kv_major": ("dense_kv_kernel", ("dense_kv.hip",)),
     "dense_dq": ("dense_dq_ds_kernel", ("dense_dq.hip",)),
     "dense_dq_recompute": ("dense_dq_kernel", ("attn_q.hip",)),
-    "selected_kv_major": ("sel_kv_kernel", ("sel_kv.hip", "index.hip")),
-    "selected_dq_reduce": ("dq_reduce_kernel", ("sel_reduce.hip",)),
+    "selected_kv_major": ("sel_kv_kernel", ("sel_kv.hip", "index.hip", "share_layout.hpp")),
+    "selected_dq_reduce": ("dq_reduce_kernel", ("sel_reduce.hip", "share_layout.hpp")),
     "selected_forward": ("sel_fwd_kv_kernel", ("sel_fwd_kv.hip", "index.hip")),
     "selected_forward_combine": ("sel_fwd_combine_kernel", ("sel_fwd_kv.hip",)),
     "selected_row_stat": ("sel_drow_kv_kernel", ("sel_fwd_kv.hip", "index.hip")),

@@ -21,8 +21,11 @@
 //   dV += P^T dY, dK += dS^T Q                       (registers, summed over all entries)
 //   dS^T -> LDS, then dQ_part^T = K^T dS^T over the block's keys (K staged in LDS once):
 //   every wave owns half of the feature columns for 32 rows, and each lane stores 8
-//   consecutive features of one row (bf16, 16 bytes) to dq_part[t - t0, slot, kvh, head, :],
-//   whose row index is (list entry t cnt + slot - t0 cnt) n2 + kvh.
+//   consecutive features of one row (bf16, 16 bytes) into the share of its (token, slot,
+//   KV head): G x DQK values at dq_part[t - t0, slot, kvh], whose index is (list entry
+//   t cnt + slot - t0 cnt) n2 + kvh.  Inside a share the 16-byte chunks are laid out so that
+//   one store instruction writes contiguous lines (share_chunk below); the reduction puts
+//   them back in (head, feature) order.
 // dq_reduce_kernel then sums the slots of each (token, KV head) in slot order.  Every
 // output row has one writer; no floating-point atomics: deterministic.
 //
@@ -38,6 +41,7 @@
 // tokens with __shfl.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "share_layout.hpp"
 
 namespace ab {
 
@@ -245,12 +249,15 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
   const uint32_t kcr = smem_lds + OKR + TR::colK(lane, 0);
   const uint32_t khm = 8u * khalf(TM{}, 4 * g + (l16 >> 2)), khr = 8u * khalf(TR{}, 4 * g + (l16 >> 2));
   int dscol[2], rmod[2];  // column reads of the dS^T tile; head of dQ-product rows 32 qh + 16 rr + l16
+  int schunk[2];           // share chunk of piece 0 for those rows (share_chunk)
+  const int SR = share_rows(G);
   {
     const int jj = l16 >> 2, qq = l16 & 3;
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       dscol[rr] = ODS + TD::off(4 * g + jj, 2 * (2 * qh + rr) + (qq >> 1)) + 8 * (qq & 1);
       rmod[rr] = (32 * qh + 16 * rr + l16) % G;
+      schunk[rr] = share_chunk<DQK>(rmod[rr], 4 * fh * (NFH / 2) + g, SR);
     }
   }
 
@@ -510,12 +517,12 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
     for (int rr = 0; rr < 2; ++rr) {
       const int r = 32 * qh + 16 * rr + l16;
       const int ent = __shfl(ent_cur, r);
-      // share row (below 2^28: the shares of a window take at most 64 GiB)
-      const int srow = (ent >= 0 ? ((ent - a.e_lo) * a.n2 + kvh) * G : a.trash_row) + rmod[rr];
-      uint16_t* dst = a.dq_part + (int64_t)srow * DQK + fh * (DQK / 2) + 8 * g;
+      // first row of the share (below 2^28: the shares of a window take at most 64 GiB)
+      const int srow0 = ent >= 0 ? ((ent - a.e_lo) * a.n2 + kvh) * G : a.trash_row;
+      uint16_t* dst = a.dq_part + (int64_t)srow0 * DQK + 8 * schunk[rr];
 #pragma unroll
-      for (int j = 0; j < NFH / 2; ++j)
-        *reinterpret_cast<V8*>(dst + 32 * j) = pack8t<T>(acc[2 * j][rr], acc[2 * j + 1][rr]);
+      for (int j = 0; j < NFH / 2; ++j)  // piece j: row chunk 4 (fh NFH / 2 + j) + g
+        *reinterpret_cast<V8*>(dst + 8 * 4 * SR * j) = pack8t<T>(acc[2 * j][rr], acc[2 * j + 1][rr]);
     }
   };
 

@@ -2,11 +2,12 @@
 //
 // Page "NsaSelectedAttentionGrad", formula section: dQ = dS K / sqrt(d) over the gathered
 // rows, i.e. the sum over the selected blocks of each block's dS_block K_block.  The
-// KV-major kernel stores every block's share (bf16) at [t - t0, slot, kvh, head, :] for the
+// KV-major kernel stores every block's share (bf16, G x DQK) at [t - t0, slot, kvh] for the
 // tokens [t0, t1) of the current window (the list entry t cnt + slot, less t0 cnt, times n2,
-// plus kvh: no division in the store address); this kernel adds the slots of each (token,
-// KV head) of the window in slot order and scales:
-//   dQ[t, kvh G + h, :] = scale * sum_slot part[t, slot, kvh, h, :].
+// plus kvh: no division in the store address), its 16-byte chunks permuted as share_chunk
+// says; this kernel adds the slots of each (token, KV head) of the window chunk by chunk in
+// slot order, scales, and writes each chunk to its place (share_pos):
+//   dQ[t, kvh G + h, :] = scale * sum_slot part[t, slot, kvh](h, :).
 // Fixed order, one writer per output row: deterministic.
 //
 // One wave per (token, KV head).  Lane l owns the 16-byte chunks l, l + 64, ... of the
@@ -16,6 +17,7 @@
 // 64 slots.  Shares and dQ are touched once: streaming (non-temporal) loads and stores.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "share_layout.hpp"
 
 namespace ab {
 
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, ui
   }
   auto slot_ok = [&](int sl) -> bool { return (valid[sl >> 6] >> (sl & 63)) & 1; };
   const int chunks = G * DQK / 8;
+  const int R = share_rows(G);
   const int64_t slot_stride = (int64_t)n2 * G * DQK;
   const uint16_t* src = part + (tw * cnt * n2 + kvh) * (int64_t)G * DQK;
   uint16_t* out = dq + (t * n1 + (int64_t)kvh * G) * DQK;
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* part, ui
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           o[j] = (uint32_t)f2t<T>(acc[u][2 * j] * scale) | ((uint32_t)f2t<T>(acc[u][2 * j + 1] * scale) << 16);
-        sts16_stream(out + 8 * c, make_uint4(o[0], o[1], o[2], o[3]));
+        sts16_stream(out + 8 * share_pos<DQK>(c, R), make_uint4(o[0], o[1], o[2], o[3]));
       }
     }
   }
