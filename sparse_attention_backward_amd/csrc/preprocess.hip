@@ -43,7 +43,10 @@ __device__ __forceinline__ float dot16(uint4 a, uint4 b, float) {
          __uint_as_float(a.z) * __uint_as_float(b.z) + __uint_as_float(a.w) * __uint_as_float(b.w);
 }
 
-// LPR lanes cooperate on one row; each lane reads 16-byte chunks.
+// LPR lanes cooperate on one row; each lane reads 16-byte chunks.  A wave takes kRowU
+// groups of 64 / LPR rows per pass, their loads issued together (more bytes in flight per
+// wave, fewer workgroups to dispatch).
+constexpr int kRowU = 4;
 template <typename T, int LPR>
 __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
   constexpr int VEC = 16 / sizeof(T);
@@ -55,20 +58,29 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
   for (int64_t i = gtid; i < a.tab_n16; i += nthreads) a.tab_dst[i] = a.tab_src[i];
   const int64_t wave = gtid >> 6;
   const int64_t nwaves = nthreads >> 6;
-  for (int64_t base = wave * RPW; base < a.rows; base += nwaves * RPW) {
-    const int64_t row = base + lane / LPR;
-    float acc = 0.f;
-    if (row < a.rows && a.out) {
-      const T* o = reinterpret_cast<const T*>(a.out) + row * a.dv;
-      const T* d = reinterpret_cast<const T*>(a.dy) + row * a.dv;
-      for (int c = sub * VEC; c < a.dv; c += LPR * VEC) acc += dot16(ldg16(o + c), ldg16(d + c), T());
+  for (int64_t base = wave * RPW * kRowU; base < a.rows; base += nwaves * RPW * kRowU) {
+    float acc[kRowU];
+#pragma unroll
+    for (int u = 0; u < kRowU; ++u) {
+      const int64_t row = base + u * RPW + lane / LPR;
+      acc[u] = 0.f;
+      if (row < a.rows && a.out) {
+        const T* o = reinterpret_cast<const T*>(a.out) + row * a.dv;
+        const T* d = reinterpret_cast<const T*>(a.dy) + row * a.dv;
+        for (int c = sub * VEC; c < a.dv; c += LPR * VEC) acc[u] += dot16(ldg16(o + c), ldg16(d + c), T());
+      }
     }
 #pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (sub == 0 && row < a.rows) {
-      if (a.out) a.ndrow[row] = -acc;  // without O the row statistic comes from another pass
-      const float m = a.smax[row * 8], l = a.ssum[row * 8];
-      a.lse2[row] = (l > 0.f && m > -INFINITY) ? (m + logf(l)) * kLog2e : INFINITY;
+    for (int u = 0; u < kRowU; ++u) {
+      const int64_t row = base + u * RPW + lane / LPR;
+      float s = acc[u];
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (sub == 0 && row < a.rows) {
+        if (a.out) a.ndrow[row] = -s;  // without O the row statistic comes from another pass
+        const float m = a.smax[row * 8], l = a.ssum[row * 8];
+        a.lse2[row] = (l > 0.f && m > -INFINITY) ? (m + logf(l)) * kLog2e : INFINITY;
+      }
     }
   }
 }
@@ -78,9 +90,9 @@ static hipError_t launch_pre_t(const PreArgs& a, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   int chunks = a.dv / VEC, lpr = 1;
   while (lpr * 2 <= chunks && lpr < 64) lpr *= 2;
-  const int64_t rows_per_block = 4 * (64 / lpr);
+  const int64_t rows_per_block = 4 * (64 / lpr) * kRowU;
   int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
-  if (blocks > 16384) blocks = 16384;
+  if (blocks > 2048) blocks = 2048;  // about what the device holds at once; the rest loop
   if (blocks < 1) blocks = 1;
   dim3 grid((unsigned)blocks), block(256);
   switch (lpr) {
