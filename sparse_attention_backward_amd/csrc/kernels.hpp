@@ -113,8 +113,9 @@ struct SelArgs {
   int32_t* list;            // [T1 * n2 * cnt]  entries t * cnt + slot, sorted per key
   int32_t* sort_scratch;    // [2 * T1 * n2 * cnt]
   int32_t* flag;            // [1] raised on an out-of-range topk id
-  void* dq_part;            // [W, cnt, n2, G, d_qk] bf16: each block's share of dQ, for the W query
-                            // tokens of the current window
+  void* dq_part;            // [W, cnt, n2] shares of G x d_qk in the element type (chunks ordered as
+                            // share_layout.hpp says): each block's share of dQ, for the W query
+                            // tokens of the current window, then one share of trash rows
   int64_t T2;
   // query-token windows: the KV-major pass and the dQ reduction run once per window of
   // win_tokens consecutive query tokens, so the share buffer holds one window
