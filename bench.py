@@ -88,13 +88,22 @@ CSRC = os.path.join(ROOT, "sparse_attention_backward_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def source_code_only(text: str) -> str:
+    """C++ source without its comments and trailing blanks: what a counter record depends on."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(name: str) -> str:
-    """sha256 over the kernel's source files and the shared headers they include."""
+    """sha256 over the code (comments removed) of the kernel's source files and the shared
+    headers they include."""
     import hashlib
     h = hashlib.sha256()
     for f in (*KERNEL_SOURCES[name][1], "common.hpp", "kernels.hpp"):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(source_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
