@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
           ndr[rt][i] = pad ? 0.f : ndr[rt][i];
         }
     }
-    constexpr int NS = KS + VS, PA = 3;
+    constexpr int NS = KS + VS, PA = KB == 128 ? 2 : 3;  // A-fragment reads in flight
     const uint32_t am = vm + TM::rowA(lane, 0), ar = vr + TR::rowA(lane, 0), ay = vy + TY::rowA(lane, 0);
     auto afrag = [&](int s, int rt) -> V8 {
       if (s < KSM) return as_v8<T>(lds_b128_at((am ^ (64u * s)) + (32 * hi + 16 * rt) * TM::RB));
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void sel_kv_kernel(SkvArgs a) {
       else { o = cr ^ (32u * (j - NV - NQM)); rb = TR::RB; }
       return as_v8<T>(join8(lds_tr16_at(o + 32 * hi * rb), lds_tr16_at(o + (32 * hi + 16) * rb)));
     };
-    constexpr int NJ = NV + NQ, PD = 4;
+    constexpr int NJ = NV + NQ, PD = KB == 128 ? 3 : 4;  // column reads in flight (128 keys: fewer registers)
     V8 ring[PD];
 #pragma unroll
     for (int i = 0; i < PD; ++i) ring[i] = colfrag(i);
