@@ -121,8 +121,8 @@ typedef struct {
   int32_t dkdv_atomic;            /* indexer: 1 = scatter dK with fp32 atomics from the
                                      query-major pass (non-deterministic, smaller workspace);
                                      0 = sum each key row's shares in a fixed order through an
-                                     inverted index (faster on the 8K / topK 2048 workload:
-                                     7.8 ms against 27.5 ms).  Ignored (treated as 0) when
+                                     inverted index (faster: on the 8K / topK 2048 workload
+                                     the whole call takes about half the time).  Ignored (treated as 0) when
                                      deterministic = 1.  Selected and selected-forward: reserved,
                                      1 with deterministic = 0 returns ATTN_ERR_UNSUPPORTED.
                                      Dense: must be 0.                                        */
