@@ -27,10 +27,16 @@ ARCH = os.environ.get("ATTN_BWD_ARCH", "gfx950")
 # once per key-block width.  Both run one wave per SIMD; asking for MFMA results in VGPRs
 # keeps their score, dS and dQ-product accumulators out of the AGPRs and saves the register
 # moves between the two files (64 keys: 3% faster at S = 32K; 128 keys: 508 -> 415
-# registers, 4% faster on the Zipf workload).
-UNITS = [(os.path.splitext(s)[0], s, []) for s in SOURCES if s != "sel_kv.hip"] + [
-    ("sel_kv_b64", "sel_kv.hip", ["-DSEL_KV_KEYS=64", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
-    ("sel_kv_b128", "sel_kv.hip", ["-DSEL_KV_KEYS=128", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
+# registers, 4% faster on the Zipf workload).  The machine scheduler's instruction-level-
+# parallelism strategy suits the selected kernels (KV-major pass 2.5% faster at S = 128K and
+# 4% on the Zipf workload, the forward and row-statistic passes 1-4%, the dQ reduction 2%)
+# but not the dense or indexer kernels or the row statistics (slower by 3-50%).
+ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+UNIT_FLAGS = {"sel_fwd_kv": ILP, "sel_reduce": ILP}
+UNITS = [(os.path.splitext(s)[0], s, UNIT_FLAGS.get(os.path.splitext(s)[0], []))
+         for s in SOURCES if s != "sel_kv.hip"] + [
+    ("sel_kv_b64", "sel_kv.hip", ["-DSEL_KV_KEYS=64", "-mllvm", "-amdgpu-mfma-vgpr-form=1", *ILP]),
+    ("sel_kv_b128", "sel_kv.hip", ["-DSEL_KV_KEYS=128", "-mllvm", "-amdgpu-mfma-vgpr-form=1", *ILP]),
 ]
 # Units whose kernels wait for their own global->LDS transfers with hand-counted vmcnt values
 # (the transfers are inline asm, which the compiler's wait counting does not see).  The counts
