@@ -32,7 +32,8 @@ ARCH = os.environ.get("ATTN_BWD_ARCH", "gfx950")
 # 4% on the Zipf workload, the forward and row-statistic passes 1-4%, the dQ reduction 2%)
 # but not the dense or indexer kernels or the row statistics (slower by 3-50%).
 ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
-UNIT_FLAGS = {"sel_fwd_kv": ILP, "sel_reduce": ILP}
+# The dense KV-major kernel gains 1% from the AMDGPU-specific register-pressure trackers.
+UNIT_FLAGS = {"sel_fwd_kv": ILP, "sel_reduce": ILP, "dense_kv": ["-mllvm", "-amdgpu-use-amdgpu-trackers"]}
 UNITS = [(os.path.splitext(s)[0], s, UNIT_FLAGS.get(os.path.splitext(s)[0], []))
          for s in SOURCES if s != "sel_kv.hip"] + [
     ("sel_kv_b64", "sel_kv.hip", ["-DSEL_KV_KEYS=64", "-mllvm", "-amdgpu-mfma-vgpr-form=1", *ILP]),
