@@ -98,12 +98,17 @@ def source_code_only(text: str) -> str:
 
 def kernel_source_hash(name: str) -> str:
     """sha256 over the code (comments removed) of the kernel's source files and the shared
-    headers they include."""
+    headers they include, and over the extra compiler options of the units built from them."""
     import hashlib
+    from sparse_attention_backward_amd.build import UNITS
     h = hashlib.sha256()
-    for f in (*KERNEL_SOURCES[name][1], "common.hpp", "kernels.hpp"):
+    files = (*KERNEL_SOURCES[name][1], "common.hpp", "kernels.hpp")
+    for f in files:
         with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
             h.update(source_code_only(fh.read()).encode())
+    for unit, src, extra in UNITS:
+        if src in files:
+            h.update(f"{unit}: {' '.join(extra)}\n".encode())
     return h.hexdigest()
 
 
